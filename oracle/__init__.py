@@ -1,0 +1,47 @@
+"""CPU oracle for the KV-eviction hot path -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, fp64 NumPy statement of what the hot path computes, written
+from the pages' definitions:
+
+  * ``score_literal``  -- the averaged RoPE query-centre/key logit, computed
+    literally: rotate both vectors, take the real dot product, average over
+    the future offsets (TriAttention summary, section 3.4: "RoPE in complex
+    form", "The attention dot product in complex form", "Handling Multiple
+    Future Positions").
+  * ``score_series`` / ``score_folded`` -- the same number through the
+    trigonometric series and through the angle-addition expansion; used as
+    cross-checks of each other and of the literal form.
+  * ``partition`` / ``select_topk`` -- prompt and recent-window pinning and
+    exact top-n selection (TriAttention summary 3.4 "KV Cache Pruning
+    Procedure"; Random Attention section 2 Eq. 2 and section 3 rule 1).
+  * ``philox4x32_10`` / ``select_random`` -- per-head uniform random eviction
+    (Random Attention section 3, Eq. 3 and Algorithm 1) with a Philox4x32-10
+    counter-based generator written from its published description
+    (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2,
+    3", SC'11).
+  * ``compact`` -- the chronological gather of kept rows (Random Attention,
+    Appendix F "Engine details").
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The product package
+(``eviction_long_reasoning_amd``) never imports it, and this package imports
+nothing from the product: the two share only the seeded input generators in
+``workloads``.
+
+Every function is pinned by ``-m "not gpu"`` tests against closed forms,
+invariants, brute force and an independent library Philox; none is marked
+"parity unpinned".
+"""
+from .rope import band_frequencies, rope_rotate
+from .score import score_literal, score_series, score_folded, fold_coefficients
+from .policy import Partition, partition, canonical_scores, select_topk, select_random, random_uniforms
+from .philox import philox4x32_10, philox4x32_10_np, PHILOX_M, PHILOX_W
+from .compact import compact
+
+__all__ = [
+    "band_frequencies", "rope_rotate",
+    "score_literal", "score_series", "score_folded", "fold_coefficients",
+    "Partition", "partition", "canonical_scores", "select_topk", "select_random", "random_uniforms",
+    "philox4x32_10", "philox4x32_10_np", "PHILOX_M", "PHILOX_W",
+    "compact",
+]

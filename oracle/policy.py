@@ -1,0 +1,125 @@
+"""Pinning, top-n selection and random selection -- oracle (test infrastructure only).
+
+Sources:
+  * TriAttention summary, section 3.4 "KV Cache Pruning Procedure": when the
+    cache exceeds the budget B, keys are ranked by score and the top B are
+    kept; the rest are evicted for good.
+  * TriAttention blog, inference-time scoring step: prefill (prompt) tokens
+    are always kept by default and only decode tokens compete for what
+    remains of the budget.
+  * Random Attention, section 2 ("Periodic eviction with budget K and buffer
+    r"): a buffer of the most recent pairs is never scored, the candidates
+    are the cached positions outside it, and the top-K candidates are kept
+    (Eq. 2).
+  * Random Attention, section 3: the prompt is never evicted; every other
+    candidate gets an i.i.d. Uniform(0,1) score drawn independently per KV
+    head at every eviction (Eq. 3, Algorithm 1).
+  * Random Attention, Appendix F: keep-sets are sorted chronologically before
+    compaction.
+
+Readings taken where the pages leave a step open (each is also listed with
+the design notes):
+  * B counts every kept entry: prompt + recent window + selected.
+  * If T <= B nothing is compressed: kept = 0..T-1.
+  * The prompt is a hard pin: if P >= B, kept = the whole prompt, nothing is
+    selected and the recent window is dropped (n_kept = P).
+  * The recent window is a soft pin clipped to R' = min(R, B - P, T - P) and
+    holds the latest R' slots, so |kept| = B whenever P <= B.
+  * Ranking is (score descending, slot ascending); NaN ranks as -inf and
+    -0.0 equals +0.0.
+  * The random score of a candidate slot j is word 0 of Philox4x32-10 with
+    counter (p_j, (layer << 16) | head, seq, event) and key (seed mod 2^32,
+    seed >> 32), read as the uniform u = word0 / 2^32; ties go to the lower
+    slot.
+"""
+from __future__ import annotations
+
+from typing import NamedTuple, Optional
+
+import numpy as np
+
+from .philox import philox4x32_10_np
+
+
+class Partition(NamedTuple):
+    T: int          # cached slots
+    P: int          # pinned prompt slots [0, P)
+    R: int          # pinned recent slots [T - R, T)
+    e_lo: int       # evictable range [e_lo, e_hi)
+    e_hi: int
+    n_sel: int      # slots selected from the evictable range
+    n_kept: int     # |kept|
+    compress: bool  # False when T <= B (kept = everything)
+
+
+def partition(T: int, P: int, B: int, R: int) -> Partition:
+    """Split a head's T slots into prompt, recent window and evictable range."""
+    T = max(int(T), 0)
+    P = min(max(int(P), 0), T)
+    B, R = int(B), max(int(R), 0)
+    if B < 1:
+        raise ValueError("budget must be >= 1")
+    if T <= B:
+        return Partition(T, P, 0, P, P, 0, T, False)
+    R_eff = min(R, max(0, B - P), T - P)
+    e_lo, e_hi = P, T - R_eff
+    n_sel = max(0, B - P - R_eff)
+    n_kept = max(B, P)
+    return Partition(T, P, R_eff, e_lo, e_hi, n_sel, n_kept, True)
+
+
+def canonical_scores(scores) -> np.ndarray:
+    """fp64 copy with NaN -> -inf and -0.0 -> +0.0 (exact upcast otherwise)."""
+    s = np.array(scores, dtype=np.float64, copy=True)
+    s[np.isnan(s)] = -np.inf
+    s[s == 0.0] = 0.0
+    return s
+
+
+def _assemble(part: Partition, selected: np.ndarray) -> np.ndarray:
+    pins = np.concatenate([np.arange(0, part.P), np.arange(part.T - part.R, part.T)])
+    kept = np.sort(np.concatenate([pins, np.asarray(selected, dtype=np.int64)]))
+    assert kept.size == part.n_kept
+    return kept.astype(np.int32)
+
+
+def _top_by_rank(values: np.ndarray, part: Partition) -> np.ndarray:
+    """The n_sel evictable slots ranked first by (value desc, slot asc)."""
+    slots = np.arange(part.e_lo, part.e_hi, dtype=np.int64)
+    v = values[part.e_lo:part.e_hi]
+    order = np.lexsort((slots, -v))          # primary key: -v ascending; secondary: slot ascending
+    return slots[order[:part.n_sel]]
+
+
+def select_topk(scores, T: int, P: int, B: int, R: int) -> np.ndarray:
+    """Kept slots (ascending) for one head under the top-n rule."""
+    part = partition(T, P, B, R)
+    if not part.compress:
+        return np.arange(part.T, dtype=np.int32)
+    s = canonical_scores(np.asarray(scores)[:part.T])
+    return _assemble(part, _top_by_rank(s, part))
+
+
+def random_uniforms(pos, layer: int, head: int, seq: int, event: int, seed: int) -> np.ndarray:
+    """u_j = word0(Philox4x32-10(ctr=(p_j, layer<<16|head, seq, event), key=seed)) / 2^32."""
+    p = np.asarray(pos, dtype=np.int64).astype(np.uint64) & np.uint64(0xFFFFFFFF)
+    n = p.size
+    c1 = np.full(n, ((int(layer) << 16) | int(head)) & 0xFFFFFFFF, np.uint64)
+    c2 = np.full(n, int(seq) & 0xFFFFFFFF, np.uint64)
+    c3 = np.full(n, int(event) & 0xFFFFFFFF, np.uint64)
+    k0 = np.full(n, int(seed) & 0xFFFFFFFF, np.uint64)
+    k1 = np.full(n, (int(seed) >> 32) & 0xFFFFFFFF, np.uint64)
+    w0 = philox4x32_10_np(p, c1, c2, c3, k0, k1)[0]
+    return w0.astype(np.float64) / 4294967296.0
+
+
+def select_random(T: int, P: int, B: int, R: int, pos: Optional[np.ndarray],
+                  seed: int, event: int, layer: int, head: int, seq: int) -> np.ndarray:
+    """Kept slots (ascending) for one head under Random Attention's rule."""
+    part = partition(T, P, B, R)
+    if not part.compress:
+        return np.arange(part.T, dtype=np.int32)
+    p_all = np.arange(part.T, dtype=np.int64) if pos is None else np.asarray(pos, np.int64)[:part.T]
+    u = np.full(part.T, -np.inf)
+    u[part.e_lo:part.e_hi] = random_uniforms(p_all[part.e_lo:part.e_hi], layer, head, seq, event, seed)
+    return _assemble(part, _top_by_rank(u, part))

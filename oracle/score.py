@@ -1,0 +1,94 @@
+"""Key scores from the query centre -- oracle (test infrastructure only).
+
+What is computed (one KV head): for each cached key k_j at position p_j and
+the current position t,
+
+    S_j = (1/|D|) * sum_{delta in D} < RoPE(q_bar, t + delta), RoPE(k_j, p_j) >
+
+where <.,.> is the real dot product. This is the trigonometric-series term
+S_trig of the TriAttention summary (section 3.4 "TriAttention Key Importance
+Scoring: The Trigonometric Series Term", with the query replaced by its
+centre and the actual key kept) averaged over the future offsets D as in
+"Handling Multiple Future Positions" (the future query sits at the key's age
+plus delta; age + delta = t + delta - p_j). No 1/sqrt(d) factor appears in
+S_trig, so none is applied. The centre q_bar is supplied per KV head.
+
+Three independent evaluations are provided:
+  * ``score_literal`` -- rotate both vectors, dot, average (the definition);
+  * ``score_series``  -- sum_f |q_f||k_f| cos(omega_f Delta + phi_f), the
+    form of the summary's "attention dot product in complex form" with
+    phi_f = arg q_f - arg k_f;
+  * ``score_folded``  -- angle addition moves the offset average into one
+    complex coefficient per band, A_f = mean_delta exp(i omega_f delta), so
+    S_j = sum_f Re(q_f A_f conj(k_f) exp(i omega_f (t - p_j))). The
+    TriAttention blog's implementation walkthrough computes the same
+    Re(q_centre * conj(k) * exp(i phase)) product per band.
+
+The oracle's reference value is ``score_literal``.
+"""
+from __future__ import annotations
+
+from typing import Sequence
+
+import numpy as np
+
+from .rope import band_frequencies, rope_rotate
+
+
+def _as_inputs(K, pos, qbar):
+    K = np.asarray(K, dtype=np.float64)
+    if K.ndim != 2 or K.shape[1] % 2:
+        raise ValueError("K must be (T, d) with even d")
+    T = K.shape[0]
+    pos = np.arange(T, dtype=np.int64) if pos is None else np.asarray(pos, dtype=np.int64)
+    q = np.asarray(qbar, dtype=np.float64)
+    if pos.shape != (T,) or q.shape != (K.shape[1],):
+        raise ValueError("shape mismatch")
+    return K, pos, q
+
+
+def score_literal(K, pos, qbar, t: int, theta: float, deltas: Sequence[int]) -> np.ndarray:
+    """Mean over delta of the real dot product of RoPE(q_bar, t+delta) and RoPE(k_j, p_j)."""
+    K, pos, q = _as_inputs(K, pos, qbar)
+    if len(deltas) == 0:
+        raise ValueError("empty offset set")
+    k_rot = rope_rotate(K, pos, theta)                      # (T, d), independent of delta
+    acc = np.zeros(K.shape[0], dtype=np.float64)
+    for delta in deltas:
+        q_rot = rope_rotate(q, int(t) + int(delta), theta)  # (d,)
+        acc += k_rot @ q_rot
+    return acc / len(deltas)
+
+
+def score_series(K, pos, qbar, t: int, theta: float, deltas: Sequence[int]) -> np.ndarray:
+    """Mean over delta of sum_f |q_f| |k_f| cos(omega_f (t + delta - p_j) + arg q_f - arg k_f)."""
+    K, pos, q = _as_inputs(K, pos, qbar)
+    omega = band_frequencies(K.shape[1], theta)
+    qc = q[0::2] + 1j * q[1::2]
+    kc = K[:, 0::2] + 1j * K[:, 1::2]
+    amp = np.abs(qc)[None, :] * np.abs(kc)                  # (T, F)
+    phi = np.angle(qc)[None, :] - np.angle(kc)              # (T, F)
+    acc = np.zeros(K.shape[0], dtype=np.float64)
+    for delta in deltas:
+        dist = (int(t) + int(delta) - pos).astype(np.float64)
+        acc += np.sum(amp * np.cos(omega[None, :] * dist[:, None] + phi), axis=1)
+    return acc / len(deltas)
+
+
+def fold_coefficients(d: int, theta: float, deltas: Sequence[int]) -> np.ndarray:
+    """A_f = (1/|D|) sum_{delta in D} exp(i omega_f delta), complex128 (F,)."""
+    omega = band_frequencies(d, theta)
+    dl = np.asarray(list(deltas), dtype=np.float64)
+    return np.exp(1j * omega[None, :] * dl[:, None]).mean(axis=0)
+
+
+def score_folded(K, pos, qbar, t: int, theta: float, deltas: Sequence[int]) -> np.ndarray:
+    """sum_f Re(q_f A_f conj(k_f) exp(i omega_f (t - p_j))) -- the angle-addition form."""
+    K, pos, q = _as_inputs(K, pos, qbar)
+    d = K.shape[1]
+    omega = band_frequencies(d, theta)
+    u = (q[0::2] + 1j * q[1::2]) * fold_coefficients(d, theta, deltas)
+    kc = K[:, 0::2] + 1j * K[:, 1::2]
+    age = (int(t) - pos).astype(np.float64)
+    rot = np.exp(1j * omega[None, :] * age[:, None])
+    return np.real(u[None, :] * np.conj(kc) * rot).sum(axis=1)

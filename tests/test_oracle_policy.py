@@ -1,0 +1,209 @@
+"""Pins for the oracle's pinning, top-n selection and random selection (CPU only)."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import partition, select_random, select_topk, random_uniforms, canonical_scores
+from workloads import random_scores, rng
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "partition_cases.json")
+
+
+def _f32(vals):
+    return np.array([float(v) for v in vals], dtype=np.float32)
+
+
+# --------------------------------------------------------------------------
+# hand-worked cases
+# --------------------------------------------------------------------------
+def test_partition_golden():
+    for c in json.load(open(GOLDEN))["partition"]:
+        p = partition(c["T"], c["P"], c["B"], c["R"])
+        got = dict(e_lo=p.e_lo, e_hi=p.e_hi, n_sel=p.n_sel, n_kept=p.n_kept, compress=p.compress)
+        exp = {k: c[k] for k in got}
+        assert got == exp, c["name"]
+
+
+def test_select_golden():
+    for c in json.load(open(GOLDEN))["select"]:
+        kept = select_topk(_f32(c["scores"]), c["T"], c["P"], c["B"], c["R"])
+        assert kept.tolist() == c["kept"], c["name"]
+
+
+def test_canonical_scores():
+    s = canonical_scores(_f32(["nan", "-0.0", "0.0", "inf", "-inf", "1.5"]))
+    assert s[0] == -np.inf and np.signbit(s[1]) == False and s[3] == np.inf and s[5] == 1.5
+
+
+# --------------------------------------------------------------------------
+# the characterising invariant and brute force
+# --------------------------------------------------------------------------
+def _beats(sa, a, sb, b):
+    return sa > sb or (sa == sb and a < b)
+
+
+def _check_kept(kept, scores, T, P, B, R):
+    p = partition(T, P, B, R)
+    kept = np.asarray(kept)
+    assert kept.size == p.n_kept
+    assert np.all(np.diff(kept) > 0) and (kept.size == 0 or (kept[0] >= 0 and kept[-1] < T))
+    if not p.compress:
+        assert kept.tolist() == list(range(T))
+        return
+    ks = set(kept.tolist())
+    pins = set(range(p.P)) | set(range(T - p.R, T))
+    assert pins <= ks
+    sel = sorted(ks - pins)
+    assert len(sel) == p.n_sel and all(p.e_lo <= j < p.e_hi for j in sel)
+    s = canonical_scores(scores)
+    rest = [j for j in range(p.e_lo, p.e_hi) if j not in ks]
+    for a in sel:
+        for b in rest:
+            assert _beats(s[a], a, s[b], b)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_selection_invariant_random(seed):
+    r = rng(200, seed)
+    T = int(r.integers(0, 80))
+    P = int(r.integers(0, 20))
+    B = int(r.integers(1, 60))
+    R = int(r.integers(0, 12))
+    s = random_scores(seed, (max(T, 1),), ties=0.3, specials=bool(seed % 2))[:T]
+    _check_kept(select_topk(s, T, P, B, R), s, T, P, B, R)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_selection_brute_force(seed):
+    # among all n_sel-subsets of the evictable range exactly one dominates the rest under
+    # (score desc, slot asc); it must be the oracle's choice
+    r = rng(201, seed)
+    T, P, R = 14, int(r.integers(0, 3)), int(r.integers(0, 3))
+    B = int(r.integers(P + R + 1, T))
+    s = random_scores(100 + seed, (T,), ties=0.4, specials=(seed % 3 == 0))
+    p = partition(T, P, B, R)
+    c = canonical_scores(s)
+    E = list(range(p.e_lo, p.e_hi))
+    winners = [sub for sub in itertools.combinations(E, p.n_sel)
+               if all(_beats(c[a], a, c[b], b) for a in sub for b in E if b not in sub)]
+    assert len(winners) == 1
+    kept = select_topk(s, T, P, B, R)
+    assert sorted(set(kept.tolist()) - set(range(P)) - set(range(T - p.R, T))) == list(winners[0])
+
+
+def test_budget_counts_every_kept_entry():
+    # |kept| = B whenever the prompt fits in the budget (the full-pass workload shape)
+    for T, P, B, R in [(32768, 1024, 3072, 128), (32768, 512, 2048, 128), (2176, 2000, 2048, 128)]:
+        p = partition(T, P, B, R)
+        assert p.n_kept == B and p.P + p.R + p.n_sel == B
+
+
+# --------------------------------------------------------------------------
+# random selection: Random Attention section 3 (Eq. 3, Algorithm 1) and Appendix D
+# --------------------------------------------------------------------------
+def test_random_kept_structure():
+    for seed in range(6):
+        T, P, B, R = 300, 40, 100, 16
+        kept = select_random(T, P, B, R, None, seed, 3, 1, 2, 5)
+        p = partition(T, P, B, R)
+        assert kept.size == B and np.all(np.diff(kept) > 0)
+        assert set(range(P)) <= set(kept.tolist()) and set(range(T - p.R, T)) <= set(kept.tolist())
+
+
+def test_random_ranks_follow_uniforms():
+    # the selected candidates are exactly those with the n_sel largest uniforms (ties to lower slot)
+    T, P, B, R = 120, 10, 50, 8
+    p = partition(T, P, B, R)
+    u = random_uniforms(np.arange(p.e_lo, p.e_hi), 2, 3, 4, 9, 0xABCDEF0123)
+    want = np.arange(p.e_lo, p.e_hi)[np.lexsort((np.arange(u.size), -u))[:p.n_sel]]
+    kept = select_random(T, P, B, R, None, 0xABCDEF0123, 9, 2, 3, 4)
+    assert sorted(set(kept.tolist()) - set(range(P)) - set(range(T - p.R, T))) == sorted(want.tolist())
+
+
+def test_random_marginals_uniform():
+    # spec check (d): each evictable slot is kept with probability n_sel/|E|;
+    # pairs are kept together with probability n(n-1)/(|E|(|E|-1)).
+    T, P, B, R = 40, 4, 14, 4
+    p = partition(T, P, B, R)
+    nE, n = p.e_hi - p.e_lo, p.n_sel
+    trials = 4000
+    counts = np.zeros(T)
+    pair = 0
+    for ev in range(trials):
+        kept = select_random(T, P, B, R, None, 0x5EED, ev, 0, 0, 0)
+        counts[kept] += 1
+        ks = set(kept.tolist())
+        pair += (p.e_lo in ks) and (p.e_lo + 1 in ks)
+    obs = counts[p.e_lo:p.e_hi]
+    expct = trials * n / nE
+    chi2 = np.sum((obs - expct) ** 2 / expct)
+    # df = nE - 1 = 31; the 0.999 quantile of chi2(31) is about 61.1
+    assert chi2 < 61.1, chi2
+    assert np.all(counts[:P] == trials) and np.all(counts[T - p.R:] == trials)
+    pp = n * (n - 1) / (nE * (nE - 1))
+    assert abs(pair / trials - pp) < 4 * math.sqrt(pp * (1 - pp) / trials)
+
+
+def test_random_heads_and_layers_draw_independently():
+    # different heads/layers/sequences must not share a keep-set: expected overlap n^2/|E|
+    T, P, B, R = 600, 0, 100, 0
+    p = partition(T, P, B, R)
+    ov = []
+    for ev in range(50):
+        a = set(select_random(T, P, B, R, None, 1, ev, 0, 0, 0).tolist())
+        for other in [(0, 1, 0), (1, 0, 0), (0, 0, 1)]:
+            b = set(select_random(T, P, B, R, None, 1, ev, *other).tolist())
+            ov.append(len(a & b))
+    assert abs(np.mean(ov) - p.n_sel ** 2 / (p.e_hi - p.e_lo)) < 2.0
+
+
+def _survival_sim(K, r, lp, events, heads, seed):
+    """Periodic random eviction in the page's framework: budget K plus a never-scored buffer r.
+
+    The keep-all budget of the partition is B = K + r with a recent window R = r; r new tokens
+    arrive between events. Returns per-age survival estimates.
+    """
+    surv_num = np.zeros(events + 1)
+    surv_den = np.zeros(events + 1)
+    for h in range(heads):
+        pos = list(range(K + r))                         # cache right after an eviction
+        for ev in range(events):
+            pos = pos + list(range(pos[-1] + 1, pos[-1] + 1 + r))
+            arr = np.array(pos)
+            kept = select_random(len(arr), lp, K + r, r, arr, seed, ev, 0, h, 0)
+            keep = set(arr[kept].tolist())
+            # a candidate that entered the candidate set at event e0 has faced (ev - e0 + 1) draws
+            cand = arr[lp:len(arr) - r]
+            for p_ in cand.tolist():
+                first = 0 if p_ < K + r else (p_ - K - r) // r + 1   # first event as a candidate
+                n = ev - first + 1
+                if 1 <= n <= events:
+                    surv_den[n] += 1
+                    surv_num[n] += p_ in keep
+            pos = [x for x in pos if x in keep]
+    return surv_num, surv_den
+
+
+def test_random_survival_law():
+    # Random Attention Appendix D ("Implicit age bias"): a position survives each eviction with
+    # probability (K - l_p)/(K + r - l_p) independently, because the draw is fresh every time.
+    K, r, lp = 48, 8, 4
+    num, den = _survival_sim(K, r, lp, events=10, heads=40, seed=77)
+    q = (K - lp) / (K + r - lp)
+    # conditional survival at each draw must be q (not the geometric of a repeated draw)
+    ok = den[1:] > 100
+    cond = num[1:][ok] / den[1:][ok]
+    tol = 4 * np.sqrt(q * (1 - q) / den[1:][ok])
+    assert ok.sum() >= 5 and np.all(np.abs(cond - q) < tol), (cond, q)
+
+
+def test_random_survival_matches_pages_rate():
+    # the pages quote about 0.94 per eviction at K=1024, r=64 (small prompt)
+    K, r, lp = 1024, 64, 0
+    num, den = _survival_sim(K, r, lp, events=3, heads=3, seed=5)
+    rate = num[1:].sum() / den[1:].sum()
+    assert abs(rate - 0.94) < 0.01 and abs((K - lp) / (K + r - lp) - 0.94) < 0.005

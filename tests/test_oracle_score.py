@@ -1,0 +1,193 @@
+"""Pins for the oracle's score (CPU only).
+
+Each test ties the oracle to something other than itself: closed forms the
+mathematics fixes, the textbook rotation-matrix statement of RoPE, invariants
+the pages state, and agreement of three independently written evaluations
+(definition, trigonometric series, angle-addition fold).
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+from oracle import (band_frequencies, fold_coefficients, rope_rotate, score_folded,
+                    score_literal, score_series)
+from workloads import rng
+
+FORMS = [score_literal, score_series, score_folded]
+
+
+# --------------------------------------------------------------------------
+# closed forms (values fixed by trigonometry, not by the oracle)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("form", FORMS)
+def test_d2_unit_vectors_give_cos_of_distance(form):
+    # d=2: one band with omega_0 = theta^0 = 1, so the logit is cos(Delta + phi).
+    K = np.array([[1.0, 0.0]])
+    assert form(K, [0], [1.0, 0.0], 3, 1e4, [0])[0] == pytest.approx(math.cos(3.0), abs=1e-14)
+    # q has phase +pi/2, k phase 0: cos(Delta + pi/2) = -sin(Delta).  Pins the sign convention
+    # phi = arg q - arg k and the direction of rotation.
+    assert form(K, [4], [0.0, 1.0], 5, 1e6, [0])[0] == pytest.approx(-math.sin(1.0), abs=1e-14)
+    # averaging over the offsets D = {1, 2} with t = p
+    assert form(K, [7], [1.0, 0.0], 7, 1e4, [1, 2])[0] == pytest.approx(
+        (math.cos(1.0) + math.cos(2.0)) / 2, abs=1e-14)
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_band_frequency_and_interleaving(form):
+    # d=4, theta=1e4: omega_1 = 1e4^(-2/4) = 0.01.  Band 1 is coordinates (2, 3).
+    K = np.array([[0.0, 0.0, 1.0, 0.0]])
+    assert form(K, [0], [0.0, 0.0, 1.0, 0.0], 100, 1e4, [0])[0] == pytest.approx(math.cos(1.0), abs=1e-13)
+    # coordinate 0 pairs with 1, not with 2: different bands never interact.
+    for dist in (0, 1, 17, 1000):
+        assert form(np.array([[0.0, 0.0, 1.0, 0.0]]), [0], [1.0, 0.0, 0.0, 0.0], dist, 1e4, [0])[0] == \
+            pytest.approx(0.0, abs=1e-14)
+    # q=(1,0,0,0), k=(0,1,0,0): phi = 0 - pi/2, so cos(1 - pi/2) = sin(1) at Delta = 1.
+    assert form(np.array([[0.0, 1.0, 0.0, 0.0]]), [0], [1.0, 0.0, 0.0, 0.0], 1, 1e4, [0])[0] == \
+        pytest.approx(math.sin(1.0), abs=1e-14)
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_magnitudes_enter_as_product(form):
+    # |q|=5, |k|=2, angle between them: atan2(4,3) - pi/2 -> logit = 10*sin(atan2(4,3)) = 8 = <q,k>.
+    assert form(np.array([[0.0, 2.0]]), [9], [3.0, 4.0], 9, 1e4, [0])[0] == pytest.approx(8.0, abs=1e-13)
+
+
+def test_band_frequencies_values():
+    w = band_frequencies(8, 1e4)
+    assert w[0] == 1.0
+    np.testing.assert_allclose(w, [1.0, 0.1, 0.01, 0.001], rtol=1e-15)
+    np.testing.assert_allclose(band_frequencies(128, 1e6)[64 - 1], 1e6 ** (-126 / 128), rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# textbook statement of RoPE as a block-diagonal rotation matrix
+# --------------------------------------------------------------------------
+def _rope_matrix(d, p, theta):
+    R = np.zeros((d, d))
+    for f in range(d // 2):
+        a = p * theta ** (-2.0 * f / d)
+        R[2 * f:2 * f + 2, 2 * f:2 * f + 2] = [[math.cos(a), -math.sin(a)], [math.sin(a), math.cos(a)]]
+    return R
+
+
+@pytest.mark.parametrize("d,theta", [(2, 1e4), (4, 1e4), (8, 1e6), (16, 500.0)])
+def test_rotation_matrix_brute_force(d, theta):
+    r = rng(100, d)
+    T = 7
+    K = r.standard_normal((T, d))
+    q = r.standard_normal(d)
+    pos = r.integers(0, 300, T)
+    t = 311
+    D = [1, 3, 8, 64]
+    ref = np.array([np.mean([(_rope_matrix(d, t + dl, theta) @ q) @ (_rope_matrix(d, p, theta) @ k)
+                             for dl in D]) for k, p in zip(K, pos)])
+    for form in FORMS:
+        np.testing.assert_allclose(form(K, pos, q, t, theta, D), ref, rtol=0, atol=1e-12)
+    # and rope_rotate itself equals the matrix action
+    np.testing.assert_allclose(rope_rotate(K, pos, theta),
+                               np.stack([_rope_matrix(d, p, theta) @ k for k, p in zip(K, pos)]), atol=1e-13)
+
+
+def test_relative_position_property_of_rotation():
+    # R(a)^T R(b) = R(b - a): the logit depends on positions only through their difference.
+    d, theta = 8, 1e4
+    for a, b in [(0, 5), (100, 37), (32768, 65536 + 32768)]:
+        np.testing.assert_allclose(_rope_matrix(d, a, theta).T @ _rope_matrix(d, b, theta),
+                                   _rope_matrix(d, b - a, theta), atol=1e-9)
+
+
+# --------------------------------------------------------------------------
+# invariants
+# --------------------------------------------------------------------------
+def _rand_head(seed, T=33, d=16):
+    r = rng(101, seed)
+    return r.standard_normal((T, d)), r.integers(0, 5000, T), r.standard_normal(d)
+
+
+@pytest.mark.parametrize("d", [2, 4, 8, 64, 128])
+@pytest.mark.parametrize("theta", [1e4, 1e6])
+def test_three_forms_agree(d, theta):
+    r = rng(102, d, int(theta))
+    K, pos, q = r.standard_normal((40, d)), r.integers(0, 40000, 40), r.standard_normal(d)
+    D = sorted(set(int(x) for x in r.integers(0, 70000, 9)))
+    t = 40000
+    lit = score_literal(K, pos, q, t, theta, D)
+    amp = np.abs(q[0::2] + 1j * q[1::2]) @ np.abs(K[:, 0::2] + 1j * K[:, 1::2]).T
+    # fp64 evaluation of cos at phase angles up to ~1.1e5 rad carries ~eps*angle absolute error
+    tol = 8 * np.finfo(np.float64).eps * (t + max(D)) + 1e-14
+    for form in (score_series, score_folded):
+        assert np.max(np.abs(form(K, pos, q, t, theta, D) - lit) / amp) < tol
+
+
+def test_shift_invariance():
+    # a common shift of the current position and every key position leaves the score unchanged
+    K, pos, q = _rand_head(1)
+    D = [2 ** i for i in range(17)]
+    a = score_literal(K, pos, q, 6000, 1e6, D)
+    for c in (1, 977, 123456):
+        np.testing.assert_allclose(score_literal(K, pos + c, q, 6000 + c, 1e6, D), a, atol=1e-9, rtol=0)
+
+
+def test_zero_offset_at_same_position_is_plain_dot_product():
+    # D = {0} and p = t: both vectors rotate by the same angle; the real dot product is unchanged
+    K, pos, q = _rand_head(2)
+    np.testing.assert_allclose(score_literal(K, np.full(len(K), 4242), q, 4242, 1e4, [0]), K @ q, atol=1e-12)
+
+
+def test_linearity_in_query_centre():
+    # the mean of G query centres scores as the mean of the G scores
+    K, pos, _ = _rand_head(3)
+    r = rng(103)
+    qs = r.standard_normal((4, K.shape[1]))
+    D = [1, 2, 4, 8]
+    mean_q = score_literal(K, pos, qs.mean(0), 5100, 1e6, D)
+    np.testing.assert_allclose(mean_q, np.mean([score_literal(K, pos, qg, 5100, 1e6, D) for qg in qs], 0),
+                               atol=1e-12)
+
+
+def test_bilinear_scaling():
+    K, pos, q = _rand_head(4)
+    D = [1, 16, 256]
+    base = score_literal(K, pos, q, 5000, 1e4, D)
+    np.testing.assert_allclose(score_literal(2.5 * K, pos, -0.5 * q, 5000, 1e4, D), -1.25 * base, atol=1e-12)
+
+
+def test_offset_average_is_mean_of_single_offsets():
+    K, pos, q = _rand_head(5)
+    D = [1, 2, 4, 8, 16]
+    singles = [score_literal(K, pos, q, 5001, 1e6, [dl]) for dl in D]
+    np.testing.assert_allclose(score_literal(K, pos, q, 5001, 1e6, D), np.mean(singles, 0), atol=1e-12)
+
+
+def test_fold_coefficients_limits():
+    # low-frequency bands barely turn over D, so A_f -> 1; D = {0} gives A_f = 1 exactly
+    A = fold_coefficients(128, 1e6, [2 ** i for i in range(17)])
+    assert abs(A[-1] - 1.0) < 0.02        # omega_63 * mean(D) ~ 1.2e-6 * 7710
+    assert np.all(np.abs(A) <= 1.0 + 1e-15)
+    np.testing.assert_allclose(fold_coefficients(16, 1e4, [0]), np.ones(8))
+
+
+def test_post_rope_formulation_of_blog_agrees():
+    # TriAttention blog (implementation walkthrough): with keys stored post-RoPE, the score is
+    # Re(q_centre * conj(k_rot) * exp(i * omega * t_query)) summed over bands.  Averaged over the
+    # offsets it must equal the pre-RoPE definition.
+    K, pos, q = _rand_head(6, d=32)
+    theta, t, D = 1e6, 5200, [1, 4, 64, 4096]
+    k_rot = rope_rotate(K, pos, theta)
+    omega = band_frequencies(32, theta)
+    kr, ki = k_rot[:, 0::2], k_rot[:, 1::2]
+    qr, qi = q[0::2], q[1::2]
+    prod_real = qr * kr + qi * ki
+    prod_imag = qi * kr - qr * ki
+    blog = np.mean([np.sum(prod_real * np.cos((t + dl) * omega) - prod_imag * np.sin((t + dl) * omega), 1)
+                    for dl in D], 0)
+    np.testing.assert_allclose(score_literal(K, pos, q, t, theta, D), blog, atol=1e-11)
+
+
+def test_bad_inputs_raise():
+    with pytest.raises(ValueError):
+        score_literal(np.zeros((3, 5)), None, np.zeros(5), 0, 1e4, [1])
+    with pytest.raises(ValueError):
+        score_literal(np.zeros((3, 4)), None, np.zeros(4), 0, 1e4, [])
