@@ -1,0 +1,231 @@
+"""Throughput of the KV-eviction hot path on one MI355X.
+
+One step = one full eviction pass over the Qwen3-8B-shaped 32K cache
+(36 layers x 8 sequences x 8 KV heads, head_dim 128, bf16, T=32768, prompt
+1024, budget 3072, recent window 128, RoPE theta 1e6, 17 geometric offsets):
+tri_score -> kv_select_topk -> kv_compact, all on device-resident inputs.
+The random-eviction pass (kv_select_random -> kv_compact) over the same
+cache is timed in the same run and reported beside it.
+
+Prints one JSON line. `value` is KV entries (layer, seq, KV head, slot)
+scored+selected+compacted per second. The roofline block is for the
+dominant kernel (tri_score): algorithmic bytes per launch (each key row read
+once + one fp32 score written per entry) over its mean launch time measured
+with HIP events on the launch stream. `cpu_baseline` times the fp64 NumPy
+oracle on a bounded sample of the same workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+METRIC = "KV tokens scored+selected+compacted/sec and HBM GB/s (% peak), Qwen3-8B 32K"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=36, help="layers of the full-pass workload (36 = full size)")
+    ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the oracle's CPU sample (0 = skip)")
+    ap.add_argument("--no-random", action="store_true", help="skip the random-eviction pass")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run one elementwise copy of known size then exit after one pass (for HBM counter runs)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, n_kept_per_head: int):
+    """Per-pass algorithmic bytes of each kernel (one read of every key row, one score
+    write and read, kept rows of K and V read and written, index and position traffic)."""
+    e, d = w.elem_bytes, w.head_dim
+    n_entries = w.entries
+    n_heads = w.n_heads_total
+    n_kept = n_heads * n_kept_per_head
+    score = n_entries * (d * e + 4)
+    select = n_entries * 4 + n_heads * w.b_cap() * 4
+    compact = n_kept * (4 * d * e + 4 + 4) + n_heads * 0
+    rnd_select = n_heads * w.b_cap() * 4
+    return dict(score=score, select=select, compact=compact, random_select=rnd_select)
+
+
+def cpu_baseline(w, K, qb, n_heads: int):
+    """The oracle (score -> select -> compact, fp64 NumPy, one thread) on a bounded sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import bf16_to_f32
+
+    units = []
+    H = w.n_kv_heads
+    for idx in range(n_heads):
+        l, h = divmod(idx, H)
+        l %= w.n_layers
+        units.append((l, 0, h))
+    T, P = int(w.seq_len[0]), int(w.prompt_len[0])
+    host = []
+    for (l, s, h) in units:
+        bits = K[l, s, h, :T].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+        host.append(((l, s, h), bf16_to_f32(bits).astype(np.float64)))
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for (l, s, h), kf in host:
+            sc = oracle.score_literal(kf, None, qb[l, h], int(w.t_cur[s]), w.theta, w.deltas)
+            kept = oracle.select_topk(sc, T, P, w.budget, w.recent)
+            oracle.compact(kf, kf, None, kept)
+        dt = time.perf_counter() - t0
+    n = len(host) * T
+    return {"value": n / dt, "unit": "KV entries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(host)} heads (layers 0..{(len(host) - 1) // H}, seq 0, all KV heads) x {T} slots "
+                      f"= {n} entries; literal fp64 score + lexsort select + gather, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the path shards per (layer, seq, KV head) with no exchange)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import eviction_long_reasoning_amd as kv
+    from workloads import centres, kv_torch, workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workload(3, L=args.layers)
+    L, S, H, Tc, d = w.n_layers, w.n_seq, w.n_kv_heads, w.t_cap, w.head_dim
+    print(f"[bench] generating {w.name}: L={L} S={S} H={H} T={Tc} d={d} bf16", file=sys.stderr, flush=True)
+    mu, qb, _ = centres(w)
+    K, V = kv_torch(w, dev, mu)
+    i32 = lambda a: torch.as_tensor(np.asarray(a, np.int32), device=dev)
+    seq, plen, tcur = i32(w.seq_len), i32(w.prompt_len), i32(w.t_cur)
+    qbd = torch.from_numpy(qb).to(dev)
+    b_cap, out_cap = w.b_cap(), w.out_cap
+    scores = torch.empty((L, S, H, Tc), dtype=torch.float32, device=dev)
+    kept = torch.empty((L, S, H, b_cap), dtype=torch.int32, device=dev)
+    nk = torch.empty((S,), dtype=torch.int32, device=dev)
+    Ko = torch.empty((L, S, H, out_cap, d), dtype=K.dtype, device=dev)
+    Vo = torch.empty_like(Ko)
+    Po = torch.empty((L, S, H, out_cap), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize(dev)
+    print("[bench] inputs resident", file=sys.stderr, flush=True)
+
+    if args.pmc_probe:
+        # elementwise copy of known size (reads 4 GiB, writes 4 GiB) to scale HBM counters
+        x = torch.ones(1 << 30, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.mul(x, 1.0, out=y)
+        kv.tri_score(K, qbd, tcur, seq, w.theta, w.deltas, out=scores)
+        kv.kv_select_topk(scores, seq, plen, w.budget, w.recent, w.prompt_cap(), b_cap=b_cap, kept=kept, n_kept=nk)
+        kv.kv_compact(K, V, kept, nk, seq, out_cap, K_out=Ko, V_out=Vo, pos_out=Po)
+        torch.cuda.synchronize(dev)
+        print("[bench] pmc probe done", file=sys.stderr, flush=True)
+        return
+
+    def scored_pass(ev=None):
+        if ev: ev[0].record()
+        kv.tri_score(K, qbd, tcur, seq, w.theta, w.deltas, out=scores)
+        if ev: ev[1].record()
+        kv.kv_select_topk(scores, seq, plen, w.budget, w.recent, w.prompt_cap(), b_cap=b_cap, kept=kept, n_kept=nk)
+        if ev: ev[2].record()
+        kv.kv_compact(K, V, kept, nk, seq, out_cap, K_out=Ko, V_out=Vo, pos_out=Po)
+        if ev: ev[3].record()
+
+    def random_pass(event, ev=None):
+        if ev: ev[0].record()
+        kv.kv_select_random((L, S, H, Tc), seq, plen, w.budget, w.recent, w.prompt_cap(), 0x5EED000000000003,
+                            event, b_cap=b_cap, kept=kept, n_kept=nk)
+        if ev: ev[1].record()
+        kv.kv_compact(K, V, kept, nk, seq, out_cap, K_out=Ko, V_out=Vo, pos_out=Po)
+        if ev: ev[2].record()
+
+    for _ in range(args.warmup):
+        scored_pass()
+    torch.cuda.synchronize(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        scored_pass(evs[i])
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    k_ms = {name: float(np.mean([evs[i][a].elapsed_time(evs[i][b]) for i in range(args.steps)]))
+            for name, a, b in (("tri_score", 0, 1), ("kv_select_topk", 1, 2), ("kv_compact", 2, 3))}
+    print(f"[bench] scored pass {ms_step:.3f} ms/step, kernels {k_ms}", file=sys.stderr, flush=True)
+
+    n_kept_head = int(nk[0].item())
+    ab = algorithmic_bytes(w, n_kept_head)
+    entries = w.entries
+    pass_bytes = ab["score"] + ab["select"] + ab["compact"]
+
+    rnd = None
+    if not args.no_random:
+        for i in range(args.warmup):
+            random_pass(i)
+        revs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize(dev)
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            random_pass(1000 + i, revs[i])
+        torch.cuda.synchronize(dev)
+        rwall = (time.perf_counter() - t1) * 1e3 / args.steps
+        rk = {"kv_select_random": float(np.mean([revs[i][0].elapsed_time(revs[i][1]) for i in range(args.steps)])),
+              "kv_compact": float(np.mean([revs[i][1].elapsed_time(revs[i][2]) for i in range(args.steps)]))}
+        rbytes = ab["random_select"] + ab["compact"]
+        rnd = {"ms_per_pass": rwall, "entries_per_s": entries / (rwall * 1e-3),
+               "gbs": rbytes / (rwall * 1e-3) / 1e9, "kernel_ms": rk, "algorithmic_bytes": rbytes}
+        print(f"[bench] random pass {rwall:.3f} ms, kernels {rk}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if args.cpu_heads > 0:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, K, qb, args.cpu_heads)
+
+    score_s = k_ms["tri_score"] * 1e-3
+    achieved = ab["score"] / score_s / 1e9
+    out = {
+        "metric": METRIC,
+        "value": entries / (ms_step * 1e-3),
+        "unit": "KV entries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded concentrated pre-RoPE keys, bf16 K/V resident in HBM)",
+        "config": {"workload": w.name, "layers": L, "seqs": S, "kv_heads": H, "head_dim": d, "seq_len": Tc,
+                   "prompt": int(w.prompt_len[0]), "budget": w.budget, "recent": w.recent,
+                   "rope_theta": w.theta, "n_offsets": len(w.deltas), "kv_dtype": "bf16",
+                   "entries_per_pass": entries},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "tri_score",
+                     "bytes_per_launch": ab["score"], "ms_per_launch": k_ms["tri_score"]},
+        "pass": {"algorithmic_bytes": pass_bytes, "gbs": pass_bytes / (ms_step * 1e-3) / 1e9,
+                 "frac_of_peak": pass_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "kernel_ms": k_ms,
+                 "kernel_gbs": {"tri_score": achieved,
+                                "kv_select_topk": ab["select"] / (k_ms["kv_select_topk"] * 1e-3) / 1e9,
+                                "kv_compact": ab["compact"] / (k_ms["kv_compact"] * 1e-3) / 1e9}},
+        "random_pass": rnd,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,88 @@
+"""ctypes declarations of the C ABI in include/kvevict.h.
+
+The shared library is loaded on first use from the package directory. There
+is no fallback: if it is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from .build import LIB_PATH
+
+KV_OK, KV_EINVAL, KV_EDTYPE, KV_ESHAPE, KV_EHIP = 0, -1, -2, -3, -5
+KV_F32, KV_BF16 = 0, 1
+
+
+class KvShape(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32),
+        ("n_seq", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("t_cap", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("seq_len", ctypes.c_void_p),
+    ]
+
+
+class KvPolicy(ctypes.Structure):
+    _fields_ = [
+        ("budget", ctypes.c_int32),
+        ("recent", ctypes.c_int32),
+        ("prompt_cap", ctypes.c_int32),
+        ("prompt_len", ctypes.c_void_p),
+    ]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SIGNATURES = {
+    "kv_version": (_I32, []),
+    "kv_status_string": (ctypes.c_char_p, [_I32]),
+    "tri_score": (_I32, [ctypes.POINTER(KvShape), _P, _P, _P, _P, ctypes.c_double, ctypes.POINTER(_I32), _I32, _P, _P]),
+    "kv_select_topk": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, _P, _I32, _P, _P]),
+    "kv_select_random": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, ctypes.c_uint64,
+                                ctypes.c_uint32, _P, _I32, _P, _P]),
+    "kv_compact": (_I32, [ctypes.POINTER(KvShape), _P, _P, _P, _P, _I32, _P, _P, _P, _P, _I32, _P]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load():
+    """The loaded C library (raises RuntimeError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build the HIP kernels first "
+                    "(python -m eviction_long_reasoning_amd.build or __graft_entry__.build())")
+            lib = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+class KvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = load().kv_status_string(status).decode()
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+def check(fn: str, status: int) -> None:
+    if status != KV_OK:
+        raise KvError(fn, status)

@@ -1,0 +1,156 @@
+"""Torch-tensor front end of the C ABI (argument marshalling only).
+
+Each function checks devices, dtypes and shapes, allocates outputs that were
+not supplied, and passes raw device pointers plus torch's current HIP stream
+to the library. All arithmetic happens in the HIP kernels.
+
+Tensor layouts (head-major, see include/kvevict.h):
+  K, V        [L, S, H, t_cap, d]  float32 or bfloat16
+  pos         [L, S, H, t_cap]     int32 (optional; slot index otherwise)
+  qbar        [L, H, d]            float32
+  scores      [L, S, H, t_cap]     float32
+  kept        [L, S, H, b_cap]     int32
+  seq_len, prompt_len, t_cur, n_kept  [S] int32
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.KV_F32, torch.bfloat16: _lib.KV_BF16}
+
+
+def _dev_ptr(t: Optional[torch.Tensor], name: str, dtype=None, shape=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _shape(L, S, H, d, t_cap, dtype_code, seq_len_ptr) -> _lib.KvShape:
+    return _lib.KvShape(int(L), int(S), int(H), int(d), int(t_cap), int(dtype_code), seq_len_ptr)
+
+
+def tri_score(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len: torch.Tensor,
+              rope_theta: float, deltas: Sequence[int], pos: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Offset-averaged RoPE query-centre score of every cached key (fp32 [L,S,H,t_cap])."""
+    if K.dim() != 5 or K.dtype not in _DT:
+        raise ValueError("K must be [L,S,H,t_cap,d] float32/bfloat16")
+    L, S, H, t_cap, d = K.shape
+    dev = K.device
+    kp = _dev_ptr(K, "K")
+    qp = _dev_ptr(qbar, "qbar", torch.float32, (L, H, d), dev)
+    tp = _dev_ptr(t_cur, "t_cur", torch.int32, (S,), dev)
+    sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
+    pp = _dev_ptr(pos, "pos", torch.int32, (L, S, H, t_cap), dev)
+    if out is None:
+        out = torch.empty((L, S, H, t_cap), dtype=torch.float32, device=dev)
+    op = _dev_ptr(out, "out", torch.float32, (L, S, H, t_cap), dev)
+    dl = [int(x) for x in deltas]
+    arr = (ctypes.c_int32 * max(1, len(dl)))(*dl)
+    shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
+    st = _lib.load().tri_score(ctypes.byref(shape), kp, pp, qp, tp, float(rope_theta), arr, len(dl), op,
+                               _stream(dev))
+    _lib.check("tri_score", st)
+    return out
+
+
+def _select_io(L, S, H, b_cap, device, kept, n_kept):
+    if kept is None:
+        kept = torch.empty((L, S, H, b_cap), dtype=torch.int32, device=device)
+    if n_kept is None:
+        n_kept = torch.empty((S,), dtype=torch.int32, device=device)
+    kp = _dev_ptr(kept, "kept", torch.int32, (L, S, H, b_cap), device)
+    np_ = _dev_ptr(n_kept, "n_kept", torch.int32, (S,), device)
+    return kept, n_kept, kp, np_
+
+
+def kv_select_topk(scores: torch.Tensor, seq_len: torch.Tensor, prompt_len: torch.Tensor, budget: int,
+                   recent: int, prompt_cap: int, b_cap: Optional[int] = None,
+                   kept: Optional[torch.Tensor] = None, n_kept: Optional[torch.Tensor] = None
+                   ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-head kept slots (ascending, -1 padded) under the top-n rule, and n_kept per sequence."""
+    if scores.dim() != 4:
+        raise ValueError("scores must be [L,S,H,t_cap]")
+    L, S, H, t_cap = scores.shape
+    dev = scores.device
+    b_cap = int(b_cap if b_cap is not None else max(budget, prompt_cap))
+    sc = _dev_ptr(scores, "scores", torch.float32)
+    sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
+    pl = _dev_ptr(prompt_len, "prompt_len", torch.int32, (S,), dev)
+    kept, n_kept, kp, nkp = _select_io(L, S, H, b_cap, dev, kept, n_kept)
+    shape = _shape(L, S, H, 0, t_cap, 0, sp)
+    pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
+    st = _lib.load().kv_select_topk(ctypes.byref(shape), ctypes.byref(pol), sc, kp, b_cap, nkp, _stream(dev))
+    _lib.check("kv_select_topk", st)
+    return kept, n_kept
+
+
+def kv_select_random(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tensor, prompt_len: torch.Tensor,
+                     budget: int, recent: int, prompt_cap: int, seed: int, event: int,
+                     pos: Optional[torch.Tensor] = None, b_cap: Optional[int] = None,
+                     kept: Optional[torch.Tensor] = None, n_kept: Optional[torch.Tensor] = None
+                     ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-head kept slots under Random Attention's rule (Philox draw per head and event)."""
+    L, S, H, t_cap = (int(x) for x in cache_shape)
+    dev = seq_len.device
+    b_cap = int(b_cap if b_cap is not None else max(budget, prompt_cap))
+    sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
+    pl = _dev_ptr(prompt_len, "prompt_len", torch.int32, (S,), dev)
+    pp = _dev_ptr(pos, "pos", torch.int32, (L, S, H, t_cap), dev)
+    kept, n_kept, kp, nkp = _select_io(L, S, H, b_cap, dev, kept, n_kept)
+    shape = _shape(L, S, H, 0, t_cap, 0, sp)
+    pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
+    st = _lib.load().kv_select_random(ctypes.byref(shape), ctypes.byref(pol), pp, int(seed) & (2 ** 64 - 1),
+                                      int(event) & 0xFFFFFFFF, kp, b_cap, nkp, _stream(dev))
+    _lib.check("kv_select_random", st)
+    return kept, n_kept
+
+
+def kv_compact(K: torch.Tensor, V: torch.Tensor, kept: torch.Tensor, n_kept: torch.Tensor, seq_len: torch.Tensor,
+               out_cap: int, pos: Optional[torch.Tensor] = None, with_pos: bool = True,
+               K_out: Optional[torch.Tensor] = None, V_out: Optional[torch.Tensor] = None,
+               pos_out: Optional[torch.Tensor] = None):
+    """Gather kept rows: returns (K_out, V_out, pos_out) shaped [L,S,H,out_cap,(d)]."""
+    if K.dim() != 5 or K.dtype not in _DT or V.shape != K.shape or V.dtype != K.dtype:
+        raise ValueError("K and V must both be [L,S,H,t_cap,d] of the same float32/bfloat16 dtype")
+    L, S, H, t_cap, d = K.shape
+    dev = K.device
+    b_cap = kept.shape[-1]
+    kin, vin = _dev_ptr(K, "K"), _dev_ptr(V, "V", None, None, dev)
+    kp = _dev_ptr(kept, "kept", torch.int32, (L, S, H, b_cap), dev)
+    nkp = _dev_ptr(n_kept, "n_kept", torch.int32, (S,), dev)
+    sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
+    pp = _dev_ptr(pos, "pos", torch.int32, (L, S, H, t_cap), dev)
+    if K_out is None:
+        K_out = torch.empty((L, S, H, out_cap, d), dtype=K.dtype, device=dev)
+    if V_out is None:
+        V_out = torch.empty((L, S, H, out_cap, d), dtype=K.dtype, device=dev)
+    if with_pos and pos_out is None:
+        pos_out = torch.empty((L, S, H, out_cap), dtype=torch.int32, device=dev)
+    kop = _dev_ptr(K_out, "K_out", K.dtype, (L, S, H, out_cap, d), dev)
+    vop = _dev_ptr(V_out, "V_out", K.dtype, (L, S, H, out_cap, d), dev)
+    pop = _dev_ptr(pos_out, "pos_out", torch.int32, (L, S, H, out_cap), dev)
+    shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
+    st = _lib.load().kv_compact(ctypes.byref(shape), kin, vin, pp, kp, int(b_cap), nkp, kop, vop, pop,
+                                int(out_cap), _stream(dev))
+    _lib.check("kv_compact", st)
+    return K_out, V_out, pos_out

@@ -1,0 +1,207 @@
+// C ABI of the KV-eviction hot path: argument validation, the fp64 fold of the
+// offset average, and kernel launches. See include/kvevict.h for the contract.
+#include <cmath>
+#include <cstdint>
+
+#include "kvevict.h"
+#include "kv_internal.hpp"
+
+#define KV_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace kvevict {
+namespace {
+
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Selectors never touch K/V rows, so they ignore head_dim and dtype (rows == false).
+kv_status check_shape(const kv_shape *sh, bool rows) {
+  if (!sh || !sh->seq_len) return KV_EINVAL;
+  if (sh->n_layers < 1 || sh->n_layers >= 65536 || sh->n_seq < 1 || sh->n_kv_heads < 1 ||
+      sh->n_kv_heads >= 65536 || sh->t_cap < 1)
+    return KV_EINVAL;
+  const long long heads = static_cast<long long>(sh->n_layers) * sh->n_seq * sh->n_kv_heads;
+  if (heads > (1ll << 31) - 1) return KV_ESHAPE;
+  if (!rows) return KV_OK;
+  if (sh->dtype != KV_F32 && sh->dtype != KV_BF16) return KV_EDTYPE;
+  const int d = sh->head_dim;
+  if (d < 2 || d > 2 * kMaxBands || (d % 2)) return KV_ESHAPE;
+  if (sh->dtype == KV_BF16 && d % 8) return KV_ESHAPE;
+  if (sh->dtype == KV_F32 && d % 4) return KV_ESHAPE;
+  return KV_OK;
+}
+
+kv_status check_policy(const kv_policy *po, int b_cap) {
+  if (!po || !po->prompt_len) return KV_EINVAL;
+  if (po->budget < 1 || po->recent < 0 || po->prompt_cap < 0) return KV_EINVAL;
+  if (b_cap < po->budget || b_cap < po->prompt_cap) return KV_ESHAPE;
+  return KV_OK;
+}
+
+kv_status hip_status(hipError_t e) { return e == hipSuccess ? KV_OK : KV_EHIP; }
+
+int elem_bytes(const kv_shape *sh) { return sh->dtype == KV_BF16 ? 2 : 4; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
+}  // namespace kvevict
+
+using namespace kvevict;
+
+KV_EXPORT int32_t kv_version(void) { return (1 << 16) | 0; }
+
+KV_EXPORT const char *kv_status_string(int32_t status) {
+  switch (status) {
+    case KV_OK: return "ok";
+    case KV_EINVAL: return "invalid argument (null pointer, non-positive size, bad policy or aliasing)";
+    case KV_EDTYPE: return "unknown element type";
+    case KV_ESHAPE: return "shape or capacity outside what the kernels support";
+    case KV_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+KV_EXPORT kv_status tri_score(const kv_shape *shape, const void *K, const int32_t *pos, const float *qbar,
+                              const int32_t *t_cur, double rope_theta, const int32_t *deltas, int32_t n_delta,
+                              float *scores, void *stream) {
+  kv_status st = check_shape(shape, true);
+  if (st != KV_OK) return st;
+  if (!K || !qbar || !t_cur || !deltas || !scores) return KV_EINVAL;
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta)) return KV_EINVAL;
+  if (n_delta < 1 || n_delta > kMaxDeltas) return KV_EINVAL;
+  if (!aligned16(K) || (reinterpret_cast<uintptr_t>(qbar) & 7u)) return KV_EINVAL;
+
+  ScoreParams p{};
+  p.K = K;
+  p.pos = pos;
+  p.qbar = qbar;
+  p.t_cur = t_cur;
+  p.seq_len = shape->seq_len;
+  p.scores = scores;
+  p.L = shape->n_layers;
+  p.S = shape->n_seq;
+  p.H = shape->n_kv_heads;
+  p.d = shape->head_dim;
+  p.F = shape->head_dim / 2;
+  p.t_cap = shape->t_cap;
+  p.chunks_per_head = (shape->t_cap + kScoreChunk - 1) / kScoreChunk;
+
+  // Band frequencies omega_f = theta^(-2f/d) and the fold coefficient
+  // A_f = (1/|D|) sum_delta exp(i omega_f delta), both in fp64 with the phase
+  // reduced to [-1/2, 1/2] revolutions before sin/cos.
+  for (int f = 0; f < p.F; ++f) {
+    const double omega = std::pow(rope_theta, -2.0 * f / p.d);
+    const double rev = omega / kTwoPi;
+    double re = 0.0, im = 0.0;
+    for (int i = 0; i < n_delta; ++i) {
+      const double x = rev * static_cast<double>(deltas[i]);
+      const double r = x - std::nearbyint(x);
+      re += std::cos(kTwoPi * r);
+      im += std::sin(kTwoPi * r);
+    }
+    p.A[f] = make_float2(static_cast<float>(re / n_delta), static_cast<float>(im / n_delta));
+    p.rev[f] = rev;
+  }
+  const int bpl = shape->dtype == KV_BF16 ? 4 : 2;  // bands per 16-byte lane piece
+  const int pieces = (p.F + bpl - 1) / bpl;
+  int lpk = 1;
+  while (lpk < pieces) lpk <<= 1;
+  if (lpk > 64) return KV_ESHAPE;
+  const long long threads = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head * kScoreThreads;
+  if (threads >= (1ll << 32)) return KV_ESHAPE;
+  return hip_status(launch_score(p, shape->dtype == KV_BF16, lpk, static_cast<hipStream_t>(stream)));
+}
+
+static kv_status select_common(const kv_shape *shape, const kv_policy *policy, int32_t *kept, int32_t b_cap,
+                               int32_t *n_kept, SelectParams &p) {
+  kv_status st = check_shape(shape, false);
+  if (st != KV_OK) return st;
+  if ((st = check_policy(policy, b_cap)) != KV_OK) return st;
+  if (!kept || !n_kept) return KV_EINVAL;
+  if (shape->t_cap > kSelectMaxSlots) return KV_ESHAPE;
+  p.seq_len = shape->seq_len;
+  p.prompt_len = policy->prompt_len;
+  p.kept = kept;
+  p.n_kept = n_kept;
+  p.L = shape->n_layers;
+  p.S = shape->n_seq;
+  p.H = shape->n_kv_heads;
+  p.t_cap = shape->t_cap;
+  p.b_cap = b_cap;
+  p.budget = policy->budget;
+  p.recent = policy->recent;
+  p.prompt_cap = policy->prompt_cap;
+  return KV_OK;
+}
+
+KV_EXPORT kv_status kv_select_topk(const kv_shape *shape, const kv_policy *policy, const float *scores,
+                                   int32_t *kept, int32_t b_cap, int32_t *n_kept, void *stream) {
+  SelectParams p{};
+  kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p);
+  if (st != KV_OK) return st;
+  if (!scores) return KV_EINVAL;
+  p.scores = scores;
+  return hip_status(launch_select(p, false, static_cast<hipStream_t>(stream)));
+}
+
+KV_EXPORT kv_status kv_select_random(const kv_shape *shape, const kv_policy *policy, const int32_t *pos,
+                                     uint64_t seed, uint32_t event, int32_t *kept, int32_t b_cap,
+                                     int32_t *n_kept, void *stream) {
+  SelectParams p{};
+  kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p);
+  if (st != KV_OK) return st;
+  p.pos = pos;
+  p.seed_lo = static_cast<uint32_t>(seed & 0xffffffffu);
+  p.seed_hi = static_cast<uint32_t>(seed >> 32);
+  p.event = event;
+  return hip_status(launch_select(p, true, static_cast<hipStream_t>(stream)));
+}
+
+KV_EXPORT kv_status kv_compact(const kv_shape *shape, const void *K_in, const void *V_in, const int32_t *pos_in,
+                               const int32_t *kept, int32_t b_cap, const int32_t *n_kept, void *K_out,
+                               void *V_out, int32_t *pos_out, int32_t out_cap, void *stream) {
+  kv_status st = check_shape(shape, true);
+  if (st != KV_OK) return st;
+  if (!K_in || !V_in || !kept || !n_kept || !K_out || !V_out) return KV_EINVAL;
+  if (b_cap < 1 || out_cap < 1) return KV_EINVAL;
+  if (!aligned16(K_in) || !aligned16(V_in) || !aligned16(K_out) || !aligned16(V_out)) return KV_EINVAL;
+  const size_t heads = static_cast<size_t>(shape->n_layers) * shape->n_seq * shape->n_kv_heads;
+  const size_t row_bytes = static_cast<size_t>(shape->head_dim) * elem_bytes(shape);
+  const size_t in_bytes = heads * shape->t_cap * row_bytes, out_bytes = heads * out_cap * row_bytes;
+  if (overlaps(K_in, in_bytes, K_out, out_bytes) || overlaps(V_in, in_bytes, V_out, out_bytes) ||
+      overlaps(K_in, in_bytes, V_out, out_bytes) || overlaps(V_in, in_bytes, K_out, out_bytes) ||
+      overlaps(K_out, out_bytes, V_out, out_bytes))
+    return KV_EINVAL;
+  if (pos_out && pos_in && overlaps(pos_in, heads * shape->t_cap * 4, pos_out, heads * out_cap * 4))
+    return KV_EINVAL;
+
+  CompactParams p{};
+  p.K_in = static_cast<const uint4 *>(K_in);
+  p.V_in = static_cast<const uint4 *>(V_in);
+  p.pos_in = pos_in;
+  p.kept = kept;
+  p.n_kept = n_kept;
+  p.K_out = static_cast<uint4 *>(K_out);
+  p.V_out = static_cast<uint4 *>(V_out);
+  p.pos_out = pos_out;
+  p.L = shape->n_layers;
+  p.S = shape->n_seq;
+  p.H = shape->n_kv_heads;
+  p.t_cap = shape->t_cap;
+  p.b_cap = b_cap;
+  p.out_cap = out_cap;
+  p.row16 = static_cast<int32_t>(row_bytes / 16);
+  int G = 1;
+  while (G < p.row16) G <<= 1;
+  const int rows_wg = compact_rows_per_wg(G);
+  const int max_rows = b_cap < out_cap ? b_cap : out_cap;
+  p.wgs_per_head = (max_rows + rows_wg - 1) / rows_wg;
+  const long long threads = static_cast<long long>(heads) * p.wgs_per_head * 256;
+  if (threads >= (1ll << 32)) return KV_ESHAPE;
+  return hip_status(launch_compact(p, static_cast<hipStream_t>(stream)));
+}

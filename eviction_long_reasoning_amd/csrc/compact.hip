@@ -1,0 +1,91 @@
+// Gather-compaction of kept K/V rows for gfx950.
+//
+// What is computed: "Random Attention: Rethinking KV Cache Eviction for
+// Efficient Reasoning", Appendix F ("Engine details"): after each eviction
+// the KV tensors are compacted with a gather, keep-sets in chronological
+// order. Row r of a head's output is row kept[r] of its input, for K, V and
+// the positions.
+//
+// Mapping: a row of d elements is row16 16-byte pieces; G = row16 rounded up
+// to a power of two lanes copy one row (global_load/store_dwordx4), 64/G rows
+// per wave instruction, and each thread keeps kUnroll rows of K and V in
+// flight before storing. A workgroup owns a contiguous range of output rows of
+// one head, so stores are fully contiguous and loads are whole rows (kept
+// indices ascend, so neighbouring kept rows often share DRAM pages).
+#include "kv_internal.hpp"
+
+namespace kvevict {
+namespace {
+
+constexpr int kCompactThreads = 256;
+constexpr int kUnroll = 4;
+
+template <int G>
+__global__ __launch_bounds__(kCompactThreads) void compact_kernel(const CompactParams p) {
+  constexpr int ROWS_PER_PASS = kCompactThreads / G;
+  constexpr int ROWS_PER_WG = ROWS_PER_PASS * kUnroll;
+  const int head = blockIdx.x / p.wgs_per_head;
+  const int part = blockIdx.x - head * p.wgs_per_head;
+  const int s = (head / p.H) % p.S;
+  const int nk = min(min(max(p.n_kept[s], 0), p.b_cap), p.out_cap);
+  const int r0 = part * ROWS_PER_WG;
+  if (r0 >= nk) return;
+
+  const int c = threadIdx.x % G;
+  const int rr = threadIdx.x / G;
+  const bool lane_live = c < p.row16;
+  const size_t in_row0 = static_cast<size_t>(head) * p.t_cap;
+  const size_t out_row0 = static_cast<size_t>(head) * p.out_cap;
+  const int32_t *kept = p.kept + static_cast<size_t>(head) * p.b_cap;
+
+  int src[kUnroll];
+  uint4 kv[kUnroll], vv[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int r = r0 + u * ROWS_PER_PASS + rr;
+    int j = r < nk ? kept[r] : -1;
+    j = (j >= 0 && j < p.t_cap) ? j : -1;
+    src[u] = j;
+    const bool ld = j >= 0 && lane_live;
+    const size_t off = (in_row0 + static_cast<size_t>(ld ? j : 0)) * p.row16 + (ld ? c : 0);
+    kv[u] = ld ? p.K_in[off] : make_uint4(0u, 0u, 0u, 0u);
+    vv[u] = ld ? p.V_in[off] : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int r = r0 + u * ROWS_PER_PASS + rr;
+    const int j = src[u];
+    if (j >= 0 && lane_live) {
+      const size_t off = (out_row0 + static_cast<size_t>(r)) * p.row16 + c;
+      p.K_out[off] = kv[u];
+      p.V_out[off] = vv[u];
+    }
+    if (j >= 0 && c == 0 && p.pos_out) p.pos_out[out_row0 + r] = p.pos_in ? p.pos_in[in_row0 + j] : j;
+  }
+}
+
+}  // namespace
+
+int compact_rows_per_wg(int group) { return (kCompactThreads / group) * kUnroll; }
+
+hipError_t launch_compact(const CompactParams &p, hipStream_t st) {
+  int G = 1;
+  while (G < p.row16) G <<= 1;
+  if (G > 64) return hipErrorInvalidValue;
+  const long long blocks = static_cast<long long>(p.L) * p.S * p.H * p.wgs_per_head;
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(blocks)), blk(kCompactThreads);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(compact_kernel<1>, grid, blk, 0, st, p); break;
+    case 2: hipLaunchKernelGGL(compact_kernel<2>, grid, blk, 0, st, p); break;
+    case 4: hipLaunchKernelGGL(compact_kernel<4>, grid, blk, 0, st, p); break;
+    case 8: hipLaunchKernelGGL(compact_kernel<8>, grid, blk, 0, st, p); break;
+    case 16: hipLaunchKernelGGL(compact_kernel<16>, grid, blk, 0, st, p); break;
+    case 32: hipLaunchKernelGGL(compact_kernel<32>, grid, blk, 0, st, p); break;
+    case 64: hipLaunchKernelGGL(compact_kernel<64>, grid, blk, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvevict

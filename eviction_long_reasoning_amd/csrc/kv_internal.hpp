@@ -1,0 +1,66 @@
+// Internal declarations shared by the kernels' translation units and the C ABI layer.
+// Not part of the public interface (include/kvevict.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvevict {
+
+constexpr int kMaxBands = 128;      // head_dim <= 256
+constexpr int kMaxDeltas = 64;
+
+// ---------------------------------------------------------------- score ----
+struct ScoreParams {
+  const void *K;            // [L,S,H,t_cap,d]
+  const int32_t *pos;       // [L,S,H,t_cap] or nullptr
+  const float *qbar;        // [L,H,d]
+  const int32_t *t_cur;     // [S]
+  const int32_t *seq_len;   // [S]
+  float *scores;            // [L,S,H,t_cap]
+  int32_t L, S, H, d, F, t_cap;
+  int32_t chunks_per_head;  // workgroups per (l,s,h)
+  float2 A[kMaxBands];      // fold coefficient per band: mean over D of exp(i omega_f delta)
+  double rev[kMaxBands];    // omega_f / (2 pi): revolutions per position, fp64
+};
+
+// Keys handled by one score workgroup (all lane layouts): 4 waves x 2 batches x 64 keys.
+constexpr int kScoreThreads = 256;
+constexpr int kScoreBatchesPerWave = 2;
+constexpr int kScoreChunk = (kScoreThreads / 64) * kScoreBatchesPerWave * 64;
+
+hipError_t launch_score(const ScoreParams &p, int dtype_bf16, int lanes_per_key, hipStream_t st);
+
+// --------------------------------------------------------------- select ----
+struct SelectParams {
+  const float *scores;      // [L,S,H,t_cap] (top-k) or nullptr (random)
+  const int32_t *pos;       // [L,S,H,t_cap] or nullptr (random counter positions)
+  const int32_t *seq_len;   // [S]
+  const int32_t *prompt_len;// [S]
+  int32_t *kept;            // [L,S,H,b_cap]
+  int32_t *n_kept;          // [S]
+  int32_t L, S, H, t_cap, b_cap;
+  int32_t budget, recent, prompt_cap;
+  uint32_t seed_lo, seed_hi, event;
+};
+
+constexpr int kSelectMaxSlots = 65536;
+hipError_t launch_select(const SelectParams &p, bool random, hipStream_t st);
+
+// -------------------------------------------------------------- compact ----
+struct CompactParams {
+  const uint4 *K_in, *V_in;   // rows of row16 x 16 B
+  const int32_t *pos_in;      // or nullptr
+  const int32_t *kept;        // [L,S,H,b_cap]
+  const int32_t *n_kept;      // [S]
+  uint4 *K_out, *V_out;
+  int32_t *pos_out;           // or nullptr
+  int32_t L, S, H, t_cap, b_cap, out_cap;
+  int32_t row16;              // 16-byte chunks per row
+  int32_t wgs_per_head;
+};
+
+int compact_rows_per_wg(int group);  // output rows per compact workgroup for a lane-group size
+hipError_t launch_compact(const CompactParams &p, hipStream_t st);
+
+}  // namespace kvevict

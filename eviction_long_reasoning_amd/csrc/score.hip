@@ -1,0 +1,204 @@
+// Streaming key-score kernel for gfx950.
+//
+// What is computed (one value per cached key): the trigonometric-series term
+// S_trig of "TriAttention: Efficient Long Reasoning with Trigonometric KV
+// Compression" (structured summary, section 3.4, "The Trigonometric Series
+// Term"), with the query replaced by its centre q_bar and averaged over the
+// future offsets D ("Handling Multiple Future Positions"):
+//
+//   S_j = sum_f Re( u_f * conj(k_{j,f}) * exp(i omega_f (t - p_j)) ),
+//   u_f = q_bar_f * A_f,   A_f = (1/|D|) sum_{delta in D} exp(i omega_f delta)
+//
+// The offset average enters only through A_f (angle addition, the a_f/b_f
+// expansion in the same section), so every key is read exactly once.
+//
+// Mapping onto CDNA4:
+//  * A key row is split into 16-byte pieces, one per lane (4 bands of bf16
+//    or 2 bands of fp32): LPK lanes per key, KPS = 64/LPK keys per wave
+//    instruction, so each wave load covers KPS consecutive rows -- a fully
+//    coalesced 1 KB (bf16, d=128) global_load_dwordx4.
+//  * A wave processes 64 consecutive keys as one batch of LPK steps, with all
+//    the batch's loads issued before the arithmetic (up to 16 x 16 B in flight
+//    per lane).
+//  * The phase exp(i omega_f m) is not evaluated per key. For contiguous
+//    positions each lane rotates its u_f * exp(i omega_f m) by a fixed step
+//    exp(-i omega_f KPS) from one key to its next; the value is re-derived
+//    exactly (fp64 reduction of omega_f m / 2pi to [-1/2, 1/2] revolutions,
+//    then fp32 sincospi) at the start of every 64-key batch, so the fp32
+//    recurrence runs at most LPK steps. With explicit (gappy) positions the
+//    phase is derived exactly for every key.
+//  * The LPK per-lane partial sums of a batch are combined by a shuffle
+//    reduce-scatter (LPK-1 exchanges per lane for LPK keys), after which each
+//    lane holds one finished score: 64 consecutive scores leave in one
+//    coalesced 256-byte store.
+#include "kv_internal.hpp"
+
+namespace kvevict {
+namespace {
+
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+  return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+
+// exp(i 2 pi rev m) with the phase reduced exactly in fp64 before the fp32 sincospi.
+__device__ __forceinline__ float2 cis_rev(double rev, double m) {
+  const double x = rev * m;
+  const double r = x - rint(x);
+  float sn, cs;
+  sincospif(2.0f * static_cast<float>(r), &sn, &cs);
+  return make_float2(cs, sn);
+}
+
+// Sum of acc[k] over the N lanes of a group (lanes differing in the low log2(N) bits);
+// lane g of the group returns the sum for k = g.
+template <int N>
+__device__ __forceinline__ float reduce_scatter(float (&acc)[N], int g) {
+#pragma unroll
+  for (int h = N / 2; h >= 1; h /= 2) {
+    const bool upper = (g & h) != 0;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      const float send = upper ? acc[i] : acc[i + h];
+      const float keep = upper ? acc[i + h] : acc[i];
+      acc[i] = keep + __shfl_xor(send, h, 64);
+    }
+  }
+  return acc[0];
+}
+
+template <bool BF16, int LPK, bool POS>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(const ScoreParams p) {
+  constexpr int BPL = BF16 ? 4 : 2;            // bands per lane (16 bytes)
+  constexpr int KPS = 64 / LPK;                // keys per wave step
+  constexpr int STEPS = LPK;                   // steps per 64-key batch
+  constexpr int SUB = STEPS < 16 ? STEPS : 16; // loads in flight per lane
+  constexpr int EB = BF16 ? 2 : 4;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane % LPK;
+  const int kk = lane / LPK;
+  const int head = blockIdx.x / p.chunks_per_head;
+  const int chunk = blockIdx.x - head * p.chunks_per_head;
+  const int h = head % p.H;
+  const int s = (head / p.H) % p.S;
+  const int l = head / (p.H * p.S);
+
+  const int T = min(max(p.seq_len[s], 0), p.t_cap);
+  const int wave_first = chunk * kScoreChunk + wave * (kScoreBatchesPerWave * 64);
+  if (wave_first >= T) return;
+  const double tq = static_cast<double>(p.t_cur[s]);
+
+  const bool live = g * BPL < p.F;
+  float2 u[BPL], w[BPL];
+  double rev[BPL];
+  const float2 *qrow = reinterpret_cast<const float2 *>(p.qbar + (static_cast<size_t>(l) * p.H + h) * p.d);
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int b = g * BPL + i;
+    if (live) {
+      u[i] = cmul(qrow[b], p.A[b]);
+      rev[i] = p.rev[b];
+      w[i] = cis_rev(rev[i], -static_cast<double>(KPS));
+    } else {
+      u[i] = make_float2(0.f, 0.f);
+      rev[i] = 0.0;
+      w[i] = make_float2(1.f, 0.f);
+    }
+  }
+
+  const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
+  const size_t row_bytes = static_cast<size_t>(p.d) * EB;
+  const char *Kh = static_cast<const char *>(p.K) + slot0 * row_bytes + static_cast<size_t>(g) * 16;
+
+#pragma unroll 1
+  for (int nb = 0; nb < kScoreBatchesPerWave; ++nb) {
+    const int j0 = wave_first + nb * 64;
+    if (j0 >= T) break;
+    float2 v[BPL];
+    if (!POS) {
+      const double m0 = tq - static_cast<double>(j0 + kk);
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) v[i] = cmul(u[i], cis_rev(rev[i], m0));
+    }
+    float acc[STEPS];
+#pragma unroll
+    for (int st0 = 0; st0 < STEPS; st0 += SUB) {
+      uint4 data[SUB];
+      int32_t pj[SUB];
+#pragma unroll
+      for (int t = 0; t < SUB; ++t) {
+        const int j = j0 + (st0 + t) * KPS + kk;
+        const bool in = j < T;
+        const int jc = in ? j : 0;  // masked lanes keep an in-range address
+        data[t] = (live && in) ? *reinterpret_cast<const uint4 *>(Kh + static_cast<size_t>(jc) * row_bytes)
+                               : make_uint4(0u, 0u, 0u, 0u);
+        if (POS) pj[t] = in ? p.pos[slot0 + jc] : 0;
+      }
+#pragma unroll
+      for (int t = 0; t < SUB; ++t) {
+        if (POS) {
+          const double m = tq - static_cast<double>(pj[t]);
+#pragma unroll
+          for (int i = 0; i < BPL; ++i) v[i] = cmul(u[i], cis_rev(rev[i], m));
+        }
+        const uint32_t wd[4] = {data[t].x, data[t].y, data[t].z, data[t].w};
+        float a = 0.f;
+        if (BF16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float re = __uint_as_float(wd[i] << 16);
+            const float im = __uint_as_float(wd[i] & 0xffff0000u);
+            a = fmaf(v[i].x, re, a);
+            a = fmaf(v[i].y, im, a);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            a = fmaf(v[i].x, __uint_as_float(wd[2 * i]), a);
+            a = fmaf(v[i].y, __uint_as_float(wd[2 * i + 1]), a);
+          }
+        }
+        acc[st0 + t] = a;
+        if (!POS) {
+#pragma unroll
+          for (int i = 0; i < BPL; ++i) v[i] = cmul(v[i], w[i]);
+        }
+      }
+    }
+    const float sc = reduce_scatter<STEPS>(acc, g);
+    const int jj = j0 + g * KPS + kk;
+    if (jj < T) p.scores[slot0 + jj] = sc;
+  }
+}
+
+template <bool BF16, bool POS>
+hipError_t launch_lpk(const ScoreParams &p, int lpk, dim3 grid, hipStream_t st) {
+  const dim3 blk(kScoreThreads);
+  switch (lpk) {
+    case 1: hipLaunchKernelGGL((score_kernel<BF16, 1, POS>), grid, blk, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((score_kernel<BF16, 2, POS>), grid, blk, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((score_kernel<BF16, 4, POS>), grid, blk, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((score_kernel<BF16, 8, POS>), grid, blk, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((score_kernel<BF16, 16, POS>), grid, blk, 0, st, p); break;
+    case 32: hipLaunchKernelGGL((score_kernel<BF16, 32, POS>), grid, blk, 0, st, p); break;
+    case 64: hipLaunchKernelGGL((score_kernel<BF16, 64, POS>), grid, blk, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score(const ScoreParams &p, int dtype_bf16, int lanes_per_key, hipStream_t st) {
+  const long long blocks = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head;
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  const bool pos = p.pos != nullptr;
+  if (dtype_bf16) return pos ? launch_lpk<true, true>(p, lanes_per_key, grid, st)
+                             : launch_lpk<true, false>(p, lanes_per_key, grid, st);
+  return pos ? launch_lpk<false, true>(p, lanes_per_key, grid, st)
+             : launch_lpk<false, false>(p, lanes_per_key, grid, st);
+}
+
+}  // namespace kvevict

@@ -1,0 +1,326 @@
+// Per-head exact top-n selection with pinned prompt and recent window, for gfx950.
+//
+// What is computed: "TriAttention: Efficient Long Reasoning with
+// Trigonometric KV Compression" (structured summary, section 3.4, "KV Cache
+// Pruning Procedure": keep the top B when the cache exceeds B), "Random
+// Attention: Rethinking KV Cache Eviction for Efficient Reasoning" (section
+// 2: a recent buffer that is never scored, top-K of the candidates, Eq. 2;
+// section 3: the prompt is never evicted, and each candidate gets an i.i.d.
+// uniform score drawn per KV head at every eviction, Eq. 3 / Algorithm 1;
+// Appendix F: keep-sets sorted chronologically).
+//
+// One workgroup owns one (layer, seq, KV head). Its T slot keys live in
+// registers in a blocked layout (thread t holds slots t*KPT .. t*KPT+KPT-1),
+// so the whole selection reads the head's scores from HBM once:
+//  1. Keys: fp32 scores mapped to order-preserving uint32 (NaN -> -inf,
+//     -0 -> +0) or, for the random selector, word 0 of Philox4x32-10.
+//  2. The bits shared by every candidate key are found with an OR/AND block
+//     reduction; radix passes start at the highest differing bit, which keeps
+//     the LDS histogram from collapsing into one bin for concentrated scores.
+//  3. 8-bit radix passes over a 256-bin LDS histogram locate the n_sel-th
+//     largest key thr and how many keys equal to thr must be taken.
+//  4. Two block prefix sums in slot order resolve ties to the lower slot and
+//     place every kept slot at its output index, so the kept list comes out
+//     in ascending order without a sort.
+#include "kv_internal.hpp"
+
+namespace kvevict {
+namespace {
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC'11): 10 rounds of two 32x32->64 products on counter
+// words 0 and 2 with the published multipliers, the key advanced between
+// rounds by the published Weyl constants. Returns output word 0.
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+  constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+  constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t lo_a = kMulA * c0, hi_a = __umulhi(kMulA, c0);
+    const uint32_t lo_b = kMulB * c2, hi_b = __umulhi(kMulB, c2);
+    const uint32_t n0 = hi_b ^ c1 ^ k0;
+    const uint32_t n2 = hi_a ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo_b;
+    c2 = n2;
+    c3 = lo_a;
+    k0 += kWeylA;
+    k1 += kWeylB;
+  }
+  return c0;
+}
+
+// Order-preserving uint32 image of an fp32 score: NaN ranks as -inf, -0 equals +0.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  if (f != f) b = 0xFF800000u;        // NaN -> -inf
+  if ((b << 1) == 0u) b = 0u;         // -0 -> +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *lds /* NT/64 + 1 */) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) lds[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t t = lane < NW ? lds[lane] : 0u;
+    uint32_t incl = t;
+#pragma unroll
+    for (int off = 1; off < NW; off <<= 1) {
+      const uint32_t y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane < NW) lds[lane] = incl - t;
+  }
+  __syncthreads();
+  return x - v + lds[wave];
+}
+
+template <int NT>
+__device__ __forceinline__ void block_or_and(uint32_t &o, uint32_t &a, uint32_t *lds /* 2*NT/64 */) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    o |= __shfl_xor(o, off, 64);
+    a &= __shfl_xor(a, off, 64);
+  }
+  if (lane == 0) {
+    lds[wave] = o;
+    lds[NW + wave] = a;
+  }
+  __syncthreads();
+  o = 0u;
+  a = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    o |= lds[i];
+    a &= lds[NW + i];
+  }
+}
+
+template <int NT, int KPT, bool RANDOM>
+__global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
+  constexpr int NW = NT / 64;
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t red[2 * NW];
+  __shared__ uint32_t scan_a[NW + 1];
+  __shared__ uint32_t scan_b[NW + 1];
+  __shared__ uint32_t found[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int head = blockIdx.x;
+  const int h = head % p.H;
+  const int s = (head / p.H) % p.S;
+  const int l = head / (p.H * p.S);
+
+  const int T = min(max(p.seq_len[s], 0), p.t_cap);
+  const int P = min(max(p.prompt_len[s], 0), min(p.prompt_cap, T));
+  const int B = p.budget;
+  int32_t *out = p.kept + static_cast<size_t>(head) * p.b_cap;
+  const bool writer = (l == 0 && h == 0 && tid == 0);
+
+  if (T <= B) {  // nothing to compress: keep 0..T-1
+    for (int r = tid; r < p.b_cap; r += NT) out[r] = r < T ? r : -1;
+    if (writer) p.n_kept[s] = T;
+    return;
+  }
+  const int Rw = min(p.recent, min(max(0, B - P), T - P));
+  const int e_lo = P, e_hi = T - Rw;
+  const int n_sel = max(0, B - P - Rw);
+  const int n_kept = max(B, P);
+  const int n_cand = e_hi - e_lo;
+
+  // ---- 1. keys, blocked layout
+  const int base = tid * KPT;
+  uint32_t key[KPT];
+  const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
+  if (!RANDOM) {
+    const float *row = p.scores + slot0;
+    if (base + KPT <= p.t_cap && ((reinterpret_cast<uintptr_t>(row + base) & 15u) == 0)) {
+#pragma unroll
+      for (int i = 0; i < KPT; i += 4) {
+        const float4 f = *reinterpret_cast<const float4 *>(row + base + i);
+        key[i] = order_key(f.x);
+        key[i + 1] = order_key(f.y);
+        key[i + 2] = order_key(f.z);
+        key[i + 3] = order_key(f.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) key[i] = (base + i < p.t_cap) ? order_key(row[base + i]) : 0u;
+    }
+  } else {
+    const uint32_t c1 = (static_cast<uint32_t>(l) << 16) | static_cast<uint32_t>(h);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int j = base + i;
+      uint32_t k = 0u;
+      if (j >= e_lo && j < e_hi) {
+        const uint32_t c0 = p.pos ? static_cast<uint32_t>(p.pos[slot0 + j]) : static_cast<uint32_t>(j);
+        k = philox_word0(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
+      }
+      key[i] = k;
+    }
+  }
+
+  // ---- 2./3. threshold: thr = n_sel-th largest candidate key; take `need` of the keys == thr
+  // mode: 0 = select none, 1 = select all candidates, 2 = threshold rule
+  int mode;
+  uint32_t thr = 0u, need = 0u;
+  if (n_sel == 0 || n_cand <= 0) {
+    mode = 0;
+  } else if (n_sel >= n_cand) {
+    mode = 1;
+  } else {
+    mode = 2;
+    uint32_t kor = 0u, kand = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int j = base + i;
+      if (j >= e_lo && j < e_hi) {
+        kor |= key[i];
+        kand &= key[i];
+      }
+    }
+    block_or_and<NT>(kor, kand, red);
+    const uint32_t diff = kor ^ kand;
+    uint32_t remaining = static_cast<uint32_t>(n_sel);
+    if (diff == 0u) {
+      thr = kand;  // all candidate keys equal
+    } else {
+      const int top = 31 - __clz(diff);
+      uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
+      uint32_t prefix = kand & mask;
+      for (int hi = top; hi >= 0;) {
+        const int lo = hi >= 7 ? hi - 7 : 0;
+        const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
+        for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+          const int j = base + i;
+          if (j >= e_lo && j < e_hi && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> lo) & dmask], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+          // lane L owns bins 4L..4L+3; count of keys in bins above each bin, scanning from the top
+          uint32_t c[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) c[q] = hist[4 * lane + q];
+          const uint32_t local = c[0] + c[1] + c[2] + c[3];
+          uint32_t suffix = local;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_down(suffix, off, 64);
+            if (lane + off < 64) suffix += y;
+          }
+          uint32_t cum = suffix - local;  // keys in bins owned by higher lanes
+#pragma unroll
+          for (int q = 3; q >= 0; --q) {
+            const uint32_t above = cum;
+            cum += c[q];
+            if (above < remaining && cum >= remaining) {
+              found[0] = static_cast<uint32_t>(4 * lane + q);
+              found[1] = above;
+            }
+          }
+        }
+        __syncthreads();
+        const uint32_t digit = found[0];
+        remaining -= found[1];
+        prefix |= digit << lo;
+        mask |= dmask << lo;
+        hi = lo - 1;
+        __syncthreads();  // everyone has read `found` before the next pass may overwrite it
+      }
+      thr = prefix;
+    }
+    need = remaining;
+  }
+
+  // ---- 4. ties to the lower slot, then ordered output
+  uint32_t my_eq = 0u;
+  if (mode == 2) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int j = base + i;
+      my_eq += (j >= e_lo && j < e_hi && key[i] == thr) ? 1u : 0u;
+    }
+  }
+  uint32_t eq_run = block_exclusive_scan<NT>(my_eq, scan_a);
+  unsigned long long flags = 0ull;
+  uint32_t my_kept = 0u;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int j = base + i;
+    bool k;
+    if (j >= T) {
+      k = false;
+    } else if (j < e_lo || j >= e_hi) {
+      k = true;  // prompt or recent window
+    } else if (mode == 0) {
+      k = false;
+    } else if (mode == 1) {
+      k = true;
+    } else if (key[i] > thr) {
+      k = true;
+    } else if (key[i] == thr) {
+      k = eq_run < need;
+      ++eq_run;
+    } else {
+      k = false;
+    }
+    if (k) {
+      flags |= 1ull << i;
+      ++my_kept;
+    }
+  }
+  uint32_t o = block_exclusive_scan<NT>(my_kept, scan_b);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    if ((flags >> i) & 1ull) {
+      if (static_cast<int>(o) < p.b_cap) out[o] = base + i;
+      ++o;
+    }
+  }
+  for (int r = n_kept + tid; r < p.b_cap; r += NT) out[r] = -1;
+  if (writer) p.n_kept[s] = n_kept;
+}
+
+template <int NT, int KPT>
+hipError_t launch_cfg(const SelectParams &p, bool random, dim3 grid, hipStream_t st) {
+  if (random)
+    hipLaunchKernelGGL((select_kernel<NT, KPT, true>), grid, dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((select_kernel<NT, KPT, false>), grid, dim3(NT), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelectParams &p, bool random, hipStream_t st) {
+  const long long heads = static_cast<long long>(p.L) * p.S * p.H;
+  if (heads <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(heads));
+  const int t = p.t_cap;
+  if (t <= 256 * 4) return launch_cfg<256, 4>(p, random, grid, st);
+  if (t <= 256 * 16) return launch_cfg<256, 16>(p, random, grid, st);
+  if (t <= 256 * 32) return launch_cfg<256, 32>(p, random, grid, st);
+  if (t <= 512 * 32) return launch_cfg<512, 32>(p, random, grid, st);
+  if (t <= 1024 * 32) return launch_cfg<1024, 32>(p, random, grid, st);
+  if (t <= 1024 * 64) return launch_cfg<1024, 64>(p, random, grid, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvevict

@@ -1,0 +1,202 @@
+/*
+ * kvevict.h -- C ABI of the MI355X (gfx950) KV-cache eviction hot path.
+ *
+ * Four calls make one eviction pass over a batch of (layer, sequence, KV
+ * head) caches:
+ *
+ *   tri_score        score every cached key from the query centre
+ *   kv_select_topk   keep prompt + recent window + top-scoring keys per head
+ *   kv_select_random keep prompt + recent window + uniformly random keys
+ *   kv_compact       gather the kept K/V rows (and positions) contiguously
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All array arguments are DEVICE pointers owned by the caller, except
+ *    where marked "host". The library allocates nothing, keeps no global
+ *    state, and never synchronises the stream; every call only enqueues
+ *    kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *    returns. Calls are re-entrant.
+ *  - Cache layout is head-major: element (l, s, h, j, e) of a
+ *    [n_layers, n_seq, n_kv_heads, t_cap, head_dim] tensor lives at
+ *    ((((l*n_seq + s)*n_kv_heads + h)*t_cap + j)*head_dim + e). Per-slot
+ *    arrays (positions, scores) are the same without the last axis.
+ *  - Slot j of a head holds the token at position pos[j] (or j when the
+ *    position pointer is NULL). Sequence s has seq_len[s] valid slots.
+ *  - Return value: KV_OK, or a negative kv_status for arguments rejected on
+ *    the host (nothing is launched then) or a failed launch (KV_EHIP).
+ *    Device-side data is never trusted for memory safety: lengths are
+ *    clamped to the capacities the host validated, and out-of-range kept
+ *    indices are skipped.
+ *
+ * Pages the operations follow (cited by title and section):
+ *  [TA-sum]  "TriAttention: Efficient Long Reasoning with Trigonometric KV
+ *            Compression" -- structured paper summary, section 3.4.
+ *  [TA-blog] "TriAttention: Efficient Long Reasoning with Trigonometric KV
+ *            Compression" -- blog walkthrough, scoring implementation and
+ *            inference-time steps.
+ *  [RA]      "Random Attention: Rethinking KV Cache Eviction for Efficient
+ *            Reasoning" -- sections 2, 3 and Appendices D, F.
+ */
+#ifndef KVEVICT_H
+#define KVEVICT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kv_status {
+  KV_OK = 0,
+  KV_EINVAL = -1,   /* NULL pointer, non-positive size, bad policy value, aliasing outputs */
+  KV_EDTYPE = -2,   /* unknown element type */
+  KV_ESHAPE = -3,   /* head_dim / capacity outside what the kernels support */
+  KV_EHIP = -5      /* a kernel launch failed (hipGetLastError after the launch) */
+} kv_status;
+
+typedef enum kv_dtype {
+  KV_F32 = 0,
+  KV_BF16 = 1
+} kv_dtype;
+
+/* A batch of per-(layer, sequence, KV head) caches. head_dim and dtype are
+ * read by tri_score and kv_compact only; the selectors ignore them. */
+typedef struct kv_shape {
+  int32_t n_layers;        /* >= 1, < 65536                                   */
+  int32_t n_seq;           /* >= 1                                             */
+  int32_t n_kv_heads;      /* >= 1, < 65536                                   */
+  int32_t head_dim;        /* even; bf16: multiple of 8, fp32: multiple of 4;
+                              at most 256                                       */
+  int32_t t_cap;           /* slots per head (slot stride), >= 1              */
+  int32_t dtype;           /* kv_dtype of K and V                              */
+  const int32_t *seq_len;  /* device [n_seq]: valid slots T_s; values outside
+                              [0, t_cap] are clamped into it                     */
+} kv_shape;
+
+/* Eviction policy: a budget of entries per KV head with pinned prompt and
+ * recent window. [TA-sum] 3.4 "KV Cache Pruning Procedure" (compress when
+ * the cache exceeds B, keep the top B); [RA] section 2 (a recent buffer that
+ * is never scored; top-K of the candidates, Eq. 2) and section 3 rule 1
+ * (the prompt is never evicted); [TA-blog] (prefill kept by default). */
+typedef struct kv_policy {
+  int32_t budget;              /* B >= 1: entries kept per head, counting prompt
+                                  and recent window                               */
+  int32_t recent;              /* R >= 0: latest slots always kept (clipped so
+                                  that prompt + window <= B)                      */
+  int32_t prompt_cap;          /* host upper bound on every prompt_len[s] (>= 0);
+                                  larger device values are clamped to it          */
+  const int32_t *prompt_len;   /* device [n_seq]: prompt slots P_s (slots 0..P_s-1) */
+} kv_policy;
+
+/*
+ * Per-sequence partition used by both selectors (T = seq_len[s] clamped to
+ * t_cap, P = prompt_len[s] clamped to [0, min(prompt_cap, T)]):
+ *   T <= B : nothing is compressed; kept = 0..T-1, n_kept = T.
+ *   T >  B : R' = min(R, max(0, B-P), T-P); evictable range E = [P, T-R');
+ *            n_sel = max(0, B-P-R') slots of E are selected;
+ *            kept = [0,P) u selected u [T-R', T) in ascending slot order;
+ *            n_kept = max(B, P)  (a prompt longer than B is kept whole and
+ *            nothing else is).
+ * Kept sets are written in ascending (chronological) order, [RA] Appendix F.
+ */
+
+/* Library version, (major << 16) | minor. */
+int32_t kv_version(void);
+
+/* Static string for a kv_status value. */
+const char *kv_status_string(int32_t status);
+
+/*
+ * tri_score -- importance of every cached key from the query centre.
+ *
+ * For each (l, s, h) and slot j < T_s:
+ *   scores[l,s,h,j] = (1/|D|) * sum_{delta in D}
+ *                     < RoPE(qbar[l,h], t_cur[s] + delta), RoPE(K[l,s,h,j], p_j) >
+ * with RoPE in complex form over interleaved pairs (x[2f] + i x[2f+1]
+ * rotated by omega_f * p, omega_f = rope_theta^(-2f/head_dim)) and <.,.> the
+ * real dot product: the trigonometric-series term of [TA-sum] 3.4
+ * ("TriAttention Key Importance Scoring: The Trigonometric Series Term")
+ * with the query replaced by its centre, averaged over the future offsets D
+ * ("Handling Multiple Future Positions"). No 1/sqrt(d) factor.
+ * The offset average is folded into one complex coefficient per band by
+ * angle addition ([TA-sum] 3.4, the a_f/b_f expansion), so each key is read
+ * once. Scores are fp32 (error within 1e-4 of max(|score|, head RMS)).
+ *
+ *  K        device [L,S,H,t_cap,d] of shape->dtype; pre-RoPE keys.
+ *  pos      device [L,S,H,t_cap] int32 absolute positions, or NULL (p_j = j).
+ *  qbar     device [L,H,d] fp32 query centre per (layer, KV head).
+ *  t_cur    device [S] int32 current position of each sequence.
+ *  rope_theta  RoPE base (> 0).
+ *  deltas   HOST [n_delta] int32 future offsets D, 1 <= n_delta <= 64.
+ *  scores   device [L,S,H,t_cap] fp32 output; slots j >= T_s are not written.
+ */
+kv_status tri_score(const kv_shape *shape, const void *K, const int32_t *pos,
+                    const float *qbar, const int32_t *t_cur, double rope_theta,
+                    const int32_t *deltas, int32_t n_delta, float *scores,
+                    void *stream);
+
+/*
+ * kv_select_topk -- exact per-head top-n_sel of the evictable range.
+ *
+ * Ranking is (score descending, slot ascending); NaN ranks as -inf and
+ * -0.0 equals +0.0. [TA-sum] 3.4 "Retention and eviction"; [RA] Eq. 2.
+ *
+ *  scores   device [L,S,H,t_cap] fp32 (slots j < T_s are read).
+ *  kept     device [L,S,H,b_cap] int32 output: the n_kept kept slots in
+ *           ascending order, then -1 up to b_cap.
+ *  b_cap    must be >= max(budget, prompt_cap).
+ *  n_kept   device [S] int32 output: |kept| of sequence s (same for every
+ *           layer and head).
+ * Requires t_cap <= 65536.
+ */
+kv_status kv_select_topk(const kv_shape *shape, const kv_policy *policy,
+                         const float *scores, int32_t *kept, int32_t b_cap,
+                         int32_t *n_kept, void *stream);
+
+/*
+ * kv_select_random -- Random Attention's per-head uniform eviction.
+ *
+ * Every evictable slot j gets u_j = word 0 of Philox4x32-10 (Salmon et al.,
+ * SC'11) with counter (p_j, (l << 16) | h, s, event) and key
+ * (seed & 0xffffffff, seed >> 32) -- an i.i.d. uniform drawn independently
+ * per KV head at every eviction; prompt and recent window are pinned; the
+ * n_sel largest u_j are kept (ties to the lower slot). [RA] section 3,
+ * Eq. 3 and Algorithm 1. No scores or keys are read.
+ *
+ *  pos      device [L,S,H,t_cap] int32 positions for the counter, or NULL (p_j = j).
+ *  seed     64-bit key; event: eviction counter (fresh draws per event).
+ *  kept, b_cap, n_kept as for kv_select_topk. Requires t_cap <= 65536.
+ */
+kv_status kv_select_random(const kv_shape *shape, const kv_policy *policy,
+                           const int32_t *pos, uint64_t seed, uint32_t event,
+                           int32_t *kept, int32_t b_cap, int32_t *n_kept,
+                           void *stream);
+
+/*
+ * kv_compact -- gather kept rows into a contiguous per-head layout.
+ *
+ * For r < min(n_kept[s], b_cap, out_cap):
+ *   K_out[l,s,h,r,:] = K_in[l,s,h,kept[r],:], V_out likewise (bit copies),
+ *   pos_out[l,s,h,r] = pos_in ? pos_in[l,s,h,kept[r]] : kept[r].
+ * Rows r >= n_kept, and rows whose kept index lies outside [0, t_cap), are
+ * not written. [RA] Appendix F (chronological keep-sets, gather
+ * compaction); [TA-blog] (slice K/V by the kept indices).
+ * Out-of-place only: K_out/V_out must not overlap K_in/V_in.
+ *
+ *  K_in, V_in  device [L,S,H,t_cap,d] (shape->dtype).
+ *  pos_in      device [L,S,H,t_cap] int32 or NULL.
+ *  kept        device [L,S,H,b_cap] int32 (from a selector).
+ *  n_kept      device [S] int32.
+ *  K_out, V_out device [L,S,H,out_cap,d]; pos_out device [L,S,H,out_cap] or NULL.
+ */
+kv_status kv_compact(const kv_shape *shape, const void *K_in, const void *V_in,
+                     const int32_t *pos_in, const int32_t *kept, int32_t b_cap,
+                     const int32_t *n_kept, void *K_out, void *V_out,
+                     int32_t *pos_out, int32_t out_cap, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVEVICT_H */

@@ -1,0 +1,88 @@
+"""The C-ABI library loads and exports every symbol include/kvevict.h declares (CPU only).
+
+No kernel is launched here: besides kv_version/kv_status_string, only calls
+that the host-side validation rejects before any launch are made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvevict.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from eviction_long_reasoning_amd import _lib
+    from eviction_long_reasoning_amd.build import build, LIB_PATH
+    if not os.path.exists(LIB_PATH):
+        build()
+    return _lib.load()
+
+
+def test_header_declares_the_four_calls():
+    names = _declared_functions()
+    for n in ("tri_score", "kv_select_topk", "kv_select_random", "kv_compact", "kv_version", "kv_status_string"):
+        assert n in names, names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kv_version() >> 16 == 1
+    assert lib.kv_status_string(0).decode() == "ok"
+    assert "invalid" in lib.kv_status_string(-1).decode()
+    assert lib.kv_status_string(12345).decode() == "unknown status"
+
+
+def test_host_validation_rejects_bad_arguments(lib):
+    from eviction_long_reasoning_amd import _lib as L
+    dummy = ctypes.c_void_p(0x1000)        # never dereferenced: validation fails first
+    seq = ctypes.c_void_p(0x2000)
+    arr = (ctypes.c_int32 * 1)(1)
+    # null shape
+    assert lib.tri_score(None, dummy, None, dummy, dummy, 1e4, arr, 1, dummy, None) == L.KV_EINVAL
+    # odd head_dim / bad dtype / misaligned K
+    sh = L.KvShape(1, 1, 1, 7, 16, L.KV_F32, seq)
+    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, dummy, 1e4, arr, 1, dummy, None) == L.KV_ESHAPE
+    sh = L.KvShape(1, 1, 1, 8, 16, 9, seq)
+    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, dummy, 1e4, arr, 1, dummy, None) == L.KV_EDTYPE
+    sh = L.KvShape(1, 1, 1, 8, 16, L.KV_BF16, seq)
+    assert lib.tri_score(ctypes.byref(sh), ctypes.c_void_p(0x1008), None, dummy, dummy, 1e4, arr, 1, dummy,
+                         None) == L.KV_EINVAL
+    # no offsets, non-positive theta
+    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, dummy, 1e4, arr, 0, dummy, None) == L.KV_EINVAL
+    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, dummy, -1.0, arr, 1, dummy, None) == L.KV_EINVAL
+    # selector: b_cap below budget or prompt cap, t_cap above the supported maximum, budget < 1
+    pol = L.KvPolicy(8, 2, 4, seq)
+    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 7, dummy, None) == L.KV_ESHAPE
+    pol = L.KvPolicy(8, 2, 12, seq)
+    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 8, dummy, None) == L.KV_ESHAPE
+    big = L.KvShape(1, 1, 1, 8, 65537, L.KV_BF16, seq)
+    pol = L.KvPolicy(8, 2, 4, seq)
+    assert lib.kv_select_random(ctypes.byref(big), ctypes.byref(pol), None, 1, 0, dummy, 8, dummy, None) == L.KV_ESHAPE
+    pol = L.KvPolicy(0, 2, 4, seq)
+    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 8, dummy, None) == L.KV_EINVAL
+    # compact: aliasing in/out is rejected
+    a = ctypes.c_void_p(0x100000)
+    assert lib.kv_compact(ctypes.byref(sh), a, ctypes.c_void_p(0x200000), None, dummy, 8, dummy, a,
+                          ctypes.c_void_p(0x300000), None, 8, None) == L.KV_EINVAL
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    import eviction_long_reasoning_amd as kv
+    with pytest.raises(ValueError):
+        kv.tri_score(torch.zeros(1, 1, 1, 4, 8), torch.zeros(1, 1, 8), torch.zeros(1, dtype=torch.int32),
+                     torch.zeros(1, dtype=torch.int32), 1e4, [1])

@@ -1,0 +1,260 @@
+"""GPU parity of each kernel against the oracle, at sizes the oracle finishes in seconds.
+
+All calls go through the C ABI (the torch binding only marshals pointers).
+Inputs come from the seeded generators in ``workloads``; expected values
+come from ``oracle``.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import eviction_long_reasoning_amd as kv
+import oracle
+from parity import assert_scores, keys_f64, log
+from workloads import bf16_bits, random_kept, random_scores, rng
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _to_dev_keys(Kf32: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        bits = bf16_bits(Kf32)
+        return torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(Kf32, np.float32)).to(DEV)
+
+
+def _host_keys(Kdev: torch.Tensor, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return Kdev.view(torch.int16).cpu().numpy().view(np.uint16)
+    return Kdev.cpu().numpy()
+
+
+def _i32(x) -> torch.Tensor:
+    return torch.as_tensor(np.asarray(x, np.int32), device=DEV)
+
+
+# ------------------------------------------------------------------ score ----
+SCORE_CASES = [
+    # name, dtype, d, L, S, H, T per seq, t_cap, theta, deltas, positions, t offsets
+    ("tiny-fp32-d64", "f32", 64, 1, 1, 1, [512], 512, 1e4, [2 ** i for i in range(7)], "slots", [0]),
+    ("bf16-d128-ragged", "bf16", 128, 2, 3, 2, [1, 700, 1000], 1030, 1e6, [2 ** i for i in range(17)], "slots", [0, 5, 0]),
+    ("bf16-d64-gappy", "bf16", 64, 2, 2, 3, [2176, 1500], 2176, 1e4, [2 ** i for i in range(17)], "gappy", [128, 0]),
+    ("bf16-d8", "bf16", 8, 1, 2, 2, [333, 64], 333, 1e4, [1, 2, 4], "slots", [0, 0]),
+    ("bf16-d16", "bf16", 16, 1, 1, 3, [129], 200, 1e6, [1, 8, 64], "slots", [0]),
+    ("bf16-d32", "bf16", 32, 1, 1, 1, [1000], 1000, 500.0, [0, 3], "slots", [0]),
+    ("bf16-d96-idle-lanes", "bf16", 96, 1, 2, 2, [777, 65], 800, 1e6, [2 ** i for i in range(17)], "slots", [0, 0]),
+    ("bf16-d256", "bf16", 256, 1, 1, 2, [600], 640, 1e6, [2 ** i for i in range(17)], "gappy", [10]),
+    ("fp32-d4", "f32", 4, 1, 1, 1, [70], 70, 1e4, [1, 2], "slots", [0]),
+    ("fp32-d128", "f32", 128, 1, 1, 2, [515], 515, 1e6, [2 ** i for i in range(17)], "slots", [0]),
+    ("fp32-d256", "f32", 256, 1, 1, 1, [300], 300, 1e6, [2 ** i for i in range(17)], "gappy", [0]),
+    ("empty-seq", "bf16", 128, 1, 2, 1, [0, 130], 130, 1e6, [1, 2], "slots", [0, 0]),
+    ("future-keys", "bf16", 64, 1, 1, 1, [256], 256, 1e4, [1, 4], "gappy", [-5000]),
+]
+
+
+def _score_inputs(case, seed):
+    name, dtype, d, L, S, H, Ts, t_cap, theta, D, pmode, toff = case
+    r = rng(500, seed)
+    mu = r.standard_normal((L, H, d))
+    K = (mu[:, None, :, None, :] + 0.3 * r.standard_normal((L, S, H, t_cap, d))).astype(np.float32)
+    qb = (r.standard_normal((L, H, d)) + 0.1 * r.standard_normal((L, H, d))).astype(np.float32)
+    Ts = np.array(Ts, np.int32)
+    if pmode == "slots":
+        pos = None
+        t_cur = Ts + np.array(toff, np.int32)
+    else:
+        pos = np.zeros((L, S, H, t_cap), np.int32)
+        for l in range(L):
+            for s in range(S):
+                for h in range(H):
+                    pos[l, s, h] = np.sort(r.choice(40000, size=t_cap, replace=False))
+        t_cur = np.full(S, 40000, np.int32) + np.array(toff, np.int32)
+    return K, qb, Ts, pos, t_cur
+
+
+@pytest.mark.parametrize("case", SCORE_CASES, ids=[c[0] for c in SCORE_CASES])
+def test_score_matches_oracle(case):
+    name, dtype, d, L, S, H, Ts, t_cap, theta, D, pmode, toff = case
+    log(f"[score] {name}")
+    K, qb, Ts, pos, t_cur = _score_inputs(case, zlib.crc32(name.encode()) % 1000)
+    Kd = _to_dev_keys(K, dtype)
+    Kh = keys_f64(_host_keys(Kd, dtype), dtype)
+    out = torch.full((L, S, H, t_cap), float("nan"), device=DEV)
+    kv.tri_score(Kd, torch.from_numpy(qb).to(DEV), _i32(t_cur), _i32(Ts), theta, D,
+                 pos=None if pos is None else _i32(pos), out=out)
+    got = out.cpu().numpy()
+    worst = 0.0
+    for l in range(L):
+        for s in range(S):
+            for h in range(H):
+                T = int(Ts[s])
+                p = None if pos is None else pos[l, s, h, :T]
+                ref = oracle.score_literal(Kh[l, s, h, :T], p, qb[l, h], int(t_cur[s]), theta, D)
+                worst = max(worst, assert_scores(got[l, s, h, :T], ref, f"{name} l{l} s{s} h{h}"))
+                assert np.all(np.isnan(got[l, s, h, T:])), "slots beyond T were written"
+    log(f"[score] {name}: worst scaled error {worst:.2e}")
+
+
+def test_score_deterministic():
+    case = SCORE_CASES[1]
+    K, qb, Ts, pos, t_cur = _score_inputs(case, 7)
+    Kd = _to_dev_keys(K, "bf16")
+    args = (Kd, torch.from_numpy(qb).to(DEV), _i32(t_cur), _i32(Ts), 1e6, [2 ** i for i in range(17)])
+    a = kv.tri_score(*args).cpu().numpy()
+    b = kv.tri_score(*args).cpu().numpy()
+    T = Ts[:, None]
+    mask = np.arange(a.shape[-1])[None, :] < T
+    for l in range(a.shape[0]):
+        for h in range(a.shape[2]):
+            assert np.array_equal(a[l, :, h][mask].view(np.uint32), b[l, :, h][mask].view(np.uint32))
+
+
+# ----------------------------------------------------------------- select ----
+SELECT_CASES = [
+    # name, t_cap, T per seq, P per seq, B, R, score kind
+    ("tier-1k", 1000, [1000, 999, 700, 5], [10, 0, 690, 0], 300, 16, "ties"),
+    ("tier-4k", 4096, [4096, 3000, 2049], [100, 2500, 1000], 2048, 128, "specials"),
+    ("tier-8k", 8192, [8192, 8000], [512, 0], 2048, 128, "ties"),
+    ("tier-16k", 16000, [16000, 12345], [1024, 77], 3072, 128, "normal"),
+    ("tier-32k", 32768, [32768, 32767, 20000], [1024, 512, 4096], 3072, 128, "normal"),
+    ("tier-64k", 65536, [65536, 40000], [1024, 0], 2048, 64, "ties"),
+    ("concentrated", 5000, [5000, 5000], [64, 64], 1000, 16, "concentrated"),
+    ("all-equal", 3000, [3000], [100], 500, 10, "equal"),
+    ("prompt-over-budget", 3000, [3000, 2500], [2500, 2049], 2048, 128, "normal"),
+    ("recent-clipped", 3000, [3000], [2000], 2048, 128, "normal"),
+    ("fits-budget", 3000, [2048, 100], [100, 50], 2048, 128, "normal"),
+    ("no-recent", 777, [777], [0], 100, 0, "specials"),
+]
+
+
+def _select_scores(name, kind, shape):
+    seed = zlib.crc32(name.encode()) % 10000
+    if kind == "ties":
+        return random_scores(seed, shape, ties=0.4)
+    if kind == "specials":
+        return random_scores(seed, shape, ties=0.1, specials=True)
+    if kind == "concentrated":
+        x = random_scores(seed, shape)
+        return (np.float32(1000.0) + np.float32(1e-3) * x).astype(np.float32)
+    if kind == "equal":
+        return np.full(shape, 3.25, np.float32)
+    return random_scores(seed, shape)
+
+
+@pytest.mark.parametrize("case", SELECT_CASES, ids=[c[0] for c in SELECT_CASES])
+def test_select_topk_bit_exact(case):
+    name, t_cap, Ts, Ps, B, R, kind = case
+    log(f"[select] {name}")
+    L, H = 2, 2
+    S = len(Ts)
+    sc = _select_scores(name, kind, (L, S, H, t_cap))
+    pcap = max(Ps)
+    b_cap = max(B, pcap) + 3
+    kept, nk = kv.kv_select_topk(torch.from_numpy(sc).to(DEV), _i32(Ts), _i32(Ps), B, R, pcap, b_cap=b_cap)
+    kept = kept.cpu().numpy()
+    nk = nk.cpu().numpy()
+    for s in range(S):
+        ref_n = oracle.partition(Ts[s], Ps[s], B, R).n_kept
+        assert nk[s] == ref_n
+        for l in range(L):
+            for h in range(H):
+                ref = oracle.select_topk(sc[l, s, h], Ts[s], Ps[s], B, R)
+                assert np.array_equal(kept[l, s, h, :ref_n], ref), f"{name} l{l} s{s} h{h}"
+                assert np.all(kept[l, s, h, ref_n:] == -1)
+
+
+@pytest.mark.parametrize("case", SELECT_CASES[:6] + SELECT_CASES[8:], ids=[c[0] for c in SELECT_CASES[:6] + SELECT_CASES[8:]])
+@pytest.mark.parametrize("with_pos", [False, True])
+def test_select_random_bit_exact(case, with_pos):
+    name, t_cap, Ts, Ps, B, R, _ = case
+    log(f"[random] {name} pos={with_pos}")
+    L, H = 2, 3
+    S = len(Ts)
+    seed, event = 0xDEADBEEF12345678, 77
+    pos = None
+    if with_pos:
+        r = rng(510, t_cap)
+        pos = np.sort(r.integers(0, 2 ** 31 - 1, (L, S, H, t_cap)), axis=-1).astype(np.int32)
+    pcap = max(Ps)
+    kept, nk = kv.kv_select_random((L, S, H, t_cap), _i32(Ts), _i32(Ps), B, R, pcap, seed, event,
+                                   pos=None if pos is None else _i32(pos))
+    kept = kept.cpu().numpy()
+    nk = nk.cpu().numpy()
+    for s in range(S):
+        for l in range(L):
+            for h in range(H):
+                p = None if pos is None else pos[l, s, h]
+                ref = oracle.select_random(Ts[s], Ps[s], B, R, p, seed, event, l, h, s)
+                assert nk[s] == ref.size
+                assert np.array_equal(kept[l, s, h, :ref.size], ref), f"{name} l{l} s{s} h{h}"
+                assert np.all(kept[l, s, h, ref.size:] == -1)
+
+
+def test_select_random_fresh_per_event_and_head():
+    Ts, Ps = [4000], [100]
+    a, _ = kv.kv_select_random((1, 1, 2, 4000), _i32(Ts), _i32(Ps), 1000, 32, 100, 9, 1)
+    b, _ = kv.kv_select_random((1, 1, 2, 4000), _i32(Ts), _i32(Ps), 1000, 32, 100, 9, 2)
+    a, b = a.cpu().numpy(), b.cpu().numpy()
+    assert not np.array_equal(a[0, 0, 0], b[0, 0, 0])
+    assert not np.array_equal(a[0, 0, 0], a[0, 0, 1])
+
+
+# ---------------------------------------------------------------- compact ----
+COMPACT_CASES = [
+    # name, dtype, d, L, S, H, t_cap, n_kept per seq, b_cap, out_cap, with pos_in
+    ("bf16-d128", "bf16", 128, 2, 3, 2, 3000, [2048, 3000, 1], 3000, 3000, False),
+    ("bf16-d64-pos", "bf16", 64, 2, 2, 3, 2176, [2048, 700], 2100, 2176, True),
+    ("bf16-d8", "bf16", 8, 1, 2, 1, 500, [100, 0], 128, 130, True),
+    ("bf16-d96", "bf16", 96, 1, 1, 2, 900, [333], 400, 400, False),
+    ("fp32-d64", "f32", 64, 1, 1, 1, 512, [128], 128, 128, False),
+    ("fp32-d256", "f32", 256, 1, 2, 1, 300, [300, 17], 300, 300, True),
+]
+
+
+@pytest.mark.parametrize("case", COMPACT_CASES, ids=[c[0] for c in COMPACT_CASES])
+def test_compact_bit_exact(case):
+    name, dtype, d, L, S, H, t_cap, nks, b_cap, out_cap, with_pos = case
+    log(f"[compact] {name}")
+    r = rng(520, d, t_cap)
+    Kf = r.standard_normal((L, S, H, t_cap, d)).astype(np.float32)
+    Vf = r.standard_normal((L, S, H, t_cap, d)).astype(np.float32)
+    Kd, Vd = _to_dev_keys(Kf, dtype), _to_dev_keys(Vf, dtype)
+    Kh, Vh = _host_keys(Kd, dtype), _host_keys(Vd, dtype)
+    kept = np.full((L, S, H, b_cap), -1, np.int32)
+    for l in range(L):
+        for s in range(S):
+            for h in range(H):
+                kept[l, s, h, :nks[s]] = random_kept(l * 100 + s * 10 + h, t_cap, nks[s])
+    pos = np.sort(r.integers(0, 10 ** 6, (L, S, H, t_cap)), axis=-1).astype(np.int32) if with_pos else None
+    sentinel = -7
+    Ko = torch.full((L, S, H, out_cap, d), sentinel, dtype=Kd.dtype, device=DEV)
+    Vo = torch.full_like(Ko, sentinel)
+    Po = torch.full((L, S, H, out_cap), sentinel, dtype=torch.int32, device=DEV)
+    kv.kv_compact(Kd, Vd, _i32(kept), _i32(nks), _i32([t_cap] * S), out_cap,
+                  pos=None if pos is None else _i32(pos), K_out=Ko, V_out=Vo, pos_out=Po)
+    Ko, Vo, Po = _host_keys(Ko, dtype), _host_keys(Vo, dtype), Po.cpu().numpy()
+    sent_k = _host_keys(torch.full((1,), sentinel, dtype=Kd.dtype), dtype)[0]
+    for l in range(L):
+        for s in range(S):
+            for h in range(H):
+                n = nks[s]
+                rk, rv, rp = oracle.compact(Kh[l, s, h], Vh[l, s, h], None if pos is None else pos[l, s, h],
+                                            kept[l, s, h, :n])
+                assert np.array_equal(Ko[l, s, h, :n], rk) and np.array_equal(Vo[l, s, h, :n], rv)
+                assert np.array_equal(Po[l, s, h, :n], rp)
+                assert np.all(Ko[l, s, h, n:] == sent_k) and np.all(Po[l, s, h, n:] == sentinel)
+
+
+def test_compact_skips_out_of_range_indices():
+    L, S, H, t_cap, d = 1, 1, 1, 64, 64
+    Kd = torch.arange(t_cap * d, dtype=torch.float32, device=DEV).reshape(L, S, H, t_cap, d)
+    kept = _i32(np.array([[[[0, -1, 63, 64, 1000, 5]]]], np.int32))
+    Ko = torch.full((L, S, H, 6, d), -3.0, device=DEV)
+    Po = torch.full((L, S, H, 6), -3, dtype=torch.int32, device=DEV)
+    kv.kv_compact(Kd, Kd.clone(), kept, _i32([6]), _i32([64]), 6, K_out=Ko, V_out=torch.empty_like(Ko), pos_out=Po)
+    Ko, Po = Ko.cpu().numpy(), Po.cpu().numpy()
+    assert Po[0, 0, 0].tolist() == [0, -3, 63, -3, -3, 5]
+    assert np.all(Ko[0, 0, 0, 1] == -3.0) and np.all(Ko[0, 0, 0, 2] == np.arange(63 * d, 64 * d))
