@@ -53,7 +53,8 @@ _lib = None
 
 
 def library_path() -> str:
-    return LIB_PATH
+    """The library to load: ``KVEVICT_LIB`` if set (an alternative build), else the in-tree one."""
+    return os.environ.get("KVEVICT_LIB") or LIB_PATH
 
 
 def load():
@@ -63,11 +64,12 @@ def load():
         return _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(LIB_PATH):
+            path = library_path()
+            if not os.path.exists(path):
                 raise RuntimeError(
-                    f"{LIB_PATH} is missing: build the HIP kernels first "
+                    f"{path} is missing: build the HIP kernels first "
                     "(python -m eviction_long_reasoning_amd.build or __graft_entry__.build())")
-            lib = ctypes.CDLL(LIB_PATH)
+            lib = ctypes.CDLL(path)
             for name, (res, args) in _SIGNATURES.items():
                 fn = getattr(lib, name)
                 fn.restype = res

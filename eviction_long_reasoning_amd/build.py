@@ -42,15 +42,21 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every kernel source and link ``libkvevict.so``; returns its path."""
+def build(verbose: bool = False, jobs: int = 8, out: str = LIB_PATH, defines=()) -> str:
+    """Compile every kernel source and link ``libkvevict.so`` (or ``out``); returns its path.
+
+    ``defines`` are extra ``NAME=VALUE`` preprocessor definitions (tuning knobs such as
+    KV_SCORE_BATCHES_PER_WAVE); the default build uses none.
+    """
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    bdir = BUILD_DIR if not defines else os.path.join(BUILD_DIR, "_".join(d.replace("=", "") for d in defines))
+    os.makedirs(bdir, exist_ok=True)
     srcs = sources()
+    dflags = [f"-D{d}" for d in defines]
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-        cmd = [hipcc, *COMPILE_FLAGS, "-c", src, "-o", obj]
+        obj = os.path.join(bdir, os.path.basename(src)[:-4] + ".o")
+        cmd = [hipcc, *COMPILE_FLAGS, *dflags, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -60,13 +66,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB_PATH + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

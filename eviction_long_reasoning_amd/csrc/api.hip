@@ -107,6 +107,8 @@ KV_EXPORT kv_status tri_score(const kv_shape *shape, const void *K, const int32_
     p.A[f] = make_float2(static_cast<float>(re / n_delta), static_cast<float>(im / n_delta));
     p.rev[f] = rev;
   }
+  // one head's rows are addressed with 32-bit buffer offsets
+  if (static_cast<long long>(p.t_cap) * p.d * elem_bytes(shape) + (64ll << 9) >= (1ll << 31)) return KV_ESHAPE;
   const int bpl = shape->dtype == KV_BF16 ? 4 : 2;  // bands per 16-byte lane piece
   const int pieces = (p.F + bpl - 1) / bpl;
   int lpk = 1;

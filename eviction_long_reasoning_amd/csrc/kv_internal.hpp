@@ -25,8 +25,11 @@ struct ScoreParams {
 };
 
 // Keys handled by one score workgroup (all lane layouts): 4 waves x 2 batches x 64 keys.
+#ifndef KV_SCORE_BATCHES_PER_WAVE
+#define KV_SCORE_BATCHES_PER_WAVE 4
+#endif
 constexpr int kScoreThreads = 256;
-constexpr int kScoreBatchesPerWave = 2;
+constexpr int kScoreBatchesPerWave = KV_SCORE_BATCHES_PER_WAVE;
 constexpr int kScoreChunk = (kScoreThreads / 64) * kScoreBatchesPerWave * 64;
 
 hipError_t launch_score(const ScoreParams &p, int dtype_bf16, int lanes_per_key, hipStream_t st);

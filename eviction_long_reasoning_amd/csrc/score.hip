@@ -22,10 +22,10 @@
 //    per lane).
 //  * The phase exp(i omega_f m) is not evaluated per key. For contiguous
 //    positions each lane rotates its u_f * exp(i omega_f m) by a fixed step
-//    exp(-i omega_f KPS) from one key to its next; the value is re-derived
+//    exp(-i omega_f KPS) from one key to its next; the value is derived
 //    exactly (fp64 reduction of omega_f m / 2pi to [-1/2, 1/2] revolutions,
-//    then fp32 sincospi) at the start of every 64-key batch, so the fp32
-//    recurrence runs at most LPK steps. With explicit (gappy) positions the
+//    then fp32 sincospi) once per wave, so the fp32 recurrence runs at most
+//    kScoreBatchesPerWave * LPK steps. With explicit (gappy) positions the
 //    phase is derived exactly for every key.
 //  * The LPK per-lane partial sums of a batch are combined by a shuffle
 //    reduce-scatter (LPK-1 exchanges per lane for LPK keys), after which each
@@ -51,6 +51,9 @@ __device__ __forceinline__ float2 cis_rev(double rev, double m) {
 
 // Sum of acc[k] over the N lanes of a group (lanes differing in the low log2(N) bits);
 // lane g of the group returns the sum for k = g.
+// The two candidates are passed through an empty asm so that the per-lane choice stays a
+// register select: left as array reads, the compiler turns the choice into a dynamically
+// indexed private array (a compare/select chain over all N elements).
 template <int N>
 __device__ __forceinline__ float reduce_scatter(float (&acc)[N], int g) {
 #pragma unroll
@@ -58,15 +61,44 @@ __device__ __forceinline__ float reduce_scatter(float (&acc)[N], int g) {
     const bool upper = (g & h) != 0;
 #pragma unroll
     for (int i = 0; i < h; ++i) {
-      const float send = upper ? acc[i] : acc[i + h];
-      const float keep = upper ? acc[i + h] : acc[i];
+      float lo = acc[i], hi = acc[i + h];
+      asm volatile("" : "+v"(lo), "+v"(hi));
+      const float send = upper ? lo : hi;
+      const float keep = upper ? hi : lo;
       acc[i] = keep + __shfl_xor(send, h, 64);
     }
   }
   return acc[0];
 }
 
-template <bool BF16, int LPK, bool POS>
+// 16-byte raw buffer load (global memory through a buffer resource): the per-step offset
+// can ride in a scalar register, so a full batch issues its loads with no vector address math.
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ float lane_dot(const uint4 &d, const float2 *v, bool bf16) {
+  const uint32_t wd[4] = {d.x, d.y, d.z, d.w};
+  float a = 0.f;
+  if (bf16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a = fmaf(v[i].x, __uint_as_float(wd[i] << 16), a);
+      a = fmaf(v[i].y, __uint_as_float(wd[i] & 0xffff0000u), a);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      a = fmaf(v[i].x, __uint_as_float(wd[2 * i]), a);
+      a = fmaf(v[i].y, __uint_as_float(wd[2 * i + 1]), a);
+    }
+  }
+  return a;
+}
+
+// FULL: every lane of a key group holds bands (head_dim fills the LPK lanes exactly).
+template <bool BF16, int LPK, bool POS, bool FULL>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(const ScoreParams p) {
   constexpr int BPL = BF16 ? 4 : 2;            // bands per lane (16 bytes)
   constexpr int KPS = 64 / LPK;                // keys per wave step
@@ -89,7 +121,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const ScoreParams 
   if (wave_first >= T) return;
   const double tq = static_cast<double>(p.t_cur[s]);
 
-  const bool live = g * BPL < p.F;
+  const bool live = FULL || g * BPL < p.F;
   float2 u[BPL], w[BPL];
   double rev[BPL];
   const float2 *qrow = reinterpret_cast<const float2 *>(p.qbar + (static_cast<size_t>(l) * p.H + h) * p.d);
@@ -108,32 +140,50 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const ScoreParams 
   }
 
   const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
-  const size_t row_bytes = static_cast<size_t>(p.d) * EB;
-  const char *Kh = static_cast<const char *>(p.K) + slot0 * row_bytes + static_cast<size_t>(g) * 16;
+  const int row_bytes = p.d * EB;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(static_cast<const char *>(p.K) + slot0 * static_cast<size_t>(row_bytes)), 0,
+      T * row_bytes, 0x00020000);
+  const int lane_off = kk * row_bytes + (live ? g * 16 : 0);
+  const int step_bytes = KPS * row_bytes;
 
+  // Contiguous positions: the lane's keys advance by KPS slots per step and by exactly 64
+  // (= LPK * KPS) per batch, so one exactly derived phase per wave seeds a recurrence of
+  // kScoreBatchesPerWave * LPK steps.
+  float2 v[BPL];
+  if (!POS) {
+    const double m0 = tq - static_cast<double>(wave_first + kk);
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) v[i] = cmul(u[i], cis_rev(rev[i], m0));
+  }
 #pragma unroll 1
   for (int nb = 0; nb < kScoreBatchesPerWave; ++nb) {
     const int j0 = wave_first + nb * 64;
     if (j0 >= T) break;
-    float2 v[BPL];
-    if (!POS) {
-      const double m0 = tq - static_cast<double>(j0 + kk);
-#pragma unroll
-      for (int i = 0; i < BPL; ++i) v[i] = cmul(u[i], cis_rev(rev[i], m0));
-    }
+    const bool full = j0 + 64 <= T;             // uniform across the wave
+    const int boff = j0 * row_bytes + lane_off;
     float acc[STEPS];
 #pragma unroll
     for (int st0 = 0; st0 < STEPS; st0 += SUB) {
       uint4 data[SUB];
       int32_t pj[SUB];
+      if (full) {
 #pragma unroll
-      for (int t = 0; t < SUB; ++t) {
-        const int j = j0 + (st0 + t) * KPS + kk;
-        const bool in = j < T;
-        const int jc = in ? j : 0;  // masked lanes keep an in-range address
-        data[t] = (live && in) ? *reinterpret_cast<const uint4 *>(Kh + static_cast<size_t>(jc) * row_bytes)
-                               : make_uint4(0u, 0u, 0u, 0u);
-        if (POS) pj[t] = in ? p.pos[slot0 + jc] : 0;
+        for (int t = 0; t < SUB; ++t) data[t] = ld16(rk, boff, (st0 + t) * step_bytes);
+      } else {
+        // ragged tail: slots at or past T read an in-range row; their sums feed unstored scores
+#pragma unroll
+        for (int t = 0; t < SUB; ++t) {
+          const bool in = j0 + (st0 + t) * KPS + kk < T;
+          data[t] = ld16(rk, in ? boff + (st0 + t) * step_bytes : lane_off - kk * row_bytes, 0);
+        }
+      }
+      if (POS) {
+#pragma unroll
+        for (int t = 0; t < SUB; ++t) {
+          const int j = min(j0 + (st0 + t) * KPS + kk, T - 1);
+          pj[t] = p.pos[slot0 + j];
+        }
       }
 #pragma unroll
       for (int t = 0; t < SUB; ++t) {
@@ -142,24 +192,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const ScoreParams 
 #pragma unroll
           for (int i = 0; i < BPL; ++i) v[i] = cmul(u[i], cis_rev(rev[i], m));
         }
-        const uint32_t wd[4] = {data[t].x, data[t].y, data[t].z, data[t].w};
-        float a = 0.f;
-        if (BF16) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float re = __uint_as_float(wd[i] << 16);
-            const float im = __uint_as_float(wd[i] & 0xffff0000u);
-            a = fmaf(v[i].x, re, a);
-            a = fmaf(v[i].y, im, a);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            a = fmaf(v[i].x, __uint_as_float(wd[2 * i]), a);
-            a = fmaf(v[i].y, __uint_as_float(wd[2 * i + 1]), a);
-          }
-        }
-        acc[st0 + t] = a;
+        const float a = lane_dot(data[t], v, BF16);
+        acc[st0 + t] = FULL ? a : (live ? a : 0.f);
         if (!POS) {
 #pragma unroll
           for (int i = 0; i < BPL; ++i) v[i] = cmul(v[i], w[i]);
@@ -172,20 +206,27 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const ScoreParams 
   }
 }
 
-template <bool BF16, bool POS>
+template <bool BF16, bool POS, bool FULL>
 hipError_t launch_lpk(const ScoreParams &p, int lpk, dim3 grid, hipStream_t st) {
   const dim3 blk(kScoreThreads);
   switch (lpk) {
-    case 1: hipLaunchKernelGGL((score_kernel<BF16, 1, POS>), grid, blk, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((score_kernel<BF16, 2, POS>), grid, blk, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((score_kernel<BF16, 4, POS>), grid, blk, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((score_kernel<BF16, 8, POS>), grid, blk, 0, st, p); break;
-    case 16: hipLaunchKernelGGL((score_kernel<BF16, 16, POS>), grid, blk, 0, st, p); break;
-    case 32: hipLaunchKernelGGL((score_kernel<BF16, 32, POS>), grid, blk, 0, st, p); break;
-    case 64: hipLaunchKernelGGL((score_kernel<BF16, 64, POS>), grid, blk, 0, st, p); break;
+    case 1: hipLaunchKernelGGL((score_kernel<BF16, 1, POS, FULL>), grid, blk, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((score_kernel<BF16, 2, POS, FULL>), grid, blk, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((score_kernel<BF16, 4, POS, FULL>), grid, blk, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((score_kernel<BF16, 8, POS, FULL>), grid, blk, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((score_kernel<BF16, 16, POS, FULL>), grid, blk, 0, st, p); break;
+    case 32: hipLaunchKernelGGL((score_kernel<BF16, 32, POS, FULL>), grid, blk, 0, st, p); break;
+    case 64: hipLaunchKernelGGL((score_kernel<BF16, 64, POS, FULL>), grid, blk, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <bool BF16, bool POS>
+hipError_t launch_full(const ScoreParams &p, int lpk, dim3 grid, hipStream_t st) {
+  const int bpl = BF16 ? 4 : 2;
+  return (lpk * bpl == p.F) ? launch_lpk<BF16, POS, true>(p, lpk, grid, st)
+                            : launch_lpk<BF16, POS, false>(p, lpk, grid, st);
 }
 
 }  // namespace
@@ -195,10 +236,10 @@ hipError_t launch_score(const ScoreParams &p, int dtype_bf16, int lanes_per_key,
   if (blocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(blocks));
   const bool pos = p.pos != nullptr;
-  if (dtype_bf16) return pos ? launch_lpk<true, true>(p, lanes_per_key, grid, st)
-                             : launch_lpk<true, false>(p, lanes_per_key, grid, st);
-  return pos ? launch_lpk<false, true>(p, lanes_per_key, grid, st)
-             : launch_lpk<false, false>(p, lanes_per_key, grid, st);
+  if (dtype_bf16) return pos ? launch_full<true, true>(p, lanes_per_key, grid, st)
+                             : launch_full<true, false>(p, lanes_per_key, grid, st);
+  return pos ? launch_full<false, true>(p, lanes_per_key, grid, st)
+             : launch_full<false, false>(p, lanes_per_key, grid, st);
 }
 
 }  // namespace kvevict

@@ -130,6 +130,7 @@ const char *kv_status_string(int32_t status);
  *  rope_theta  RoPE base (> 0).
  *  deltas   HOST [n_delta] int32 future offsets D, 1 <= n_delta <= 64.
  *  scores   device [L,S,H,t_cap] fp32 output; slots j >= T_s are not written.
+ * One head's rows must span less than 2 GiB (t_cap * head_dim * elem < 2^31 - 2^15).
  */
 kv_status tri_score(const kv_shape *shape, const void *K, const int32_t *pos,
                     const float *qbar, const int32_t *t_cur, double rope_theta,

@@ -1,0 +1,322 @@
+"""End-to-end GPU parity on the five synthetic workloads (full sizes, launch configuration of bench.py).
+
+Per pass: tri_score -> kv_select_topk -> kv_compact (scored) and
+kv_select_random -> kv_compact (random), all through the C ABI.
+
+* Scores: every checked head against the literal fp64 oracle under the 1e-4 rule.
+* Kept sets (scored): equal size; differences only at near-threshold slots.
+* Kept sets (random): bit-exact.
+* Compaction: bit-exact -- against the oracle's gather when the kept sets agree,
+  and always as the property K_out[r] == K_in[kept[r]] on every head.
+Heads the oracle cannot cover one by one at full size are sampled; every head
+is checked for the structural properties (size, order, range, pins, gather).
+"""
+import numpy as np
+import pytest
+import torch
+
+import eviction_long_reasoning_amd as kv
+import oracle
+from parity import assert_scores, assert_selection_near_threshold, keys_f64, log
+from workloads import (centres, kv_numpy, kv_torch, periodic_prompt_torch, periodic_tokens_torch,
+                       workload)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def i32(a):
+    return torch.as_tensor(np.asarray(a, np.int32), device=DEV)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy()
+
+
+def dev_from_host(a: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def check_structure(w, kept, nk, Ks, Ko, pos_out, T, P, label, pos_in=None):
+    """Properties on every head: size, strict ascent, range, pinned slots, exact gather."""
+    L, S, H = kept.shape[:3]
+    nk_h = nk.cpu().numpy()
+    for s in range(S):
+        part = oracle.partition(int(T[s]), int(P[s]), w.budget, w.recent)
+        assert nk_h[s] == part.n_kept, f"{label}: n_kept seq {s}"
+    n = torch.as_tensor(nk_h.astype(np.int64), device=DEV)[None, :, None, None]
+    r = torch.arange(kept.shape[-1], device=DEV)[None, None, None, :]
+    valid = r < n
+    kk = kept.long()
+    assert torch.all(torch.where(valid, kk >= 0, kk == -1)), f"{label}: padding / negative index"
+    Tt = torch.as_tensor(np.asarray(T, np.int64), device=DEV)[None, :, None, None]
+    assert torch.all(torch.where(valid, kk < Tt, True)), f"{label}: index >= T"
+    inc = (kk[..., 1:] > kk[..., :-1]) | ~valid[..., 1:]
+    assert torch.all(inc), f"{label}: kept not strictly ascending"
+    # pins: the prompt and the clipped recent window are present
+    for s in range(S):
+        part = oracle.partition(int(T[s]), int(P[s]), w.budget, w.recent)
+        if not part.compress:
+            continue
+        head = kk[:, s, :, :part.n_kept]
+        if part.P:
+            assert torch.all(head[..., :part.P] == torch.arange(part.P, device=DEV)), f"{label}: prompt seq {s}"
+        if part.R:
+            assert torch.all(head[..., part.n_kept - part.R:] ==
+                             torch.arange(int(T[s]) - part.R, int(T[s]), device=DEV)), f"{label}: recent seq {s}"
+    # exact gather, every head (bit comparison on the device)
+    idx = torch.where(valid, kk, 0)
+    m = min(kept.shape[-1], Ko.shape[3])
+    src = torch.take_along_dim(Ks.view(torch.int16) if Ks.dtype == torch.bfloat16 else Ks.view(torch.int32),
+                               idx[..., :m, None], dim=3)
+    dst = (Ko.view(torch.int16) if Ko.dtype == torch.bfloat16 else Ko.view(torch.int32))[:, :, :, :m]
+    ok = (src == dst).all(dim=-1) | ~valid[..., :m]
+    assert torch.all(ok), f"{label}: compacted rows differ from K_in[kept]"
+    if pos_out is not None:
+        want = idx[..., :m].to(torch.int32) if pos_in is None else torch.take_along_dim(pos_in, idx[..., :m], 3)
+        assert torch.all((pos_out[..., :m] == want) | ~valid[..., :m]), f"{label}: positions"
+
+
+def compare_head(w, Kh, Vh, qb, l, s, h, T, P, t, gpu_scores, gpu_kept, Ko, Vo, Po, label, pos=None):
+    """Oracle comparison of one head: scores, near-threshold kept rule, gather."""
+    kf = keys_f64(Kh[:T], w.dtype)
+    ref = oracle.score_literal(kf, None if pos is None else pos[:T], qb[l, h], t, w.theta, w.deltas)
+    err = assert_scores(gpu_scores[:T], ref, f"{label} l{l} s{s} h{h}")
+    rk = oracle.select_topk(ref, T, P, w.budget, w.recent)
+    nd = assert_selection_near_threshold(gpu_kept, rk, ref, T, P, w.budget, w.recent, f"{label} l{l} s{s} h{h}")
+    if nd == 0:
+        rK, rV, rP = oracle.compact(Kh, Vh, pos, rk)
+        assert np.array_equal(Ko[:rk.size], rK) and np.array_equal(Vo[:rk.size], rV)
+        assert np.array_equal(Po[:rk.size], rP)
+    return err, nd
+
+
+# --------------------------------------------------------------------------------------------
+def test_workload1_tiny_full():
+    w = workload(1)
+    K, V, _, qb = kv_numpy(w)
+    Kd, Vd = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
+    sc = kv.tri_score(Kd, torch.from_numpy(qb).to(DEV), i32(w.t_cur), i32(w.seq_len), w.theta, w.deltas)
+    kept, nk = kv.kv_select_topk(sc, i32(w.seq_len), i32(w.prompt_len), w.budget, w.recent, w.prompt_cap())
+    Ko, Vo, Po = kv.kv_compact(Kd, Vd, kept, nk, i32(w.seq_len), w.out_cap)
+    n = int(nk[0])
+    err, nd = compare_head(w, K[0, 0, 0], V[0, 0, 0], qb, 0, 0, 0, 512, 64, 512, sc[0, 0, 0].cpu().numpy(),
+                           kept[0, 0, 0, :n].cpu().numpy(), Ko[0, 0, 0].cpu().numpy(), Vo[0, 0, 0].cpu().numpy(),
+                           Po[0, 0, 0].cpu().numpy(), "tiny")
+    log(f"[w1] worst scaled score error {err:.2e}, kept differences {nd}")
+
+
+def test_workload2_full():
+    w = workload(2)
+    K, V, _, qb = kv_numpy(w)
+    Kd, Vd = dev_from_host(K, w.dtype), dev_from_host(V, w.dtype)
+    T, P = w.seq_len, w.prompt_len
+    sc = kv.tri_score(Kd, torch.from_numpy(qb).to(DEV), i32(w.t_cur), i32(T), w.theta, w.deltas)
+    kept, nk = kv.kv_select_topk(sc, i32(T), i32(P), w.budget, w.recent, w.prompt_cap())
+    Ko, Vo, Po = kv.kv_compact(Kd, Vd, kept, nk, i32(T), w.out_cap)
+    check_structure(w, kept, nk, Kd, Ko, Po, T, P, "w2")
+    sch, kh, Koh, Voh, Poh = sc.cpu().numpy(), kept.cpu().numpy(), host_bits(Ko), host_bits(Vo), Po.cpu().numpy()
+    worst, diffs = 0.0, 0
+    for h in range(w.n_kv_heads):
+        e, nd = compare_head(w, K[0, 0, h], V[0, 0, h], qb, 0, 0, h, int(T[0]), int(P[0]), int(w.t_cur[0]),
+                             sch[0, 0, h], kh[0, 0, h, :int(nk[0])], Koh[0, 0, h], Voh[0, 0, h], Poh[0, 0, h], "w2")
+        worst, diffs = max(worst, e), diffs + nd
+    log(f"[w2] 8 heads: worst scaled score error {worst:.2e}, kept differences {diffs}")
+    # random selector, bit-exact on every head
+    kr, nkr = kv.kv_select_random((1, 1, 8, w.t_cap), i32(T), i32(P), w.budget, w.recent, w.prompt_cap(), 2, 0)
+    kr = kr.cpu().numpy()
+    for h in range(8):
+        ref = oracle.select_random(int(T[0]), int(P[0]), w.budget, w.recent, None, 2, 0, 0, h, 0)
+        assert np.array_equal(kr[0, 0, h, :ref.size], ref)
+
+
+# --------------------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def full_pass():
+    w = workload(3)
+    log("[w3] generating the 36x8x8x32768x128 bf16 cache on the device")
+    mu, qb, _ = centres(w)
+    K, V = kv_torch(w, DEV, mu)
+    torch.cuda.synchronize()
+    yield w, K, V, qb
+    del K, V
+    torch.cuda.empty_cache()
+
+
+SAMPLED_HEADS = [(0, 0, 0), (0, 7, 7), (17, 3, 4), (35, 7, 7), (35, 0, 3), (9, 5, 1)]
+
+
+def test_workload3_full_pass_scored(full_pass):
+    w, K, V, qb = full_pass
+    T, P = w.seq_len, w.prompt_len
+    seq, plen = i32(T), i32(P)
+    sc = kv.tri_score(K, torch.from_numpy(qb).to(DEV), i32(w.t_cur), seq, w.theta, w.deltas)
+    kept, nk = kv.kv_select_topk(sc, seq, plen, w.budget, w.recent, w.prompt_cap())
+    Ko, Vo, Po = kv.kv_compact(K, V, kept, nk, seq, w.out_cap)
+    torch.cuda.synchronize()
+    log("[w3] scored pass done; structural checks on all 2304 heads")
+    check_structure(w, kept, nk, K, Ko, Po, T, P, "w3")
+    check_structure(w, kept, nk, V, Vo, None, T, P, "w3-V")
+    # determinism: a second pass is bit-identical
+    sc2 = kv.tri_score(K, torch.from_numpy(qb).to(DEV), i32(w.t_cur), seq, w.theta, w.deltas)
+    kept2, _ = kv.kv_select_topk(sc2, seq, plen, w.budget, w.recent, w.prompt_cap())
+    assert torch.equal(sc.view(torch.int32), sc2.view(torch.int32)) and torch.equal(kept, kept2)
+    worst, diffs = 0.0, 0
+    for (l, s, h) in SAMPLED_HEADS:
+        e, nd = compare_head(w, host_bits(K[l, s, h]), host_bits(V[l, s, h]), qb, l, s, h, int(T[s]), int(P[s]),
+                             int(w.t_cur[s]), sc[l, s, h].cpu().numpy(), kept[l, s, h, :int(nk[s])].cpu().numpy(),
+                             host_bits(Ko[l, s, h]), host_bits(Vo[l, s, h]), Po[l, s, h].cpu().numpy(), "w3")
+        worst, diffs = max(worst, e), diffs + nd
+        log(f"[w3] head {(l, s, h)}: scaled error {e:.2e}, kept differences {nd}")
+    log(f"[w3] sampled heads: worst scaled score error {worst:.2e}, kept differences {diffs}")
+
+
+def test_workload3_full_pass_random(full_pass):
+    w, K, V, qb = full_pass
+    T, P = w.seq_len, w.prompt_len
+    seed, event = 0x5EED000000000003, 11
+    kept, nk = kv.kv_select_random((w.n_layers, w.n_seq, w.n_kv_heads, w.t_cap), i32(T), i32(P), w.budget,
+                                   w.recent, w.prompt_cap(), seed, event)
+    Ko, Vo, Po = kv.kv_compact(K, V, kept, nk, i32(T), w.out_cap)
+    check_structure(w, kept, nk, K, Ko, Po, T, P, "w3-random")
+    kh = kept.cpu().numpy()
+    for (l, s, h) in SAMPLED_HEADS + [(1, 1, 1), (20, 6, 2)]:
+        ref = oracle.select_random(int(T[s]), int(P[s]), w.budget, w.recent, None, seed, event, l, h, s)
+        assert np.array_equal(kh[l, s, h, :ref.size], ref), (l, s, h)
+    log("[w3] random pass: sampled heads bit-exact, all heads structurally valid")
+
+
+# --------------------------------------------------------------------------------------------
+def test_workload5_ragged_scored_vs_random():
+    w = workload(5)
+    T, P = w.seq_len, w.prompt_len
+    log(f"[w5] 128 ragged sequences, sum T = {int(T.sum())}, {int((P > w.budget).sum())} prompts over budget")
+    mu, qb, _ = centres(w)
+    K, V = kv_torch(w, DEV, mu)
+    seq, plen = i32(T), i32(P)
+    sc = kv.tri_score(K, torch.from_numpy(qb).to(DEV), i32(w.t_cur), seq, w.theta, w.deltas)
+    ks, nks = kv.kv_select_topk(sc, seq, plen, w.budget, w.recent, w.prompt_cap())
+    Ko, Vo, Po = kv.kv_compact(K, V, ks, nks, seq, w.out_cap)
+    check_structure(w, ks, nks, K, Ko, Po, T, P, "w5-scored")
+    worst, diffs = 0.0, 0
+    rng_s = np.random.default_rng(5)
+    seqs = sorted(set([int(np.argmin(T)), int(np.argmax(T)), int(np.argmax(P)), int(np.argmin(P))] +
+                      rng_s.choice(w.n_seq, 4, replace=False).tolist()))
+    for s in seqs:
+        for h in (0, 5):
+            e, nd = compare_head(w, host_bits(K[0, s, h]), host_bits(V[0, s, h]), qb, 0, s, h, int(T[s]), int(P[s]),
+                                 int(w.t_cur[s]), sc[0, s, h].cpu().numpy(), ks[0, s, h, :int(nks[s])].cpu().numpy(),
+                                 host_bits(Ko[0, s, h]), host_bits(Vo[0, s, h]), Po[0, s, h].cpu().numpy(), "w5")
+            worst, diffs = max(worst, e), diffs + nd
+    log(f"[w5] scored: sampled {len(seqs)} seqs x 2 heads, worst scaled error {worst:.2e}, kept diffs {diffs}")
+    kr, nkr = kv.kv_select_random((1, w.n_seq, w.n_kv_heads, w.t_cap), seq, plen, w.budget, w.recent,
+                                  w.prompt_cap(), w.seed_random, 0)
+    Kro, Vro, Pro = kv.kv_compact(K, V, kr, nkr, seq, w.out_cap)
+    check_structure(w, kr, nkr, K, Kro, Pro, T, P, "w5-random")
+    krh, ksh = kr.cpu().numpy(), ks.cpu().numpy()
+    jac = []
+    for s in range(w.n_seq):
+        for h in range(w.n_kv_heads):
+            ref = oracle.select_random(int(T[s]), int(P[s]), w.budget, w.recent, None, w.seed_random, 0, 0, h, s)
+            assert np.array_equal(krh[0, s, h, :ref.size], ref), (s, h)
+            a, b = set(ksh[0, s, h, :ref.size].tolist()), set(ref.tolist())
+            jac.append(len(a & b) / max(1, len(a | b)))
+    log(f"[w5] random: all 1024 heads bit-exact; mean Jaccard(scored, random) = {np.mean(jac):.3f}")
+
+
+# --------------------------------------------------------------------------------------------
+class _OracleHead:
+    """The oracle's own trajectory of one (layer, seq, head) through the periodic workload."""
+
+    def __init__(self, K0, V0, P):
+        self.K, self.V = K0[:P].copy(), V0[:P].copy()
+        self.pos = np.arange(P, dtype=np.int32)
+
+    def append(self, Kn, Vn, pn):
+        self.K = np.concatenate([self.K, Kn])
+        self.V = np.concatenate([self.V, Vn])
+        self.pos = np.concatenate([self.pos, pn.astype(np.int32)])
+
+
+@pytest.mark.parametrize("mode", ["scored", "random"])
+def test_workload4_periodic_events(mode):
+    w = workload(4)
+    L, S, H, Tc, d = w.n_layers, w.n_seq, w.n_kv_heads, w.t_cap, w.head_dim
+    P = w.prompt_len.astype(np.int64)
+    mu0, qb, dr = centres(w)
+    K0, V0 = periodic_prompt_torch(w, mu0, dr, DEV)
+    bufs = [(K0, V0, torch.arange(Tc, dtype=torch.int32, device=DEV).expand(L, S, H, Tc).contiguous()),
+            (torch.empty_like(K0), torch.empty_like(V0), torch.empty((L, S, H, Tc), dtype=torch.int32, device=DEV))]
+    cur = 0
+    T = P.copy()
+    sampled = [(0, int(np.argmin(P)), 0), (23, int(np.argmax(P)), 7), (11, 5, 3), (5, 40, 6)]
+    ora = {k: _OracleHead(host_bits(K0[k]), host_bits(V0[k]), int(P[k[1]])) for k in sampled}
+    diverged = set()
+    qbd = torch.from_numpy(qb).to(DEV)
+    worst, compared, near = 0.0, 0, 0
+    for ev in range(1, w.n_events + 1):
+        Kc, Vc, Pc = bufs[cur]
+        Kn, Vn, pn = periodic_tokens_torch(w, ev, (P + w.new_per_event * (ev - 1)).astype(np.int32), mu0, dr, DEV)
+        for s in range(S):
+            t0 = int(T[s])
+            Kc[:, s, :, t0:t0 + w.new_per_event] = Kn[:, s]
+            Vc[:, s, :, t0:t0 + w.new_per_event] = Vn[:, s]
+            Pc[:, s, :, t0:t0 + w.new_per_event] = pn[s][None, None, :]
+        T = T + w.new_per_event
+        t_cur = (P + w.new_per_event * ev).astype(np.int32)
+        for k in sampled:
+            l, s, h = k
+            ora[k].append(host_bits(Kn[l, s, h]), host_bits(Vn[l, s, h]), pn[s].cpu().numpy())
+        seq = i32(T)
+        if mode == "scored":
+            sc = kv.tri_score(Kc, qbd, i32(t_cur), seq, w.theta, w.deltas, pos=Pc)
+            kept, nk = kv.kv_select_topk(sc, seq, i32(P), w.budget, w.recent, w.prompt_cap())
+        else:
+            kept, nk = kv.kv_select_random((L, S, H, Tc), seq, i32(P), w.budget, w.recent, w.prompt_cap(),
+                                           w.seed_random, ev, pos=Pc)
+        Ko, Vo, Po = bufs[1 - cur]
+        kv.kv_compact(Kc, Vc, kept, nk, seq, Tc, pos=Pc, K_out=Ko, V_out=Vo, pos_out=Po)
+        if ev in (1, 2, 64, 256) or ev % 32 == 0:
+            check_structure(w, kept, nk, Kc, Ko, Po, T, P, f"w4-{mode} ev{ev}", pos_in=Pc)
+        nk_h = nk.cpu().numpy()
+        for k in sampled:
+            l, s, h = k
+            o = ora[k]
+            Tn = int(T[s])
+            if mode == "random":
+                rk = oracle.select_random(Tn, int(P[s]), w.budget, w.recent, o.pos, w.seed_random, ev, l, h, s)
+                gk = kept[l, s, h, :int(nk_h[s])].cpu().numpy()
+                assert np.array_equal(gk, rk), (ev, k)
+            else:
+                if k in diverged:
+                    rk = oracle.select_topk(np.zeros(Tn), Tn, int(P[s]), w.budget, w.recent)  # keeps sizes only
+                else:
+                    ref = oracle.score_literal(keys_f64(o.K, w.dtype), o.pos, qb[l, h], int(t_cur[s]), w.theta,
+                                               w.deltas)
+                    worst = max(worst, assert_scores(sc[l, s, h, :Tn].cpu().numpy(), ref, f"w4 ev{ev} {k}"))
+                    rk = oracle.select_topk(ref, Tn, int(P[s]), w.budget, w.recent)
+                    gk = kept[l, s, h, :int(nk_h[s])].cpu().numpy()
+                    nd = assert_selection_near_threshold(gk, rk, ref, Tn, int(P[s]), w.budget, w.recent,
+                                                         f"w4 ev{ev} {k}")
+                    compared += 1
+                    if nd:
+                        near += nd
+                        diverged.add(k)   # the trajectories legitimately part here
+            if k in diverged and mode == "scored":
+                continue
+            rK, rV, rP = oracle.compact(o.K, o.V, o.pos, rk)
+            n = rk.size
+            assert np.array_equal(host_bits(Ko[l, s, h, :n]), rK) and np.array_equal(host_bits(Vo[l, s, h, :n]), rV)
+            assert np.array_equal(Po[l, s, h, :n].cpu().numpy(), rP), (ev, k)
+            o.K, o.V, o.pos = rK, rV, rP
+        T = nk_h.astype(np.int64)
+        cur = 1 - cur
+        if ev % 32 == 0:
+            log(f"[w4-{mode}] event {ev}/{w.n_events}: cache {int(T.min())}..{int(T.max())} per head")
+    if mode == "scored":
+        log(f"[w4-scored] {compared} head-events compared, worst scaled error {worst:.2e}, "
+            f"near-threshold swaps {near}, diverged heads {len(diverged)}")
