@@ -20,6 +20,17 @@ namespace {
 constexpr int kCompactThreads = 256;
 constexpr int kUnroll = 4;
 
+// Every row is moved exactly once, so loads and stores use the non-temporal cache policy.
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
+  const v4u32 v = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st_stream(uint4 *p, const uint4 &x) {
+  const v4u32 v = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<v4u32 *>(p));
+}
+
 template <int G>
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(const CompactParams p) {
   constexpr int ROWS_PER_PASS = kCompactThreads / G;
@@ -48,8 +59,8 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(const CompactP
     src[u] = j;
     const bool ld = j >= 0 && lane_live;
     const size_t off = (in_row0 + static_cast<size_t>(ld ? j : 0)) * p.row16 + (ld ? c : 0);
-    kv[u] = ld ? p.K_in[off] : make_uint4(0u, 0u, 0u, 0u);
-    vv[u] = ld ? p.V_in[off] : make_uint4(0u, 0u, 0u, 0u);
+    kv[u] = ld ? ld_stream(p.K_in + off) : make_uint4(0u, 0u, 0u, 0u);
+    vv[u] = ld ? ld_stream(p.V_in + off) : make_uint4(0u, 0u, 0u, 0u);
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
@@ -57,8 +68,8 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(const CompactP
     const int j = src[u];
     if (j >= 0 && lane_live) {
       const size_t off = (out_row0 + static_cast<size_t>(r)) * p.row16 + c;
-      p.K_out[off] = kv[u];
-      p.V_out[off] = vv[u];
+      st_stream(p.K_out + off, kv[u]);
+      st_stream(p.V_out + off, vv[u]);
     }
     if (j >= 0 && c == 0 && p.pos_out) p.pos_out[out_row0 + r] = p.pos_in ? p.pos_in[in_row0 + j] : j;
   }

@@ -26,7 +26,7 @@ struct ScoreParams {
 
 // Keys handled by one score workgroup (all lane layouts): 4 waves x 2 batches x 64 keys.
 #ifndef KV_SCORE_BATCHES_PER_WAVE
-#define KV_SCORE_BATCHES_PER_WAVE 4
+#define KV_SCORE_BATCHES_PER_WAVE 2
 #endif
 constexpr int kScoreThreads = 256;
 constexpr int kScoreBatchesPerWave = KV_SCORE_BATCHES_PER_WAVE;

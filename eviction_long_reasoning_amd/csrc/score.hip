@@ -33,6 +33,10 @@
 //    coalesced 256-byte store.
 #include "kv_internal.hpp"
 
+#ifndef KV_SCORE_PIPELINE
+#define KV_SCORE_PIPELINE 1
+#endif
+
 namespace kvevict {
 namespace {
 
@@ -73,10 +77,17 @@ __device__ __forceinline__ float reduce_scatter(float (&acc)[N], int g) {
 
 // 16-byte raw buffer load (global memory through a buffer resource): the per-step offset
 // can ride in a scalar register, so a full batch issues its loads with no vector address math.
+// Keys are read exactly once, so the loads carry the non-temporal (streaming) cache policy.
+constexpr int kStreamingLoad = 2;  // cache-policy bit "nt"
 __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamingLoad);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+
+// Scores are written once and read back by the selector from HBM (far more than fits in
+// cache), so the stores carry the non-temporal policy: mixed into the key stream, plain
+// stores cost the read stream far more bandwidth than their own 4 bytes per key.
+__device__ __forceinline__ void st_score(float *p, float x) { __builtin_nontemporal_store(x, p); }
 
 __device__ __forceinline__ float lane_dot(const uint4 &d, const float2 *v, bool bf16) {
   const uint32_t wd[4] = {d.x, d.y, d.z, d.w};
@@ -202,13 +213,121 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const ScoreParams 
     }
     const float sc = reduce_scatter<STEPS>(acc, g);
     const int jj = j0 + g * KPS + kk;
-    if (jj < T) p.scores[slot0 + jj] = sc;
+    if (jj < T) st_score(p.scores + slot0 + jj, sc);
+  }
+}
+
+// Contiguous positions, LPK <= 16: a software-pipelined stream. The wave issues batch 0's
+// loads before its phase set-up, and the loads of batch n+1 before the arithmetic of batch n
+// (two register buffers), so each wave keeps a batch of 16-byte loads in flight while it
+// computes.
+template <bool BF16, int LPK, bool FULL>
+__global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const ScoreParams p) {
+  static_assert(LPK <= 16, "pipelined variant holds two batches of LPK loads per lane");
+  constexpr int BPL = BF16 ? 4 : 2;
+  constexpr int KPS = 64 / LPK;
+  constexpr int STEPS = LPK;
+  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int NB = kScoreBatchesPerWave;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane % LPK;
+  const int kk = lane / LPK;
+  const int head = blockIdx.x / p.chunks_per_head;
+  const int chunk = blockIdx.x - head * p.chunks_per_head;
+  const int h = head % p.H;
+  const int s = (head / p.H) % p.S;
+  const int l = head / (p.H * p.S);
+
+  const int T = min(max(p.seq_len[s], 0), p.t_cap);
+  const int wave_first = chunk * kScoreChunk + wave * (NB * 64);
+  if (wave_first >= T) return;
+  const int nbat = min(NB, (T - wave_first + 63) / 64);
+
+  const bool live = FULL || g * BPL < p.F;
+  const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
+  const int row_bytes = p.d * EB;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(static_cast<const char *>(p.K) + slot0 * static_cast<size_t>(row_bytes)), 0,
+      T * row_bytes, 0x00020000);
+  const int piece = live ? g * 16 : 0;
+  const int lane_off = kk * row_bytes + piece;
+  const int step_bytes = KPS * row_bytes;
+
+  auto issue = [&](int nb, uint4(&d)[STEPS]) {
+    const int j0 = wave_first + nb * 64;
+    const int boff = j0 * row_bytes + lane_off;
+    if (j0 + 64 <= T) {
+#pragma unroll
+      for (int t = 0; t < STEPS; ++t) d[t] = ld16(rk, boff, t * step_bytes);
+    } else {
+      // ragged tail: slots at or past T read an in-range row; their sums feed unstored scores
+#pragma unroll
+      for (int t = 0; t < STEPS; ++t) {
+        const bool in = j0 + t * KPS + kk < T;
+        d[t] = ld16(rk, in ? boff + t * step_bytes : piece, 0);
+      }
+    }
+  };
+  uint4 da[STEPS], db[STEPS];
+  issue(0, da);
+
+  const double tq = static_cast<double>(p.t_cur[s]);
+  float2 v[BPL], w[BPL];
+  const float2 *qrow = reinterpret_cast<const float2 *>(p.qbar + (static_cast<size_t>(l) * p.H + h) * p.d);
+  const double m0 = tq - static_cast<double>(wave_first + kk);
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int b = g * BPL + i;
+    if (live) {
+      const double rev = p.rev[b];
+      w[i] = cis_rev(rev, -static_cast<double>(KPS));
+      v[i] = cmul(cmul(qrow[b], p.A[b]), cis_rev(rev, m0));
+    } else {
+      w[i] = make_float2(1.f, 0.f);
+      v[i] = make_float2(0.f, 0.f);
+    }
+  }
+
+  auto consume = [&](int nb, const uint4(&d)[STEPS]) {
+    float acc[STEPS];
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      const float a = lane_dot(d[t], v, BF16);
+      acc[t] = FULL ? a : (live ? a : 0.f);
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) v[i] = cmul(v[i], w[i]);
+    }
+    const float sc = reduce_scatter<STEPS>(acc, g);
+    const int jj = wave_first + nb * 64 + g * KPS + kk;
+    if (jj < T) st_score(p.scores + slot0 + jj, sc);
+  };
+
+#pragma unroll
+  for (int nb = 0; nb < NB; nb += 2) {
+    if (nb >= nbat) break;
+    if (nb + 1 < nbat) issue(nb + 1, db);
+    consume(nb, da);
+    if (nb + 1 >= nbat) break;
+    if (nb + 2 < nbat) issue(nb + 2, da);
+    consume(nb + 1, db);
   }
 }
 
 template <bool BF16, bool POS, bool FULL>
 hipError_t launch_lpk(const ScoreParams &p, int lpk, dim3 grid, hipStream_t st) {
   const dim3 blk(kScoreThreads);
+  if (!POS && KV_SCORE_PIPELINE) {
+    switch (lpk) {
+      case 1: hipLaunchKernelGGL((score_stream_kernel<BF16, 1, FULL>), grid, blk, 0, st, p); return hipGetLastError();
+      case 2: hipLaunchKernelGGL((score_stream_kernel<BF16, 2, FULL>), grid, blk, 0, st, p); return hipGetLastError();
+      case 4: hipLaunchKernelGGL((score_stream_kernel<BF16, 4, FULL>), grid, blk, 0, st, p); return hipGetLastError();
+      case 8: hipLaunchKernelGGL((score_stream_kernel<BF16, 8, FULL>), grid, blk, 0, st, p); return hipGetLastError();
+      case 16: hipLaunchKernelGGL((score_stream_kernel<BF16, 16, FULL>), grid, blk, 0, st, p); return hipGetLastError();
+      default: break;
+    }
+  }
   switch (lpk) {
     case 1: hipLaunchKernelGGL((score_kernel<BF16, 1, POS, FULL>), grid, blk, 0, st, p); break;
     case 2: hipLaunchKernelGGL((score_kernel<BF16, 2, POS, FULL>), grid, blk, 0, st, p); break;

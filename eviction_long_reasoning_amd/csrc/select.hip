@@ -10,19 +10,26 @@
 // Appendix F: keep-sets sorted chronologically).
 //
 // One workgroup owns one (layer, seq, KV head). Its T slot keys live in
-// registers in a blocked layout (thread t holds slots t*KPT .. t*KPT+KPT-1),
-// so the whole selection reads the head's scores from HBM once:
+// registers; thread t holds, for each round i, the four consecutive slots
+// 4*(i*NT + t) .. +3, so every round is one fully coalesced 16-byte-per-lane
+// load and the head's scores are read from HBM exactly once:
 //  1. Keys: fp32 scores mapped to order-preserving uint32 (NaN -> -inf,
 //     -0 -> +0) or, for the random selector, word 0 of Philox4x32-10.
 //  2. The bits shared by every candidate key are found with an OR/AND block
 //     reduction; radix passes start at the highest differing bit, which keeps
 //     the LDS histogram from collapsing into one bin for concentrated scores.
 //  3. 8-bit radix passes over a 256-bin LDS histogram locate the n_sel-th
-//     largest key thr and how many keys equal to thr must be taken.
-//  4. Two block prefix sums in slot order resolve ties to the lower slot and
-//     place every kept slot at its output index, so the kept list comes out
-//     in ascending order without a sort.
+//     largest key thr and how many keys equal to thr must be taken (need).
+//  4. One ordered scan in slot order counts, before each slot, the slots kept
+//     unconditionally (pinned, or above thr) and the slots equal to thr. A
+//     kept slot's output index is then (unconditional before) +
+//     min(equal before, need): ties go to the lower slot and the kept list is
+//     written in ascending order without a sort.
 #include "kv_internal.hpp"
+
+#ifndef KV_SELECT_WIDE
+#define KV_SELECT_WIDE 0
+#endif
 
 namespace kvevict {
 namespace {
@@ -60,32 +67,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *lds /* NT/64 + 1 */) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) lds[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t t = lane < NW ? lds[lane] : 0u;
-    uint32_t incl = t;
-#pragma unroll
-    for (int off = 1; off < NW; off <<= 1) {
-      const uint32_t y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
-    if (lane < NW) lds[lane] = incl - t;
-  }
-  __syncthreads();
-  return x - v + lds[wave];
-}
-
-template <int NT>
 __device__ __forceinline__ void block_or_and(uint32_t &o, uint32_t &a, uint32_t *lds /* 2*NT/64 */) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -108,13 +89,30 @@ __device__ __forceinline__ void block_or_and(uint32_t &o, uint32_t &a, uint32_t 
   }
 }
 
+// In-place exclusive scan of n values held in LDS, run by one wave (n may exceed 64).
+__device__ __forceinline__ void wave_exclusive_scan_lds(uint32_t *a, int n, int lane) {
+  uint32_t carry = 0u;
+  for (int c = 0; c < n; c += 64) {
+    const uint32_t v = (c + lane < n) ? a[c + lane] : 0u;
+    uint32_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (c + lane < n) a[c + lane] = carry + x - v;
+    carry += __shfl(x, 63, 64);
+  }
+}
+
 template <int NT, int KPT, bool RANDOM>
 __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   constexpr int NW = NT / 64;
+  constexpr int R = KPT / 4;   // rounds of four consecutive slots per thread
   __shared__ uint32_t hist[256];
   __shared__ uint32_t red[2 * NW];
-  __shared__ uint32_t scan_a[NW + 1];
-  __shared__ uint32_t scan_b[NW + 1];
+  __shared__ uint32_t tot_a[R * NW];   // per (round, wave): slots kept unconditionally
+  __shared__ uint32_t tot_e[R * NW];   // per (round, wave): slots whose key equals thr
   __shared__ uint32_t found[2];
 
   const int tid = threadIdx.x;
@@ -141,30 +139,31 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   const int n_kept = max(B, P);
   const int n_cand = e_hi - e_lo;
 
-  // ---- 1. keys, blocked layout
-  const int base = tid * KPT;
+  // ---- 1. keys: key[4*i + q] belongs to slot 4*(i*NT + tid) + q
   uint32_t key[KPT];
   const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
   if (!RANDOM) {
     const float *row = p.scores + slot0;
-    if (base + KPT <= p.t_cap && ((reinterpret_cast<uintptr_t>(row + base) & 15u) == 0)) {
+    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
 #pragma unroll
-      for (int i = 0; i < KPT; i += 4) {
-        const float4 f = *reinterpret_cast<const float4 *>(row + base + i);
-        key[i] = order_key(f.x);
-        key[i + 1] = order_key(f.y);
-        key[i + 2] = order_key(f.z);
-        key[i + 3] = order_key(f.w);
+    for (int i = 0; i < R; ++i) {
+      const int j4 = 4 * (i * NT + tid);
+      if (vec && j4 + 4 <= T) {
+        const float4 f = *reinterpret_cast<const float4 *>(row + j4);
+        key[4 * i] = order_key(f.x);
+        key[4 * i + 1] = order_key(f.y);
+        key[4 * i + 2] = order_key(f.z);
+        key[4 * i + 3] = order_key(f.w);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) key[4 * i + q] = (j4 + q < T) ? order_key(row[j4 + q]) : 0u;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) key[i] = (base + i < p.t_cap) ? order_key(row[base + i]) : 0u;
     }
   } else {
     const uint32_t c1 = (static_cast<uint32_t>(l) << 16) | static_cast<uint32_t>(h);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int j = base + i;
+      const int j = 4 * ((i >> 2) * NT + tid) + (i & 3);
       uint32_t k = 0u;
       if (j >= e_lo && j < e_hi) {
         const uint32_t c0 = p.pos ? static_cast<uint32_t>(p.pos[slot0 + j]) : static_cast<uint32_t>(j);
@@ -172,6 +171,13 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
       }
       key[i] = k;
     }
+  }
+  auto slot_of = [&](int i) { return 4 * ((i >> 2) * NT + tid) + (i & 3); };
+  uint64_t cand = 0ull;  // bit i: key[i] is an evictable candidate
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int j = slot_of(i);
+    cand |= static_cast<uint64_t>(j >= e_lo && j < e_hi) << i;
   }
 
   // ---- 2./3. threshold: thr = n_sel-th largest candidate key; take `need` of the keys == thr
@@ -187,8 +193,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
     uint32_t kor = 0u, kand = 0xFFFFFFFFu;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int j = base + i;
-      if (j >= e_lo && j < e_hi) {
+      if ((cand >> i) & 1ull) {
         kor |= key[i];
         kand &= key[i];
       }
@@ -209,8 +214,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-          const int j = base + i;
-          if (j >= e_lo && j < e_hi && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> lo) & dmask], 1u);
+          if (((cand >> i) & 1ull) && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> lo) & dmask], 1u);
         }
         __syncthreads();
         if (wave == 0) {
@@ -249,49 +253,58 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
     need = remaining;
   }
 
-  // ---- 4. ties to the lower slot, then ordered output
-  uint32_t my_eq = 0u;
-  if (mode == 2) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int j = base + i;
-      my_eq += (j >= e_lo && j < e_hi && key[i] == thr) ? 1u : 0u;
-    }
-  }
-  uint32_t eq_run = block_exclusive_scan<NT>(my_eq, scan_a);
-  unsigned long long flags = 0ull;
-  uint32_t my_kept = 0u;
+  // ---- 4. one ordered scan: unconditional (A) and equal-to-thr (E) slots before each slot
+  uint64_t fa = 0ull, fe = 0ull;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    const int j = base + i;
-    bool k;
-    if (j >= T) {
-      k = false;
-    } else if (j < e_lo || j >= e_hi) {
-      k = true;  // prompt or recent window
-    } else if (mode == 0) {
-      k = false;
-    } else if (mode == 1) {
-      k = true;
-    } else if (key[i] > thr) {
-      k = true;
-    } else if (key[i] == thr) {
-      k = eq_run < need;
-      ++eq_run;
-    } else {
-      k = false;
-    }
-    if (k) {
-      flags |= 1ull << i;
-      ++my_kept;
-    }
+    const bool c = (cand >> i) & 1ull;
+    const bool pinned = !c && slot_of(i) < T;  // prompt or recent window
+    const bool a = pinned || (c && (mode == 1 || (mode == 2 && key[i] > thr)));
+    const bool e = c && mode == 2 && key[i] == thr;
+    fa |= static_cast<uint64_t>(a) << i;
+    fe |= static_cast<uint64_t>(e) << i;
   }
-  uint32_t o = block_exclusive_scan<NT>(my_kept, scan_b);
+  // per round: the two counts packed as (A | E << 16); a wave's sums stay below 2^9 per half
+  uint32_t ex[R];
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    if ((flags >> i) & 1ull) {
-      if (static_cast<int>(o) < p.b_cap) out[o] = base + i;
-      ++o;
+  for (int i = 0; i < R; ++i) {
+    const uint32_t c = static_cast<uint32_t>(__popcll((fa >> (4 * i)) & 0xFull)) |
+                       (static_cast<uint32_t>(__popcll((fe >> (4 * i)) & 0xFull)) << 16);
+    uint32_t x = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) {
+      tot_a[i * NW + wave] = x & 0xFFFFu;
+      tot_e[i * NW + wave] = x >> 16;
+    }
+    ex[i] = x - c;
+  }
+  __syncthreads();
+  if (wave == 0) wave_exclusive_scan_lds(tot_a, R * NW, lane);
+  if (wave == (NW > 1 ? 1 : 0)) wave_exclusive_scan_lds(tot_e, R * NW, lane);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    uint32_t na = tot_a[i * NW + wave] + (ex[i] & 0xFFFFu);
+    uint32_t ne = tot_e[i * NW + wave] + (ex[i] >> 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int bit = 4 * i + q;
+      const int j = slot_of(bit);
+      if ((fa >> bit) & 1ull) {
+        const uint32_t o = na + min(ne, need);
+        if (static_cast<int>(o) < p.b_cap) out[o] = j;
+        ++na;
+      } else if ((fe >> bit) & 1ull) {
+        if (ne < need) {
+          const uint32_t o = na + ne;
+          if (static_cast<int>(o) < p.b_cap) out[o] = j;
+        }
+        ++ne;
+      }
     }
   }
   for (int r = n_kept + tid; r < p.b_cap; r += NT) out[r] = -1;
@@ -318,7 +331,11 @@ hipError_t launch_select(const SelectParams &p, bool random, hipStream_t st) {
   if (t <= 256 * 16) return launch_cfg<256, 16>(p, random, grid, st);
   if (t <= 256 * 32) return launch_cfg<256, 32>(p, random, grid, st);
   if (t <= 512 * 32) return launch_cfg<512, 32>(p, random, grid, st);
+#if KV_SELECT_WIDE
+  if (t <= 512 * 64) return launch_cfg<512, 64>(p, random, grid, st);
+#else
   if (t <= 1024 * 32) return launch_cfg<1024, 32>(p, random, grid, st);
+#endif
   if (t <= 1024 * 64) return launch_cfg<1024, 64>(p, random, grid, st);
   return hipErrorInvalidValue;
 }
