@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=36, help="layers of the full-pass workload (36 = full size)")
-    ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the oracle's CPU sample (0 = skip)")
+    ap.add_argument("--cpu-heads", type=int, default=256, help="heads in the oracle's CPU sample (0 = skip)")
     ap.add_argument("--no-random", action="store_true", help="skip the random-eviction pass")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run one elementwise copy of known size then exit after one pass (for HBM counter runs)")

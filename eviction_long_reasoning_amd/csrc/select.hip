@@ -89,23 +89,38 @@ __device__ __forceinline__ void block_or_and(uint32_t &o, uint32_t &a, uint32_t 
   }
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave with DPP lane moves (no LDS): row
+// shifts by 1, 2, 4, 8 scan each row of 16 lanes (bound_ctrl feeds 0 past the row start),
+// then the last lane of row 0 is broadcast into row 1 and row 2's into row 3, and the last
+// lane of rows 0-1 into rows 2-3. Lanes a move does not write keep the 0 passed as `old`.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x111, 0xf, 0xf, true));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x112, 0xf, 0xf, true));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x114, 0xf, 0xf, true));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x118, 0xf, 0xf, true));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x142, 0xa, 0xf, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x143, 0xc, 0xf, false));
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_total(uint32_t incl) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+}
+
 // In-place exclusive scan of n values held in LDS, run by one wave (n may exceed 64).
 __device__ __forceinline__ void wave_exclusive_scan_lds(uint32_t *a, int n, int lane) {
   uint32_t carry = 0u;
   for (int c = 0; c < n; c += 64) {
     const uint32_t v = (c + lane < n) ? a[c + lane] : 0u;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_inclusive_sum(v);
     if (c + lane < n) a[c + lane] = carry + x - v;
-    carry += __shfl(x, 63, 64);
+    carry += wave_total(x);
   }
 }
 
-template <int NT, int KPT, bool RANDOM>
+// VEC (top-k only): every head's score row is 16-byte aligned and t_cap is a multiple of 4, so
+// each round is one float4 load per lane (slots past T are loaded but never used).
+template <int NT, int KPT, bool RANDOM, bool VEC>
 __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   constexpr int NW = NT / 64;
   constexpr int R = KPT / 4;   // rounds of four consecutive slots per thread
@@ -144,12 +159,12 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
   if (!RANDOM) {
     const float *row = p.scores + slot0;
-    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int j4 = 4 * (i * NT + tid);
-      if (vec && j4 + 4 <= T) {
-        const float4 f = *reinterpret_cast<const float4 *>(row + j4);
+      if (VEC) {
+        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j4 < p.t_cap) f = *reinterpret_cast<const float4 *>(row + j4);
         key[4 * i] = order_key(f.x);
         key[4 * i + 1] = order_key(f.y);
         key[4 * i + 2] = order_key(f.z);
@@ -223,13 +238,8 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) c[q] = hist[4 * lane + q];
           const uint32_t local = c[0] + c[1] + c[2] + c[3];
-          uint32_t suffix = local;
-#pragma unroll
-          for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_down(suffix, off, 64);
-            if (lane + off < 64) suffix += y;
-          }
-          uint32_t cum = suffix - local;  // keys in bins owned by higher lanes
+          const uint32_t incl = wave_inclusive_sum(local);
+          uint32_t cum = wave_total(incl) - incl;  // keys in bins owned by higher lanes
 #pragma unroll
           for (int q = 3; q >= 0; --q) {
             const uint32_t above = cum;
@@ -270,12 +280,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   for (int i = 0; i < R; ++i) {
     const uint32_t c = static_cast<uint32_t>(__popcll((fa >> (4 * i)) & 0xFull)) |
                        (static_cast<uint32_t>(__popcll((fe >> (4 * i)) & 0xFull)) << 16);
-    uint32_t x = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_inclusive_sum(c);
     if (lane == 63) {
       tot_a[i * NW + wave] = x & 0xFFFFu;
       tot_e[i * NW + wave] = x >> 16;
@@ -313,10 +318,13 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
 
 template <int NT, int KPT>
 hipError_t launch_cfg(const SelectParams &p, bool random, dim3 grid, hipStream_t st) {
+  const bool vec = (p.t_cap % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.scores) & 15u) == 0);
   if (random)
-    hipLaunchKernelGGL((select_kernel<NT, KPT, true>), grid, dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((select_kernel<NT, KPT, true, false>), grid, dim3(NT), 0, st, p);
+  else if (vec)
+    hipLaunchKernelGGL((select_kernel<NT, KPT, false, true>), grid, dim3(NT), 0, st, p);
   else
-    hipLaunchKernelGGL((select_kernel<NT, KPT, false>), grid, dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((select_kernel<NT, KPT, false, false>), grid, dim3(NT), 0, st, p);
   return hipGetLastError();
 }
 
