@@ -66,6 +66,92 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave with DPP lane moves (no LDS): row
+// shifts by 1, 2, 4, 8 scan each row of 16 lanes (bound_ctrl feeds 0 past the row start),
+// then the last lane of row 0 is broadcast into row 1 and row 2's into row 3, and the last
+// lane of rows 0-1 into rows 2-3. Lanes a move does not write keep the 0 passed as `old`.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x111, 0xf, 0xf, true));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x112, 0xf, 0xf, true));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x114, 0xf, 0xf, true));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x118, 0xf, 0xf, true));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x142, 0xa, 0xf, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x143, 0xc, 0xf, false));
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_total(uint32_t incl) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+}
+
+constexpr uint32_t kKeyNegInf = 0x007FFFFFu;  // order_key(-inf)
+constexpr uint32_t kKeyPosInf = 0xFF800000u;  // order_key(+inf)
+constexpr int kValueBins = 1024;
+
+// The fp32 value an order key stands for (inverse of order_key on non-NaN values).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Monotone (non-decreasing) map of a key to one of kValueBins bins spanning [fmin, fmax];
+// -inf and +inf go to the end bins. Rounded operations that cannot be contracted keep the
+// two evaluations of a key (histogram and membership) bit-identical.
+__device__ __forceinline__ uint32_t value_bin(uint32_t k, float fmin, float scale) {
+  if (k <= kKeyNegInf) return 0u;
+  if (k >= kKeyPosInf) return kValueBins - 1u;
+  const float x = __fmul_rn(__fsub_rn(key_value(k), fmin), scale);
+  return min(static_cast<uint32_t>(x), static_cast<uint32_t>(kValueBins - 1));
+}
+
+// Run by one wave: lane L owns bins (NBINS/64)*L ...; finds the bin b holding the remaining-th
+// largest key (counting from the top) and the number of keys in bins above it.
+template <int NBINS>
+__device__ __forceinline__ void find_bin(const uint32_t *hist, uint32_t remaining, int lane, uint32_t *found) {
+  constexpr int PER = NBINS / 64;
+  uint32_t c[PER];
+  uint32_t local = 0u;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    c[q] = hist[PER * lane + q];
+    local += c[q];
+  }
+  const uint32_t incl = wave_inclusive_sum(local);
+  uint32_t cum = wave_total(incl) - incl;  // keys in bins owned by higher lanes
+#pragma unroll
+  for (int q = PER - 1; q >= 0; --q) {
+    const uint32_t above = cum;
+    cum += c[q];
+    if (above < remaining && cum >= remaining) {
+      found[0] = static_cast<uint32_t>(PER * lane + q);
+      found[1] = above;
+    }
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void block_min_max(uint32_t &mn, uint32_t &mx, uint32_t *lds /* 2*NT/64 */) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mn = min(mn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mn), off, 64)));
+    mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), off, 64)));
+  }
+  if (lane == 0) {
+    lds[wave] = mn;
+    lds[NW + wave] = mx;
+  }
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    mn = min(mn, lds[i]);
+    mx = max(mx, lds[NW + i]);
+  }
+  __syncthreads();  // lds may be reused right after
+}
+
 template <int NT>
 __device__ __forceinline__ void block_or_and(uint32_t &o, uint32_t &a, uint32_t *lds /* 2*NT/64 */) {
   constexpr int NW = NT / 64;
@@ -87,24 +173,7 @@ __device__ __forceinline__ void block_or_and(uint32_t &o, uint32_t &a, uint32_t 
     o |= lds[i];
     a &= lds[NW + i];
   }
-}
-
-// Inclusive prefix sum across the 64 lanes of a wave with DPP lane moves (no LDS): row
-// shifts by 1, 2, 4, 8 scan each row of 16 lanes (bound_ctrl feeds 0 past the row start),
-// then the last lane of row 0 is broadcast into row 1 and row 2's into row 3, and the last
-// lane of rows 0-1 into rows 2-3. Lanes a move does not write keep the 0 passed as `old`.
-__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
-  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x111, 0xf, 0xf, true));
-  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x112, 0xf, 0xf, true));
-  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x114, 0xf, 0xf, true));
-  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x118, 0xf, 0xf, true));
-  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x142, 0xa, 0xf, false));
-  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x143, 0xc, 0xf, false));
-  return x;
-}
-
-__device__ __forceinline__ uint32_t wave_total(uint32_t incl) {
-  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+  __syncthreads();  // lds may be reused right after
 }
 
 // In-place exclusive scan of n values held in LDS, run by one wave (n may exceed 64).
@@ -124,7 +193,7 @@ template <int NT, int KPT, bool RANDOM, bool VEC>
 __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   constexpr int NW = NT / 64;
   constexpr int R = KPT / 4;   // rounds of four consecutive slots per thread
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kValueBins];
   __shared__ uint32_t red[2 * NW];
   __shared__ uint32_t tot_a[R * NW];   // per (round, wave): slots kept unconditionally
   __shared__ uint32_t tot_e[R * NW];   // per (round, wave): slots whose key equals thr
@@ -205,19 +274,55 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
     mode = 1;
   } else {
     mode = 2;
+    uint32_t remaining = static_cast<uint32_t>(n_sel);
+    uint64_t mem = cand;  // keys the exact radix passes still have to order
+    if (!RANDOM) {
+      // Pass 1 (scores): 1024 bins uniform in value between the smallest and largest finite
+      // candidate. The binning is monotone, so the threshold lies in one bin and every key in a
+      // higher bin is strictly larger; the exact passes then only see that bin's keys. Binning by
+      // value keeps a concentrated score distribution from piling into a few radix bins.
+      uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        if (((cand >> i) & 1ull) && key[i] > kKeyNegInf && key[i] < kKeyPosInf) {
+          kmn = min(kmn, key[i]);
+          kmx = max(kmx, key[i]);
+        }
+      }
+      block_min_max<NT>(kmn, kmx, red);
+      const float fmin = key_value(kmn), fmax = key_value(kmx);
+      const float scale = static_cast<float>(kValueBins) / (fmax - fmin);
+      if (kmn < kmx && scale > 0.f && scale < 3.0e38f) {
+        for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+          if ((cand >> i) & 1ull) atomicAdd(&hist[value_bin(key[i], fmin, scale)], 1u);
+        __syncthreads();
+        if (wave == 0) find_bin<kValueBins>(hist, remaining, lane, found);
+        __syncthreads();
+        const uint32_t b = found[0];
+        remaining -= found[1];
+        mem = 0ull;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+          if (((cand >> i) & 1ull) && value_bin(key[i], fmin, scale) == b) mem |= 1ull << i;
+        __syncthreads();  // `found` and `hist` are reused below
+      }
+    }
+    // Exact radix passes over the member keys, from their highest differing bit.
     uint32_t kor = 0u, kand = 0xFFFFFFFFu;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      if ((cand >> i) & 1ull) {
+      if ((mem >> i) & 1ull) {
         kor |= key[i];
         kand &= key[i];
       }
     }
     block_or_and<NT>(kor, kand, red);
     const uint32_t diff = kor ^ kand;
-    uint32_t remaining = static_cast<uint32_t>(n_sel);
     if (diff == 0u) {
-      thr = kand;  // all candidate keys equal
+      thr = kand;  // all member keys equal
     } else {
       const int top = 31 - __clz(diff);
       uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
@@ -229,27 +334,10 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-          if (((cand >> i) & 1ull) && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> lo) & dmask], 1u);
+          if (((mem >> i) & 1ull) && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> lo) & dmask], 1u);
         }
         __syncthreads();
-        if (wave == 0) {
-          // lane L owns bins 4L..4L+3; count of keys in bins above each bin, scanning from the top
-          uint32_t c[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) c[q] = hist[4 * lane + q];
-          const uint32_t local = c[0] + c[1] + c[2] + c[3];
-          const uint32_t incl = wave_inclusive_sum(local);
-          uint32_t cum = wave_total(incl) - incl;  // keys in bins owned by higher lanes
-#pragma unroll
-          for (int q = 3; q >= 0; --q) {
-            const uint32_t above = cum;
-            cum += c[q];
-            if (above < remaining && cum >= remaining) {
-              found[0] = static_cast<uint32_t>(4 * lane + q);
-              found[1] = above;
-            }
-          }
-        }
+        if (wave == 0) find_bin<256>(hist, remaining, lane, found);
         __syncthreads();
         const uint32_t digit = found[0];
         remaining -= found[1];

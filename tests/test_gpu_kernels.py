@@ -127,6 +127,10 @@ SELECT_CASES = [
     ("recent-clipped", 3000, [3000], [2000], 2048, 128, "normal"),
     ("fits-budget", 3000, [2048, 100], [100, 50], 2048, 128, "normal"),
     ("no-recent", 777, [777], [0], 100, 0, "specials"),
+    ("huge-range", 4000, [4000, 3000], [10, 10], 1000, 8, "huge"),
+    ("ulp-range", 4000, [4000], [10], 1500, 8, "ulp"),
+    ("denormals", 2500, [2500], [0], 300, 4, "denormal"),
+    ("inf-mix", 6000, [6000, 5000], [32, 0], 2048, 64, "infmix"),
 ]
 
 
@@ -141,6 +145,27 @@ def _select_scores(name, kind, shape):
         return (np.float32(1000.0) + np.float32(1e-3) * x).astype(np.float32)
     if kind == "equal":
         return np.full(shape, 3.25, np.float32)
+    if kind == "huge":      # value range overflows fp32: the value-binned pass must stand aside
+        x = random_scores(seed, shape)
+        x.reshape(-1)[::7] = np.float32(3.0e38)
+        x.reshape(-1)[3::7] = np.float32(-3.0e38)
+        return x
+    if kind == "ulp":       # distinct values a few ulps apart around 1.0
+        n = int(np.prod(shape))
+        r = rng(530, seed)
+        bits = (np.float32(1.0).view(np.uint32) + r.integers(0, 4 * n, n).astype(np.uint32))
+        return bits.view(np.float32).reshape(shape)
+    if kind == "denormal":  # range narrower than any normal float
+        n = int(np.prod(shape))
+        r = rng(531, seed)
+        return r.integers(0, 0x7FFFF, n).astype(np.uint32).view(np.float32).reshape(shape)
+    if kind == "infmix":
+        x = random_scores(seed, shape, ties=0.05)
+        flat = x.reshape(-1)
+        flat[::5] = np.inf
+        flat[2::9] = -np.inf
+        flat[4::11] = np.nan
+        return x
     return random_scores(seed, shape)
 
 
