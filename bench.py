@@ -188,6 +188,20 @@ def main():
                "gbs": rbytes / (rwall * 1e-3) / 1e9, "kernel_ms": rk, "algorithmic_bytes": rbytes}
         print(f"[bench] random pass {rwall:.3f} ms, kernels {rk}", file=sys.stderr, flush=True)
 
+    # the full TriAttention score (trigonometric + norm-based term) over the same cache
+    from workloads import query_magnitudes
+    qabs = torch.from_numpy(query_magnitudes(w, qb)).to(dev)
+    for _ in range(args.warmup):
+        kv.tri_score(K, qbd, tcur, seq, w.theta, w.deltas, out=scores, qabs=qabs)
+    fev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    fev[0].record()
+    for _ in range(args.steps):
+        kv.tri_score(K, qbd, tcur, seq, w.theta, w.deltas, out=scores, qabs=qabs)
+    fev[1].record()
+    torch.cuda.synchronize(dev)
+    full_ms = fev[0].elapsed_time(fev[1]) / args.steps
+    print(f"[bench] tri_score with norm term {full_ms:.3f} ms", file=sys.stderr, flush=True)
+
     cpu = None
     if args.cpu_heads > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -222,6 +236,7 @@ def main():
                                 "kv_select_topk": ab["select"] / (k_ms["kv_select_topk"] * 1e-3) / 1e9,
                                 "kv_compact": ab["compact"] / (k_ms["kv_compact"] * 1e-3) / 1e9}},
         "random_pass": rnd,
+        "score_with_norm_term": {"ms_per_launch": full_ms, "gbs": ab["score"] / (full_ms * 1e-3) / 1e9},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

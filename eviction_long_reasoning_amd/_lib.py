@@ -41,7 +41,8 @@ _I32 = ctypes.c_int32
 _SIGNATURES = {
     "kv_version": (_I32, []),
     "kv_status_string": (ctypes.c_char_p, [_I32]),
-    "tri_score": (_I32, [ctypes.POINTER(KvShape), _P, _P, _P, _P, ctypes.c_double, ctypes.POINTER(_I32), _I32, _P, _P]),
+    "tri_score": (_I32, [ctypes.POINTER(KvShape), _P, _P, _P, _P, _P, ctypes.c_double, ctypes.POINTER(_I32), _I32,
+                         _P, _P]),
     "kv_select_topk": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, _P, _I32, _P, _P]),
     "kv_select_random": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, ctypes.c_uint64,
                                 ctypes.c_uint32, _P, _I32, _P, _P]),

@@ -50,8 +50,11 @@ def _shape(L, S, H, d, t_cap, dtype_code, seq_len_ptr) -> _lib.KvShape:
 
 def tri_score(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len: torch.Tensor,
               rope_theta: float, deltas: Sequence[int], pos: Optional[torch.Tensor] = None,
-              out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Offset-averaged RoPE query-centre score of every cached key (fp32 [L,S,H,t_cap])."""
+              out: Optional[torch.Tensor] = None, qabs: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Offset-averaged RoPE query-centre score of every cached key (fp32 [L,S,H,t_cap]).
+
+    With ``qabs`` ([L,H,d/2] fp32, mean query magnitude per band) the norm-based term is added.
+    """
     if K.dim() != 5 or K.dtype not in _DT:
         raise ValueError("K must be [L,S,H,t_cap,d] float32/bfloat16")
     L, S, H, t_cap, d = K.shape
@@ -61,13 +64,14 @@ def tri_score(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len:
     tp = _dev_ptr(t_cur, "t_cur", torch.int32, (S,), dev)
     sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
     pp = _dev_ptr(pos, "pos", torch.int32, (L, S, H, t_cap), dev)
+    ap = _dev_ptr(qabs, "qabs", torch.float32, (L, H, d // 2), dev)
     if out is None:
         out = torch.empty((L, S, H, t_cap), dtype=torch.float32, device=dev)
     op = _dev_ptr(out, "out", torch.float32, (L, S, H, t_cap), dev)
     dl = [int(x) for x in deltas]
     arr = (ctypes.c_int32 * max(1, len(dl)))(*dl)
     shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
-    st = _lib.load().tri_score(ctypes.byref(shape), kp, pp, qp, tp, float(rope_theta), arr, len(dl), op,
+    st = _lib.load().tri_score(ctypes.byref(shape), kp, pp, qp, ap, tp, float(rope_theta), arr, len(dl), op,
                                _stream(dev))
     _lib.check("tri_score", st)
     return out

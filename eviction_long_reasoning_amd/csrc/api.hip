@@ -67,8 +67,8 @@ KV_EXPORT const char *kv_status_string(int32_t status) {
 }
 
 KV_EXPORT kv_status tri_score(const kv_shape *shape, const void *K, const int32_t *pos, const float *qbar,
-                              const int32_t *t_cur, double rope_theta, const int32_t *deltas, int32_t n_delta,
-                              float *scores, void *stream) {
+                              const float *qabs, const int32_t *t_cur, double rope_theta, const int32_t *deltas,
+                              int32_t n_delta, float *scores, void *stream) {
   kv_status st = check_shape(shape, true);
   if (st != KV_OK) return st;
   if (!K || !qbar || !t_cur || !deltas || !scores) return KV_EINVAL;
@@ -80,6 +80,7 @@ KV_EXPORT kv_status tri_score(const kv_shape *shape, const void *K, const int32_
   p.K = K;
   p.pos = pos;
   p.qbar = qbar;
+  p.qabs = qabs;
   p.t_cur = t_cur;
   p.seq_len = shape->seq_len;
   p.scores = scores;

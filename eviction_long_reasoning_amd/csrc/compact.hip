@@ -18,7 +18,10 @@ namespace kvevict {
 namespace {
 
 constexpr int kCompactThreads = 256;
-constexpr int kUnroll = 4;
+#ifndef KV_COMPACT_UNROLL
+#define KV_COMPACT_UNROLL 2
+#endif
+constexpr int kUnroll = KV_COMPACT_UNROLL;
 
 // Every row is moved exactly once, so loads and stores use the non-temporal cache policy.
 typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));

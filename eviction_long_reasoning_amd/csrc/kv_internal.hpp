@@ -15,6 +15,7 @@ struct ScoreParams {
   const void *K;            // [L,S,H,t_cap,d]
   const int32_t *pos;       // [L,S,H,t_cap] or nullptr
   const float *qbar;        // [L,H,d]
+  const float *qabs;        // [L,H,d/2] or nullptr
   const int32_t *t_cur;     // [S]
   const int32_t *seq_len;   // [S]
   float *scores;            // [L,S,H,t_cap]

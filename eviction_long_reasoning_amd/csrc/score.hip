@@ -89,27 +89,32 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int voff, int so
 // stores cost the read stream far more bandwidth than their own 4 bytes per key.
 __device__ __forceinline__ void st_score(float *p, float x) { __builtin_nontemporal_store(x, p); }
 
-__device__ __forceinline__ float lane_dot(const uint4 &d, const float2 *v, bool bf16) {
+// One lane's share of a key's score: sum over its bands of Re(v_b * conj(k_b)), plus, with
+// NORM, the norm-based term cn_b * |k_b| (cn_b = (1 - R_b) E|q_b|).
+template <bool BF16, bool NORM>
+__device__ __forceinline__ float lane_dot(const uint4 &d, const float2 *v, const float *cn) {
+  constexpr int BPL = BF16 ? 4 : 2;
   const uint32_t wd[4] = {d.x, d.y, d.z, d.w};
   float a = 0.f;
-  if (bf16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a = fmaf(v[i].x, __uint_as_float(wd[i] << 16), a);
-      a = fmaf(v[i].y, __uint_as_float(wd[i] & 0xffff0000u), a);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      a = fmaf(v[i].x, __uint_as_float(wd[2 * i]), a);
-      a = fmaf(v[i].y, __uint_as_float(wd[2 * i + 1]), a);
-    }
+  for (int i = 0; i < BPL; ++i) {
+    const float re = BF16 ? __uint_as_float(wd[i] << 16) : __uint_as_float(wd[2 * i]);
+    const float im = BF16 ? __uint_as_float(wd[i] & 0xffff0000u) : __uint_as_float(wd[2 * i + 1]);
+    a = fmaf(v[i].x, re, a);
+    a = fmaf(v[i].y, im, a);
+    if (NORM) a = fmaf(cn[i], sqrtf(fmaf(re, re, im * im)), a);
   }
   return a;
 }
 
+// Norm-term weight of band b: E|q_b| - |q_bar_b| = (1 - R_b) E|q_b|, zero when E|q_b| = 0.
+__device__ __forceinline__ float norm_weight(const float *qabs, float2 q, int b) {
+  const float qa = qabs[b];
+  return qa > 0.f ? qa - sqrtf(fmaf(q.x, q.x, q.y * q.y)) : 0.f;
+}
+
 // FULL: every lane of a key group holds bands (head_dim fills the LPK lanes exactly).
-template <bool BF16, int LPK, bool POS, bool FULL>
+template <bool BF16, int LPK, bool POS, bool FULL, bool NORM>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(const ScoreParams p) {
   constexpr int BPL = BF16 ? 4 : 2;            // bands per lane (16 bytes)
   constexpr int KPS = 64 / LPK;                // keys per wave step
@@ -134,8 +139,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const ScoreParams 
 
   const bool live = FULL || g * BPL < p.F;
   float2 u[BPL], w[BPL];
+  float cn[BPL];
   double rev[BPL];
-  const float2 *qrow = reinterpret_cast<const float2 *>(p.qbar + (static_cast<size_t>(l) * p.H + h) * p.d);
+  const size_t lh = static_cast<size_t>(l) * p.H + h;
+  const float2 *qrow = reinterpret_cast<const float2 *>(p.qbar + lh * p.d);
 #pragma unroll
   for (int i = 0; i < BPL; ++i) {
     const int b = g * BPL + i;
@@ -143,10 +150,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const ScoreParams 
       u[i] = cmul(qrow[b], p.A[b]);
       rev[i] = p.rev[b];
       w[i] = cis_rev(rev[i], -static_cast<double>(KPS));
+      cn[i] = NORM ? norm_weight(p.qabs + lh * p.F, qrow[b], b) : 0.f;
     } else {
       u[i] = make_float2(0.f, 0.f);
       rev[i] = 0.0;
       w[i] = make_float2(1.f, 0.f);
+      cn[i] = 0.f;
     }
   }
 
@@ -203,7 +212,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const ScoreParams 
 #pragma unroll
           for (int i = 0; i < BPL; ++i) v[i] = cmul(u[i], cis_rev(rev[i], m));
         }
-        const float a = lane_dot(data[t], v, BF16);
+        const float a = lane_dot<BF16, NORM>(data[t], v, cn);
         acc[st0 + t] = FULL ? a : (live ? a : 0.f);
         if (!POS) {
 #pragma unroll
@@ -221,7 +230,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const ScoreParams 
 // loads before its phase set-up, and the loads of batch n+1 before the arithmetic of batch n
 // (two register buffers), so each wave keeps a batch of 16-byte loads in flight while it
 // computes.
-template <bool BF16, int LPK, bool FULL>
+template <bool BF16, int LPK, bool FULL, bool NORM>
 __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const ScoreParams p) {
   static_assert(LPK <= 16, "pipelined variant holds two batches of LPK loads per lane");
   constexpr int BPL = BF16 ? 4 : 2;
@@ -275,7 +284,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const Score
 
   const double tq = static_cast<double>(p.t_cur[s]);
   float2 v[BPL], w[BPL];
-  const float2 *qrow = reinterpret_cast<const float2 *>(p.qbar + (static_cast<size_t>(l) * p.H + h) * p.d);
+  float cn[BPL];
+  const size_t lh = static_cast<size_t>(l) * p.H + h;
+  const float2 *qrow = reinterpret_cast<const float2 *>(p.qbar + lh * p.d);
   const double m0 = tq - static_cast<double>(wave_first + kk);
 #pragma unroll
   for (int i = 0; i < BPL; ++i) {
@@ -284,9 +295,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const Score
       const double rev = p.rev[b];
       w[i] = cis_rev(rev, -static_cast<double>(KPS));
       v[i] = cmul(cmul(qrow[b], p.A[b]), cis_rev(rev, m0));
+      cn[i] = NORM ? norm_weight(p.qabs + lh * p.F, qrow[b], b) : 0.f;
     } else {
       w[i] = make_float2(1.f, 0.f);
       v[i] = make_float2(0.f, 0.f);
+      cn[i] = 0.f;
     }
   }
 
@@ -294,7 +307,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const Score
     float acc[STEPS];
 #pragma unroll
     for (int t = 0; t < STEPS; ++t) {
-      const float a = lane_dot(d[t], v, BF16);
+      const float a = lane_dot<BF16, NORM>(d[t], v, cn);
       acc[t] = FULL ? a : (live ? a : 0.f);
 #pragma unroll
       for (int i = 0; i < BPL; ++i) v[i] = cmul(v[i], w[i]);
@@ -315,27 +328,27 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const Score
   }
 }
 
-template <bool BF16, bool POS, bool FULL>
+template <bool BF16, bool POS, bool FULL, bool NORM>
 hipError_t launch_lpk(const ScoreParams &p, int lpk, dim3 grid, hipStream_t st) {
   const dim3 blk(kScoreThreads);
   if (!POS && KV_SCORE_PIPELINE) {
     switch (lpk) {
-      case 1: hipLaunchKernelGGL((score_stream_kernel<BF16, 1, FULL>), grid, blk, 0, st, p); return hipGetLastError();
-      case 2: hipLaunchKernelGGL((score_stream_kernel<BF16, 2, FULL>), grid, blk, 0, st, p); return hipGetLastError();
-      case 4: hipLaunchKernelGGL((score_stream_kernel<BF16, 4, FULL>), grid, blk, 0, st, p); return hipGetLastError();
-      case 8: hipLaunchKernelGGL((score_stream_kernel<BF16, 8, FULL>), grid, blk, 0, st, p); return hipGetLastError();
-      case 16: hipLaunchKernelGGL((score_stream_kernel<BF16, 16, FULL>), grid, blk, 0, st, p); return hipGetLastError();
+      case 1: hipLaunchKernelGGL((score_stream_kernel<BF16, 1, FULL, NORM>), grid, blk, 0, st, p); return hipGetLastError();
+      case 2: hipLaunchKernelGGL((score_stream_kernel<BF16, 2, FULL, NORM>), grid, blk, 0, st, p); return hipGetLastError();
+      case 4: hipLaunchKernelGGL((score_stream_kernel<BF16, 4, FULL, NORM>), grid, blk, 0, st, p); return hipGetLastError();
+      case 8: hipLaunchKernelGGL((score_stream_kernel<BF16, 8, FULL, NORM>), grid, blk, 0, st, p); return hipGetLastError();
+      case 16: hipLaunchKernelGGL((score_stream_kernel<BF16, 16, FULL, NORM>), grid, blk, 0, st, p); return hipGetLastError();
       default: break;
     }
   }
   switch (lpk) {
-    case 1: hipLaunchKernelGGL((score_kernel<BF16, 1, POS, FULL>), grid, blk, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((score_kernel<BF16, 2, POS, FULL>), grid, blk, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((score_kernel<BF16, 4, POS, FULL>), grid, blk, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((score_kernel<BF16, 8, POS, FULL>), grid, blk, 0, st, p); break;
-    case 16: hipLaunchKernelGGL((score_kernel<BF16, 16, POS, FULL>), grid, blk, 0, st, p); break;
-    case 32: hipLaunchKernelGGL((score_kernel<BF16, 32, POS, FULL>), grid, blk, 0, st, p); break;
-    case 64: hipLaunchKernelGGL((score_kernel<BF16, 64, POS, FULL>), grid, blk, 0, st, p); break;
+    case 1: hipLaunchKernelGGL((score_kernel<BF16, 1, POS, FULL, NORM>), grid, blk, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((score_kernel<BF16, 2, POS, FULL, NORM>), grid, blk, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((score_kernel<BF16, 4, POS, FULL, NORM>), grid, blk, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((score_kernel<BF16, 8, POS, FULL, NORM>), grid, blk, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((score_kernel<BF16, 16, POS, FULL, NORM>), grid, blk, 0, st, p); break;
+    case 32: hipLaunchKernelGGL((score_kernel<BF16, 32, POS, FULL, NORM>), grid, blk, 0, st, p); break;
+    case 64: hipLaunchKernelGGL((score_kernel<BF16, 64, POS, FULL, NORM>), grid, blk, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -344,8 +357,11 @@ hipError_t launch_lpk(const ScoreParams &p, int lpk, dim3 grid, hipStream_t st) 
 template <bool BF16, bool POS>
 hipError_t launch_full(const ScoreParams &p, int lpk, dim3 grid, hipStream_t st) {
   const int bpl = BF16 ? 4 : 2;
-  return (lpk * bpl == p.F) ? launch_lpk<BF16, POS, true>(p, lpk, grid, st)
-                            : launch_lpk<BF16, POS, false>(p, lpk, grid, st);
+  const bool full = lpk * bpl == p.F;
+  if (p.qabs) return full ? launch_lpk<BF16, POS, true, true>(p, lpk, grid, st)
+                          : launch_lpk<BF16, POS, false, true>(p, lpk, grid, st);
+  return full ? launch_lpk<BF16, POS, true, false>(p, lpk, grid, st)
+              : launch_lpk<BF16, POS, false, false>(p, lpk, grid, st);
 }
 
 }  // namespace

@@ -122,10 +122,16 @@ const char *kv_status_string(int32_t status);
  * The offset average is folded into one complex coefficient per band by
  * angle addition ([TA-sum] 3.4, the a_f/b_f expansion), so each key is read
  * once. Scores are fp32 (error within 1e-4 of max(|score|, head RMS)).
+ * With qabs given, the distance-free norm-based term of [TA-sum] 3.4 ("The
+ * Norm-Based Term", "Adaptive Weighting via Q/K Concentration") is added:
+ *   + sum_f (1 - R_f) * qabs_f * |k_f|,  R_f = |qbar_f| / qabs_f
+ * (a band with qabs_f = 0 contributes nothing).
  *
  *  K        device [L,S,H,t_cap,d] of shape->dtype; pre-RoPE keys.
  *  pos      device [L,S,H,t_cap] int32 absolute positions, or NULL (p_j = j).
  *  qbar     device [L,H,d] fp32 query centre per (layer, KV head).
+ *  qabs     device [L,H,d/2] fp32 mean query magnitude E|q_f| per band, or
+ *           NULL for the trigonometric term alone.
  *  t_cur    device [S] int32 current position of each sequence.
  *  rope_theta  RoPE base (> 0).
  *  deltas   HOST [n_delta] int32 future offsets D, 1 <= n_delta <= 64.
@@ -133,7 +139,7 @@ const char *kv_status_string(int32_t status);
  * One head's rows must span less than 2 GiB (t_cap * head_dim * elem < 2^31 - 2^15).
  */
 kv_status tri_score(const kv_shape *shape, const void *K, const int32_t *pos,
-                    const float *qbar, const int32_t *t_cur, double rope_theta,
+                    const float *qbar, const float *qabs, const int32_t *t_cur, double rope_theta,
                     const int32_t *deltas, int32_t n_delta, float *scores,
                     void *stream);
 

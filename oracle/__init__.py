@@ -11,6 +11,9 @@ from the pages' definitions:
   * ``score_series`` / ``score_folded`` -- the same number through the
     trigonometric series and through the angle-addition expansion; used as
     cross-checks of each other and of the literal form.
+  * ``norm_term`` / ``score_full`` -- the norm-based term S_norm weighted by
+    one minus the mean resultant length, and S_trig + S_norm (TriAttention
+    summary 3.4 "The Norm-Based Term", "Adaptive Weighting").
   * ``partition`` / ``select_topk`` -- prompt and recent-window pinning and
     exact top-n selection (TriAttention summary 3.4 "KV Cache Pruning
     Procedure"; Random Attention section 2 Eq. 2 and section 3 rule 1).
@@ -33,14 +36,14 @@ invariants, brute force and an independent library Philox; none is marked
 "parity unpinned".
 """
 from .rope import band_frequencies, rope_rotate
-from .score import score_literal, score_series, score_folded, fold_coefficients
+from .score import score_literal, score_series, score_folded, fold_coefficients, norm_term, score_full
 from .policy import Partition, partition, canonical_scores, select_topk, select_random, random_uniforms
 from .philox import philox4x32_10, philox4x32_10_np, PHILOX_M, PHILOX_W
 from .compact import compact
 
 __all__ = [
     "band_frequencies", "rope_rotate",
-    "score_literal", "score_series", "score_folded", "fold_coefficients",
+    "score_literal", "score_series", "score_folded", "fold_coefficients", "norm_term", "score_full",
     "Partition", "partition", "canonical_scores", "select_topk", "select_random", "random_uniforms",
     "philox4x32_10", "philox4x32_10_np", "PHILOX_M", "PHILOX_W",
     "compact",

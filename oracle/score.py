@@ -25,6 +25,14 @@ Three independent evaluations are provided:
     Re(q_centre * conj(k) * exp(i phase)) product per band.
 
 The oracle's reference value is ``score_literal``.
+
+The full TriAttention score adds the norm-based term of the same section
+("The Norm-Based Term", "Adaptive Weighting via Q/K Concentration"):
+
+    S_norm(k) = sum_f (1 - R_f) * E[|q_f|] * |k_f|,   R_f = |q_bar_f| / E[|q_f|]
+
+which does not depend on the distance, so the offset-averaged full score is
+``score_full = score_literal + norm_term``.
 """
 from __future__ import annotations
 
@@ -92,3 +100,24 @@ def score_folded(K, pos, qbar, t: int, theta: float, deltas: Sequence[int]) -> n
     age = (int(t) - pos).astype(np.float64)
     rot = np.exp(1j * omega[None, :] * age[:, None])
     return np.real(u[None, :] * np.conj(kc) * rot).sum(axis=1)
+
+
+def norm_term(K, qbar, qabs) -> np.ndarray:
+    """S_norm(k_j) = sum_f (1 - R_f) E|q_f| |k_f| with R_f = |q_bar_f| / E|q_f| (R_f := 1 where E|q_f| = 0)."""
+    K = np.asarray(K, dtype=np.float64)
+    q = np.asarray(qbar, dtype=np.float64)
+    qa = np.asarray(qabs, dtype=np.float64)
+    F = K.shape[1] // 2
+    if q.shape != (2 * F,) or qa.shape != (F,):
+        raise ValueError("shape mismatch")
+    centre = np.abs(q[0::2] + 1j * q[1::2])
+    with np.errstate(divide="ignore", invalid="ignore"):
+        R = np.where(qa > 0, centre / np.where(qa > 0, qa, 1.0), 1.0)
+    weight = (1.0 - R) * qa
+    k_abs = np.abs(K[:, 0::2] + 1j * K[:, 1::2])
+    return k_abs @ weight
+
+
+def score_full(K, pos, qbar, qabs, t: int, theta: float, deltas: Sequence[int]) -> np.ndarray:
+    """Offset-averaged S_trig plus S_norm (the full TriAttention score before GQA aggregation)."""
+    return score_literal(K, pos, qbar, t, theta, deltas) + norm_term(K, qbar, qabs)

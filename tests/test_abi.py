@@ -52,18 +52,18 @@ def test_host_validation_rejects_bad_arguments(lib):
     seq = ctypes.c_void_p(0x2000)
     arr = (ctypes.c_int32 * 1)(1)
     # null shape
-    assert lib.tri_score(None, dummy, None, dummy, dummy, 1e4, arr, 1, dummy, None) == L.KV_EINVAL
+    assert lib.tri_score(None, dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, None) == L.KV_EINVAL
     # odd head_dim / bad dtype / misaligned K
     sh = L.KvShape(1, 1, 1, 7, 16, L.KV_F32, seq)
-    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, dummy, 1e4, arr, 1, dummy, None) == L.KV_ESHAPE
+    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, None) == L.KV_ESHAPE
     sh = L.KvShape(1, 1, 1, 8, 16, 9, seq)
-    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, dummy, 1e4, arr, 1, dummy, None) == L.KV_EDTYPE
+    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, None) == L.KV_EDTYPE
     sh = L.KvShape(1, 1, 1, 8, 16, L.KV_BF16, seq)
-    assert lib.tri_score(ctypes.byref(sh), ctypes.c_void_p(0x1008), None, dummy, dummy, 1e4, arr, 1, dummy,
+    assert lib.tri_score(ctypes.byref(sh), ctypes.c_void_p(0x1008), None, dummy, None, dummy, 1e4, arr, 1, dummy,
                          None) == L.KV_EINVAL
     # no offsets, non-positive theta
-    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, dummy, 1e4, arr, 0, dummy, None) == L.KV_EINVAL
-    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, dummy, -1.0, arr, 1, dummy, None) == L.KV_EINVAL
+    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, 1e4, arr, 0, dummy, None) == L.KV_EINVAL
+    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, -1.0, arr, 1, dummy, None) == L.KV_EINVAL
     # selector: b_cap below budget or prompt cap, t_cap above the supported maximum, budget < 1
     pol = L.KvPolicy(8, 2, 4, seq)
     assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 7, dummy, None) == L.KV_ESHAPE

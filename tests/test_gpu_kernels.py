@@ -98,6 +98,35 @@ def test_score_matches_oracle(case):
     log(f"[score] {name}: worst scaled error {worst:.2e}")
 
 
+NORM_CASES = [c for c in SCORE_CASES if c[0] in ("tiny-fp32-d64", "bf16-d128-ragged", "bf16-d64-gappy",
+                                                  "bf16-d96-idle-lanes", "fp32-d128")]
+
+
+@pytest.mark.parametrize("case", NORM_CASES, ids=[c[0] for c in NORM_CASES])
+def test_score_with_norm_term_matches_oracle(case):
+    name, dtype, d, L, S, H, Ts, t_cap, theta, D, pmode, toff = case
+    log(f"[score+norm] {name}")
+    K, qb, Ts, pos, t_cur = _score_inputs(case, zlib.crc32(name.encode()) % 1000)
+    r = rng(540, d)
+    centre = np.abs(qb[..., 0::2].astype(np.float64) + 1j * qb[..., 1::2])
+    qabs = (centre / r.uniform(0.5, 1.0, centre.shape)).astype(np.float32)
+    qabs[..., 1] = 0.0                                   # a band without statistics contributes nothing
+    Kd = _to_dev_keys(K, dtype)
+    Kh = keys_f64(_host_keys(Kd, dtype), dtype)
+    out = kv.tri_score(Kd, torch.from_numpy(qb).to(DEV), _i32(t_cur), _i32(Ts), theta, D,
+                       pos=None if pos is None else _i32(pos), qabs=torch.from_numpy(qabs).to(DEV))
+    got = out.cpu().numpy()
+    worst = 0.0
+    for l in range(L):
+        for s in range(S):
+            for h in range(H):
+                T = int(Ts[s])
+                p = None if pos is None else pos[l, s, h, :T]
+                ref = oracle.score_full(Kh[l, s, h, :T], p, qb[l, h], qabs[l, h], int(t_cur[s]), theta, D)
+                worst = max(worst, assert_scores(got[l, s, h, :T], ref, f"{name} l{l} s{s} h{h}"))
+    log(f"[score+norm] {name}: worst scaled error {worst:.2e}")
+
+
 def test_score_deterministic():
     case = SCORE_CASES[1]
     K, qb, Ts, pos, t_cur = _score_inputs(case, 7)

@@ -19,7 +19,7 @@ import eviction_long_reasoning_amd as kv
 import oracle
 from parity import assert_scores, assert_selection_near_threshold, keys_f64, log
 from workloads import (centres, kv_numpy, kv_torch, periodic_prompt_torch, periodic_tokens_torch,
-                       workload)
+                       query_magnitudes, workload)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -132,6 +132,28 @@ def test_workload2_full():
     for h in range(8):
         ref = oracle.select_random(int(T[0]), int(P[0]), w.budget, w.recent, None, 2, 0, 0, h, 0)
         assert np.array_equal(kr[0, 0, h, :ref.size], ref)
+
+
+def test_workload2_full_score_with_norm_term():
+    # the full TriAttention score (S_trig + S_norm) on the Qwen3-8B-shaped layer
+    w = workload(2)
+    K, V, _, qb = kv_numpy(w)
+    qabs = query_magnitudes(w, qb)
+    Kd, Vd = dev_from_host(K, w.dtype), dev_from_host(V, w.dtype)
+    T, P = w.seq_len, w.prompt_len
+    sc = kv.tri_score(Kd, torch.from_numpy(qb).to(DEV), i32(w.t_cur), i32(T), w.theta, w.deltas,
+                      qabs=torch.from_numpy(qabs).to(DEV))
+    kept, nk = kv.kv_select_topk(sc, i32(T), i32(P), w.budget, w.recent, w.prompt_cap())
+    sch, kh = sc.cpu().numpy(), kept.cpu().numpy()
+    worst, diffs = 0.0, 0
+    for h in range(w.n_kv_heads):
+        ref = oracle.score_full(keys_f64(K[0, 0, h], w.dtype), None, qb[0, h], qabs[0, h], int(w.t_cur[0]),
+                                w.theta, w.deltas)
+        worst = max(worst, assert_scores(sch[0, 0, h], ref, f"w2+norm h{h}"))
+        rk = oracle.select_topk(ref, int(T[0]), int(P[0]), w.budget, w.recent)
+        diffs += assert_selection_near_threshold(kh[0, 0, h, :int(nk[0])], rk, ref, int(T[0]), int(P[0]),
+                                                 w.budget, w.recent, f"w2+norm h{h}")
+    log(f"[w2+norm] 8 heads: worst scaled score error {worst:.2e}, kept differences {diffs}")
 
 
 # --------------------------------------------------------------------------------------------

@@ -191,3 +191,44 @@ def test_bad_inputs_raise():
         score_literal(np.zeros((3, 5)), None, np.zeros(5), 0, 1e4, [1])
     with pytest.raises(ValueError):
         score_literal(np.zeros((3, 4)), None, np.zeros(4), 0, 1e4, [])
+
+
+# --------------------------------------------------------------------------
+# the norm-based term (TriAttention summary 3.4, "The Norm-Based Term")
+# --------------------------------------------------------------------------
+from oracle import norm_term, score_full  # noqa: E402
+
+
+def test_norm_term_hand_example():
+    # |q_bar| = 5, E|q| = 7 (R = 5/7), |k| = 2: (1 - 5/7) * 7 * 2 = 4
+    assert norm_term(np.array([[0.0, 2.0]]), [3.0, 4.0], [7.0])[0] == pytest.approx(4.0, abs=1e-14)
+    # two bands: only band 1 is dispersed; band 0 has R = 1 and contributes nothing
+    K = np.array([[3.0, 4.0, 1.0, 0.0]])
+    assert norm_term(K, [1.0, 0.0, 0.0, 2.0], [1.0, 3.0])[0] == pytest.approx((3.0 - 2.0) * 1.0, abs=1e-14)
+
+
+def test_norm_term_limits():
+    r = rng(110)
+    K, q = r.standard_normal((9, 16)), r.standard_normal(16)
+    centre = np.abs(q[0::2] + 1j * q[1::2])
+    # perfect concentration (R_f = 1): the norm term vanishes and the full score is S_trig
+    np.testing.assert_allclose(norm_term(K, q, centre), 0.0, atol=1e-14)
+    np.testing.assert_allclose(score_full(K, None, q, centre, 500, 1e4, [1, 2]),
+                               score_literal(K, None, q, 500, 1e4, [1, 2]), atol=1e-12)
+    # no directional signal (q_bar = 0, R_f = 0): the basic form sum_f E|q_f| |k_f|
+    qa = np.abs(r.standard_normal(8)) + 0.1
+    kabs = np.hypot(K[:, 0::2], K[:, 1::2])
+    np.testing.assert_allclose(norm_term(K, np.zeros(16), qa), kabs @ qa, atol=1e-12)
+    # the dispersion form stated beside it: sum_f (E|q_f| - |q_bar_f|) |k_f|
+    qa2 = centre + np.abs(r.standard_normal(8))
+    np.testing.assert_allclose(norm_term(K, q, qa2), kabs @ (qa2 - centre), atol=1e-12)
+
+
+def test_norm_term_is_distance_free_and_scales():
+    r = rng(111)
+    K, q = r.standard_normal((7, 8)), r.standard_normal(8)
+    qa = np.abs(q[0::2] + 1j * q[1::2]) * 1.3
+    a = score_full(K, np.arange(7), q, qa, 100, 1e4, [1, 4])
+    b = score_full(K, np.arange(7) + 50, q, qa, 150, 1e4, [1, 4])
+    np.testing.assert_allclose(a, b, atol=1e-10)
+    np.testing.assert_allclose(norm_term(3 * K, 2 * q, 2 * qa), 6 * norm_term(K, q, qa), atol=1e-12)

@@ -35,7 +35,7 @@ import numpy as np
 SEED_ROOT = 20261202
 
 # kinds of draws (the last SeedSequence word)
-K_MU, K_NU, K_KEYNOISE, K_QNOISE, K_VAL, K_LEN, K_DRIFT, K_NEWKEY, K_NEWVAL = range(9)
+K_MU, K_NU, K_KEYNOISE, K_QNOISE, K_VAL, K_LEN, K_DRIFT, K_NEWKEY, K_NEWVAL, K_QABS = range(10)
 
 
 def rng(*ids: int) -> np.random.Generator:
@@ -223,6 +223,19 @@ def centres(w: Workload) -> Tuple[np.ndarray, np.ndarray, Optional[np.ndarray]]:
         if dr is not None:
             dr[l] = rng(w.wid, l, K_DRIFT).standard_normal((H, d)).astype(np.float32)
     return mu, qb, dr
+
+
+def query_magnitudes(w: Workload, qbar: np.ndarray) -> np.ndarray:
+    """Mean query magnitude per band, E|q_f| = |q_bar_f| / R_f, fp32 [L,H,d/2].
+
+    The mean resultant length R_f is drawn U(0.85, 1.0) per (layer, KV head, band): most
+    heads are highly concentrated, a few bands less so.
+    """
+    L, H, F = w.n_layers, w.n_kv_heads, w.n_bands
+    q = np.asarray(qbar, np.float64)
+    centre = np.abs(q[..., 0::2] + 1j * q[..., 1::2])
+    R = np.stack([rng(w.wid, l, K_QABS).uniform(0.85, 1.0, (H, F)) for l in range(L)])
+    return (centre / R).astype(np.float32)
 
 
 def head_kv_numpy(w: Workload, l: int, s: int, mu: np.ndarray):
