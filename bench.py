@@ -202,6 +202,30 @@ def main():
     full_ms = fev[0].elapsed_time(fev[1]) / args.steps
     print(f"[bench] tri_score with norm term {full_ms:.3f} ms", file=sys.stderr, flush=True)
 
+    # keys stored after RoPE: dense, and through a block table over the same memory viewed as a
+    # paged pool [L, n_blocks, 16, H, d] with a shuffled table
+    def time_launches(fn):
+        for _ in range(args.warmup):
+            fn()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        for _ in range(args.steps):
+            fn()
+        e[1].record()
+        torch.cuda.synchronize(dev)
+        return e[0].elapsed_time(e[1]) / args.steps
+
+    rot_ms = time_launches(lambda: kv.tri_score_rotated(K, qbd, tcur, seq, w.theta, w.deltas, out=scores))
+    bs = 16
+    bps = Tc // bs
+    pool = K.view(L, S * bps, bs, H, d)
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(7)
+    table = torch.randperm(S * bps, generator=gen).view(S, bps).to(torch.int32).to(dev)
+    paged_ms = time_launches(lambda: kv.tri_score_rotated(pool, qbd, tcur, seq, w.theta, w.deltas,
+                                                          block_table=table, out=scores))
+    print(f"[bench] rotated keys: dense {rot_ms:.3f} ms, paged {paged_ms:.3f} ms", file=sys.stderr, flush=True)
+
     cpu = None
     if args.cpu_heads > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -237,6 +261,8 @@ def main():
                                 "kv_compact": ab["compact"] / (k_ms["kv_compact"] * 1e-3) / 1e9}},
         "random_pass": rnd,
         "score_with_norm_term": {"ms_per_launch": full_ms, "gbs": ab["score"] / (full_ms * 1e-3) / 1e9},
+        "score_rotated_keys": {"dense_ms": rot_ms, "dense_gbs": ab["score"] / (rot_ms * 1e-3) / 1e9,
+                               "paged16_ms": paged_ms, "paged16_gbs": ab["score"] / (paged_ms * 1e-3) / 1e9},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

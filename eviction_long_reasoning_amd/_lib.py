@@ -13,6 +13,7 @@ from .build import LIB_PATH
 
 KV_OK, KV_EINVAL, KV_EDTYPE, KV_ESHAPE, KV_EHIP = 0, -1, -2, -3, -5
 KV_F32, KV_BF16 = 0, 1
+KV_ROPE_INTERLEAVED, KV_ROPE_HALF = 0, 1
 
 
 class KvShape(ctypes.Structure):
@@ -24,6 +25,15 @@ class KvShape(ctypes.Structure):
         ("t_cap", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("seq_len", ctypes.c_void_p),
+    ]
+
+
+class KvPaged(ctypes.Structure):
+    _fields_ = [
+        ("block_table", ctypes.c_void_p),
+        ("blocks_per_seq", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("n_blocks", ctypes.c_int32),
     ]
 
 
@@ -43,6 +53,8 @@ _SIGNATURES = {
     "kv_status_string": (ctypes.c_char_p, [_I32]),
     "tri_score": (_I32, [ctypes.POINTER(KvShape), _P, _P, _P, _P, _P, ctypes.c_double, ctypes.POINTER(_I32), _I32,
                          _P, _P]),
+    "tri_score_rotated": (_I32, [ctypes.POINTER(KvShape), _P, ctypes.POINTER(KvPaged), _I32, _P, _P, _P,
+                                 ctypes.c_double, ctypes.POINTER(_I32), _I32, _P, _P]),
     "kv_select_topk": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, _P, _I32, _P, _P]),
     "kv_select_random": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, ctypes.c_uint64,
                                 ctypes.c_uint32, _P, _I32, _P, _P]),

@@ -77,6 +77,46 @@ def tri_score(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len:
     return out
 
 
+def tri_score_rotated(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len: torch.Tensor,
+                      rope_theta: float, deltas: Sequence[int], rope_style: str = "interleaved",
+                      block_table: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                      qabs: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Scores of keys stored after RoPE (fp32 [L,S,H,t_cap]).
+
+    Dense: ``K`` is [L,S,H,t_cap,d]. Paged: ``K`` is the pool [L,n_blocks,block_size,H,d] and
+    ``block_table`` is int32 [S, blocks_per_seq]; t_cap = blocks_per_seq * block_size.
+    ``rope_style`` is "interleaved" (x[2f], x[2f+1]) or "half" (x[f], x[f+d/2]).
+    """
+    if K.dim() != 5 or K.dtype not in _DT:
+        raise ValueError("K must be a 5-D float32/bfloat16 tensor")
+    style = {"interleaved": _lib.KV_ROPE_INTERLEAVED, "half": _lib.KV_ROPE_HALF}[rope_style]
+    dev = K.device
+    paged = None
+    if block_table is None:
+        L, S, H, t_cap, d = K.shape
+    else:
+        L, n_blocks, bs, H, d = K.shape
+        S, bps = block_table.shape
+        t_cap = bps * bs
+        paged = _lib.KvPaged(_dev_ptr(block_table, "block_table", torch.int32, (S, bps), dev), int(bps), int(bs),
+                             int(n_blocks))
+    kp = _dev_ptr(K, "K")
+    qp = _dev_ptr(qbar, "qbar", torch.float32, (L, H, d), dev)
+    ap = _dev_ptr(qabs, "qabs", torch.float32, (L, H, d // 2), dev)
+    tp = _dev_ptr(t_cur, "t_cur", torch.int32, (S,), dev)
+    sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
+    if out is None:
+        out = torch.empty((L, S, H, t_cap), dtype=torch.float32, device=dev)
+    op = _dev_ptr(out, "out", torch.float32, (L, S, H, t_cap), dev)
+    dl = [int(x) for x in deltas]
+    arr = (ctypes.c_int32 * max(1, len(dl)))(*dl)
+    shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
+    st = _lib.load().tri_score_rotated(ctypes.byref(shape), kp, None if paged is None else ctypes.byref(paged),
+                                       style, qp, ap, tp, float(rope_theta), arr, len(dl), op, _stream(dev))
+    _lib.check("tri_score_rotated", st)
+    return out
+
+
 def _select_io(L, S, H, b_cap, device, kept, n_kept):
     if kept is None:
         kept = torch.empty((L, S, H, b_cap), dtype=torch.int32, device=device)

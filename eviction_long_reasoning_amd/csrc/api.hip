@@ -41,6 +41,25 @@ kv_status check_policy(const kv_policy *po, int b_cap) {
 
 kv_status hip_status(hipError_t e) { return e == hipSuccess ? KV_OK : KV_EHIP; }
 
+// Band frequencies omega_f = theta^(-2f/d) (as revolutions per position, omega_f / 2pi) and the
+// fold coefficient A_f = (1/|D|) sum_delta exp(i omega_f delta), both in fp64 with the phase
+// reduced to [-1/2, 1/2] revolutions before sin/cos.
+void fold_coefficients(int d, double rope_theta, const int32_t *deltas, int n_delta, float2 *A, double *rev_out) {
+  for (int f = 0; f < d / 2; ++f) {
+    const double omega = std::pow(rope_theta, -2.0 * f / d);
+    const double rev = omega / kTwoPi;
+    double re = 0.0, im = 0.0;
+    for (int i = 0; i < n_delta; ++i) {
+      const double x = rev * static_cast<double>(deltas[i]);
+      const double r = x - std::nearbyint(x);
+      re += std::cos(kTwoPi * r);
+      im += std::sin(kTwoPi * r);
+    }
+    A[f] = make_float2(static_cast<float>(re / n_delta), static_cast<float>(im / n_delta));
+    rev_out[f] = rev;
+  }
+}
+
 int elem_bytes(const kv_shape *sh) { return sh->dtype == KV_BF16 ? 2 : 4; }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -92,22 +111,7 @@ KV_EXPORT kv_status tri_score(const kv_shape *shape, const void *K, const int32_
   p.t_cap = shape->t_cap;
   p.chunks_per_head = (shape->t_cap + kScoreChunk - 1) / kScoreChunk;
 
-  // Band frequencies omega_f = theta^(-2f/d) and the fold coefficient
-  // A_f = (1/|D|) sum_delta exp(i omega_f delta), both in fp64 with the phase
-  // reduced to [-1/2, 1/2] revolutions before sin/cos.
-  for (int f = 0; f < p.F; ++f) {
-    const double omega = std::pow(rope_theta, -2.0 * f / p.d);
-    const double rev = omega / kTwoPi;
-    double re = 0.0, im = 0.0;
-    for (int i = 0; i < n_delta; ++i) {
-      const double x = rev * static_cast<double>(deltas[i]);
-      const double r = x - std::nearbyint(x);
-      re += std::cos(kTwoPi * r);
-      im += std::sin(kTwoPi * r);
-    }
-    p.A[f] = make_float2(static_cast<float>(re / n_delta), static_cast<float>(im / n_delta));
-    p.rev[f] = rev;
-  }
+  fold_coefficients(p.d, rope_theta, deltas, n_delta, p.A, p.rev);
   // one head's rows are addressed with 32-bit buffer offsets
   if (static_cast<long long>(p.t_cap) * p.d * elem_bytes(shape) + (64ll << 9) >= (1ll << 31)) return KV_ESHAPE;
   const int bpl = shape->dtype == KV_BF16 ? 4 : 2;  // bands per 16-byte lane piece
@@ -118,6 +122,56 @@ KV_EXPORT kv_status tri_score(const kv_shape *shape, const void *K, const int32_
   const long long threads = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head * kScoreThreads;
   if (threads >= (1ll << 32)) return KV_ESHAPE;
   return hip_status(launch_score(p, shape->dtype == KV_BF16, lpk, static_cast<hipStream_t>(stream)));
+}
+
+KV_EXPORT kv_status tri_score_rotated(const kv_shape *shape, const void *K, const kv_paged *paged,
+                                      int32_t rope_style, const float *qbar, const float *qabs,
+                                      const int32_t *t_cur, double rope_theta, const int32_t *deltas,
+                                      int32_t n_delta, float *scores, void *stream) {
+  kv_status st = check_shape(shape, true);
+  if (st != KV_OK) return st;
+  if (!K || !qbar || !t_cur || !deltas || !scores) return KV_EINVAL;
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta)) return KV_EINVAL;
+  if (n_delta < 1 || n_delta > kMaxDeltas) return KV_EINVAL;
+  if (rope_style != KV_ROPE_INTERLEAVED && rope_style != KV_ROPE_HALF) return KV_EINVAL;
+  if (!aligned16(K) || (reinterpret_cast<uintptr_t>(qbar) & 3u)) return KV_EINVAL;
+
+  RotScoreParams p{};
+  p.K = K;
+  p.qbar = qbar;
+  p.qabs = qabs;
+  p.t_cur = t_cur;
+  p.seq_len = shape->seq_len;
+  p.scores = scores;
+  p.L = shape->n_layers;
+  p.S = shape->n_seq;
+  p.H = shape->n_kv_heads;
+  p.d = shape->head_dim;
+  p.F = shape->head_dim / 2;
+  p.t_cap = shape->t_cap;
+  p.half = rope_style == KV_ROPE_HALF;
+  p.chunks_per_head = (shape->t_cap + kScoreChunk - 1) / kScoreChunk;
+  if (paged) {
+    if (!paged->block_table || paged->blocks_per_seq < 1 || paged->n_blocks < 1 || paged->block_size < 1 ||
+        (paged->block_size & (paged->block_size - 1)))
+      return KV_EINVAL;
+    if (static_cast<long long>(paged->blocks_per_seq) * paged->block_size < shape->t_cap) return KV_ESHAPE;
+    p.block_table = paged->block_table;
+    p.blocks_per_seq = paged->blocks_per_seq;
+    p.n_blocks = paged->n_blocks;
+    int shift = 0;
+    while ((1 << shift) < paged->block_size) ++shift;
+    p.block_shift = shift;
+  }
+  fold_coefficients(p.d, rope_theta, deltas, n_delta, p.A, p.rev);
+  const int pieces = p.d * elem_bytes(shape) / 16;  // 16-byte lane pieces per row
+  int lpk = 1;
+  while (lpk < pieces) lpk <<= 1;
+  if (lpk > 64) return KV_ESHAPE;
+  if (p.half && (lpk != pieces || lpk < 2)) return KV_ESHAPE;  // the two halves must fill whole lanes
+  const long long threads = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head * kScoreThreads;
+  if (threads >= (1ll << 32)) return KV_ESHAPE;
+  return hip_status(launch_score_rotated(p, shape->dtype == KV_BF16, lpk, static_cast<hipStream_t>(stream)));
 }
 
 static kv_status select_common(const kv_shape *shape, const kv_policy *policy, int32_t *kept, int32_t b_cap,

@@ -35,6 +35,25 @@ constexpr int kScoreChunk = (kScoreThreads / 64) * kScoreBatchesPerWave * 64;
 
 hipError_t launch_score(const ScoreParams &p, int dtype_bf16, int lanes_per_key, hipStream_t st);
 
+// Keys stored after RoPE, dense or paged.
+struct RotScoreParams {
+  const void *K;               // dense [L,S,H,t_cap,d] or paged pool [L,n_blocks,block_size,H,d]
+  const int32_t *block_table;  // [S, blocks_per_seq] or nullptr (dense)
+  int32_t blocks_per_seq, block_shift, n_blocks;
+  const float *qbar;           // [L,H,d] in the storage layout
+  const float *qabs;           // [L,H,d/2] or nullptr
+  const int32_t *t_cur;        // [S]
+  const int32_t *seq_len;      // [S]
+  float *scores;               // [L,S,H,t_cap]
+  int32_t L, S, H, d, F, t_cap;
+  int32_t chunks_per_head;
+  int32_t half;                // 1: half-split pairing (x[f], x[f+d/2]); 0: interleaved
+  float2 A[kMaxBands];
+  double rev[kMaxBands];
+};
+
+hipError_t launch_score_rotated(const RotScoreParams &p, int dtype_bf16, int lanes_per_key, hipStream_t st);
+
 // --------------------------------------------------------------- select ----
 struct SelectParams {
   const float *scores;      // [L,S,H,t_cap] (top-k) or nullptr (random)

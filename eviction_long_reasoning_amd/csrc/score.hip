@@ -90,7 +90,9 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int voff, int so
 __device__ __forceinline__ void st_score(float *p, float x) { __builtin_nontemporal_store(x, p); }
 
 // One lane's share of a key's score: sum over its bands of Re(v_b * conj(k_b)), plus, with
-// NORM, the norm-based term cn_b * |k_b| (cn_b = (1 - R_b) E|q_b|).
+// NORM, the norm-based term cn_b * |k_b| (cn_b = (1 - R_b) E|q_b|). |k_b| uses the hardware
+// square root (within 1 ulp); the library sqrtf's correctly rounded expansion made the kernel
+// ALU-bound.
 template <bool BF16, bool NORM>
 __device__ __forceinline__ float lane_dot(const uint4 &d, const float2 *v, const float *cn) {
   constexpr int BPL = BF16 ? 4 : 2;
@@ -102,7 +104,7 @@ __device__ __forceinline__ float lane_dot(const uint4 &d, const float2 *v, const
     const float im = BF16 ? __uint_as_float(wd[i] & 0xffff0000u) : __uint_as_float(wd[2 * i + 1]);
     a = fmaf(v[i].x, re, a);
     a = fmaf(v[i].y, im, a);
-    if (NORM) a = fmaf(cn[i], sqrtf(fmaf(re, re, im * im)), a);
+    if (NORM) a = fmaf(cn[i], __builtin_amdgcn_sqrtf(fmaf(re, re, im * im)), a);
   }
   return a;
 }

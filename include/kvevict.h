@@ -5,6 +5,7 @@
  * head) caches:
  *
  *   tri_score        score every cached key from the query centre
+ *   tri_score_rotated  the same for keys stored after RoPE (dense or paged)
  *   kv_select_topk   keep prompt + recent window + top-scoring keys per head
  *   kv_select_random keep prompt + recent window + uniformly random keys
  *   kv_compact       gather the kept K/V rows (and positions) contiguously
@@ -142,6 +143,44 @@ kv_status tri_score(const kv_shape *shape, const void *K, const int32_t *pos,
                     const float *qbar, const float *qabs, const int32_t *t_cur, double rope_theta,
                     const int32_t *deltas, int32_t n_delta, float *scores,
                     void *stream);
+
+/* RoPE pairing of the stored coordinates: band f is (x[2f], x[2f+1]) or (x[f], x[f+d/2]). */
+typedef enum kv_rope_style {
+  KV_ROPE_INTERLEAVED = 0,
+  KV_ROPE_HALF = 1
+} kv_rope_style;
+
+/* A paged key pool: per layer, n_blocks blocks of block_size tokens, all KV heads of a token
+ * together. The row of (layer l, physical block pb, token o in the block, KV head h) starts at
+ * element ((((l*n_blocks + pb)*block_size + o)*n_kv_heads + h)*head_dim). Slot j of sequence s
+ * lives in physical block block_table[s*blocks_per_seq + j/block_size], token j % block_size.
+ * Block ids outside [0, n_blocks) are clamped into it (memory safety, not a result). */
+typedef struct kv_paged {
+  const int32_t *block_table;  /* device [n_seq][blocks_per_seq] */
+  int32_t blocks_per_seq;      /* >= 1; blocks_per_seq * block_size >= t_cap */
+  int32_t block_size;          /* a power of two */
+  int32_t n_blocks;            /* physical blocks per layer in the pool */
+} kv_paged;
+
+/*
+ * tri_score_rotated -- tri_score for keys stored after RoPE, dense or paged.
+ *
+ * Same score as tri_score with K replaced by its rotated form: a serving
+ * engine keeps k_rot = RoPE(k, p) ([TA-blog] scoring implementation), and
+ *   scores[l,s,h,j] = (1/|D|) sum_{delta in D} < RoPE(qbar[l,h], t_cur[s]+delta), k_rot[j] >
+ * (+ the norm-based term when qabs is given; |k_rot_f| = |k_f|). No key
+ * position is needed. qbar and the keys use the pairing rope_style; with
+ * KV_ROPE_HALF the two halves of a row must each fill whole 16-byte pieces
+ * (bf16: head_dim a power of two >= 16; fp32: >= 8).
+ *
+ *  K        dense device [L,S,H,t_cap,d] (paged == NULL) or the paged pool.
+ *  paged    NULL, or the host descriptor of a device block table.
+ *  other arguments as for tri_score; scores are dense [L,S,H,t_cap].
+ */
+kv_status tri_score_rotated(const kv_shape *shape, const void *K, const kv_paged *paged,
+                            int32_t rope_style, const float *qbar, const float *qabs,
+                            const int32_t *t_cur, double rope_theta, const int32_t *deltas,
+                            int32_t n_delta, float *scores, void *stream);
 
 /*
  * kv_select_topk -- exact per-head top-n_sel of the evictable range.

@@ -19,20 +19,33 @@ def band_frequencies(d: int, theta: float) -> np.ndarray:
     return np.power(np.float64(theta), -2.0 * f / d)
 
 
-def rope_rotate(x: np.ndarray, p, theta: float) -> np.ndarray:
-    """RoPE(x, p): rotate each band of x (last axis, interleaved pairs) by omega_f * p.
+def band_slices(d: int, style: str = "interleaved"):
+    """Where band f's real and imaginary parts sit: interleaved (2f, 2f+1) or half-split (f, f+d/2)."""
+    if style == "interleaved":
+        return slice(0, d, 2), slice(1, d, 2)
+    if style == "half":
+        return slice(0, d // 2), slice(d // 2, d)
+    raise ValueError(f"unknown RoPE style {style!r}")
+
+
+def rope_rotate(x: np.ndarray, p, theta: float, style: str = "interleaved") -> np.ndarray:
+    """RoPE(x, p): rotate each band of x (last axis) by omega_f * p.
 
     ``x`` has shape (..., d); ``p`` broadcasts against x.shape[:-1].
     The 2-D rotation of (a, b) by angle phi is (a cos phi - b sin phi,
     a sin phi + b cos phi), i.e. multiplication of a + ib by exp(i phi).
+    ``style`` says which coordinates form band f: "interleaved" pairs
+    x[2f], x[2f+1] (the summary's complex form); "half" pairs x[f], x[f+d/2]
+    (the rotate-half layout that some models store).
     """
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     omega = band_frequencies(d, theta)
     ang = np.asarray(p, dtype=np.float64)[..., None] * omega
     c, s = np.cos(ang), np.sin(ang)
-    a, b = x[..., 0::2], x[..., 1::2]
+    re, im = band_slices(d, style)
+    a, b = x[..., re], x[..., im]
     out = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (d,)), dtype=np.float64)
-    out[..., 0::2] = a * c - b * s
-    out[..., 1::2] = a * s + b * c
+    out[..., re] = a * c - b * s
+    out[..., im] = a * s + b * c
     return out

@@ -33,6 +33,10 @@ The full TriAttention score adds the norm-based term of the same section
 
 which does not depend on the distance, so the offset-averaged full score is
 ``score_full = score_literal + norm_term``.
+
+Keys stored after RoPE (the TriAttention blog's implementation walkthrough:
+the serving engine keeps rotated keys) are scored by ``score_rotated``: the
+same average, with the key already rotated, so no key position is needed.
 """
 from __future__ import annotations
 
@@ -40,7 +44,7 @@ from typing import Sequence
 
 import numpy as np
 
-from .rope import band_frequencies, rope_rotate
+from .rope import band_frequencies, band_slices, rope_rotate
 
 
 def _as_inputs(K, pos, qbar):
@@ -121,3 +125,28 @@ def norm_term(K, qbar, qabs) -> np.ndarray:
 def score_full(K, pos, qbar, qabs, t: int, theta: float, deltas: Sequence[int]) -> np.ndarray:
     """Offset-averaged S_trig plus S_norm (the full TriAttention score before GQA aggregation)."""
     return score_literal(K, pos, qbar, t, theta, deltas) + norm_term(K, qbar, qabs)
+
+
+def score_rotated(K_rot, qbar, t: int, theta: float, deltas: Sequence[int], style: str = "interleaved",
+                  qabs=None) -> np.ndarray:
+    """Mean over delta of <RoPE(q_bar, t+delta), k_rot_j> for keys stored after RoPE.
+
+    ``style`` is the layout of both q_bar and the stored keys. With ``qabs`` the norm term
+    sum_f (1 - R_f) E|q_f| |k_f| is added (rotation leaves |k_f| unchanged).
+    """
+    K = np.asarray(K_rot, dtype=np.float64)
+    q = np.asarray(qbar, dtype=np.float64)
+    if K.ndim != 2 or q.shape != (K.shape[1],):
+        raise ValueError("shape mismatch")
+    acc = np.zeros(K.shape[0], dtype=np.float64)
+    for delta in deltas:
+        acc += K @ rope_rotate(q, int(t) + int(delta), theta, style)
+    out = acc / len(deltas)
+    if qabs is not None:
+        re, im = band_slices(K.shape[1], style)
+        qa = np.asarray(qabs, dtype=np.float64)
+        centre = np.hypot(q[re], q[im])
+        with np.errstate(divide="ignore", invalid="ignore"):
+            R = np.where(qa > 0, centre / np.where(qa > 0, qa, 1.0), 1.0)
+        out = out + np.hypot(K[:, re], K[:, im]) @ ((1.0 - R) * qa)
+    return out

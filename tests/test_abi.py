@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_the_four_calls():
     names = _declared_functions()
-    for n in ("tri_score", "kv_select_topk", "kv_select_random", "kv_compact", "kv_version", "kv_status_string"):
+    for n in ("tri_score", "tri_score_rotated", "kv_select_topk", "kv_select_random", "kv_compact", "kv_version",
+              "kv_status_string"):
         assert n in names, names
 
 
@@ -64,6 +65,18 @@ def test_host_validation_rejects_bad_arguments(lib):
     # no offsets, non-positive theta
     assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, 1e4, arr, 0, dummy, None) == L.KV_EINVAL
     assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, -1.0, arr, 1, dummy, None) == L.KV_EINVAL
+    # rotated keys: unknown style, half-split rows that do not split into whole lanes, bad paging
+    assert lib.tri_score_rotated(ctypes.byref(sh), dummy, None, 7, dummy, None, dummy, 1e4, arr, 1, dummy,
+                                 None) == L.KV_EINVAL
+    sh96 = L.KvShape(1, 1, 1, 96, 16, L.KV_BF16, seq)
+    assert lib.tri_score_rotated(ctypes.byref(sh96), dummy, None, L.KV_ROPE_HALF, dummy, None, dummy, 1e4, arr, 1,
+                                 dummy, None) == L.KV_ESHAPE
+    pg = L.KvPaged(dummy, 1, 12, 4)       # block size not a power of two
+    assert lib.tri_score_rotated(ctypes.byref(sh), dummy, ctypes.byref(pg), 0, dummy, None, dummy, 1e4, arr, 1,
+                                 dummy, None) == L.KV_EINVAL
+    pg = L.KvPaged(dummy, 1, 8, 4)        # 1 block of 8 cannot hold t_cap = 16 slots
+    assert lib.tri_score_rotated(ctypes.byref(sh), dummy, ctypes.byref(pg), 0, dummy, None, dummy, 1e4, arr, 1,
+                                 dummy, None) == L.KV_ESHAPE
     # selector: b_cap below budget or prompt cap, t_cap above the supported maximum, budget < 1
     pol = L.KvPolicy(8, 2, 4, seq)
     assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 7, dummy, None) == L.KV_ESHAPE

@@ -127,6 +127,63 @@ def test_score_with_norm_term_matches_oracle(case):
     log(f"[score+norm] {name}: worst scaled error {worst:.2e}")
 
 
+ROT_CASES = [
+    # name, dtype, d, L, S, H, T per seq, style, norm, paged block size (0 = dense)
+    ("rot-bf16-d128-inter", "bf16", 128, 2, 2, 2, [1000, 777], "interleaved", False, 0),
+    ("rot-bf16-d128-half", "bf16", 128, 1, 2, 3, [1030, 64], "half", False, 0),
+    ("rot-bf16-d64-half-norm", "bf16", 64, 2, 1, 2, [900], "half", True, 0),
+    ("rot-bf16-d96-inter-norm", "bf16", 96, 1, 2, 2, [500, 130], "interleaved", True, 0),
+    ("rot-fp32-d64-half", "f32", 64, 1, 1, 2, [333], "half", False, 0),
+    ("rot-fp32-d8-inter", "f32", 8, 1, 1, 1, [200], "interleaved", True, 0),
+    ("rot-paged16-bf16-d128", "bf16", 128, 2, 3, 4, [1000, 1, 517], "interleaved", True, 16),
+    ("rot-paged64-bf16-d64-half", "bf16", 64, 1, 2, 8, [2000, 1500], "half", False, 64),
+]
+
+
+@pytest.mark.parametrize("case", ROT_CASES, ids=[c[0] for c in ROT_CASES])
+def test_score_rotated_matches_oracle(case):
+    name, dtype, d, L, S, H, Ts, style, norm, bs = case
+    log(f"[rotated] {name}")
+    r = rng(550, zlib.crc32(name.encode()) % 1000)
+    Ts = np.array(Ts, np.int32)
+    theta, D = 1e6, [2 ** i for i in range(17)]
+    qb = r.standard_normal((L, H, d)).astype(np.float32)
+    qabs = None
+    if norm:
+        re, im = oracle.band_slices(d, style)
+        qabs = (np.hypot(qb[..., re], qb[..., im]) / r.uniform(0.6, 1.0, (L, H, d // 2))).astype(np.float32)
+    t_cur = (Ts + 7).astype(np.int32)
+    if bs == 0:
+        t_cap = int(Ts.max()) + 3
+        K = (r.standard_normal((L, 1, H, 1, d)) + 0.3 * r.standard_normal((L, S, H, t_cap, d))).astype(np.float32)
+        Kd = _to_dev_keys(K, dtype)
+        Kh = keys_f64(_host_keys(Kd, dtype), dtype)
+        rows = lambda l, s, h, T: Kh[l, s, h, :T]
+        out = kv.tri_score_rotated(Kd, torch.from_numpy(qb).to(DEV), _i32(t_cur), _i32(Ts), theta, D, rope_style=style,
+                                   qabs=None if qabs is None else torch.from_numpy(qabs).to(DEV))
+    else:
+        bps = (int(Ts.max()) + bs - 1) // bs
+        n_blocks = S * bps + 5
+        pool = (r.standard_normal((L, 1, 1, H, d)) + 0.3 * r.standard_normal((L, n_blocks, bs, H, d))).astype(np.float32)
+        table = r.permutation(n_blocks)[:S * bps].reshape(S, bps).astype(np.int32)
+        Kd = _to_dev_keys(pool, dtype)
+        Ph = keys_f64(_host_keys(Kd, dtype), dtype)
+        rows = lambda l, s, h, T: np.stack([Ph[l, table[s, j // bs], j % bs, h] for j in range(T)]) if T else \
+            np.zeros((0, d))
+        out = kv.tri_score_rotated(Kd, torch.from_numpy(qb).to(DEV), _i32(t_cur), _i32(Ts), theta, D, rope_style=style,
+                                   block_table=_i32(table), qabs=None if qabs is None else torch.from_numpy(qabs).to(DEV))
+    got = out.cpu().numpy()
+    worst = 0.0
+    for l in range(L):
+        for s in range(S):
+            for h in range(H):
+                T = int(Ts[s])
+                ref = oracle.score_rotated(rows(l, s, h, T), qb[l, h], int(t_cur[s]), theta, D, style=style,
+                                           qabs=None if qabs is None else qabs[l, h])
+                worst = max(worst, assert_scores(got[l, s, h, :T], ref, f"{name} l{l} s{s} h{h}"))
+    log(f"[rotated] {name}: worst scaled error {worst:.2e}")
+
+
 def test_score_deterministic():
     case = SCORE_CASES[1]
     K, qb, Ts, pos, t_cur = _score_inputs(case, 7)

@@ -232,3 +232,44 @@ def test_norm_term_is_distance_free_and_scales():
     b = score_full(K, np.arange(7) + 50, q, qa, 150, 1e4, [1, 4])
     np.testing.assert_allclose(a, b, atol=1e-10)
     np.testing.assert_allclose(norm_term(3 * K, 2 * q, 2 * qa), 6 * norm_term(K, q, qa), atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# keys stored after RoPE (TriAttention blog, implementation walkthrough)
+# --------------------------------------------------------------------------
+from oracle import score_rotated  # noqa: E402
+
+
+@pytest.mark.parametrize("d", [2, 8, 64])
+def test_rotated_keys_score_like_pre_rope_keys(d):
+    # scoring the stored rotated key directly gives the pre-RoPE score (the blog's two routes agree)
+    r = rng(120, d)
+    K, pos, q = r.standard_normal((11, d)), r.integers(0, 30000, 11), r.standard_normal(d)
+    qa = np.abs(q[0::2] + 1j * q[1::2]) * 1.2
+    D = [1, 4, 64, 1024]
+    np.testing.assert_allclose(score_rotated(rope_rotate(K, pos, 1e6), q, 31000, 1e6, D),
+                               score_literal(K, pos, q, 31000, 1e6, D), atol=1e-10)
+    np.testing.assert_allclose(score_rotated(rope_rotate(K, pos, 1e6), q, 31000, 1e6, D, qabs=qa),
+                               score_full(K, pos, q, qa, 31000, 1e6, D), atol=1e-10)
+
+
+def test_half_split_style_is_a_coordinate_permutation():
+    # the half-split layout is the interleaved one with coordinates permuted (band f at f and f+d/2)
+    d = 16
+    r = rng(121)
+    K, q = r.standard_normal((6, d)), r.standard_normal(d)
+    perm = np.empty(d, np.int64)
+    perm[0::2] = np.arange(d // 2)
+    perm[1::2] = np.arange(d // 2) + d // 2          # interleaved[i] = half[perm[i]]
+    D = [1, 2, 3]
+    np.testing.assert_allclose(score_rotated(K, q, 777, 1e4, D, style="half"),
+                               score_rotated(K[:, perm], q[perm], 777, 1e4, D), atol=1e-12)
+    np.testing.assert_allclose(rope_rotate(K, 5, 1e4, "half")[:, perm], rope_rotate(K[:, perm], 5, 1e4), atol=1e-12)
+    # d=2: both styles pair the same two coordinates
+    np.testing.assert_allclose(rope_rotate(K[:, :2], 9, 1e4, "half"), rope_rotate(K[:, :2], 9, 1e4), atol=1e-15)
+
+
+def test_rotated_closed_form():
+    # d=2, stored key = RoPE((1,0), p) at p = 2, query centre (1,0), t = 5, D={0}: cos(5 - 2)
+    k = rope_rotate(np.array([[1.0, 0.0]]), 2, 1e4)
+    assert score_rotated(k, [1.0, 0.0], 5, 1e4, [0])[0] == pytest.approx(np.cos(3.0), abs=1e-14)
