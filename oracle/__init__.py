@@ -14,6 +14,9 @@ from the pages' definitions:
   * ``norm_term`` / ``score_full`` -- the norm-based term S_norm weighted by
     one minus the mean resultant length, and S_trig + S_norm (TriAttention
     summary 3.4 "The Norm-Based Term", "Adaptive Weighting").
+  * ``score_gqa`` -- per-query-head scores, z-normalised per query head over
+    the cached keys, maximum over the query heads of a KV head (summary 3.4,
+    GQA handling).
   * ``score_rotated`` -- the same score for keys stored after RoPE
     (interleaved or half-split pairing), as serving engines keep them.
   * ``partition`` / ``select_topk`` -- prompt and recent-window pinning and
@@ -38,14 +41,14 @@ invariants, brute force and an independent library Philox; none is marked
 "parity unpinned".
 """
 from .rope import band_frequencies, band_slices, rope_rotate
-from .score import score_literal, score_series, score_folded, fold_coefficients, norm_term, score_full, score_rotated
+from .score import score_literal, score_series, score_folded, fold_coefficients, norm_term, score_full, score_rotated, score_gqa, zscore
 from .policy import Partition, partition, canonical_scores, select_topk, select_random, random_uniforms
 from .philox import philox4x32_10, philox4x32_10_np, PHILOX_M, PHILOX_W
 from .compact import compact
 
 __all__ = [
     "band_frequencies", "band_slices", "rope_rotate",
-    "score_literal", "score_series", "score_folded", "fold_coefficients", "norm_term", "score_full", "score_rotated",
+    "score_literal", "score_series", "score_folded", "fold_coefficients", "norm_term", "score_full", "score_rotated", "score_gqa", "zscore",
     "Partition", "partition", "canonical_scores", "select_topk", "select_random", "random_uniforms",
     "philox4x32_10", "philox4x32_10_np", "PHILOX_M", "PHILOX_W",
     "compact",

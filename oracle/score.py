@@ -34,6 +34,11 @@ The full TriAttention score adds the norm-based term of the same section
 which does not depend on the distance, so the offset-averaged full score is
 ``score_full = score_literal + norm_term``.
 
+Grouped-query attention (summary 3.4 "KV Cache Pruning Procedure", GQA):
+each of the G query heads sharing a KV head has its own centre; its scores
+are z-normalised over the head's cached keys and the final score is the
+maximum over the G query heads (``score_gqa``).
+
 Keys stored after RoPE (the TriAttention blog's implementation walkthrough:
 the serving engine keeps rotated keys) are scored by ``score_rotated``: the
 same average, with the key already rotated, so no key position is needed.
@@ -150,3 +155,30 @@ def score_rotated(K_rot, qbar, t: int, theta: float, deltas: Sequence[int], styl
             R = np.where(qa > 0, centre / np.where(qa > 0, qa, 1.0), 1.0)
         out = out + np.hypot(K[:, re], K[:, im]) @ ((1.0 - R) * qa)
     return out
+
+
+def zscore(s) -> np.ndarray:
+    """(s - mean) / std over all entries, population std; all zeros when the std is 0."""
+    s = np.asarray(s, dtype=np.float64)
+    if s.size == 0:
+        return s.copy()
+    mu = s.mean()
+    sd = np.sqrt(np.mean((s - mu) ** 2))
+    return np.zeros_like(s) if sd == 0 else (s - mu) / sd
+
+
+def score_gqa(K, pos, qbar_g, t: int, theta: float, deltas: Sequence[int], qabs_g=None):
+    """Per-query-head scores, z-normalised per query head over the T cached keys, max over heads.
+
+    ``qbar_g`` is (G, d) and ``qabs_g`` (G, d/2) or None. Returns (final (T,), per_head (G, T)).
+    """
+    qg = np.asarray(qbar_g, dtype=np.float64)
+    per = []
+    for g in range(qg.shape[0]):
+        if qabs_g is None:
+            per.append(score_literal(K, pos, qg[g], t, theta, deltas))
+        else:
+            per.append(score_full(K, pos, qg[g], np.asarray(qabs_g)[g], t, theta, deltas))
+    per = np.stack(per)
+    z = np.stack([zscore(row) for row in per])
+    return z.max(axis=0), per

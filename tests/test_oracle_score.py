@@ -273,3 +273,44 @@ def test_rotated_closed_form():
     # d=2, stored key = RoPE((1,0), p) at p = 2, query centre (1,0), t = 5, D={0}: cos(5 - 2)
     k = rope_rotate(np.array([[1.0, 0.0]]), 2, 1e4)
     assert score_rotated(k, [1.0, 0.0], 5, 1e4, [0])[0] == pytest.approx(np.cos(3.0), abs=1e-14)
+
+
+# --------------------------------------------------------------------------
+# GQA: z-score per query head, then max (TriAttention summary 3.4, GQA)
+# --------------------------------------------------------------------------
+from oracle import score_gqa, zscore  # noqa: E402
+
+
+def test_zscore_hand_example():
+    z = zscore([1.0, 2.0, 3.0])                      # mean 2, population std sqrt(2/3)
+    np.testing.assert_allclose(z, [-np.sqrt(1.5), 0.0, np.sqrt(1.5)], atol=1e-15)
+    assert np.all(zscore([4.0, 4.0, 4.0]) == 0.0)     # no spread: no preference
+
+
+def test_gqa_single_query_head_keeps_the_ranking():
+    r = rng(130)
+    K, q = r.standard_normal((50, 16)), r.standard_normal((1, 16))
+    final, per = score_gqa(K, None, q, 60, 1e4, [1, 8])
+    assert np.array_equal(np.argsort(final, kind="stable"), np.argsort(per[0], kind="stable"))
+    np.testing.assert_allclose(per[0], score_literal(K, None, q[0], 60, 1e4, [1, 8]), atol=1e-12)
+
+
+def test_gqa_is_scale_free_per_query_head():
+    # each query head is normalised separately: rescaling one head's centre changes nothing
+    r = rng(131)
+    K, q = r.standard_normal((40, 8)), r.standard_normal((3, 8))
+    a, _ = score_gqa(K, None, q, 90, 1e4, [1, 2, 4])
+    q2 = q * np.array([[10.0], [0.01], [3.0]])
+    b, _ = score_gqa(K, None, q2, 90, 1e4, [1, 2, 4])
+    np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+def test_gqa_max_over_heads():
+    r = rng(132)
+    K, q = r.standard_normal((30, 8)), r.standard_normal((4, 8))
+    final, per = score_gqa(K, None, q, 40, 1e4, [1])
+    z = np.stack([(p - p.mean()) / p.std() for p in per])
+    np.testing.assert_allclose(final, z.max(0), atol=1e-12)
+    # duplicating a query head changes nothing
+    f2, _ = score_gqa(K, None, np.concatenate([q, q[:1]]), 40, 1e4, [1])
+    np.testing.assert_allclose(final, f2, atol=1e-15)
