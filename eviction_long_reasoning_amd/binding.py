@@ -117,6 +117,57 @@ def tri_score_rotated(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, 
     return out
 
 
+def tri_score_gqa(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len: torch.Tensor,
+                  rope_theta: float, deltas: Sequence[int], pos: Optional[torch.Tensor] = None,
+                  qabs: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  head_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Grouped-query scores: (max over the group of the z-normalised per-query-head scores
+    [L,S,H,t_cap], the per-query-head scores [L,S,H,G,t_cap]).
+
+    ``qbar`` is [L,H,G,d] fp32 (one centre per query head), ``qabs`` optionally [L,H,G,d/2].
+    ``workspace`` is a uint8 GPU tensor of at least ``gqa_workspace_bytes`` bytes (allocated
+    here when omitted).
+    """
+    if K.dim() != 5 or K.dtype not in _DT:
+        raise ValueError("K must be [L,S,H,t_cap,d] float32/bfloat16")
+    if qbar.dim() != 4:
+        raise ValueError("qbar must be [L,H,G,d]")
+    L, S, H, t_cap, d = K.shape
+    G = qbar.shape[2]
+    dev = K.device
+    kp = _dev_ptr(K, "K")
+    qp = _dev_ptr(qbar, "qbar", torch.float32, (L, H, G, d), dev)
+    tp = _dev_ptr(t_cur, "t_cur", torch.int32, (S,), dev)
+    sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
+    pp = _dev_ptr(pos, "pos", torch.int32, (L, S, H, t_cap), dev)
+    ap = _dev_ptr(qabs, "qabs", torch.float32, (L, H, G, d // 2), dev)
+    if out is None:
+        out = torch.empty((L, S, H, t_cap), dtype=torch.float32, device=dev)
+    if head_out is None:
+        head_out = torch.empty((L, S, H, G, t_cap), dtype=torch.float32, device=dev)
+    op = _dev_ptr(out, "out", torch.float32, (L, S, H, t_cap), dev)
+    hp = _dev_ptr(head_out, "head_out", torch.float32, (L, S, H, G, t_cap), dev)
+    shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
+    lib = _lib.load()
+    need = int(lib.kv_score_gqa_workspace_bytes(ctypes.byref(shape), int(G)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 8),), dtype=torch.uint8, device=dev)
+    wp = _dev_ptr(workspace, "workspace", torch.uint8, None, dev)
+    dl = [int(x) for x in deltas]
+    arr = (ctypes.c_int32 * max(1, len(dl)))(*dl)
+    st = lib.tri_score_gqa(ctypes.byref(shape), kp, pp, int(G), qp, ap, tp, float(rope_theta), arr, len(dl), hp, op,
+                           wp, workspace.numel(), _stream(dev))
+    _lib.check("tri_score_gqa", st)
+    return out, head_out
+
+
+def gqa_workspace_bytes(L: int, S: int, H: int, t_cap: int, d: int, dtype: torch.dtype, group: int) -> int:
+    """Workspace bytes ``tri_score_gqa`` needs (0 for a shape or group it rejects)."""
+    shape = _shape(L, S, H, d, t_cap, _DT[dtype], None)
+    return int(_lib.load().kv_score_gqa_workspace_bytes(ctypes.byref(shape), int(group)))
+
+
 def _select_io(L, S, H, b_cap, device, kept, n_kept):
     if kept is None:
         kept = torch.empty((L, S, H, b_cap), dtype=torch.int32, device=device)

@@ -16,8 +16,9 @@ constexpr double kTwoPi = 6.283185307179586476925286766559;
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Selectors never touch K/V rows, so they ignore head_dim and dtype (rows == false).
-kv_status check_shape(const kv_shape *sh, bool rows) {
-  if (!sh || !sh->seq_len) return KV_EINVAL;
+// need_len == false: only the sizes are checked (workspace queries take no device arrays).
+kv_status check_shape(const kv_shape *sh, bool rows, bool need_len = true) {
+  if (!sh || (need_len && !sh->seq_len)) return KV_EINVAL;
   if (sh->n_layers < 1 || sh->n_layers >= 65536 || sh->n_seq < 1 || sh->n_kv_heads < 1 ||
       sh->n_kv_heads >= 65536 || sh->t_cap < 1)
     return KV_EINVAL;
@@ -172,6 +173,71 @@ KV_EXPORT kv_status tri_score_rotated(const kv_shape *shape, const void *K, cons
   const long long threads = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head * kScoreThreads;
   if (threads >= (1ll << 32)) return KV_ESHAPE;
   return hip_status(launch_score_rotated(p, shape->dtype == KV_BF16, lpk, static_cast<hipStream_t>(stream)));
+}
+
+namespace kvevict {
+namespace {
+// Partial sums of tri_score_gqa: per (l, s, h, score chunk, g), the fp64 sums of s and s^2.
+size_t gqa_workspace(const kv_shape *sh, int group) {
+  const size_t heads = static_cast<size_t>(sh->n_layers) * sh->n_seq * sh->n_kv_heads;
+  const size_t chunks = (static_cast<size_t>(sh->t_cap) + kScoreChunk - 1) / kScoreChunk;
+  return heads * chunks * static_cast<size_t>(group) * 2 * sizeof(double);
+}
+}  // namespace
+}  // namespace kvevict
+
+KV_EXPORT size_t kv_score_gqa_workspace_bytes(const kv_shape *shape, int32_t group) {
+  if (check_shape(shape, true, false) != KV_OK || group < 1 || group > kGqaMaxGroup) return 0;
+  return gqa_workspace(shape, group);
+}
+
+KV_EXPORT kv_status tri_score_gqa(const kv_shape *shape, const void *K, const int32_t *pos, int32_t group,
+                                  const float *qbar, const float *qabs, const int32_t *t_cur, double rope_theta,
+                                  const int32_t *deltas, int32_t n_delta, float *head_scores, float *scores,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+  kv_status st = check_shape(shape, true);
+  if (st != KV_OK) return st;
+  if (!K || !qbar || !t_cur || !deltas || !scores || !head_scores || !workspace) return KV_EINVAL;
+  if (group < 1 || group > kGqaMaxGroup) return KV_EINVAL;
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta)) return KV_EINVAL;
+  if (n_delta < 1 || n_delta > kMaxDeltas) return KV_EINVAL;
+  if (!aligned16(K) || (reinterpret_cast<uintptr_t>(qbar) & 7u) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
+    return KV_EINVAL;
+  if (workspace_bytes < gqa_workspace(shape, group)) return KV_ESHAPE;
+  const size_t heads = static_cast<size_t>(shape->n_layers) * shape->n_seq * shape->n_kv_heads;
+  const size_t score_bytes = heads * shape->t_cap * sizeof(float);
+  if (overlaps(head_scores, score_bytes * group, scores, score_bytes) ||
+      overlaps(workspace, workspace_bytes, scores, score_bytes) ||
+      overlaps(workspace, workspace_bytes, head_scores, score_bytes * group))
+    return KV_EINVAL;
+
+  GqaParams p{};
+  p.K = K;
+  p.pos = pos;
+  p.qbar = qbar;
+  p.qabs = qabs;
+  p.t_cur = t_cur;
+  p.seq_len = shape->seq_len;
+  p.raw = head_scores;
+  p.partials = static_cast<double *>(workspace);
+  p.scores = scores;
+  p.L = shape->n_layers;
+  p.S = shape->n_seq;
+  p.H = shape->n_kv_heads;
+  p.d = shape->head_dim;
+  p.F = shape->head_dim / 2;
+  p.t_cap = shape->t_cap;
+  p.G = group;
+  p.chunks_per_head = (shape->t_cap + kScoreChunk - 1) / kScoreChunk;
+  fold_coefficients(p.d, rope_theta, deltas, n_delta, p.A, p.rev);
+  const int bpl = shape->dtype == KV_BF16 ? 4 : 2;
+  const int pieces = (p.F + bpl - 1) / bpl;
+  int lpk = 1;
+  while (lpk < pieces) lpk <<= 1;
+  if (lpk > 16) return KV_ESHAPE;  // G accumulators per key step stay in registers up to 16 lanes per key
+  const long long threads = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head * kScoreThreads;
+  if (threads >= (1ll << 32)) return KV_ESHAPE;
+  return hip_status(launch_score_gqa(p, shape->dtype == KV_BF16, lpk, static_cast<hipStream_t>(stream)));
 }
 
 static kv_status select_common(const kv_shape *shape, const kv_policy *policy, int32_t *kept, int32_t b_cap,

@@ -54,6 +54,26 @@ struct RotScoreParams {
 
 hipError_t launch_score_rotated(const RotScoreParams &p, int dtype_bf16, int lanes_per_key, hipStream_t st);
 
+// Grouped-query scores: G query-head centres per KV head, z-normalised per query head, max over G.
+constexpr int kGqaMaxGroup = 8;
+struct GqaParams {
+  const void *K;            // [L,S,H,t_cap,d]
+  const int32_t *pos;       // [L,S,H,t_cap] or nullptr
+  const float *qbar;        // [L,H,G,d]
+  const float *qabs;        // [L,H,G,d/2] or nullptr
+  const int32_t *t_cur;     // [S]
+  const int32_t *seq_len;   // [S]
+  float *raw;               // [L,S,H,G,t_cap] per-query-head scores
+  double *partials;         // [L,S,H,chunks_per_head,G,2]: per-chunk sums of s and s^2
+  float *scores;            // [L,S,H,t_cap] max over g of the normalised scores
+  int32_t L, S, H, d, F, t_cap, G;
+  int32_t chunks_per_head;
+  float2 A[kMaxBands];
+  double rev[kMaxBands];
+};
+
+hipError_t launch_score_gqa(const GqaParams &p, int dtype_bf16, int lanes_per_key, hipStream_t st);
+
 // --------------------------------------------------------------- select ----
 struct SelectParams {
   const float *scores;      // [L,S,H,t_cap] (top-k) or nullptr (random)

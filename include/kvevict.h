@@ -6,6 +6,7 @@
  *
  *   tri_score        score every cached key from the query centre
  *   tri_score_rotated  the same for keys stored after RoPE (dense or paged)
+ *   tri_score_gqa    per-query-head scores of a GQA group, z-normalised, max over the group
  *   kv_select_topk   keep prompt + recent window + top-scoring keys per head
  *   kv_select_random keep prompt + recent window + uniformly random keys
  *   kv_compact       gather the kept K/V rows (and positions) contiguously
@@ -181,6 +182,43 @@ kv_status tri_score_rotated(const kv_shape *shape, const void *K, const kv_paged
                             int32_t rope_style, const float *qbar, const float *qabs,
                             const int32_t *t_cur, double rope_theta, const int32_t *deltas,
                             int32_t n_delta, float *scores, void *stream);
+
+/*
+ * tri_score_gqa -- the grouped-query rule of [TA-sum] 3.4 ("KV Cache Pruning
+ * Procedure", GQA handling): the `group` query heads that share a KV head
+ * each score the keys with their own centre (the tri_score score, with the
+ * norm-based term when qabs is given), each query head's scores are
+ * normalised to zero mean and unit standard deviation over the head's T_s
+ * cached keys, and the final score is the maximum over the group:
+ *   head_scores[l,s,h,g,j] = tri_score with qbar[l,h,g] (and qabs[l,h,g])
+ *   scores[l,s,h,j] = max_g (head_scores[l,s,h,g,j] - mu_g) / sigma_g
+ * mu_g and sigma_g are the mean and population standard deviation over the
+ * T_s slots, accumulated in fp64 in a fixed order (the result does not
+ * depend on scheduling); a query head whose scores do not vary (sigma_g = 0,
+ * or T_s = 1) contributes 0. The normalised value is computed in fp64 from
+ * the fp32 head scores and rounded to fp32.
+ *
+ *  group        G, 1 <= G <= 8 query heads per KV head.
+ *  head_dim     at most 128 (bf16) or 64 (fp32).
+ *  qbar         device [L,H,G,d] fp32 per-query-head centres.
+ *  qabs         device [L,H,G,d/2] fp32 or NULL.
+ *  head_scores  device [L,S,H,G,t_cap] fp32 output (per-query-head scores).
+ *  scores       device [L,S,H,t_cap] fp32 output.
+ *  workspace    device, 8-byte aligned, at least
+ *               kv_score_gqa_workspace_bytes(shape, group) bytes; its contents
+ *               on entry do not matter and on return are unspecified.
+ *               Calls that share a workspace must not overlap in time.
+ *  other arguments as for tri_score; slots j >= T_s are not written.
+ */
+kv_status tri_score_gqa(const kv_shape *shape, const void *K, const int32_t *pos, int32_t group,
+                        const float *qbar, const float *qabs, const int32_t *t_cur,
+                        double rope_theta, const int32_t *deltas, int32_t n_delta,
+                        float *head_scores, float *scores, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace tri_score_gqa needs for this shape and group (0 for sizes or a group it
+ * rejects). shape->seq_len is not read and may be NULL. */
+size_t kv_score_gqa_workspace_bytes(const kv_shape *shape, int32_t group);
 
 /*
  * kv_select_topk -- exact per-head top-n_sel of the evictable range.

@@ -55,6 +55,24 @@ def assert_scores(gpu, ref, what=""):
     return worst
 
 
+Z_TOL = 1e-4
+
+
+def assert_z(gpu, ref, what=""):
+    """Normalised (z) scores: |z - z_ref| <= 1e-4 * max(|z_ref|, 1).
+
+    A z-score is a dimensionless O(1) quantity, so unit scale floors the
+    relative rule the same way the head RMS floors it for raw scores.
+    """
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    err = np.abs(np.asarray(gpu, np.float64) - ref) / np.maximum(np.abs(ref), 1.0)
+    worst = float(err.max())
+    assert worst <= Z_TOL, f"{what}: worst scaled z error {worst:.3e} > {Z_TOL}"
+    return worst
+
+
 def assert_selection_near_threshold(gpu_kept, ref_kept, ref_scores, T, P, B, R, what=""):
     """End-to-end kept-set rule: equal size; differences only at near-threshold evictable slots."""
     g = set(int(x) for x in gpu_kept)

@@ -30,7 +30,7 @@ def lib():
 
 def test_header_declares_the_four_calls():
     names = _declared_functions()
-    for n in ("tri_score", "tri_score_rotated", "kv_select_topk", "kv_select_random", "kv_compact", "kv_version",
+    for n in ("tri_score", "tri_score_rotated", "tri_score_gqa", "kv_score_gqa_workspace_bytes", "kv_select_topk", "kv_select_random", "kv_compact", "kv_version",
               "kv_status_string"):
         assert n in names, names
 
@@ -77,6 +77,28 @@ def test_host_validation_rejects_bad_arguments(lib):
     pg = L.KvPaged(dummy, 1, 8, 4)        # 1 block of 8 cannot hold t_cap = 16 slots
     assert lib.tri_score_rotated(ctypes.byref(sh), dummy, ctypes.byref(pg), 0, dummy, None, dummy, 1e4, arr, 1,
                                  dummy, None) == L.KV_ESHAPE
+    # grouped-query scores: group outside 1..8, workspace too small, head_dim beyond 128 (bf16)
+    shg = L.KvShape(2, 3, 4, 128, 1000, L.KV_BF16, None)
+    need = lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg), 4)
+    assert need == 2 * 3 * 4 * 2 * 4 * 2 * 8       # (L*S*H) heads x 2 chunks of 512 keys x G x (sum, sum of squares)
+    assert lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg), 9) == 0
+    assert lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg), 0) == 0
+    assert lib.kv_score_gqa_workspace_bytes(None, 4) == 0
+    shg.seq_len = seq
+    ws, hs, sc = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x400000)
+    for grp in (0, 9):
+        assert lib.tri_score_gqa(ctypes.byref(shg), dummy, None, grp, dummy, None, dummy, 1e4, arr, 1, hs, sc, ws,
+                                 1 << 20, None) == L.KV_EINVAL
+    assert lib.tri_score_gqa(ctypes.byref(shg), dummy, None, 4, dummy, None, dummy, 1e4, arr, 1, hs, sc, ws,
+                             need - 8, None) == L.KV_ESHAPE
+    assert lib.tri_score_gqa(ctypes.byref(shg), dummy, None, 4, dummy, None, dummy, 1e4, arr, 1, hs, sc,
+                             ctypes.c_void_p(0x100004), need, None) == L.KV_EINVAL      # misaligned workspace
+    assert lib.tri_score_gqa(ctypes.byref(shg), dummy, None, 4, dummy, None, dummy, 1e4, arr, 1, hs, hs, ws,
+                             need, None) == L.KV_EINVAL      # scores alias the per-query-head scores
+    sh256 = L.KvShape(1, 1, 1, 256, 16, L.KV_BF16, seq)
+    need256 = lib.kv_score_gqa_workspace_bytes(ctypes.byref(sh256), 2)
+    assert lib.tri_score_gqa(ctypes.byref(sh256), dummy, None, 2, dummy, None, dummy, 1e4, arr, 1, hs, sc, ws,
+                             need256, None) == L.KV_ESHAPE
     # selector: b_cap below budget or prompt cap, t_cap above the supported maximum, budget < 1
     pol = L.KvPolicy(8, 2, 4, seq)
     assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 7, dummy, None) == L.KV_ESHAPE

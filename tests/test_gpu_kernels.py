@@ -12,7 +12,7 @@ import torch
 
 import eviction_long_reasoning_amd as kv
 import oracle
-from parity import assert_scores, keys_f64, log
+from parity import assert_scores, assert_z, keys_f64, log
 from workloads import bf16_bits, random_kept, random_scores, rng
 
 pytestmark = pytest.mark.gpu
@@ -125,6 +125,81 @@ def test_score_with_norm_term_matches_oracle(case):
                 ref = oracle.score_full(Kh[l, s, h, :T], p, qb[l, h], qabs[l, h], int(t_cur[s]), theta, D)
                 worst = max(worst, assert_scores(got[l, s, h, :T], ref, f"{name} l{l} s{s} h{h}"))
     log(f"[score+norm] {name}: worst scaled error {worst:.2e}")
+
+
+GQA_CASES = [
+    # name, dtype, d, L, S, H, G, T per seq, t_cap, positions, norm, zero query head
+    ("gqa-bf16-d128-g4", "bf16", 128, 1, 2, 2, 4, [1500, 513], 1500, "slots", False, -1),
+    ("gqa-bf16-d128-g8-norm", "bf16", 128, 2, 1, 2, 8, [1100], 1100, "slots", True, -1),
+    ("gqa-bf16-d64-g8-gappy", "bf16", 64, 1, 2, 3, 8, [2000, 700], 2048, "gappy", False, -1),
+    ("gqa-bf16-d64-g7-norm-gappy", "bf16", 64, 1, 1, 2, 7, [999], 1024, "gappy", True, -1),
+    ("gqa-bf16-d96-g3", "bf16", 96, 1, 1, 2, 3, [600], 640, "slots", False, 1),
+    ("gqa-bf16-d16-g5", "bf16", 16, 1, 2, 1, 5, [300, 1], 300, "slots", False, -1),
+    ("gqa-fp32-d64-g2", "f32", 64, 1, 1, 2, 2, [777], 800, "slots", True, 0),
+    ("gqa-fp32-d8-g1", "f32", 8, 1, 1, 1, 1, [100], 100, "slots", False, -1),
+    ("gqa-bf16-d128-g6-empty", "bf16", 128, 1, 2, 1, 6, [0, 1030], 1030, "slots", False, -1),
+]
+
+
+@pytest.mark.parametrize("case", GQA_CASES, ids=[c[0] for c in GQA_CASES])
+def test_gqa_score_matches_oracle(case):
+    name, dtype, d, L, S, H, G, Ts, t_cap, pmode, norm, zero_g = case
+    log(f"[gqa] {name}")
+    seed = zlib.crc32(name.encode()) % 1000
+    r = rng(560, seed)
+    theta, D = 1e6, [2 ** i for i in range(17)]
+    mu = r.standard_normal((L, H, d))
+    K = (mu[:, None, :, None, :] + 0.3 * r.standard_normal((L, S, H, t_cap, d))).astype(np.float32)
+    nu = r.standard_normal((L, H, G, d)).astype(np.float32)
+    if zero_g >= 0:
+        nu[:, :, zero_g] = 0.0                       # a query head whose scores are all 0: sigma = 0, z = 0
+    Ts = np.array(Ts, np.int32)
+    if pmode == "slots":
+        pos, t_cur = None, Ts.copy()
+    else:
+        pos = np.stack([np.sort(r.choice(50000, size=t_cap, replace=False)) for _ in range(L * S * H)])
+        pos = pos.reshape(L, S, H, t_cap).astype(np.int32)
+        t_cur = np.full(S, 50000, np.int32)
+    qabs = None
+    if norm:
+        centre = np.abs(nu[..., 0::2].astype(np.float64) + 1j * nu[..., 1::2])
+        qabs = (centre / r.uniform(0.5, 1.0, centre.shape)).astype(np.float32)
+    Kd = _to_dev_keys(K, dtype)
+    Kh = keys_f64(_host_keys(Kd, dtype), dtype)
+    out = torch.full((L, S, H, t_cap), float("nan"), device=DEV)
+    hout = torch.full((L, S, H, G, t_cap), float("nan"), device=DEV)
+    ws = torch.full((kv.gqa_workspace_bytes(L, S, H, t_cap, d, Kd.dtype, G),), 0xAB, dtype=torch.uint8, device=DEV)
+    kv.tri_score_gqa(Kd, torch.from_numpy(nu).to(DEV), _i32(t_cur), _i32(Ts), theta, D,
+                     pos=None if pos is None else _i32(pos), qabs=None if qabs is None else torch.from_numpy(qabs).to(DEV),
+                     out=out, head_out=hout, workspace=ws)
+    got, ghead = out.cpu().numpy(), hout.cpu().numpy()
+    worst_s = worst_z = 0.0
+    for l in range(L):
+        for s in range(S):
+            for h in range(H):
+                T = int(Ts[s])
+                p = None if pos is None else pos[l, s, h, :T]
+                zref, sref = oracle.score_gqa(Kh[l, s, h, :T], p, nu[l, h], int(t_cur[s]), theta, D,
+                                              None if qabs is None else qabs[l, h])
+                for g in range(G):
+                    worst_s = max(worst_s, assert_scores(ghead[l, s, h, g, :T], sref[g], f"{name} l{l} s{s} h{h} g{g}"))
+                worst_z = max(worst_z, assert_z(got[l, s, h, :T], zref, f"{name} l{l} s{s} h{h}"))
+                assert np.all(np.isnan(got[l, s, h, T:])) and np.all(np.isnan(ghead[l, s, h, :, T:])), \
+                    "slots beyond T were written"
+    log(f"[gqa] {name}: worst scaled head-score error {worst_s:.2e}, worst z error {worst_z:.2e}")
+
+
+def test_gqa_is_deterministic():
+    # the per-query-head statistics are reduced in a fixed order: repeated calls agree bit for bit
+    L, S, H, G, T, d = 1, 1, 4, 8, 4000, 128
+    r = rng(561, 0)
+    K = _to_dev_keys(r.standard_normal((L, S, H, T, d)).astype(np.float32), "bf16")
+    nu = torch.from_numpy(r.standard_normal((L, H, G, d)).astype(np.float32)).to(DEV)
+    a, ha = kv.tri_score_gqa(K, nu, _i32([T]), _i32([T]), 1e6, [1, 2, 4])
+    for _ in range(3):
+        b, hb = kv.tri_score_gqa(K, nu, _i32([T]), _i32([T]), 1e6, [1, 2, 4])
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+        assert torch.equal(ha.view(torch.int32), hb.view(torch.int32))
 
 
 ROT_CASES = [

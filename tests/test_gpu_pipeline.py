@@ -17,9 +17,9 @@ import torch
 
 import eviction_long_reasoning_amd as kv
 import oracle
-from parity import assert_scores, assert_selection_near_threshold, keys_f64, log
+from parity import assert_scores, assert_selection_near_threshold, assert_z, keys_f64, log
 from workloads import (centres, kv_numpy, kv_torch, periodic_prompt_torch, periodic_tokens_torch,
-                       query_magnitudes, workload)
+                       query_head_centres, query_head_magnitudes, query_magnitudes, workload)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -156,6 +156,36 @@ def test_workload2_full_score_with_norm_term():
     log(f"[w2+norm] 8 heads: worst scaled score error {worst:.2e}, kept differences {diffs}")
 
 
+def test_workload2_gqa_zscore_max():
+    # the GQA rule on the Qwen3-8B-shaped layer: 4 query heads per KV head, each with its own
+    # centre, z-normalised per query head over the 32768 keys, max over the group; with and
+    # without the norm-based term
+    w = workload(2)
+    K, V, _, _ = kv_numpy(w)
+    nu = query_head_centres(w)
+    qabs = query_head_magnitudes(w, nu)
+    Kd = dev_from_host(K, w.dtype)
+    T, P = w.seq_len, w.prompt_len
+    for with_norm in (False, True):
+        sc, hs = kv.tri_score_gqa(Kd, torch.from_numpy(nu).to(DEV), i32(w.t_cur), i32(T), w.theta, w.deltas,
+                                  qabs=torch.from_numpy(qabs).to(DEV) if with_norm else None)
+        kept, nk = kv.kv_select_topk(sc, i32(T), i32(P), w.budget, w.recent, w.prompt_cap())
+        sch, hsh, kh = sc.cpu().numpy(), hs.cpu().numpy(), kept.cpu().numpy()
+        worst_s = worst_z = 0.0
+        diffs = 0
+        for h in range(w.n_kv_heads):
+            zref, per = oracle.score_gqa(keys_f64(K[0, 0, h], w.dtype), None, nu[0, h], int(w.t_cur[0]), w.theta,
+                                         w.deltas, qabs[0, h] if with_norm else None)
+            for g in range(w.group):
+                worst_s = max(worst_s, assert_scores(hsh[0, 0, h, g], per[g], f"w2-gqa h{h} g{g}"))
+            worst_z = max(worst_z, assert_z(sch[0, 0, h], zref, f"w2-gqa h{h}"))
+            rk = oracle.select_topk(zref, int(T[0]), int(P[0]), w.budget, w.recent)
+            diffs += assert_selection_near_threshold(kh[0, 0, h, :int(nk[0])], rk, zref, int(T[0]), int(P[0]),
+                                                     w.budget, w.recent, f"w2-gqa h{h}")
+        log(f"[w2-gqa norm={with_norm}] 8 KV heads x 4 query heads: worst head-score error {worst_s:.2e}, "
+            f"worst z error {worst_z:.2e}, kept differences {diffs}")
+
+
 # --------------------------------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def full_pass():
@@ -264,9 +294,11 @@ class _OracleHead:
         self.pos = np.concatenate([self.pos, pn.astype(np.int32)])
 
 
-@pytest.mark.parametrize("mode", ["scored", "random"])
+@pytest.mark.parametrize("mode", ["scored", "random", "gqa"])
 def test_workload4_periodic_events(mode):
+    # gqa: the z-score + max rule over the 8 query heads of each KV head, first 64 events
     w = workload(4)
+    n_events = 64 if mode == "gqa" else w.n_events
     L, S, H, Tc, d = w.n_layers, w.n_seq, w.n_kv_heads, w.t_cap, w.head_dim
     P = w.prompt_len.astype(np.int64)
     mu0, qb, dr = centres(w)
@@ -279,8 +311,15 @@ def test_workload4_periodic_events(mode):
     ora = {k: _OracleHead(host_bits(K0[k]), host_bits(V0[k]), int(P[k[1]])) for k in sampled}
     diverged = set()
     qbd = torch.from_numpy(qb).to(DEV)
+    if mode == "gqa":
+        nu = query_head_centres(w)
+        nud = torch.from_numpy(nu).to(DEV)
+        gq_out = torch.empty((L, S, H, Tc), dtype=torch.float32, device=DEV)
+        gq_head = torch.empty((L, S, H, w.group, Tc), dtype=torch.float32, device=DEV)
+        gq_ws = torch.empty((kv.gqa_workspace_bytes(L, S, H, Tc, d, K0.dtype, w.group),), dtype=torch.uint8,
+                            device=DEV)
     worst, compared, near = 0.0, 0, 0
-    for ev in range(1, w.n_events + 1):
+    for ev in range(1, n_events + 1):
         Kc, Vc, Pc = bufs[cur]
         Kn, Vn, pn = periodic_tokens_torch(w, ev, (P + w.new_per_event * (ev - 1)).astype(np.int32), mu0, dr, DEV)
         for s in range(S):
@@ -296,6 +335,10 @@ def test_workload4_periodic_events(mode):
         seq = i32(T)
         if mode == "scored":
             sc = kv.tri_score(Kc, qbd, i32(t_cur), seq, w.theta, w.deltas, pos=Pc)
+            kept, nk = kv.kv_select_topk(sc, seq, i32(P), w.budget, w.recent, w.prompt_cap())
+        elif mode == "gqa":
+            sc, _ = kv.tri_score_gqa(Kc, nud, i32(t_cur), seq, w.theta, w.deltas, pos=Pc, out=gq_out,
+                                     head_out=gq_head, workspace=gq_ws)
             kept, nk = kv.kv_select_topk(sc, seq, i32(P), w.budget, w.recent, w.prompt_cap())
         else:
             kept, nk = kv.kv_select_random((L, S, H, Tc), seq, i32(P), w.budget, w.recent, w.prompt_cap(),
@@ -317,9 +360,14 @@ def test_workload4_periodic_events(mode):
                 if k in diverged:
                     rk = oracle.select_topk(np.zeros(Tn), Tn, int(P[s]), w.budget, w.recent)  # keeps sizes only
                 else:
-                    ref = oracle.score_literal(keys_f64(o.K, w.dtype), o.pos, qb[l, h], int(t_cur[s]), w.theta,
-                                               w.deltas)
-                    worst = max(worst, assert_scores(sc[l, s, h, :Tn].cpu().numpy(), ref, f"w4 ev{ev} {k}"))
+                    if mode == "gqa":
+                        ref, _ = oracle.score_gqa(keys_f64(o.K, w.dtype), o.pos, nu[l, h], int(t_cur[s]), w.theta,
+                                                  w.deltas)
+                        worst = max(worst, assert_z(sc[l, s, h, :Tn].cpu().numpy(), ref, f"w4-gqa ev{ev} {k}"))
+                    else:
+                        ref = oracle.score_literal(keys_f64(o.K, w.dtype), o.pos, qb[l, h], int(t_cur[s]), w.theta,
+                                                   w.deltas)
+                        worst = max(worst, assert_scores(sc[l, s, h, :Tn].cpu().numpy(), ref, f"w4 ev{ev} {k}"))
                     rk = oracle.select_topk(ref, Tn, int(P[s]), w.budget, w.recent)
                     gk = kept[l, s, h, :int(nk_h[s])].cpu().numpy()
                     nd = assert_selection_near_threshold(gk, rk, ref, Tn, int(P[s]), w.budget, w.recent,
@@ -328,7 +376,7 @@ def test_workload4_periodic_events(mode):
                     if nd:
                         near += nd
                         diverged.add(k)   # the trajectories legitimately part here
-            if k in diverged and mode == "scored":
+            if k in diverged and mode != "random":
                 continue
             rK, rV, rP = oracle.compact(o.K, o.V, o.pos, rk)
             n = rk.size
@@ -338,7 +386,7 @@ def test_workload4_periodic_events(mode):
         T = nk_h.astype(np.int64)
         cur = 1 - cur
         if ev % 32 == 0:
-            log(f"[w4-{mode}] event {ev}/{w.n_events}: cache {int(T.min())}..{int(T.max())} per head")
-    if mode == "scored":
-        log(f"[w4-scored] {compared} head-events compared, worst scaled error {worst:.2e}, "
+            log(f"[w4-{mode}] event {ev}/{n_events}: cache {int(T.min())}..{int(T.max())} per head")
+    if mode != "random":
+        log(f"[w4-{mode}] {compared} head-events compared, worst scaled error {worst:.2e}, "
             f"near-threshold swaps {near}, diverged heads {len(diverged)}")

@@ -225,6 +225,23 @@ def centres(w: Workload) -> Tuple[np.ndarray, np.ndarray, Optional[np.ndarray]]:
     return mu, qb, dr
 
 
+def query_head_centres(w: Workload) -> np.ndarray:
+    """Per-query-head centres nu_g, fp32 [L,H,G,d] (the draws whose mean is q_bar in GQA workloads)."""
+    if w.q_mode != "group-mean":
+        raise ValueError("per-query-head centres exist only for group-mean workloads")
+    L, H, d = w.n_layers, w.n_kv_heads, w.head_dim
+    return np.stack([rng(w.wid, l, K_NU).standard_normal((H, w.group, d)).astype(np.float32) for l in range(L)])
+
+
+def query_head_magnitudes(w: Workload, nu: np.ndarray) -> np.ndarray:
+    """E|q_f| = |nu_{g,f}| / R_{g,f} per query head, fp32 [L,H,G,d/2]; R ~ U(0.85, 1.0)."""
+    L, H, G, F = w.n_layers, w.n_kv_heads, w.group, w.n_bands
+    q = np.asarray(nu, np.float64)
+    centre = np.abs(q[..., 0::2] + 1j * q[..., 1::2])
+    R = np.stack([rng(w.wid, l, K_QABS, 1).uniform(0.85, 1.0, (H, G, F)) for l in range(L)])
+    return (centre / R).astype(np.float32)
+
+
 def query_magnitudes(w: Workload, qbar: np.ndarray) -> np.ndarray:
     """Mean query magnitude per band, E|q_f| = |q_bar_f| / R_f, fp32 [L,H,d/2].
 
