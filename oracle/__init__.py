@@ -28,7 +28,11 @@ from the pages' definitions:
     (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2,
     3", SC'11).
   * ``compact`` -- the chronological gather of kept rows (Random Attention,
-    Appendix F "Engine details").
+    Appendix F "Engine details"); ``compact_holes`` -- the in-place variant
+    that moves only kept rows beyond the new length into evicted slots.
+  * ``select_recent`` / ``select_random_shared`` / ``select_union`` -- the
+    recency+prompt and shared-draw controls (Random Attention sections 4.1,
+    5.2-5.3) and union-based selection (TriAttention blog, eviction step).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. The product package
@@ -42,14 +46,16 @@ invariants, brute force and an independent library Philox; none is marked
 """
 from .rope import band_frequencies, band_slices, rope_rotate
 from .score import score_literal, score_series, score_folded, fold_coefficients, norm_term, score_full, score_rotated, score_gqa, zscore
-from .policy import Partition, partition, canonical_scores, select_topk, select_random, random_uniforms
+from .policy import (Partition, partition, canonical_scores, select_topk, select_random, random_uniforms,
+                     select_recent, select_random_shared, select_union)
 from .philox import philox4x32_10, philox4x32_10_np, PHILOX_M, PHILOX_W
-from .compact import compact
+from .compact import compact, compact_holes
 
 __all__ = [
     "band_frequencies", "band_slices", "rope_rotate",
     "score_literal", "score_series", "score_folded", "fold_coefficients", "norm_term", "score_full", "score_rotated", "score_gqa", "zscore",
     "Partition", "partition", "canonical_scores", "select_topk", "select_random", "random_uniforms",
+    "select_recent", "select_random_shared", "select_union",
     "philox4x32_10", "philox4x32_10_np", "PHILOX_M", "PHILOX_W",
-    "compact",
+    "compact", "compact_holes",
 ]

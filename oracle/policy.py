@@ -16,6 +16,12 @@ Sources:
     head at every eviction (Eq. 3, Algorithm 1).
   * Random Attention, Appendix F: keep-sets are sorted chronologically before
     compaction.
+  * Random Attention, section 4.1 (the recency+prompt diagnostic: keep the
+    prompt and fill the rest with the contiguous recent window) and sections
+    5.2-5.3 (the shared-draw control: one random keep-set used by every head).
+  * TriAttention blog, eviction step (union-based selection: each head picks
+    its own top-k, the union is formed, the final set is taken from the union
+    by a combined score and topped up by score order when the union is short).
 
 Readings taken where the pages leave a step open (each is also listed with
 the design notes):
@@ -31,6 +37,14 @@ the design notes):
     counter (p_j, (layer << 16) | head, seq, event) and key (seed mod 2^32,
     seed >> 32), read as the uniform u = word0 / 2^32; ties go to the lower
     slot.
+  * Recency+prompt keeps the prompt and the n_kept - P latest slots (the
+    evictable range's n_sel latest slots joined to the recent window).
+  * The shared draw is the draw of layer 0, KV head 0, used by every
+    (layer, KV head) of the sequence.
+  * Union-based selection works per KV head over its G query heads, ranks
+    each query head's evictable slots by its own score, takes per-head top-k
+    (k = ceil(n_sel / G) unless given), and ranks by the combined score
+    (slot ascending on ties) both inside the union and for the top-up.
 """
 from __future__ import annotations
 
@@ -123,3 +137,46 @@ def select_random(T: int, P: int, B: int, R: int, pos: Optional[np.ndarray],
     u = np.full(part.T, -np.inf)
     u[part.e_lo:part.e_hi] = random_uniforms(p_all[part.e_lo:part.e_hi], layer, head, seq, event, seed)
     return _assemble(part, _top_by_rank(u, part))
+
+
+def select_recent(T: int, P: int, B: int, R: int) -> np.ndarray:
+    """Kept slots (ascending) under recency+prompt: the prompt plus the latest slots."""
+    part = partition(T, P, B, R)
+    if not part.compress:
+        return np.arange(part.T, dtype=np.int32)
+    latest = np.arange(part.e_hi - part.n_sel, part.e_hi)      # the n_sel latest evictable slots
+    return _assemble(part, latest)
+
+
+def select_random_shared(T: int, P: int, B: int, R: int, pos: Optional[np.ndarray],
+                         seed: int, event: int, seq: int) -> np.ndarray:
+    """The shared-draw control: one keep-set for every head, drawn as layer 0 / KV head 0's."""
+    return select_random(T, P, B, R, pos, seed, event, 0, 0, seq)
+
+
+def select_union(head_scores, combined, T: int, P: int, B: int, R: int, k: Optional[int] = None) -> np.ndarray:
+    """Kept slots (ascending) under union-based selection over the G query heads of a KV head.
+
+    1. every query head g takes its own top-k evictable slots by head_scores[g];
+    2. the union of those sets is formed;
+    3. the n_sel slots of the union ranked first by the combined score are kept;
+    4. if the union holds fewer than n_sel slots, the rest of the evictable range
+       tops it up in combined-score order.
+    """
+    part = partition(T, P, B, R)
+    if not part.compress:
+        return np.arange(part.T, dtype=np.int32)
+    hs = np.atleast_2d(np.asarray(head_scores))
+    G = hs.shape[0]
+    if k is None:
+        k = -(-part.n_sel // G)
+    union = set()
+    slots = np.arange(part.e_lo, part.e_hi, dtype=np.int64)
+    for g in range(G):
+        v = canonical_scores(hs[g][:part.T])[part.e_lo:part.e_hi]
+        order = np.lexsort((slots, -v))
+        union.update(int(x) for x in slots[order[:k]])
+    c = canonical_scores(np.asarray(combined)[:part.T])[part.e_lo:part.e_hi]
+    in_u = np.array([int(x) in union for x in slots])
+    order = np.lexsort((slots, -c, ~in_u))   # union first, then combined score desc, then slot asc
+    return _assemble(part, slots[order[:part.n_sel]])

@@ -7,7 +7,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import partition, select_random, select_topk, random_uniforms, canonical_scores
+from oracle import (canonical_scores, partition, random_uniforms, select_random, select_random_shared, select_recent,
+                    select_topk, select_union)
 from workloads import random_scores, rng
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "partition_cases.json")
@@ -207,3 +208,82 @@ def test_random_survival_matches_pages_rate():
     num, den = _survival_sim(K, r, lp, events=3, heads=3, seed=5)
     rate = num[1:].sum() / den[1:].sum()
     assert abs(rate - 0.94) < 0.01 and abs((K - lp) / (K + r - lp) - 0.94) < 0.005
+
+
+# --------------------------------------------------------------------------
+# policy variants: recency+prompt, shared draw, union-based selection
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,P,B,R", [(10, 2, 6, 1), (100, 0, 30, 8), (100, 40, 30, 8), (50, 5, 50, 3),
+                                     (51, 5, 50, 3), (1000, 100, 300, 64), (7, 7, 3, 2)])
+def test_recent_is_prompt_plus_latest(T, P, B, R):
+    kept = select_recent(T, P, B, R)
+    part = partition(T, P, B, R)
+    # closed form: the prompt and the n_kept - P latest slots
+    want = list(range(min(P, T))) + list(range(T - (part.n_kept - part.P), T))
+    assert kept.tolist() == sorted(set(want)) and kept.size == part.n_kept
+    # the top-n rule ranking slots by their own index picks the same set
+    assert np.array_equal(kept, select_topk(np.arange(T, dtype=np.float64), T, P, B, R))
+
+
+def test_recent_hand_example():
+    # T=10, P=2, B=6, R=1: keep slots 0,1 and the 4 latest
+    assert select_recent(10, 2, 6, 1).tolist() == [0, 1, 6, 7, 8, 9]
+
+
+def test_shared_draw_is_one_keep_set_for_every_head():
+    T, P, B, R = 900, 64, 300, 32
+    pos = np.arange(T) * 3 + 11
+    a = select_random_shared(T, P, B, R, pos, 99, 4, 2)
+    assert np.array_equal(a, select_random(T, P, B, R, pos, 99, 4, 0, 0, 2))
+    # the per-head rule draws differently for another head; the shared one does not depend on it
+    assert not np.array_equal(a, select_random(T, P, B, R, pos, 99, 4, 3, 5, 2))
+    assert not np.array_equal(a, select_random_shared(T, P, B, R, pos, 99, 4, 3))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_union_with_budget_sized_heads_equals_top_n_of_the_max(seed):
+    # with per-head k = n_sel and the combined score max_g s_g, a slot among the n_sel best by
+    # its max is among its arg-max head's n_sel best, so the union rule is the top-n rule on
+    # the max (continuous scores: no ties)
+    r = rng(620, seed)
+    G, T, P, B, R = int(r.integers(1, 9)), 600, 40, 200, 16
+    hs = r.standard_normal((G, T))
+    comb = hs.max(axis=0)
+    part = partition(T, P, B, R)
+    assert np.array_equal(select_union(hs, comb, T, P, B, R, k=part.n_sel), select_topk(comb, T, P, B, R))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_union_keeps_the_whole_union_when_short_and_only_union_when_long(seed):
+    r = rng(621, seed)
+    G, T, P, B, R = 4, 400, 20, 150, 10
+    part = partition(T, P, B, R)
+    base = r.standard_normal(T)
+    hs = base[None, :] + 0.05 * r.standard_normal((G, T))       # heads agree: the union is short
+    comb = r.standard_normal(T)
+    for k, short in ((part.n_sel // G, True), (part.n_sel, False)):
+        kept = set(select_union(hs, comb, T, P, B, R, k=k).tolist())
+        ev = np.arange(part.e_lo, part.e_hi)
+        union = set()
+        for g in range(G):
+            union |= set(ev[np.argsort(-hs[g, part.e_lo:part.e_hi], kind="stable")[:k]].tolist())
+        sel = kept - set(range(P)) - set(range(T - part.R, T))
+        assert len(sel) == part.n_sel
+        if len(union) <= part.n_sel:
+            assert union <= sel                       # short union: all of it is kept ...
+            rest = sorted(set(ev.tolist()) - union, key=lambda j: (-comb[j], j))
+            assert sel - union == set(rest[:part.n_sel - len(union)])   # ... topped up by combined score
+        else:
+            assert sel <= union                       # long union: the choice stays inside it
+            assert sel == set(sorted(union, key=lambda j: (-comb[j], j))[:part.n_sel])
+        if short:
+            assert len(union) < part.n_sel
+
+
+def test_union_hand_example():
+    # T=8, no prompt or window, B=3 -> n_sel=3; two heads, k=1 each
+    hs = np.array([[0, 5, 1, 0, 0, 0, 0, 0],
+                   [0, 0, 0, 0, 0, 0, 4, 0]], dtype=np.float64)
+    comb = np.array([0, 1, 9, 3, 0, 0, 2, 8], dtype=np.float64)
+    # union = {1, 6}; top-up by combined score from the rest: slot 2 (9)
+    assert select_union(hs, comb, 8, 0, 3, 0, k=1).tolist() == [1, 2, 6]
