@@ -11,12 +11,19 @@ package is a thin torch-tensor binding over it.
   kv_select_random  keep prompt + recent window + per-head uniform random keys
   kv_compact        gather kept K/V rows and positions contiguously
 
+and the policy variants:
+
+  kv_select_random_shared  one random keep-set shared by every head
+  kv_select_recent         keep the prompt and the latest slots
+  kv_compact_inplace       fill evicted slots with the kept rows beyond the new length
+
 The binding holds no arithmetic of its own and has no CPU fallback: without
 the built library every call raises.
 """
 from ._lib import KvError, library_path, load as load_library
-from .binding import (gqa_workspace_bytes, kv_compact, kv_select_random, kv_select_topk, tri_score, tri_score_gqa,
-                      tri_score_rotated)
+from .binding import (gqa_workspace_bytes, kv_compact, kv_compact_inplace, kv_select_random, kv_select_random_shared,
+                      kv_select_recent, kv_select_topk, tri_score, tri_score_gqa, tri_score_rotated)
 
-__all__ = ["tri_score", "tri_score_rotated", "tri_score_gqa", "gqa_workspace_bytes", "kv_select_topk", "kv_select_random", "kv_compact", "KvError", "library_path",
+__all__ = ["tri_score", "tri_score_rotated", "tri_score_gqa", "gqa_workspace_bytes", "kv_select_topk", "kv_select_random", "kv_compact",
+           "kv_select_random_shared", "kv_select_recent", "kv_compact_inplace", "KvError", "library_path",
            "load_library"]

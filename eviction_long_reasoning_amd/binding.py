@@ -220,6 +220,63 @@ def kv_select_random(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tens
     return kept, n_kept
 
 
+def kv_select_random_shared(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tensor,
+                            prompt_len: torch.Tensor, budget: int, recent: int, prompt_cap: int, seed: int,
+                            event: int, pos: Optional[torch.Tensor] = None, b_cap: Optional[int] = None,
+                            kept: Optional[torch.Tensor] = None, n_kept: Optional[torch.Tensor] = None
+                            ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The shared-draw control: every head keeps what layer 0 / KV head 0 would draw."""
+    L, S, H, t_cap = (int(x) for x in cache_shape)
+    dev = seq_len.device
+    b_cap = int(b_cap if b_cap is not None else max(budget, prompt_cap))
+    sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
+    pl = _dev_ptr(prompt_len, "prompt_len", torch.int32, (S,), dev)
+    pp = _dev_ptr(pos, "pos", torch.int32, (L, S, H, t_cap), dev)
+    kept, n_kept, kp, nkp = _select_io(L, S, H, b_cap, dev, kept, n_kept)
+    shape = _shape(L, S, H, 0, t_cap, 0, sp)
+    pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
+    st = _lib.load().kv_select_random_shared(ctypes.byref(shape), ctypes.byref(pol), pp, int(seed) & (2 ** 64 - 1),
+                                             int(event) & 0xFFFFFFFF, kp, b_cap, nkp, _stream(dev))
+    _lib.check("kv_select_random_shared", st)
+    return kept, n_kept
+
+
+def kv_select_recent(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tensor, prompt_len: torch.Tensor,
+                     budget: int, recent: int, prompt_cap: int, b_cap: Optional[int] = None,
+                     kept: Optional[torch.Tensor] = None, n_kept: Optional[torch.Tensor] = None
+                     ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Recency+prompt: the prompt and the latest slots of each head (no scores)."""
+    L, S, H, t_cap = (int(x) for x in cache_shape)
+    dev = seq_len.device
+    b_cap = int(b_cap if b_cap is not None else max(budget, prompt_cap))
+    sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
+    pl = _dev_ptr(prompt_len, "prompt_len", torch.int32, (S,), dev)
+    kept, n_kept, kp, nkp = _select_io(L, S, H, b_cap, dev, kept, n_kept)
+    shape = _shape(L, S, H, 0, t_cap, 0, sp)
+    pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
+    st = _lib.load().kv_select_recent(ctypes.byref(shape), ctypes.byref(pol), kp, b_cap, nkp, _stream(dev))
+    _lib.check("kv_select_recent", st)
+    return kept, n_kept
+
+
+def kv_compact_inplace(K: torch.Tensor, V: torch.Tensor, kept: torch.Tensor, n_kept: torch.Tensor,
+                       seq_len: torch.Tensor, pos: Optional[torch.Tensor] = None) -> None:
+    """In-place hole filling: afterwards slots 0..n_kept-1 of each head hold the kept rows."""
+    if K.dim() != 5 or K.dtype not in _DT or V.shape != K.shape or V.dtype != K.dtype:
+        raise ValueError("K and V must both be [L,S,H,t_cap,d] of the same float32/bfloat16 dtype")
+    L, S, H, t_cap, d = K.shape
+    dev = K.device
+    b_cap = kept.shape[-1]
+    kp_, vp_ = _dev_ptr(K, "K"), _dev_ptr(V, "V", None, None, dev)
+    kp = _dev_ptr(kept, "kept", torch.int32, (L, S, H, b_cap), dev)
+    nkp = _dev_ptr(n_kept, "n_kept", torch.int32, (S,), dev)
+    sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
+    pp = _dev_ptr(pos, "pos", torch.int32, (L, S, H, t_cap), dev)
+    shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
+    st = _lib.load().kv_compact_inplace(ctypes.byref(shape), kp_, vp_, pp, kp, int(b_cap), nkp, _stream(dev))
+    _lib.check("kv_compact_inplace", st)
+
+
 def kv_compact(K: torch.Tensor, V: torch.Tensor, kept: torch.Tensor, n_kept: torch.Tensor, seq_len: torch.Tensor,
                out_cap: int, pos: Optional[torch.Tensor] = None, with_pos: bool = True,
                K_out: Optional[torch.Tensor] = None, V_out: Optional[torch.Tensor] = None,

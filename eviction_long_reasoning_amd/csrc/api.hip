@@ -285,6 +285,65 @@ KV_EXPORT kv_status kv_select_random(const kv_shape *shape, const kv_policy *pol
   return hip_status(launch_select(p, true, static_cast<hipStream_t>(stream)));
 }
 
+KV_EXPORT kv_status kv_select_random_shared(const kv_shape *shape, const kv_policy *policy, const int32_t *pos,
+                                          uint64_t seed, uint32_t event, int32_t *kept, int32_t b_cap,
+                                          int32_t *n_kept, void *stream) {
+  SelectParams p{};
+  kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p);
+  if (st != KV_OK) return st;
+  p.pos = pos;
+  p.seed_lo = static_cast<uint32_t>(seed & 0xffffffffu);
+  p.seed_hi = static_cast<uint32_t>(seed >> 32);
+  p.event = event;
+  p.shared_draw = 1;
+  return hip_status(launch_select(p, true, static_cast<hipStream_t>(stream)));
+}
+
+KV_EXPORT kv_status kv_select_recent(const kv_shape *shape, const kv_policy *policy, int32_t *kept, int32_t b_cap,
+                                     int32_t *n_kept, void *stream) {
+  SelectParams p{};
+  kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p);
+  if (st != KV_OK) return st;
+  const long long blocks = static_cast<long long>(p.L) * p.S * p.H * ((b_cap + 255) / 256);
+  if (blocks >= (1ll << 31)) return KV_ESHAPE;
+  return hip_status(launch_select_recent(p, static_cast<hipStream_t>(stream)));
+}
+
+KV_EXPORT kv_status kv_compact_inplace(const kv_shape *shape, void *K, void *V, int32_t *pos, const int32_t *kept,
+                                       int32_t b_cap, const int32_t *n_kept, void *stream) {
+  kv_status st = check_shape(shape, true);
+  if (st != KV_OK) return st;
+  if (!K || !V || !kept || !n_kept) return KV_EINVAL;
+  if (b_cap < 1) return KV_EINVAL;
+  if (!aligned16(K) || !aligned16(V)) return KV_EINVAL;
+  const size_t heads = static_cast<size_t>(shape->n_layers) * shape->n_seq * shape->n_kv_heads;
+  const size_t row_bytes = static_cast<size_t>(shape->head_dim) * elem_bytes(shape);
+  const size_t bytes = heads * shape->t_cap * row_bytes;
+  if (overlaps(K, bytes, V, bytes)) return KV_EINVAL;
+  if (pos && (overlaps(pos, heads * shape->t_cap * 4, K, bytes) || overlaps(pos, heads * shape->t_cap * 4, V, bytes)))
+    return KV_EINVAL;
+
+  HoleParams p{};
+  p.K = static_cast<uint4 *>(K);
+  p.V = static_cast<uint4 *>(V);
+  p.pos = pos;
+  p.kept = kept;
+  p.n_kept = n_kept;
+  p.L = shape->n_layers;
+  p.S = shape->n_seq;
+  p.H = shape->n_kv_heads;
+  p.t_cap = shape->t_cap;
+  p.b_cap = b_cap;
+  p.row16 = static_cast<int32_t>(row_bytes / 16);
+  // movers per head are at most min(n_kept, T - n_kept) <= t_cap / 2; about 1024 of them per workgroup
+  const int max_movers = (b_cap < shape->t_cap / 2 ? b_cap : shape->t_cap / 2);
+  int wgs = (max_movers + 1023) / 1024;
+  p.wgs_per_head = wgs < 1 ? 1 : (wgs > 32 ? 32 : wgs);
+  const long long threads = static_cast<long long>(heads) * p.wgs_per_head * 256;
+  if (threads >= (1ll << 32)) return KV_ESHAPE;
+  return hip_status(launch_compact_holes(p, static_cast<hipStream_t>(stream)));
+}
+
 KV_EXPORT kv_status kv_compact(const kv_shape *shape, const void *K_in, const void *V_in, const int32_t *pos_in,
                                const int32_t *kept, int32_t b_cap, const int32_t *n_kept, void *K_out,
                                void *V_out, int32_t *pos_out, int32_t out_cap, void *stream) {

@@ -12,6 +12,12 @@
 // flight before storing. A workgroup owns a contiguous range of output rows of
 // one head, so stores are fully contiguous and loads are whole rows (kept
 // indices ascend, so neighbouring kept rows often share DRAM pages).
+//
+// Hole filling is the in-place alternative: only kept rows at or beyond the
+// new length move, each into an evicted slot below it, so a periodic eviction
+// that drops a few hundred rows per head moves a few hundred rows instead of
+// rewriting the whole cache. Slot order then stops being chronological and the
+// positions move with the rows.
 #include "kv_internal.hpp"
 
 namespace kvevict {
@@ -78,6 +84,53 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(const CompactP
   }
 }
 
+// In-place hole filling. With n = n_kept and kept ascending, the kept slots below n are the
+// prefix kept[0..r0) and the movers are the suffix kept[r0..n); the holes are the n - r0 slots
+// below n missing from the prefix. The i-th hole is i + #{r < r0 : kept[r] - r <= i} (kept[r] - r
+// counts the holes before kept[r] and never decreases). Movers are read only from slots >= n and
+// written only to slots < n, so no slot is both read and written.
+template <int G>
+__global__ __launch_bounds__(kCompactThreads) void holes_kernel(const HoleParams p) {
+  constexpr int ROWS_PER_PASS = kCompactThreads / G;
+  __shared__ int prefix;
+  const int head = blockIdx.x / p.wgs_per_head;
+  const int part = blockIdx.x - head * p.wgs_per_head;
+  const int s = (head / p.H) % p.S;
+  const int n = min(min(max(p.n_kept[s], 0), p.b_cap), p.t_cap);
+  const int32_t *kept = p.kept + static_cast<size_t>(head) * p.b_cap;
+  if (threadIdx.x == 0) {
+    int lo = 0, hi = n;  // first r with kept[r] >= n
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (kept[mid] < n) lo = mid + 1; else hi = mid;
+    }
+    prefix = lo;
+  }
+  __syncthreads();
+  const int r0 = prefix;
+  const int movers = n - r0;
+  const int c = threadIdx.x % G;
+  const int rr = threadIdx.x / G;
+  const size_t row0 = static_cast<size_t>(head) * p.t_cap;
+  for (int i = part * ROWS_PER_PASS + rr; i < movers; i += ROWS_PER_PASS * p.wgs_per_head) {
+    const int src = kept[r0 + i];
+    if (src < n || src >= p.t_cap) continue;   // not a mover (kept not ascending) or out of range
+    int lo = 0, hi = r0;                        // #{r < r0 : kept[r] - r <= i}
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (kept[mid] - mid <= i) lo = mid + 1; else hi = mid;
+    }
+    const int dst = i + lo;                     // < n
+    if (c < p.row16) {
+      const size_t so = (row0 + src) * p.row16 + c, dso = (row0 + dst) * p.row16 + c;
+      const uint4 k = ld_stream(p.K + so), v = ld_stream(p.V + so);
+      st_stream(p.K + dso, k);
+      st_stream(p.V + dso, v);
+    }
+    if (c == 0 && p.pos) p.pos[row0 + dst] = p.pos[row0 + src];
+  }
+}
+
 }  // namespace
 
 int compact_rows_per_wg(int group) { return (kCompactThreads / group) * kUnroll; }
@@ -97,6 +150,26 @@ hipError_t launch_compact(const CompactParams &p, hipStream_t st) {
     case 16: hipLaunchKernelGGL(compact_kernel<16>, grid, blk, 0, st, p); break;
     case 32: hipLaunchKernelGGL(compact_kernel<32>, grid, blk, 0, st, p); break;
     case 64: hipLaunchKernelGGL(compact_kernel<64>, grid, blk, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_holes(const HoleParams &p, hipStream_t st) {
+  int G = 1;
+  while (G < p.row16) G <<= 1;
+  if (G > 64) return hipErrorInvalidValue;
+  const long long blocks = static_cast<long long>(p.L) * p.S * p.H * p.wgs_per_head;
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(blocks)), blk(kCompactThreads);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(holes_kernel<1>, grid, blk, 0, st, p); break;
+    case 2: hipLaunchKernelGGL(holes_kernel<2>, grid, blk, 0, st, p); break;
+    case 4: hipLaunchKernelGGL(holes_kernel<4>, grid, blk, 0, st, p); break;
+    case 8: hipLaunchKernelGGL(holes_kernel<8>, grid, blk, 0, st, p); break;
+    case 16: hipLaunchKernelGGL(holes_kernel<16>, grid, blk, 0, st, p); break;
+    case 32: hipLaunchKernelGGL(holes_kernel<32>, grid, blk, 0, st, p); break;
+    case 64: hipLaunchKernelGGL(holes_kernel<64>, grid, blk, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

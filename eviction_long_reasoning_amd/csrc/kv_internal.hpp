@@ -85,10 +85,12 @@ struct SelectParams {
   int32_t L, S, H, t_cap, b_cap;
   int32_t budget, recent, prompt_cap;
   uint32_t seed_lo, seed_hi, event;
+  int32_t shared_draw;      // random: every (layer, head) draws as layer 0 / head 0
 };
 
 constexpr int kSelectMaxSlots = 65536;
 hipError_t launch_select(const SelectParams &p, bool random, hipStream_t st);
+hipError_t launch_select_recent(const SelectParams &p, hipStream_t st);
 
 // -------------------------------------------------------------- compact ----
 struct CompactParams {
@@ -105,5 +107,18 @@ struct CompactParams {
 
 int compact_rows_per_wg(int group);  // output rows per compact workgroup for a lane-group size
 hipError_t launch_compact(const CompactParams &p, hipStream_t st);
+
+// In-place hole filling: kept rows at or beyond n_kept move into evicted slots below it.
+struct HoleParams {
+  uint4 *K, *V;               // [L,S,H,t_cap] rows of row16 x 16 B, updated in place
+  int32_t *pos;               // [L,S,H,t_cap] or nullptr
+  const int32_t *kept;        // [L,S,H,b_cap], ascending
+  const int32_t *n_kept;      // [S]
+  int32_t L, S, H, t_cap, b_cap;
+  int32_t row16;
+  int32_t wgs_per_head;
+};
+
+hipError_t launch_compact_holes(const HoleParams &p, hipStream_t st);
 
 }  // namespace kvevict

@@ -244,7 +244,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
       }
     }
   } else {
-    const uint32_t c1 = (static_cast<uint32_t>(l) << 16) | static_cast<uint32_t>(h);
+    const uint32_t c1 = p.shared_draw ? 0u : (static_cast<uint32_t>(l) << 16) | static_cast<uint32_t>(h);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int j = 4 * ((i >> 2) * NT + tid) + (i & 3);
@@ -404,6 +404,26 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   if (writer) p.n_kept[s] = n_kept;
 }
 
+// Recency+prompt ("Random Attention", section 4.1, the StreamingLLM-style diagnostic): the
+// prompt and the n_kept - P latest slots, i.e. the evictable range's n_sel latest slots joined to
+// the recent window. No scores are read; one thread per output entry.
+__global__ __launch_bounds__(256) void recent_kernel(const SelectParams p, int chunks) {
+  const int head = blockIdx.x / chunks;
+  const int r = (blockIdx.x - head * chunks) * 256 + static_cast<int>(threadIdx.x);
+  const int h = head % p.H;
+  const int s = (head / p.H) % p.S;
+  const int l = head / (p.H * p.S);
+  const int T = min(max(p.seq_len[s], 0), p.t_cap);
+  const int P = min(max(p.prompt_len[s], 0), min(p.prompt_cap, T));
+  const bool compress = T > p.budget;
+  const int n_kept = compress ? max(p.budget, P) : T;
+  if (r == 0 && l == 0 && h == 0) p.n_kept[s] = n_kept;
+  if (r >= p.b_cap) return;
+  int v = -1;
+  if (r < n_kept) v = (!compress || r < P) ? r : T - (n_kept - r);
+  p.kept[static_cast<size_t>(head) * p.b_cap + r] = v;
+}
+
 template <int NT, int KPT>
 hipError_t launch_cfg(const SelectParams &p, bool random, dim3 grid, hipStream_t st) {
   const bool vec = (p.t_cap % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.scores) & 15u) == 0);
@@ -417,6 +437,14 @@ hipError_t launch_cfg(const SelectParams &p, bool random, dim3 grid, hipStream_t
 }
 
 }  // namespace
+
+hipError_t launch_select_recent(const SelectParams &p, hipStream_t st) {
+  const long long heads = static_cast<long long>(p.L) * p.S * p.H;
+  const int chunks = (p.b_cap + 255) / 256;
+  if (heads <= 0) return hipSuccess;
+  hipLaunchKernelGGL(recent_kernel, dim3(static_cast<unsigned>(heads * chunks)), dim3(256), 0, st, p, chunks);
+  return hipGetLastError();
+}
 
 hipError_t launch_select(const SelectParams &p, bool random, hipStream_t st) {
   const long long heads = static_cast<long long>(p.L) * p.S * p.H;

@@ -11,6 +11,12 @@
  *   kv_select_random keep prompt + recent window + uniformly random keys
  *   kv_compact       gather the kept K/V rows (and positions) contiguously
  *
+ * and the policy variants the pages use as controls or alternatives:
+ *
+ *   kv_select_random_shared  one random keep-set shared by every head
+ *   kv_select_recent         keep the prompt and the latest slots (no scores)
+ *   kv_compact_inplace       fill evicted slots with the kept rows beyond the new length
+ *
  * Conventions shared by every call
  * --------------------------------
  *  - All array arguments are DEVICE pointers owned by the caller, except
@@ -256,6 +262,51 @@ kv_status kv_select_random(const kv_shape *shape, const kv_policy *policy,
                            const int32_t *pos, uint64_t seed, uint32_t event,
                            int32_t *kept, int32_t b_cap, int32_t *n_kept,
                            void *stream);
+
+/*
+ * kv_select_random_shared -- the shared-draw control of [RA] sections 5.2-5.3:
+ * one random keep-set that every (layer, KV head) of a sequence uses. It is
+ * kv_select_random with the counter's second word fixed to 0, i.e. every head
+ * draws what layer 0 / KV head 0 draws. Heads whose position arrays agree keep
+ * the same slots. Arguments as for kv_select_random.
+ */
+kv_status kv_select_random_shared(const kv_shape *shape, const kv_policy *policy,
+                                  const int32_t *pos, uint64_t seed, uint32_t event,
+                                  int32_t *kept, int32_t b_cap, int32_t *n_kept,
+                                  void *stream);
+
+/*
+ * kv_select_recent -- recency+prompt ([RA] section 4.1, the StreamingLLM-style
+ * diagnostic): keep the prompt and fill the rest of the budget with the
+ * contiguous latest slots. With the partition above, kept = [0, P) followed by
+ * [T - (n_kept - P), T) (the evictable range's n_sel latest slots joined to the
+ * recent window); slot order is taken as time order. No scores are read.
+ * kept, b_cap, n_kept as for kv_select_topk (no t_cap limit beyond it).
+ */
+kv_status kv_select_recent(const kv_shape *shape, const kv_policy *policy,
+                           int32_t *kept, int32_t b_cap, int32_t *n_kept, void *stream);
+
+/*
+ * kv_compact_inplace -- in-place hole filling: the engine compaction of [RA]
+ * Appendix F without the copy of the whole cache. With n = n_kept[s] and kept
+ * ascending (as the selectors write it), the kept rows below n stay where they
+ * are and the i-th kept row at or beyond n (in slot order) moves into the i-th
+ * evicted slot below n. Afterwards slots 0..n-1 of every head hold exactly the
+ * kept rows, in an order that is no longer chronological; pos (if given) moves
+ * with the rows, so later scoring and random draws use the true positions.
+ * Slots >= n are left as they were. With a recent window of R slots, slot
+ * order keeps naming the latest R tokens only while at least R tokens are
+ * appended between evictions.
+ *
+ *  K, V     device [L,S,H,t_cap,d] (shape->dtype), updated in place.
+ *  pos      device [L,S,H,t_cap] int32 updated in place, or NULL.
+ *  kept     device [L,S,H,b_cap] int32, ascending (kept indices that do not
+ *           ascend give unspecified rows, never an out-of-range access).
+ *  n_kept   device [S] int32.
+ */
+kv_status kv_compact_inplace(const kv_shape *shape, void *K, void *V, int32_t *pos,
+                             const int32_t *kept, int32_t b_cap, const int32_t *n_kept,
+                             void *stream);
 
 /*
  * kv_compact -- gather kept rows into a contiguous per-head layout.

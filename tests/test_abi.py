@@ -77,6 +77,7 @@ def test_host_validation_rejects_bad_arguments(lib):
     pg = L.KvPaged(dummy, 1, 8, 4)        # 1 block of 8 cannot hold t_cap = 16 slots
     assert lib.tri_score_rotated(ctypes.byref(sh), dummy, ctypes.byref(pg), 0, dummy, None, dummy, 1e4, arr, 1,
                                  dummy, None) == L.KV_ESHAPE
+    big = L.KvShape(1, 1, 1, 8, 65537, L.KV_BF16, seq)
     # grouped-query scores: group outside 1..8, workspace too small, head_dim beyond 128 (bf16)
     shg = L.KvShape(2, 3, 4, 128, 1000, L.KV_BF16, None)
     need = lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg), 4)
@@ -99,12 +100,25 @@ def test_host_validation_rejects_bad_arguments(lib):
     need256 = lib.kv_score_gqa_workspace_bytes(ctypes.byref(sh256), 2)
     assert lib.tri_score_gqa(ctypes.byref(sh256), dummy, None, 2, dummy, None, dummy, 1e4, arr, 1, hs, sc, ws,
                              need256, None) == L.KV_ESHAPE
+    # policy variants: the recency selector and the shared draw validate like the others;
+    # in-place compaction refuses K and V that overlap, and positions overlapping either
+    pol = L.KvPolicy(8, 2, 4, seq)
+    assert lib.kv_select_recent(ctypes.byref(sh), ctypes.byref(pol), dummy, 7, dummy, None) == L.KV_ESHAPE
+    assert lib.kv_select_recent(ctypes.byref(sh), None, dummy, 8, dummy, None) == L.KV_EINVAL
+    assert lib.kv_select_random_shared(ctypes.byref(big), ctypes.byref(pol), None, 1, 0, dummy, 8, dummy,
+                                       None) == L.KV_ESHAPE
+    a = ctypes.c_void_p(0x100000)
+    assert lib.kv_compact_inplace(ctypes.byref(sh), a, ctypes.c_void_p(0x100010), None, dummy, 8, dummy,
+                                  None) == L.KV_EINVAL
+    assert lib.kv_compact_inplace(ctypes.byref(sh), a, ctypes.c_void_p(0x200000), ctypes.c_void_p(0x100000), dummy, 8,
+                                  dummy, None) == L.KV_EINVAL
+    assert lib.kv_compact_inplace(ctypes.byref(sh), a, ctypes.c_void_p(0x200008), None, dummy, 8, dummy,
+                                  None) == L.KV_EINVAL       # V not 16-byte aligned
     # selector: b_cap below budget or prompt cap, t_cap above the supported maximum, budget < 1
     pol = L.KvPolicy(8, 2, 4, seq)
     assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 7, dummy, None) == L.KV_ESHAPE
     pol = L.KvPolicy(8, 2, 12, seq)
     assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 8, dummy, None) == L.KV_ESHAPE
-    big = L.KvShape(1, 1, 1, 8, 65537, L.KV_BF16, seq)
     pol = L.KvPolicy(8, 2, 4, seq)
     assert lib.kv_select_random(ctypes.byref(big), ctypes.byref(pol), None, 1, 0, dummy, 8, dummy, None) == L.KV_ESHAPE
     pol = L.KvPolicy(0, 2, 4, seq)

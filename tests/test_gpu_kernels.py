@@ -444,3 +444,93 @@ def test_compact_skips_out_of_range_indices():
     Ko, Po = Ko.cpu().numpy(), Po.cpu().numpy()
     assert Po[0, 0, 0].tolist() == [0, -3, 63, -3, -3, 5]
     assert np.all(Ko[0, 0, 0, 1] == -3.0) and np.all(Ko[0, 0, 0, 2] == np.arange(63 * d, 64 * d))
+
+
+# -------------------------------------------------------------- policy variants ----
+@pytest.mark.parametrize("case", SELECT_CASES[:6] + SELECT_CASES[8:12], ids=[c[0] for c in SELECT_CASES[:6] + SELECT_CASES[8:12]])
+def test_select_recent_bit_exact(case):
+    name, t_cap, Ts, Ps, B, R, _ = case
+    log(f"[recent] {name}")
+    L, H = 2, 3
+    S = len(Ts)
+    pcap = max(Ps)
+    b_cap = max(B, pcap) + 5
+    kept, nk = kv.kv_select_recent((L, S, H, t_cap), _i32(Ts), _i32(Ps), B, R, pcap, b_cap=b_cap)
+    kept, nk = kept.cpu().numpy(), nk.cpu().numpy()
+    for s in range(S):
+        ref = oracle.select_recent(Ts[s], Ps[s], B, R)
+        assert nk[s] == ref.size
+        for l in range(L):
+            for h in range(H):
+                assert np.array_equal(kept[l, s, h, :ref.size], ref), f"{name} l{l} s{s} h{h}"
+                assert np.all(kept[l, s, h, ref.size:] == -1)
+
+
+@pytest.mark.parametrize("with_pos", [False, True])
+def test_select_random_shared_bit_exact(with_pos):
+    L, S, H, t_cap = 3, 2, 4, 5000
+    Ts, Ps, B, R = [5000, 3100], [200, 0], 1500, 64
+    seed, event = 0x1234567890ABCDEF, 12
+    pos = None
+    if with_pos:
+        r = rng(511, 0)
+        pos = np.sort(r.integers(0, 2 ** 31 - 1, (L, S, H, t_cap)), axis=-1).astype(np.int32)
+        pos[:, :, 1] = pos[:, :, 0]           # heads 0 and 1 share positions, the others do not
+    kept, nk = kv.kv_select_random_shared((L, S, H, t_cap), _i32(Ts), _i32(Ps), B, R, max(Ps), seed, event,
+                                          pos=None if pos is None else _i32(pos))
+    kept, nk = kept.cpu().numpy(), nk.cpu().numpy()
+    for s in range(S):
+        for l in range(L):
+            for h in range(H):
+                p = None if pos is None else pos[l, s, h]
+                ref = oracle.select_random_shared(Ts[s], Ps[s], B, R, p, seed, event, s)
+                assert nk[s] == ref.size
+                assert np.array_equal(kept[l, s, h, :ref.size], ref), f"shared l{l} s{s} h{h}"
+        if pos is None:
+            assert np.all(kept[:, s] == kept[0, s, 0][None, None])      # one keep-set for every head
+        else:
+            assert np.array_equal(kept[:, s, 0], kept[:, s, 1])
+
+
+HOLE_CASES = [
+    # name, dtype, d, L, S, H, t_cap, T per seq, B, R, with pos
+    ("holes-bf16-d64-periodic", "bf16", 64, 2, 3, 2, 2176, [2176, 2100, 900], 2048, 128, True),
+    ("holes-bf16-d128-deep", "bf16", 128, 1, 2, 2, 9000, [9000, 4000], 3072, 128, True),
+    ("holes-fp32-d8-nopos", "f32", 8, 1, 1, 3, 700, [700], 200, 0, False),
+    ("holes-bf16-d96", "bf16", 96, 1, 2, 1, 1500, [1500, 1499], 1000, 16, True),
+]
+
+
+@pytest.mark.parametrize("case", HOLE_CASES, ids=[c[0] for c in HOLE_CASES])
+def test_compact_inplace_bit_exact(case):
+    name, dtype, d, L, S, H, t_cap, Ts, B, R, with_pos = case
+    log(f"[holes] {name}")
+    r = rng(525, d, t_cap)
+    Kf = r.standard_normal((L, S, H, t_cap, d)).astype(np.float32)
+    Vf = r.standard_normal((L, S, H, t_cap, d)).astype(np.float32)
+    Kd, Vd = _to_dev_keys(Kf, dtype), _to_dev_keys(Vf, dtype)
+    Kh, Vh = _host_keys(Kd, dtype), _host_keys(Vd, dtype)
+    pos = np.sort(r.integers(0, 10 ** 6, (L, S, H, t_cap)), axis=-1).astype(np.int32) if with_pos else None
+    Ps = [min(64, T) for T in Ts]
+    kept, nk = kv.kv_select_random((L, S, H, t_cap), _i32(Ts), _i32(Ps), B, R, max(Ps), 5, 3,
+                                   pos=None if pos is None else _i32(pos))
+    pd = None if pos is None else _i32(pos)
+    kv.kv_compact_inplace(Kd, Vd, kept, nk, _i32(Ts), pos=pd)
+    Ko, Vo = _host_keys(Kd, dtype), _host_keys(Vd, dtype)
+    Po = None if pd is None else pd.cpu().numpy()
+    kh, nkh = kept.cpu().numpy(), nk.cpu().numpy()
+    moved = 0
+    for l in range(L):
+        for s in range(S):
+            for h in range(H):
+                n = int(nkh[s])
+                T = Ts[s]
+                p = None if pos is None else pos[l, s, h, :T]
+                rk, rv, rp, moves = oracle.compact_holes(Kh[l, s, h, :T], Vh[l, s, h, :T], p, kh[l, s, h, :n])
+                moved += len(moves)
+                assert np.array_equal(Ko[l, s, h, :n], rk) and np.array_equal(Vo[l, s, h, :n], rv), f"{name} {l}{s}{h}"
+                if Po is not None:
+                    assert np.array_equal(Po[l, s, h, :n], rp)
+                    assert np.array_equal(Po[l, s, h, n:], pos[l, s, h, n:])
+                assert np.array_equal(Ko[l, s, h, n:], Kh[l, s, h, n:])     # slots >= n untouched
+    log(f"[holes] {name}: {moved} rows moved")

@@ -156,6 +156,28 @@ def test_workload2_full_score_with_norm_term():
     log(f"[w2+norm] 8 heads: worst scaled score error {worst:.2e}, kept differences {diffs}")
 
 
+def test_workload2_prefill_compression():
+    # the TriAttention engine option that lets prefill tokens compete too: prompt_len = 0, so the
+    # whole cache outside the recent window is scored and selected
+    w = workload(2)
+    K, V, _, qb = kv_numpy(w)
+    Kd = dev_from_host(K, w.dtype)
+    T = w.seq_len
+    P0 = np.zeros_like(w.prompt_len)
+    sc = kv.tri_score(Kd, torch.from_numpy(qb).to(DEV), i32(w.t_cur), i32(T), w.theta, w.deltas)
+    kept, nk = kv.kv_select_topk(sc, i32(T), i32(P0), w.budget, w.recent, 0)
+    assert int(nk[0]) == w.budget
+    sch, kh = sc.cpu().numpy(), kept.cpu().numpy()
+    diffs, low = 0, 0
+    for h in range(w.n_kv_heads):
+        ref = oracle.score_literal(keys_f64(K[0, 0, h], w.dtype), None, qb[0, h], int(w.t_cur[0]), w.theta, w.deltas)
+        rk = oracle.select_topk(ref, int(T[0]), 0, w.budget, w.recent)
+        diffs += assert_selection_near_threshold(kh[0, 0, h, :w.budget], rk, ref, int(T[0]), 0, w.budget, w.recent,
+                                                 f"w2-prefill h{h}")
+        low += int(np.sum(kh[0, 0, h, :w.budget] < int(w.prompt_len[0])))
+    log(f"[w2-prefill] 8 heads: kept differences {diffs}; slots kept from the former prompt range {low}")
+
+
 def test_workload2_gqa_zscore_max():
     # the GQA rule on the Qwen3-8B-shaped layer: 4 query heads per KV head, each with its own
     # centre, z-normalised per query head over the 32768 keys, max over the group; with and
@@ -294,11 +316,13 @@ class _OracleHead:
         self.pos = np.concatenate([self.pos, pn.astype(np.int32)])
 
 
-@pytest.mark.parametrize("mode", ["scored", "random", "gqa"])
+@pytest.mark.parametrize("mode", ["scored", "random", "gqa", "random-inplace"])
 def test_workload4_periodic_events(mode):
-    # gqa: the z-score + max rule over the 8 query heads of each KV head, first 64 events
+    # gqa: the z-score + max rule over the 8 query heads of each KV head, first 64 events;
+    # random-inplace: random eviction with in-place hole filling instead of the gather
     w = workload(4)
     n_events = 64 if mode == "gqa" else w.n_events
+    inplace = mode == "random-inplace"
     L, S, H, Tc, d = w.n_layers, w.n_seq, w.n_kv_heads, w.t_cap, w.head_dim
     P = w.prompt_len.astype(np.int64)
     mu0, qb, dr = centres(w)
@@ -343,16 +367,20 @@ def test_workload4_periodic_events(mode):
         else:
             kept, nk = kv.kv_select_random((L, S, H, Tc), seq, i32(P), w.budget, w.recent, w.prompt_cap(),
                                            w.seed_random, ev, pos=Pc)
-        Ko, Vo, Po = bufs[1 - cur]
-        kv.kv_compact(Kc, Vc, kept, nk, seq, Tc, pos=Pc, K_out=Ko, V_out=Vo, pos_out=Po)
-        if ev in (1, 2, 64, 256) or ev % 32 == 0:
+        if inplace:
+            kv.kv_compact_inplace(Kc, Vc, kept, nk, seq, pos=Pc)
+            Ko, Vo, Po = Kc, Vc, Pc
+        else:
+            Ko, Vo, Po = bufs[1 - cur]
+            kv.kv_compact(Kc, Vc, kept, nk, seq, Tc, pos=Pc, K_out=Ko, V_out=Vo, pos_out=Po)
+        if not inplace and (ev in (1, 2, 64, 256) or ev % 32 == 0):
             check_structure(w, kept, nk, Kc, Ko, Po, T, P, f"w4-{mode} ev{ev}", pos_in=Pc)
         nk_h = nk.cpu().numpy()
         for k in sampled:
             l, s, h = k
             o = ora[k]
             Tn = int(T[s])
-            if mode == "random":
+            if mode.startswith("random"):
                 rk = oracle.select_random(Tn, int(P[s]), w.budget, w.recent, o.pos, w.seed_random, ev, l, h, s)
                 gk = kept[l, s, h, :int(nk_h[s])].cpu().numpy()
                 assert np.array_equal(gk, rk), (ev, k)
@@ -376,17 +404,21 @@ def test_workload4_periodic_events(mode):
                     if nd:
                         near += nd
                         diverged.add(k)   # the trajectories legitimately part here
-            if k in diverged and mode != "random":
+            if k in diverged and not mode.startswith("random"):
                 continue
-            rK, rV, rP = oracle.compact(o.K, o.V, o.pos, rk)
+            if inplace:
+                rK, rV, rP, _ = oracle.compact_holes(o.K, o.V, o.pos, rk)
+            else:
+                rK, rV, rP = oracle.compact(o.K, o.V, o.pos, rk)
             n = rk.size
             assert np.array_equal(host_bits(Ko[l, s, h, :n]), rK) and np.array_equal(host_bits(Vo[l, s, h, :n]), rV)
             assert np.array_equal(Po[l, s, h, :n].cpu().numpy(), rP), (ev, k)
             o.K, o.V, o.pos = rK, rV, rP
         T = nk_h.astype(np.int64)
-        cur = 1 - cur
+        if not inplace:
+            cur = 1 - cur
         if ev % 32 == 0:
             log(f"[w4-{mode}] event {ev}/{n_events}: cache {int(T.min())}..{int(T.max())} per head")
-    if mode != "random":
+    if not mode.startswith("random"):
         log(f"[w4-{mode}] {compared} head-events compared, worst scaled error {worst:.2e}, "
             f"near-threshold swaps {near}, diverged heads {len(diverged)}")
