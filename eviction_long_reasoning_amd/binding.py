@@ -220,6 +220,33 @@ def kv_select_random(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tens
     return kept, n_kept
 
 
+def kv_select_union(head_scores: torch.Tensor, scores: torch.Tensor, seq_len: torch.Tensor,
+                    prompt_len: torch.Tensor, budget: int, recent: int, prompt_cap: int, k_per_head: int = 0,
+                    b_cap: Optional[int] = None, kept: Optional[torch.Tensor] = None,
+                    n_kept: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Union of the per-query-head top-k sets, final choice by the combined score.
+
+    ``head_scores`` is [L,S,H,G,t_cap] and ``scores`` (the combined score) [L,S,H,t_cap], both
+    fp32, as ``tri_score_gqa`` returns them; ``k_per_head`` <= 0 means ceil(n_sel / G).
+    """
+    if head_scores.dim() != 5 or scores.dim() != 4:
+        raise ValueError("head_scores must be [L,S,H,G,t_cap] and scores [L,S,H,t_cap]")
+    L, S, H, G, t_cap = head_scores.shape
+    dev = scores.device
+    b_cap = int(b_cap if b_cap is not None else max(budget, prompt_cap))
+    hp = _dev_ptr(head_scores, "head_scores", torch.float32, (L, S, H, G, t_cap), dev)
+    cp = _dev_ptr(scores, "scores", torch.float32, (L, S, H, t_cap), dev)
+    sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
+    pl = _dev_ptr(prompt_len, "prompt_len", torch.int32, (S,), dev)
+    kept, n_kept, kp, nkp = _select_io(L, S, H, b_cap, dev, kept, n_kept)
+    shape = _shape(L, S, H, 0, t_cap, 0, sp)
+    pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
+    st = _lib.load().kv_select_union(ctypes.byref(shape), ctypes.byref(pol), int(G), int(k_per_head), hp, cp, kp,
+                                     b_cap, nkp, _stream(dev))
+    _lib.check("kv_select_union", st)
+    return kept, n_kept
+
+
 def kv_select_random_shared(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tensor,
                             prompt_len: torch.Tensor, budget: int, recent: int, prompt_cap: int, seed: int,
                             event: int, pos: Optional[torch.Tensor] = None, b_cap: Optional[int] = None,

@@ -269,7 +269,7 @@ KV_EXPORT kv_status kv_select_topk(const kv_shape *shape, const kv_policy *polic
   if (st != KV_OK) return st;
   if (!scores) return KV_EINVAL;
   p.scores = scores;
-  return hip_status(launch_select(p, false, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_select(p, SelectKind::kTopk, static_cast<hipStream_t>(stream)));
 }
 
 KV_EXPORT kv_status kv_select_random(const kv_shape *shape, const kv_policy *policy, const int32_t *pos,
@@ -282,7 +282,22 @@ KV_EXPORT kv_status kv_select_random(const kv_shape *shape, const kv_policy *pol
   p.seed_lo = static_cast<uint32_t>(seed & 0xffffffffu);
   p.seed_hi = static_cast<uint32_t>(seed >> 32);
   p.event = event;
-  return hip_status(launch_select(p, true, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_select(p, SelectKind::kRandom, static_cast<hipStream_t>(stream)));
+}
+
+KV_EXPORT kv_status kv_select_union(const kv_shape *shape, const kv_policy *policy, int32_t group,
+                                    int32_t k_per_head, const float *head_scores, const float *scores,
+                                    int32_t *kept, int32_t b_cap, int32_t *n_kept, void *stream) {
+  SelectParams p{};
+  kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p);
+  if (st != KV_OK) return st;
+  if (!head_scores || !scores) return KV_EINVAL;
+  if (group < 1 || group > 64) return KV_EINVAL;
+  p.scores = scores;
+  p.head_scores = head_scores;
+  p.G = group;
+  p.k_per_head = k_per_head;
+  return hip_status(launch_select(p, SelectKind::kUnion, static_cast<hipStream_t>(stream)));
 }
 
 KV_EXPORT kv_status kv_select_random_shared(const kv_shape *shape, const kv_policy *policy, const int32_t *pos,
@@ -296,7 +311,7 @@ KV_EXPORT kv_status kv_select_random_shared(const kv_shape *shape, const kv_poli
   p.seed_hi = static_cast<uint32_t>(seed >> 32);
   p.event = event;
   p.shared_draw = 1;
-  return hip_status(launch_select(p, true, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_select(p, SelectKind::kRandom, static_cast<hipStream_t>(stream)));
 }
 
 KV_EXPORT kv_status kv_select_recent(const kv_shape *shape, const kv_policy *policy, int32_t *kept, int32_t b_cap,

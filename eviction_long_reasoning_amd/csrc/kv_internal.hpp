@@ -86,10 +86,14 @@ struct SelectParams {
   int32_t budget, recent, prompt_cap;
   uint32_t seed_lo, seed_hi, event;
   int32_t shared_draw;      // random: every (layer, head) draws as layer 0 / head 0
+  const float *head_scores; // union: [L,S,H,G,t_cap] per-query-head scores (scores = combined)
+  int32_t G, k_per_head;    // union: query heads per KV head; per-head top-k (<= 0: ceil(n_sel / G))
 };
 
+enum class SelectKind { kTopk, kRandom, kUnion };
+
 constexpr int kSelectMaxSlots = 65536;
-hipError_t launch_select(const SelectParams &p, bool random, hipStream_t st);
+hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st);
 hipError_t launch_select_recent(const SelectParams &p, hipStream_t st);
 
 // -------------------------------------------------------------- compact ----

@@ -7,7 +7,8 @@
 // 2: a recent buffer that is never scored, top-K of the candidates, Eq. 2;
 // section 3: the prompt is never evicted, and each candidate gets an i.i.d.
 // uniform score drawn per KV head at every eviction, Eq. 3 / Algorithm 1;
-// Appendix F: keep-sets sorted chronologically).
+// Appendix F: keep-sets sorted chronologically) and "TriAttention" (blog
+// walkthrough, eviction step: union-based selection over per-head top-k sets).
 //
 // One workgroup owns one (layer, seq, KV head). Its T slot keys live in
 // registers; thread t holds, for each round i, the four consecutive slots
@@ -187,12 +188,21 @@ __device__ __forceinline__ void wave_exclusive_scan_lds(uint32_t *a, int n, int 
   }
 }
 
-// VEC (top-k only): every head's score row is 16-byte aligned and t_cap is a multiple of 4, so
+// The three rankings share one kernel body. KIND 0 (top-k): keys are the fp32 scores. KIND 1
+// (random): keys are Philox words. KIND 2 (union, "TriAttention" blog, eviction step): G + 1
+// passes over the same registers -- pass g < G ranks the evictable slots by query head g's own
+// score and adds its top-k to a per-thread union bit mask; the last pass ranks by the combined
+// score, inside the union when it holds at least n_sel slots, otherwise over the rest of the
+// evictable range with the whole union kept. Every pass is a threshold search (steps 2-3) and an
+// ordered scan (step 4); top-k and random run exactly one pass.
+//
+// VEC (score keys only): every score row is 16-byte aligned and t_cap is a multiple of 4, so
 // each round is one float4 load per lane (slots past T are loaded but never used).
-template <int NT, int KPT, bool RANDOM, bool VEC>
+template <int NT, int KPT, int KIND, bool VEC>
 __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   constexpr int NW = NT / 64;
   constexpr int R = KPT / 4;   // rounds of four consecutive slots per thread
+  constexpr bool RANDOM = KIND == 1, UNION = KIND == 2;
   __shared__ uint32_t hist[kValueBins];
   __shared__ uint32_t red[2 * NW];
   __shared__ uint32_t tot_a[R * NW];   // per (round, wave): slots kept unconditionally
@@ -223,39 +233,6 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   const int n_kept = max(B, P);
   const int n_cand = e_hi - e_lo;
 
-  // ---- 1. keys: key[4*i + q] belongs to slot 4*(i*NT + tid) + q
-  uint32_t key[KPT];
-  const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
-  if (!RANDOM) {
-    const float *row = p.scores + slot0;
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int j4 = 4 * (i * NT + tid);
-      if (VEC) {
-        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (j4 < p.t_cap) f = *reinterpret_cast<const float4 *>(row + j4);
-        key[4 * i] = order_key(f.x);
-        key[4 * i + 1] = order_key(f.y);
-        key[4 * i + 2] = order_key(f.z);
-        key[4 * i + 3] = order_key(f.w);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) key[4 * i + q] = (j4 + q < T) ? order_key(row[j4 + q]) : 0u;
-      }
-    }
-  } else {
-    const uint32_t c1 = p.shared_draw ? 0u : (static_cast<uint32_t>(l) << 16) | static_cast<uint32_t>(h);
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int j = 4 * ((i >> 2) * NT + tid) + (i & 3);
-      uint32_t k = 0u;
-      if (j >= e_lo && j < e_hi) {
-        const uint32_t c0 = p.pos ? static_cast<uint32_t>(p.pos[slot0 + j]) : static_cast<uint32_t>(j);
-        k = philox_word0(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
-      }
-      key[i] = k;
-    }
-  }
   auto slot_of = [&](int i) { return 4 * ((i >> 2) * NT + tid) + (i & 3); };
   uint64_t cand = 0ull;  // bit i: key[i] is an evictable candidate
 #pragma unroll
@@ -263,142 +240,218 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
     const int j = slot_of(i);
     cand |= static_cast<uint64_t>(j >= e_lo && j < e_hi) << i;
   }
+  const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
+  const int passes = UNION ? (n_sel > 0 ? p.G : 0) + 1 : 1;
+  const int k_head = UNION ? (p.k_per_head > 0 ? p.k_per_head : (n_sel + p.G - 1) / p.G) : 0;
+  uint64_t umask = 0ull;    // union: slots some query head ranks in its top-k
 
-  // ---- 2./3. threshold: thr = n_sel-th largest candidate key; take `need` of the keys == thr
-  // mode: 0 = select none, 1 = select all candidates, 2 = threshold rule
-  int mode;
-  uint32_t thr = 0u, need = 0u;
-  if (n_sel == 0 || n_cand <= 0) {
-    mode = 0;
-  } else if (n_sel >= n_cand) {
-    mode = 1;
-  } else {
-    mode = 2;
-    uint32_t remaining = static_cast<uint32_t>(n_sel);
-    uint64_t mem = cand;  // keys the exact radix passes still have to order
+  uint32_t key[KPT];
+#pragma unroll 1
+  for (int pass = 0; pass < passes; ++pass) {
+    const bool last = pass == passes - 1;
+    // ---- 1. keys: key[4*i + q] belongs to slot 4*(i*NT + tid) + q
     if (!RANDOM) {
-      // Pass 1 (scores): 1024 bins uniform in value between the smallest and largest finite
-      // candidate. The binning is monotone, so the threshold lies in one bin and every key in a
-      // higher bin is strictly larger; the exact passes then only see that bin's keys. Binning by
-      // value keeps a concentrated score distribution from piling into a few radix bins.
-      uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+      const float *row = p.scores + slot0;
+      if (UNION && !last) row = p.head_scores + (static_cast<size_t>(head) * p.G + pass) * p.t_cap;
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int j4 = 4 * (i * NT + tid);
+        if (VEC) {
+          float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (j4 < p.t_cap) f = *reinterpret_cast<const float4 *>(row + j4);
+          key[4 * i] = order_key(f.x);
+          key[4 * i + 1] = order_key(f.y);
+          key[4 * i + 2] = order_key(f.z);
+          key[4 * i + 3] = order_key(f.w);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) key[4 * i + q] = (j4 + q < T) ? order_key(row[j4 + q]) : 0u;
+        }
+      }
+    } else {
+      const uint32_t c1 = p.shared_draw ? 0u : (static_cast<uint32_t>(l) << 16) | static_cast<uint32_t>(h);
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
-        if (((cand >> i) & 1ull) && key[i] > kKeyNegInf && key[i] < kKeyPosInf) {
-          kmn = min(kmn, key[i]);
-          kmx = max(kmx, key[i]);
+        const int j = slot_of(i);
+        uint32_t k = 0u;
+        if (j >= e_lo && j < e_hi) {
+          const uint32_t c0 = p.pos ? static_cast<uint32_t>(p.pos[slot0 + j]) : static_cast<uint32_t>(j);
+          k = philox_word0(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
         }
-      }
-      block_min_max<NT>(kmn, kmx, red);
-      const float fmin = key_value(kmn), fmax = key_value(kmx);
-      const float scale = static_cast<float>(kValueBins) / (fmax - fmin);
-      if (kmn < kmx && scale > 0.f && scale < 3.0e38f) {
-        for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < KPT; ++i)
-          if ((cand >> i) & 1ull) atomicAdd(&hist[value_bin(key[i], fmin, scale)], 1u);
-        __syncthreads();
-        if (wave == 0) find_bin<kValueBins>(hist, remaining, lane, found);
-        __syncthreads();
-        const uint32_t b = found[0];
-        remaining -= found[1];
-        mem = 0ull;
-#pragma unroll
-        for (int i = 0; i < KPT; ++i)
-          if (((cand >> i) & 1ull) && value_bin(key[i], fmin, scale) == b) mem |= 1ull << i;
-        __syncthreads();  // `found` and `hist` are reused below
+        key[i] = k;
       }
     }
-    // Exact radix passes over the member keys, from their highest differing bit.
-    uint32_t kor = 0u, kand = 0xFFFFFFFFu;
+    // Union, last pass: rank by the combined score with the union folded into the keys. A long
+    // union (>= n_sel slots) drops every other slot to key 0, below any score; a short one lifts
+    // its own slots to the top key, above any score, so the top-up comes from the rest.
+    int p_sel = n_sel;
+    if (UNION && !last) {
+      p_sel = k_head;
+    } else if (UNION) {
+      uint32_t nu = static_cast<uint32_t>(__popcll(umask));
+      nu = wave_total(wave_inclusive_sum(nu));
+      if (lane == 0) red[wave] = nu;
+      __syncthreads();
+      int n_union = 0;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      if ((mem >> i) & 1ull) {
-        kor |= key[i];
-        kand &= key[i];
+      for (int w = 0; w < NW; ++w) n_union += static_cast<int>(red[w]);
+      __syncthreads();
+      const bool long_union = n_union >= n_sel;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const bool in_u = (umask >> i) & 1ull;
+        if (long_union && !in_u) key[i] = 0u;
+        if (!long_union && in_u) key[i] = 0xFFFFFFFFu;
       }
     }
-    block_or_and<NT>(kor, kand, red);
-    const uint32_t diff = kor ^ kand;
-    if (diff == 0u) {
-      thr = kand;  // all member keys equal
+
+    // ---- 2./3. threshold: thr = p_sel-th largest candidate key; take `need` of the keys == thr
+    // mode: 0 = select none, 1 = select all candidates, 2 = threshold rule
+    int mode;
+    uint32_t thr = 0u, need = 0u;
+    if (p_sel <= 0 || n_cand <= 0) {
+      mode = 0;
+    } else if (p_sel >= n_cand) {
+      mode = 1;
     } else {
-      const int top = 31 - __clz(diff);
-      uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
-      uint32_t prefix = kand & mask;
-      for (int hi = top; hi >= 0;) {
-        const int lo = hi >= 7 ? hi - 7 : 0;
-        const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
-        for (int i = tid; i < 256; i += NT) hist[i] = 0u;
-        __syncthreads();
+      mode = 2;
+      uint32_t remaining = static_cast<uint32_t>(p_sel);
+      uint64_t mem = cand;  // keys the exact radix passes still have to order
+      if (!RANDOM) {
+        // Pass 1 (scores): 1024 bins uniform in value between the smallest and largest finite
+        // candidate. The binning is monotone, so the threshold lies in one bin and every key in a
+        // higher bin is strictly larger; the exact passes then only see that bin's keys. Binning
+        // by value keeps a concentrated score distribution from piling into a few radix bins.
+        uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-          if (((mem >> i) & 1ull) && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> lo) & dmask], 1u);
+          if (((cand >> i) & 1ull) && key[i] > kKeyNegInf && key[i] < kKeyPosInf) {
+            kmn = min(kmn, key[i]);
+            kmx = max(kmx, key[i]);
+          }
         }
-        __syncthreads();
-        if (wave == 0) find_bin<256>(hist, remaining, lane, found);
-        __syncthreads();
-        const uint32_t digit = found[0];
-        remaining -= found[1];
-        prefix |= digit << lo;
-        mask |= dmask << lo;
-        hi = lo - 1;
-        __syncthreads();  // everyone has read `found` before the next pass may overwrite it
+        block_min_max<NT>(kmn, kmx, red);
+        const float fmin = key_value(kmn), fmax = key_value(kmx);
+        const float scale = static_cast<float>(kValueBins) / (fmax - fmin);
+        if (kmn < kmx && scale > 0.f && scale < 3.0e38f) {
+          for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < KPT; ++i)
+            if ((cand >> i) & 1ull) atomicAdd(&hist[value_bin(key[i], fmin, scale)], 1u);
+          __syncthreads();
+          if (wave == 0) find_bin<kValueBins>(hist, remaining, lane, found);
+          __syncthreads();
+          const uint32_t b = found[0];
+          remaining -= found[1];
+          mem = 0ull;
+#pragma unroll
+          for (int i = 0; i < KPT; ++i)
+            if (((cand >> i) & 1ull) && value_bin(key[i], fmin, scale) == b) mem |= 1ull << i;
+          __syncthreads();  // `found` and `hist` are reused below
+        }
       }
-      thr = prefix;
+      // Exact radix passes over the member keys, from their highest differing bit.
+      uint32_t kor = 0u, kand = 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        if ((mem >> i) & 1ull) {
+          kor |= key[i];
+          kand &= key[i];
+        }
+      }
+      block_or_and<NT>(kor, kand, red);
+      const uint32_t diff = kor ^ kand;
+      if (diff == 0u) {
+        thr = kand;  // all member keys equal
+      } else {
+        const int top = 31 - __clz(diff);
+        uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
+        uint32_t prefix = kand & mask;
+        for (int hi = top; hi >= 0;) {
+          const int lo = hi >= 7 ? hi - 7 : 0;
+          const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
+          for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < KPT; ++i) {
+            if (((mem >> i) & 1ull) && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> lo) & dmask], 1u);
+          }
+          __syncthreads();
+          if (wave == 0) find_bin<256>(hist, remaining, lane, found);
+          __syncthreads();
+          const uint32_t digit = found[0];
+          remaining -= found[1];
+          prefix |= digit << lo;
+          mask |= dmask << lo;
+          hi = lo - 1;
+          __syncthreads();  // everyone has read `found` before the next pass may overwrite it
+        }
+        thr = prefix;
+      }
+      need = remaining;
     }
-    need = remaining;
-  }
 
-  // ---- 4. one ordered scan: unconditional (A) and equal-to-thr (E) slots before each slot
-  uint64_t fa = 0ull, fe = 0ull;
+    // ---- 4. one ordered scan: unconditional (A) and equal-to-thr (E) slots before each slot.
+    // The last pass writes the kept list; a union head pass adds its top-k to the union.
+    uint64_t fa = 0ull, fe = 0ull;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const bool c = (cand >> i) & 1ull;
-    const bool pinned = !c && slot_of(i) < T;  // prompt or recent window
-    const bool a = pinned || (c && (mode == 1 || (mode == 2 && key[i] > thr)));
-    const bool e = c && mode == 2 && key[i] == thr;
-    fa |= static_cast<uint64_t>(a) << i;
-    fe |= static_cast<uint64_t>(e) << i;
-  }
-  // per round: the two counts packed as (A | E << 16); a wave's sums stay below 2^9 per half
-  uint32_t ex[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const uint32_t c = static_cast<uint32_t>(__popcll((fa >> (4 * i)) & 0xFull)) |
-                       (static_cast<uint32_t>(__popcll((fe >> (4 * i)) & 0xFull)) << 16);
-    const uint32_t x = wave_inclusive_sum(c);
-    if (lane == 63) {
-      tot_a[i * NW + wave] = x & 0xFFFFu;
-      tot_e[i * NW + wave] = x >> 16;
+    for (int i = 0; i < KPT; ++i) {
+      const bool c = (cand >> i) & 1ull;
+      const bool pinned = last && !c && slot_of(i) < T;  // prompt or recent window
+      const bool a = pinned || (c && (mode == 1 || (mode == 2 && key[i] > thr)));
+      const bool e = c && mode == 2 && key[i] == thr;
+      fa |= static_cast<uint64_t>(a) << i;
+      fe |= static_cast<uint64_t>(e) << i;
     }
-    ex[i] = x - c;
-  }
-  __syncthreads();
-  if (wave == 0) wave_exclusive_scan_lds(tot_a, R * NW, lane);
-  if (wave == (NW > 1 ? 1 : 0)) wave_exclusive_scan_lds(tot_e, R * NW, lane);
-  __syncthreads();
+    if (UNION && !last) {
+      umask |= fa;
+      if (mode != 2) continue;   // uniform: no ties to rank
+      fa = 0ull;
+    }
+    // per round: the two counts packed as (A | E << 16); a wave's sums stay below 2^9 per half
+    uint32_t ex[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    uint32_t na = tot_a[i * NW + wave] + (ex[i] & 0xFFFFu);
-    uint32_t ne = tot_e[i * NW + wave] + (ex[i] >> 16);
+    for (int i = 0; i < R; ++i) {
+      const uint32_t c = static_cast<uint32_t>(__popcll((fa >> (4 * i)) & 0xFull)) |
+                         (static_cast<uint32_t>(__popcll((fe >> (4 * i)) & 0xFull)) << 16);
+      const uint32_t x = wave_inclusive_sum(c);
+      if (lane == 63) {
+        tot_a[i * NW + wave] = x & 0xFFFFu;
+        tot_e[i * NW + wave] = x >> 16;
+      }
+      ex[i] = x - c;
+    }
+    __syncthreads();
+    if (wave == 0) wave_exclusive_scan_lds(tot_a, R * NW, lane);
+    if (wave == (NW > 1 ? 1 : 0)) wave_exclusive_scan_lds(tot_e, R * NW, lane);
+    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int bit = 4 * i + q;
-      const int j = slot_of(bit);
-      if ((fa >> bit) & 1ull) {
-        const uint32_t o = na + min(ne, need);
-        if (static_cast<int>(o) < p.b_cap) out[o] = j;
-        ++na;
-      } else if ((fe >> bit) & 1ull) {
-        if (ne < need) {
-          const uint32_t o = na + ne;
+    for (int i = 0; i < R; ++i) {
+      uint32_t na = tot_a[i * NW + wave] + (ex[i] & 0xFFFFu);
+      uint32_t ne = tot_e[i * NW + wave] + (ex[i] >> 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int bit = 4 * i + q;
+        const int j = slot_of(bit);
+        if ((fa >> bit) & 1ull) {
+          const uint32_t o = na + min(ne, need);
           if (static_cast<int>(o) < p.b_cap) out[o] = j;
+          ++na;
+        } else if ((fe >> bit) & 1ull) {
+          if (ne < need) {
+            if (UNION && !last) {
+              umask |= 1ull << bit;
+            } else {
+              const uint32_t o = na + ne;
+              if (static_cast<int>(o) < p.b_cap) out[o] = j;
+            }
+          }
+          ++ne;
         }
-        ++ne;
       }
     }
+    if (UNION && !last) __syncthreads();  // tot_a / tot_e are rewritten by the next pass
   }
   for (int r = n_kept + tid; r < p.b_cap; r += NT) out[r] = -1;
   if (writer) p.n_kept[s] = n_kept;
@@ -425,14 +478,21 @@ __global__ __launch_bounds__(256) void recent_kernel(const SelectParams p, int c
 }
 
 template <int NT, int KPT>
-hipError_t launch_cfg(const SelectParams &p, bool random, dim3 grid, hipStream_t st) {
-  const bool vec = (p.t_cap % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.scores) & 15u) == 0);
-  if (random)
-    hipLaunchKernelGGL((select_kernel<NT, KPT, true, false>), grid, dim3(NT), 0, st, p);
-  else if (vec)
-    hipLaunchKernelGGL((select_kernel<NT, KPT, false, true>), grid, dim3(NT), 0, st, p);
-  else
-    hipLaunchKernelGGL((select_kernel<NT, KPT, false, false>), grid, dim3(NT), 0, st, p);
+hipError_t launch_cfg(const SelectParams &p, SelectKind kind, dim3 grid, hipStream_t st) {
+  bool vec = (p.t_cap % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.scores) & 15u) == 0);
+  if (kind == SelectKind::kUnion) {
+    vec = vec && ((reinterpret_cast<uintptr_t>(p.head_scores) & 15u) == 0);
+    if (vec)
+      hipLaunchKernelGGL((select_kernel<NT, KPT, 2, true>), grid, dim3(NT), 0, st, p);
+    else
+      hipLaunchKernelGGL((select_kernel<NT, KPT, 2, false>), grid, dim3(NT), 0, st, p);
+  } else if (kind == SelectKind::kRandom) {
+    hipLaunchKernelGGL((select_kernel<NT, KPT, 1, false>), grid, dim3(NT), 0, st, p);
+  } else if (vec) {
+    hipLaunchKernelGGL((select_kernel<NT, KPT, 0, true>), grid, dim3(NT), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((select_kernel<NT, KPT, 0, false>), grid, dim3(NT), 0, st, p);
+  }
   return hipGetLastError();
 }
 
@@ -446,21 +506,32 @@ hipError_t launch_select_recent(const SelectParams &p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_select(const SelectParams &p, bool random, hipStream_t st) {
+hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st) {
   const long long heads = static_cast<long long>(p.L) * p.S * p.H;
   if (heads <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(heads));
   const int t = p.t_cap;
-  if (t <= 256 * 4) return launch_cfg<256, 4>(p, random, grid, st);
-  if (t <= 256 * 16) return launch_cfg<256, 16>(p, random, grid, st);
-  if (t <= 256 * 32) return launch_cfg<256, 32>(p, random, grid, st);
-  if (t <= 512 * 32) return launch_cfg<512, 32>(p, random, grid, st);
+  if (kind == SelectKind::kUnion) {
+    // The union's extra passes hold more registers: past 8192 slots it runs 512-thread tiers
+    // (a 1024-thread workgroup is limited to 128 registers per lane).
+    if (t <= 256 * 4) return launch_cfg<256, 4>(p, kind, grid, st);
+    if (t <= 256 * 16) return launch_cfg<256, 16>(p, kind, grid, st);
+    if (t <= 256 * 32) return launch_cfg<256, 32>(p, kind, grid, st);
+    if (t <= 512 * 32) return launch_cfg<512, 32>(p, kind, grid, st);
+    if (t <= 512 * 64) return launch_cfg<512, 64>(p, kind, grid, st);
+    if (t <= 1024 * 64) return launch_cfg<1024, 64>(p, kind, grid, st);
+    return hipErrorInvalidValue;
+  }
+  if (t <= 256 * 4) return launch_cfg<256, 4>(p, kind, grid, st);
+  if (t <= 256 * 16) return launch_cfg<256, 16>(p, kind, grid, st);
+  if (t <= 256 * 32) return launch_cfg<256, 32>(p, kind, grid, st);
+  if (t <= 512 * 32) return launch_cfg<512, 32>(p, kind, grid, st);
 #if KV_SELECT_WIDE
-  if (t <= 512 * 64) return launch_cfg<512, 64>(p, random, grid, st);
+  if (t <= 512 * 64) return launch_cfg<512, 64>(p, kind, grid, st);
 #else
-  if (t <= 1024 * 32) return launch_cfg<1024, 32>(p, random, grid, st);
+  if (t <= 1024 * 32) return launch_cfg<1024, 32>(p, kind, grid, st);
 #endif
-  if (t <= 1024 * 64) return launch_cfg<1024, 64>(p, random, grid, st);
+  if (t <= 1024 * 64) return launch_cfg<1024, 64>(p, kind, grid, st);
   return hipErrorInvalidValue;
 }
 

@@ -13,6 +13,7 @@
  *
  * and the policy variants the pages use as controls or alternatives:
  *
+ *   kv_select_union          union of per-query-head top-k sets, ranked by a combined score
  *   kv_select_random_shared  one random keep-set shared by every head
  *   kv_select_recent         keep the prompt and the latest slots (no scores)
  *   kv_compact_inplace       fill evicted slots with the kept rows beyond the new length
@@ -262,6 +263,30 @@ kv_status kv_select_random(const kv_shape *shape, const kv_policy *policy,
                            const int32_t *pos, uint64_t seed, uint32_t event,
                            int32_t *kept, int32_t b_cap, int32_t *n_kept,
                            void *stream);
+
+/*
+ * kv_select_union -- union-based selection ([TA-blog] eviction step) over the
+ * `group` query heads of each KV head. Within the evictable range:
+ *   1. every query head g takes its own top-k slots by head_scores[.., g, ..]
+ *      (k = k_per_head, or ceil(n_sel / group) when k_per_head <= 0);
+ *   2. the union U of those sets is formed;
+ *   3. if |U| >= n_sel, the n_sel slots of U ranked first by `scores` (the
+ *      combined score) are kept;
+ *   4. otherwise all of U is kept and the rest of the evictable range tops it
+ *      up in `scores` order.
+ * Every ranking is (score descending, slot ascending) with NaN as -inf, as
+ * for kv_select_topk; prompt and recent window are pinned as there.
+ * tri_score_gqa writes both inputs: its per-query-head scores and, as the
+ * combined score, the maximum over the group of the normalised scores.
+ *
+ *  head_scores  device [L,S,H,group,t_cap] fp32.
+ *  scores       device [L,S,H,t_cap] fp32 combined score.
+ *  group        1 <= group <= 64.
+ *  kept, b_cap, n_kept as for kv_select_topk. Requires t_cap <= 65536.
+ */
+kv_status kv_select_union(const kv_shape *shape, const kv_policy *policy, int32_t group,
+                          int32_t k_per_head, const float *head_scores, const float *scores,
+                          int32_t *kept, int32_t b_cap, int32_t *n_kept, void *stream);
 
 /*
  * kv_select_random_shared -- the shared-draw control of [RA] sections 5.2-5.3:

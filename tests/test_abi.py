@@ -107,6 +107,12 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert lib.kv_select_recent(ctypes.byref(sh), None, dummy, 8, dummy, None) == L.KV_EINVAL
     assert lib.kv_select_random_shared(ctypes.byref(big), ctypes.byref(pol), None, 1, 0, dummy, 8, dummy,
                                        None) == L.KV_ESHAPE
+    assert lib.kv_select_union(ctypes.byref(sh), ctypes.byref(pol), 4, 0, None, dummy, dummy, 8, dummy,
+                               None) == L.KV_EINVAL
+    assert lib.kv_select_union(ctypes.byref(sh), ctypes.byref(pol), 0, 0, dummy, dummy, dummy, 8, dummy,
+                               None) == L.KV_EINVAL
+    assert lib.kv_select_union(ctypes.byref(big), ctypes.byref(pol), 2, 0, dummy, dummy, dummy, 8, dummy,
+                               None) == L.KV_ESHAPE
     a = ctypes.c_void_p(0x100000)
     assert lib.kv_compact_inplace(ctypes.byref(sh), a, ctypes.c_void_p(0x100010), None, dummy, 8, dummy,
                                   None) == L.KV_EINVAL

@@ -534,3 +534,40 @@ def test_compact_inplace_bit_exact(case):
                     assert np.array_equal(Po[l, s, h, n:], pos[l, s, h, n:])
                 assert np.array_equal(Ko[l, s, h, n:], Kh[l, s, h, n:])     # slots >= n untouched
     log(f"[holes] {name}: {moved} rows moved")
+
+
+UNION_CASES = [
+    # name, t_cap, T per seq, P per seq, B, R, G, k_per_head (0: ceil(n_sel / G)), score kind
+    ("union-1k-g4", 1000, [1000, 700, 5], [10, 0, 0], 300, 16, 4, 0, "normal"),
+    ("union-4k-g8-ties", 4096, [4096, 3000], [100, 2500], 2048, 128, 8, 0, "ties"),
+    ("union-8k-g2-long", 8192, [8192, 8000], [512, 0], 2048, 128, 2, 2048, "normal"),
+    ("union-16k-g4-specials", 16000, [16000, 12345], [1024, 77], 3072, 128, 4, 0, "specials"),
+    ("union-32k-g4", 32768, [32768, 20000], [1024, 4096], 3072, 128, 4, 0, "normal"),
+    ("union-32k-g8-k1", 32768, [32768], [512], 2048, 128, 8, 1, "ties"),
+    ("union-64k-g2", 65536, [65536, 40000], [1024, 0], 2048, 64, 2, 0, "ties"),
+    ("union-g1", 3000, [3000], [100], 500, 10, 1, 0, "normal"),
+    ("union-equal", 3000, [3000], [100], 500, 10, 4, 0, "equal"),
+    ("union-fits", 3000, [2048, 100], [100, 50], 2048, 128, 4, 0, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", UNION_CASES, ids=[c[0] for c in UNION_CASES])
+def test_select_union_bit_exact(case):
+    name, t_cap, Ts, Ps, B, R, G, k, kind = case
+    log(f"[union] {name}")
+    L, H = 1, 2
+    S = len(Ts)
+    hs = _select_scores(name + "-heads", kind, (L, S, H, G, t_cap))
+    comb = _select_scores(name + "-combined", kind if kind != "equal" else "normal", (L, S, H, t_cap))
+    pcap = max(Ps)
+    b_cap = max(B, pcap) + 2
+    kept, nk = kv.kv_select_union(torch.from_numpy(hs).to(DEV), torch.from_numpy(comb).to(DEV), _i32(Ts), _i32(Ps),
+                                  B, R, pcap, k_per_head=k, b_cap=b_cap)
+    kept, nk = kept.cpu().numpy(), nk.cpu().numpy()
+    for s in range(S):
+        for l in range(L):
+            for h in range(H):
+                ref = oracle.select_union(hs[l, s, h], comb[l, s, h], Ts[s], Ps[s], B, R, k=k or None)
+                assert nk[s] == ref.size
+                assert np.array_equal(kept[l, s, h, :ref.size], ref), f"{name} l{l} s{s} h{h}"
+                assert np.all(kept[l, s, h, ref.size:] == -1)
