@@ -57,6 +57,26 @@ def algorithmic_bytes(w, n_kept_per_head: int):
     return dict(score=score, select=select, compact=compact, random_select=rnd_select)
 
 
+def counter_traffic():
+    """HBM bytes per tri_score launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+    (already scaled by the copy calibration), or None when the score kernel's sources have changed
+    since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "tri_score_full_pass_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = hashlib.sha256()
+    for f in ("score.hip", "kv_internal.hpp"):
+        h.update(open(os.path.join(ROOT, "eviction_long_reasoning_amd", "csrc", f), "rb").read())
+    m = re.search(r"sha256 `([0-9a-f]+)`", text)
+    row = re.search(r"^\| `void score_stream_kernel<[^`]*>` \| ([0-9.]+) \| ([0-9.]+) \|", text, re.M)
+    if not m or m.group(1) != h.hexdigest() or not row:
+        return None
+    return (float(row.group(1)) + float(row.group(2))) * 1e9
+
+
 def cpu_baseline(w, K, qb, n_heads: int):
     """The oracle (score -> select -> compact, fp64 NumPy, one thread) on a bounded sample."""
     import numpy as np
@@ -226,6 +246,84 @@ def main():
                                                           block_table=table, out=scores))
     print(f"[bench] rotated keys: dense {rot_ms:.3f} ms, paged {paged_ms:.3f} ms", file=sys.stderr, flush=True)
 
+    # grouped-query scores (z-score per query head, max over the group): the 4 query heads of
+    # each KV head of this cache with their own centres, and the gpt-oss-20b-shaped cache
+    # (G = 8, head_dim 64) with explicit positions
+    from workloads import query_head_centres
+
+    def gqa_case(wg, Kg, seqg, tcurg, posg, keep=False):
+        Lg, Sg, Hg, Tg, dg = Kg.shape
+        G = wg.group
+        # this cache's own query draws are one centre per KV head; the per-query-head centres
+        # come from the group-mean recipe with the same shapes
+        nud = torch.from_numpy(query_head_centres(wg if wg.q_mode == "group-mean" else
+                                                  workload(wg.wid, L=Lg, q_mode="group-mean"))).to(dev)
+        outg = torch.empty((Lg, Sg, Hg, Tg), dtype=torch.float32, device=dev)
+        head = torch.empty((Lg, Sg, Hg, G, Tg), dtype=torch.float32, device=dev)
+        ws = torch.empty((kv.gqa_workspace_bytes(Lg, Sg, Hg, Tg, dg, Kg.dtype, G),), dtype=torch.uint8, device=dev)
+        ms = time_launches(lambda: kv.tri_score_gqa(Kg, nud, tcurg, seqg, wg.theta, wg.deltas, pos=posg, out=outg,
+                                                    head_out=head, workspace=ws))
+        n = int(np.sum(np.minimum(wg.seq_len, Tg))) * Lg * Hg
+        # each key row read once; G fp32 scores per key written, read back for the z-score, one written
+        byts = n * (dg * Kg.element_size() + 8 * G + 4) + (0 if posg is None else n * 4)
+        res = {"workload": wg.name, "group": G, "head_dim": dg, "positions": posg is not None, "ms_per_launch": ms,
+               "entries_per_s": n / (ms * 1e-3), "algorithmic_bytes": byts, "gbs": byts / (ms * 1e-3) / 1e9}
+        del ws
+        return (res, outg, head) if keep else res
+
+    g3, zmax, head3 = gqa_case(w, K, seq, tcur, None, keep=True)
+    gqa = [g3]
+    # union-based selection over the 4 query heads on those scores (per-head top-k, k = ceil(n_sel/4))
+    union_ms = time_launches(lambda: kv.kv_select_union(head3, zmax, seq, plen, w.budget, w.recent, w.prompt_cap(),
+                                                        b_cap=b_cap, kept=kept, n_kept=nk))
+    union_bytes = entries * 4 * (w.group + 1) + w.n_heads_total * b_cap * 4
+    del zmax, head3
+    recent_ms = time_launches(lambda: kv.kv_select_recent((L, S, H, Tc), seq, plen, w.budget, w.recent,
+                                                          w.prompt_cap(), b_cap=b_cap, kept=kept, n_kept=nk))
+
+    w4 = workload(4)
+    mu4, _, _ = centres(w4)
+    K4, _ = kv_torch(w4, dev, mu4, with_values=False)
+    pos4 = torch.arange(w4.t_cap, dtype=torch.int32, device=dev).expand(*K4.shape[:4]).contiguous()
+    gqa.append(gqa_case(w4, K4, i32(w4.seq_len), i32(w4.t_cur), pos4))
+    del K4
+    print(f"[bench] grouped-query scores: {[(g['group'], round(g['ms_per_launch'], 3)) for g in gqa]}, "
+          f"union select {union_ms:.3f} ms, recency select {recent_ms:.3f} ms", file=sys.stderr, flush=True)
+
+    # one periodic eviction of the gpt-oss-20b-shaped workload at its steady state (every head
+    # holds B + 128 = 2176 entries): random selection, then the gather into a second buffer or
+    # in-place hole filling
+    w4f = workload(4, seq_len=np.full(w4.n_seq, w4.t_cap, np.int32))
+    K4, V4 = kv_torch(w4f, dev, mu4)
+    seq4, plen4 = i32(w4f.seq_len), i32(w4f.prompt_len)
+    kept4, nk4 = kv.kv_select_random(tuple(K4.shape[:4]), seq4, plen4, w4f.budget, w4f.recent, w4f.prompt_cap(),
+                                     w4f.seed_random, 1, pos=pos4)
+    sel4_ms = time_launches(lambda: kv.kv_select_random(tuple(K4.shape[:4]), seq4, plen4, w4f.budget, w4f.recent,
+                                                        w4f.prompt_cap(), w4f.seed_random, 1, pos=pos4,
+                                                        kept=kept4, n_kept=nk4))
+    out4 = w4f.budget
+    Ko4 = torch.empty((*K4.shape[:3], out4, K4.shape[4]), dtype=K4.dtype, device=dev)
+    Vo4 = torch.empty_like(Ko4)
+    Po4 = torch.empty(Ko4.shape[:4], dtype=torch.int32, device=dev)
+    gather_ms = time_launches(lambda: kv.kv_compact(K4, V4, kept4, nk4, seq4, out4, pos=pos4, K_out=Ko4, V_out=Vo4,
+                                                    pos_out=Po4))
+    del Ko4, Vo4, Po4
+    inplace_ms = time_launches(lambda: kv.kv_compact_inplace(K4, V4, kept4, nk4, seq4, pos=pos4))
+    nkh = nk4.to(torch.int64)[None, :, None, None]
+    movers = int(((kept4.to(torch.int64) >= nkh) & (torch.arange(kept4.shape[-1], device=dev) < nkh)).sum())
+    row4 = K4.shape[4] * K4.element_size()
+    n_kept4 = int(nk4.sum()) * w4f.n_layers * w4f.n_kv_heads
+    gather_bytes = n_kept4 * (4 * row4 + 4 + 4 + 4)
+    inplace_bytes = movers * (4 * row4 + 4 + 4)
+    del K4, V4, pos4
+    periodic = {"workload": w4f.name, "entries_per_event": w4f.entries, "random_select_ms": sel4_ms,
+                "gather": {"ms": gather_ms, "algorithmic_bytes": gather_bytes,
+                           "gbs": gather_bytes / (gather_ms * 1e-3) / 1e9},
+                "in_place": {"ms": inplace_ms, "rows_moved": movers, "algorithmic_bytes": inplace_bytes,
+                             "gbs": inplace_bytes / (inplace_ms * 1e-3) / 1e9}}
+    print(f"[bench] periodic event: select {sel4_ms:.3f} ms, gather {gather_ms:.3f} ms, in place {inplace_ms:.3f} ms "
+          f"({movers} rows moved)", file=sys.stderr, flush=True)
+
     cpu = None
     if args.cpu_heads > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -251,7 +349,7 @@ def main():
                    "rope_theta": w.theta, "n_offsets": len(w.deltas), "kv_dtype": "bf16",
                    "entries_per_pass": entries},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "tri_score",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(), "kernel": "tri_score",
                      "bytes_per_launch": ab["score"], "ms_per_launch": k_ms["tri_score"]},
         "pass": {"algorithmic_bytes": pass_bytes, "gbs": pass_bytes / (ms_step * 1e-3) / 1e9,
                  "frac_of_peak": pass_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -263,6 +361,11 @@ def main():
         "score_with_norm_term": {"ms_per_launch": full_ms, "gbs": ab["score"] / (full_ms * 1e-3) / 1e9},
         "score_rotated_keys": {"dense_ms": rot_ms, "dense_gbs": ab["score"] / (rot_ms * 1e-3) / 1e9,
                                "paged16_ms": paged_ms, "paged16_gbs": ab["score"] / (paged_ms * 1e-3) / 1e9},
+        "score_gqa": gqa,
+        "select_union": {"group": w.group, "ms_per_launch": union_ms, "algorithmic_bytes": union_bytes,
+                         "gbs": union_bytes / (union_ms * 1e-3) / 1e9},
+        "select_recent": {"ms_per_launch": recent_ms},
+        "periodic_event": periodic,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
