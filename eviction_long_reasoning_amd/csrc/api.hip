@@ -180,7 +180,7 @@ namespace {
 // Partial sums of tri_score_gqa: per (l, s, h, score chunk, g), the fp64 sums of s and s^2.
 size_t gqa_workspace(const kv_shape *sh, int group) {
   const size_t heads = static_cast<size_t>(sh->n_layers) * sh->n_seq * sh->n_kv_heads;
-  const size_t chunks = (static_cast<size_t>(sh->t_cap) + kScoreChunk - 1) / kScoreChunk;
+  const size_t chunks = (static_cast<size_t>(sh->t_cap) + kGqaChunk - 1) / kGqaChunk;
   return heads * chunks * static_cast<size_t>(group) * 2 * sizeof(double);
 }
 }  // namespace
@@ -228,16 +228,20 @@ KV_EXPORT kv_status tri_score_gqa(const kv_shape *shape, const void *K, const in
   p.F = shape->head_dim / 2;
   p.t_cap = shape->t_cap;
   p.G = group;
-  p.chunks_per_head = (shape->t_cap + kScoreChunk - 1) / kScoreChunk;
+  p.chunks_per_head = (shape->t_cap + kGqaChunk - 1) / kGqaChunk;
   fold_coefficients(p.d, rope_theta, deltas, n_delta, p.A, p.rev);
-  const int bpl = shape->dtype == KV_BF16 ? 4 : 2;
-  const int pieces = (p.F + bpl - 1) / bpl;
-  int lpk = 1;
-  while (lpk < pieces) lpk <<= 1;
-  if (lpk > 16) return KV_ESHAPE;  // G accumulators per key step stay in registers up to 16 lanes per key
+  for (int f = 0; f < p.F; ++f) {  // exp(-i omega_f kGqaTile), reduced in revolutions first
+    const double x = -p.rev[f] * kGqaTile;
+    const double r = x - std::nearbyint(x);
+    p.W[f] = make_float2(static_cast<float>(std::cos(kTwoPi * r)), static_cast<float>(std::sin(kTwoPi * r)));
+  }
+  const int pieces = p.d * elem_bytes(shape) / 16;   // 16-byte pieces per row, four lanes share a row
+  int ppq = 1;
+  while (4 * ppq < pieces) ppq <<= 1;
+  if (ppq > 8) return KV_ESHAPE;
   const long long threads = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head * kScoreThreads;
   if (threads >= (1ll << 32)) return KV_ESHAPE;
-  return hip_status(launch_score_gqa(p, shape->dtype == KV_BF16, lpk, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_score_gqa(p, shape->dtype == KV_BF16, ppq, static_cast<hipStream_t>(stream)));
 }
 
 static kv_status select_common(const kv_shape *shape, const kv_policy *policy, int32_t *kept, int32_t b_cap,

@@ -55,7 +55,7 @@ struct RotScoreParams {
 hipError_t launch_score_rotated(const RotScoreParams &p, int dtype_bf16, int lanes_per_key, hipStream_t st);
 
 // Grouped-query scores: G query-head centres per KV head, z-normalised per query head, max over G.
-constexpr int kGqaMaxGroup = 8;
+constexpr int kGqaMaxGroup = 16;
 struct GqaParams {
   const void *K;            // [L,S,H,t_cap,d]
   const int32_t *pos;       // [L,S,H,t_cap] or nullptr
@@ -67,12 +67,17 @@ struct GqaParams {
   double *partials;         // [L,S,H,chunks_per_head,G,2]: per-chunk sums of s and s^2
   float *scores;            // [L,S,H,t_cap] max over g of the normalised scores
   int32_t L, S, H, d, F, t_cap, G;
-  int32_t chunks_per_head;
+  int32_t chunks_per_head;  // workgroups per (l,s,h), kGqaChunk keys each
   float2 A[kMaxBands];
   double rev[kMaxBands];
+  float2 W[kMaxBands];      // exp(-i omega_f kGqaTile): the phase step from one key tile to the next
 };
 
-hipError_t launch_score_gqa(const GqaParams &p, int dtype_bf16, int lanes_per_key, hipStream_t st);
+constexpr int kGqaTile = 16;                                   // keys per MFMA tile
+constexpr int kGqaTilesPerWave = 16;
+constexpr int kGqaChunk = (kScoreThreads / 64) * kGqaTilesPerWave * kGqaTile;
+
+hipError_t launch_score_gqa(const GqaParams &p, int dtype_bf16, int pieces_per_lane, hipStream_t st);
 
 // --------------------------------------------------------------- select ----
 struct SelectParams {

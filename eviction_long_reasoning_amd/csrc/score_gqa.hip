@@ -7,14 +7,21 @@
 // unit (population) standard deviation over the head's T cached keys, and the
 // key's final score is the maximum of its G normalised scores.
 //
-// Kernel A reads every key once. Per band it forms y_f = exp(i omega_f m) *
-// conj(k_f) once (m = t - p, the phase carried by the same recurrence as the
-// single-centre kernel, or derived exactly per key for explicit positions),
-// then each query head costs two FMAs: Re(u_{g,f} y_f). It writes the G raw
-// scores and, per (head, chunk of keys), fp64 sums of s and s^2 for each g.
-// Kernel B reduces a head's chunk sums in a fixed order (deterministic, no
-// atomics) and writes max_g (s_g - mu_g) / sigma_g (0 for a query head whose
-// scores do not vary).
+// The G dot products of a key are a dense contraction: for a tile of 16 keys, Y (16 keys x the 2F
+// real coordinates of y_f = exp(i omega_f m) conj(k_f), m = t - p) times U (2F x G, the real and
+// imaginary parts of u_{g,f} = q_bar_{g,f} A_f), since Re(u y) = u.x y.x - u.y y.y. Kernel A
+// runs it on the matrix cores with v_mfma_f32_16x16x4_f32: lane l holds key l % 16 of the tile
+// and the coordinates of quarter l / 16 of its row (16-byte pieces q, q + 4, q + 8, ... so each
+// load instruction reads 64 contiguous bytes of 16 rows), forms y on the VALU (one complex
+// product per band, the phase advanced by a fixed rotation per tile, or derived exactly per key
+// for explicit positions) and feeds it as the A operand; the B operand is the same lane's slot
+// of U for query head l % 16, and the four quarters are the MFMA's K = 4. Every coordinate of
+// the tile is one MFMA and the product needs no cross-lane reduction: lane l ends up holding
+// query head l % 16's scores of keys 4 (l / 16) .. + 3. Up to 16 query heads cost the same as
+// one. The norm-based term is the same contraction over |k_f| and (E|q_f| - |q_bar_f|).
+// Kernel A writes the G raw scores and, per (head, chunk of keys), fp64 sums of s and s^2 for
+// each g. Kernel B reduces a head's chunk sums in a fixed order (deterministic, no atomics) and
+// writes max_g (s_g - mu_g) / sigma_g (0 for a query head whose scores do not vary).
 #include "kv_internal.hpp"
 
 namespace kvevict {
@@ -32,166 +39,216 @@ __device__ __forceinline__ float2 cis_rev(double rev, double m) {
   return make_float2(cs, sn);
 }
 
-template <int N>
-__device__ __forceinline__ float reduce_scatter(float (&acc)[N], int g) {
-#pragma unroll
-  for (int h = N / 2; h >= 1; h /= 2) {
-    const bool upper = (g & h) != 0;
-#pragma unroll
-    for (int i = 0; i < h; ++i) {
-      float lo = acc[i], hi = acc[i + h];
-      asm volatile("" : "+v"(lo), "+v"(hi));  // keep the per-lane choice a register select
-      const float send = upper ? lo : hi;
-      const float keep = upper ? hi : lo;
-      acc[i] = keep + __shfl_xor(send, h, 64);
-    }
-  }
-  return acc[0];
-}
-
 typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-// GM: group size rounded up to a power of two; query heads g >= p.G have zero centres and are not stored.
-template <bool BF16, int LPK, bool POS, bool NORM, int GM>
-__global__ __launch_bounds__(kScoreThreads) void score_gqa_kernel(const GqaParams p) {
-  constexpr int BPL = BF16 ? 4 : 2;
-  constexpr int KPS = 64 / LPK;
-  constexpr int STEPS = LPK;
-  constexpr int SUB = STEPS < 8 ? STEPS : 8;
+constexpr int kTile = kGqaTile;
+constexpr int kTilesPerWave = kGqaTilesPerWave;
+
+// PPQ: 16-byte pieces per lane (pieces q, q + 4, ...); the row has p.d * e / 16 pieces, exactly
+// 4 * PPQ of them when FULL. Up to PPQ = 4 the register budget is held to two waves per SIMD
+// (one wave per SIMD measured 35 % slower).
+template <bool BF16, int PPQ, bool FULL, bool POS, bool NORM>
+__global__ __launch_bounds__(kScoreThreads, PPQ <= 4 ? 2 : 1) void score_gqa_kernel(const GqaParams p) {
+  constexpr int BPL = BF16 ? 4 : 2;   // bands per piece
+  constexpr int NB = PPQ * BPL;       // bands per lane
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int NW = kScoreThreads / 64;
-  __shared__ double part[NW][GM][2];
+  __shared__ double part[NW][16][2];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int gl = lane % LPK;  // band group of this lane
-  const int kk = lane / LPK;
+  const int row = lane & 15;          // A: key of the tile; B and D: query head
+  const int q = lane >> 4;            // quarter of the row (the MFMA's K index)
   const int head = blockIdx.x / p.chunks_per_head;
   const int chunk = blockIdx.x - head * p.chunks_per_head;
   const int h = head % p.H;
   const int s = (head / p.H) % p.S;
   const int l = head / (p.H * p.S);
+  const int G = p.G;
 
   const int T = min(max(p.seq_len[s], 0), p.t_cap);
-  const int wave_first = chunk * kScoreChunk + wave * (kScoreBatchesPerWave * 64);
+  const int wave_first = chunk * kGqaChunk + wave * (kTilesPerWave * kTile);
   const double tq = static_cast<double>(p.t_cur[s]);
+  const int pieces = FULL ? 4 * PPQ : p.d * EB / 16;
 
-  const bool live = gl * BPL < p.F;
-  float2 u[GM][BPL], w[BPL], z[BPL];
-  float cn[GM][BPL];
-  double rev[BPL];
-  const size_t lhg = (static_cast<size_t>(l) * p.H + h) * p.G;
+  // this lane's slot of U (query head `row`) and its bands' phase constants
+  float ux[NB], uy[NB], cn[NB];
+  double rev[NB];
+  const size_t lhg = (static_cast<size_t>(l) * p.H + h) * G;
 #pragma unroll
-  for (int i = 0; i < BPL; ++i) {
-    const int b = gl * BPL + i;
-    rev[i] = live ? p.rev[b] : 0.0;
-    w[i] = live ? cis_rev(rev[i], -static_cast<double>(KPS)) : make_float2(1.f, 0.f);
+  for (int m = 0; m < PPQ; ++m) {
 #pragma unroll
-    for (int g = 0; g < GM; ++g) {
-      if (live && g < p.G) {
-        const float2 q = reinterpret_cast<const float2 *>(p.qbar + (lhg + g) * p.d)[b];
-        u[g][i] = cmul(q, p.A[b]);
-        float c = 0.f;
+    for (int c = 0; c < BPL; ++c) {
+      const int n = m * BPL + c;
+      const int pc = q + 4 * m;
+      const int f = pc * BPL + c;
+      const bool live = FULL || pc < pieces;
+      rev[n] = live ? p.rev[f] : 0.0;
+      ux[n] = uy[n] = cn[n] = 0.f;
+      if (live && row < G) {
+        const float2 qf = reinterpret_cast<const float2 *>(p.qbar + (lhg + row) * p.d)[f];
+        const float2 A = p.A[f];
+        ux[n] = qf.x * A.x - qf.y * A.y;
+        uy[n] = -(qf.x * A.y + qf.y * A.x);          // Re(u y) = u.x y.x + (-u.y) y.y
         if (NORM) {
-          const float qa = p.qabs[(lhg + g) * p.F + b];
-          c = qa > 0.f ? qa - __builtin_amdgcn_sqrtf(fmaf(q.x, q.x, q.y * q.y)) : 0.f;
+          const float qa = p.qabs[(lhg + row) * p.F + f];
+          cn[n] = qa > 0.f ? qa - __builtin_amdgcn_sqrtf(fmaf(qf.x, qf.x, qf.y * qf.y)) : 0.f;
         }
-        cn[g][i] = c;
-      } else {
-        u[g][i] = make_float2(0.f, 0.f);
-        cn[g][i] = 0.f;
       }
     }
   }
-  double sum[GM], sum2[GM];
-#pragma unroll
-  for (int g = 0; g < GM; ++g) sum[g] = sum2[g] = 0.0;
+  double sum = 0.0, sum2 = 0.0;
 
   const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
   const size_t row_bytes = static_cast<size_t>(p.d) * EB;
-  const char *Kh = static_cast<const char *>(p.K) + slot0 * row_bytes + static_cast<size_t>(live ? gl : 0) * 16;
+  const char *Kh = static_cast<const char *>(p.K) + slot0 * row_bytes;
+  float2 z[NB], w[NB];
   if (!POS && wave_first < T) {
-    const double m0 = tq - static_cast<double>(wave_first + kk);
+    const double m0 = tq - static_cast<double>(wave_first + row);
 #pragma unroll
-    for (int i = 0; i < BPL; ++i) z[i] = cis_rev(rev[i], m0);
-  }
-#pragma unroll 1
-  for (int nb = 0; nb < kScoreBatchesPerWave; ++nb) {
-    const int j0 = wave_first + nb * 64;
-    if (j0 >= T) break;
-    float acc[GM][STEPS];
+    for (int m = 0; m < PPQ; ++m) {
 #pragma unroll
-    for (int st0 = 0; st0 < STEPS; st0 += SUB) {
-      uint4 data[SUB];
-      int32_t pj[SUB];
-#pragma unroll
-      for (int t = 0; t < SUB; ++t) {
-        const int j = j0 + (st0 + t) * KPS + kk;
-        const int jc = j < T ? j : 0;  // slots past T read row 0; their sums are not used
-        const v4u32 v = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(Kh + jc * row_bytes));
-        data[t] = make_uint4(v[0], v[1], v[2], v[3]);
-        if (POS) pj[t] = p.pos[slot0 + jc];
+      for (int c = 0; c < BPL; ++c) {
+        const int n = m * BPL + c;
+        const int pc = q + 4 * m;
+        z[n] = cis_rev(rev[n], m0);
+        w[n] = (FULL || pc < pieces) ? p.W[pc * BPL + c] : make_float2(1.f, 0.f);
       }
+    }
+  }
+  auto load_tile = [&](int j0, uint4 (&d)[PPQ], int32_t &pj) {
+    const int j = j0 + row;
+    const int jc = j < T ? j : T - 1;   // slots past T repeat the last row; their scores are not kept
+    const char *r = Kh + static_cast<size_t>(jc) * row_bytes;
 #pragma unroll
-      for (int t = 0; t < SUB; ++t) {
-        if (POS) {
-          const double m = tq - static_cast<double>(pj[t]);
+    for (int m = 0; m < PPQ; ++m) {
+      const int pc = q + 4 * m;
+      if (FULL || pc < pieces) {
+        const v4u32 v = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(r + pc * 16));
+        d[m] = make_uint4(v[0], v[1], v[2], v[3]);
+      } else {
+        d[m] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    if (POS) pj = p.pos[slot0 + jc];
+  };
+
+  // Tiles in flight: tile t + AHEAD loads while tile t is computed. The buffers shift down one
+  // slot per tile; fully unrolled (contiguous slots), the shifts are register renames. Explicit
+  // positions make the tile body too large to unroll, so that path keeps one tile ahead.
+  constexpr int AHEAD = (POS || PPQ > 4) ? 1 : 3;
+  uint4 buf[AHEAD + 1][PPQ];
+  int32_t pbuf[AHEAD + 1];
 #pragma unroll
-          for (int i = 0; i < BPL; ++i) z[i] = cis_rev(rev[i], m);
+  for (int a = 0; a < AHEAD; ++a)
+    if (wave_first + a * kTile < T) load_tile(wave_first + a * kTile, buf[a], pbuf[a]);
+
+  // one tile: y on the VALU, the contraction on the matrix cores
+  auto tile_scores = [&](const uint4 (&cur)[PPQ], int32_t pcur) -> v4f {
+    if (POS) {
+      const double m = tq - static_cast<double>(pcur);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) z[n] = cis_rev(rev[n], m);
+    }
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < PPQ; ++m) {
+      const uint32_t wd[4] = {cur[m].x, cur[m].y, cur[m].z, cur[m].w};
+#pragma unroll
+      for (int c = 0; c < BPL; ++c) {
+        const int n = m * BPL + c;
+        const float re = BF16 ? __uint_as_float(wd[c] << 16) : __uint_as_float(wd[2 * c]);
+        const float im = BF16 ? __uint_as_float(wd[c] & 0xffff0000u) : __uint_as_float(wd[2 * c + 1]);
+        const float yx = fmaf(z[n].x, re, z[n].y * im);    // y = z conj(k)
+        const float yy = fmaf(z[n].y, re, -z[n].x * im);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(yx, ux[n], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(yy, uy[n], acc, 0, 0, 0);
+        if (NORM) {
+          const float ka = __builtin_amdgcn_sqrtf(fmaf(re, re, im * im));
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, cn[n], acc, 0, 0, 0);
         }
-        const uint32_t wd[4] = {data[t].x, data[t].y, data[t].z, data[t].w};
-        float a[GM];
+      }
+    }
+    if (!POS) {
 #pragma unroll
-        for (int g = 0; g < GM; ++g) a[g] = 0.f;
+      for (int n = 0; n < NB; ++n) z[n] = cmul(z[n], w[n]);
+    }
+    return acc;
+  };
+  auto next_tile = [&](int t, int j0, uint4 (&cur)[PPQ], int32_t &pcur) {
+    if (t + AHEAD < kTilesPerWave && j0 + AHEAD * kTile < T) load_tile(j0 + AHEAD * kTile, buf[AHEAD], pbuf[AHEAD]);
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-          const float re = BF16 ? __uint_as_float(wd[i] << 16) : __uint_as_float(wd[2 * i]);
-          const float im = BF16 ? __uint_as_float(wd[i] & 0xffff0000u) : __uint_as_float(wd[2 * i + 1]);
-          // y = z * conj(k): shared by every query head of the group
-          const float yx = fmaf(z[i].x, re, z[i].y * im);
-          const float yy = fmaf(z[i].y, re, -z[i].x * im);
-          const float kabs = NORM ? __builtin_amdgcn_sqrtf(fmaf(re, re, im * im)) : 0.f;
+    for (int m = 0; m < PPQ; ++m) cur[m] = buf[0][m];
+    pcur = pbuf[0];
 #pragma unroll
-          for (int g = 0; g < GM; ++g) {
-            a[g] = fmaf(u[g][i].x, yx, a[g]);
-            a[g] = fmaf(-u[g][i].y, yy, a[g]);
-            if (NORM) a[g] = fmaf(cn[g][i], kabs, a[g]);
+    for (int a = 0; a < AHEAD; ++a) {
+#pragma unroll
+      for (int m = 0; m < PPQ; ++m) buf[a][m] = buf[a + 1][m];
+      pbuf[a] = pbuf[a + 1];
+    }
+  };
+
+  // lane holds query head `row`'s scores of keys j0 + 4q .. + 3; a query head row >= G has all
+  // zero scores and is not stored
+  float *raw_head = p.raw + static_cast<size_t>(head) * G * p.t_cap;
+  if (wave_first + kTilesPerWave * kTile <= T) {
+    // every tile of the wave is full: a branch-free body, stored through a buffer resource whose
+    // bounds drop the stores of rows >= G
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        raw_head, 0, static_cast<int>(static_cast<size_t>(G) * p.t_cap * 4), 0x00020000);
+    const int row_off = row < G ? row * p.t_cap * 4 : 0x7FFFFFF0;
+#pragma unroll
+    for (int t = 0; t < kTilesPerWave; ++t) {
+      const int j0 = wave_first + t * kTile;
+      uint4 cur[PPQ];
+      int32_t pcur;
+      next_tile(t, j0, cur, pcur);
+      const v4f acc = tile_scores(cur, pcur);
+      const v4u32 bits = {__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                          __float_as_uint(acc[3])};
+      __builtin_amdgcn_raw_buffer_store_b128(bits, rr, row_off + (j0 + 4 * q) * 4, 0, 2);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sum += static_cast<double>(acc[r]);
+        sum2 += static_cast<double>(acc[r]) * static_cast<double>(acc[r]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < kTilesPerWave; ++t) {
+      const int j0 = wave_first + t * kTile;
+      if (j0 >= T) break;
+      uint4 cur[PPQ];
+      int32_t pcur;
+      next_tile(t, j0, cur, pcur);
+      const v4f acc = tile_scores(cur, pcur);
+      const int jk = j0 + 4 * q;
+      if (row < G) {
+        float *dst = raw_head + static_cast<size_t>(row) * p.t_cap + jk;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (jk + r < T) {
+            const float sc = acc[r];
+            __builtin_nontemporal_store(sc, dst + r);
+            sum += static_cast<double>(sc);
+            sum2 += static_cast<double>(sc) * static_cast<double>(sc);
           }
         }
-#pragma unroll
-        for (int g = 0; g < GM; ++g) acc[g][st0 + t] = live ? a[g] : 0.f;
-        if (!POS) {
-#pragma unroll
-          for (int i = 0; i < BPL; ++i) z[i] = cmul(z[i], w[i]);
-        }
-      }
-    }
-    const int jj = j0 + gl * KPS + kk;
-#pragma unroll
-    for (int g = 0; g < GM; ++g) {
-      const float sc = reduce_scatter<STEPS>(acc[g], gl);
-      if (jj < T && g < p.G) {
-        __builtin_nontemporal_store(sc, p.raw + (static_cast<size_t>(head) * p.G + g) * p.t_cap + jj);
-        sum[g] += static_cast<double>(sc);
-        sum2[g] += static_cast<double>(sc) * static_cast<double>(sc);
       }
     }
   }
-  // per (head, chunk) sums of s and s^2 for each query head, in a fixed reduction order
-#pragma unroll
-  for (int g = 0; g < GM; ++g) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      sum[g] += __shfl_xor(sum[g], off, 64);
-      sum2[g] += __shfl_xor(sum2[g], off, 64);
-    }
-    if (lane == 0) {
-      part[wave][g][0] = sum[g];
-      part[wave][g][1] = sum2[g];
-    }
+  // per (head, chunk) sums for each query head, in a fixed reduction order
+  sum += __shfl_xor(sum, 16, 64);
+  sum2 += __shfl_xor(sum2, 16, 64);
+  sum += __shfl_xor(sum, 32, 64);
+  sum2 += __shfl_xor(sum2, 32, 64);
+  if (q == 0) {
+    part[wave][row][0] = sum;
+    part[wave][row][1] = sum2;
   }
   __syncthreads();
-  if (static_cast<int>(threadIdx.x) < p.G) {
+  if (static_cast<int>(threadIdx.x) < G) {
     const int g = threadIdx.x;
     double a = 0.0, b = 0.0;
 #pragma unroll
@@ -199,7 +256,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_gqa_kernel(const GqaParam
       a += part[wv][g][0];
       b += part[wv][g][1];
     }
-    double *dst = p.partials + ((static_cast<size_t>(head) * p.chunks_per_head + chunk) * p.G + g) * 2;
+    double *dst = p.partials + ((static_cast<size_t>(head) * p.chunks_per_head + chunk) * G + g) * 2;
     dst[0] = a;
     dst[1] = b;
   }
@@ -213,11 +270,11 @@ __global__ __launch_bounds__(kScoreThreads) void gqa_finish_kernel(const GqaPara
   const int chunk = blockIdx.x - head * p.chunks_per_head;
   const int s = (head / p.H) % p.S;
   const int T = min(max(p.seq_len[s], 0), p.t_cap);
-  const int j0 = chunk * kScoreChunk;
+  const int j0 = chunk * kGqaChunk;
   if (j0 >= T) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) {
-    const int n_chunks = (T + kScoreChunk - 1) / kScoreChunk;
+    const int n_chunks = (T + kGqaChunk - 1) / kGqaChunk;
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
       if (g >= p.G) break;
@@ -241,7 +298,7 @@ __global__ __launch_bounds__(kScoreThreads) void gqa_finish_kernel(const GqaPara
     }
   }
   __syncthreads();
-  const int jend = min(j0 + kScoreChunk, T);
+  const int jend = min(j0 + kGqaChunk, T);
   for (int j = j0 + static_cast<int>(threadIdx.x); j < jend; j += kScoreThreads) {
     double best = -INFINITY;
 #pragma unroll
@@ -260,50 +317,41 @@ int group_bound(int G) {
   return gm;
 }
 
-template <bool BF16, int LPK, bool POS, bool NORM>
-hipError_t launch_g(const GqaParams &p, dim3 grid, hipStream_t st) {
+template <bool BF16, bool FULL, bool POS, bool NORM>
+hipError_t launch_ppq(const GqaParams &p, int ppq, dim3 grid, hipStream_t st) {
   const dim3 blk(kScoreThreads);
-  const int gm = group_bound(p.G);
-  switch (gm) {
-    case 1: hipLaunchKernelGGL((score_gqa_kernel<BF16, LPK, POS, NORM, 1>), grid, blk, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((score_gqa_kernel<BF16, LPK, POS, NORM, 2>), grid, blk, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((score_gqa_kernel<BF16, LPK, POS, NORM, 4>), grid, blk, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((score_gqa_kernel<BF16, LPK, POS, NORM, 8>), grid, blk, 0, st, p); break;
+  switch (ppq) {
+    case 1: hipLaunchKernelGGL((score_gqa_kernel<BF16, 1, FULL, POS, NORM>), grid, blk, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((score_gqa_kernel<BF16, 2, FULL, POS, NORM>), grid, blk, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((score_gqa_kernel<BF16, 4, FULL, POS, NORM>), grid, blk, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((score_gqa_kernel<BF16, 8, FULL, POS, NORM>), grid, blk, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <bool BF16, bool POS, bool NORM>
-hipError_t launch_lpk_g(const GqaParams &p, int lpk, dim3 grid, hipStream_t st) {
-  switch (lpk) {
-    case 1: return launch_g<BF16, 1, POS, NORM>(p, grid, st);
-    case 2: return launch_g<BF16, 2, POS, NORM>(p, grid, st);
-    case 4: return launch_g<BF16, 4, POS, NORM>(p, grid, st);
-    case 8: return launch_g<BF16, 8, POS, NORM>(p, grid, st);
-    case 16: return launch_g<BF16, 16, POS, NORM>(p, grid, st);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_full(const GqaParams &p, int ppq, dim3 grid, hipStream_t st) {
+  const int pieces = p.d * (BF16 ? 2 : 4) / 16;
+  return pieces == 4 * ppq ? launch_ppq<BF16, true, POS, NORM>(p, ppq, grid, st)
+                           : launch_ppq<BF16, false, POS, NORM>(p, ppq, grid, st);
 }
 
 }  // namespace
 
-hipError_t launch_score_gqa(const GqaParams &p, int dtype_bf16, int lanes_per_key, hipStream_t st) {
+hipError_t launch_score_gqa(const GqaParams &p, int dtype_bf16, int pieces_per_lane, hipStream_t st) {
   const long long blocks = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head;
   if (blocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(blocks));
   const bool pos = p.pos != nullptr, norm = p.qabs != nullptr;
+  const int ppq = pieces_per_lane;
   hipError_t e;
   if (dtype_bf16)
-    e = pos ? (norm ? launch_lpk_g<true, true, true>(p, lanes_per_key, grid, st)
-                    : launch_lpk_g<true, true, false>(p, lanes_per_key, grid, st))
-            : (norm ? launch_lpk_g<true, false, true>(p, lanes_per_key, grid, st)
-                    : launch_lpk_g<true, false, false>(p, lanes_per_key, grid, st));
+    e = pos ? (norm ? launch_full<true, true, true>(p, ppq, grid, st) : launch_full<true, true, false>(p, ppq, grid, st))
+            : (norm ? launch_full<true, false, true>(p, ppq, grid, st) : launch_full<true, false, false>(p, ppq, grid, st));
   else
-    e = pos ? (norm ? launch_lpk_g<false, true, true>(p, lanes_per_key, grid, st)
-                    : launch_lpk_g<false, true, false>(p, lanes_per_key, grid, st))
-            : (norm ? launch_lpk_g<false, false, true>(p, lanes_per_key, grid, st)
-                    : launch_lpk_g<false, false, false>(p, lanes_per_key, grid, st));
+    e = pos ? (norm ? launch_full<false, true, true>(p, ppq, grid, st) : launch_full<false, true, false>(p, ppq, grid, st))
+            : (norm ? launch_full<false, false, true>(p, ppq, grid, st) : launch_full<false, false, false>(p, ppq, grid, st));
   if (e != hipSuccess) return e;
   const dim3 blk(kScoreThreads);
   switch (group_bound(p.G)) {
@@ -311,6 +359,7 @@ hipError_t launch_score_gqa(const GqaParams &p, int dtype_bf16, int lanes_per_ke
     case 2: hipLaunchKernelGGL(gqa_finish_kernel<2>, grid, blk, 0, st, p); break;
     case 4: hipLaunchKernelGGL(gqa_finish_kernel<4>, grid, blk, 0, st, p); break;
     case 8: hipLaunchKernelGGL(gqa_finish_kernel<8>, grid, blk, 0, st, p); break;
+    case 16: hipLaunchKernelGGL(gqa_finish_kernel<16>, grid, blk, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

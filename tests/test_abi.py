@@ -78,16 +78,18 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert lib.tri_score_rotated(ctypes.byref(sh), dummy, ctypes.byref(pg), 0, dummy, None, dummy, 1e4, arr, 1,
                                  dummy, None) == L.KV_ESHAPE
     big = L.KvShape(1, 1, 1, 8, 65537, L.KV_BF16, seq)
-    # grouped-query scores: group outside 1..8, workspace too small, head_dim beyond 128 (bf16)
+    # grouped-query scores: group outside 1..16, workspace too small, fp32 head_dim beyond 128
     shg = L.KvShape(2, 3, 4, 128, 1000, L.KV_BF16, None)
     need = lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg), 4)
-    assert need == 2 * 3 * 4 * 2 * 4 * 2 * 8       # (L*S*H) heads x 2 chunks of 512 keys x G x (sum, sum of squares)
-    assert lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg), 9) == 0
+    assert need == 2 * 3 * 4 * 1 * 4 * 2 * 8       # (L*S*H) heads x 1 chunk of 1024 keys x G x (sum, sum of squares)
+    shg2 = L.KvShape(2, 3, 4, 128, 1025, L.KV_BF16, None)
+    assert lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg2), 4) == 2 * need
+    assert lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg), 17) == 0
     assert lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg), 0) == 0
     assert lib.kv_score_gqa_workspace_bytes(None, 4) == 0
     shg.seq_len = seq
     ws, hs, sc = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x400000)
-    for grp in (0, 9):
+    for grp in (0, 17):
         assert lib.tri_score_gqa(ctypes.byref(shg), dummy, None, grp, dummy, None, dummy, 1e4, arr, 1, hs, sc, ws,
                                  1 << 20, None) == L.KV_EINVAL
     assert lib.tri_score_gqa(ctypes.byref(shg), dummy, None, 4, dummy, None, dummy, 1e4, arr, 1, hs, sc, ws,
@@ -96,7 +98,7 @@ def test_host_validation_rejects_bad_arguments(lib):
                              ctypes.c_void_p(0x100004), need, None) == L.KV_EINVAL      # misaligned workspace
     assert lib.tri_score_gqa(ctypes.byref(shg), dummy, None, 4, dummy, None, dummy, 1e4, arr, 1, hs, hs, ws,
                              need, None) == L.KV_EINVAL      # scores alias the per-query-head scores
-    sh256 = L.KvShape(1, 1, 1, 256, 16, L.KV_BF16, seq)
+    sh256 = L.KvShape(1, 1, 1, 256, 16, L.KV_F32, seq)       # fp32 rows beyond 128 elements
     need256 = lib.kv_score_gqa_workspace_bytes(ctypes.byref(sh256), 2)
     assert lib.tri_score_gqa(ctypes.byref(sh256), dummy, None, 2, dummy, None, dummy, 1e4, arr, 1, hs, sc, ws,
                              need256, None) == L.KV_ESHAPE

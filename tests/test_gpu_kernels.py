@@ -138,6 +138,9 @@ GQA_CASES = [
     ("gqa-fp32-d64-g2", "f32", 64, 1, 1, 2, 2, [777], 800, "slots", True, 0),
     ("gqa-fp32-d8-g1", "f32", 8, 1, 1, 1, 1, [100], 100, "slots", False, -1),
     ("gqa-bf16-d128-g6-empty", "bf16", 128, 1, 2, 1, 6, [0, 1030], 1030, "slots", False, -1),
+    ("gqa-bf16-d256-g16-norm", "bf16", 256, 1, 1, 2, 16, [700], 704, "slots", True, 3),
+    ("gqa-fp32-d128-g12-gappy", "f32", 128, 1, 2, 1, 12, [600, 17], 640, "gappy", False, -1),
+    ("gqa-bf16-d32-g4-tiny", "bf16", 32, 2, 1, 1, 4, [3], 5, "slots", False, -1),
 ]
 
 
