@@ -282,7 +282,7 @@ def main():
                                                           w.prompt_cap(), b_cap=b_cap, kept=kept, n_kept=nk))
 
     w4 = workload(4)
-    mu4, _, _ = centres(w4)
+    mu4, qb4, _ = centres(w4)
     K4, _ = kv_torch(w4, dev, mu4, with_values=False)
     pos4 = torch.arange(w4.t_cap, dtype=torch.int32, device=dev).expand(*K4.shape[:4]).contiguous()
     gqa.append(gqa_case(w4, K4, i32(w4.seq_len), i32(w4.t_cur), pos4))
@@ -301,6 +301,15 @@ def main():
     sel4_ms = time_launches(lambda: kv.kv_select_random(tuple(K4.shape[:4]), seq4, plen4, w4f.budget, w4f.recent,
                                                         w4f.prompt_cap(), w4f.seed_random, 1, pos=pos4,
                                                         kept=kept4, n_kept=nk4))
+    # the scored eviction of the same event: scores with explicit positions, then top-B
+    sc4 = torch.empty(K4.shape[:4], dtype=torch.float32, device=dev)
+    qb4d, tcur4 = torch.from_numpy(qb4).to(dev), i32(np.full(w4f.n_seq, w4f.t_cap))   # next position
+    score4_ms = time_launches(lambda: kv.tri_score(K4, qb4d, tcur4, seq4, w4f.theta, w4f.deltas, pos=pos4, out=sc4))
+    topk4 = torch.empty_like(kept4)
+    topk4_ms = time_launches(lambda: kv.kv_select_topk(sc4, seq4, plen4, w4f.budget, w4f.recent, w4f.prompt_cap(),
+                                                       kept=topk4, n_kept=torch.empty_like(nk4)))
+    score4_bytes = w4f.entries * (K4.shape[4] * K4.element_size() + 4 + 4)
+    del sc4, topk4
     out4 = w4f.budget
     Ko4 = torch.empty((*K4.shape[:3], out4, K4.shape[4]), dtype=K4.dtype, device=dev)
     Vo4 = torch.empty_like(Ko4)
@@ -317,11 +326,15 @@ def main():
     inplace_bytes = movers * (4 * row4 + 4 + 4)
     del K4, V4, pos4
     periodic = {"workload": w4f.name, "entries_per_event": w4f.entries, "random_select_ms": sel4_ms,
+                "tri_score_with_positions": {"ms": score4_ms, "algorithmic_bytes": score4_bytes,
+                                             "gbs": score4_bytes / (score4_ms * 1e-3) / 1e9},
+                "topk_select_ms": topk4_ms,
                 "gather": {"ms": gather_ms, "algorithmic_bytes": gather_bytes,
                            "gbs": gather_bytes / (gather_ms * 1e-3) / 1e9},
                 "in_place": {"ms": inplace_ms, "rows_moved": movers, "algorithmic_bytes": inplace_bytes,
                              "gbs": inplace_bytes / (inplace_ms * 1e-3) / 1e9}}
-    print(f"[bench] periodic event: select {sel4_ms:.3f} ms, gather {gather_ms:.3f} ms, in place {inplace_ms:.3f} ms "
+    print(f"[bench] periodic event: score (positions) {score4_ms:.3f} ms, top-k {topk4_ms:.3f} ms, "
+          f"random select {sel4_ms:.3f} ms, gather {gather_ms:.3f} ms, in place {inplace_ms:.3f} ms "
           f"({movers} rows moved)", file=sys.stderr, flush=True)
 
     cpu = None
