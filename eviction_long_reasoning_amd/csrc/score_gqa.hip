@@ -266,6 +266,9 @@ __global__ __launch_bounds__(kScoreThreads, PPQ <= 4 ? 2 : 1) void score_gqa_ker
 // One workgroup per (head, chunk): reduce the head's chunk sums, then normalise and take the max.
 template <int GM>
 __global__ __launch_bounds__(kScoreThreads) void gqa_finish_kernel(const GqaParams p) {
+  constexpr int NW = kScoreThreads / 64;
+  constexpr int KPT = kGqaChunk / kScoreThreads;   // consecutive keys per thread
+  static_assert(KPT == 4, "one float4 of keys per thread");
   __shared__ double stats[GM][2];  // mean, 1/std (0 when the std is 0)
   const int head = blockIdx.x / p.chunks_per_head;
   const int chunk = blockIdx.x - head * p.chunks_per_head;
@@ -274,41 +277,56 @@ __global__ __launch_bounds__(kScoreThreads) void gqa_finish_kernel(const GqaPara
   const int j0 = chunk * kGqaChunk;
   if (j0 >= T) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (wave == 0) {
-    const int n_chunks = (T + kGqaChunk - 1) / kGqaChunk;
+  // the head's statistics, one query head per wave at a time (fixed summation order)
+  const int n_chunks = (T + kGqaChunk - 1) / kGqaChunk;
+  for (int g = wave; g < p.G; g += NW) {
+    double a = 0.0, b = 0.0;
+    for (int c = lane; c < n_chunks; c += 64) {
+      const double *src = p.partials + ((static_cast<size_t>(head) * p.chunks_per_head + c) * p.G + g) * 2;
+      a += src[0];
+      b += src[1];
+    }
 #pragma unroll
-    for (int g = 0; g < GM; ++g) {
-      if (g >= p.G) break;
-      double a = 0.0, b = 0.0;
-      for (int c = lane; c < n_chunks; c += 64) {
-        const double *src = p.partials + ((static_cast<size_t>(head) * p.chunks_per_head + c) * p.G + g) * 2;
-        a += src[0];
-        b += src[1];
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        a += __shfl_xor(a, off, 64);
-        b += __shfl_xor(b, off, 64);
-      }
-      if (lane == 0) {
-        const double mu = a / T;
-        const double var = b / T - mu * mu;
-        stats[g][0] = mu;
-        stats[g][1] = var > 0.0 ? 1.0 / sqrt(var) : 0.0;
-      }
+    for (int off = 32; off >= 1; off >>= 1) {
+      a += __shfl_xor(a, off, 64);
+      b += __shfl_xor(b, off, 64);
+    }
+    if (lane == 0) {
+      const double mu = a / T;
+      const double var = b / T - mu * mu;
+      stats[g][0] = mu;
+      stats[g][1] = var > 0.0 ? 1.0 / sqrt(var) : 0.0;
     }
   }
   __syncthreads();
-  const int jend = min(j0 + kGqaChunk, T);
-  for (int j = j0 + static_cast<int>(threadIdx.x); j < jend; j += kScoreThreads) {
-    double best = -INFINITY;
+  const int j = j0 + KPT * static_cast<int>(threadIdx.x);
+  if (j >= T) return;
+  const float *raw = p.raw + static_cast<size_t>(head) * p.G * p.t_cap + j;
+  float *out = p.scores + static_cast<size_t>(head) * p.t_cap + j;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(p.raw) | reinterpret_cast<uintptr_t>(p.scores)) & 15u) == 0;
+  if (aligned && (p.t_cap & 3) == 0 && j + KPT <= T) {
+    v4f x[GM];
 #pragma unroll
-    for (int g = 0; g < GM; ++g) {
-      if (g >= p.G) break;
-      const double sc = p.raw[(static_cast<size_t>(head) * p.G + g) * p.t_cap + j];
-      best = fmax(best, (sc - stats[g][0]) * stats[g][1]);
+    for (int g = 0; g < GM; ++g)
+      if (g < p.G) x[g] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(raw + static_cast<size_t>(g) * p.t_cap));
+    v4f best;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      double m = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < GM; ++g)
+        if (g < p.G) m = fmax(m, (static_cast<double>(x[g][k]) - stats[g][0]) * stats[g][1]);
+      best[k] = static_cast<float>(m);
     }
-    p.scores[static_cast<size_t>(head) * p.t_cap + j] = static_cast<float>(best);
+    __builtin_nontemporal_store(best, reinterpret_cast<v4f *>(out));
+  } else {
+    for (int k = 0; k < KPT && j + k < T; ++k) {
+      double m = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < GM; ++g)
+        if (g < p.G) m = fmax(m, (static_cast<double>(raw[static_cast<size_t>(g) * p.t_cap + k]) - stats[g][0]) * stats[g][1]);
+      out[k] = static_cast<float>(m);
+    }
   }
 }
 
