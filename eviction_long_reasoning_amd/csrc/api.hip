@@ -204,6 +204,8 @@ KV_EXPORT kv_status tri_score_gqa(const kv_shape *shape, const void *K, const in
   if (!aligned16(K) || (reinterpret_cast<uintptr_t>(qbar) & 7u) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
     return KV_EINVAL;
   if (workspace_bytes < gqa_workspace(shape, group)) return KV_ESHAPE;
+  // one head's per-query-head scores are stored through a 32-bit buffer offset
+  if (static_cast<long long>(group) * shape->t_cap * 4 >= (1ll << 31)) return KV_ESHAPE;
   const size_t heads = static_cast<size_t>(shape->n_layers) * shape->n_seq * shape->n_kv_heads;
   const size_t score_bytes = heads * shape->t_cap * sizeof(float);
   if (overlaps(head_scores, score_bytes * group, scores, score_bytes) ||

@@ -205,7 +205,7 @@ kv_status tri_score_rotated(const kv_shape *shape, const void *K, const kv_paged
  * or T_s = 1) contributes 0. The normalised value is computed in fp64 from
  * the fp32 head scores and rounded to fp32.
  *
- *  group        G, 1 <= G <= 16 query heads per KV head.
+ *  group        G, 1 <= G <= 16 query heads per KV head; G * t_cap < 2^29.
  *  head_dim     at most 256 (bf16) or 128 (fp32).
  *  qbar         device [L,H,G,d] fp32 per-query-head centres.
  *  qabs         device [L,H,G,d/2] fp32 or NULL.

@@ -98,6 +98,10 @@ def test_host_validation_rejects_bad_arguments(lib):
                              ctypes.c_void_p(0x100004), need, None) == L.KV_EINVAL      # misaligned workspace
     assert lib.tri_score_gqa(ctypes.byref(shg), dummy, None, 4, dummy, None, dummy, 1e4, arr, 1, hs, hs, ws,
                              need, None) == L.KV_EINVAL      # scores alias the per-query-head scores
+    shbig = L.KvShape(1, 1, 1, 16, 1 << 26, L.KV_BF16, seq)  # 16 query heads x 2^26 slots overflow 2^31 bytes
+    needbig = lib.kv_score_gqa_workspace_bytes(ctypes.byref(shbig), 16)
+    assert lib.tri_score_gqa(ctypes.byref(shbig), dummy, None, 16, dummy, None, dummy, 1e4, arr, 1, hs, sc, ws,
+                             needbig, None) == L.KV_ESHAPE
     sh256 = L.KvShape(1, 1, 1, 256, 16, L.KV_F32, seq)       # fp32 rows beyond 128 elements
     need256 = lib.kv_score_gqa_workspace_bytes(ctypes.byref(sh256), 2)
     assert lib.tri_score_gqa(ctypes.byref(sh256), dummy, None, 2, dummy, None, dummy, 1e4, arr, 1, hs, sc, ws,
