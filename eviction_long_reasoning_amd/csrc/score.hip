@@ -24,9 +24,9 @@
 //    positions each lane rotates its u_f * exp(i omega_f m) by a fixed step
 //    exp(-i omega_f KPS) from one key to its next; the value is derived
 //    exactly (fp64 reduction of omega_f m / 2pi to [-1/2, 1/2] revolutions,
-//    then fp32 sincospi) once per wave, so the fp32 recurrence runs at most
+//    then the hardware sine and cosine) once per wave, so the fp32 recurrence runs at most
 //    kScoreBatchesPerWave * LPK steps. With explicit (gappy) positions the
-//    phase is derived exactly for every key.
+//    phase is derived the same way for every key.
 //  * The LPK per-lane partial sums of a batch are combined by a shuffle
 //    reduce-scatter (LPK-1 exchanges per lane for LPK keys), after which each
 //    lane holds one finished score: 64 consecutive scores leave in one
