@@ -244,7 +244,11 @@ def main():
     table = torch.randperm(S * bps, generator=gen).view(S, bps).to(torch.int32).to(dev)
     paged_ms = time_launches(lambda: kv.tri_score_rotated(pool, qbd, tcur, seq, w.theta, w.deltas,
                                                           block_table=table, out=scores))
-    print(f"[bench] rotated keys: dense {rot_ms:.3f} ms, paged {paged_ms:.3f} ms", file=sys.stderr, flush=True)
+    pool_hm = K.view(L, S * bps, H, bs, d)   # the same bytes as a head-major pool
+    paged_hm_ms = time_launches(lambda: kv.tri_score_rotated(pool_hm, qbd, tcur, seq, w.theta, w.deltas,
+                                                             block_table=table, out=scores, head_major=True))
+    print(f"[bench] rotated keys: dense {rot_ms:.3f} ms, paged {paged_ms:.3f} ms, paged head-major "
+          f"{paged_hm_ms:.3f} ms", file=sys.stderr, flush=True)
 
     # grouped-query scores (z-score per query head, max over the group): the 4 query heads of
     # each KV head of this cache with their own centres, and the gpt-oss-20b-shaped cache
@@ -373,7 +377,9 @@ def main():
         "random_pass": rnd,
         "score_with_norm_term": {"ms_per_launch": full_ms, "gbs": ab["score"] / (full_ms * 1e-3) / 1e9},
         "score_rotated_keys": {"dense_ms": rot_ms, "dense_gbs": ab["score"] / (rot_ms * 1e-3) / 1e9,
-                               "paged16_ms": paged_ms, "paged16_gbs": ab["score"] / (paged_ms * 1e-3) / 1e9},
+                               "paged16_ms": paged_ms, "paged16_gbs": ab["score"] / (paged_ms * 1e-3) / 1e9,
+                               "paged16_head_major_ms": paged_hm_ms,
+                               "paged16_head_major_gbs": ab["score"] / (paged_hm_ms * 1e-3) / 1e9},
         "score_gqa": gqa,
         "select_union": {"group": w.group, "ms_per_launch": union_ms, "algorithmic_bytes": union_bytes,
                          "gbs": union_bytes / (union_ms * 1e-3) / 1e9},

@@ -34,6 +34,7 @@ class KvPaged(ctypes.Structure):
         ("blocks_per_seq", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
         ("n_blocks", ctypes.c_int32),
+        ("head_major", ctypes.c_int32),
     ]
 
 

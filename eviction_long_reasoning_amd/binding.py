@@ -80,11 +80,12 @@ def tri_score(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len:
 def tri_score_rotated(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len: torch.Tensor,
                       rope_theta: float, deltas: Sequence[int], rope_style: str = "interleaved",
                       block_table: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                      qabs: Optional[torch.Tensor] = None) -> torch.Tensor:
+                      qabs: Optional[torch.Tensor] = None, head_major: bool = False) -> torch.Tensor:
     """Scores of keys stored after RoPE (fp32 [L,S,H,t_cap]).
 
-    Dense: ``K`` is [L,S,H,t_cap,d]. Paged: ``K`` is the pool [L,n_blocks,block_size,H,d] and
-    ``block_table`` is int32 [S, blocks_per_seq]; t_cap = blocks_per_seq * block_size.
+    Dense: ``K`` is [L,S,H,t_cap,d]. Paged: ``K`` is the pool [L,n_blocks,block_size,H,d]
+    ([L,n_blocks,H,block_size,d] with ``head_major``) and ``block_table`` is int32
+    [S, blocks_per_seq]; t_cap = blocks_per_seq * block_size.
     ``rope_style`` is "interleaved" (x[2f], x[2f+1]) or "half" (x[f], x[f+d/2]).
     """
     if K.dim() != 5 or K.dtype not in _DT:
@@ -95,11 +96,14 @@ def tri_score_rotated(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, 
     if block_table is None:
         L, S, H, t_cap, d = K.shape
     else:
-        L, n_blocks, bs, H, d = K.shape
+        if head_major:
+            L, n_blocks, H, bs, d = K.shape
+        else:
+            L, n_blocks, bs, H, d = K.shape
         S, bps = block_table.shape
         t_cap = bps * bs
         paged = _lib.KvPaged(_dev_ptr(block_table, "block_table", torch.int32, (S, bps), dev), int(bps), int(bs),
-                             int(n_blocks))
+                             int(n_blocks), int(bool(head_major)))
     kp = _dev_ptr(K, "K")
     qp = _dev_ptr(qbar, "qbar", torch.float32, (L, H, d), dev)
     ap = _dev_ptr(qabs, "qabs", torch.float32, (L, H, d // 2), dev)

@@ -153,6 +153,7 @@ KV_EXPORT kv_status tri_score_rotated(const kv_shape *shape, const void *K, cons
   p.half = rope_style == KV_ROPE_HALF;
   p.chunks_per_head = (shape->t_cap + kScoreChunk - 1) / kScoreChunk;
   if (paged) {
+    if (paged->head_major != 0 && paged->head_major != 1) return KV_EINVAL;
     if (!paged->block_table || paged->blocks_per_seq < 1 || paged->n_blocks < 1 || paged->block_size < 1 ||
         (paged->block_size & (paged->block_size - 1)))
       return KV_EINVAL;
@@ -160,6 +161,7 @@ KV_EXPORT kv_status tri_score_rotated(const kv_shape *shape, const void *K, cons
     p.block_table = paged->block_table;
     p.blocks_per_seq = paged->blocks_per_seq;
     p.n_blocks = paged->n_blocks;
+    p.head_major = paged->head_major;
     int shift = 0;
     while ((1 << shift) < paged->block_size) ++shift;
     p.block_shift = shift;

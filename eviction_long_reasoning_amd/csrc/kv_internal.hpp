@@ -38,8 +38,9 @@ hipError_t launch_score(const ScoreParams &p, int dtype_bf16, int lanes_per_key,
 // Keys stored after RoPE, dense or paged.
 struct RotScoreParams {
   const void *K;               // dense [L,S,H,t_cap,d] or paged pool [L,n_blocks,block_size,H,d]
+                               // (head-major: [L,n_blocks,H,block_size,d])
   const int32_t *block_table;  // [S, blocks_per_seq] or nullptr (dense)
-  int32_t blocks_per_seq, block_shift, n_blocks;
+  int32_t blocks_per_seq, block_shift, n_blocks, head_major;
   const float *qbar;           // [L,H,d] in the storage layout
   const float *qabs;           // [L,H,d/2] or nullptr
   const int32_t *t_cur;        // [S]

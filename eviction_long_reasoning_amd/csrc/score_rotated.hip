@@ -15,9 +15,10 @@
 // is stored, the imaginary part where its imaginary part is stored), for the
 // interleaved (x[2f], x[2f+1]) or the half-split (x[f], x[f+d/2]) pairing.
 //
-// Keys come from a dense [L,S,H,t_cap,d] tensor or from a paged pool
-// [L, n_blocks, block_size, H, d] through a per-sequence block table. Lane
-// layout, batching and the shuffle reduce-scatter follow the pre-RoPE kernel.
+// Keys come from a dense [L,S,H,t_cap,d] tensor or from a paged pool through a per-sequence
+// block table, token-major [L, n_blocks, block_size, H, d] or head-major
+// [L, n_blocks, H, block_size, d]. Lane layout, batching and the shuffle reduce-scatter follow
+// the pre-RoPE kernel.
 #include "kv_internal.hpp"
 
 namespace kvevict {
@@ -66,10 +67,11 @@ __device__ __forceinline__ float elem(const uint4 &d, int e) {
   return __uint_as_float(wd[e]);
 }
 
-// BF16: 8 coordinates per 16-byte lane piece (fp32: 4). HALF: half-split pairing. PAGED: rows
-// through the block table. NORM: add (1 - R_f) E|q_f| |k_f|.
-template <bool BF16, int LPK, bool HALF, bool PAGED, bool NORM>
+// BF16: 8 coordinates per 16-byte lane piece (fp32: 4). HALF: half-split pairing. LAYOUT: 0 dense,
+// 1 token-major paged pool, 2 head-major paged pool. NORM: add (1 - R_f) E|q_f| |k_f|.
+template <bool BF16, int LPK, bool HALF, int LAYOUT, bool NORM>
 __global__ __launch_bounds__(kScoreThreads) void score_rotated_kernel(const RotScoreParams p) {
+  constexpr bool PAGED = LAYOUT != 0;
   constexpr int EPL = BF16 ? 8 : 4;            // coordinates per lane
   constexpr int KPS = 64 / LPK;
   constexpr int STEPS = LPK;
@@ -125,7 +127,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_rotated_kernel(const RotS
     if (PAGED) {
       int pb = table[j >> p.block_shift];
       pb = min(max(pb, 0), p.n_blocks - 1);  // never leave the pool
-      row = ((static_cast<size_t>(l) * p.n_blocks + pb) * (bmask + 1) + (j & bmask)) * p.H + h;
+      const size_t blk = static_cast<size_t>(l) * p.n_blocks + pb;
+      row = LAYOUT == 2 ? (blk * p.H + h) * (bmask + 1) + (j & bmask) : (blk * (bmask + 1) + (j & bmask)) * p.H + h;
     } else {
       row = dense0 + j;
     }
@@ -176,29 +179,33 @@ __global__ __launch_bounds__(kScoreThreads) void score_rotated_kernel(const RotS
   }
 }
 
-template <bool BF16, bool HALF, bool PAGED, bool NORM>
+template <bool BF16, bool HALF, int LAYOUT, bool NORM>
 hipError_t launch_rot(const RotScoreParams &p, int lpk, dim3 grid, hipStream_t st) {
   const dim3 blk(kScoreThreads);
   switch (lpk) {
-    case 1: hipLaunchKernelGGL((score_rotated_kernel<BF16, 1, HALF, PAGED, NORM>), grid, blk, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((score_rotated_kernel<BF16, 2, HALF, PAGED, NORM>), grid, blk, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((score_rotated_kernel<BF16, 4, HALF, PAGED, NORM>), grid, blk, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((score_rotated_kernel<BF16, 8, HALF, PAGED, NORM>), grid, blk, 0, st, p); break;
-    case 16: hipLaunchKernelGGL((score_rotated_kernel<BF16, 16, HALF, PAGED, NORM>), grid, blk, 0, st, p); break;
-    case 32: hipLaunchKernelGGL((score_rotated_kernel<BF16, 32, HALF, PAGED, NORM>), grid, blk, 0, st, p); break;
-    case 64: hipLaunchKernelGGL((score_rotated_kernel<BF16, 64, HALF, PAGED, NORM>), grid, blk, 0, st, p); break;
+    case 1: hipLaunchKernelGGL((score_rotated_kernel<BF16, 1, HALF, LAYOUT, NORM>), grid, blk, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((score_rotated_kernel<BF16, 2, HALF, LAYOUT, NORM>), grid, blk, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((score_rotated_kernel<BF16, 4, HALF, LAYOUT, NORM>), grid, blk, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((score_rotated_kernel<BF16, 8, HALF, LAYOUT, NORM>), grid, blk, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((score_rotated_kernel<BF16, 16, HALF, LAYOUT, NORM>), grid, blk, 0, st, p); break;
+    case 32: hipLaunchKernelGGL((score_rotated_kernel<BF16, 32, HALF, LAYOUT, NORM>), grid, blk, 0, st, p); break;
+    case 64: hipLaunchKernelGGL((score_rotated_kernel<BF16, 64, HALF, LAYOUT, NORM>), grid, blk, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <bool BF16, bool HALF, int LAYOUT>
+hipError_t launch_rot_norm(const RotScoreParams &p, int lpk, dim3 grid, hipStream_t st) {
+  return p.qabs != nullptr ? launch_rot<BF16, HALF, LAYOUT, true>(p, lpk, grid, st)
+                           : launch_rot<BF16, HALF, LAYOUT, false>(p, lpk, grid, st);
+}
+
 template <bool BF16, bool HALF>
 hipError_t launch_rot_flags(const RotScoreParams &p, int lpk, dim3 grid, hipStream_t st) {
-  const bool paged = p.block_table != nullptr, norm = p.qabs != nullptr;
-  if (paged) return norm ? launch_rot<BF16, HALF, true, true>(p, lpk, grid, st)
-                         : launch_rot<BF16, HALF, true, false>(p, lpk, grid, st);
-  return norm ? launch_rot<BF16, HALF, false, true>(p, lpk, grid, st)
-              : launch_rot<BF16, HALF, false, false>(p, lpk, grid, st);
+  if (p.block_table == nullptr) return launch_rot_norm<BF16, HALF, 0>(p, lpk, grid, st);
+  return p.head_major ? launch_rot_norm<BF16, HALF, 2>(p, lpk, grid, st)
+                      : launch_rot_norm<BF16, HALF, 1>(p, lpk, grid, st);
 }
 
 }  // namespace

@@ -158,16 +158,20 @@ typedef enum kv_rope_style {
   KV_ROPE_HALF = 1
 } kv_rope_style;
 
-/* A paged key pool: per layer, n_blocks blocks of block_size tokens, all KV heads of a token
- * together. The row of (layer l, physical block pb, token o in the block, KV head h) starts at
- * element ((((l*n_blocks + pb)*block_size + o)*n_kv_heads + h)*head_dim). Slot j of sequence s
- * lives in physical block block_table[s*blocks_per_seq + j/block_size], token j % block_size.
+/* A paged key pool: per layer, n_blocks blocks of block_size tokens. Token-major pools
+ * (head_major = 0) keep all KV heads of a token together: the row of (layer l, physical block pb,
+ * token o in the block, KV head h) starts at element
+ * ((((l*n_blocks + pb)*block_size + o)*n_kv_heads + h)*head_dim). Head-major pools
+ * (head_major = 1) keep each head's block contiguous: ((((l*n_blocks + pb)*n_kv_heads + h)
+ * *block_size + o)*head_dim). Slot j of sequence s lives in physical block
+ * block_table[s*blocks_per_seq + j/block_size], token j % block_size.
  * Block ids outside [0, n_blocks) are clamped into it (memory safety, not a result). */
 typedef struct kv_paged {
   const int32_t *block_table;  /* device [n_seq][blocks_per_seq] */
   int32_t blocks_per_seq;      /* >= 1; blocks_per_seq * block_size >= t_cap */
   int32_t block_size;          /* a power of two */
   int32_t n_blocks;            /* physical blocks per layer in the pool */
+  int32_t head_major;          /* 0: [L, n_blocks, block_size, H, d]; 1: [L, n_blocks, H, block_size, d] */
 } kv_paged;
 
 /*

@@ -74,6 +74,9 @@ def test_host_validation_rejects_bad_arguments(lib):
     pg = L.KvPaged(dummy, 1, 12, 4)       # block size not a power of two
     assert lib.tri_score_rotated(ctypes.byref(sh), dummy, ctypes.byref(pg), 0, dummy, None, dummy, 1e4, arr, 1,
                                  dummy, None) == L.KV_EINVAL
+    pg = L.KvPaged(dummy, 2, 8, 4, 2)     # unknown pool layout
+    assert lib.tri_score_rotated(ctypes.byref(sh), dummy, ctypes.byref(pg), 0, dummy, None, dummy, 1e4, arr, 1,
+                                 dummy, None) == L.KV_EINVAL
     pg = L.KvPaged(dummy, 1, 8, 4)        # 1 block of 8 cannot hold t_cap = 16 slots
     assert lib.tri_score_rotated(ctypes.byref(sh), dummy, ctypes.byref(pg), 0, dummy, None, dummy, 1e4, arr, 1,
                                  dummy, None) == L.KV_ESHAPE

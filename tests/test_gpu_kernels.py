@@ -206,21 +206,23 @@ def test_gqa_is_deterministic():
 
 
 ROT_CASES = [
-    # name, dtype, d, L, S, H, T per seq, style, norm, paged block size (0 = dense)
-    ("rot-bf16-d128-inter", "bf16", 128, 2, 2, 2, [1000, 777], "interleaved", False, 0),
-    ("rot-bf16-d128-half", "bf16", 128, 1, 2, 3, [1030, 64], "half", False, 0),
-    ("rot-bf16-d64-half-norm", "bf16", 64, 2, 1, 2, [900], "half", True, 0),
-    ("rot-bf16-d96-inter-norm", "bf16", 96, 1, 2, 2, [500, 130], "interleaved", True, 0),
-    ("rot-fp32-d64-half", "f32", 64, 1, 1, 2, [333], "half", False, 0),
-    ("rot-fp32-d8-inter", "f32", 8, 1, 1, 1, [200], "interleaved", True, 0),
-    ("rot-paged16-bf16-d128", "bf16", 128, 2, 3, 4, [1000, 1, 517], "interleaved", True, 16),
-    ("rot-paged64-bf16-d64-half", "bf16", 64, 1, 2, 8, [2000, 1500], "half", False, 64),
+    # name, dtype, d, L, S, H, T per seq, style, norm, paged block size (0 = dense), head-major pool
+    ("rot-bf16-d128-inter", "bf16", 128, 2, 2, 2, [1000, 777], "interleaved", False, 0, False),
+    ("rot-bf16-d128-half", "bf16", 128, 1, 2, 3, [1030, 64], "half", False, 0, False),
+    ("rot-bf16-d64-half-norm", "bf16", 64, 2, 1, 2, [900], "half", True, 0, False),
+    ("rot-bf16-d96-inter-norm", "bf16", 96, 1, 2, 2, [500, 130], "interleaved", True, 0, False),
+    ("rot-fp32-d64-half", "f32", 64, 1, 1, 2, [333], "half", False, 0, False),
+    ("rot-fp32-d8-inter", "f32", 8, 1, 1, 1, [200], "interleaved", True, 0, False),
+    ("rot-paged16-bf16-d128", "bf16", 128, 2, 3, 4, [1000, 1, 517], "interleaved", True, 16, False),
+    ("rot-paged64-bf16-d64-half", "bf16", 64, 1, 2, 8, [2000, 1500], "half", False, 64, False),
+    ("rot-paged16-headmajor-bf16-d128", "bf16", 128, 2, 3, 4, [1000, 1, 517], "interleaved", True, 16, True),
+    ("rot-paged32-headmajor-fp32-d64-half", "f32", 64, 1, 2, 3, [700, 64], "half", False, 32, True),
 ]
 
 
 @pytest.mark.parametrize("case", ROT_CASES, ids=[c[0] for c in ROT_CASES])
 def test_score_rotated_matches_oracle(case):
-    name, dtype, d, L, S, H, Ts, style, norm, bs = case
+    name, dtype, d, L, S, H, Ts, style, norm, bs, hm = case
     log(f"[rotated] {name}")
     r = rng(550, zlib.crc32(name.encode()) % 1000)
     Ts = np.array(Ts, np.int32)
@@ -243,13 +245,17 @@ def test_score_rotated_matches_oracle(case):
         bps = (int(Ts.max()) + bs - 1) // bs
         n_blocks = S * bps + 5
         pool = (r.standard_normal((L, 1, 1, H, d)) + 0.3 * r.standard_normal((L, n_blocks, bs, H, d))).astype(np.float32)
+        if hm:
+            pool = np.ascontiguousarray(pool.transpose(0, 1, 3, 2, 4))     # [L, n_blocks, H, bs, d]
         table = r.permutation(n_blocks)[:S * bps].reshape(S, bps).astype(np.int32)
         Kd = _to_dev_keys(pool, dtype)
         Ph = keys_f64(_host_keys(Kd, dtype), dtype)
-        rows = lambda l, s, h, T: np.stack([Ph[l, table[s, j // bs], j % bs, h] for j in range(T)]) if T else \
+        at = (lambda l, b, o, h: Ph[l, b, h, o]) if hm else (lambda l, b, o, h: Ph[l, b, o, h])
+        rows = lambda l, s, h, T: np.stack([at(l, table[s, j // bs], j % bs, h) for j in range(T)]) if T else \
             np.zeros((0, d))
         out = kv.tri_score_rotated(Kd, torch.from_numpy(qb).to(DEV), _i32(t_cur), _i32(Ts), theta, D, rope_style=style,
-                                   block_table=_i32(table), qabs=None if qabs is None else torch.from_numpy(qabs).to(DEV))
+                                   block_table=_i32(table), qabs=None if qabs is None else torch.from_numpy(qabs).to(DEV),
+                                   head_major=hm)
     got = out.cpu().numpy()
     worst = 0.0
     for l in range(L):
