@@ -150,3 +150,23 @@ def test_binding_fails_loudly_without_gpu_tensors():
     with pytest.raises(ValueError):
         kv.tri_score(torch.zeros(1, 1, 1, 4, 8), torch.zeros(1, 1, 8), torch.zeros(1, dtype=torch.int32),
                      torch.zeros(1, dtype=torch.int32), 1e4, [1])
+
+
+def test_missing_library_raises_instead_of_falling_back():
+    # with no built library every call fails loudly; nothing computes on the CPU instead
+    import subprocess
+    import sys
+    code = ("import eviction_long_reasoning_amd._lib as L\n"
+            "try:\n    L.load()\nexcept RuntimeError as e:\n    print('raised', 'missing' in str(e))\n")
+    env = dict(os.environ, KVEVICT_LIB=os.path.join(ROOT, "no_such_library.so"))
+    out = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert out.stdout.strip() == "raised True", out.stdout + out.stderr
+
+
+def test_product_package_never_imports_the_oracle():
+    # the oracle is test infrastructure: no module of the product package may import it
+    pkg = os.path.join(ROOT, "eviction_long_reasoning_amd")
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            src = open(os.path.join(pkg, name)).read()
+            assert not re.search(r"^\s*(from|import)\s+oracle\b", src, flags=re.M), name

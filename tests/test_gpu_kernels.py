@@ -580,3 +580,33 @@ def test_select_union_bit_exact(case):
                 assert nk[s] == ref.size
                 assert np.array_equal(kept[l, s, h, :ref.size], ref), f"{name} l{l} s{s} h{h}"
                 assert np.all(kept[l, s, h, ref.size:] == -1)
+
+
+def test_calls_run_on_the_current_stream():
+    # every call enqueues on torch's current stream: work on a side stream, ordered by events,
+    # gives the same bits as on the default stream
+    r = rng(570, 0)
+    L, S, H, T, d = 2, 2, 3, 3000, 128
+    K = _to_dev_keys(r.standard_normal((L, S, H, T, d)).astype(np.float32), "bf16")
+    V = K.clone()
+    qb = torch.from_numpy(r.standard_normal((L, H, d)).astype(np.float32)).to(DEV)
+    Ts, Ps = _i32([T, 2500]), _i32([100, 0])
+    args = (1e6, [1, 2, 4, 8])
+
+    def run():
+        sc = kv.tri_score(K, qb, Ts, Ts, *args)
+        kept, nk = kv.kv_select_topk(sc, Ts, Ps, 1000, 32, 100)
+        Ko, Vo, Po = kv.kv_compact(K, V, kept, nk, Ts, 1000)
+        return sc, kept, Ko
+
+    ref = run()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
