@@ -607,6 +607,6 @@ def test_calls_run_on_the_current_stream():
         got = run()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    bits = {torch.float32: torch.int32, torch.bfloat16: torch.int16, torch.int32: torch.int32}
     for a, b in zip(ref, got):
-        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
-                           b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+        assert torch.equal(a.view(bits[a.dtype]), b.view(bits[b.dtype]))
