@@ -557,6 +557,8 @@ UNION_CASES = [
     ("union-g1", 3000, [3000], [100], 500, 10, 1, 0, "normal"),
     ("union-equal", 3000, [3000], [100], 500, 10, 4, 0, "equal"),
     ("union-fits", 3000, [2048, 100], [100, 50], 2048, 128, 4, 0, "normal"),
+    ("union-ragged-rows", 2999, [2999, 2500], [7, 0], 700, 9, 3, 0, "specials"),   # t_cap % 4 != 0
+    ("union-20k-ragged-rows", 20001, [20001], [300], 2048, 64, 4, 0, "ties"),
 ]
 
 
@@ -607,6 +609,8 @@ def test_calls_run_on_the_current_stream():
         got = run()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    bits = {torch.float32: torch.int32, torch.bfloat16: torch.int16, torch.int32: torch.int32}
-    for a, b in zip(ref, got):
-        assert torch.equal(a.view(bits[a.dtype]), b.view(bits[b.dtype]))
+    # compare what the calls write: scores of slots < T, the whole kept lists, the first n_kept rows
+    for s_, T_ in enumerate((T, 2500)):
+        assert torch.equal(ref[0][:, s_, :, :T_].view(torch.int32), got[0][:, s_, :, :T_].view(torch.int32))
+    assert torch.equal(ref[1], got[1])
+    assert torch.equal(ref[2][..., :1000, :].view(torch.int16), got[2][..., :1000, :].view(torch.int16))
