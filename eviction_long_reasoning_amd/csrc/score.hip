@@ -350,7 +350,10 @@ hipError_t launch_lpk(const ScoreParams &p, int lpk, dim3 grid, hipStream_t st) 
     case 8: hipLaunchKernelGGL((score_kernel<BF16, 8, POS, FULL, NORM>), grid, blk, 0, st, p); break;
     case 16: hipLaunchKernelGGL((score_kernel<BF16, 16, POS, FULL, NORM>), grid, blk, 0, st, p); break;
     case 32: hipLaunchKernelGGL((score_kernel<BF16, 32, POS, FULL, NORM>), grid, blk, 0, st, p); break;
-    case 64: hipLaunchKernelGGL((score_kernel<BF16, 64, POS, FULL, NORM>), grid, blk, 0, st, p); break;
+    case 64:  // only fp32 rows reach 64 pieces (head_dim 256)
+      if constexpr (BF16) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL((score_kernel<BF16, 64, POS, FULL, NORM>), grid, blk, 0, st, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -189,7 +189,10 @@ hipError_t launch_rot(const RotScoreParams &p, int lpk, dim3 grid, hipStream_t s
     case 8: hipLaunchKernelGGL((score_rotated_kernel<BF16, 8, HALF, LAYOUT, NORM>), grid, blk, 0, st, p); break;
     case 16: hipLaunchKernelGGL((score_rotated_kernel<BF16, 16, HALF, LAYOUT, NORM>), grid, blk, 0, st, p); break;
     case 32: hipLaunchKernelGGL((score_rotated_kernel<BF16, 32, HALF, LAYOUT, NORM>), grid, blk, 0, st, p); break;
-    case 64: hipLaunchKernelGGL((score_rotated_kernel<BF16, 64, HALF, LAYOUT, NORM>), grid, blk, 0, st, p); break;
+    case 64:  // only fp32 rows reach 64 pieces (head_dim 256)
+      if constexpr (BF16) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL((score_rotated_kernel<BF16, 64, HALF, LAYOUT, NORM>), grid, blk, 0, st, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

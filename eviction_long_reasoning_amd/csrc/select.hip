@@ -477,21 +477,23 @@ __global__ __launch_bounds__(256) void recent_kernel(const SelectParams p, int c
   p.kept[static_cast<size_t>(head) * p.b_cap + r] = v;
 }
 
-template <int NT, int KPT>
+// Only the (tier, ranking) pairs launch_select dispatches are instantiated.
+template <int NT, int KPT, bool UNION>
 hipError_t launch_cfg(const SelectParams &p, SelectKind kind, dim3 grid, hipStream_t st) {
   bool vec = (p.t_cap % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.scores) & 15u) == 0);
-  if (kind == SelectKind::kUnion) {
+  if constexpr (UNION) {
     vec = vec && ((reinterpret_cast<uintptr_t>(p.head_scores) & 15u) == 0);
     if (vec)
       hipLaunchKernelGGL((select_kernel<NT, KPT, 2, true>), grid, dim3(NT), 0, st, p);
     else
       hipLaunchKernelGGL((select_kernel<NT, KPT, 2, false>), grid, dim3(NT), 0, st, p);
-  } else if (kind == SelectKind::kRandom) {
-    hipLaunchKernelGGL((select_kernel<NT, KPT, 1, false>), grid, dim3(NT), 0, st, p);
-  } else if (vec) {
-    hipLaunchKernelGGL((select_kernel<NT, KPT, 0, true>), grid, dim3(NT), 0, st, p);
   } else {
-    hipLaunchKernelGGL((select_kernel<NT, KPT, 0, false>), grid, dim3(NT), 0, st, p);
+    if (kind == SelectKind::kRandom)
+      hipLaunchKernelGGL((select_kernel<NT, KPT, 1, false>), grid, dim3(NT), 0, st, p);
+    else if (vec)
+      hipLaunchKernelGGL((select_kernel<NT, KPT, 0, true>), grid, dim3(NT), 0, st, p);
+    else
+      hipLaunchKernelGGL((select_kernel<NT, KPT, 0, false>), grid, dim3(NT), 0, st, p);
   }
   return hipGetLastError();
 }
@@ -514,24 +516,24 @@ hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st)
   if (kind == SelectKind::kUnion) {
     // The union's extra passes hold more registers: past 8192 slots it runs 512-thread tiers
     // (a 1024-thread workgroup is limited to 128 registers per lane).
-    if (t <= 256 * 4) return launch_cfg<256, 4>(p, kind, grid, st);
-    if (t <= 256 * 16) return launch_cfg<256, 16>(p, kind, grid, st);
-    if (t <= 256 * 32) return launch_cfg<256, 32>(p, kind, grid, st);
-    if (t <= 512 * 32) return launch_cfg<512, 32>(p, kind, grid, st);
-    if (t <= 512 * 64) return launch_cfg<512, 64>(p, kind, grid, st);
-    if (t <= 1024 * 64) return launch_cfg<1024, 64>(p, kind, grid, st);
+    if (t <= 256 * 4) return launch_cfg<256, 4, true>(p, kind, grid, st);
+    if (t <= 256 * 16) return launch_cfg<256, 16, true>(p, kind, grid, st);
+    if (t <= 256 * 32) return launch_cfg<256, 32, true>(p, kind, grid, st);
+    if (t <= 512 * 32) return launch_cfg<512, 32, true>(p, kind, grid, st);
+    if (t <= 512 * 64) return launch_cfg<512, 64, true>(p, kind, grid, st);
+    if (t <= 1024 * 64) return launch_cfg<1024, 64, true>(p, kind, grid, st);
     return hipErrorInvalidValue;
   }
-  if (t <= 256 * 4) return launch_cfg<256, 4>(p, kind, grid, st);
-  if (t <= 256 * 16) return launch_cfg<256, 16>(p, kind, grid, st);
-  if (t <= 256 * 32) return launch_cfg<256, 32>(p, kind, grid, st);
-  if (t <= 512 * 32) return launch_cfg<512, 32>(p, kind, grid, st);
+  if (t <= 256 * 4) return launch_cfg<256, 4, false>(p, kind, grid, st);
+  if (t <= 256 * 16) return launch_cfg<256, 16, false>(p, kind, grid, st);
+  if (t <= 256 * 32) return launch_cfg<256, 32, false>(p, kind, grid, st);
+  if (t <= 512 * 32) return launch_cfg<512, 32, false>(p, kind, grid, st);
 #if KV_SELECT_WIDE
-  if (t <= 512 * 64) return launch_cfg<512, 64>(p, kind, grid, st);
+  if (t <= 512 * 64) return launch_cfg<512, 64, false>(p, kind, grid, st);
 #else
-  if (t <= 1024 * 32) return launch_cfg<1024, 32>(p, kind, grid, st);
+  if (t <= 1024 * 32) return launch_cfg<1024, 32, false>(p, kind, grid, st);
 #endif
-  if (t <= 1024 * 64) return launch_cfg<1024, 64>(p, kind, grid, st);
+  if (t <= 1024 * 64) return launch_cfg<1024, 64, false>(p, kind, grid, st);
   return hipErrorInvalidValue;
 }
 
