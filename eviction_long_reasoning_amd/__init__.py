@@ -17,14 +17,15 @@ and the policy variants:
   kv_select_random_shared  one random keep-set shared by every head
   kv_select_recent         keep the prompt and the latest slots
   kv_compact_inplace       fill evicted slots with the kept rows beyond the new length
+  kv_audit_kept            per-head count of kept-list entries that break the partition rules
 
 The binding holds no arithmetic of its own and has no CPU fallback: without
 the built library every call raises.
 """
 from ._lib import KvError, library_path, load as load_library
-from .binding import (gqa_workspace_bytes, kv_compact, kv_compact_inplace, kv_select_random, kv_select_random_shared,
+from .binding import (gqa_workspace_bytes, kv_audit_kept, kv_compact, kv_compact_inplace, kv_select_random, kv_select_random_shared,
                       kv_select_recent, kv_select_union, kv_select_topk, tri_score, tri_score_gqa, tri_score_rotated)
 
 __all__ = ["tri_score", "tri_score_rotated", "tri_score_gqa", "gqa_workspace_bytes", "kv_select_topk", "kv_select_random", "kv_compact",
-           "kv_select_union", "kv_select_random_shared", "kv_select_recent", "kv_compact_inplace", "KvError", "library_path",
+           "kv_select_union", "kv_select_random_shared", "kv_select_recent", "kv_compact_inplace", "kv_audit_kept", "KvError", "library_path",
            "load_library"]

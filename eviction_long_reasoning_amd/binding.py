@@ -290,6 +290,28 @@ def kv_select_recent(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tens
     return kept, n_kept
 
 
+def kv_audit_kept(kept: torch.Tensor, n_kept: torch.Tensor, seq_len: torch.Tensor, prompt_len: torch.Tensor,
+                  budget: int, recent: int, prompt_cap: int, t_cap: int,
+                  bad: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-head count of kept-list entries that break the partition rules (int32 [L,S,H]; 0 = valid)."""
+    if kept.dim() != 4:
+        raise ValueError("kept must be [L,S,H,b_cap]")
+    L, S, H, b_cap = kept.shape
+    dev = kept.device
+    kp = _dev_ptr(kept, "kept", torch.int32, (L, S, H, b_cap), dev)
+    nkp = _dev_ptr(n_kept, "n_kept", torch.int32, (S,), dev)
+    sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
+    pl = _dev_ptr(prompt_len, "prompt_len", torch.int32, (S,), dev)
+    if bad is None:
+        bad = torch.empty((L, S, H), dtype=torch.int32, device=dev)
+    bp = _dev_ptr(bad, "bad", torch.int32, (L, S, H), dev)
+    shape = _shape(L, S, H, 0, int(t_cap), 0, sp)
+    pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
+    st = _lib.load().kv_audit_kept(ctypes.byref(shape), ctypes.byref(pol), kp, int(b_cap), nkp, bp, _stream(dev))
+    _lib.check("kv_audit_kept", st)
+    return bad
+
+
 def kv_compact_inplace(K: torch.Tensor, V: torch.Tensor, kept: torch.Tensor, n_kept: torch.Tensor,
                        seq_len: torch.Tensor, pos: Optional[torch.Tensor] = None) -> None:
     """In-place hole filling: afterwards slots 0..n_kept-1 of each head hold the kept rows."""

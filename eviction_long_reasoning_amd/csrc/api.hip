@@ -308,6 +308,15 @@ KV_EXPORT kv_status kv_select_union(const kv_shape *shape, const kv_policy *poli
   return hip_status(launch_select(p, SelectKind::kUnion, static_cast<hipStream_t>(stream)));
 }
 
+KV_EXPORT kv_status kv_audit_kept(const kv_shape *shape, const kv_policy *policy, const int32_t *kept,
+                                  int32_t b_cap, const int32_t *n_kept, int32_t *bad, void *stream) {
+  SelectParams p{};
+  kv_status st = select_common(shape, policy, const_cast<int32_t *>(kept), b_cap, const_cast<int32_t *>(n_kept), p);
+  if (st != KV_OK) return st;
+  if (!bad) return KV_EINVAL;
+  return hip_status(launch_audit(p, bad, static_cast<hipStream_t>(stream)));
+}
+
 KV_EXPORT kv_status kv_select_random_shared(const kv_shape *shape, const kv_policy *policy, const int32_t *pos,
                                           uint64_t seed, uint32_t event, int32_t *kept, int32_t b_cap,
                                           int32_t *n_kept, void *stream) {

@@ -101,6 +101,7 @@ enum class SelectKind { kTopk, kRandom, kUnion };
 constexpr int kSelectMaxSlots = 65536;
 hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st);
 hipError_t launch_select_recent(const SelectParams &p, hipStream_t st);
+hipError_t launch_audit(const SelectParams &p, int32_t *bad, hipStream_t st);
 
 // -------------------------------------------------------------- compact ----
 struct CompactParams {

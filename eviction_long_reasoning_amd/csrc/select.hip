@@ -477,6 +477,41 @@ __global__ __launch_bounds__(256) void recent_kernel(const SelectParams p, int c
   p.kept[static_cast<size_t>(head) * p.b_cap + r] = v;
 }
 
+// Audit of a kept list against the partition rules: one workgroup per head counts the entries
+// that break them -- a kept index outside [0, T) or not above its predecessor, a prompt slot or
+// recent-window slot missing from its place, an entry past n_kept that is not -1 -- and writes
+// the count (0 = a valid keep-set), plus 1 if n_kept[s] differs from the partition's n_kept.
+__global__ __launch_bounds__(256) void audit_kernel(const SelectParams p, int32_t *bad) {
+  __shared__ int32_t red[4];
+  const int head = blockIdx.x;
+  const int s = (head / p.H) % p.S;
+  const int T = min(max(p.seq_len[s], 0), p.t_cap);
+  const int P = min(max(p.prompt_len[s], 0), min(p.prompt_cap, T));
+  const int B = p.budget;
+  const bool compress = T > B;
+  const int Rw = compress ? min(p.recent, min(max(0, B - P), T - P)) : 0;
+  const int n_kept = compress ? max(B, P) : T;
+  const int nk = p.n_kept[s];
+  const int32_t *kept = p.kept + static_cast<size_t>(head) * p.b_cap;
+  int count = 0;
+  for (int r = threadIdx.x; r < p.b_cap; r += 256) {
+    const int v = kept[r];
+    if (r >= n_kept) {
+      count += v != -1;
+    } else {
+      const bool in_range = v >= 0 && v < T;
+      const bool ascending = r == 0 || v > kept[r - 1];
+      const bool prompt_ok = r >= P || v == r;
+      const bool recent_ok = r < n_kept - Rw || v == T - (n_kept - r);
+      count += !(in_range && ascending && prompt_ok && recent_ok);
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) count += __shfl_xor(count, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = count;
+  __syncthreads();
+  if (threadIdx.x == 0) bad[head] = red[0] + red[1] + red[2] + red[3] + (nk != n_kept);
+}
+
 // Only the (tier, ranking) pairs launch_select dispatches are instantiated.
 template <int NT, int KPT, bool UNION>
 hipError_t launch_cfg(const SelectParams &p, SelectKind kind, dim3 grid, hipStream_t st) {
@@ -499,6 +534,13 @@ hipError_t launch_cfg(const SelectParams &p, SelectKind kind, dim3 grid, hipStre
 }
 
 }  // namespace
+
+hipError_t launch_audit(const SelectParams &p, int32_t *bad, hipStream_t st) {
+  const long long heads = static_cast<long long>(p.L) * p.S * p.H;
+  if (heads <= 0) return hipSuccess;
+  hipLaunchKernelGGL(audit_kernel, dim3(static_cast<unsigned>(heads)), dim3(256), 0, st, p, bad);
+  return hipGetLastError();
+}
 
 hipError_t launch_select_recent(const SelectParams &p, hipStream_t st) {
   const long long heads = static_cast<long long>(p.L) * p.S * p.H;

@@ -18,6 +18,10 @@
  *   kv_select_recent         keep the prompt and the latest slots (no scores)
  *   kv_compact_inplace       fill evicted slots with the kept rows beyond the new length
  *
+ * and a device-side check of any keep-set against the partition rules:
+ *
+ *   kv_audit_kept            count, per head, the entries of a kept list that break the rules
+ *
  * Conventions shared by every call
  * --------------------------------
  *  - All array arguments are DEVICE pointers owned by the caller, except
@@ -267,6 +271,21 @@ kv_status kv_select_random(const kv_shape *shape, const kv_policy *policy,
                            const int32_t *pos, uint64_t seed, uint32_t event,
                            int32_t *kept, int32_t b_cap, int32_t *n_kept,
                            void *stream);
+
+/*
+ * kv_audit_kept -- device-side audit of kept lists (for instance a caller's own selection, or a
+ * selection after the cache was edited). For each (l, s, h), bad[l,s,h] is the number of
+ * entries that break the partition rules above: an index r < n_kept whose slot lies outside
+ * [0, T_s) or does not exceed kept[r-1]; r < P whose slot is not r (prompt); one of the last R'
+ * entries that is not the matching slot of the recent window; r >= n_kept (below b_cap) that is
+ * not -1; plus 1 when n_kept[s] differs from the partition's n_kept. 0 means a valid keep-set.
+ * Memory safety never depends on the kept values.
+ *
+ *  kept, b_cap, n_kept as written by the selectors (device).
+ *  bad     device [L,S,H] int32 output.
+ */
+kv_status kv_audit_kept(const kv_shape *shape, const kv_policy *policy, const int32_t *kept,
+                        int32_t b_cap, const int32_t *n_kept, int32_t *bad, void *stream);
 
 /*
  * kv_select_union -- union-based selection ([TA-blog] eviction step) over the

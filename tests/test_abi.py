@@ -122,6 +122,8 @@ def test_host_validation_rejects_bad_arguments(lib):
                                None) == L.KV_EINVAL
     assert lib.kv_select_union(ctypes.byref(big), ctypes.byref(pol), 2, 0, dummy, dummy, dummy, 8, dummy,
                                None) == L.KV_ESHAPE
+    assert lib.kv_audit_kept(ctypes.byref(sh), ctypes.byref(pol), dummy, 8, dummy, None, None) == L.KV_EINVAL
+    assert lib.kv_audit_kept(ctypes.byref(sh), ctypes.byref(pol), dummy, 7, dummy, dummy, None) == L.KV_ESHAPE
     a = ctypes.c_void_p(0x100000)
     assert lib.kv_compact_inplace(ctypes.byref(sh), a, ctypes.c_void_p(0x100010), None, dummy, 8, dummy,
                                   None) == L.KV_EINVAL

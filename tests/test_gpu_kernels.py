@@ -614,3 +614,34 @@ def test_calls_run_on_the_current_stream():
         assert torch.equal(ref[0][:, s_, :, :T_].view(torch.int32), got[0][:, s_, :, :T_].view(torch.int32))
     assert torch.equal(ref[1], got[1])
     assert torch.equal(ref[2][..., :1000, :].view(torch.int16), got[2][..., :1000, :].view(torch.int16))
+
+
+def test_audit_accepts_every_selector_and_flags_broken_lists():
+    L, S, H, t_cap = 2, 3, 2, 5000
+    Ts, Ps, B, R = [5000, 1800, 4000], [100, 0, 3900], 2000, 64
+    pcap = max(Ps)
+    sc = torch.from_numpy(random_scores(77, (L, S, H, t_cap), ties=0.2)).to(DEV)
+    hs = torch.from_numpy(random_scores(78, (L, S, H, 3, t_cap))).to(DEV)
+    Td, Pd = _i32(Ts), _i32(Ps)
+    lists = {
+        "topk": kv.kv_select_topk(sc, Td, Pd, B, R, pcap),
+        "random": kv.kv_select_random((L, S, H, t_cap), Td, Pd, B, R, pcap, 5, 1),
+        "shared": kv.kv_select_random_shared((L, S, H, t_cap), Td, Pd, B, R, pcap, 5, 1),
+        "recent": kv.kv_select_recent((L, S, H, t_cap), Td, Pd, B, R, pcap),
+        "union": kv.kv_select_union(hs, sc, Td, Pd, B, R, pcap),
+    }
+    for name, (kept, nk) in lists.items():
+        bad = kv.kv_audit_kept(kept, nk, Td, Pd, B, R, pcap, t_cap)
+        assert int(bad.abs().sum()) == 0, name
+    kept, nk = lists["topk"]
+    k2 = kept.clone()
+    k2[0, 0, 0, 500], k2[0, 0, 0, 501] = kept[0, 0, 0, 501], kept[0, 0, 0, 500]     # order broken
+    k2[1, 2, 1, 7] = 3999                                                             # prompt slot replaced
+    k2[0, 1, 1, nk[1].item()] = 0                                                    # padding overwritten
+    bad = kv.kv_audit_kept(k2, nk, Td, Pd, B, R, pcap, t_cap).cpu().numpy()
+    assert bad[0, 0, 0] >= 1 and bad[1, 2, 1] >= 1 and bad[0, 1, 1] == 1
+    assert bad.sum() == bad[0, 0, 0] + bad[1, 2, 1] + bad[0, 1, 1]
+    nk2 = nk.clone()
+    nk2[2] += 1
+    bad = kv.kv_audit_kept(kept, nk2, Td, Pd, B, R, pcap, t_cap).cpu().numpy()
+    assert np.all(bad[:, 2] == 1) and bad[:, :2].sum() == 0
