@@ -42,21 +42,29 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, jobs: int = 8, out: str = LIB_PATH, defines=()) -> str:
+def build(verbose: bool = False, jobs: int = 8, out: str = LIB_PATH, defines=(), host_flags=(),
+          tag: str = "", device_flags=()) -> str:
     """Compile every kernel source and link ``libkvevict.so`` (or ``out``); returns its path.
 
     ``defines`` are extra ``NAME=VALUE`` preprocessor definitions (tuning knobs such as
-    KV_SCORE_BATCHES_PER_WAVE); the default build uses none.
+    KV_SCORE_BATCHES_PER_WAVE); the default build uses none. ``host_flags`` apply to the host
+    compilation and the link only (each is passed as ``-Xarch_host <flag>``), for
+    instance a sanitizer for the host-side argument checks; ``tag`` names their object folder.
+    ``device_flags`` likewise apply to the device compilation only (``-Xarch_device <flag>``);
+    ``("-O0",)`` gives a quick build for host-side checks that launch no kernel.
     """
     hipcc = _hipcc()
-    bdir = BUILD_DIR if not defines else os.path.join(BUILD_DIR, "_".join(d.replace("=", "") for d in defines))
+    sub = "_".join([d.replace("=", "") for d in defines] + ([tag] if tag else []))
+    bdir = BUILD_DIR if not sub else os.path.join(BUILD_DIR, sub)
     os.makedirs(bdir, exist_ok=True)
     srcs = sources()
     dflags = [f"-D{d}" for d in defines]
+    hflags = [x for f in host_flags for x in ("-Xarch_host", f)]
+    xflags = [x for f in device_flags for x in ("-Xarch_device", f)]
 
     def compile_one(src):
         obj = os.path.join(bdir, os.path.basename(src)[:-4] + ".o")
-        cmd = [hipcc, *COMPILE_FLAGS, *dflags, "-c", src, "-o", obj]
+        cmd = [hipcc, *COMPILE_FLAGS, *dflags, *hflags, *xflags, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -67,7 +75,7 @@ def build(verbose: bool = False, jobs: int = 8, out: str = LIB_PATH, defines=())
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
         objs = list(ex.map(compile_one, srcs))
     tmp = out + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *hflags, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
