@@ -80,6 +80,9 @@ def test_host_validation_rejects_bad_arguments(lib):
     pg = L.KvPaged(dummy, 1, 8, 4)        # 1 block of 8 cannot hold t_cap = 16 slots
     assert lib.tri_score_rotated(ctypes.byref(sh), dummy, ctypes.byref(pg), 0, dummy, None, dummy, 1e4, arr, 1,
                                  dummy, None) == L.KV_ESHAPE
+    # one head's bf16 d = 128 rows beyond 32-bit byte offsets
+    huge = L.KvShape(1, 1, 1, 128, ((1 << 31) - (64 << 9)) // 256, L.KV_BF16, seq)
+    assert lib.tri_score(ctypes.byref(huge), dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, None) == L.KV_ESHAPE
     big = L.KvShape(1, 1, 1, 8, 65537, L.KV_BF16, seq)
     # grouped-query scores: group outside 1..16, workspace too small, fp32 head_dim beyond 128
     shg = L.KvShape(2, 3, 4, 128, 1000, L.KV_BF16, None)

@@ -102,6 +102,35 @@ NORM_CASES = [c for c in SCORE_CASES if c[0] in ("tiny-fp32-d64", "bf16-d128-rag
                                                   "bf16-d96-idle-lanes", "fp32-d128")]
 
 
+# The largest bf16 d = 128 cache one head may hold: its rows are addressed with 32-bit byte offsets
+# (t_cap * 256 bytes plus one batch of look-ahead must stay below 2^31).
+MAX_T_CAP_BF16_D128 = ((1 << 31) - (64 << 9)) // 256 - 1
+
+
+def test_score_at_the_largest_t_cap_matches_oracle_on_sampled_slots():
+    d, t_cap, theta, D = 128, MAX_T_CAP_BF16_D128, 1e6, [2 ** i for i in range(17)]
+    log(f"[score-max] bf16 d{d} t_cap {t_cap} ({t_cap * d * 2 / 2 ** 30:.2f} GiB of keys)")
+    r = rng(560, 1)
+    block = (r.standard_normal(d) + 0.3 * r.standard_normal((1 << 16, d))).astype(np.float32)
+    qb = r.standard_normal((1, 1, d)).astype(np.float32)
+    kb = torch.from_numpy(bf16_bits(block).view(np.int16)).to(DEV)
+    reps = -(-t_cap // block.shape[0])
+    K = kb.repeat(reps, 1)[:t_cap].contiguous().view(torch.bfloat16).view(1, 1, 1, t_cap, d)
+    del kb
+    Ts = np.array([t_cap], np.int32)
+    t_cur = np.array([t_cap + 3], np.int32)
+    out = torch.full((1, 1, 1, t_cap), float("nan"), device=DEV)
+    kv.tri_score(K, torch.from_numpy(qb).to(DEV), _i32(t_cur), _i32(Ts), theta, D, out=out)
+    sample = np.unique(np.concatenate([np.arange(64), np.arange(t_cap - 256, t_cap),
+                                       r.choice(t_cap, size=4096, replace=False)]))
+    got = out[0, 0, 0, torch.from_numpy(sample).to(DEV)].cpu().numpy()
+    Kh = keys_f64(bf16_bits(block[sample % block.shape[0]]), "bf16")
+    ref = oracle.score_literal(Kh, sample.astype(np.int64), qb[0, 0], int(t_cur[0]), theta, D)
+    worst = assert_scores(got, ref, "largest t_cap")
+    assert not torch.isnan(out).any().item(), "a slot below T was not written"
+    log(f"[score-max] {sample.size} sampled slots: worst scaled error {worst:.2e}")
+
+
 @pytest.mark.parametrize("case", NORM_CASES, ids=[c[0] for c in NORM_CASES])
 def test_score_with_norm_term_matches_oracle(case):
     name, dtype, d, L, S, H, Ts, t_cap, theta, D, pmode, toff = case
