@@ -40,8 +40,16 @@ def _dev_ptr(t: Optional[torch.Tensor], name: str, dtype=None, shape=None, devic
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+def _invoke(name: str, device, *args) -> None:
+    """Call entry point ``name`` with ``device`` current and its current stream as the last argument.
+
+    The library launches on the calling thread's current HIP device, so a tensor on another device
+    than the current one would otherwise get its kernels on the wrong GPU.
+    """
+    fn = getattr(_lib.load(), name)
+    with torch.cuda.device(device):
+        st = fn(*args, ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream))
+    _lib.check(name, st)
 
 
 def _shape(L, S, H, d, t_cap, dtype_code, seq_len_ptr) -> _lib.KvShape:
@@ -71,9 +79,7 @@ def tri_score(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len:
     dl = [int(x) for x in deltas]
     arr = (ctypes.c_int32 * max(1, len(dl)))(*dl)
     shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
-    st = _lib.load().tri_score(ctypes.byref(shape), kp, pp, qp, ap, tp, float(rope_theta), arr, len(dl), op,
-                               _stream(dev))
-    _lib.check("tri_score", st)
+    _invoke("tri_score", dev, ctypes.byref(shape), kp, pp, qp, ap, tp, float(rope_theta), arr, len(dl), op)
     return out
 
 
@@ -115,9 +121,8 @@ def tri_score_rotated(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, 
     dl = [int(x) for x in deltas]
     arr = (ctypes.c_int32 * max(1, len(dl)))(*dl)
     shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
-    st = _lib.load().tri_score_rotated(ctypes.byref(shape), kp, None if paged is None else ctypes.byref(paged),
-                                       style, qp, ap, tp, float(rope_theta), arr, len(dl), op, _stream(dev))
-    _lib.check("tri_score_rotated", st)
+    _invoke("tri_score_rotated", dev, ctypes.byref(shape), kp, None if paged is None else ctypes.byref(paged),
+            style, qp, ap, tp, float(rope_theta), arr, len(dl), op)
     return out
 
 
@@ -160,9 +165,8 @@ def tri_score_gqa(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_
     wp = _dev_ptr(workspace, "workspace", torch.uint8, None, dev)
     dl = [int(x) for x in deltas]
     arr = (ctypes.c_int32 * max(1, len(dl)))(*dl)
-    st = lib.tri_score_gqa(ctypes.byref(shape), kp, pp, int(G), qp, ap, tp, float(rope_theta), arr, len(dl), hp, op,
-                           wp, workspace.numel(), _stream(dev))
-    _lib.check("tri_score_gqa", st)
+    _invoke("tri_score_gqa", dev, ctypes.byref(shape), kp, pp, int(G), qp, ap, tp, float(rope_theta), arr,
+            len(dl), hp, op, wp, workspace.numel())
     return out, head_out
 
 
@@ -198,8 +202,7 @@ def kv_select_topk(scores: torch.Tensor, seq_len: torch.Tensor, prompt_len: torc
     kept, n_kept, kp, nkp = _select_io(L, S, H, b_cap, dev, kept, n_kept)
     shape = _shape(L, S, H, 0, t_cap, 0, sp)
     pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
-    st = _lib.load().kv_select_topk(ctypes.byref(shape), ctypes.byref(pol), sc, kp, b_cap, nkp, _stream(dev))
-    _lib.check("kv_select_topk", st)
+    _invoke("kv_select_topk", dev, ctypes.byref(shape), ctypes.byref(pol), sc, kp, b_cap, nkp)
     return kept, n_kept
 
 
@@ -218,9 +221,8 @@ def kv_select_random(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tens
     kept, n_kept, kp, nkp = _select_io(L, S, H, b_cap, dev, kept, n_kept)
     shape = _shape(L, S, H, 0, t_cap, 0, sp)
     pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
-    st = _lib.load().kv_select_random(ctypes.byref(shape), ctypes.byref(pol), pp, int(seed) & (2 ** 64 - 1),
-                                      int(event) & 0xFFFFFFFF, kp, b_cap, nkp, _stream(dev))
-    _lib.check("kv_select_random", st)
+    _invoke("kv_select_random", dev, ctypes.byref(shape), ctypes.byref(pol), pp, int(seed) & (2 ** 64 - 1),
+            int(event) & 0xFFFFFFFF, kp, b_cap, nkp)
     return kept, n_kept
 
 
@@ -245,9 +247,8 @@ def kv_select_union(head_scores: torch.Tensor, scores: torch.Tensor, seq_len: to
     kept, n_kept, kp, nkp = _select_io(L, S, H, b_cap, dev, kept, n_kept)
     shape = _shape(L, S, H, 0, t_cap, 0, sp)
     pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
-    st = _lib.load().kv_select_union(ctypes.byref(shape), ctypes.byref(pol), int(G), int(k_per_head), hp, cp, kp,
-                                     b_cap, nkp, _stream(dev))
-    _lib.check("kv_select_union", st)
+    _invoke("kv_select_union", dev, ctypes.byref(shape), ctypes.byref(pol), int(G), int(k_per_head), hp, cp, kp,
+            b_cap, nkp)
     return kept, n_kept
 
 
@@ -266,9 +267,8 @@ def kv_select_random_shared(cache_shape: Tuple[int, int, int, int], seq_len: tor
     kept, n_kept, kp, nkp = _select_io(L, S, H, b_cap, dev, kept, n_kept)
     shape = _shape(L, S, H, 0, t_cap, 0, sp)
     pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
-    st = _lib.load().kv_select_random_shared(ctypes.byref(shape), ctypes.byref(pol), pp, int(seed) & (2 ** 64 - 1),
-                                             int(event) & 0xFFFFFFFF, kp, b_cap, nkp, _stream(dev))
-    _lib.check("kv_select_random_shared", st)
+    _invoke("kv_select_random_shared", dev, ctypes.byref(shape), ctypes.byref(pol), pp,
+            int(seed) & (2 ** 64 - 1), int(event) & 0xFFFFFFFF, kp, b_cap, nkp)
     return kept, n_kept
 
 
@@ -285,8 +285,7 @@ def kv_select_recent(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tens
     kept, n_kept, kp, nkp = _select_io(L, S, H, b_cap, dev, kept, n_kept)
     shape = _shape(L, S, H, 0, t_cap, 0, sp)
     pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
-    st = _lib.load().kv_select_recent(ctypes.byref(shape), ctypes.byref(pol), kp, b_cap, nkp, _stream(dev))
-    _lib.check("kv_select_recent", st)
+    _invoke("kv_select_recent", dev, ctypes.byref(shape), ctypes.byref(pol), kp, b_cap, nkp)
     return kept, n_kept
 
 
@@ -307,8 +306,7 @@ def kv_audit_kept(kept: torch.Tensor, n_kept: torch.Tensor, seq_len: torch.Tenso
     bp = _dev_ptr(bad, "bad", torch.int32, (L, S, H), dev)
     shape = _shape(L, S, H, 0, int(t_cap), 0, sp)
     pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
-    st = _lib.load().kv_audit_kept(ctypes.byref(shape), ctypes.byref(pol), kp, int(b_cap), nkp, bp, _stream(dev))
-    _lib.check("kv_audit_kept", st)
+    _invoke("kv_audit_kept", dev, ctypes.byref(shape), ctypes.byref(pol), kp, int(b_cap), nkp, bp)
     return bad
 
 
@@ -326,8 +324,7 @@ def kv_compact_inplace(K: torch.Tensor, V: torch.Tensor, kept: torch.Tensor, n_k
     sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
     pp = _dev_ptr(pos, "pos", torch.int32, (L, S, H, t_cap), dev)
     shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
-    st = _lib.load().kv_compact_inplace(ctypes.byref(shape), kp_, vp_, pp, kp, int(b_cap), nkp, _stream(dev))
-    _lib.check("kv_compact_inplace", st)
+    _invoke("kv_compact_inplace", dev, ctypes.byref(shape), kp_, vp_, pp, kp, int(b_cap), nkp)
 
 
 def kv_compact(K: torch.Tensor, V: torch.Tensor, kept: torch.Tensor, n_kept: torch.Tensor, seq_len: torch.Tensor,
@@ -355,7 +352,6 @@ def kv_compact(K: torch.Tensor, V: torch.Tensor, kept: torch.Tensor, n_kept: tor
     vop = _dev_ptr(V_out, "V_out", K.dtype, (L, S, H, out_cap, d), dev)
     pop = _dev_ptr(pos_out, "pos_out", torch.int32, (L, S, H, out_cap), dev)
     shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
-    st = _lib.load().kv_compact(ctypes.byref(shape), kin, vin, pp, kp, int(b_cap), nkp, kop, vop, pop,
-                                int(out_cap), _stream(dev))
-    _lib.check("kv_compact", st)
+    _invoke("kv_compact", dev, ctypes.byref(shape), kin, vin, pp, kp, int(b_cap), nkp, kop, vop, pop,
+            int(out_cap))
     return K_out, V_out, pos_out
