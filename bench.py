@@ -112,7 +112,7 @@ def cpu_baseline(w, K, qb, n_heads: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "the KV-eviction path runs on one GPU; --gpus must be 1 "
                                    "(the path shards per (layer, seq, KV head) with no exchange)"}))
         sys.exit(2)
     import numpy as np
