@@ -68,7 +68,7 @@ def counter_traffic():
         return None
     text = open(path).read()
     h = hashlib.sha256()
-    for f in ("score.hip", "kv_internal.hpp"):
+    for f in ("score.hip", "score_params.hpp"):
         h.update(open(os.path.join(ROOT, "eviction_long_reasoning_amd", "csrc", f), "rb").read())
     m = re.search(r"sha256 `([0-9a-f]+)`", text)
     row = re.search(r"^\| `void score_stream_kernel<[^`]*>` \| ([0-9.]+) \| ([0-9.]+) \|", text, re.M)
@@ -284,6 +284,26 @@ def main():
     del zmax, head3
     recent_ms = time_launches(lambda: kv.kv_select_recent((L, S, H, Tc), seq, plen, w.budget, w.recent,
                                                           w.prompt_cap(), b_cap=b_cap, kept=kept, n_kept=nk))
+    # 131072-token caches (context lengths reach 128K tokens): the same score memory viewed as
+    # L layers x S/4 seqs x 8 KV heads of 4 * T slots, past the selectors' register tiers
+    long_sel = None
+    if S % 4 == 0:
+        Sl, Tl = S // 4, 4 * Tc
+        sc_long = scores.view(L, Sl, H, Tl)
+        seq_l, plen_l = i32(np.full(Sl, Tl)), i32(np.full(Sl, w.prompt_len[0]))
+        kept_l = torch.empty((L, Sl, H, b_cap), dtype=torch.int32, device=dev)
+        nk_l = torch.empty((Sl,), dtype=torch.int32, device=dev)
+        lt_ms = time_launches(lambda: kv.kv_select_topk(sc_long, seq_l, plen_l, w.budget, w.recent, w.prompt_cap(),
+                                                        b_cap=b_cap, kept=kept_l, n_kept=nk_l))
+        lr_ms = time_launches(lambda: kv.kv_select_random((L, Sl, H, Tl), seq_l, plen_l, w.budget, w.recent,
+                                                          w.prompt_cap(), 1, 0, b_cap=b_cap, kept=kept_l,
+                                                          n_kept=nk_l))
+        n_long = L * Sl * H * Tl
+        long_sel = {"t_cap": Tl, "heads": L * Sl * H, "topk_ms": lt_ms, "random_ms": lr_ms,
+                    "topk_entries_per_s": n_long / (lt_ms * 1e-3), "random_entries_per_s": n_long / (lr_ms * 1e-3)}
+        print(f"[bench] {Tl}-slot caches: top-k select {lt_ms:.3f} ms, random select {lr_ms:.3f} ms",
+              file=sys.stderr, flush=True)
+        del sc_long, kept_l
 
     w4 = workload(4)
     mu4, qb4, _ = centres(w4)
@@ -384,6 +404,7 @@ def main():
         "select_union": {"group": w.group, "ms_per_launch": union_ms, "algorithmic_bytes": union_bytes,
                          "gbs": union_bytes / (union_ms * 1e-3) / 1e9},
         "select_recent": {"ms_per_launch": recent_ms},
+        "select_long_cache": long_sel,
         "periodic_event": periodic,
         "cpu_baseline": cpu,
     }

@@ -248,13 +248,14 @@ KV_EXPORT kv_status tri_score_gqa(const kv_shape *shape, const void *K, const in
   return hip_status(launch_score_gqa(p, shape->dtype == KV_BF16, ppq, static_cast<hipStream_t>(stream)));
 }
 
+// max_slots: the largest t_cap the selector kernel behind the entry point takes.
 static kv_status select_common(const kv_shape *shape, const kv_policy *policy, int32_t *kept, int32_t b_cap,
-                               int32_t *n_kept, SelectParams &p) {
+                               int32_t *n_kept, SelectParams &p, int max_slots = kSelectMaxSlotsStream) {
   kv_status st = check_shape(shape, false);
   if (st != KV_OK) return st;
   if ((st = check_policy(policy, b_cap)) != KV_OK) return st;
   if (!kept || !n_kept) return KV_EINVAL;
-  if (shape->t_cap > kSelectMaxSlots) return KV_ESHAPE;
+  if (shape->t_cap > max_slots) return KV_ESHAPE;
   p.seq_len = shape->seq_len;
   p.prompt_len = policy->prompt_len;
   p.kept = kept;
@@ -297,7 +298,7 @@ KV_EXPORT kv_status kv_select_union(const kv_shape *shape, const kv_policy *poli
                                     int32_t k_per_head, const float *head_scores, const float *scores,
                                     int32_t *kept, int32_t b_cap, int32_t *n_kept, void *stream) {
   SelectParams p{};
-  kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p);
+  kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p, kSelectMaxSlots);
   if (st != KV_OK) return st;
   if (!head_scores || !scores) return KV_EINVAL;
   if (group < 1 || group > 64) return KV_EINVAL;

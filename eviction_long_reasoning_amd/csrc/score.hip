@@ -31,7 +31,7 @@
 //    reduce-scatter (LPK-1 exchanges per lane for LPK keys), after which each
 //    lane holds one finished score: 64 consecutive scores leave in one
 //    coalesced 256-byte store.
-#include "kv_internal.hpp"
+#include "score_params.hpp"
 
 #ifndef KV_SCORE_PIPELINE
 #define KV_SCORE_PIPELINE 1

@@ -31,6 +31,10 @@
 #ifndef KV_SELECT_WIDE
 #define KV_SELECT_WIDE 0
 #endif
+// top-k and random caches longer than this run the kernel that re-reads its keys
+#ifndef KV_SELECT_STREAM_ABOVE
+#define KV_SELECT_STREAM_ABOVE 65536
+#endif
 
 namespace kvevict {
 namespace {
@@ -457,6 +461,194 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   if (writer) p.n_kept[s] = n_kept;
 }
 
+// Caches longer than the register tiers hold (t_cap > 65536 slots; long-context models reach
+// 128K tokens): the same two rankings, threshold rule and ordered scan, with every step
+// recomputing the keys from memory (a score load, or the Philox draw) instead of keeping them in
+// registers. Steps: min/max and a value-binned histogram (scores only), OR/AND of the member
+// keys, 8-bit radix passes from their highest differing bit, then the ordered scan in chunks of
+// 4 * NT slots in slot order with the kept and tied counts carried from chunk to chunk.
+constexpr int kStreamThreads = 1024;
+
+template <int KIND>
+__global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const SelectParams p) {
+  constexpr int NT = kStreamThreads;
+  constexpr int NW = NT / 64;
+  constexpr bool RANDOM = KIND == 1;
+  __shared__ uint32_t hist[kValueBins];
+  __shared__ uint32_t red[2 * NW];
+  __shared__ uint32_t wsum[2 * NW];
+  __shared__ uint32_t found[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int head = blockIdx.x;
+  const int h = head % p.H;
+  const int s = (head / p.H) % p.S;
+  const int l = head / (p.H * p.S);
+
+  const int T = min(max(p.seq_len[s], 0), p.t_cap);
+  const int P = min(max(p.prompt_len[s], 0), min(p.prompt_cap, T));
+  const int B = p.budget;
+  int32_t *out = p.kept + static_cast<size_t>(head) * p.b_cap;
+  const bool writer = (l == 0 && h == 0 && tid == 0);
+
+  if (T <= B) {  // nothing to compress: keep 0..T-1
+    for (int r = tid; r < p.b_cap; r += NT) out[r] = r < T ? r : -1;
+    if (writer) p.n_kept[s] = T;
+    return;
+  }
+  const int Rw = min(p.recent, min(max(0, B - P), T - P));
+  const int e_lo = P, e_hi = T - Rw;
+  const int n_sel = max(0, B - P - Rw);
+  const int n_kept = max(B, P);
+  const int n_cand = e_hi - e_lo;
+  const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
+  const uint32_t c1 = p.shared_draw ? 0u : (static_cast<uint32_t>(l) << 16) | static_cast<uint32_t>(h);
+  auto key_of = [&](int j) -> uint32_t {  // j in [e_lo, e_hi)
+    if (RANDOM) {
+      const uint32_t c0 = p.pos ? static_cast<uint32_t>(p.pos[slot0 + j]) : static_cast<uint32_t>(j);
+      return philox_word0(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
+    }
+    return order_key(p.scores[slot0 + j]);
+  };
+
+  // mode: 0 = select none, 1 = select all candidates, 2 = threshold rule
+  int mode;
+  uint32_t thr = 0u, need = 0u;
+  if (n_sel <= 0 || n_cand <= 0) {
+    mode = 0;
+  } else if (n_sel >= n_cand) {
+    mode = 1;
+  } else {
+    mode = 2;
+    uint32_t remaining = static_cast<uint32_t>(n_sel);
+    // member keys: every candidate, or (scores with a usable value range) those in the value bin
+    // that holds the threshold
+    bool binned = false;
+    uint32_t bsel = 0u;
+    float fmin = 0.f, scale = 0.f;
+    if (!RANDOM) {
+      uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+      for (int j = e_lo + tid; j < e_hi; j += NT) {
+        const uint32_t k = key_of(j);
+        if (k > kKeyNegInf && k < kKeyPosInf) {
+          kmn = min(kmn, k);
+          kmx = max(kmx, k);
+        }
+      }
+      block_min_max<NT>(kmn, kmx, red);
+      fmin = key_value(kmn);
+      const float fmax = key_value(kmx);
+      scale = static_cast<float>(kValueBins) / (fmax - fmin);
+      if (kmn < kmx && scale > 0.f && scale < 3.0e38f) {
+        for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
+        __syncthreads();
+        for (int j = e_lo + tid; j < e_hi; j += NT) atomicAdd(&hist[value_bin(key_of(j), fmin, scale)], 1u);
+        __syncthreads();
+        if (wave == 0) find_bin<kValueBins>(hist, remaining, lane, found);
+        __syncthreads();
+        bsel = found[0];
+        remaining -= found[1];
+        binned = true;
+        __syncthreads();  // `found` and `hist` are reused below
+      }
+    }
+    auto member = [&](uint32_t k) { return !binned || value_bin(k, fmin, scale) == bsel; };
+    uint32_t kor = 0u, kand = 0xFFFFFFFFu;
+    for (int j = e_lo + tid; j < e_hi; j += NT) {
+      const uint32_t k = key_of(j);
+      if (member(k)) {
+        kor |= k;
+        kand &= k;
+      }
+    }
+    block_or_and<NT>(kor, kand, red);
+    const uint32_t diff = kor ^ kand;
+    if (diff == 0u) {
+      thr = kand;  // all member keys equal
+    } else {
+      const int top = 31 - __clz(diff);
+      uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
+      uint32_t prefix = kand & mask;
+      for (int hi = top; hi >= 0;) {
+        const int lo = hi >= 7 ? hi - 7 : 0;
+        const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
+        for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+        __syncthreads();
+        for (int j = e_lo + tid; j < e_hi; j += NT) {
+          const uint32_t k = key_of(j);
+          if ((k & mask) == prefix && member(k)) atomicAdd(&hist[(k >> lo) & dmask], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) find_bin<256>(hist, remaining, lane, found);
+        __syncthreads();
+        prefix |= found[0] << lo;
+        mask |= dmask << lo;
+        remaining -= found[1];
+        hi = lo - 1;
+        __syncthreads();  // everyone has read `found` before the next pass may overwrite it
+      }
+      thr = prefix;
+    }
+    need = remaining;
+  }
+
+  // ordered scan: thread t takes slots c + 4t .. c + 4t + 3 of each chunk
+  uint32_t carry_a = 0u, carry_e = 0u;  // unconditional / tied slots in earlier chunks
+  for (int c = 0; c < T; c += 4 * NT) {
+    const int j0 = c + 4 * tid;
+    uint32_t fa = 0u, fe = 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = j0 + q;
+      if (j >= T) break;
+      const bool cnd = j >= e_lo && j < e_hi;
+      bool a = !cnd || mode == 1, e = false;   // prompt and recent window are pinned
+      if (cnd && mode == 2) {
+        const uint32_t k = key_of(j);
+        a = k > thr;
+        e = k == thr;
+      }
+      fa |= static_cast<uint32_t>(a) << q;
+      fe |= static_cast<uint32_t>(e) << q;
+    }
+    const uint32_t cnt = static_cast<uint32_t>(__popc(fa)) | (static_cast<uint32_t>(__popc(fe)) << 16);
+    const uint32_t x = wave_inclusive_sum(cnt);   // a wave's halves stay below 2^9
+    if (lane == 63) {
+      wsum[wave] = x & 0xFFFFu;
+      wsum[NW + wave] = x >> 16;
+    }
+    __syncthreads();
+    uint32_t na = carry_a + ((x - cnt) & 0xFFFFu), ne = carry_e + ((x - cnt) >> 16);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) {
+        na += wsum[w];
+        ne += wsum[NW + w];
+      }
+      carry_a += wsum[w];
+      carry_e += wsum[NW + w];
+    }
+    __syncthreads();  // wsum is rewritten by the next chunk
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if ((fa >> q) & 1u) {
+        const uint32_t o = na + min(ne, need);
+        if (o < static_cast<uint32_t>(p.b_cap)) out[o] = j0 + q;
+        ++na;
+      } else if ((fe >> q) & 1u) {
+        if (ne < need) {
+          const uint32_t o = na + ne;
+          if (o < static_cast<uint32_t>(p.b_cap)) out[o] = j0 + q;
+        }
+        ++ne;
+      }
+    }
+  }
+  for (int r = n_kept + tid; r < p.b_cap; r += NT) out[r] = -1;
+  if (writer) p.n_kept[s] = n_kept;
+}
+
 // Recency+prompt ("Random Attention", section 4.1, the StreamingLLM-style diagnostic): the
 // prompt and the n_kept - P latest slots, i.e. the evictable range's n_sel latest slots joined to
 // the recent window. No scores are read; one thread per output entry.
@@ -565,6 +757,13 @@ hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st)
     if (t <= 512 * 64) return launch_cfg<512, 64, true>(p, kind, grid, st);
     if (t <= 1024 * 64) return launch_cfg<1024, 64, true>(p, kind, grid, st);
     return hipErrorInvalidValue;
+  }
+  if (t > KV_SELECT_STREAM_ABOVE) {
+    if (kind == SelectKind::kRandom)
+      hipLaunchKernelGGL(select_stream_kernel<1>, grid, dim3(kStreamThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL(select_stream_kernel<0>, grid, dim3(kStreamThreads), 0, st, p);
+    return hipGetLastError();
   }
   if (t <= 256 * 4) return launch_cfg<256, 4, false>(p, kind, grid, st);
   if (t <= 256 * 16) return launch_cfg<256, 16, false>(p, kind, grid, st);

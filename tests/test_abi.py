@@ -83,7 +83,8 @@ def test_host_validation_rejects_bad_arguments(lib):
     # one head's bf16 d = 128 rows beyond 32-bit byte offsets
     huge = L.KvShape(1, 1, 1, 128, ((1 << 31) - (64 << 9)) // 256, L.KV_BF16, seq)
     assert lib.tri_score(ctypes.byref(huge), dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, None) == L.KV_ESHAPE
-    big = L.KvShape(1, 1, 1, 8, 65537, L.KV_BF16, seq)
+    big = L.KvShape(1, 1, 1, 8, 65537, L.KV_BF16, seq)          # past the union selector's register tiers
+    huge_sel = L.KvShape(1, 1, 1, 8, (1 << 26) + 1, L.KV_BF16, seq)  # past every selector
     # grouped-query scores: group outside 1..16, workspace too small, fp32 head_dim beyond 128
     shg = L.KvShape(2, 3, 4, 128, 1000, L.KV_BF16, None)
     need = lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg), 4)
@@ -117,7 +118,7 @@ def test_host_validation_rejects_bad_arguments(lib):
     pol = L.KvPolicy(8, 2, 4, seq)
     assert lib.kv_select_recent(ctypes.byref(sh), ctypes.byref(pol), dummy, 7, dummy, None) == L.KV_ESHAPE
     assert lib.kv_select_recent(ctypes.byref(sh), None, dummy, 8, dummy, None) == L.KV_EINVAL
-    assert lib.kv_select_random_shared(ctypes.byref(big), ctypes.byref(pol), None, 1, 0, dummy, 8, dummy,
+    assert lib.kv_select_random_shared(ctypes.byref(huge_sel), ctypes.byref(pol), None, 1, 0, dummy, 8, dummy,
                                        None) == L.KV_ESHAPE
     assert lib.kv_select_union(ctypes.byref(sh), ctypes.byref(pol), 4, 0, None, dummy, dummy, 8, dummy,
                                None) == L.KV_EINVAL
@@ -140,7 +141,10 @@ def test_host_validation_rejects_bad_arguments(lib):
     pol = L.KvPolicy(8, 2, 12, seq)
     assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 8, dummy, None) == L.KV_ESHAPE
     pol = L.KvPolicy(8, 2, 4, seq)
-    assert lib.kv_select_random(ctypes.byref(big), ctypes.byref(pol), None, 1, 0, dummy, 8, dummy, None) == L.KV_ESHAPE
+    assert lib.kv_select_random(ctypes.byref(huge_sel), ctypes.byref(pol), None, 1, 0, dummy, 8, dummy,
+                                None) == L.KV_ESHAPE
+    assert lib.kv_select_topk(ctypes.byref(huge_sel), ctypes.byref(pol), dummy, dummy, 8, dummy, None) == L.KV_ESHAPE
+    assert lib.kv_select_recent(ctypes.byref(huge_sel), ctypes.byref(pol), dummy, 8, dummy, None) == L.KV_ESHAPE
     pol = L.KvPolicy(0, 2, 4, seq)
     assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 8, dummy, None) == L.KV_EINVAL
     # compact: aliasing in/out is rejected

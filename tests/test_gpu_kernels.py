@@ -330,6 +330,15 @@ SELECT_CASES = [
     ("ulp-range", 4000, [4000], [10], 1500, 8, "ulp"),
     ("denormals", 2500, [2500], [0], 300, 4, "denormal"),
     ("inf-mix", 6000, [6000, 5000], [32, 0], 2048, 64, "infmix"),
+    # past 65536 slots: the kernel that re-reads its keys at every step
+    ("stream-70k-specials", 70000, [70000, 65537, 3000], [1024, 0, 100], 3072, 128, "specials"),
+    ("stream-128k", 131072, [131072, 100001], [2048, 4096], 4096, 128, "normal"),
+    ("stream-96k-ties", 98304, [98304, 80000], [512, 0], 3072, 64, "ties"),
+    ("stream-80k-concentrated", 80000, [80000], [64], 2048, 16, "concentrated"),
+    ("stream-66k-infmix", 66000, [66000, 66000], [32, 0], 2048, 64, "infmix"),
+    ("stream-66k-huge", 66000, [66000], [10], 1000, 8, "huge"),
+    ("stream-70k-equal", 70000, [70000], [100], 500, 10, "equal"),
+    ("stream-70k-prompt-over-budget", 70000, [70000, 69000], [2500, 2049], 2048, 128, "normal"),
 ]
 
 
@@ -505,9 +514,10 @@ def test_select_recent_bit_exact(case):
 
 
 @pytest.mark.parametrize("with_pos", [False, True])
-def test_select_random_shared_bit_exact(with_pos):
-    L, S, H, t_cap = 3, 2, 4, 5000
-    Ts, Ps, B, R = [5000, 3100], [200, 0], 1500, 64
+@pytest.mark.parametrize("t_cap", [5000, 70000])
+def test_select_random_shared_bit_exact(with_pos, t_cap):
+    L, S, H = 3, 2, 4
+    Ts, Ps, B, R = [t_cap, 3100], [200, 0], 1500, 64
     seed, event = 0x1234567890ABCDEF, 12
     pos = None
     if with_pos:

@@ -134,6 +134,35 @@ def test_workload2_full():
         assert np.array_equal(kr[0, 0, h, :ref.size], ref)
 
 
+def test_workload2_shape_at_128k_tokens():
+    # the Qwen3-8B-shaped layer at a 131072-token cache: past the selectors' register tiers, so
+    # the top-k and random selections run the kernel that re-reads its keys at every step
+    w = workload(2, T=131072)
+    K, V, _, qb = kv_numpy(w)
+    Kd, Vd = dev_from_host(K, w.dtype), dev_from_host(V, w.dtype)
+    T, P = w.seq_len, w.prompt_len
+    sc = kv.tri_score(Kd, torch.from_numpy(qb).to(DEV), i32(w.t_cur), i32(T), w.theta, w.deltas)
+    kept, nk = kv.kv_select_topk(sc, i32(T), i32(P), w.budget, w.recent, w.prompt_cap())
+    Ko, Vo, Po = kv.kv_compact(Kd, Vd, kept, nk, i32(T), w.out_cap)
+    check_structure(w, kept, nk, Kd, Ko, Po, T, P, "w2-128k")
+    sch, kh, Koh, Voh, Poh = sc.cpu().numpy(), kept.cpu().numpy(), host_bits(Ko), host_bits(Vo), Po.cpu().numpy()
+    worst, diffs = 0.0, 0
+    for h in range(w.n_kv_heads):
+        e, nd = compare_head(w, K[0, 0, h], V[0, 0, h], qb, 0, 0, h, int(T[0]), int(P[0]), int(w.t_cur[0]),
+                             sch[0, 0, h], kh[0, 0, h, :int(nk[0])], Koh[0, 0, h], Voh[0, 0, h], Poh[0, 0, h],
+                             "w2-128k")
+        worst, diffs = max(worst, e), diffs + nd
+        # the selector on the GPU's own scores is bit-exact
+        assert np.array_equal(kh[0, 0, h, :int(nk[0])],
+                              oracle.select_topk(sch[0, 0, h], int(T[0]), int(P[0]), w.budget, w.recent))
+    log(f"[w2-128k] 8 heads: worst scaled score error {worst:.2e}, kept differences {diffs}")
+    kr, _ = kv.kv_select_random((1, 1, 8, w.t_cap), i32(T), i32(P), w.budget, w.recent, w.prompt_cap(), 3, 1)
+    kr = kr.cpu().numpy()
+    for h in range(8):
+        ref = oracle.select_random(int(T[0]), int(P[0]), w.budget, w.recent, None, 3, 1, 0, h, 0)
+        assert np.array_equal(kr[0, 0, h, :ref.size], ref)
+
+
 def test_workload2_full_score_with_norm_term():
     # the full TriAttention score (S_trig + S_norm) on the Qwen3-8B-shaped layer
     w = workload(2)
