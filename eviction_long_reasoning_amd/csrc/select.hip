@@ -192,6 +192,37 @@ __device__ __forceinline__ void wave_exclusive_scan_lds(uint32_t *a, int n, int 
   }
 }
 
+// Threshold among a short member list held in LDS (list[0..m), zero-padded to a multiple of 4;
+// keys are >= 0, so a pad only ever ties with a key equal to 0): the key with fewer than
+// `remaining` larger members and at least `remaining` larger-or-equal ones, how many keys equal
+// to it are taken, and how many there are. Every thread that finds it writes the same triple into
+// found[0..2].
+template <int NT>
+__device__ __forceinline__ void rank_members(const uint32_t *list, uint32_t m, uint32_t remaining,
+                                             uint32_t *found) {
+  const uint32_t m4 = (m + 3u) & ~3u, pads = m4 - m;
+  for (uint32_t t = threadIdx.x; t < m; t += NT) {
+    const uint32_t k = list[t];
+    uint32_t gt = 0u, ge = 0u;
+    for (uint32_t u = 0; u < m4; u += 4) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(list + u);
+      gt += (v.x > k) + (v.y > k) + (v.z > k) + (v.w > k);
+      ge += (v.x >= k) + (v.y >= k) + (v.z >= k) + (v.w >= k);
+    }
+    if (k == 0u) ge -= pads;
+    if (gt < remaining && ge >= remaining) {
+      found[0] = k;
+      found[1] = remaining - gt;
+      found[2] = ge - gt;
+    }
+  }
+}
+
+// Largest member list ranked directly (it lives in the value histogram's LDS with 4 slots of
+// padding to spare); longer lists go through the radix passes.
+template <int NT>
+constexpr uint32_t member_cap() { return 2 * NT < kValueBins - 4 ? 2 * NT : kValueBins - 4; }
+
 // The three rankings share one kernel body. KIND 0 (top-k): keys are the fp32 scores. KIND 1
 // (random): keys are Philox words. KIND 2 (union, "TriAttention" blog, eviction step): G + 1
 // passes over the same registers -- pass g < G ranks the evictable slots by query head g's own
@@ -207,11 +238,12 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   constexpr int NW = NT / 64;
   constexpr int R = KPT / 4;   // rounds of four consecutive slots per thread
   constexpr bool RANDOM = KIND == 1, UNION = KIND == 2;
-  __shared__ uint32_t hist[kValueBins];
+  __shared__ __align__(16) uint32_t hist[kValueBins];
   __shared__ uint32_t red[2 * NW];
   __shared__ uint32_t tot_a[R * NW];   // per (round, wave): slots kept unconditionally
   __shared__ uint32_t tot_e[R * NW];   // per (round, wave): slots whose key equals thr
-  __shared__ uint32_t found[2];
+  __shared__ uint32_t found[3];
+  __shared__ uint32_t n_members;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -313,6 +345,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
     // mode: 0 = select none, 1 = select all candidates, 2 = threshold rule
     int mode;
     uint32_t thr = 0u, need = 0u;
+    bool all_ties = false;  // every key equal to thr is taken
     if (p_sel <= 0 || n_cand <= 0) {
       mode = 0;
     } else if (p_sel >= n_cand) {
@@ -321,6 +354,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
       mode = 2;
       uint32_t remaining = static_cast<uint32_t>(p_sel);
       uint64_t mem = cand;  // keys the exact radix passes still have to order
+      bool ranked = false;  // threshold found by ranking a short member list
       if (!RANDOM) {
         // Pass 1 (scores): 1024 bins uniform in value between the smallest and largest finite
         // candidate. The binning is monotone, so the threshold lies in one bin and every key in a
@@ -339,6 +373,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
         const float scale = static_cast<float>(kValueBins) / (fmax - fmin);
         if (kmn < kmx && scale > 0.f && scale < 3.0e38f) {
           for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
+          if (tid == 0) n_members = 0u;
           __syncthreads();
 #pragma unroll
           for (int i = 0; i < KPT; ++i)
@@ -353,47 +388,71 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
           for (int i = 0; i < KPT; ++i)
             if (((cand >> i) & 1ull) && value_bin(key[i], fmin, scale) == b) mem |= 1ull << i;
           __syncthreads();  // `found` and `hist` are reused below
+          // The threshold's bin usually holds a few keys: list them in LDS (hist is free) and rank
+          // them directly instead of running the radix passes.
+#pragma unroll
+          for (int i = 0; i < KPT; ++i) {
+            if ((mem >> i) & 1ull) {
+              const uint32_t at = atomicAdd(&n_members, 1u);
+              if (at < member_cap<NT>()) hist[at] = key[i];
+            }
+          }
+          __syncthreads();
+          const uint32_t m = n_members;
+          if (m <= member_cap<NT>()) {
+            if (tid < 4) hist[m + tid] = 0u;   // pad to a multiple of 4 (m + 3 < kValueBins)
+            __syncthreads();
+            rank_members<NT>(hist, m, remaining, found);
+            __syncthreads();
+            thr = found[0];
+            need = found[1];
+            all_ties = found[2] == need;   // equal keys share the threshold's bin: all are listed
+            ranked = true;
+          }
+          __syncthreads();  // `found`, `hist` and n_members are reused below
         }
       }
       // Exact radix passes over the member keys, from their highest differing bit.
-      uint32_t kor = 0u, kand = 0xFFFFFFFFu;
+      if (!ranked) {
+        uint32_t kor = 0u, kand = 0xFFFFFFFFu;
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        if ((mem >> i) & 1ull) {
-          kor |= key[i];
-          kand &= key[i];
-        }
-      }
-      block_or_and<NT>(kor, kand, red);
-      const uint32_t diff = kor ^ kand;
-      if (diff == 0u) {
-        thr = kand;  // all member keys equal
-      } else {
-        const int top = 31 - __clz(diff);
-        uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
-        uint32_t prefix = kand & mask;
-        for (int hi = top; hi >= 0;) {
-          const int lo = hi >= 7 ? hi - 7 : 0;
-          const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
-          for (int i = tid; i < 256; i += NT) hist[i] = 0u;
-          __syncthreads();
-#pragma unroll
-          for (int i = 0; i < KPT; ++i) {
-            if (((mem >> i) & 1ull) && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> lo) & dmask], 1u);
+        for (int i = 0; i < KPT; ++i) {
+          if ((mem >> i) & 1ull) {
+            kor |= key[i];
+            kand &= key[i];
           }
-          __syncthreads();
-          if (wave == 0) find_bin<256>(hist, remaining, lane, found);
-          __syncthreads();
-          const uint32_t digit = found[0];
-          remaining -= found[1];
-          prefix |= digit << lo;
-          mask |= dmask << lo;
-          hi = lo - 1;
-          __syncthreads();  // everyone has read `found` before the next pass may overwrite it
         }
-        thr = prefix;
+        block_or_and<NT>(kor, kand, red);
+        const uint32_t diff = kor ^ kand;
+        if (diff == 0u) {
+          thr = kand;  // all member keys equal
+        } else {
+          const int top = 31 - __clz(diff);
+          uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
+          uint32_t prefix = kand & mask;
+          for (int hi = top; hi >= 0;) {
+            const int lo = hi >= 7 ? hi - 7 : 0;
+            const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
+            for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) {
+              if (((mem >> i) & 1ull) && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> lo) & dmask], 1u);
+            }
+            __syncthreads();
+            if (wave == 0) find_bin<256>(hist, remaining, lane, found);
+            __syncthreads();
+            const uint32_t digit = found[0];
+            remaining -= found[1];
+            prefix |= digit << lo;
+            mask |= dmask << lo;
+            hi = lo - 1;
+            __syncthreads();  // everyone has read `found` before the next pass may overwrite it
+          }
+          thr = prefix;
+        }
+        need = remaining;
       }
-      need = remaining;
     }
 
     // ---- 4. one ordered scan: unconditional (A) and equal-to-thr (E) slots before each slot.
@@ -411,6 +470,10 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
     if (UNION && !last) {
       umask |= fa;
       if (mode != 2) continue;   // uniform: no ties to rank
+      if (all_ties) {            // uniform: the ties need no order either
+        umask |= fe;
+        continue;
+      }
       fa = 0ull;
     }
     // per round: the two counts packed as (A | E << 16); a wave's sums stay below 2^9 per half
@@ -474,10 +537,11 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
   constexpr int NT = kStreamThreads;
   constexpr int NW = NT / 64;
   constexpr bool RANDOM = KIND == 1;
-  __shared__ uint32_t hist[kValueBins];
+  __shared__ __align__(16) uint32_t hist[kValueBins];
   __shared__ uint32_t red[2 * NW];
   __shared__ uint32_t wsum[2 * NW];
-  __shared__ uint32_t found[2];
+  __shared__ uint32_t found[3];
+  __shared__ uint32_t n_members;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -524,7 +588,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
     uint32_t remaining = static_cast<uint32_t>(n_sel);
     // member keys: every candidate, or (scores with a usable value range) those in the value bin
     // that holds the threshold
-    bool binned = false;
+    bool binned = false, ranked = false;
     uint32_t bsel = 0u;
     float fmin = 0.f, scale = 0.f;
     if (!RANDOM) {
@@ -542,6 +606,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
       scale = static_cast<float>(kValueBins) / (fmax - fmin);
       if (kmn < kmx && scale > 0.f && scale < 3.0e38f) {
         for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
+        if (tid == 0) n_members = 0u;
         __syncthreads();
         for (int j = e_lo + tid; j < e_hi; j += NT) atomicAdd(&hist[value_bin(key_of(j), fmin, scale)], 1u);
         __syncthreads();
@@ -551,46 +616,68 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
         remaining -= found[1];
         binned = true;
         __syncthreads();  // `found` and `hist` are reused below
+        // a short member list is ranked directly (as in the register kernel)
+        for (int j = e_lo + tid; j < e_hi; j += NT) {
+          const uint32_t k = key_of(j);
+          if (value_bin(k, fmin, scale) == bsel) {
+            const uint32_t at = atomicAdd(&n_members, 1u);
+            if (at < member_cap<NT>()) hist[at] = k;
+          }
+        }
+        __syncthreads();
+        const uint32_t m = n_members;
+        if (m <= member_cap<NT>()) {
+          if (tid < 4) hist[m + tid] = 0u;
+          __syncthreads();
+          rank_members<NT>(hist, m, remaining, found);
+          __syncthreads();
+          thr = found[0];
+          need = found[1];
+          ranked = true;
+        }
+        __syncthreads();  // `found` and `hist` are reused below
       }
     }
     auto member = [&](uint32_t k) { return !binned || value_bin(k, fmin, scale) == bsel; };
-    uint32_t kor = 0u, kand = 0xFFFFFFFFu;
-    for (int j = e_lo + tid; j < e_hi; j += NT) {
-      const uint32_t k = key_of(j);
-      if (member(k)) {
-        kor |= k;
-        kand &= k;
-      }
-    }
-    block_or_and<NT>(kor, kand, red);
-    const uint32_t diff = kor ^ kand;
-    if (diff == 0u) {
-      thr = kand;  // all member keys equal
-    } else {
-      const int top = 31 - __clz(diff);
-      uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
-      uint32_t prefix = kand & mask;
-      for (int hi = top; hi >= 0;) {
-        const int lo = hi >= 7 ? hi - 7 : 0;
-        const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
-        for (int i = tid; i < 256; i += NT) hist[i] = 0u;
-        __syncthreads();
-        for (int j = e_lo + tid; j < e_hi; j += NT) {
-          const uint32_t k = key_of(j);
-          if ((k & mask) == prefix && member(k)) atomicAdd(&hist[(k >> lo) & dmask], 1u);
+    if (!ranked) {
+      uint32_t kor = 0u, kand = 0xFFFFFFFFu;
+      for (int j = e_lo + tid; j < e_hi; j += NT) {
+        const uint32_t k = key_of(j);
+        if (member(k)) {
+          kor |= k;
+          kand &= k;
         }
-        __syncthreads();
-        if (wave == 0) find_bin<256>(hist, remaining, lane, found);
-        __syncthreads();
-        prefix |= found[0] << lo;
-        mask |= dmask << lo;
-        remaining -= found[1];
-        hi = lo - 1;
-        __syncthreads();  // everyone has read `found` before the next pass may overwrite it
       }
-      thr = prefix;
+      block_or_and<NT>(kor, kand, red);
+      const uint32_t diff = kor ^ kand;
+      if (diff == 0u) {
+        thr = kand;  // all member keys equal
+      } else {
+        const int top = 31 - __clz(diff);
+        uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
+        uint32_t prefix = kand & mask;
+        for (int hi = top; hi >= 0;) {
+          const int lo = hi >= 7 ? hi - 7 : 0;
+          const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
+          for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+          __syncthreads();
+          for (int j = e_lo + tid; j < e_hi; j += NT) {
+            const uint32_t k = key_of(j);
+            if ((k & mask) == prefix && member(k)) atomicAdd(&hist[(k >> lo) & dmask], 1u);
+          }
+          __syncthreads();
+          if (wave == 0) find_bin<256>(hist, remaining, lane, found);
+          __syncthreads();
+          prefix |= found[0] << lo;
+          mask |= dmask << lo;
+          remaining -= found[1];
+          hi = lo - 1;
+          __syncthreads();  // everyone has read `found` before the next pass may overwrite it
+        }
+        thr = prefix;
+      }
+      need = remaining;
     }
-    need = remaining;
   }
 
   // ordered scan: thread t takes slots c + 4t .. c + 4t + 3 of each chunk
