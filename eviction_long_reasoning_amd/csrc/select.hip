@@ -16,11 +16,15 @@
 // load and the head's scores are read from HBM exactly once:
 //  1. Keys: fp32 scores mapped to order-preserving uint32 (NaN -> -inf,
 //     -0 -> +0) or, for the random selector, word 0 of Philox4x32-10.
-//  2. The bits shared by every candidate key are found with an OR/AND block
-//     reduction; radix passes start at the highest differing bit, which keeps
-//     the LDS histogram from collapsing into one bin for concentrated scores.
-//  3. 8-bit radix passes over a 256-bin LDS histogram locate the n_sel-th
-//     largest key thr and how many keys equal to thr must be taken (need).
+//  2. A 1024-bin LDS histogram (scores binned by value between the smallest
+//     and largest finite candidate, random keys by their top 10 bits) finds
+//     the bin holding the n_sel-th largest key; every key in a higher bin is
+//     larger.
+//  3. That bin's keys, usually a few dozen, are listed in LDS and ranked
+//     directly to give the n_sel-th largest key thr and how many keys equal to
+//     thr must be taken (need). A crowded bin instead goes through 8-bit radix
+//     passes over a 256-bin histogram, from the highest bit where its keys
+//     differ (an OR/AND block reduction).
 //  4. One ordered scan in slot order counts, before each slot, the slots kept
 //     unconditionally (pinned, or above thr) and the slots equal to thr. A
 //     kept slot's output index is then (unconditional before) +
@@ -355,11 +359,14 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
       uint32_t remaining = static_cast<uint32_t>(p_sel);
       uint64_t mem = cand;  // keys the exact radix passes still have to order
       bool ranked = false;  // threshold found by ranking a short member list
+      // Pass 1: 1024 bins. Scores are binned uniformly in value between the smallest and largest
+      // finite candidate (binning by value keeps a concentrated score distribution from piling
+      // into a few bins); uniform random keys by their top 10 bits. The binning is monotone, so
+      // the threshold lies in one bin and every key in a higher bin is strictly larger; the exact
+      // step then only sees that bin's keys.
+      bool binned = RANDOM;
+      float fmin = 0.f, scale = 0.f;
       if (!RANDOM) {
-        // Pass 1 (scores): 1024 bins uniform in value between the smallest and largest finite
-        // candidate. The binning is monotone, so the threshold lies in one bin and every key in a
-        // higher bin is strictly larger; the exact passes then only see that bin's keys. Binning
-        // by value keeps a concentrated score distribution from piling into a few radix bins.
         uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
@@ -369,15 +376,20 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
           }
         }
         block_min_max<NT>(kmn, kmx, red);
-        const float fmin = key_value(kmn), fmax = key_value(kmx);
-        const float scale = static_cast<float>(kValueBins) / (fmax - fmin);
-        if (kmn < kmx && scale > 0.f && scale < 3.0e38f) {
+        fmin = key_value(kmn);
+        const float fmax = key_value(kmx);
+        scale = static_cast<float>(kValueBins) / (fmax - fmin);
+        binned = kmn < kmx && scale > 0.f && scale < 3.0e38f;
+      }
+      {
+        auto bin_of = [&](uint32_t k) { return RANDOM ? (k >> 22) : value_bin(k, fmin, scale); };
+        if (binned) {
           for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
           if (tid == 0) n_members = 0u;
           __syncthreads();
 #pragma unroll
           for (int i = 0; i < KPT; ++i)
-            if ((cand >> i) & 1ull) atomicAdd(&hist[value_bin(key[i], fmin, scale)], 1u);
+            if ((cand >> i) & 1ull) atomicAdd(&hist[bin_of(key[i])], 1u);
           __syncthreads();
           if (wave == 0) find_bin<kValueBins>(hist, remaining, lane, found);
           __syncthreads();
@@ -386,7 +398,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
           mem = 0ull;
 #pragma unroll
           for (int i = 0; i < KPT; ++i)
-            if (((cand >> i) & 1ull) && value_bin(key[i], fmin, scale) == b) mem |= 1ull << i;
+            if (((cand >> i) & 1ull) && bin_of(key[i]) == b) mem |= 1ull << i;
           __syncthreads();  // `found` and `hist` are reused below
           // The threshold's bin usually holds a few keys: list them in LDS (hist is free) and rank
           // them directly instead of running the radix passes.
@@ -586,11 +598,12 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
   } else {
     mode = 2;
     uint32_t remaining = static_cast<uint32_t>(n_sel);
-    // member keys: every candidate, or (scores with a usable value range) those in the value bin
-    // that holds the threshold
-    bool binned = false, ranked = false;
+    // member keys: those in the bin that holds the threshold (bins as in the register kernel),
+    // or every candidate when the scores have no usable value range
+    bool binned = RANDOM, ranked = false;
     uint32_t bsel = 0u;
     float fmin = 0.f, scale = 0.f;
+    auto bin_of = [&](uint32_t k) { return RANDOM ? (k >> 22) : value_bin(k, fmin, scale); };
     if (!RANDOM) {
       uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
       for (int j = e_lo + tid; j < e_hi; j += NT) {
@@ -604,41 +617,41 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
       fmin = key_value(kmn);
       const float fmax = key_value(kmx);
       scale = static_cast<float>(kValueBins) / (fmax - fmin);
-      if (kmn < kmx && scale > 0.f && scale < 3.0e38f) {
-        for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
-        if (tid == 0) n_members = 0u;
-        __syncthreads();
-        for (int j = e_lo + tid; j < e_hi; j += NT) atomicAdd(&hist[value_bin(key_of(j), fmin, scale)], 1u);
-        __syncthreads();
-        if (wave == 0) find_bin<kValueBins>(hist, remaining, lane, found);
-        __syncthreads();
-        bsel = found[0];
-        remaining -= found[1];
-        binned = true;
-        __syncthreads();  // `found` and `hist` are reused below
-        // a short member list is ranked directly (as in the register kernel)
-        for (int j = e_lo + tid; j < e_hi; j += NT) {
-          const uint32_t k = key_of(j);
-          if (value_bin(k, fmin, scale) == bsel) {
-            const uint32_t at = atomicAdd(&n_members, 1u);
-            if (at < member_cap<NT>()) hist[at] = k;
-          }
-        }
-        __syncthreads();
-        const uint32_t m = n_members;
-        if (m <= member_cap<NT>()) {
-          if (tid < 4) hist[m + tid] = 0u;
-          __syncthreads();
-          rank_members<NT>(hist, m, remaining, found);
-          __syncthreads();
-          thr = found[0];
-          need = found[1];
-          ranked = true;
-        }
-        __syncthreads();  // `found` and `hist` are reused below
-      }
+      binned = kmn < kmx && scale > 0.f && scale < 3.0e38f;
     }
-    auto member = [&](uint32_t k) { return !binned || value_bin(k, fmin, scale) == bsel; };
+    if (binned) {
+      for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
+      if (tid == 0) n_members = 0u;
+      __syncthreads();
+      for (int j = e_lo + tid; j < e_hi; j += NT) atomicAdd(&hist[bin_of(key_of(j))], 1u);
+      __syncthreads();
+      if (wave == 0) find_bin<kValueBins>(hist, remaining, lane, found);
+      __syncthreads();
+      bsel = found[0];
+      remaining -= found[1];
+      __syncthreads();  // `found` and `hist` are reused below
+      // a short member list is ranked directly (as in the register kernel)
+      for (int j = e_lo + tid; j < e_hi; j += NT) {
+        const uint32_t k = key_of(j);
+        if (bin_of(k) == bsel) {
+          const uint32_t at = atomicAdd(&n_members, 1u);
+          if (at < member_cap<NT>()) hist[at] = k;
+        }
+      }
+      __syncthreads();
+      const uint32_t m = n_members;
+      if (m <= member_cap<NT>()) {
+        if (tid < 4) hist[m + tid] = 0u;
+        __syncthreads();
+        rank_members<NT>(hist, m, remaining, found);
+        __syncthreads();
+        thr = found[0];
+        need = found[1];
+        ranked = true;
+      }
+      __syncthreads();  // `found` and `hist` are reused below
+    }
+    auto member = [&](uint32_t k) { return !binned || bin_of(k) == bsel; };
     if (!ranked) {
       uint32_t kor = 0u, kand = 0xFFFFFFFFu;
       for (int j = e_lo + tid; j < e_hi; j += NT) {

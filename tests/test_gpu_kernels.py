@@ -339,6 +339,9 @@ SELECT_CASES = [
     ("stream-66k-huge", 66000, [66000], [10], 1000, 8, "huge"),
     ("stream-70k-equal", 70000, [70000], [100], 500, 10, "equal"),
     ("stream-70k-prompt-over-budget", 70000, [70000, 69000], [2500, 2049], 2048, 128, "normal"),
+    # the threshold's value bin holds thousands of keys: the radix passes resolve it
+    ("crowded-bin", 20000, [20000, 15000], [100, 0], 3000, 64, "cluster"),
+    ("stream-70k-crowded-bin", 70000, [70000], [100], 3000, 64, "cluster"),
 ]
 
 
@@ -367,6 +370,13 @@ def _select_scores(name, kind, shape):
         n = int(np.prod(shape))
         r = rng(531, seed)
         return r.integers(0, 0x7FFFF, n).astype(np.uint32).view(np.float32).reshape(shape)
+    if kind == "cluster":   # outliers stretch the value range: the threshold's bin is crowded
+        n = int(np.prod(shape))
+        r = rng(532, seed)
+        x = (np.float32(1.0) + np.float32(1e-3) * r.random(n, dtype=np.float32)).astype(np.float32)
+        x[::97] = np.float32(1e6)
+        x[1::101] = np.float32(-1e6)
+        return x.reshape(shape)
     if kind == "infmix":
         x = random_scores(seed, shape, ties=0.05)
         flat = x.reshape(-1)
