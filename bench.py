@@ -281,11 +281,9 @@ def main():
     union_ms = time_launches(lambda: kv.kv_select_union(head3, zmax, seq, plen, w.budget, w.recent, w.prompt_cap(),
                                                         b_cap=b_cap, kept=kept, n_kept=nk))
     union_bytes = entries * 4 * (w.group + 1) + w.n_heads_total * b_cap * 4
-    del zmax, head3
-    recent_ms = time_launches(lambda: kv.kv_select_recent((L, S, H, Tc), seq, plen, w.budget, w.recent,
-                                                          w.prompt_cap(), b_cap=b_cap, kept=kept, n_kept=nk))
-    # 131072-token caches (context lengths reach 128K tokens): the same score memory viewed as
-    # L layers x S/4 seqs x 8 KV heads of 4 * T slots, past the selectors' register tiers
+    # 131072-token caches (context lengths reach 128K tokens): the same score memory (and the
+    # grouped-query scores) viewed as L layers x S/4 seqs x 8 KV heads of 4 * T slots, past the
+    # selectors' register tiers
     long_sel = None
     if S % 4 == 0:
         Sl, Tl = S // 4, 4 * Tc
@@ -298,12 +296,18 @@ def main():
         lr_ms = time_launches(lambda: kv.kv_select_random((L, Sl, H, Tl), seq_l, plen_l, w.budget, w.recent,
                                                           w.prompt_cap(), 1, 0, b_cap=b_cap, kept=kept_l,
                                                           n_kept=nk_l))
+        hs_long, z_long = head3.view(L, Sl, H, w.group, Tl), zmax.view(L, Sl, H, Tl)
+        lu_ms = time_launches(lambda: kv.kv_select_union(hs_long, z_long, seq_l, plen_l, w.budget, w.recent,
+                                                         w.prompt_cap(), b_cap=b_cap, kept=kept_l, n_kept=nk_l))
         n_long = L * Sl * H * Tl
-        long_sel = {"t_cap": Tl, "heads": L * Sl * H, "topk_ms": lt_ms, "random_ms": lr_ms,
+        long_sel = {"t_cap": Tl, "heads": L * Sl * H, "topk_ms": lt_ms, "random_ms": lr_ms, "union_ms": lu_ms,
                     "topk_entries_per_s": n_long / (lt_ms * 1e-3), "random_entries_per_s": n_long / (lr_ms * 1e-3)}
-        print(f"[bench] {Tl}-slot caches: top-k select {lt_ms:.3f} ms, random select {lr_ms:.3f} ms",
-              file=sys.stderr, flush=True)
-        del sc_long, kept_l
+        print(f"[bench] {Tl}-slot caches: top-k select {lt_ms:.3f} ms, random select {lr_ms:.3f} ms, "
+              f"union select {lu_ms:.3f} ms", file=sys.stderr, flush=True)
+        del sc_long, kept_l, hs_long, z_long
+    del zmax, head3
+    recent_ms = time_launches(lambda: kv.kv_select_recent((L, S, H, Tc), seq, plen, w.budget, w.recent,
+                                                          w.prompt_cap(), b_cap=b_cap, kept=kept, n_kept=nk))
 
     w4 = workload(4)
     mu4, qb4, _ = centres(w4)

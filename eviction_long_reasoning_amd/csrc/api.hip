@@ -298,7 +298,7 @@ KV_EXPORT kv_status kv_select_union(const kv_shape *shape, const kv_policy *poli
                                     int32_t k_per_head, const float *head_scores, const float *scores,
                                     int32_t *kept, int32_t b_cap, int32_t *n_kept, void *stream) {
   SelectParams p{};
-  kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p, kSelectMaxSlots);
+  kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p, kSelectMaxSlotsUnion);
   if (st != KV_OK) return st;
   if (!head_scores || !scores) return KV_EINVAL;
   if (group < 1 || group > 64) return KV_EINVAL;

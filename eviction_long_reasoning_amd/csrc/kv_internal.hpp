@@ -69,8 +69,9 @@ struct SelectParams {
 
 enum class SelectKind { kTopk, kRandom, kUnion };
 
-constexpr int kSelectMaxSlots = 65536;        // register-resident tiers (and the union selector)
-constexpr int kSelectMaxSlotsStream = 1 << 26;  // top-k and random past the tiers: keys re-read per step
+constexpr int kSelectMaxSlots = 65536;          // register-resident tiers
+constexpr int kSelectMaxSlotsStream = 1 << 26;    // top-k and random past the tiers: keys re-read per step
+constexpr int kSelectMaxSlotsUnion = 1 << 18;     // union past the tiers: a bit per slot in LDS
 hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st);
 hipError_t launch_select_recent(const SelectParams &p, hipStream_t st);
 hipError_t launch_audit(const SelectParams &p, int32_t *bad, hipStream_t st);

@@ -537,23 +537,26 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
 }
 
 // Caches longer than the register tiers hold (t_cap > 65536 slots; long-context models reach
-// 128K tokens): the same two rankings, threshold rule and ordered scan, with every step
-// recomputing the keys from memory (a score load, or the Philox draw) instead of keeping them in
-// registers. Steps: min/max and a value-binned histogram (scores only), OR/AND of the member
-// keys, 8-bit radix passes from their highest differing bit, then the ordered scan in chunks of
-// 4 * NT slots in slot order with the kept and tied counts carried from chunk to chunk.
+// 128K tokens): the same rankings, threshold rule and ordered scan, with every step recomputing
+// the keys from memory (a score load, or the Philox draw) instead of keeping them in registers.
+// Steps: min/max (scores) and the 1024-bin histogram, the threshold bin's keys ranked in LDS (or,
+// when crowded, OR/AND and 8-bit radix passes), then the ordered scan in chunks of 4 * NT slots
+// in slot order with the kept and tied counts carried from chunk to chunk. The union (KIND 2)
+// runs G + 1 such passes and keeps its union as a bit per slot in dynamic LDS (t_cap / 8 bytes).
 constexpr int kStreamThreads = 1024;
+static_assert(kSelectMaxSlotsUnion / 8 <= 32 * 1024, "union bits fit in 32 KB of LDS");
 
 template <int KIND>
 __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const SelectParams p) {
   constexpr int NT = kStreamThreads;
   constexpr int NW = NT / 64;
-  constexpr bool RANDOM = KIND == 1;
+  constexpr bool RANDOM = KIND == 1, UNION = KIND == 2;
   __shared__ __align__(16) uint32_t hist[kValueBins];
   __shared__ uint32_t red[2 * NW];
   __shared__ uint32_t wsum[2 * NW];
   __shared__ uint32_t found[3];
   __shared__ uint32_t n_members;
+  extern __shared__ uint32_t ubits[];   // union: bit j set when slot j is in some head's top-k
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -580,170 +583,230 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
   const int n_cand = e_hi - e_lo;
   const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
   const uint32_t c1 = p.shared_draw ? 0u : (static_cast<uint32_t>(l) << 16) | static_cast<uint32_t>(h);
-  auto key_of = [&](int j) -> uint32_t {  // j in [e_lo, e_hi)
-    if (RANDOM) {
-      const uint32_t c0 = p.pos ? static_cast<uint32_t>(p.pos[slot0 + j]) : static_cast<uint32_t>(j);
-      return philox_word0(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
-    }
-    return order_key(p.scores[slot0 + j]);
-  };
-
-  // mode: 0 = select none, 1 = select all candidates, 2 = threshold rule
-  int mode;
-  uint32_t thr = 0u, need = 0u;
-  if (n_sel <= 0 || n_cand <= 0) {
-    mode = 0;
-  } else if (n_sel >= n_cand) {
-    mode = 1;
-  } else {
-    mode = 2;
-    uint32_t remaining = static_cast<uint32_t>(n_sel);
-    // member keys: those in the bin that holds the threshold (bins as in the register kernel),
-    // or every candidate when the scores have no usable value range
-    bool binned = RANDOM, ranked = false;
-    uint32_t bsel = 0u;
-    float fmin = 0.f, scale = 0.f;
-    auto bin_of = [&](uint32_t k) { return RANDOM ? (k >> 22) : value_bin(k, fmin, scale); };
-    if (!RANDOM) {
-      uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
-      for (int j = e_lo + tid; j < e_hi; j += NT) {
-        const uint32_t k = key_of(j);
-        if (k > kKeyNegInf && k < kKeyPosInf) {
-          kmn = min(kmn, k);
-          kmx = max(kmx, k);
-        }
-      }
-      block_min_max<NT>(kmn, kmx, red);
-      fmin = key_value(kmn);
-      const float fmax = key_value(kmx);
-      scale = static_cast<float>(kValueBins) / (fmax - fmin);
-      binned = kmn < kmx && scale > 0.f && scale < 3.0e38f;
-    }
-    if (binned) {
-      for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
-      if (tid == 0) n_members = 0u;
-      __syncthreads();
-      for (int j = e_lo + tid; j < e_hi; j += NT) atomicAdd(&hist[bin_of(key_of(j))], 1u);
-      __syncthreads();
-      if (wave == 0) find_bin<kValueBins>(hist, remaining, lane, found);
-      __syncthreads();
-      bsel = found[0];
-      remaining -= found[1];
-      __syncthreads();  // `found` and `hist` are reused below
-      // a short member list is ranked directly (as in the register kernel)
-      for (int j = e_lo + tid; j < e_hi; j += NT) {
-        const uint32_t k = key_of(j);
-        if (bin_of(k) == bsel) {
-          const uint32_t at = atomicAdd(&n_members, 1u);
-          if (at < member_cap<NT>()) hist[at] = k;
-        }
-      }
-      __syncthreads();
-      const uint32_t m = n_members;
-      if (m <= member_cap<NT>()) {
-        if (tid < 4) hist[m + tid] = 0u;
-        __syncthreads();
-        rank_members<NT>(hist, m, remaining, found);
-        __syncthreads();
-        thr = found[0];
-        need = found[1];
-        ranked = true;
-      }
-      __syncthreads();  // `found` and `hist` are reused below
-    }
-    auto member = [&](uint32_t k) { return !binned || bin_of(k) == bsel; };
-    if (!ranked) {
-      uint32_t kor = 0u, kand = 0xFFFFFFFFu;
-      for (int j = e_lo + tid; j < e_hi; j += NT) {
-        const uint32_t k = key_of(j);
-        if (member(k)) {
-          kor |= k;
-          kand &= k;
-        }
-      }
-      block_or_and<NT>(kor, kand, red);
-      const uint32_t diff = kor ^ kand;
-      if (diff == 0u) {
-        thr = kand;  // all member keys equal
-      } else {
-        const int top = 31 - __clz(diff);
-        uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
-        uint32_t prefix = kand & mask;
-        for (int hi = top; hi >= 0;) {
-          const int lo = hi >= 7 ? hi - 7 : 0;
-          const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
-          for (int i = tid; i < 256; i += NT) hist[i] = 0u;
-          __syncthreads();
-          for (int j = e_lo + tid; j < e_hi; j += NT) {
-            const uint32_t k = key_of(j);
-            if ((k & mask) == prefix && member(k)) atomicAdd(&hist[(k >> lo) & dmask], 1u);
-          }
-          __syncthreads();
-          if (wave == 0) find_bin<256>(hist, remaining, lane, found);
-          __syncthreads();
-          prefix |= found[0] << lo;
-          mask |= dmask << lo;
-          remaining -= found[1];
-          hi = lo - 1;
-          __syncthreads();  // everyone has read `found` before the next pass may overwrite it
-        }
-        thr = prefix;
-      }
-      need = remaining;
-    }
-  }
-
-  // ordered scan: thread t takes slots c + 4t .. c + 4t + 3 of each chunk
-  uint32_t carry_a = 0u, carry_e = 0u;  // unconditional / tied slots in earlier chunks
-  for (int c = 0; c < T; c += 4 * NT) {
-    const int j0 = c + 4 * tid;
-    uint32_t fa = 0u, fe = 0u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = j0 + q;
-      if (j >= T) break;
-      const bool cnd = j >= e_lo && j < e_hi;
-      bool a = !cnd || mode == 1, e = false;   // prompt and recent window are pinned
-      if (cnd && mode == 2) {
-        const uint32_t k = key_of(j);
-        a = k > thr;
-        e = k == thr;
-      }
-      fa |= static_cast<uint32_t>(a) << q;
-      fe |= static_cast<uint32_t>(e) << q;
-    }
-    const uint32_t cnt = static_cast<uint32_t>(__popc(fa)) | (static_cast<uint32_t>(__popc(fe)) << 16);
-    const uint32_t x = wave_inclusive_sum(cnt);   // a wave's halves stay below 2^9
-    if (lane == 63) {
-      wsum[wave] = x & 0xFFFFu;
-      wsum[NW + wave] = x >> 16;
-    }
+  const int passes = UNION ? (n_sel > 0 ? p.G : 0) + 1 : 1;
+  const int k_head = UNION ? (p.k_per_head > 0 ? p.k_per_head : (n_sel + p.G - 1) / p.G) : 0;
+  const int words = (T + 31) >> 5;
+  if (UNION) {
+    for (int w = tid; w < words; w += NT) ubits[w] = 0u;
     __syncthreads();
-    uint32_t na = carry_a + ((x - cnt) & 0xFFFFu), ne = carry_e + ((x - cnt) >> 16);
+  }
+  auto in_union = [&](int j) { return (ubits[j >> 5] >> (j & 31)) & 1u; };
+
+#pragma unroll 1
+  for (int pass = 0; pass < passes; ++pass) {
+    const bool last = pass == passes - 1;
+    // union, last pass: the union folded into the combined score's keys as in the register kernel
+    bool long_union = false;
+    if (UNION && last) {
+      uint32_t cnt = 0u;
+      for (int w = tid; w < words; w += NT) cnt += __popc(ubits[w]);
+      cnt = wave_total(wave_inclusive_sum(cnt));
+      if (lane == 0) red[wave] = cnt;
+      __syncthreads();
+      int n_union = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      if (w < wave) {
-        na += wsum[w];
-        ne += wsum[NW + w];
-      }
-      carry_a += wsum[w];
-      carry_e += wsum[NW + w];
+      for (int w = 0; w < NW; ++w) n_union += static_cast<int>(red[w]);
+      __syncthreads();
+      long_union = n_union >= n_sel;
     }
-    __syncthreads();  // wsum is rewritten by the next chunk
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if ((fa >> q) & 1u) {
-        const uint32_t o = na + min(ne, need);
-        if (o < static_cast<uint32_t>(p.b_cap)) out[o] = j0 + q;
-        ++na;
-      } else if ((fe >> q) & 1u) {
-        if (ne < need) {
-          const uint32_t o = na + ne;
-          if (o < static_cast<uint32_t>(p.b_cap)) out[o] = j0 + q;
+    const float *row = nullptr;   // the scores this pass ranks by (not read by the random draw)
+    if (!RANDOM) row = UNION && !last ? p.head_scores + (static_cast<size_t>(head) * p.G + pass) * p.t_cap
+                                      : p.scores + slot0;
+    auto key_of = [&](int j) -> uint32_t {  // j in [e_lo, e_hi)
+      if (RANDOM) {
+        const uint32_t c0 = p.pos ? static_cast<uint32_t>(p.pos[slot0 + j]) : static_cast<uint32_t>(j);
+        return philox_word0(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
+      }
+      const uint32_t k = order_key(row[j]);
+      if (UNION && last) {
+        const bool in_u = in_union(j);
+        if (long_union && !in_u) return 0u;
+        if (!long_union && in_u) return 0xFFFFFFFFu;
+      }
+      return k;
+    };
+    const int p_sel = UNION && !last ? k_head : n_sel;
+
+    // mode: 0 = select none, 1 = select all candidates, 2 = threshold rule
+    int mode;
+    uint32_t thr = 0u, need = 0u;
+    bool all_ties = false;  // every key equal to thr is taken
+    if (p_sel <= 0 || n_cand <= 0) {
+      mode = 0;
+    } else if (p_sel >= n_cand) {
+      mode = 1;
+    } else {
+      mode = 2;
+      uint32_t remaining = static_cast<uint32_t>(p_sel);
+      // member keys: those in the bin that holds the threshold (bins as in the register kernel),
+      // or every candidate when the scores have no usable value range
+      bool binned = RANDOM, ranked = false;
+      uint32_t bsel = 0u;
+      float fmin = 0.f, scale = 0.f;
+      auto bin_of = [&](uint32_t k) { return RANDOM ? (k >> 22) : value_bin(k, fmin, scale); };
+      if (!RANDOM) {
+        uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+        for (int j = e_lo + tid; j < e_hi; j += NT) {
+          const uint32_t k = key_of(j);
+          if (k > kKeyNegInf && k < kKeyPosInf) {
+            kmn = min(kmn, k);
+            kmx = max(kmx, k);
+          }
         }
-        ++ne;
+        block_min_max<NT>(kmn, kmx, red);
+        fmin = key_value(kmn);
+        const float fmax = key_value(kmx);
+        scale = static_cast<float>(kValueBins) / (fmax - fmin);
+        binned = kmn < kmx && scale > 0.f && scale < 3.0e38f;
+      }
+      if (binned) {
+        for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
+        if (tid == 0) n_members = 0u;
+        __syncthreads();
+        for (int j = e_lo + tid; j < e_hi; j += NT) atomicAdd(&hist[bin_of(key_of(j))], 1u);
+        __syncthreads();
+        if (wave == 0) find_bin<kValueBins>(hist, remaining, lane, found);
+        __syncthreads();
+        bsel = found[0];
+        remaining -= found[1];
+        __syncthreads();  // `found` and `hist` are reused below
+        // a short member list is ranked directly (as in the register kernel)
+        for (int j = e_lo + tid; j < e_hi; j += NT) {
+          const uint32_t k = key_of(j);
+          if (bin_of(k) == bsel) {
+            const uint32_t at = atomicAdd(&n_members, 1u);
+            if (at < member_cap<NT>()) hist[at] = k;
+          }
+        }
+        __syncthreads();
+        const uint32_t m = n_members;
+        if (m <= member_cap<NT>()) {
+          if (tid < 4) hist[m + tid] = 0u;
+          __syncthreads();
+          rank_members<NT>(hist, m, remaining, found);
+          __syncthreads();
+          thr = found[0];
+          need = found[1];
+          all_ties = found[2] == need;
+          ranked = true;
+        }
+        __syncthreads();  // `found` and `hist` are reused below
+      }
+      auto member = [&](uint32_t k) { return !binned || bin_of(k) == bsel; };
+      if (!ranked) {
+        uint32_t kor = 0u, kand = 0xFFFFFFFFu;
+        for (int j = e_lo + tid; j < e_hi; j += NT) {
+          const uint32_t k = key_of(j);
+          if (member(k)) {
+            kor |= k;
+            kand &= k;
+          }
+        }
+        block_or_and<NT>(kor, kand, red);
+        const uint32_t diff = kor ^ kand;
+        if (diff == 0u) {
+          thr = kand;  // all member keys equal
+        } else {
+          const int top = 31 - __clz(diff);
+          uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
+          uint32_t prefix = kand & mask;
+          for (int hi = top; hi >= 0;) {
+            const int lo = hi >= 7 ? hi - 7 : 0;
+            const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
+            for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+            __syncthreads();
+            for (int j = e_lo + tid; j < e_hi; j += NT) {
+              const uint32_t k = key_of(j);
+              if ((k & mask) == prefix && member(k)) atomicAdd(&hist[(k >> lo) & dmask], 1u);
+            }
+            __syncthreads();
+            if (wave == 0) find_bin<256>(hist, remaining, lane, found);
+            __syncthreads();
+            prefix |= found[0] << lo;
+            mask |= dmask << lo;
+            remaining -= found[1];
+            hi = lo - 1;
+            __syncthreads();  // everyone has read `found` before the next pass may overwrite it
+          }
+          thr = prefix;
+        }
+        need = remaining;
       }
     }
+
+    if (UNION && !last && (mode != 2 || all_ties)) {
+      // a head's top-k needs no order: mark every candidate above (or at) the threshold
+      for (int j = e_lo + tid; j < e_hi; j += NT) {
+        const uint32_t k = mode == 2 ? key_of(j) : 0u;
+        if (mode == 1 || (mode == 2 && k >= thr)) atomicOr(&ubits[j >> 5], 1u << (j & 31));
+      }
+      __syncthreads();
+      continue;
+    }
+
+    // ordered scan: thread t takes slots c + 4t .. c + 4t + 3 of each chunk. The last pass writes
+    // the kept list; a union head pass adds its top-k (ties to the lower slots) to the union.
+    uint32_t carry_a = 0u, carry_e = 0u;  // unconditional / tied slots in earlier chunks
+    for (int c = 0; c < T; c += 4 * NT) {
+      const int j0 = c + 4 * tid;
+      uint32_t fa = 0u, fe = 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + q;
+        if (j >= T) break;
+        const bool cnd = j >= e_lo && j < e_hi;
+        bool a = last ? (!cnd || mode == 1) : (cnd && mode == 1), e = false;  // pins: last pass
+        if (cnd && mode == 2) {
+          const uint32_t k = key_of(j);
+          a = k > thr;
+          e = k == thr;
+        }
+        fa |= static_cast<uint32_t>(a) << q;
+        fe |= static_cast<uint32_t>(e) << q;
+      }
+      const uint32_t cnt = static_cast<uint32_t>(__popc(fa)) | (static_cast<uint32_t>(__popc(fe)) << 16);
+      const uint32_t x = wave_inclusive_sum(cnt);   // a wave's halves stay below 2^9
+      if (lane == 63) {
+        wsum[wave] = x & 0xFFFFu;
+        wsum[NW + wave] = x >> 16;
+      }
+      __syncthreads();
+      uint32_t na = carry_a + ((x - cnt) & 0xFFFFu), ne = carry_e + ((x - cnt) >> 16);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        if (w < wave) {
+          na += wsum[w];
+          ne += wsum[NW + w];
+        }
+        carry_a += wsum[w];
+        carry_e += wsum[NW + w];
+      }
+      __syncthreads();  // wsum is rewritten by the next chunk
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + q;
+        if ((fa >> q) & 1u) {
+          if (UNION && !last) {
+            atomicOr(&ubits[j >> 5], 1u << (j & 31));
+          } else {
+            const uint32_t o = na + min(ne, need);
+            if (o < static_cast<uint32_t>(p.b_cap)) out[o] = j;
+          }
+          ++na;
+        } else if ((fe >> q) & 1u) {
+          if (ne < need) {
+            if (UNION && !last) {
+              atomicOr(&ubits[j >> 5], 1u << (j & 31));
+            } else {
+              const uint32_t o = na + ne;
+              if (o < static_cast<uint32_t>(p.b_cap)) out[o] = j;
+            }
+          }
+          ++ne;
+        }
+      }
+    }
+    if (UNION && !last) __syncthreads();  // the union bits are complete before the next pass
   }
   for (int r = n_kept + tid; r < p.b_cap; r += NT) out[r] = -1;
   if (writer) p.n_kept[s] = n_kept;
@@ -849,14 +912,18 @@ hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st)
   const int t = p.t_cap;
   if (kind == SelectKind::kUnion) {
     // The union's extra passes hold more registers: past 8192 slots it runs 512-thread tiers
-    // (a 1024-thread workgroup is limited to 128 registers per lane).
+    // (a 1024-thread workgroup is limited to 128 registers per lane); past 65536 slots, the
+    // re-reading kernel with the union bits in dynamic LDS.
     if (t <= 256 * 4) return launch_cfg<256, 4, true>(p, kind, grid, st);
     if (t <= 256 * 16) return launch_cfg<256, 16, true>(p, kind, grid, st);
     if (t <= 256 * 32) return launch_cfg<256, 32, true>(p, kind, grid, st);
     if (t <= 512 * 32) return launch_cfg<512, 32, true>(p, kind, grid, st);
     if (t <= 512 * 64) return launch_cfg<512, 64, true>(p, kind, grid, st);
     if (t <= 1024 * 64) return launch_cfg<1024, 64, true>(p, kind, grid, st);
-    return hipErrorInvalidValue;
+    if (t > kSelectMaxSlotsUnion) return hipErrorInvalidValue;
+    const size_t union_bytes = static_cast<size_t>((t + 31) / 32) * 4;
+    hipLaunchKernelGGL(select_stream_kernel<2>, grid, dim3(kStreamThreads), union_bytes, st, p);
+    return hipGetLastError();
   }
   if (t > KV_SELECT_STREAM_ABOVE) {
     if (kind == SelectKind::kRandom)

@@ -64,7 +64,7 @@ int main() {
   EXPECT(tri_score_gqa(&sh, dummy, nullptr, 4, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, hs, ws, need, nullptr), KV_EINVAL);
 
   // selectors: b_cap below the budget, t_cap past every selector (2^26) or past the union's
-  // register tiers (65536), budget < 1, union without head scores
+  // limit (2^18), budget < 1, union without head scores
   int32_t *kept = reinterpret_cast<int32_t *>(0x3000), *nk = reinterpret_cast<int32_t *>(0x4000);
   EXPECT(kv_select_topk(&sh, &pol, (const float *)dummy, kept, 1000, nk, nullptr), KV_ESHAPE);
   kv_shape big = sh;
@@ -72,7 +72,7 @@ int main() {
   EXPECT(kv_select_topk(&big, &pol, (const float *)dummy, kept, 1024, nk, nullptr), KV_ESHAPE);
   EXPECT(kv_select_random(&big, &pol, nullptr, 1, 0, kept, 1024, nk, nullptr), KV_ESHAPE);
   EXPECT(kv_select_random_shared(&big, &pol, nullptr, 1, 0, kept, 1024, nk, nullptr), KV_ESHAPE);
-  big.t_cap = 65537;
+  big.t_cap = (1 << 18) + 1;
   EXPECT(kv_select_union(&big, &pol, 4, 0, (const float *)dummy, (const float *)dummy, kept, 1024, nk, nullptr), KV_ESHAPE);
   kv_policy zero = pol;
   zero.budget = 0;

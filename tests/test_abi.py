@@ -83,7 +83,7 @@ def test_host_validation_rejects_bad_arguments(lib):
     # one head's bf16 d = 128 rows beyond 32-bit byte offsets
     huge = L.KvShape(1, 1, 1, 128, ((1 << 31) - (64 << 9)) // 256, L.KV_BF16, seq)
     assert lib.tri_score(ctypes.byref(huge), dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, None) == L.KV_ESHAPE
-    big = L.KvShape(1, 1, 1, 8, 65537, L.KV_BF16, seq)          # past the union selector's register tiers
+    big = L.KvShape(1, 1, 1, 8, (1 << 18) + 1, L.KV_BF16, seq)   # past the union selector's LDS bits
     huge_sel = L.KvShape(1, 1, 1, 8, (1 << 26) + 1, L.KV_BF16, seq)  # past every selector
     # grouped-query scores: group outside 1..16, workspace too small, fp32 head_dim beyond 128
     shg = L.KvShape(2, 3, 4, 128, 1000, L.KV_BF16, None)

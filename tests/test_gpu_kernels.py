@@ -608,6 +608,14 @@ UNION_CASES = [
     ("union-fits", 3000, [2048, 100], [100, 50], 2048, 128, 4, 0, "normal"),
     ("union-ragged-rows", 2999, [2999, 2500], [7, 0], 700, 9, 3, 0, "specials"),   # t_cap % 4 != 0
     ("union-20k-ragged-rows", 20001, [20001], [300], 2048, 64, 4, 0, "ties"),
+    # past 65536 slots: the re-reading kernel with the union as a bit per slot in LDS
+    ("union-stream-70k-g4", 70000, [70000, 65537], [1024, 0], 3072, 128, 4, 0, "normal"),
+    ("union-stream-128k-g8-ties", 131072, [131072, 100000], [2048, 10], 4096, 128, 8, 0, "ties"),
+    ("union-stream-100k-g2-long", 100000, [100000], [512], 2048, 128, 2, 2048, "normal"),
+    ("union-stream-80k-g4-short", 80000, [80000, 3000], [100, 0], 2048, 64, 4, 1, "specials"),
+    ("union-stream-70k-crowded", 70000, [70000], [100], 3000, 64, 3, 0, "cluster"),
+    ("union-stream-66k-equal", 66000, [66000], [100], 500, 10, 4, 0, "equal"),
+    ("union-stream-262k-g4", 262144, [262144, 70001], [1024, 3], 3072, 128, 4, 0, "normal"),
 ]
 
 
