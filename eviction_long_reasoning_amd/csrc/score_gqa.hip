@@ -19,6 +19,11 @@
 // the tile is one MFMA and the product needs no cross-lane reduction: lane l ends up holding
 // query head l % 16's scores of keys 4 (l / 16) .. + 3. Up to 16 query heads cost the same as
 // one. The norm-based term is the same contraction over |k_f| and (E|q_f| - |q_bar_f|).
+// Forming y costs as many VALU cycles per tile as the 32 MFMAs take, and the two were measured
+// not to overlap; with at most four query heads 12 of the MFMA's 16 columns idle, and the VALU
+// form (two FMAs per head and band on the y it forms anyway, gqa_stream_kernel) is faster. So
+// groups of at most four with contiguous positions and bf16 rows of 4, 8 or 16 pieces take the
+// VALU form; everything else the matrix form.
 // Kernel A writes the G raw scores and, per (head, chunk of keys), fp64 sums of s and s^2 for
 // each g. Kernel B reduces a head's chunk sums in a fixed order (deterministic, no atomics) and
 // writes max_g (s_g - mu_g) / sigma_g (0 for a query head whose scores do not vary).
@@ -42,6 +47,12 @@ __device__ __forceinline__ float2 cis_rev(double rev, double m) {
 
 typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Largest group scored by the VALU stream form (gqa_stream_kernel); 0 sends every group to the
+// matrix cores
+#ifndef KV_GQA_STREAM_MAX_G
+#define KV_GQA_STREAM_MAX_G 4
+#endif
 
 constexpr int kTile = kGqaTile;
 constexpr int kTilesPerWave = kGqaTilesPerWave;
@@ -330,10 +341,230 @@ __global__ __launch_bounds__(kScoreThreads) void gqa_finish_kernel(const GqaPara
   }
 }
 
+// Small groups (G <= 4) with contiguous positions: the VALU form in the single-centre stream
+// layout. LPK lanes share a key (one 16-byte piece each), KPS = 64 / LPK keys per wave load, the
+// phase z = exp(i omega_f m) of a lane's key carried from key to key by a fixed step and derived
+// exactly at every batch of 64 keys. Per band the lane forms y = z conj(k) once; each query head
+// then costs two FMAs, Re(u_g y). Work goes in sub-batches of SUB = min(LPK, 8) steps whose loads
+// are issued one sub-batch ahead (two register buffers); a sub-batch's SUB partial sums per query
+// head are combined by a reduce-scatter over SUB lanes plus one exchange per further lane
+// doubling, after which each lane of the first SUB of its key group holds one finished score.
+// The fp64 sums of s and s^2 per (head, chunk) have the layout kernel B reads.
+template <int N>
+__device__ __forceinline__ float reduce_scatter(float (&acc)[N], int g) {
+#pragma unroll
+  for (int h = N / 2; h >= 1; h /= 2) {
+    const bool upper = (g & h) != 0;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      float lo = acc[i], hi = acc[i + h];
+      asm volatile("" : "+v"(lo), "+v"(hi));  // keep the per-lane choice a register select
+      const float send = upper ? lo : hi;
+      const float keep = upper ? hi : lo;
+      acc[i] = keep + __shfl_xor(send, h, 64);
+    }
+  }
+  return acc[0];
+}
+
+constexpr int kStreamLoadNt = 2;  // cache-policy bit "nt": every key row is read once
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamLoadNt);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Steps per sub-batch (at most): 4 was measured as fast as 8 (three waves per SIMD instead of two)
+#ifndef KV_GQA_SUB
+#define KV_GQA_SUB 8
+#endif
+template <bool BF16, int LPK, bool FULL, bool NORM, int GM>
+__global__ __launch_bounds__(kScoreThreads) void gqa_stream_kernel(const GqaParams p) {
+  constexpr int BPL = BF16 ? 4 : 2;
+  constexpr int KPS = 64 / LPK;
+  constexpr int SUB = LPK < KV_GQA_SUB ? LPK : KV_GQA_SUB;  // steps per sub-batch
+  constexpr int SUB_KEYS = SUB * KPS;
+  constexpr int NW = kScoreThreads / 64;
+  constexpr int WAVE_KEYS = kGqaChunk / NW;
+  constexpr int NSB = WAVE_KEYS / SUB_KEYS;       // sub-batches per wave
+  constexpr int SB_PER_BATCH = 64 / SUB_KEYS;     // sub-batches per 64 keys (phase re-derived)
+  constexpr int EB = BF16 ? 2 : 4;
+  static_assert(WAVE_KEYS % 64 == 0 && NSB % 2 == 0, "whole batches, pairs of sub-batches");
+  __shared__ double part[NW][GM][2];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane % LPK;
+  const int kk = lane / LPK;
+  const int head = blockIdx.x / p.chunks_per_head;
+  const int chunk = blockIdx.x - head * p.chunks_per_head;
+  const int h = head % p.H;
+  const int s = (head / p.H) % p.S;
+  const int l = head / (p.H * p.S);
+  const int G = p.G;
+
+  const int T = min(max(p.seq_len[s], 0), p.t_cap);
+  const int wave_first = chunk * kGqaChunk + wave * WAVE_KEYS;
+  const int nsb = wave_first < T ? min(NSB, (T - wave_first + SUB_KEYS - 1) / SUB_KEYS) : 0;
+
+  const bool live = FULL || g * BPL < p.F;
+  const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
+  const int row_bytes = p.d * EB;
+  // rows at or past T read as zeros (buffer range check); their scores are not stored
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(static_cast<const char *>(p.K) + slot0 * static_cast<size_t>(row_bytes)), 0,
+      T * row_bytes, 0x00020000);
+  const int lane_off = kk * row_bytes + (live ? g * 16 : 0);
+  const int step_bytes = KPS * row_bytes;
+  auto issue = [&](int sb, uint4(&d)[SUB]) {
+    const int boff = (wave_first + sb * SUB_KEYS) * row_bytes + lane_off;
+#pragma unroll
+    for (int t = 0; t < SUB; ++t) d[t] = ld16(rk, boff, t * step_bytes);
+  };
+  uint4 da[SUB], db[SUB];
+  if (nsb > 0) issue(0, da);
+
+  const double tq = static_cast<double>(p.t_cur[s]);
+  const size_t lhg = (static_cast<size_t>(l) * p.H + h) * G;
+  float ux[GM][BPL], uyn[GM][BPL], cn[GM][BPL];
+  double rev[BPL];
+  float2 w[BPL], z[BPL];
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int b = g * BPL + i;
+    rev[i] = live ? p.rev[b] : 0.0;
+    w[i] = live ? cis_rev(rev[i], -static_cast<double>(KPS)) : make_float2(1.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < GM; ++q) {
+      ux[q][i] = uyn[q][i] = cn[q][i] = 0.f;
+      if (live && q < G) {
+        const float2 qf = reinterpret_cast<const float2 *>(p.qbar + (lhg + q) * p.d)[b];
+        const float2 A = p.A[b];
+        ux[q][i] = qf.x * A.x - qf.y * A.y;
+        uyn[q][i] = -(qf.x * A.y + qf.y * A.x);       // Re(u y) = u.x y.x + (-u.y) y.y
+        if (NORM) {
+          const float qa = p.qabs[(lhg + q) * p.F + b];
+          cn[q][i] = qa > 0.f ? qa - __builtin_amdgcn_sqrtf(fmaf(qf.x, qf.x, qf.y * qf.y)) : 0.f;
+        }
+      }
+    }
+  }
+  double sum[GM], sum2[GM];
+#pragma unroll
+  for (int q = 0; q < GM; ++q) sum[q] = sum2[q] = 0.0;
+  float *raw_head = p.raw + static_cast<size_t>(head) * G * p.t_cap;
+
+  auto consume = [&](int sb, const uint4(&d)[SUB]) {
+    const int j0 = wave_first + sb * SUB_KEYS;
+    if (sb % SB_PER_BATCH == 0) {   // exact phase of this lane's first key of the batch
+      const double m0 = tq - static_cast<double>(j0 + kk);
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) z[i] = live ? cis_rev(rev[i], m0) : make_float2(0.f, 0.f);
+    }
+    float acc[GM][SUB];
+#pragma unroll
+    for (int t = 0; t < SUB; ++t) {
+      const uint32_t wd[4] = {d[t].x, d[t].y, d[t].z, d[t].w};
+      float a[GM];
+#pragma unroll
+      for (int q = 0; q < GM; ++q) a[q] = 0.f;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        const float re = BF16 ? __uint_as_float(wd[i] << 16) : __uint_as_float(wd[2 * i]);
+        const float im = BF16 ? __uint_as_float(wd[i] & 0xffff0000u) : __uint_as_float(wd[2 * i + 1]);
+        const float yx = fmaf(z[i].x, re, z[i].y * im);    // y = z conj(k)
+        const float yy = fmaf(z[i].y, re, -z[i].x * im);
+        const float ka = NORM ? __builtin_amdgcn_sqrtf(fmaf(re, re, im * im)) : 0.f;
+#pragma unroll
+        for (int q = 0; q < GM; ++q) {
+          a[q] = fmaf(ux[q][i], yx, a[q]);
+          a[q] = fmaf(uyn[q][i], yy, a[q]);
+          if (NORM) a[q] = fmaf(cn[q][i], ka, a[q]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < GM; ++q) acc[q][t] = FULL ? a[q] : (live ? a[q] : 0.f);
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) z[i] = cmul(z[i], w[i]);
+    }
+    const int jj = j0 + (g % SUB) * KPS + kk;
+    const bool store = g < SUB && jj < T;
+#pragma unroll
+    for (int q = 0; q < GM; ++q) {
+      float sc = reduce_scatter<SUB>(acc[q], g % SUB);
+#pragma unroll
+      for (int hh = SUB; hh < LPK; hh *= 2) sc += __shfl_xor(sc, hh, 64);
+      if (store && q < G) {
+        __builtin_nontemporal_store(sc, raw_head + static_cast<size_t>(q) * p.t_cap + jj);
+        sum[q] += static_cast<double>(sc);
+        sum2[q] += static_cast<double>(sc) * static_cast<double>(sc);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int sb = 0; sb < NSB; sb += 2) {
+    if (sb >= nsb) break;
+    if (sb + 1 < nsb) issue(sb + 1, db);
+    consume(sb, da);
+    if (sb + 1 >= nsb) break;
+    if (sb + 2 < nsb) issue(sb + 2, da);
+    consume(sb + 1, db);
+  }
+
+  // per (head, chunk) sums for each query head, in a fixed reduction order
+#pragma unroll
+  for (int q = 0; q < GM; ++q) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      sum[q] += __shfl_xor(sum[q], off, 64);
+      sum2[q] += __shfl_xor(sum2[q], off, 64);
+    }
+    if (lane == 0) {
+      part[wave][q][0] = sum[q];
+      part[wave][q][1] = sum2[q];
+    }
+  }
+  __syncthreads();
+  if (static_cast<int>(threadIdx.x) < G) {
+    const int q = threadIdx.x;
+    double a = 0.0, b = 0.0;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) {
+      a += part[wv][q][0];
+      b += part[wv][q][1];
+    }
+    double *dst = p.partials + ((static_cast<size_t>(head) * p.chunks_per_head + chunk) * G + q) * 2;
+    dst[0] = a;
+    dst[1] = b;
+  }
+}
+
 int group_bound(int G) {
   int gm = 1;
   while (gm < G) gm <<= 1;
   return gm;
+}
+
+template <bool NORM, int GM>
+hipError_t launch_stream_lpk(const GqaParams &p, int lpk, dim3 grid, hipStream_t st) {
+  const dim3 blk(kScoreThreads);
+  switch (lpk) {
+    case 4: hipLaunchKernelGGL((gqa_stream_kernel<true, 4, true, NORM, GM>), grid, blk, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((gqa_stream_kernel<true, 8, true, NORM, GM>), grid, blk, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((gqa_stream_kernel<true, 16, true, NORM, GM>), grid, blk, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <bool NORM>
+hipError_t launch_stream(const GqaParams &p, int lpk, dim3 grid, hipStream_t st) {
+  switch (group_bound(p.G)) {
+    case 1: return launch_stream_lpk<NORM, 1>(p, lpk, grid, st);
+    case 2: return launch_stream_lpk<NORM, 2>(p, lpk, grid, st);
+    case 4: return launch_stream_lpk<NORM, 4>(p, lpk, grid, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <bool BF16, bool FULL, bool POS, bool NORM>
@@ -365,7 +596,14 @@ hipError_t launch_score_gqa(const GqaParams &p, int dtype_bf16, int pieces_per_l
   const bool pos = p.pos != nullptr, norm = p.qabs != nullptr;
   const int ppq = pieces_per_lane;
   hipError_t e;
-  if (dtype_bf16)
+  // bf16 rows of 4, 8 or 16 pieces (head_dim 32, 64, 128), G <= 4, contiguous positions, rows
+  // addressable with 32-bit offsets: the VALU stream form; everything else: the matrix cores
+  const int pieces = p.d * (dtype_bf16 ? 2 : 4) / 16;
+  const bool stream = dtype_bf16 && !pos && p.G <= KV_GQA_STREAM_MAX_G && (pieces == 4 || pieces == 8 || pieces == 16) &&
+                      static_cast<long long>(p.t_cap + kGqaChunk) * p.d * 2 < (1ll << 31);
+  if (stream)
+    e = norm ? launch_stream<true>(p, pieces, grid, st) : launch_stream<false>(p, pieces, grid, st);
+  else if (dtype_bf16)
     e = pos ? (norm ? launch_full<true, true, true>(p, ppq, grid, st) : launch_full<true, true, false>(p, ppq, grid, st))
             : (norm ? launch_full<true, false, true>(p, ppq, grid, st) : launch_full<true, false, false>(p, ppq, grid, st));
   else

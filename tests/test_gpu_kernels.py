@@ -170,6 +170,13 @@ GQA_CASES = [
     ("gqa-bf16-d256-g16-norm", "bf16", 256, 1, 1, 2, 16, [700], 704, "slots", True, 3),
     ("gqa-fp32-d128-g12-gappy", "f32", 128, 1, 2, 1, 12, [600, 17], 640, "gappy", False, -1),
     ("gqa-bf16-d32-g4-tiny", "bf16", 32, 2, 1, 1, 4, [3], 5, "slots", False, -1),
+    # groups of at most four with contiguous positions and bf16 rows of 4, 8 or 16 pieces take the
+    # VALU form: G = 1..4, with and without the norm term, a zero query head, ragged tails
+    ("gqa-valu-bf16-d64-g2-norm", "bf16", 64, 1, 2, 2, 2, [1500, 1025], 1536, "slots", True, -1),
+    ("gqa-valu-bf16-d128-g1", "bf16", 128, 1, 1, 2, 1, [2049], 2100, "slots", False, -1),
+    ("gqa-valu-bf16-d128-g3-zero", "bf16", 128, 2, 1, 1, 3, [1030], 1030, "slots", False, 2),
+    ("gqa-valu-bf16-d128-g4-norm", "bf16", 128, 1, 2, 1, 4, [3000, 1], 3000, "slots", True, -1),
+    ("gqa-valu-bf16-d32-g4", "bf16", 32, 1, 1, 3, 4, [4097], 4100, "slots", False, -1),
 ]
 
 
