@@ -35,9 +35,15 @@
 #ifndef KV_SELECT_WIDE
 #define KV_SELECT_WIDE 0
 #endif
-// top-k and random caches longer than this run the kernel that re-reads its keys
+// Top-k and random (union) caches longer than this run the kernel that re-reads its keys. Past
+// 32768 slots the 1024 x 64 register tier spills; the re-reading kernel was measured faster there
+// for top-k (40000 slots: 0.32 -> 0.22 ms; 65536: within 4 %) and random (0.48 -> 0.35, 0.66 ->
+// 0.57 ms), slower for the union (1.34 -> 1.54, 1.64 -> 2.72 ms), on 1152 heads.
 #ifndef KV_SELECT_STREAM_ABOVE
-#define KV_SELECT_STREAM_ABOVE 65536
+#define KV_SELECT_STREAM_ABOVE 32768
+#endif
+#ifndef KV_UNION_STREAM_ABOVE
+#define KV_UNION_STREAM_ABOVE 65536
 #endif
 
 namespace kvevict {
@@ -536,8 +542,8 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   if (writer) p.n_kept[s] = n_kept;
 }
 
-// Caches longer than the register tiers hold (t_cap > 65536 slots; long-context models reach
-// 128K tokens): the same rankings, threshold rule and ordered scan, with every step recomputing
+// Caches past the register tiers (top-k and random past 32768 slots, the union past 65536;
+// context lengths reach 128K tokens): the same rankings, threshold rule and ordered scan, with every step recomputing
 // the keys from memory (a score load, or the Philox draw) instead of keeping them in registers.
 // Steps: min/max (scores) and the 1024-bin histogram, the threshold bin's keys ranked in LDS (or,
 // when crowded, OR/AND and 8-bit radix passes), then the ordered scan in chunks of 4 * NT slots
@@ -914,12 +920,14 @@ hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st)
     // The union's extra passes hold more registers: past 8192 slots it runs 512-thread tiers
     // (a 1024-thread workgroup is limited to 128 registers per lane); past 65536 slots, the
     // re-reading kernel with the union bits in dynamic LDS.
-    if (t <= 256 * 4) return launch_cfg<256, 4, true>(p, kind, grid, st);
-    if (t <= 256 * 16) return launch_cfg<256, 16, true>(p, kind, grid, st);
-    if (t <= 256 * 32) return launch_cfg<256, 32, true>(p, kind, grid, st);
-    if (t <= 512 * 32) return launch_cfg<512, 32, true>(p, kind, grid, st);
-    if (t <= 512 * 64) return launch_cfg<512, 64, true>(p, kind, grid, st);
-    if (t <= 1024 * 64) return launch_cfg<1024, 64, true>(p, kind, grid, st);
+    if (t <= KV_UNION_STREAM_ABOVE) {
+      if (t <= 256 * 4) return launch_cfg<256, 4, true>(p, kind, grid, st);
+      if (t <= 256 * 16) return launch_cfg<256, 16, true>(p, kind, grid, st);
+      if (t <= 256 * 32) return launch_cfg<256, 32, true>(p, kind, grid, st);
+      if (t <= 512 * 32) return launch_cfg<512, 32, true>(p, kind, grid, st);
+      if (t <= 512 * 64) return launch_cfg<512, 64, true>(p, kind, grid, st);
+      if (t <= 1024 * 64) return launch_cfg<1024, 64, true>(p, kind, grid, st);
+    }
     if (t > kSelectMaxSlotsUnion) return hipErrorInvalidValue;
     const size_t union_bytes = static_cast<size_t>((t + 31) / 32) * 4;
     hipLaunchKernelGGL(select_stream_kernel<2>, grid, dim3(kStreamThreads), union_bytes, st, p);
@@ -941,7 +949,9 @@ hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st)
 #else
   if (t <= 1024 * 32) return launch_cfg<1024, 32, false>(p, kind, grid, st);
 #endif
+#if KV_SELECT_STREAM_ABOVE > 32768
   if (t <= 1024 * 64) return launch_cfg<1024, 64, false>(p, kind, grid, st);
+#endif
   return hipErrorInvalidValue;
 }
 

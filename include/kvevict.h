@@ -247,7 +247,7 @@ size_t kv_score_gqa_workspace_bytes(const kv_shape *shape, int32_t group);
  *  b_cap    must be >= max(budget, prompt_cap).
  *  n_kept   device [S] int32 output: |kept| of sequence s (same for every
  *           layer and head).
- * Requires t_cap <= 2^26. Up to 65536 slots a head's keys stay in registers;
+ * Requires t_cap <= 2^26. Up to 32768 slots a head's keys stay in registers;
  * longer caches (context lengths reach 128K tokens, [TA-sum] 3.4 "Handling
  * Multiple Future Positions", on the offset range) run a kernel that
  * re-reads the scores at every step.
@@ -268,7 +268,7 @@ kv_status kv_select_topk(const kv_shape *shape, const kv_policy *policy,
  *
  *  pos      device [L,S,H,t_cap] int32 positions for the counter, or NULL (p_j = j).
  *  seed     64-bit key; event: eviction counter (fresh draws per event).
- *  kept, b_cap, n_kept as for kv_select_topk (t_cap <= 2^26; past 65536
+ *  kept, b_cap, n_kept as for kv_select_topk (t_cap <= 2^26; past 32768
  *  slots the draws are recomputed at every step).
  */
 kv_status kv_select_random(const kv_shape *shape, const kv_policy *policy,
