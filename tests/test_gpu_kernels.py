@@ -680,6 +680,64 @@ def test_calls_run_on_the_current_stream():
     assert torch.equal(ref[2][..., :1000, :].view(torch.int16), got[2][..., :1000, :].view(torch.int16))
 
 
+def test_pass_replays_from_a_hip_graph():
+    # the calls only launch kernels on the current stream (no allocation, no memset, no sync), so a
+    # pass captures into a HIP graph; every replay, with eager work in between that changes the
+    # inputs, matches the eager pass on the same inputs bit for bit
+    r = rng(571, 0)
+    L, S, H, T, d, B = 2, 2, 3, 4000, 128, 1000
+    Kf = [r.standard_normal((L, S, H, T, d)).astype(np.float32) for _ in range(3)]
+    K = _to_dev_keys(Kf[0], "bf16")
+    V = K.clone()
+    qb = torch.from_numpy(r.standard_normal((L, H, d)).astype(np.float32)).to(DEV)
+    Ts, Ps = _i32([T, 3100]), _i32([100, 0])
+    sc = torch.empty((L, S, H, T), device=DEV)
+    kept = torch.empty((L, S, H, B), dtype=torch.int32, device=DEV)
+    nk = torch.empty((S,), dtype=torch.int32, device=DEV)
+    Ko = torch.empty((L, S, H, B, d), dtype=K.dtype, device=DEV)
+    Vo = torch.empty_like(Ko)
+    Po = torch.empty((L, S, H, B), dtype=torch.int32, device=DEV)
+    args = (1e6, [2 ** i for i in range(17)])
+
+    def run():
+        kv.tri_score(K, qb, Ts, Ts, *args, out=sc)
+        kv.kv_select_topk(sc, Ts, Ps, B, 32, 100, kept=kept, n_kept=nk)
+        kv.kv_compact(K, V, kept, nk, Ts, B, K_out=Ko, V_out=Vo, pos_out=Po)
+
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+
+    def written():
+        out = [sc[:, 0].clone(), sc[:, 1, :, :3100].clone(), kept.clone(), nk.clone()]
+        n = int(nk[0])
+        out += [Ko[:, 0, :, :n].clone(), Vo[:, 0, :, :n].clone(), Po[:, 0, :, :n].clone()]
+        n1 = int(nk[1])
+        out += [Ko[:, 1, :, :n1].clone(), Po[:, 1, :, :n1].clone()]
+        return out
+
+    for rep in range(3):
+        K.copy_(_to_dev_keys(Kf[rep], "bf16"))          # eager work between replays
+        V.copy_(K.flip(-1))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = written()
+        run()
+        torch.cuda.synchronize()
+        ref = written()
+        for a, b in zip(got, ref):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), f"replay {rep}"
+
+
 def test_audit_accepts_every_selector_and_flags_broken_lists():
     L, S, H, t_cap = 2, 3, 2, 5000
     Ts, Ps, B, R = [5000, 1800, 4000], [100, 0, 3900], 2000, 64
