@@ -443,6 +443,42 @@ def test_select_random_bit_exact(case, with_pos):
                 assert np.all(kept[l, s, h, ref.size:] == -1)
 
 
+# every tier boundary of the selectors (register tiers, the union's tiers, the re-reading kernel)
+TIER_EDGES = [1, 3, 1024, 1025, 4096, 4097, 8192, 8193, 16384, 16385, 32768, 32769, 65536, 65537]
+
+
+@pytest.mark.parametrize("t_cap", TIER_EDGES)
+def test_selectors_at_tier_edges_bit_exact(t_cap):
+    # seeded shapes around each boundary: a full head, a ragged one and a short one per sequence,
+    # budgets below and above the prompt, ties in the scores; top-k, random and union checked
+    # against the oracle on every head
+    r = rng(580, t_cap)
+    S, L, H, G = 3, 1, 2, int(r.integers(1, 6))
+    Ts = [t_cap, int(r.integers(0, t_cap + 1)), min(t_cap, int(r.integers(0, 300)))]
+    B = int(r.integers(1, max(2, t_cap // 2) + 1))
+    Ps = [int(r.integers(0, min(t_cap, 2 * B) + 1)) for _ in range(S)]
+    R = int(r.integers(0, 200))
+    pcap = max(Ps)
+    name = f"edge-{t_cap}"
+    sc = _select_scores(name, "ties", (L, S, H, t_cap))
+    hs = _select_scores(name + "-heads", "ties", (L, S, H, G, t_cap))
+    Td, Pd = _i32(Ts), _i32(Ps)
+    log(f"[edges] t_cap {t_cap}: T {Ts}, P {Ps}, B {B}, R {R}, G {G}")
+    kt, nt = kv.kv_select_topk(torch.from_numpy(sc).to(DEV), Td, Pd, B, R, pcap)
+    kr, nr = kv.kv_select_random((L, S, H, t_cap), Td, Pd, B, R, pcap, 99, 4)
+    ku, nu = kv.kv_select_union(torch.from_numpy(hs).to(DEV), torch.from_numpy(sc).to(DEV), Td, Pd, B, R, pcap)
+    kt, kr, ku = kt.cpu().numpy(), kr.cpu().numpy(), ku.cpu().numpy()
+    for s in range(S):
+        for h in range(H):
+            refs = (oracle.select_topk(sc[0, s, h], Ts[s], Ps[s], B, R),
+                    oracle.select_random(Ts[s], Ps[s], B, R, None, 99, 4, 0, h, s),
+                    oracle.select_union(hs[0, s, h], sc[0, s, h], Ts[s], Ps[s], B, R))
+            for what, got, n, ref in zip(("topk", "random", "union"), (kt, kr, ku), (nt, nr, nu), refs):
+                assert int(n[s]) == ref.size, f"{name} {what} s{s}"
+                assert np.array_equal(got[0, s, h, :ref.size], ref), f"{name} {what} s{s} h{h}"
+                assert np.all(got[0, s, h, ref.size:] == -1), f"{name} {what} s{s} h{h} padding"
+
+
 def test_select_random_fresh_per_event_and_head():
     Ts, Ps = [4000], [100]
     a, _ = kv.kv_select_random((1, 1, 2, 4000), _i32(Ts), _i32(Ps), 1000, 32, 100, 9, 1)
