@@ -497,6 +497,9 @@ COMPACT_CASES = [
     ("bf16-d96", "bf16", 96, 1, 1, 2, 900, [333], 400, 400, False),
     ("fp32-d64", "f32", 64, 1, 1, 1, 512, [128], 128, 128, False),
     ("fp32-d256", "f32", 256, 1, 2, 1, 300, [300, 17], 300, 300, True),
+    # an output narrower than n_kept keeps the first out_cap rows
+    ("bf16-d128-out-narrower", "bf16", 128, 1, 2, 2, 3000, [2048, 500], 2048, 1000, True),
+    ("bf16-d64-out-1", "bf16", 64, 1, 1, 2, 700, [600], 600, 1, False),
 ]
 
 
@@ -526,7 +529,7 @@ def test_compact_bit_exact(case):
     for l in range(L):
         for s in range(S):
             for h in range(H):
-                n = nks[s]
+                n = min(nks[s], out_cap)
                 rk, rv, rp = oracle.compact(Kh[l, s, h], Vh[l, s, h], None if pos is None else pos[l, s, h],
                                             kept[l, s, h, :n])
                 assert np.array_equal(Ko[l, s, h, :n], rk) and np.array_equal(Vo[l, s, h, :n], rv)
