@@ -2,6 +2,7 @@
 // offset average, and kernel launches. See include/kvevict.h for the contract.
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "kvevict.h"
 #include "kv_internal.hpp"
@@ -14,6 +15,13 @@ namespace {
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// 4-byte element arrays (int32 / fp32) are read and written as whole words; NULL passes (optional
+// arguments are checked for presence separately)
+bool words(std::initializer_list<const void *> ps) {
+  for (const void *p : ps)
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return false;
+  return true;
+}
 
 // Selectors never touch K/V rows, so they ignore head_dim and dtype (rows == false).
 // need_len == false: only the sizes are checked (workspace queries take no device arrays).
@@ -95,6 +103,7 @@ KV_EXPORT kv_status tri_score(const kv_shape *shape, const void *K, const int32_
   if (!(rope_theta > 0.0) || !std::isfinite(rope_theta)) return KV_EINVAL;
   if (n_delta < 1 || n_delta > kMaxDeltas) return KV_EINVAL;
   if (!aligned16(K) || (reinterpret_cast<uintptr_t>(qbar) & 7u)) return KV_EINVAL;
+  if (!words({pos, qabs, t_cur, scores, shape->seq_len})) return KV_EINVAL;
 
   ScoreParams p{};
   p.K = K;
@@ -136,6 +145,7 @@ KV_EXPORT kv_status tri_score_rotated(const kv_shape *shape, const void *K, cons
   if (n_delta < 1 || n_delta > kMaxDeltas) return KV_EINVAL;
   if (rope_style != KV_ROPE_INTERLEAVED && rope_style != KV_ROPE_HALF) return KV_EINVAL;
   if (!aligned16(K) || (reinterpret_cast<uintptr_t>(qbar) & 3u)) return KV_EINVAL;
+  if (!words({qabs, t_cur, scores, shape->seq_len, paged ? paged->block_table : nullptr})) return KV_EINVAL;
 
   RotScoreParams p{};
   p.K = K;
@@ -205,6 +215,7 @@ KV_EXPORT kv_status tri_score_gqa(const kv_shape *shape, const void *K, const in
   if (n_delta < 1 || n_delta > kMaxDeltas) return KV_EINVAL;
   if (!aligned16(K) || (reinterpret_cast<uintptr_t>(qbar) & 7u) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
     return KV_EINVAL;
+  if (!words({pos, qabs, t_cur, head_scores, scores, shape->seq_len})) return KV_EINVAL;
   if (workspace_bytes < gqa_workspace(shape, group)) return KV_ESHAPE;
   // one head's per-query-head scores are stored through a 32-bit buffer offset
   if (static_cast<long long>(group) * shape->t_cap * 4 >= (1ll << 31)) return KV_ESHAPE;
@@ -255,6 +266,7 @@ static kv_status select_common(const kv_shape *shape, const kv_policy *policy, i
   if (st != KV_OK) return st;
   if ((st = check_policy(policy, b_cap)) != KV_OK) return st;
   if (!kept || !n_kept) return KV_EINVAL;
+  if (!words({kept, n_kept, shape->seq_len, policy->prompt_len})) return KV_EINVAL;
   if (shape->t_cap > max_slots) return KV_ESHAPE;
   p.seq_len = shape->seq_len;
   p.prompt_len = policy->prompt_len;
@@ -276,7 +288,7 @@ KV_EXPORT kv_status kv_select_topk(const kv_shape *shape, const kv_policy *polic
   SelectParams p{};
   kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p);
   if (st != KV_OK) return st;
-  if (!scores) return KV_EINVAL;
+  if (!scores || !words({scores})) return KV_EINVAL;
   p.scores = scores;
   return hip_status(launch_select(p, SelectKind::kTopk, static_cast<hipStream_t>(stream)));
 }
@@ -287,6 +299,7 @@ KV_EXPORT kv_status kv_select_random(const kv_shape *shape, const kv_policy *pol
   SelectParams p{};
   kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p);
   if (st != KV_OK) return st;
+  if (!words({pos})) return KV_EINVAL;
   p.pos = pos;
   p.seed_lo = static_cast<uint32_t>(seed & 0xffffffffu);
   p.seed_hi = static_cast<uint32_t>(seed >> 32);
@@ -300,7 +313,7 @@ KV_EXPORT kv_status kv_select_union(const kv_shape *shape, const kv_policy *poli
   SelectParams p{};
   kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p, kSelectMaxSlotsUnion);
   if (st != KV_OK) return st;
-  if (!head_scores || !scores) return KV_EINVAL;
+  if (!head_scores || !scores || !words({head_scores, scores})) return KV_EINVAL;
   if (group < 1 || group > 64) return KV_EINVAL;
   p.scores = scores;
   p.head_scores = head_scores;
@@ -314,7 +327,7 @@ KV_EXPORT kv_status kv_audit_kept(const kv_shape *shape, const kv_policy *policy
   SelectParams p{};
   kv_status st = select_common(shape, policy, const_cast<int32_t *>(kept), b_cap, const_cast<int32_t *>(n_kept), p);
   if (st != KV_OK) return st;
-  if (!bad) return KV_EINVAL;
+  if (!bad || !words({bad})) return KV_EINVAL;
   return hip_status(launch_audit(p, bad, static_cast<hipStream_t>(stream)));
 }
 
@@ -324,6 +337,7 @@ KV_EXPORT kv_status kv_select_random_shared(const kv_shape *shape, const kv_poli
   SelectParams p{};
   kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p);
   if (st != KV_OK) return st;
+  if (!words({pos})) return KV_EINVAL;
   p.pos = pos;
   p.seed_lo = static_cast<uint32_t>(seed & 0xffffffffu);
   p.seed_hi = static_cast<uint32_t>(seed >> 32);
@@ -349,6 +363,7 @@ KV_EXPORT kv_status kv_compact_inplace(const kv_shape *shape, void *K, void *V, 
   if (!K || !V || !kept || !n_kept) return KV_EINVAL;
   if (b_cap < 1) return KV_EINVAL;
   if (!aligned16(K) || !aligned16(V)) return KV_EINVAL;
+  if (!words({pos, kept, n_kept, shape->seq_len})) return KV_EINVAL;
   const size_t heads = static_cast<size_t>(shape->n_layers) * shape->n_seq * shape->n_kv_heads;
   const size_t row_bytes = static_cast<size_t>(shape->head_dim) * elem_bytes(shape);
   const size_t bytes = heads * shape->t_cap * row_bytes;
@@ -385,6 +400,7 @@ KV_EXPORT kv_status kv_compact(const kv_shape *shape, const void *K_in, const vo
   if (!K_in || !V_in || !kept || !n_kept || !K_out || !V_out) return KV_EINVAL;
   if (b_cap < 1 || out_cap < 1) return KV_EINVAL;
   if (!aligned16(K_in) || !aligned16(V_in) || !aligned16(K_out) || !aligned16(V_out)) return KV_EINVAL;
+  if (!words({pos_in, kept, n_kept, pos_out, shape->seq_len})) return KV_EINVAL;
   const size_t heads = static_cast<size_t>(shape->n_layers) * shape->n_seq * shape->n_kv_heads;
   const size_t row_bytes = static_cast<size_t>(shape->head_dim) * elem_bytes(shape);
   const size_t in_bytes = heads * shape->t_cap * row_bytes, out_bytes = heads * out_cap * row_bytes;

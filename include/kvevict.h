@@ -35,6 +35,9 @@
  *    arrays (positions, scores) are the same without the last axis.
  *  - Slot j of a head holds the token at position pos[j] (or j when the
  *    position pointer is NULL). Sequence s has seq_len[s] valid slots.
+ *  - Alignment: K and V (and compaction outputs) 16 bytes; query centres
+ *    8 bytes (tri_score_rotated: 4); every int32 / fp32 array 4 bytes.
+ *    A misaligned pointer is rejected with KV_EINVAL.
  *  - Return value: KV_OK, or a negative kv_status for arguments rejected on
  *    the host (nothing is launched then) or a failed launch (KV_EHIP).
  *    Device-side data is never trusted for memory safety: lengths are
@@ -62,7 +65,7 @@ extern "C" {
 
 typedef enum kv_status {
   KV_OK = 0,
-  KV_EINVAL = -1,   /* NULL pointer, non-positive size, bad policy value, aliasing outputs */
+  KV_EINVAL = -1,   /* NULL or misaligned pointer, non-positive size, bad policy value, aliasing outputs */
   KV_EDTYPE = -2,   /* unknown element type */
   KV_ESHAPE = -3,   /* head_dim / capacity outside what the kernels support */
   KV_EHIP = -5      /* a kernel launch failed (hipGetLastError after the launch) */

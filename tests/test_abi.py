@@ -153,6 +153,39 @@ def test_host_validation_rejects_bad_arguments(lib):
                           ctypes.c_void_p(0x300000), None, 8, None) == L.KV_EINVAL
 
 
+def test_misaligned_word_arrays_are_rejected(lib):
+    # int32 / fp32 arrays must be 4-byte aligned: one misaligned pointer per entry point
+    from eviction_long_reasoning_amd import _lib as L
+    ok, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1002)
+    arr = (ctypes.c_int32 * 1)(1)
+    sh = L.KvShape(1, 1, 1, 128, 4096, L.KV_BF16, ok)
+    sh_odd = L.KvShape(1, 1, 1, 128, 4096, L.KV_BF16, odd)
+    assert lib.tri_score(ctypes.byref(sh), ok, None, ok, None, ok, 1e4, arr, 1, odd, None) == L.KV_EINVAL
+    assert lib.tri_score(ctypes.byref(sh_odd), ok, None, ok, None, ok, 1e4, arr, 1, ok, None) == L.KV_EINVAL
+    assert lib.tri_score(ctypes.byref(sh), ok, odd, ok, None, ok, 1e4, arr, 1, ok, None) == L.KV_EINVAL
+    assert lib.tri_score_rotated(ctypes.byref(sh), ok, None, 0, ok, None, odd, 1e4, arr, 1, ok, None) == L.KV_EINVAL
+    ws = ctypes.c_void_p(0x100000)
+    need = lib.kv_score_gqa_workspace_bytes(ctypes.byref(sh), 4)
+    assert lib.tri_score_gqa(ctypes.byref(sh), ok, None, 4, ok, None, ok, 1e4, arr, 1, ctypes.c_void_p(0x200002),
+                             ctypes.c_void_p(0x300000), ws, need, None) == L.KV_EINVAL
+    pol = L.KvPolicy(1024, 64, 128, ok)
+    pol_odd = L.KvPolicy(1024, 64, 128, odd)
+    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), odd, ok, 1024, ok, None) == L.KV_EINVAL
+    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol_odd), ok, ok, 1024, ok, None) == L.KV_EINVAL
+    assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, odd, 1024, ok, None) == L.KV_EINVAL
+    assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), odd, 1, 0, ok, 1024, ok, None) == L.KV_EINVAL
+    assert lib.kv_select_random_shared(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, ok, 1024, odd,
+                                       None) == L.KV_EINVAL
+    assert lib.kv_select_union(ctypes.byref(sh), ctypes.byref(pol), 2, 0, odd, ok, ok, 1024, ok, None) == L.KV_EINVAL
+    assert lib.kv_select_recent(ctypes.byref(sh_odd), ctypes.byref(pol), ok, 1024, ok, None) == L.KV_EINVAL
+    assert lib.kv_audit_kept(ctypes.byref(sh), ctypes.byref(pol), ok, 1024, ok, odd, None) == L.KV_EINVAL
+    assert lib.kv_compact(ctypes.byref(sh), ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000), None, odd, 1024,
+                          ok, ctypes.c_void_p(0x3000000), ctypes.c_void_p(0x4000000), None, 1024,
+                          None) == L.KV_EINVAL
+    assert lib.kv_compact_inplace(ctypes.byref(sh), ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000), odd, ok,
+                                  1024, ok, None) == L.KV_EINVAL
+
+
 def test_binding_fails_loudly_without_gpu_tensors():
     import torch
     import eviction_long_reasoning_amd as kv
