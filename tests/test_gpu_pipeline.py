@@ -303,6 +303,61 @@ def test_workload3_full_pass_random(full_pass):
     log("[w3] random pass: sampled heads bit-exact, all heads structurally valid")
 
 
+def test_workload3_full_size_next_rows(full_pass):
+    # the next rows at the full pass's size, in the launch configurations bench.py times, on the
+    # sampled heads: the norm term, the same memory read as post-RoPE keys (dense, and through a
+    # shuffled block table over a head-major pool), the grouped-query z-score + max with G = 4 and
+    # union selection on its outputs; recency on every head
+    w, K, V, qb = full_pass
+    L, S, H, T, d = K.shape
+    Tn, Pn = w.seq_len, w.prompt_len
+    seq, plen, tcur = i32(Tn), i32(Pn), i32(w.t_cur)
+    qbd = torch.from_numpy(qb).to(DEV)
+    qabs = query_magnitudes(w, qb)
+    sc_full = kv.tri_score(K, qbd, tcur, seq, w.theta, w.deltas, qabs=torch.from_numpy(qabs).to(DEV))
+    sc_rot = kv.tri_score_rotated(K, qbd, tcur, seq, w.theta, w.deltas)
+    bs, bps = 16, T // 16
+    g = torch.Generator(device="cpu")
+    g.manual_seed(7)
+    table = torch.randperm(S * bps, generator=g).view(S, bps).to(torch.int32).to(DEV)
+    pool = K.view(L, S * bps, H, bs, d)                        # head-major pool over the same memory
+    sc_pg = kv.tri_score_rotated(pool, qbd, tcur, seq, w.theta, w.deltas, block_table=table, head_major=True)
+    nu = query_head_centres(workload(3, q_mode="group-mean"))
+    zmax, head = kv.tri_score_gqa(K, torch.from_numpy(nu).to(DEV), tcur, seq, w.theta, w.deltas)
+    ku, nku = kv.kv_select_union(head, zmax, seq, plen, w.budget, w.recent, w.prompt_cap())
+    kr, nkr = kv.kv_select_recent((L, S, H, T), seq, plen, w.budget, w.recent, w.prompt_cap())
+    torch.cuda.synchronize()
+    # recency: every head is the prompt followed by the latest slots
+    part = oracle.partition(int(Tn[0]), int(Pn[0]), w.budget, w.recent)
+    want = torch.from_numpy(oracle.select_recent(int(Tn[0]), int(Pn[0]), w.budget, w.recent)).to(DEV)
+    assert torch.all(nkr == part.n_kept) and torch.all(kr[..., :part.n_kept] == want)
+    worst = {"norm": 0.0, "rot": 0.0, "paged": 0.0, "head": 0.0, "z": 0.0}
+    tbl = table.cpu().numpy()
+    for (l, s, h) in SAMPLED_HEADS[:4]:
+        Tl, t = int(Tn[s]), int(w.t_cur[s])
+        kf = keys_f64(host_bits(K[l, s, h, :Tl]), w.dtype)
+        ref = oracle.score_full(kf, None, qb[l, h], qabs[l, h], t, w.theta, w.deltas)
+        worst["norm"] = max(worst["norm"], assert_scores(sc_full[l, s, h, :Tl].cpu().numpy(), ref, f"norm {l, s, h}"))
+        ref = oracle.score_rotated(kf, qb[l, h], t, w.theta, w.deltas)
+        worst["rot"] = max(worst["rot"], assert_scores(sc_rot[l, s, h, :Tl].cpu().numpy(), ref, f"rot {l, s, h}"))
+        j = np.arange(Tl)
+        rows = pool[l, torch.from_numpy(tbl[s, j // bs].astype(np.int64)).to(DEV), h,
+                    torch.from_numpy(j % bs).to(DEV)]
+        ref = oracle.score_rotated(keys_f64(host_bits(rows), w.dtype), qb[l, h], t, w.theta, w.deltas)
+        worst["paged"] = max(worst["paged"], assert_scores(sc_pg[l, s, h, :Tl].cpu().numpy(), ref, f"paged {l, s, h}"))
+        zref, sref = oracle.score_gqa(kf, None, nu[l, h], t, w.theta, w.deltas)
+        hh = head[l, s, h, :, :Tl].cpu().numpy()
+        for gq in range(w.group):
+            worst["head"] = max(worst["head"], assert_scores(hh[gq], sref[gq], f"gqa {l, s, h} g{gq}"))
+        zz = zmax[l, s, h, :Tl].cpu().numpy()
+        worst["z"] = max(worst["z"], assert_z(zz, zref, f"gqa z {l, s, h}"))
+        # union selection on the kernel's own scores is bit-exact
+        uref = oracle.select_union(hh, zz, Tl, int(Pn[s]), w.budget, w.recent)
+        assert int(nku[s]) == uref.size
+        assert np.array_equal(ku[l, s, h, :uref.size].cpu().numpy(), uref), f"union {l, s, h}"
+    log(f"[w3-next] sampled heads: worst scaled errors {worst}")
+
+
 # --------------------------------------------------------------------------------------------
 def test_workload5_ragged_scored_vs_random():
     w = workload(5)
