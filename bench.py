@@ -40,7 +40,63 @@ def parse():
     ap.add_argument("--no-random", action="store_true", help="skip the random-eviction pass")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run one elementwise copy of known size then exit after one pass (for HBM counter runs)")
+    ap.add_argument("--pmc-probe-next", action="store_true",
+                    help="like --pmc-probe, then one launch of each next-row kernel over the same cache; prints "
+                         "their algorithmic bytes as one JSON line")
     return ap.parse_args()
+
+
+def pmc_probe_next(w, K, qb, qbd, seq, plen, tcur, scores, kept, nk, b_cap, dev):
+    """One launch of each next-row kernel over the full-pass cache, in this order, for the HBM
+    counter runs; returns [kernel-name fragment, algorithmic read bytes, algorithmic write bytes]
+    per dispatch."""
+    import numpy as np
+    import torch
+
+    import eviction_long_reasoning_amd as kv
+    from workloads import query_head_centres, query_magnitudes, workload
+    L, S, H, T, d = K.shape
+    e = K.element_size()
+    n = L * S * H * T
+    heads = L * S * H
+    out = []
+    kv.tri_score(K, qbd, tcur, seq, w.theta, w.deltas, out=scores,
+                 qabs=torch.from_numpy(query_magnitudes(w, qb)).to(dev))
+    out.append(["score_stream_kernel<true, 16, true, true>", n * d * e, n * 4])
+    kv.tri_score_rotated(K, qbd, tcur, seq, w.theta, w.deltas, out=scores)
+    out.append(["score_rotated_kernel<true, 16, false, 0, false>", n * d * e, n * 4])
+    bs, bps = 16, T // 16
+    g = torch.Generator(device="cpu")
+    g.manual_seed(7)
+    table = torch.randperm(S * bps, generator=g).view(S, bps).to(torch.int32).to(dev)
+    kv.tri_score_rotated(K.view(L, S * bps, H, bs, d), qbd, tcur, seq, w.theta, w.deltas, block_table=table,
+                         out=scores, head_major=True)
+    out.append(["score_rotated_kernel<true, 16, false, 2, false>", n * d * e + L * H * S * bps * 4, n * 4])
+    G = w.group
+    nu = torch.from_numpy(query_head_centres(workload(w.wid, L=L, q_mode="group-mean"))).to(dev)
+    zmax, head = kv.tri_score_gqa(K, nu, tcur, seq, w.theta, w.deltas)
+    out.append(["gqa_stream_kernel<true, 16, true, false, 4>", n * d * e, n * 4 * G])
+    out.append(["gqa_finish_kernel<4>", n * 4 * G, n * 4])
+    kv.kv_select_union(head, zmax, seq, plen, w.budget, w.recent, w.prompt_cap(), b_cap=b_cap, kept=kept, n_kept=nk)
+    out.append(["select_kernel<512, 64, 2, true>", n * 4 * (G + 1), heads * b_cap * 4])
+    del zmax, head
+    kv.kv_select_random((L, S, H, T), seq, plen, w.budget, w.recent, w.prompt_cap(), 1, 0, b_cap=b_cap, kept=kept,
+                        n_kept=nk)
+    out.append(["select_kernel<1024, 32, 1, false>", 0, heads * b_cap * 4])
+    Sl, Tl = S // 4, 4 * T
+    kl = torch.empty((L, Sl, H, b_cap), dtype=torch.int32, device=dev)
+    nkl = torch.empty((Sl,), dtype=torch.int32, device=dev)
+    kv.kv_select_topk(scores.view(L, Sl, H, Tl), i32_dev(np.full(Sl, Tl), dev), i32_dev(np.full(Sl, w.prompt_len[0]), dev),
+                      w.budget, w.recent, w.prompt_cap(), b_cap=b_cap, kept=kl, n_kept=nkl)
+    out.append(["select_stream_kernel<0>", n * 4, L * Sl * H * b_cap * 4])
+    torch.cuda.synchronize(dev)
+    return {"next_row_dispatches": out}
+
+
+def i32_dev(a, dev):
+    import numpy as np
+    import torch
+    return torch.as_tensor(np.asarray(a, np.int32), device=dev)
 
 
 def algorithmic_bytes(w, n_kept_per_head: int):
@@ -141,15 +197,18 @@ def main():
     torch.cuda.synchronize(dev)
     print("[bench] inputs resident", file=sys.stderr, flush=True)
 
-    if args.pmc_probe:
+    if args.pmc_probe or args.pmc_probe_next:
         # elementwise copy of known size (reads 4 GiB, writes 4 GiB) to scale HBM counters
         x = torch.ones(1 << 30, dtype=torch.float32, device=dev)
         y = torch.empty_like(x)
         torch.mul(x, 1.0, out=y)
+        del x, y
         kv.tri_score(K, qbd, tcur, seq, w.theta, w.deltas, out=scores)
         kv.kv_select_topk(scores, seq, plen, w.budget, w.recent, w.prompt_cap(), b_cap=b_cap, kept=kept, n_kept=nk)
         kv.kv_compact(K, V, kept, nk, seq, out_cap, K_out=Ko, V_out=Vo, pos_out=Po)
         torch.cuda.synchronize(dev)
+        if args.pmc_probe_next:
+            print(json.dumps(pmc_probe_next(w, K, qb, qbd, seq, plen, tcur, scores, kept, nk, b_cap, dev)), flush=True)
         print("[bench] pmc probe done", file=sys.stderr, flush=True)
         return
 
