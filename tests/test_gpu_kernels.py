@@ -654,6 +654,7 @@ UNION_CASES = [
     ("union-fits", 3000, [2048, 100], [100, 50], 2048, 128, 4, 0, "normal"),
     ("union-ragged-rows", 2999, [2999, 2500], [7, 0], 700, 9, 3, 0, "specials"),   # t_cap % 4 != 0
     ("union-20k-ragged-rows", 20001, [20001], [300], 2048, 64, 4, 0, "ties"),
+    ("union-g64", 4000, [4000, 2500], [100, 0], 1000, 32, 64, 0, "normal"),   # the largest group
     # past 65536 slots: the re-reading kernel with the union as a bit per slot in LDS
     ("union-stream-70k-g4", 70000, [70000, 65537], [1024, 0], 3072, 128, 4, 0, "normal"),
     ("union-stream-128k-g8-ties", 131072, [131072, 100000], [2048, 10], 4096, 128, 8, 0, "ties"),
