@@ -778,6 +778,69 @@ def test_pass_replays_from_a_hip_graph():
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), f"replay {rep}"
 
 
+def test_next_row_calls_replay_from_a_hip_graph():
+    # the next rows' calls capture too: grouped-query scores (caller workspace), union, random,
+    # recency and in-place compaction; each replay matches the eager calls on changed inputs
+    r = rng(572, 0)
+    L, S, H, T, d, G, B = 1, 2, 2, 3000, 64, 4, 800
+    Kf = [r.standard_normal((L, S, H, T, d)).astype(np.float32) for _ in range(3)]
+    K = _to_dev_keys(Kf[0], "bf16")
+    nu = torch.from_numpy(r.standard_normal((L, H, G, d)).astype(np.float32)).to(DEV)
+    Ts, Ps = _i32([T, 2100]), _i32([64, 0])
+    z = torch.empty((L, S, H, T), device=DEV)
+    hs = torch.empty((L, S, H, G, T), device=DEV)
+    ws = torch.empty((kv.gqa_workspace_bytes(L, S, H, T, d, K.dtype, G),), dtype=torch.uint8, device=DEV)
+    outs = {k: (torch.empty((L, S, H, B), dtype=torch.int32, device=DEV), torch.empty((S,), dtype=torch.int32, device=DEV))
+            for k in ("union", "random", "recent")}
+    Kc, Vc, Pc = K.clone(), K.clone(), torch.arange(T, dtype=torch.int32, device=DEV).expand(L, S, H, T).contiguous()
+    args = (1e4, [1, 2, 4, 8, 16])
+
+    def run():
+        kv.tri_score_gqa(K, nu, Ts, Ts, *args, out=z, head_out=hs, workspace=ws)
+        kv.kv_select_union(hs, z, Ts, Ps, B, 16, 64, kept=outs["union"][0], n_kept=outs["union"][1])
+        kv.kv_select_random((L, S, H, T), Ts, Ps, B, 16, 64, 5, 3, kept=outs["random"][0], n_kept=outs["random"][1])
+        kv.kv_select_recent((L, S, H, T), Ts, Ps, B, 16, 64, kept=outs["recent"][0], n_kept=outs["recent"][1])
+        kv.kv_compact_inplace(Kc, Vc, outs["union"][0], outs["union"][1], Ts, pos=Pc)
+
+    def reset(rep):
+        K.copy_(_to_dev_keys(Kf[rep], "bf16"))
+        Kc.copy_(K)
+        Vc.copy_(K.flip(-1))
+        Pc.copy_(torch.arange(T, dtype=torch.int32, device=DEV).expand(L, S, H, T))
+
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+
+    def written():
+        got = [z[:, 0].clone(), z[:, 1, :, :2100].clone(), hs[:, 0].clone(), hs[:, 1, :, :, :2100].clone()]
+        for k in ("union", "random", "recent"):
+            got += [outs[k][0].clone(), outs[k][1].clone()]
+        got += [Kc.clone(), Vc.clone(), Pc.clone()]
+        return got
+
+    for rep in range(3):
+        reset(rep)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = written()
+        reset(rep)
+        run()
+        torch.cuda.synchronize()
+        ref = written()
+        for i, (a, b) in enumerate(zip(got, ref)):
+            bits = (lambda x: x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32))
+            assert torch.equal(bits(a), bits(b)), f"replay {rep}, output {i}"
+
+
 def test_audit_accepts_every_selector_and_flags_broken_lists():
     L, S, H, t_cap = 2, 3, 2, 5000
     Ts, Ps, B, R = [5000, 1800, 4000], [100, 0, 3900], 2000, 64
