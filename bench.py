@@ -89,6 +89,11 @@ def pmc_probe_next(w, K, qb, qbd, seq, plen, tcur, scores, kept, nk, b_cap, dev)
     kv.kv_select_topk(scores.view(L, Sl, H, Tl), i32_dev(np.full(Sl, Tl), dev), i32_dev(np.full(Sl, w.prompt_len[0]), dev),
                       w.budget, w.recent, w.prompt_cap(), b_cap=b_cap, kept=kl, n_kept=nkl)
     out.append(["select_stream_kernel<0>", n * 4, L * Sl * H * b_cap * 4])
+    zmax, head = kv.tri_score_gqa_rotated(K.view(L, S * bps, bs, H, d), nu, tcur, seq, w.theta, w.deltas,
+                                          block_table=table)
+    out.append(["gqa_rotated_kernel<true, 16, false, 1, false, 4>", n * d * e + L * H * S * bps * 4, n * 4 * G])
+    out.append(["gqa_finish_kernel<4>", n * 4 * G, n * 4])
+    del zmax, head
     torch.cuda.synchronize(dev)
     return {"next_row_dispatches": out}
 
@@ -334,7 +339,9 @@ def main():
     # (G = 8, head_dim 64) with explicit positions
     from workloads import query_head_centres
 
-    def gqa_case(wg, Kg, seqg, tcurg, posg, keep=False):
+    def gqa_case(wg, Kg, seqg, tcurg, posg, keep=False, rotated=None):
+        """rotated: None for pre-RoPE keys (tri_score_gqa); else (label, key tensor, block table or None,
+        head-major) for the same keys read as stored after RoPE (tri_score_gqa_rotated)."""
         Lg, Sg, Hg, Tg, dg = Kg.shape
         G = wg.group
         # this cache's own query draws are one centre per KV head; the per-query-head centres
@@ -344,18 +351,33 @@ def main():
         outg = torch.empty((Lg, Sg, Hg, Tg), dtype=torch.float32, device=dev)
         head = torch.empty((Lg, Sg, Hg, G, Tg), dtype=torch.float32, device=dev)
         ws = torch.empty((kv.gqa_workspace_bytes(Lg, Sg, Hg, Tg, dg, Kg.dtype, G),), dtype=torch.uint8, device=dev)
-        ms = time_launches(lambda: kv.tri_score_gqa(Kg, nud, tcurg, seqg, wg.theta, wg.deltas, pos=posg, out=outg,
-                                                    head_out=head, workspace=ws))
+        if rotated is None:
+            ms = time_launches(lambda: kv.tri_score_gqa(Kg, nud, tcurg, seqg, wg.theta, wg.deltas, pos=posg,
+                                                        out=outg, head_out=head, workspace=ws))
+        else:
+            _, Kr, tab, hm = rotated
+            ms = time_launches(lambda: kv.tri_score_gqa_rotated(Kr, nud, tcurg, seqg, wg.theta, wg.deltas,
+                                                                block_table=tab, head_major=hm, out=outg,
+                                                                head_out=head, workspace=ws))
         n = int(np.sum(np.minimum(wg.seq_len, Tg))) * Lg * Hg
         # each key row read once; G fp32 scores per key written, read back for the z-score, one written
         byts = n * (dg * Kg.element_size() + 8 * G + 4) + (0 if posg is None else n * 4)
-        res = {"workload": wg.name, "group": G, "head_dim": dg, "positions": posg is not None, "ms_per_launch": ms,
+        if rotated is not None and rotated[2] is not None:
+            byts += rotated[2].numel() * 4 * Lg * Hg      # each (layer, head) reads its sequence's table
+        res = {"workload": wg.name, "group": G, "head_dim": dg, "positions": posg is not None,
+               "keys": "pre-rope" if rotated is None else rotated[0], "ms_per_launch": ms,
                "entries_per_s": n / (ms * 1e-3), "algorithmic_bytes": byts, "gbs": byts / (ms * 1e-3) / 1e9}
         del ws
         return (res, outg, head) if keep else res
 
     g3, zmax, head3 = gqa_case(w, K, seq, tcur, None, keep=True)
     gqa = [g3]
+    # the same scores over keys stored after RoPE: dense, and the two paged pools above
+    gqa_rot = [gqa_case(w, K, seq, tcur, None, rotated=r) for r in
+               (("rotated dense", K, None, False), ("rotated paged16", pool, table, False),
+                ("rotated paged16 head-major", pool_hm, table, True))]
+    print(f"[bench] grouped-query scores over rotated keys: "
+          f"{[(g['keys'], round(g['ms_per_launch'], 3)) for g in gqa_rot]}", file=sys.stderr, flush=True)
     # union-based selection over the 4 query heads on those scores (per-head top-k, k = ceil(n_sel/4))
     union_ms = time_launches(lambda: kv.kv_select_union(head3, zmax, seq, plen, w.budget, w.recent, w.prompt_cap(),
                                                         b_cap=b_cap, kept=kept, n_kept=nk))
@@ -486,6 +508,7 @@ def main():
                                "paged16_head_major_ms": paged_hm_ms,
                                "paged16_head_major_gbs": ab["score"] / (paged_hm_ms * 1e-3) / 1e9},
         "score_gqa": gqa,
+        "score_gqa_rotated_keys": gqa_rot,
         "select_union": {"group": w.group, "ms_per_launch": union_ms, "algorithmic_bytes": union_bytes,
                          "gbs": union_bytes / (union_ms * 1e-3) / 1e9},
         "select_recent": {"ms_per_launch": recent_ms},

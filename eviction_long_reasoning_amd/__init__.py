@@ -7,6 +7,7 @@ package is a thin torch-tensor binding over it.
   tri_score         offset-averaged RoPE query-centre score of every key
   tri_score_rotated the same for keys stored after RoPE, dense or paged
   tri_score_gqa     per-query-head scores of a GQA group, z-normalised, max over the group
+  tri_score_gqa_rotated  the same for keys stored after RoPE, dense or paged
   kv_select_topk    keep prompt + recent window + top-scoring keys per head
   kv_select_random  keep prompt + recent window + per-head uniform random keys
   kv_compact        gather kept K/V rows and positions contiguously
@@ -24,8 +25,9 @@ the built library every call raises.
 """
 from ._lib import KvError, library_path, load as load_library
 from .binding import (gqa_workspace_bytes, kv_audit_kept, kv_compact, kv_compact_inplace, kv_select_random, kv_select_random_shared,
-                      kv_select_recent, kv_select_union, kv_select_topk, tri_score, tri_score_gqa, tri_score_rotated)
+                      kv_select_recent, kv_select_union, kv_select_topk, tri_score, tri_score_gqa,
+                      tri_score_gqa_rotated, tri_score_rotated)
 
-__all__ = ["tri_score", "tri_score_rotated", "tri_score_gqa", "gqa_workspace_bytes", "kv_select_topk", "kv_select_random", "kv_compact",
+__all__ = ["tri_score", "tri_score_rotated", "tri_score_gqa", "tri_score_gqa_rotated", "gqa_workspace_bytes", "kv_select_topk", "kv_select_random", "kv_compact",
            "kv_select_union", "kv_select_random_shared", "kv_select_recent", "kv_compact_inplace", "kv_audit_kept", "KvError", "library_path",
            "load_library"]

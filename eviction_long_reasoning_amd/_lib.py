@@ -59,6 +59,8 @@ _SIGNATURES = {
     "tri_score_gqa": (_I32, [ctypes.POINTER(KvShape), _P, _P, _I32, _P, _P, _P, ctypes.c_double,
                              ctypes.POINTER(_I32), _I32, _P, _P, _P, ctypes.c_size_t, _P]),
     "kv_score_gqa_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(KvShape), _I32]),
+    "tri_score_gqa_rotated": (_I32, [ctypes.POINTER(KvShape), _P, ctypes.POINTER(KvPaged), _I32, _I32, _P, _P, _P,
+                                     ctypes.c_double, ctypes.POINTER(_I32), _I32, _P, _P, _P, ctypes.c_size_t, _P]),
     "kv_select_topk": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, _P, _I32, _P, _P]),
     "kv_select_random": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, ctypes.c_uint64,
                                 ctypes.c_uint32, _P, _I32, _P, _P]),

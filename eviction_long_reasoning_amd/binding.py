@@ -170,6 +170,60 @@ def tri_score_gqa(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_
     return out, head_out
 
 
+def tri_score_gqa_rotated(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len: torch.Tensor,
+                          rope_theta: float, deltas: Sequence[int], rope_style: str = "interleaved",
+                          block_table: Optional[torch.Tensor] = None, head_major: bool = False,
+                          qabs: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                          head_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+                          ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Grouped-query scores of keys stored after RoPE: (max over the group of the z-normalised
+    per-query-head scores [L,S,H,t_cap], the per-query-head scores [L,S,H,G,t_cap]).
+
+    ``K`` and ``block_table`` as for ``tri_score_rotated``; ``qbar`` is [L,H,G,d] fp32 and ``qabs``
+    optionally [L,H,G,d/2], both in the stored keys' pairing.
+    """
+    if K.dim() != 5 or K.dtype not in _DT:
+        raise ValueError("K must be a 5-D float32/bfloat16 tensor")
+    if qbar.dim() != 4:
+        raise ValueError("qbar must be [L,H,G,d]")
+    style = {"interleaved": _lib.KV_ROPE_INTERLEAVED, "half": _lib.KV_ROPE_HALF}[rope_style]
+    dev = K.device
+    paged = None
+    if block_table is None:
+        L, S, H, t_cap, d = K.shape
+    else:
+        if head_major:
+            L, n_blocks, H, bs, d = K.shape
+        else:
+            L, n_blocks, bs, H, d = K.shape
+        S, bps = block_table.shape
+        t_cap = bps * bs
+        paged = _lib.KvPaged(_dev_ptr(block_table, "block_table", torch.int32, (S, bps), dev), int(bps), int(bs),
+                             int(n_blocks), int(bool(head_major)))
+    G = qbar.shape[2]
+    kp = _dev_ptr(K, "K")
+    qp = _dev_ptr(qbar, "qbar", torch.float32, (L, H, G, d), dev)
+    ap = _dev_ptr(qabs, "qabs", torch.float32, (L, H, G, d // 2), dev)
+    tp = _dev_ptr(t_cur, "t_cur", torch.int32, (S,), dev)
+    sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
+    if out is None:
+        out = torch.empty((L, S, H, t_cap), dtype=torch.float32, device=dev)
+    if head_out is None:
+        head_out = torch.empty((L, S, H, G, t_cap), dtype=torch.float32, device=dev)
+    op = _dev_ptr(out, "out", torch.float32, (L, S, H, t_cap), dev)
+    hp = _dev_ptr(head_out, "head_out", torch.float32, (L, S, H, G, t_cap), dev)
+    shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
+    need = int(_lib.load().kv_score_gqa_workspace_bytes(ctypes.byref(shape), int(G)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 8),), dtype=torch.uint8, device=dev)
+    wp = _dev_ptr(workspace, "workspace", torch.uint8, None, dev)
+    dl = [int(x) for x in deltas]
+    arr = (ctypes.c_int32 * max(1, len(dl)))(*dl)
+    _invoke("tri_score_gqa_rotated", dev, ctypes.byref(shape), kp, None if paged is None else ctypes.byref(paged),
+            style, int(G), qp, ap, tp, float(rope_theta), arr, len(dl), hp, op, wp, workspace.numel())
+    return out, head_out
+
+
 def gqa_workspace_bytes(L: int, S: int, H: int, t_cap: int, d: int, dtype: torch.dtype, group: int) -> int:
     """Workspace bytes ``tri_score_gqa`` needs (0 for a shape or group it rejects)."""
     shape = _shape(L, S, H, d, t_cap, _DT[dtype], None)

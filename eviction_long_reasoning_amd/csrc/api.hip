@@ -260,6 +260,77 @@ KV_EXPORT kv_status tri_score_gqa(const kv_shape *shape, const void *K, const in
 }
 
 // max_slots: the largest t_cap the selector kernel behind the entry point takes.
+KV_EXPORT kv_status tri_score_gqa_rotated(const kv_shape *shape, const void *K, const kv_paged *paged,
+                                          int32_t rope_style, int32_t group, const float *qbar, const float *qabs,
+                                          const int32_t *t_cur, double rope_theta, const int32_t *deltas,
+                                          int32_t n_delta, float *head_scores, float *scores, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+  kv_status st = check_shape(shape, true);
+  if (st != KV_OK) return st;
+  if (!K || !qbar || !t_cur || !deltas || !scores || !head_scores || !workspace) return KV_EINVAL;
+  if (group < 1 || group > kGqaRotatedMaxGroup) return KV_EINVAL;
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta)) return KV_EINVAL;
+  if (n_delta < 1 || n_delta > kMaxDeltas) return KV_EINVAL;
+  if (rope_style != KV_ROPE_INTERLEAVED && rope_style != KV_ROPE_HALF) return KV_EINVAL;
+  if (!aligned16(K) || (reinterpret_cast<uintptr_t>(qbar) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
+    return KV_EINVAL;
+  if (!words({qabs, t_cur, head_scores, scores, shape->seq_len, paged ? paged->block_table : nullptr}))
+    return KV_EINVAL;
+  if (workspace_bytes < gqa_workspace(shape, group)) return KV_ESHAPE;
+  const size_t heads = static_cast<size_t>(shape->n_layers) * shape->n_seq * shape->n_kv_heads;
+  const size_t score_bytes = heads * shape->t_cap * sizeof(float);
+  if (overlaps(head_scores, score_bytes * group, scores, score_bytes) ||
+      overlaps(workspace, workspace_bytes, scores, score_bytes) ||
+      overlaps(workspace, workspace_bytes, head_scores, score_bytes * group))
+    return KV_EINVAL;
+
+  GqaParams p{};
+  p.K = K;
+  p.qbar = qbar;
+  p.qabs = qabs;
+  p.t_cur = t_cur;
+  p.seq_len = shape->seq_len;
+  p.raw = head_scores;
+  p.partials = static_cast<double *>(workspace);
+  p.scores = scores;
+  p.L = shape->n_layers;
+  p.S = shape->n_seq;
+  p.H = shape->n_kv_heads;
+  p.d = shape->head_dim;
+  p.F = shape->head_dim / 2;
+  p.t_cap = shape->t_cap;
+  p.G = group;
+  p.chunks_per_head = (shape->t_cap + kGqaChunk - 1) / kGqaChunk;
+  p.half = rope_style == KV_ROPE_HALF;
+  int layout = 0;
+  if (paged) {
+    if (paged->head_major != 0 && paged->head_major != 1) return KV_EINVAL;
+    if (!paged->block_table || paged->blocks_per_seq < 1 || paged->n_blocks < 1 || paged->block_size < 1 ||
+        (paged->block_size & (paged->block_size - 1)))
+      return KV_EINVAL;
+    if (static_cast<long long>(paged->blocks_per_seq) * paged->block_size < shape->t_cap) return KV_ESHAPE;
+    p.block_table = paged->block_table;
+    p.blocks_per_seq = paged->blocks_per_seq;
+    p.n_blocks = paged->n_blocks;
+    int shift = 0;
+    while ((1 << shift) < paged->block_size) ++shift;
+    p.block_shift = shift;
+    layout = paged->head_major ? 2 : 1;
+  }
+  fold_coefficients(p.d, rope_theta, deltas, n_delta, p.A, p.rev);
+  const int pieces = p.d * elem_bytes(shape) / 16;  // 16-byte lane pieces per row
+  int lpk = 1;
+  while (lpk < pieces) lpk <<= 1;
+  if (lpk > 16) return KV_ESHAPE;                     // one piece per lane, at most 16 lanes per key
+  if (p.half && (lpk != pieces || lpk < 2)) return KV_ESHAPE;
+  // one head's per-query-head scores are addressed with 32-bit offsets
+  if (static_cast<long long>(group) * shape->t_cap * 4 >= (1ll << 31)) return KV_ESHAPE;
+  const long long threads = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head * kScoreThreads;
+  if (threads >= (1ll << 32)) return KV_ESHAPE;
+  return hip_status(launch_score_gqa_rotated(p, shape->dtype == KV_BF16, layout, lpk,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 static kv_status select_common(const kv_shape *shape, const kv_policy *policy, int32_t *kept, int32_t b_cap,
                                int32_t *n_kept, SelectParams &p, int max_slots = kSelectMaxSlotsStream) {
   kv_status st = check_shape(shape, false);

@@ -43,6 +43,10 @@ struct GqaParams {
   float2 A[kMaxBands];
   double rev[kMaxBands];
   float2 W[kMaxBands];      // exp(-i omega_f kGqaTile): the phase step from one key tile to the next
+  // keys stored after RoPE (tri_score_gqa_rotated): pairing and, for a paged pool, the block table
+  int32_t half;                // 1: half-split pairing (x[f], x[f+d/2]); 0: interleaved
+  const int32_t *block_table;  // [S, blocks_per_seq] or nullptr (dense)
+  int32_t blocks_per_seq, block_shift, n_blocks;
 };
 
 constexpr int kGqaTile = 16;                                   // keys per MFMA tile
@@ -50,6 +54,10 @@ constexpr int kGqaTilesPerWave = 16;
 constexpr int kGqaChunk = (kScoreThreads / 64) * kGqaTilesPerWave * kGqaTile;
 
 hipError_t launch_score_gqa(const GqaParams &p, int dtype_bf16, int pieces_per_lane, hipStream_t st);
+constexpr int kGqaRotatedMaxGroup = 8;
+// layout: 0 dense, 1 token-major paged pool, 2 head-major paged pool
+hipError_t launch_score_gqa_rotated(const GqaParams &p, int dtype_bf16, int layout, int lanes_per_key,
+                                    hipStream_t st);
 
 // --------------------------------------------------------------- select ----
 struct SelectParams {

@@ -27,6 +27,8 @@
 // Kernel A writes the G raw scores and, per (head, chunk of keys), fp64 sums of s and s^2 for
 // each g. Kernel B reduces a head's chunk sums in a fixed order (deterministic, no atomics) and
 // writes max_g (s_g - mu_g) / sigma_g (0 for a query head whose scores do not vary).
+#include <type_traits>
+
 #include "kv_internal.hpp"
 
 namespace kvevict {
@@ -539,6 +541,178 @@ __global__ __launch_bounds__(kScoreThreads) void gqa_stream_kernel(const GqaPara
   }
 }
 
+// Grouped-query scores of keys stored after RoPE, dense or paged (the serving layout). With
+// k_rot = RoPE(k, p) a key's own rotation cancels, and query head g's score is one dot product with
+// W_{g,f} = q_bar_{g,f} A_f exp(i omega_f t), written out per stored coordinate (the real part of
+// W where band f's real part is stored, the imaginary part where its imaginary part is), for the
+// interleaved or the half-split pairing. Lane layout (one 16-byte piece per lane, LPK lanes per
+// key), the block-table addressing and the reduce-scatter follow the single-centre rotated
+// kernel, with G accumulators per key; the raw scores and chunk sums have kernel A's layout, so
+// kernel B is shared.
+template <typename T>
+__device__ __forceinline__ float coord(const uint4 &d, int e) {
+  const uint32_t wd[4] = {d.x, d.y, d.z, d.w};
+  if constexpr (sizeof(T) == 2) return __uint_as_float((e & 1) ? (wd[e >> 1] & 0xffff0000u) : (wd[e >> 1] << 16));
+  else return __uint_as_float(wd[e]);
+}
+
+template <bool BF16, int LPK, bool HALF, int LAYOUT, bool NORM, int GM>
+__global__ __launch_bounds__(kScoreThreads) void gqa_rotated_kernel(const GqaParams p) {
+  constexpr bool PAGED = LAYOUT != 0;
+  constexpr int EPL = BF16 ? 8 : 4;               // coordinates per lane (one 16-byte piece)
+  constexpr int KPS = 64 / LPK;
+  constexpr int STEPS = LPK;
+  constexpr int NW = kScoreThreads / 64;
+  constexpr int NB = kGqaChunk / NW / 64;         // 64-key batches per wave
+  constexpr int EB = BF16 ? 2 : 4;
+  using Elem = typename std::conditional<BF16, uint16_t, float>::type;
+  __shared__ double part[NW][GM][2];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane % LPK;
+  const int kk = lane / LPK;
+  const int head = blockIdx.x / p.chunks_per_head;
+  const int chunk = blockIdx.x - head * p.chunks_per_head;
+  const int h = head % p.H;
+  const int s = (head / p.H) % p.S;
+  const int l = head / (p.H * p.S);
+  const int G = p.G;
+  const int F = p.F;
+
+  const int T = min(max(p.seq_len[s], 0), p.t_cap);
+  const int wave_first = chunk * kGqaChunk + wave * (NB * 64);
+  const double tq = static_cast<double>(p.t_cur[s]);
+  const bool live = g * EPL < p.d;
+  const size_t lhg = (static_cast<size_t>(l) * p.H + h) * G;
+
+  // per query head, the weight of each coordinate of this lane's piece (and the norm weight of the
+  // band whose real part the coordinate holds)
+  float wgt[GM][EPL], cn[GM][EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int x = g * EPL + e;
+    const int f = HALF ? (x < F ? x : x - F) : (x >> 1);
+    const bool is_re = HALF ? (x < F) : ((x & 1) == 0);
+    float2 ph = make_float2(0.f, 0.f);
+    if (live && x < p.d) ph = cmul(p.A[f], cis_rev(p.rev[f], tq));
+#pragma unroll
+    for (int q = 0; q < GM; ++q) {
+      wgt[q][e] = cn[q][e] = 0.f;
+      if (live && x < p.d && q < G) {
+        const float *qg = p.qbar + (lhg + q) * p.d;
+        const float2 qf = HALF ? make_float2(qg[f], qg[f + F]) : make_float2(qg[2 * f], qg[2 * f + 1]);
+        const float2 W = cmul(qf, ph);
+        wgt[q][e] = is_re ? W.x : W.y;
+        if (NORM && is_re) {
+          const float qa = p.qabs[(lhg + q) * F + f];
+          cn[q][e] = qa > 0.f ? qa - __builtin_amdgcn_sqrtf(fmaf(qf.x, qf.x, qf.y * qf.y)) : 0.f;
+        }
+      }
+    }
+  }
+
+  const size_t row_bytes = static_cast<size_t>(p.d) * EB;
+  const char *Kb = static_cast<const char *>(p.K);
+  const size_t dense0 = static_cast<size_t>(head) * p.t_cap;
+  const int32_t *table = PAGED ? p.block_table + static_cast<size_t>(s) * p.blocks_per_seq : nullptr;
+  const int bmask = (1 << p.block_shift) - 1;
+  auto row_ptr = [&](int j) -> const char * {
+    size_t row;
+    if (PAGED) {
+      const int pb = min(max(table[j >> p.block_shift], 0), p.n_blocks - 1);   // never leave the pool
+      const size_t blk = static_cast<size_t>(l) * p.n_blocks + pb;
+      row = LAYOUT == 2 ? (blk * p.H + h) * (bmask + 1) + (j & bmask) : (blk * (bmask + 1) + (j & bmask)) * p.H + h;
+    } else {
+      row = dense0 + j;
+    }
+    return Kb + row * row_bytes + static_cast<size_t>(live ? g : 0) * 16;
+  };
+
+  double sum[GM], sum2[GM];
+#pragma unroll
+  for (int q = 0; q < GM; ++q) sum[q] = sum2[q] = 0.0;
+  float *raw_head = p.raw + static_cast<size_t>(head) * G * p.t_cap;
+
+#pragma unroll 1
+  for (int nb = 0; nb < NB; ++nb) {
+    const int j0 = wave_first + nb * 64;
+    if (j0 >= T) break;
+    uint4 data[STEPS];
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      const int j = j0 + t * KPS + kk;
+      const v4u32 v = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(row_ptr(j < T ? j : 0)));
+      data[t] = make_uint4(v[0], v[1], v[2], v[3]);   // slots past T read row 0; not stored
+    }
+    float acc[GM][STEPS];
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      float a[GM];
+#pragma unroll
+      for (int q = 0; q < GM; ++q) a[q] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float x = coord<Elem>(data[t], e);
+#pragma unroll
+        for (int q = 0; q < GM; ++q) a[q] = fmaf(wgt[q][e], x, a[q]);
+        if (NORM) {
+          float ka;
+          if (HALF) {
+            // band f's two coordinates sit in lanes g and g ^ LPK/2; the lower lane adds the term
+            const float other = __shfl_xor(x, LPK / 2, 64);
+            ka = __builtin_amdgcn_sqrtf(fmaf(x, x, other * other));
+          } else {
+            const float y = coord<Elem>(data[t], e ^ 1);
+            ka = __builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
+          }
+#pragma unroll
+          for (int q = 0; q < GM; ++q) a[q] = fmaf(cn[q][e], ka, a[q]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < GM; ++q) acc[q][t] = live ? a[q] : 0.f;
+    }
+    const int jj = j0 + g * KPS + kk;
+#pragma unroll
+    for (int q = 0; q < GM; ++q) {
+      const float sc = reduce_scatter<STEPS>(acc[q], g);
+      if (jj < T && q < G) {
+        __builtin_nontemporal_store(sc, raw_head + static_cast<size_t>(q) * p.t_cap + jj);
+        sum[q] += static_cast<double>(sc);
+        sum2[q] += static_cast<double>(sc) * static_cast<double>(sc);
+      }
+    }
+  }
+
+  // per (head, chunk) sums for each query head, in a fixed reduction order
+#pragma unroll
+  for (int q = 0; q < GM; ++q) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      sum[q] += __shfl_xor(sum[q], off, 64);
+      sum2[q] += __shfl_xor(sum2[q], off, 64);
+    }
+    if (lane == 0) {
+      part[wave][q][0] = sum[q];
+      part[wave][q][1] = sum2[q];
+    }
+  }
+  __syncthreads();
+  if (static_cast<int>(threadIdx.x) < G) {
+    const int q = threadIdx.x;
+    double a = 0.0, b = 0.0;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) {
+      a += part[wv][q][0];
+      b += part[wv][q][1];
+    }
+    double *dst = p.partials + ((static_cast<size_t>(head) * p.chunks_per_head + chunk) * G + q) * 2;
+    dst[0] = a;
+    dst[1] = b;
+  }
+}
+
 int group_bound(int G) {
   int gm = 1;
   while (gm < G) gm <<= 1;
@@ -589,6 +763,69 @@ hipError_t launch_full(const GqaParams &p, int ppq, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
+// Kernel B over the raw scores and chunk sums kernel A wrote.
+hipError_t launch_finish(const GqaParams &p, dim3 grid, hipStream_t st) {
+  const dim3 blk(kScoreThreads);
+  switch (group_bound(p.G)) {
+    case 1: hipLaunchKernelGGL(gqa_finish_kernel<1>, grid, blk, 0, st, p); break;
+    case 2: hipLaunchKernelGGL(gqa_finish_kernel<2>, grid, blk, 0, st, p); break;
+    case 4: hipLaunchKernelGGL(gqa_finish_kernel<4>, grid, blk, 0, st, p); break;
+    case 8: hipLaunchKernelGGL(gqa_finish_kernel<8>, grid, blk, 0, st, p); break;
+    case 16: hipLaunchKernelGGL(gqa_finish_kernel<16>, grid, blk, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <bool BF16, bool HALF, int LAYOUT, bool NORM, int GM>
+hipError_t launch_gqa_rot_lpk(const GqaParams &p, int lpk, dim3 grid, hipStream_t st) {
+  const dim3 blk(kScoreThreads);
+  switch (lpk) {
+    case 1: hipLaunchKernelGGL((gqa_rotated_kernel<BF16, 1, HALF, LAYOUT, NORM, GM>), grid, blk, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((gqa_rotated_kernel<BF16, 2, HALF, LAYOUT, NORM, GM>), grid, blk, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((gqa_rotated_kernel<BF16, 4, HALF, LAYOUT, NORM, GM>), grid, blk, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((gqa_rotated_kernel<BF16, 8, HALF, LAYOUT, NORM, GM>), grid, blk, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((gqa_rotated_kernel<BF16, 16, HALF, LAYOUT, NORM, GM>), grid, blk, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <bool BF16, bool HALF, int LAYOUT, bool NORM>
+hipError_t launch_gqa_rot_group(const GqaParams &p, int lpk, dim3 grid, hipStream_t st) {
+  switch (group_bound(p.G)) {
+    case 1: return launch_gqa_rot_lpk<BF16, HALF, LAYOUT, NORM, 1>(p, lpk, grid, st);
+    case 2: return launch_gqa_rot_lpk<BF16, HALF, LAYOUT, NORM, 2>(p, lpk, grid, st);
+    case 4: return launch_gqa_rot_lpk<BF16, HALF, LAYOUT, NORM, 4>(p, lpk, grid, st);
+    case 8: return launch_gqa_rot_lpk<BF16, HALF, LAYOUT, NORM, 8>(p, lpk, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool BF16, bool HALF, int LAYOUT>
+hipError_t launch_gqa_rot_norm(const GqaParams &p, int lpk, dim3 grid, hipStream_t st) {
+  return p.qabs ? launch_gqa_rot_group<BF16, HALF, LAYOUT, true>(p, lpk, grid, st)
+                : launch_gqa_rot_group<BF16, HALF, LAYOUT, false>(p, lpk, grid, st);
+}
+
+template <bool BF16>
+hipError_t launch_gqa_rot_layout(const GqaParams &p, int layout, int lpk, dim3 grid, hipStream_t st) {
+  if (p.half) {
+    switch (layout) {
+      case 0: return launch_gqa_rot_norm<BF16, true, 0>(p, lpk, grid, st);
+      case 1: return launch_gqa_rot_norm<BF16, true, 1>(p, lpk, grid, st);
+      case 2: return launch_gqa_rot_norm<BF16, true, 2>(p, lpk, grid, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (layout) {
+    case 0: return launch_gqa_rot_norm<BF16, false, 0>(p, lpk, grid, st);
+    case 1: return launch_gqa_rot_norm<BF16, false, 1>(p, lpk, grid, st);
+    case 2: return launch_gqa_rot_norm<BF16, false, 2>(p, lpk, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_score_gqa(const GqaParams &p, int dtype_bf16, int pieces_per_lane, hipStream_t st) {
   const long long blocks = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head;
   if (blocks <= 0) return hipSuccess;
@@ -610,16 +847,18 @@ hipError_t launch_score_gqa(const GqaParams &p, int dtype_bf16, int pieces_per_l
     e = pos ? (norm ? launch_full<false, true, true>(p, ppq, grid, st) : launch_full<false, true, false>(p, ppq, grid, st))
             : (norm ? launch_full<false, false, true>(p, ppq, grid, st) : launch_full<false, false, false>(p, ppq, grid, st));
   if (e != hipSuccess) return e;
-  const dim3 blk(kScoreThreads);
-  switch (group_bound(p.G)) {
-    case 1: hipLaunchKernelGGL(gqa_finish_kernel<1>, grid, blk, 0, st, p); break;
-    case 2: hipLaunchKernelGGL(gqa_finish_kernel<2>, grid, blk, 0, st, p); break;
-    case 4: hipLaunchKernelGGL(gqa_finish_kernel<4>, grid, blk, 0, st, p); break;
-    case 8: hipLaunchKernelGGL(gqa_finish_kernel<8>, grid, blk, 0, st, p); break;
-    case 16: hipLaunchKernelGGL(gqa_finish_kernel<16>, grid, blk, 0, st, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return launch_finish(p, grid, st);
+}
+
+hipError_t launch_score_gqa_rotated(const GqaParams &p, int dtype_bf16, int layout, int lanes_per_key,
+                                    hipStream_t st) {
+  const long long blocks = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head;
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  const hipError_t e = dtype_bf16 ? launch_gqa_rot_layout<true>(p, layout, lanes_per_key, grid, st)
+                                  : launch_gqa_rot_layout<false>(p, layout, lanes_per_key, grid, st);
+  if (e != hipSuccess) return e;
+  return launch_finish(p, grid, st);
 }
 
 }  // namespace kvevict

@@ -7,6 +7,7 @@
  *   tri_score        score every cached key from the query centre
  *   tri_score_rotated  the same for keys stored after RoPE (dense or paged)
  *   tri_score_gqa    per-query-head scores of a GQA group, z-normalised, max over the group
+ *   tri_score_gqa_rotated  the same for keys stored after RoPE (dense or paged)
  *   kv_select_topk   keep prompt + recent window + top-scoring keys per head
  *   kv_select_random keep prompt + recent window + uniformly random keys
  *   kv_compact       gather the kept K/V rows (and positions) contiguously
@@ -235,8 +236,30 @@ kv_status tri_score_gqa(const kv_shape *shape, const void *K, const int32_t *pos
                         size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace tri_score_gqa needs for this shape and group (0 for sizes or a group it
- * rejects). shape->seq_len is not read and may be NULL. */
+ * rejects). shape->seq_len is not read and may be NULL. tri_score_gqa_rotated needs the same. */
 size_t kv_score_gqa_workspace_bytes(const kv_shape *shape, int32_t group);
+
+/*
+ * tri_score_gqa_rotated -- the grouped-query rule (as tri_score_gqa) for keys
+ * stored after RoPE, dense or through a paged block table, as a serving
+ * engine keeps them ([TA-blog] implementation excerpt: the scorer works on
+ * the rotated keys). Query head g's score of key j is tri_score_rotated's
+ * score with qbar[l,h,g] (and qabs[l,h,g]); normalisation and the maximum as
+ * for tri_score_gqa.
+ *
+ *  K, paged, rope_style  as for tri_score_rotated; qbar and qabs are in the
+ *               same pairing as the stored keys.
+ *  group        G, 1 <= G <= 8.
+ *  head_dim     at most 128 (bf16) or 64 (fp32): one 16-byte piece per lane,
+ *               at most 16 lanes per key.
+ *  qbar, qabs, head_scores, scores, workspace  as for tri_score_gqa.
+ */
+kv_status tri_score_gqa_rotated(const kv_shape *shape, const void *K, const kv_paged *paged,
+                                int32_t rope_style, int32_t group, const float *qbar,
+                                const float *qabs, const int32_t *t_cur, double rope_theta,
+                                const int32_t *deltas, int32_t n_delta, float *head_scores,
+                                float *scores, void *workspace, size_t workspace_bytes,
+                                void *stream);
 
 /*
  * kv_select_topk -- exact per-head top-n_sel of the evictable range.

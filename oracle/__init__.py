@@ -17,6 +17,8 @@ from the pages' definitions:
   * ``score_gqa`` -- per-query-head scores, z-normalised per query head over
     the cached keys, maximum over the query heads of a KV head (summary 3.4,
     GQA handling).
+  * ``score_gqa_rotated`` -- the same grouped-query rule over keys stored
+    after RoPE.
   * ``score_rotated`` -- the same score for keys stored after RoPE
     (interleaved or half-split pairing), as serving engines keep them.
   * ``partition`` / ``select_topk`` -- prompt and recent-window pinning and
@@ -45,7 +47,8 @@ invariants, brute force and an independent library Philox; none is marked
 "parity unpinned".
 """
 from .rope import band_frequencies, band_slices, rope_rotate
-from .score import score_literal, score_series, score_folded, fold_coefficients, norm_term, score_full, score_rotated, score_gqa, zscore
+from .score import (score_literal, score_series, score_folded, fold_coefficients, norm_term, score_full, score_rotated,
+                    score_gqa, score_gqa_rotated, zscore)
 from .policy import (Partition, partition, canonical_scores, select_topk, select_random, random_uniforms,
                      select_recent, select_random_shared, select_union)
 from .philox import philox4x32_10, philox4x32_10_np, PHILOX_M, PHILOX_W
@@ -53,7 +56,7 @@ from .compact import compact, compact_holes
 
 __all__ = [
     "band_frequencies", "band_slices", "rope_rotate",
-    "score_literal", "score_series", "score_folded", "fold_coefficients", "norm_term", "score_full", "score_rotated", "score_gqa", "zscore",
+    "score_literal", "score_series", "score_folded", "fold_coefficients", "norm_term", "score_full", "score_rotated", "score_gqa", "score_gqa_rotated", "zscore",
     "Partition", "partition", "canonical_scores", "select_topk", "select_random", "random_uniforms",
     "select_recent", "select_random_shared", "select_union",
     "philox4x32_10", "philox4x32_10_np", "PHILOX_M", "PHILOX_W",

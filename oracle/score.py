@@ -182,3 +182,17 @@ def score_gqa(K, pos, qbar_g, t: int, theta: float, deltas: Sequence[int], qabs_
     per = np.stack(per)
     z = np.stack([zscore(row) for row in per])
     return z.max(axis=0), per
+
+
+def score_gqa_rotated(K_rot, qbar_g, t: int, theta: float, deltas: Sequence[int], style: str = "interleaved",
+                      qabs_g=None):
+    """The grouped-query rule (``score_gqa``) for keys stored after RoPE: each query head scores the
+    rotated keys with ``score_rotated`` (same pairing for keys and centres), z per head, max.
+
+    Returns (final (T,), per_head (G, T)).
+    """
+    qg = np.asarray(qbar_g, dtype=np.float64)
+    per = np.stack([score_rotated(K_rot, qg[g], t, theta, deltas, style,
+                                  None if qabs_g is None else np.asarray(qabs_g)[g]) for g in range(qg.shape[0])])
+    z = np.stack([zscore(row) for row in per])
+    return z.max(axis=0), per

@@ -63,6 +63,18 @@ int main() {
   EXPECT(tri_score_gqa(&sh, dummy, nullptr, 4, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, sc, ws, need - 8, nullptr), KV_ESHAPE);
   EXPECT(tri_score_gqa(&sh, dummy, nullptr, 4, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, hs, ws, need, nullptr), KV_EINVAL);
 
+  // grouped-query scores of rotated keys: group beyond 8, head_dim beyond one piece per lane,
+  // half-split rows that do not fill whole lanes, unknown pool layout
+  EXPECT(tri_score_gqa_rotated(&sh, dummy, nullptr, 0, 9, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, sc, ws, need, nullptr), KV_EINVAL);
+  kv_shape sh256 = sh;
+  sh256.head_dim = 256;
+  EXPECT(tri_score_gqa_rotated(&sh256, dummy, nullptr, 0, 4, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, sc, ws, 1 << 20, nullptr), KV_ESHAPE);
+  kv_shape sh96 = sh;
+  sh96.head_dim = 96;
+  EXPECT(tri_score_gqa_rotated(&sh96, dummy, nullptr, 1, 4, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, sc, ws, need, nullptr), KV_ESHAPE);
+  kv_paged pg3{seq, 256, 16, 8, 3};
+  EXPECT(tri_score_gqa_rotated(&sh, dummy, &pg3, 0, 4, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, sc, ws, need, nullptr), KV_EINVAL);
+
   // selectors: b_cap below the budget, t_cap past every selector (2^26) or past the union's
   // limit (2^18), budget < 1, union without head scores
   int32_t *kept = reinterpret_cast<int32_t *>(0x3000), *nk = reinterpret_cast<int32_t *>(0x4000);

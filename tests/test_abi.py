@@ -153,6 +153,31 @@ def test_host_validation_rejects_bad_arguments(lib):
                           ctypes.c_void_p(0x300000), None, 8, None) == L.KV_EINVAL
 
 
+def test_gqa_rotated_validation(lib):
+    from eviction_long_reasoning_amd import _lib as L
+    ok = ctypes.c_void_p(0x1000)
+    arr = (ctypes.c_int32 * 1)(1)
+    hs, sc, ws = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x900000), ctypes.c_void_p(0xA00000)
+    sh = L.KvShape(1, 1, 1, 128, 4096, L.KV_BF16, ok)
+    need = lib.kv_score_gqa_workspace_bytes(ctypes.byref(sh), 4)
+
+    def call(shape, paged=None, style=0, group=4, workspace_bytes=None, qbar=ok):
+        return lib.tri_score_gqa_rotated(ctypes.byref(shape), ok, None if paged is None else ctypes.byref(paged), style,
+                                         group, qbar, None, ok, 1e4, arr, 1, hs, sc, ws,
+                                         need if workspace_bytes is None else workspace_bytes, None)
+    assert call(sh, group=9) == L.KV_EINVAL                     # groups of at most 8
+    assert call(sh, group=0) == L.KV_EINVAL
+    assert call(sh, style=5) == L.KV_EINVAL
+    assert call(sh, workspace_bytes=need - 8) == L.KV_ESHAPE
+    assert call(sh, qbar=ctypes.c_void_p(0x1002)) == L.KV_EINVAL
+    sh256 = L.KvShape(1, 1, 1, 256, 4096, L.KV_BF16, ok)       # 32 pieces: more than 16 lanes per key
+    assert call(sh256, workspace_bytes=1 << 20) == L.KV_ESHAPE
+    sh96 = L.KvShape(1, 1, 1, 96, 4096, L.KV_BF16, ok)         # half-split rows must fill whole lanes
+    assert call(sh96, style=1) == L.KV_ESHAPE
+    assert call(sh, paged=L.KvPaged(ok, 256, 16, 8, 3)) == L.KV_EINVAL     # unknown pool layout
+    assert call(sh, paged=L.KvPaged(ok, 2, 16, 8, 0)) == L.KV_ESHAPE       # table shorter than t_cap
+
+
 def test_misaligned_word_arrays_are_rejected(lib):
     # int32 / fp32 arrays must be 4-byte aligned: one misaligned pointer per entry point
     from eviction_long_reasoning_amd import _lib as L

@@ -304,6 +304,75 @@ def test_score_rotated_matches_oracle(case):
     log(f"[rotated] {name}: worst scaled error {worst:.2e}")
 
 
+GQA_ROT_CASES = [
+    # name, dtype, d, L, S, H, G, T per seq, style, norm, paged block size (0 = dense), head-major pool
+    ("gqa-rot-bf16-d128-g4-inter", "bf16", 128, 2, 2, 2, 4, [1500, 777], "interleaved", False, 0, False),
+    ("gqa-rot-bf16-d128-g4-half-norm", "bf16", 128, 1, 2, 2, 4, [1030, 64], "half", True, 0, False),
+    ("gqa-rot-paged16-bf16-d128-g8", "bf16", 128, 2, 3, 2, 8, [2000, 1, 517], "interleaved", False, 16, False),
+    ("gqa-rot-paged16-hm-bf16-d128-g4-norm", "bf16", 128, 1, 2, 4, 4, [1100, 600], "interleaved", True, 16, True),
+    ("gqa-rot-paged64-hm-bf16-d64-g2-half", "bf16", 64, 1, 2, 3, 2, [2100, 900], "half", False, 64, True),
+    ("gqa-rot-fp32-d64-g3-norm", "f32", 64, 1, 1, 2, 3, [999], "interleaved", True, 0, False),
+    ("gqa-rot-bf16-d96-g1-idle-lanes", "bf16", 96, 1, 1, 2, 1, [700], "interleaved", False, 0, False),
+    ("gqa-rot-bf16-d32-g5-empty", "bf16", 32, 1, 2, 1, 5, [0, 1030], "interleaved", False, 32, False),
+]
+
+
+@pytest.mark.parametrize("case", GQA_ROT_CASES, ids=[c[0] for c in GQA_ROT_CASES])
+def test_gqa_rotated_matches_oracle(case):
+    name, dtype, d, L, S, H, G, Ts, style, norm, bs, hm = case
+    log(f"[gqa-rot] {name}")
+    r = rng(551, zlib.crc32(name.encode()) % 1000)
+    Ts = np.array(Ts, np.int32)
+    theta, D = 1e6, [2 ** i for i in range(17)]
+    nu = r.standard_normal((L, H, G, d)).astype(np.float32)
+    qabs = None
+    if norm:
+        re, im = oracle.band_slices(d, style)
+        qabs = (np.hypot(nu[..., re], nu[..., im]) / r.uniform(0.6, 1.0, (L, H, G, d // 2))).astype(np.float32)
+    t_cur = (Ts + 7).astype(np.int32)
+    kw = dict(rope_style=style, qabs=None if qabs is None else torch.from_numpy(qabs).to(DEV))
+    if bs == 0:
+        t_cap = int(Ts.max()) + 3
+        K = (r.standard_normal((L, 1, H, 1, d)) + 0.3 * r.standard_normal((L, S, H, t_cap, d))).astype(np.float32)
+        Kd = _to_dev_keys(K, dtype)
+        Kh = keys_f64(_host_keys(Kd, dtype), dtype)
+        rows = lambda l, s, h, T: Kh[l, s, h, :T]
+    else:
+        bps = (int(Ts.max()) + bs - 1) // bs
+        t_cap = bps * bs
+        n_blocks = S * bps + 5
+        pool = (r.standard_normal((L, 1, 1, H, d)) + 0.3 * r.standard_normal((L, n_blocks, bs, H, d))).astype(np.float32)
+        if hm:
+            pool = np.ascontiguousarray(pool.transpose(0, 1, 3, 2, 4))     # [L, n_blocks, H, bs, d]
+        table = r.permutation(n_blocks)[:S * bps].reshape(S, bps).astype(np.int32)
+        Kd = _to_dev_keys(pool, dtype)
+        Ph = keys_f64(_host_keys(Kd, dtype), dtype)
+        at = (lambda l, b, o, h: Ph[l, b, h, o]) if hm else (lambda l, b, o, h: Ph[l, b, o, h])
+        rows = lambda l, s, h, T: np.stack([at(l, table[s, j // bs], j % bs, h) for j in range(T)]) if T else \
+            np.zeros((0, d))
+        kw.update(block_table=_i32(table), head_major=hm)
+    out = torch.full((L, S, H, t_cap), float("nan"), device=DEV)
+    hout = torch.full((L, S, H, G, t_cap), float("nan"), device=DEV)
+    kv.tri_score_gqa_rotated(Kd, torch.from_numpy(nu).to(DEV), _i32(t_cur), _i32(Ts), theta, D, out=out,
+                             head_out=hout, **kw)
+    got, ghead = out.cpu().numpy(), hout.cpu().numpy()
+    worst_s = worst_z = 0.0
+    for l in range(L):
+        for s in range(S):
+            for h in range(H):
+                T = int(Ts[s])
+                if T == 0:
+                    assert np.all(np.isnan(got[l, s, h])), "an empty sequence was written"
+                    continue
+                zref, sref = oracle.score_gqa_rotated(rows(l, s, h, T), nu[l, h], int(t_cur[s]), theta, D, style,
+                                                      None if qabs is None else qabs[l, h])
+                for g in range(G):
+                    worst_s = max(worst_s, assert_scores(ghead[l, s, h, g, :T], sref[g], f"{name} l{l} s{s} h{h} g{g}"))
+                worst_z = max(worst_z, assert_z(got[l, s, h, :T], zref, f"{name} l{l} s{s} h{h}"))
+                assert np.all(np.isnan(got[l, s, h, T:])) and np.all(np.isnan(ghead[l, s, h, :, T:]))
+    log(f"[gqa-rot] {name}: worst scaled head-score error {worst_s:.2e}, worst z error {worst_z:.2e}")
+
+
 def test_score_deterministic():
     case = SCORE_CASES[1]
     K, qb, Ts, pos, t_cur = _score_inputs(case, 7)

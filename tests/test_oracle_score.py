@@ -314,3 +314,35 @@ def test_gqa_max_over_heads():
     # duplicating a query head changes nothing
     f2, _ = score_gqa(K, None, np.concatenate([q, q[:1]]), 40, 1e4, [1])
     np.testing.assert_allclose(final, f2, atol=1e-15)
+
+
+from oracle import score_gqa_rotated  # noqa: E402
+
+
+@pytest.mark.parametrize("with_norm", [False, True])
+def test_gqa_over_rotated_keys_equals_gqa_over_pre_rope_keys(with_norm):
+    # the grouped-query rule over stored rotated keys reproduces the rule over the pre-RoPE keys at
+    # their positions (relative-position identity), per query head and after the z-score + max
+    d, G = 16, 3
+    r = rng(125, int(with_norm))
+    K, pos = r.standard_normal((40, d)), np.sort(r.integers(0, 5000, 40))
+    qg = r.standard_normal((G, d))
+    qa = np.abs(qg[:, 0::2] + 1j * qg[:, 1::2]) * 1.3 if with_norm else None
+    D = [1, 8, 512]
+    z_rot, s_rot = score_gqa_rotated(rope_rotate(K, pos, 1e4), qg, 5100, 1e4, D, qabs_g=qa)
+    z_pre, s_pre = score_gqa(K, pos, qg, 5100, 1e4, D, qabs_g=qa)
+    np.testing.assert_allclose(s_rot, s_pre, atol=1e-10)
+    np.testing.assert_allclose(z_rot, z_pre, atol=1e-9)
+
+
+def test_gqa_over_rotated_keys_half_split_is_a_permutation():
+    d, G = 12, 2
+    r = rng(126)
+    K, qg = r.standard_normal((25, d)), r.standard_normal((G, d))
+    perm = np.empty(d, np.int64)
+    perm[0::2] = np.arange(d // 2)
+    perm[1::2] = np.arange(d // 2) + d // 2
+    zh, sh = score_gqa_rotated(K, qg, 300, 1e6, [1, 2], style="half")
+    zi, si = score_gqa_rotated(K[:, perm], qg[:, perm], 300, 1e6, [1, 2])
+    np.testing.assert_allclose(sh, si, atol=1e-12)
+    np.testing.assert_allclose(zh, zi, atol=1e-12)
