@@ -33,11 +33,13 @@ METRIC = "KV tokens scored+selected+compacted/sec and HBM GB/s (% peak), Qwen3-8
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=36, help="layers of the full-pass workload (36 = full size)")
     ap.add_argument("--cpu-heads", type=int, default=256, help="heads in the oracle's CPU sample (0 = skip)")
     ap.add_argument("--no-random", action="store_true", help="skip the random-eviction pass")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the 512-slot, one-layer and ragged-batch workloads")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run one elementwise copy of known size then exit after one pass (for HBM counter runs)")
     ap.add_argument("--pmc-probe-next", action="store_true",
@@ -136,6 +138,137 @@ def counter_traffic():
     if not m or m.group(1) != h.hexdigest() or not row:
         return None
     return (float(row.group(1)) + float(row.group(2))) * 1e9
+
+
+def percentiles(ms):
+    import numpy as np
+    q = np.percentile(np.asarray(ms, np.float64), [10, 50, 90])
+    return {"p10_ms": float(q[0]), "median_ms": float(q[1]), "p90_ms": float(q[2]), "reps": len(ms)}
+
+
+def kept_jaccard(ka, kb, t_cap):
+    """Mean over heads of |A & B| / |A | B| for two [..., b_cap] kept lists (-1 padded)."""
+    import torch
+    bc = ka.shape[-1]
+
+    def mask(k):
+        idx = k.reshape(-1, bc).long()
+        idx = torch.where(idx < 0, torch.full_like(idx, t_cap), idx)
+        m = torch.zeros((idx.shape[0], t_cap + 1), dtype=torch.bool, device=k.device)
+        m.scatter_(1, idx, True)
+        return m[:, :t_cap]
+    a, b = mask(ka), mask(kb)
+    inter = (a & b).sum(1).double()
+    union = (a | b).sum(1).double().clamp(min=1)
+    return float((inter / union).mean())
+
+
+def other_workloads(args, dev):
+    """Whole passes over the pages' other single-GPU shapes, each rep timed alone with HIP events:
+    one 512-slot fp32 head (launch latency), one 8-head layer of 32768 slots with the 256 MB
+    last-level cache flushed before every rep (cold) or not (warm), and 128 ragged sequences
+    scored and randomly evicted (the two passes' ratio and kept-set overlap)."""
+    import numpy as np
+    import torch
+
+    import eviction_long_reasoning_amd as kv
+    from workloads import centres, kv_torch, workload
+    reps = max(20, args.steps)
+    i32 = lambda a: torch.as_tensor(np.asarray(a, np.int32), device=dev)
+    flush_buf = torch.empty((1 << 28,), dtype=torch.float32, device=dev)   # 1 GiB
+
+    def timed(fn, cold=False, host=False):
+        """Per-rep milliseconds between two events around fn(). The GPU is kept busy before the
+        first event (the cache flush, or a bounded spin) so that the host has queued the whole pass
+        when it starts: the events then time the device alone. host=True starts each rep on an idle
+        GPU, so the time includes the host's launch path."""
+        for _ in range(args.warmup):
+            fn()
+        out = []
+        for i in range(reps):
+            if cold:
+                flush_buf.fill_(float(i))
+            elif not host:
+                torch.cuda._sleep(100000)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            fn()
+            e[1].record()
+            torch.cuda.synchronize(dev)
+            out.append(e[0].elapsed_time(e[1]))
+        return out
+
+    def prepare(wid):
+        w = workload(wid)
+        mu, qb, _ = centres(w)
+        K, V = kv_torch(w, dev, mu)
+        L, S, H = w.n_layers, w.n_seq, w.n_kv_heads
+        c = dict(w=w, K=K, V=V, qb=torch.from_numpy(qb).to(dev), seq=i32(w.seq_len), plen=i32(w.prompt_len),
+                 tcur=i32(w.t_cur), scores=torch.empty((L, S, H, w.t_cap), dtype=torch.float32, device=dev),
+                 kept=torch.empty((L, S, H, w.b_cap()), dtype=torch.int32, device=dev),
+                 nk=torch.empty((S,), dtype=torch.int32, device=dev),
+                 Ko=torch.empty((L, S, H, w.out_cap, w.head_dim), dtype=K.dtype, device=dev),
+                 Po=torch.empty((L, S, H, w.out_cap), dtype=torch.int32, device=dev))
+        c["Vo"] = torch.empty_like(c["Ko"])
+        return c
+
+    def scored(c):
+        w = c["w"]
+        kv.tri_score(c["K"], c["qb"], c["tcur"], c["seq"], w.theta, w.deltas, out=c["scores"])
+        kv.kv_select_topk(c["scores"], c["seq"], c["plen"], w.budget, w.recent, w.prompt_cap(), b_cap=w.b_cap(),
+                          kept=c["kept"], n_kept=c["nk"])
+        kv.kv_compact(c["K"], c["V"], c["kept"], c["nk"], c["seq"], w.out_cap, K_out=c["Ko"], V_out=c["Vo"],
+                      pos_out=c["Po"])
+
+    def random(c):
+        w = c["w"]
+        kv.kv_select_random(tuple(c["scores"].shape), c["seq"], c["plen"], w.budget, w.recent, w.prompt_cap(),
+                            w.seed_random, 0, b_cap=w.b_cap(), kept=c["kept"], n_kept=c["nk"])
+        kv.kv_compact(c["K"], c["V"], c["kept"], c["nk"], c["seq"], w.out_cap, K_out=c["Ko"], V_out=c["Vo"],
+                      pos_out=c["Po"])
+
+    def pass_bytes(c, with_score):
+        w = c["w"]
+        e, d = c["K"].element_size(), w.head_dim
+        rows = int(c["nk"].sum()) * w.n_layers * w.n_kv_heads
+        b = rows * (4 * d * e + 8) + w.n_heads_total * w.b_cap() * 4
+        return b + (w.entries * (d * e + 8) if with_score else 0)
+
+    res = {}
+    c = prepare(1)
+    t, th = timed(lambda: scored(c)), timed(lambda: scored(c), host=True)
+    res["fp32_512_slots"] = {"workload": c["w"].name, "entries": c["w"].entries, "scored_pass": percentiles(t),
+                             "scored_pass_host_inclusive": percentiles(th)}
+    print(f"[bench] 512-slot fp32 head: scored pass {np.median(t) * 1e3:.1f} us on the device, "
+          f"{np.median(th) * 1e3:.1f} us from an idle GPU (host launch path included)", file=sys.stderr, flush=True)
+    del c
+    c = prepare(2)
+    warm, cold = timed(lambda: scored(c)), timed(lambda: scored(c), cold=True)
+    b2 = pass_bytes(c, True)
+    res["one_layer_32k"] = {"workload": c["w"].name, "entries": c["w"].entries, "algorithmic_bytes": b2,
+                            "warm": percentiles(warm), "cold": percentiles(cold),
+                            "cold_gbs": b2 / (np.median(cold) * 1e-3) / 1e9}
+    print(f"[bench] one 8-head layer of 32768 slots: warm {np.median(warm):.4f} ms, cold {np.median(cold):.4f} ms",
+          file=sys.stderr, flush=True)
+    del c
+    c = prepare(5)
+    ts = timed(lambda: scored(c))
+    bs_ = pass_bytes(c, True)
+    ks = c["kept"].clone()
+    tr = timed(lambda: random(c))
+    br = pass_bytes(c, False)
+    jac = kept_jaccard(ks, c["kept"], c["w"].t_cap)
+    ms_s, ms_r = float(np.median(ts)), float(np.median(tr))
+    res["ragged_128_seqs"] = {"workload": c["w"].name, "entries": c["w"].entries,
+                              "scored_pass": percentiles(ts), "scored_gbs": bs_ / (ms_s * 1e-3) / 1e9,
+                              "scored_entries_per_s": c["w"].entries / (ms_s * 1e-3),
+                              "random_pass": percentiles(tr), "random_gbs": br / (ms_r * 1e-3) / 1e9,
+                              "random_over_scored_time": ms_r / ms_s, "mean_kept_jaccard": jac}
+    print(f"[bench] 128 ragged sequences: scored {ms_s:.3f} ms, random {ms_r:.3f} ms, mean Jaccard {jac:.3f}",
+          file=sys.stderr, flush=True)
+    del c, ks, flush_buf
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, K, qb, n_heads: int):
@@ -247,6 +380,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
     k_ms = {name: float(np.mean([evs[i][a].elapsed_time(evs[i][b]) for i in range(args.steps)]))
             for name, a, b in (("tri_score", 0, 1), ("kv_select_topk", 1, 2), ("kv_compact", 2, 3))}
+    step_dist = percentiles([evs[i][0].elapsed_time(evs[i][3]) for i in range(args.steps)])
     print(f"[bench] scored pass {ms_step:.3f} ms/step, kernels {k_ms}", file=sys.stderr, flush=True)
 
     # the same pass captured once into a HIP graph and replayed: the calls only launch kernels on
@@ -273,6 +407,35 @@ def main():
     ab = algorithmic_bytes(w, n_kept_head)
     entries = w.entries
     pass_bytes = ab["score"] + ab["select"] + ab["compact"]
+
+    # measured copy ceilings: torch's device copy of a quarter of K, and kv_compact over the
+    # contiguous slots 0..n_kept-1 of every head (the pass's compaction bytes, no gather)
+    quarter = K[: max(1, L // 4)]
+    dst = torch.empty_like(quarter)
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    dst.copy_(quarter)
+    cev[0].record()
+    for _ in range(args.steps):
+        dst.copy_(quarter)
+    cev[1].record()
+    torch.cuda.synchronize(dev)
+    copy_gbs = 2 * quarter.numel() * quarter.element_size() / (cev[0].elapsed_time(cev[1]) / args.steps * 1e-3) / 1e9
+    del dst, quarter
+    kept_c = torch.arange(b_cap, dtype=torch.int32, device=dev)
+    kept_c = torch.where(kept_c < n_kept_head, kept_c, torch.full_like(kept_c, -1)).expand(L, S, H, b_cap).contiguous()
+    kv.kv_compact(K, V, kept_c, nk, seq, out_cap, K_out=Ko, V_out=Vo, pos_out=Po)
+    cev[0].record()
+    for _ in range(args.steps):
+        kv.kv_compact(K, V, kept_c, nk, seq, out_cap, K_out=Ko, V_out=Vo, pos_out=Po)
+    cev[1].record()
+    torch.cuda.synchronize(dev)
+    contig_gbs = ab["compact"] / (cev[0].elapsed_time(cev[1]) / args.steps * 1e-3) / 1e9
+    del kept_c
+    ceilings = {"device_copy_gbs": copy_gbs, "compact_contiguous_gbs": contig_gbs,
+                "kv_compact_frac_of_contiguous": ab["compact"] / (k_ms["kv_compact"] * 1e-3) / 1e9 / contig_gbs,
+                "pass_gbs_over_device_copy": pass_bytes / (ms_step * 1e-3) / 1e9 / copy_gbs}
+    print(f"[bench] copy ceilings: device copy {copy_gbs:.0f} GB/s, kv_compact on contiguous slots "
+          f"{contig_gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
     rnd = None
     if not args.no_random:
@@ -471,6 +634,10 @@ def main():
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, K, qb, args.cpu_heads)
 
+    others = None
+    if not args.no_other_workloads:
+        others = other_workloads(args, dev)
+
     score_s = k_ms["tri_score"] * 1e-3
     achieved = ab["score"] / score_s / 1e9
     out = {
@@ -495,6 +662,8 @@ def main():
                      "bytes_per_launch": ab["score"], "ms_per_launch": k_ms["tri_score"]},
         "pass": {"algorithmic_bytes": pass_bytes, "gbs": pass_bytes / (ms_step * 1e-3) / 1e9,
                  "frac_of_peak": pass_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "step_ms": step_dist,
+                 "ceilings": ceilings,
                  "graph_replay_ms": graph_ms,
                  "graph_replay_entries_per_s": None if graph_ms is None else entries / (graph_ms * 1e-3),
                  "kernel_ms": k_ms,
@@ -514,6 +683,7 @@ def main():
         "select_recent": {"ms_per_launch": recent_ms},
         "select_long_cache": long_sel,
         "periodic_event": periodic,
+        "other_workloads": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
