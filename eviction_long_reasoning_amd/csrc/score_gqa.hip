@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "kv_internal.hpp"
+#include "rot_rows.hpp"
 
 namespace kvevict {
 namespace {
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(kScoreThreads) void gqa_rotated_kernel(const GqaPar
   __shared__ double part[NW][GM][2];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int g = lane % LPK;
   const int kk = lane / LPK;
   const int head = blockIdx.x / p.chunks_per_head;
@@ -585,6 +586,22 @@ __global__ __launch_bounds__(kScoreThreads) void gqa_rotated_kernel(const GqaPar
   const double tq = static_cast<double>(p.t_cur[s]);
   const bool live = g * EPL < p.d;
   const size_t lhg = (static_cast<size_t>(l) * p.H + h) * G;
+
+  RowSpace rs;
+  rs.K = static_cast<const char *>(p.K);
+  rs.row_bytes = static_cast<int64_t>(p.d) * EB;
+  rs.first = static_cast<int64_t>(head) * p.t_cap;
+  rs.blk0 = static_cast<int64_t>(l) * p.n_blocks;
+  rs.H = p.H;
+  rs.h = h;
+  rs.shift = p.block_shift;
+  rs.n_blocks = p.n_blocks;
+  rs.table = PAGED ? p.block_table + static_cast<size_t>(s) * p.blocks_per_seq : nullptr;
+  const bool uni = uniform_steps<LAYOUT, KPS>(rs);
+  const int lane_off = live ? static_cast<int>(kk * slot_stride<LAYOUT>(rs)) + g * 16 : kRowOffIdle;
+  // block-table entries of the next batch's steps (one per lane), read one batch ahead
+  int ent_next = 0;
+  if (PAGED && uni && wave_first < T) ent_next = step_entry<KPS>(rs, wave_first, T, lane);
 
   // per query head, the weight of each coordinate of this lane's piece (and the norm weight of the
   // band whose real part the coordinate holds)
@@ -639,11 +656,21 @@ __global__ __launch_bounds__(kScoreThreads) void gqa_rotated_kernel(const GqaPar
     const int j0 = wave_first + nb * 64;
     if (j0 >= T) break;
     uint4 data[STEPS];
+    if (uni) {
+      const BatchSteps steps = batch_steps<LAYOUT, KPS>(rs, j0, T, lane, ent_next);
 #pragma unroll
-    for (int t = 0; t < STEPS; ++t) {
-      const int j = j0 + t * KPS + kk;
-      const v4u32 v = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(row_ptr(j < T ? j : 0)));
-      data[t] = make_uint4(v[0], v[1], v[2], v[3]);   // slots past T read row 0; not stored
+      for (int t = 0; t < STEPS; ++t) data[t] = load_row_piece(step_rsrc(steps, t), lane_off);
+      if (PAGED && nb + 1 < NB && j0 + 64 < T) ent_next = step_entry<KPS>(rs, j0 + 64, T, lane);
+      // all of the batch's loads go out before any of its arithmetic (left free, the scheduler
+      // interleaves unpacking with the loads of dense heads and waits after every few)
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+      for (int t = 0; t < STEPS; ++t) {
+        const int j = j0 + t * KPS + kk;
+        const v4u32 v = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(row_ptr(j < T ? j : 0)));
+        data[t] = make_uint4(v[0], v[1], v[2], v[3]);   // slots past T read row 0; not stored
+      }
     }
     float acc[GM][STEPS];
 #pragma unroll
@@ -671,7 +698,20 @@ __global__ __launch_bounds__(kScoreThreads) void gqa_rotated_kernel(const GqaPar
         }
       }
 #pragma unroll
-      for (int q = 0; q < GM; ++q) acc[q][t] = live ? a[q] : 0.f;
+      for (int q = 0; q < GM; ++q) {
+        acc[q][t] = a[q];
+        // materialise every head's sum here: left free, the compiler sinks the dot products of
+        // heads q >= 1 into the branches below and keeps the whole batch's keys in registers
+        asm volatile("" : "+v"(acc[q][t]));
+      }
+      // one step at a time: unpacking a later piece early only holds more registers
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!uni && !live) {   // per-slot rows: idle lanes read a live piece (uniform rows read zeros there)
+#pragma unroll
+      for (int q = 0; q < GM; ++q)
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) acc[q][t] = 0.f;
     }
     const int jj = j0 + g * KPS + kk;
 #pragma unroll

@@ -20,6 +20,7 @@
 // [L, n_blocks, H, block_size, d]. Lane layout, batching and the shuffle reduce-scatter follow
 // the pre-RoPE kernel.
 #include "kv_internal.hpp"
+#include "rot_rows.hpp"
 
 #ifndef KV_ROT_PREFETCH
 #define KV_ROT_PREFETCH 1
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_rotated_kernel(const RotS
   constexpr int EB = BF16 ? 2 : 4;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int g = lane % LPK;
   const int kk = lane / LPK;
   const int head = blockIdx.x / p.chunks_per_head;
@@ -96,26 +97,53 @@ __global__ __launch_bounds__(kScoreThreads) void score_rotated_kernel(const RotS
   const int wave_first = chunk * kScoreChunk + wave * (kScoreBatchesPerWave * 64);
   if (wave_first >= T) return;
 
+  RowSpace rs;
+  rs.K = static_cast<const char *>(p.K);
+  rs.row_bytes = static_cast<int64_t>(p.d) * EB;
+  rs.first = static_cast<int64_t>(head) * p.t_cap;
+  rs.blk0 = static_cast<int64_t>(l) * p.n_blocks;
+  rs.H = p.H;
+  rs.h = h;
+  rs.shift = p.block_shift;
+  rs.n_blocks = p.n_blocks;
+  rs.table = PAGED ? p.block_table + static_cast<size_t>(s) * p.blocks_per_seq : nullptr;
+  const bool uni = uniform_steps<LAYOUT, KPS>(rs);
+  const bool live = g * EPL < p.d;
+  const int lane_off = live ? static_cast<int>(kk * slot_stride<LAYOUT>(rs)) + g * 16 : kRowOffIdle;
+
   // Block-table entries of the wave's slots, read before the weight set-up so that their latency
   // overlaps it (measured 4-7 % faster on shuffled paged pools; KV_ROT_PREFETCH=0 reads each
-  // entry just before its row, as the dense path does)
-  constexpr bool PREFETCH = PAGED && KV_ROT_PREFETCH && STEPS <= 16;
-  int pbs[PREFETCH ? kScoreBatchesPerWave : 1][PREFETCH ? STEPS : 1];
-  if constexpr (PREFETCH) {
-    const int32_t *tb = p.block_table + static_cast<size_t>(s) * p.blocks_per_seq;
+  // entry just before its row, as the dense path does): one id per block and batch when steps
+  // share a block, else one per slot
+  int ents[PAGED ? kScoreBatchesPerWave : 1];
+  if constexpr (PAGED) {
+    if (uni) {
 #pragma unroll
-    for (int nb = 0; nb < kScoreBatchesPerWave; ++nb) {
-#pragma unroll
-      for (int t = 0; t < STEPS; ++t) {
-        int j = wave_first + nb * 64 + t * KPS + kk;
-        j = j < T ? j : 0;
-        pbs[nb][t] = min(max(tb[j >> p.block_shift], 0), p.n_blocks - 1);
+      for (int nb = 0; nb < kScoreBatchesPerWave; ++nb) {
+        const int j0 = wave_first + nb * 64;
+        ents[nb] = step_entry<KPS>(rs, j0 < T ? j0 : 0, T, lane);
       }
     }
   }
+  constexpr bool PREFETCH = PAGED && KV_ROT_PREFETCH && STEPS <= 16;
+  int pbs[PREFETCH ? kScoreBatchesPerWave : 1][PREFETCH ? STEPS : 1];
+  if constexpr (PREFETCH) {
+    if (!uni) {
+      const int32_t *tb = p.block_table + static_cast<size_t>(s) * p.blocks_per_seq;
+#pragma unroll
+      for (int nb = 0; nb < kScoreBatchesPerWave; ++nb) {
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+          int j = wave_first + nb * 64 + t * KPS + kk;
+          j = j < T ? j : 0;
+          pbs[nb][t] = min(max(tb[j >> p.block_shift], 0), p.n_blocks - 1);
+        }
+      }
+    }
+  }
+
   // per-coordinate weights of this lane's piece
   const int F = p.F;
-  const bool live = g * EPL < p.d;
   const size_t lh = static_cast<size_t>(l) * p.H + h;
   const float *q = p.qbar + lh * p.d;
   const double tq = static_cast<double>(p.t_cur[s]);
@@ -156,24 +184,26 @@ __global__ __launch_bounds__(kScoreThreads) void score_rotated_kernel(const RotS
     return Kb + row * row_bytes + static_cast<size_t>(live ? g : 0) * 16;
   };
 
-#if KV_ROT_PREFETCH
 #pragma unroll
-#else
-#pragma unroll 1
-#endif
   for (int nb = 0; nb < kScoreBatchesPerWave; ++nb) {
     const int j0 = wave_first + nb * 64;
     if (j0 >= T) break;
     float acc[STEPS];
+    BatchSteps steps{};
+    if (uni) steps = batch_steps<LAYOUT, KPS>(rs, j0, T, lane, PAGED ? ents[PAGED ? nb : 0] : 0);
 #pragma unroll
     for (int st0 = 0; st0 < STEPS; st0 += SUB) {
       uint4 data[SUB];
 #pragma unroll
       for (int t = 0; t < SUB; ++t) {
-        const int j = j0 + (st0 + t) * KPS + kk;
-        int pre = 0;
-        if constexpr (PREFETCH) pre = pbs[nb][st0 + t];
-        data[t] = ld_stream(row_ptr(j < T ? j : 0, pre));  // slots past T read row 0; their sums are not stored
+        if (uni) {
+          data[t] = load_row_piece(step_rsrc(steps, st0 + t), lane_off);
+        } else {
+          const int j = j0 + (st0 + t) * KPS + kk;
+          int pre = 0;
+          if constexpr (PREFETCH) pre = pbs[nb][st0 + t];
+          data[t] = ld_stream(row_ptr(j < T ? j : 0, pre));  // slots past T read row 0; their sums are not stored
+        }
       }
 #pragma unroll
       for (int t = 0; t < SUB; ++t) {
@@ -197,8 +227,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_rotated_kernel(const RotS
             }
           }
         }
-        acc[st0 + t] = live ? a : 0.f;
+        acc[st0 + t] = a;
       }
+    }
+    if (!uni && !live) {   // per-slot rows: idle lanes read a live piece (uniform rows read zeros there)
+#pragma unroll
+      for (int t = 0; t < STEPS; ++t) acc[t] = 0.f;
     }
     const float sc = reduce_scatter<STEPS>(acc, g);
     const int jj = j0 + g * KPS + kk;
