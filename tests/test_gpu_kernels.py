@@ -253,6 +253,12 @@ ROT_CASES = [
     ("rot-paged64-bf16-d64-half", "bf16", 64, 1, 2, 8, [2000, 1500], "half", False, 64, False),
     ("rot-paged16-headmajor-bf16-d128", "bf16", 128, 2, 3, 4, [1000, 1, 517], "interleaved", True, 16, True),
     ("rot-paged32-headmajor-fp32-d64-half", "f32", 64, 1, 2, 3, [700, 64], "half", False, 32, True),
+    # blocks smaller than a wave step's slots (4 at 16 lanes per key, 32 at 2): per-slot rows
+    ("rot-paged2-bf16-d96-inter-norm-idle", "bf16", 96, 1, 2, 2, [301, 45], "interleaved", True, 2, False),
+    ("rot-paged1-headmajor-bf16-d128-half", "bf16", 128, 1, 2, 2, [130, 77], "half", False, 1, True),
+    ("rot-paged8-fp32-d8-norm", "f32", 8, 1, 2, 1, [200, 31], "interleaved", True, 8, False),
+    # a block of exactly one step, idle lanes past head_dim 96
+    ("rot-paged4-bf16-d96-inter", "bf16", 96, 1, 2, 3, [259, 3], "interleaved", False, 4, False),
 ]
 
 
@@ -314,6 +320,12 @@ GQA_ROT_CASES = [
     ("gqa-rot-fp32-d64-g3-norm", "f32", 64, 1, 1, 2, 3, [999], "interleaved", True, 0, False),
     ("gqa-rot-bf16-d96-g1-idle-lanes", "bf16", 96, 1, 1, 2, 1, [700], "interleaved", False, 0, False),
     ("gqa-rot-bf16-d32-g5-empty", "bf16", 32, 1, 2, 1, 5, [0, 1030], "interleaved", False, 32, False),
+    # blocks smaller than a wave step's slots: per-slot rows (idle lanes zeroed after the sums)
+    ("gqa-rot-paged2-bf16-d96-g4-norm-idle", "bf16", 96, 1, 2, 2, 4, [301, 45], "interleaved", True, 2, False),
+    ("gqa-rot-paged1-hm-bf16-d128-g3-half", "bf16", 128, 1, 2, 2, 3, [130, 77], "half", False, 1, True),
+    ("gqa-rot-paged2-hm-fp32-d64-g8-norm", "f32", 64, 1, 1, 2, 8, [260], "interleaved", True, 2, True),
+    # a block of exactly one step, idle lanes past head_dim 96
+    ("gqa-rot-paged4-bf16-d96-g2", "bf16", 96, 1, 2, 3, 2, [259, 3], "interleaved", False, 4, False),
 ]
 
 
