@@ -395,7 +395,7 @@ __global__ __launch_bounds__(kScoreThreads) void gqa_stream_kernel(const GqaPara
   __shared__ double part[NW][GM][2];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int g = lane % LPK;
   const int kk = lane / LPK;
   const int head = blockIdx.x / p.chunks_per_head;
@@ -423,8 +423,12 @@ __global__ __launch_bounds__(kScoreThreads) void gqa_stream_kernel(const GqaPara
 #pragma unroll
     for (int t = 0; t < SUB; ++t) d[t] = ld16(rk, boff, t * step_bytes);
   };
+  // Sub-batches are issued whether or not they hold live keys: past T the buffer range check
+  // returns zeros without a memory access (offsets stay below 2^31: the launch requires
+  // t_cap plus two chunks of rows to fit), and a load that is always issued lets each wait count only
+  // the older sub-batch (a conditional issue forces a wait for every load in flight).
   uint4 da[SUB], db[SUB];
-  if (nsb > 0) issue(0, da);
+  issue(0, da);
 
   const double tq = static_cast<double>(p.t_cur[s]);
   const size_t lhg = (static_cast<size_t>(l) * p.H + h) * G;
@@ -507,10 +511,10 @@ __global__ __launch_bounds__(kScoreThreads) void gqa_stream_kernel(const GqaPara
 #pragma unroll
   for (int sb = 0; sb < NSB; sb += 2) {
     if (sb >= nsb) break;
-    if (sb + 1 < nsb) issue(sb + 1, db);
+    issue(sb + 1, db);
     consume(sb, da);
     if (sb + 1 >= nsb) break;
-    if (sb + 2 < nsb) issue(sb + 2, da);
+    issue(sb + 2, da);
     consume(sb + 1, db);
   }
 
@@ -877,7 +881,7 @@ hipError_t launch_score_gqa(const GqaParams &p, int dtype_bf16, int pieces_per_l
   // addressable with 32-bit offsets: the VALU stream form; everything else: the matrix cores
   const int pieces = p.d * (dtype_bf16 ? 2 : 4) / 16;
   const bool stream = dtype_bf16 && !pos && p.G <= KV_GQA_STREAM_MAX_G && (pieces == 4 || pieces == 8 || pieces == 16) &&
-                      static_cast<long long>(p.t_cap + kGqaChunk) * p.d * 2 < (1ll << 31);
+                      static_cast<long long>(p.t_cap + 2 * kGqaChunk) * p.d * 2 < (1ll << 31);
   if (stream)
     e = norm ? launch_stream<true>(p, pieces, grid, st) : launch_stream<false>(p, pieces, grid, st);
   else if (dtype_bf16)
