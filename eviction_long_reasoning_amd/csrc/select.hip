@@ -59,8 +59,10 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
   constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    const uint32_t lo_a = kMulA * c0, hi_a = __umulhi(kMulA, c0);
-    const uint32_t lo_b = kMulB * c2, hi_b = __umulhi(kMulB, c2);
+    // one 32 x 32 -> 64-bit product per multiplier (v_mad_u64_u32) gives both halves
+    const uint64_t pa = static_cast<uint64_t>(kMulA) * c0, pb = static_cast<uint64_t>(kMulB) * c2;
+    const uint32_t lo_a = static_cast<uint32_t>(pa), hi_a = static_cast<uint32_t>(pa >> 32);
+    const uint32_t lo_b = static_cast<uint32_t>(pb), hi_b = static_cast<uint32_t>(pb >> 32);
     const uint32_t n0 = hi_b ^ c1 ^ k0;
     const uint32_t n2 = hi_a ^ c3 ^ k1;
     c0 = n0;
