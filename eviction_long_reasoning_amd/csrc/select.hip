@@ -120,6 +120,43 @@ __device__ __forceinline__ uint32_t value_bin(uint32_t k, float fmin, float scal
   return min(static_cast<uint32_t>(x), static_cast<uint32_t>(kValueBins - 1));
 }
 
+// value_bin never decreases as the key grows (over all 2^32 keys), so the keys of one bin form an
+// interval. Run by one wave: the smallest key whose bin is at least `target`, or 2^32 when none
+// is, by a 64-way search over the key space (at most seven rounds). It evaluates the same
+// rounded expression as the histogram pass, so the interval test that replaces a second
+// evaluation per key agrees with it key for key.
+__device__ __forceinline__ uint64_t first_key_reaching(uint32_t target, float fmin, float scale, int lane) {
+  uint64_t lo = 0, hi = uint64_t{1} << 32;   // keys below lo stay under target; hi reaches it (2^32: none)
+  while (lo < hi) {
+    const uint64_t step = (hi - lo + 63) >> 6;
+    const uint64_t c = lo + static_cast<uint64_t>(lane) * step;
+    const bool reach = c >= hi || value_bin(static_cast<uint32_t>(c), fmin, scale) >= target;
+    const uint64_t m = __ballot(reach);
+    if (m & 1ull) return lo;
+    const int f = m ? __builtin_ctzll(m) : 64;               // first probe that reaches (64: none)
+    const uint64_t below = lo + static_cast<uint64_t>(f - 1) * step;  // the last probe that does not
+    if (f < 64) hi = min(hi, lo + static_cast<uint64_t>(f) * step);
+    lo = below + 1;
+  }
+  return hi;
+}
+
+// Interval [lo, hi] of the keys of bin b, in LDS slots kb[0], kb[1]: scores (value bins) by waves 0
+// and 1 of the workgroup (the caller then synchronises), random keys (top 10 bits) directly.
+template <bool RANDOM>
+__device__ __forceinline__ void bin_interval(uint32_t b, float fmin, float scale, int wave, int lane,
+                                             uint32_t *kb) {
+  if (RANDOM) {
+    if (wave == 0 && lane == 0) {
+      kb[0] = b << 22;
+      kb[1] = (b << 22) | 0x3FFFFFu;
+    }
+  } else if (wave < 2) {
+    const uint64_t k = first_key_reaching(b + static_cast<uint32_t>(wave), fmin, scale, lane);
+    if (lane == 0) kb[wave] = static_cast<uint32_t>(k - static_cast<uint64_t>(wave));  // bin b+1's first, minus one
+  }
+}
+
 // Run by one wave: lane L owns bins (NBINS/64)*L ...; finds the bin b holding the remaining-th
 // largest key (counting from the top) and the number of keys in bins above it.
 template <int NBINS>
@@ -256,6 +293,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   __shared__ uint32_t tot_e[R * NW];   // per (round, wave): slots whose key equals thr
   __shared__ uint32_t found[3];
   __shared__ uint32_t n_members;
+  __shared__ uint32_t kb[2];   // key interval of the threshold's bin
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -404,9 +442,22 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
           const uint32_t b = found[0];
           remaining -= found[1];
           mem = 0ull;
+          // Membership in the threshold's bin. With 32 or more keys per thread, testing each key
+          // against the bin's key interval (found once by waves 0 and 1) beats evaluating its bin
+          // again; with fewer, the search and its barrier cost more than they save (2176-slot
+          // heads: 0.095 -> 0.111 ms). A random key's bin is a shift, cheaper than either.
+          if constexpr (!RANDOM && KPT >= 32) {
+            bin_interval<RANDOM>(b, fmin, scale, wave, lane, kb);
+            __syncthreads();
+            const uint32_t klo = kb[0], khi = kb[1];
 #pragma unroll
-          for (int i = 0; i < KPT; ++i)
-            if (((cand >> i) & 1ull) && bin_of(key[i]) == b) mem |= 1ull << i;
+            for (int i = 0; i < KPT; ++i)
+              if (((cand >> i) & 1ull) && key[i] >= klo && key[i] <= khi) mem |= 1ull << i;
+          } else {
+#pragma unroll
+            for (int i = 0; i < KPT; ++i)
+              if (((cand >> i) & 1ull) && bin_of(key[i]) == b) mem |= 1ull << i;
+          }
           __syncthreads();  // `found` and `hist` are reused below
           // The threshold's bin usually holds a few keys: list them in LDS (hist is free) and rank
           // them directly instead of running the radix passes.
@@ -564,6 +615,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
   __shared__ uint32_t wsum[2 * NW];
   __shared__ uint32_t found[3];
   __shared__ uint32_t n_members;
+  __shared__ uint32_t kb[2];   // key interval of the threshold's bin
   extern __shared__ uint32_t ubits[];   // union: bit j set when slot j is in some head's top-k
 
   const int tid = threadIdx.x;
@@ -649,7 +701,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
       // member keys: those in the bin that holds the threshold (bins as in the register kernel),
       // or every candidate when the scores have no usable value range
       bool binned = RANDOM, ranked = false;
-      uint32_t bsel = 0u;
+      uint32_t bsel = 0u, klo = 0u, khi = 0xFFFFFFFFu;   // key interval of the threshold's bin
       float fmin = 0.f, scale = 0.f;
       auto bin_of = [&](uint32_t k) { return RANDOM ? (k >> 22) : value_bin(k, fmin, scale); };
       if (!RANDOM) {
@@ -677,11 +729,14 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
         __syncthreads();
         bsel = found[0];
         remaining -= found[1];
-        __syncthreads();  // `found` and `hist` are reused below
+        bin_interval<RANDOM>(bsel, fmin, scale, wave, lane, kb);
+        __syncthreads();  // `found` and `hist` are reused below; kb is written
+        klo = kb[0];
+        khi = kb[1];
         // a short member list is ranked directly (as in the register kernel)
         for (int j = e_lo + tid; j < e_hi; j += NT) {
           const uint32_t k = key_of(j);
-          if (bin_of(k) == bsel) {
+          if (k >= klo && k <= khi) {
             const uint32_t at = atomicAdd(&n_members, 1u);
             if (at < member_cap<NT>()) hist[at] = k;
           }
@@ -700,7 +755,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
         }
         __syncthreads();  // `found` and `hist` are reused below
       }
-      auto member = [&](uint32_t k) { return !binned || bin_of(k) == bsel; };
+      auto member = [&](uint32_t k) { return !binned || (k >= klo && k <= khi); };
       if (!ranked) {
         uint32_t kor = 0u, kand = 0xFFFFFFFFu;
         for (int j = e_lo + tid; j < e_hi; j += NT) {
