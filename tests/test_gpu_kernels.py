@@ -259,6 +259,12 @@ ROT_CASES = [
     ("rot-paged8-fp32-d8-norm", "f32", 8, 1, 2, 1, [200, 31], "interleaved", True, 8, False),
     # a block of exactly one step, idle lanes past head_dim 96
     ("rot-paged4-bf16-d96-inter", "bf16", 96, 1, 2, 3, [259, 3], "interleaved", False, 4, False),
+    # head_dim 256: 32 lanes per key (two slots a step) and, in fp32, 64 (one slot a step)
+    ("rot-bf16-d256-half-norm", "bf16", 256, 1, 2, 2, [300, 77], "half", True, 0, False),
+    ("rot-paged1-bf16-d256", "bf16", 256, 1, 2, 2, [300, 77], "interleaved", False, 1, False),
+    ("rot-paged2-headmajor-bf16-d256", "bf16", 256, 1, 2, 2, [300, 77], "interleaved", True, 2, True),
+    ("rot-fp32-d256-inter", "f32", 256, 1, 2, 2, [300, 77], "interleaved", False, 0, False),
+    ("rot-paged1-fp32-d256-half-norm", "f32", 256, 1, 2, 2, [300, 77], "half", True, 1, False),
 ]
 
 
