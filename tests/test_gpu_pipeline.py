@@ -307,7 +307,8 @@ def test_workload3_full_size_next_rows(full_pass):
     # the next rows at the full pass's size, in the launch configurations bench.py times, on the
     # sampled heads: the norm term, the same memory read as post-RoPE keys (dense, and through a
     # shuffled block table over a head-major pool), the grouped-query z-score + max with G = 4 and
-    # union selection on its outputs; recency on every head
+    # union selection on its outputs, the same rule over the memory read as post-RoPE keys through
+    # the shuffled table over a token-major pool; recency on every head
     w, K, V, qb = full_pass
     L, S, H, T, d = K.shape
     Tn, Pn = w.seq_len, w.prompt_len
@@ -325,13 +326,16 @@ def test_workload3_full_size_next_rows(full_pass):
     nu = query_head_centres(workload(3, q_mode="group-mean"))
     zmax, head = kv.tri_score_gqa(K, torch.from_numpy(nu).to(DEV), tcur, seq, w.theta, w.deltas)
     ku, nku = kv.kv_select_union(head, zmax, seq, plen, w.budget, w.recent, w.prompt_cap())
+    pool_tm = K.view(L, S * bps, bs, H, d)                     # token-major pool over the same memory
+    zrot, hrot = kv.tri_score_gqa_rotated(pool_tm, torch.from_numpy(nu).to(DEV), tcur, seq, w.theta, w.deltas,
+                                          block_table=table)
     kr, nkr = kv.kv_select_recent((L, S, H, T), seq, plen, w.budget, w.recent, w.prompt_cap())
     torch.cuda.synchronize()
     # recency: every head is the prompt followed by the latest slots
     part = oracle.partition(int(Tn[0]), int(Pn[0]), w.budget, w.recent)
     want = torch.from_numpy(oracle.select_recent(int(Tn[0]), int(Pn[0]), w.budget, w.recent)).to(DEV)
     assert torch.all(nkr == part.n_kept) and torch.all(kr[..., :part.n_kept] == want)
-    worst = {"norm": 0.0, "rot": 0.0, "paged": 0.0, "head": 0.0, "z": 0.0}
+    worst = {"norm": 0.0, "rot": 0.0, "paged": 0.0, "head": 0.0, "z": 0.0, "rot_head": 0.0, "rot_z": 0.0}
     tbl = table.cpu().numpy()
     for (l, s, h) in SAMPLED_HEADS[:4]:
         Tl, t = int(Tn[s]), int(w.t_cur[s])
@@ -355,6 +359,13 @@ def test_workload3_full_size_next_rows(full_pass):
         uref = oracle.select_union(hh, zz, Tl, int(Pn[s]), w.budget, w.recent)
         assert int(nku[s]) == uref.size
         assert np.array_equal(ku[l, s, h, :uref.size].cpu().numpy(), uref), f"union {l, s, h}"
+        rows = pool_tm[l, torch.from_numpy(tbl[s, j // bs].astype(np.int64)).to(DEV),
+                       torch.from_numpy(j % bs).to(DEV), h]
+        zref, sref = oracle.score_gqa_rotated(keys_f64(host_bits(rows), w.dtype), nu[l, h], t, w.theta, w.deltas)
+        hh = hrot[l, s, h, :, :Tl].cpu().numpy()
+        for gq in range(w.group):
+            worst["rot_head"] = max(worst["rot_head"], assert_scores(hh[gq], sref[gq], f"gqa rot {l, s, h} g{gq}"))
+        worst["rot_z"] = max(worst["rot_z"], assert_z(zrot[l, s, h, :Tl].cpu().numpy(), zref, f"gqa rot z {l, s, h}"))
     log(f"[w3-next] sampled heads: worst scaled errors {worst}")
 
 
