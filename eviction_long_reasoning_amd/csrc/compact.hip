@@ -89,20 +89,30 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(const CompactP
 // below n missing from the prefix. The i-th hole is i + #{r < r0 : kept[r] - r <= i} (kept[r] - r
 // counts the holes before kept[r] and never decreases). Movers are read only from slots >= n and
 // written only to slots < n, so no slot is both read and written.
+// Kept lists up to this long are copied to LDS first, so that the binary searches (about a dozen
+// dependent reads per mover) run at LDS rather than global-memory latency.
+constexpr int kHoleStage = 4096;
+
 template <int G>
 __global__ __launch_bounds__(kCompactThreads) void holes_kernel(const HoleParams p) {
   constexpr int ROWS_PER_PASS = kCompactThreads / G;
   __shared__ int prefix;
+  __shared__ int32_t staged_kept[kHoleStage];
   const int head = blockIdx.x / p.wgs_per_head;
   const int part = blockIdx.x - head * p.wgs_per_head;
   const int s = (head / p.H) % p.S;
   const int n = min(min(max(p.n_kept[s], 0), p.b_cap), p.t_cap);
-  const int32_t *kept = p.kept + static_cast<size_t>(head) * p.b_cap;
+  const int32_t *kept_g = p.kept + static_cast<size_t>(head) * p.b_cap;
+  const bool staged = n <= kHoleStage;
+  if (staged)
+    for (int r = threadIdx.x; r < n; r += kCompactThreads) staged_kept[r] = kept_g[r];
+  __syncthreads();
+  auto kept = [&](int r) { return staged ? staged_kept[r] : kept_g[r]; };
   if (threadIdx.x == 0) {
     int lo = 0, hi = n;  // first r with kept[r] >= n
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (kept[mid] < n) lo = mid + 1; else hi = mid;
+      if (kept(mid) < n) lo = mid + 1; else hi = mid;
     }
     prefix = lo;
   }
@@ -113,12 +123,12 @@ __global__ __launch_bounds__(kCompactThreads) void holes_kernel(const HoleParams
   const int rr = threadIdx.x / G;
   const size_t row0 = static_cast<size_t>(head) * p.t_cap;
   for (int i = part * ROWS_PER_PASS + rr; i < movers; i += ROWS_PER_PASS * p.wgs_per_head) {
-    const int src = kept[r0 + i];
+    const int src = kept(r0 + i);
     if (src < n || src >= p.t_cap) continue;   // not a mover (kept not ascending) or out of range
     int lo = 0, hi = r0;                        // #{r < r0 : kept[r] - r <= i}
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (kept[mid] - mid <= i) lo = mid + 1; else hi = mid;
+      if (kept(mid) - mid <= i) lo = mid + 1; else hi = mid;
     }
     const int dst = i + lo;                     // < n
     if (c < p.row16) {
