@@ -689,6 +689,10 @@ HOLE_CASES = [
     ("holes-bf16-d128-deep", "bf16", 128, 1, 2, 2, 9000, [9000, 4000], 3072, 128, True),
     ("holes-fp32-d8-nopos", "f32", 8, 1, 1, 3, 700, [700], 200, 0, False),
     ("holes-bf16-d96", "bf16", 96, 1, 2, 1, 1500, [1500, 1499], 1000, 16, True),
+    # kept lists at and past the 4096 entries a workgroup copies to LDS (the longer one searches
+    # global memory)
+    ("holes-bf16-d64-list4096", "bf16", 64, 1, 1, 2, 6000, [6000], 4096, 128, True),
+    ("holes-bf16-d64-list5000", "bf16", 64, 1, 2, 2, 12000, [12000, 7000], 5000, 128, True),
 ]
 
 
