@@ -7,8 +7,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (canonical_scores, partition, random_uniforms, select_random, select_random_shared, select_recent,
-                    select_topk, select_union)
+from oracle import (canonical_scores, partition, philox4x32_10, random_uniforms, select_random, select_random_shared,
+                    select_recent, select_topk, select_union)
 from workloads import random_scores, rng
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "partition_cases.json")
@@ -115,6 +115,23 @@ def test_random_kept_structure():
         assert set(range(P)) <= set(kept.tolist()) and set(range(T - p.R, T)) <= set(kept.tolist())
 
 
+def test_random_uniforms_layout():
+    # slot position p draws word 0 of the Philox block with counter (p, layer<<16|head, seq, event)
+    # and key (seed mod 2^32, seed >> 32): checked against the scalar generator (itself pinned to an
+    # independent implementation), so a wrong counter word, word or key order fails here
+    layer, head, seq, event, seed = 5, 3, 7, 11, 0x0123456789ABCDEF
+    key = (seed & 0xFFFFFFFF, seed >> 32)
+    pos = np.array([0, 1, 2, 3, 4097, 2 ** 31 + 6])
+    want = [philox4x32_10((p, (layer << 16) | head, seq, event), key)[0] / 2 ** 32 for p in pos.tolist()]
+    assert np.array_equal(random_uniforms(pos, layer, head, seq, event, seed), np.array(want))
+    # each argument reaches the draw
+    base = random_uniforms(pos, layer, head, seq, event, seed)
+    for args in ((layer + 1, head, seq, event, seed), (layer, head + 1, seq, event, seed),
+                 (layer, head, seq + 1, event, seed), (layer, head, seq, event + 1, seed),
+                 (layer, head, seq, event, seed ^ (1 << 40))):
+        assert not np.any(random_uniforms(pos, *args) == base)
+
+
 def test_random_ranks_follow_uniforms():
     # the selected candidates are exactly those with the n_sel largest uniforms (ties to lower slot)
     T, P, B, R = 120, 10, 50, 8
@@ -126,7 +143,7 @@ def test_random_ranks_follow_uniforms():
 
 
 def test_random_marginals_uniform():
-    # spec check (d): each evictable slot is kept with probability n_sel/|E|;
+    # uniform marginals: each evictable slot is kept with probability n_sel/|E|;
     # pairs are kept together with probability n(n-1)/(|E|(|E|-1)).
     T, P, B, R = 40, 4, 14, 4
     p = partition(T, P, B, R)
