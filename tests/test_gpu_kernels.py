@@ -961,3 +961,81 @@ def test_audit_accepts_every_selector_and_flags_broken_lists():
     nk2[2] += 1
     bad = kv.kv_audit_kept(kept, nk2, Td, Pd, B, R, pcap, t_cap).cpu().numpy()
     assert np.all(bad[:, 2] == 1) and bad[:, :2].sum() == 0
+
+
+def test_every_other_entry_point_is_deterministic():
+    # each call run twice on the same inputs gives the same bits (score, GQA and the scored pass are
+    # covered by their own tests): rotated keys dense and paged, grouped-query scores over rotated
+    # keys, random / shared / recency / union selection, the audit, both compactions
+    log("[determinism] every other entry point")
+    r = rng(777, 1)
+    L, S, H, T, d, G, B, R = 2, 3, 2, 3008, 128, 4, 700, 64
+    Ts = _i32([3000, 2500, 1700])
+    Ps = _i32([100, 800, 10])
+    tcur = _i32([3004, 2600, 1800])
+    D = [2 ** i for i in range(17)]
+    K = _to_dev_keys((r.standard_normal((L, 1, H, 1, d)) + 0.3 * r.standard_normal((L, S, H, T, d))).astype(np.float32),
+                     "bf16")
+    V = _to_dev_keys(r.standard_normal((L, S, H, T, d)).astype(np.float32), "bf16")
+    pos = torch.from_numpy(np.sort(r.integers(0, 10 ** 6, (L, S, H, T)), axis=-1).astype(np.int32)).to(DEV)
+    qb = torch.from_numpy(r.standard_normal((L, H, d)).astype(np.float32)).to(DEV)
+    nu = torch.from_numpy(r.standard_normal((L, H, G, d)).astype(np.float32)).to(DEV)
+    bs = 16
+    bps = T // bs
+    pool = K.view(L, S * bps, bs, H, d)
+    table = _i32(r.permutation(S * bps).reshape(S, bps))
+    pc = int(Ps.max())
+
+    def same(a, b, what):
+        a = a if isinstance(a, tuple) else (a,)
+        b = b if isinstance(b, tuple) else (b,)
+        for x, y in zip(a, b):
+            assert torch.equal(x.view(torch.int32) if x.dtype == torch.float32 else x,
+                               y.view(torch.int32) if y.dtype == torch.float32 else y), what
+
+    Tl = Ts.cpu().tolist()
+
+    def written(x):
+        # score outputs hold nothing at or past a sequence's length: compare the written slots
+        y = x.clone()
+        for si, t in enumerate(Tl):
+            y[:, si, ..., t:] = 0
+        return y
+
+    calls = {
+        "rotated dense": lambda: kv.tri_score_rotated(K, qb, tcur, Ts, 1e6, D),
+        "rotated paged": lambda: kv.tri_score_rotated(pool, qb, tcur, Ts, 1e6, D, block_table=table),
+        "gqa rotated paged": lambda: kv.tri_score_gqa_rotated(pool, nu, tcur, Ts, 1e6, D, block_table=table),
+        "random": lambda: kv.kv_select_random((L, S, H, T), Ts, Ps, B, R, pc, 99, 4, pos=pos),
+        "random shared": lambda: kv.kv_select_random_shared((L, S, H, T), Ts, Ps, B, R, pc, 99, 4),
+        "recent": lambda: kv.kv_select_recent((L, S, H, T), Ts, Ps, B, R, pc),
+    }
+    out = {}
+    for name, fn in calls.items():
+        a, b = fn(), fn()
+        if name.startswith(("rotated", "gqa")):
+            a = tuple(written(x) for x in a) if isinstance(a, tuple) else written(a)
+            b = tuple(written(x) for x in b) if isinstance(b, tuple) else written(b)
+        same(a, b, name)
+        out[name] = a
+    zmax, head = out["gqa rotated paged"]
+    u1 = kv.kv_select_union(head, zmax, Ts, Ps, B, R, pc)
+    same(u1, kv.kv_select_union(head, zmax, Ts, Ps, B, R, pc), "union")
+    kept, nk = out["random"]
+    a1 = kv.kv_audit_kept(kept, nk, Ts, Ps, B, R, pc, T)
+    same(a1, kv.kv_audit_kept(kept, nk, Ts, Ps, B, R, pc, T), "audit")
+    assert int(a1.sum()) == 0
+    oc = max(B, pc)                 # a prompt longer than the budget is kept whole
+    outs = []
+    for _ in range(2):              # rows past n_kept are not written: start both from zeros
+        Ko = torch.zeros((L, S, H, oc, d), dtype=K.dtype, device=DEV)
+        Vo, Po = torch.zeros_like(Ko), torch.zeros((L, S, H, oc), dtype=torch.int32, device=DEV)
+        kv.kv_compact(K, V, kept, nk, Ts, oc, pos=pos, K_out=Ko, V_out=Vo, pos_out=Po)
+        outs.append((Ko.view(torch.int16), Vo.view(torch.int16), Po))
+    same(outs[0], outs[1], "compact")
+    Ka, Va, Pa = K.clone(), V.clone(), pos.clone()
+    Kb, Vb, Pb = K.clone(), V.clone(), pos.clone()
+    kv.kv_compact_inplace(Ka, Va, kept, nk, Ts, pos=Pa)
+    kv.kv_compact_inplace(Kb, Vb, kept, nk, Ts, pos=Pb)
+    same((Ka.view(torch.int16), Va.view(torch.int16), Pa), (Kb.view(torch.int16), Vb.view(torch.int16), Pb), "in place")
+    log("[determinism] all bit-identical")
