@@ -177,6 +177,6 @@ def select_union(head_scores, combined, T: int, P: int, B: int, R: int, k: Optio
         order = np.lexsort((slots, -v))
         union.update(int(x) for x in slots[order[:k]])
     c = canonical_scores(np.asarray(combined)[:part.T])[part.e_lo:part.e_hi]
-    in_u = np.array([int(x) in union for x in slots])
+    in_u = np.array([int(x) in union for x in slots], dtype=bool)   # bool also when the range is empty
     order = np.lexsort((slots, -c, ~in_u))   # union first, then combined score desc, then slot asc
     return _assemble(part, slots[order[:part.n_sel]])

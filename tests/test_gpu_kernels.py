@@ -746,6 +746,10 @@ UNION_CASES = [
     ("union-ragged-rows", 2999, [2999, 2500], [7, 0], 700, 9, 3, 0, "specials"),   # t_cap % 4 != 0
     ("union-20k-ragged-rows", 20001, [20001], [300], 2048, 64, 4, 0, "ties"),
     ("union-g64", 4000, [4000, 2500], [100, 0], 1000, 32, 64, 0, "normal"),   # the largest group
+    # the prompt is the whole cache (empty evictable range) beside a sequence with none, and a
+    # prompt exactly the budget
+    ("union-prompt-whole-cache", 3000, [3000, 2600, 1000], [3000, 2600, 0], 2048, 128, 4, 0, "normal"),
+    ("union-prompt-equals-budget", 3000, [3000], [2048], 2048, 128, 4, 0, "ties"),
     # past 65536 slots: the re-reading kernel with the union as a bit per slot in LDS
     ("union-stream-70k-g4", 70000, [70000, 65537], [1024, 0], 3072, 128, 4, 0, "normal"),
     ("union-stream-128k-g8-ties", 131072, [131072, 100000], [2048, 10], 4096, 128, 8, 0, "ties"),
