@@ -1,13 +1,14 @@
 """Property tests of the oracle over random tiny heads (CPU only): the partition arithmetic, the
-selectors' structure and ranking rule (stated a second way, with Python's own sort), and hole
-filling against the gather."""
+selectors' structure and ranking rule (stated a second way, with Python's own sort), hole filling
+against the gather, and the score's three statements (literal RoPE dot product, series, fold), its
+dependence on t - p only, and its post-RoPE form."""
 import math
 
 import numpy as np
 from hypothesis import given, settings, strategies as st
 
-from oracle import (compact, compact_holes, partition, random_uniforms, select_random, select_recent, select_topk,
-                    select_union)
+from oracle import (compact, compact_holes, partition, random_uniforms, rope_rotate, score_folded, score_literal,
+                    score_rotated, score_series, select_random, select_recent, select_topk, select_union)
 
 SETTINGS = settings(max_examples=80, deadline=None)
 
@@ -139,3 +140,65 @@ def test_hole_filling_is_a_permutation_of_the_gather(shape, seed):
             assert hk[j, 0] == 2 * j
     assert all(src >= n > dst for src, dst in moves)
     assert len(moves) == sum(1 for j in kept if j >= n)
+
+
+# ---------------------------------------------------------------- scores ----
+score_inputs = st.tuples(
+    st.sampled_from([2, 4, 6, 8, 16]),                       # head_dim
+    st.integers(1, 6),                                       # keys
+    st.sampled_from([1e4, 1e6, 500.0]),                      # theta
+    st.lists(st.integers(0, 70000), min_size=1, max_size=5),  # offsets
+    st.integers(0, 2 ** 31 - 1),                             # value seed
+    st.integers(0, 100000),                                  # current position
+)
+
+
+def _draw(d, n, seed, t):
+    r = np.random.default_rng(seed)
+    K = r.standard_normal((n, d))
+    q = r.standard_normal(d)
+    pos = r.integers(0, t + 1, n)
+    return K, q, pos
+
+
+@SETTINGS
+@given(score_inputs)
+def test_series_and_fold_equal_the_literal_score(args):
+    d, n, theta, deltas, seed, t = args
+    K, q, pos = _draw(d, n, seed, t)
+    lit = score_literal(K, pos, q, t, theta, deltas)
+    scale = np.linalg.norm(q) * np.linalg.norm(K, axis=1) + 1e-300
+    # three statements of one quantity agree to a few ulps of the angles they reduce
+    for other in (score_series(K, pos, q, t, theta, deltas), score_folded(K, pos, q, t, theta, deltas)):
+        assert np.all(np.abs(other - lit) <= 1e-9 * scale), (other, lit)
+
+
+@SETTINGS
+@given(score_inputs, st.integers(-5000, 5000))
+def test_score_depends_on_t_minus_p_only(args, shift):
+    d, n, theta, deltas, seed, t = args
+    K, q, pos = _draw(d, n, seed, t)
+    if t + shift < 0 or np.any(pos + shift < 0):
+        return
+    a = score_folded(K, pos, q, t, theta, deltas)
+    b = score_folded(K, pos + shift, q, t + shift, theta, deltas)
+    scale = np.linalg.norm(q) * np.linalg.norm(K, axis=1) + 1e-300
+    assert np.all(np.abs(a - b) <= 1e-9 * scale)
+
+
+@SETTINGS
+@given(score_inputs, st.sampled_from(["interleaved", "half"]))
+def test_rotated_keys_give_the_pre_rope_score(args, style):
+    d, n, theta, deltas, seed, t = args
+    K, q, _ = _draw(d, n, seed, t)
+    slots = np.arange(n)
+    if style == "interleaved":
+        ref = score_literal(K, slots, q, t, theta, deltas)
+        got = score_rotated(rope_rotate(K, slots, theta, style), q, t, theta, deltas, style)
+    else:
+        # half-split storage is the interleaved layout under a fixed permutation of coordinates
+        perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+        ref = score_literal(K, slots, q, t, theta, deltas)
+        got = score_rotated(rope_rotate(K[:, perm], slots, theta, style), q[perm], t, theta, deltas, style)
+    scale = np.linalg.norm(q) * np.linalg.norm(K, axis=1) + 1e-300
+    assert np.all(np.abs(got - ref) <= 1e-9 * scale)
