@@ -1043,3 +1043,49 @@ def test_every_other_entry_point_is_deterministic():
     kv.kv_compact_inplace(Kb, Vb, kept, nk, Ts, pos=Pb)
     same((Ka.view(torch.int16), Va.view(torch.int16), Pa), (Kb.view(torch.int16), Vb.view(torch.int16), Pb), "in place")
     log("[determinism] all bit-identical")
+
+
+@pytest.mark.parametrize("sweep", range(16))
+def test_selectors_random_sweep(sweep):
+    # random ragged batches (lengths, prompts, budget, window and cache capacity drawn per sweep,
+    # crossing the register tiers): top-k on scores with ties and special values, random with and
+    # without positions, recency and union, every head bit-exact against the oracle
+    r = rng(4242, sweep)
+    t_cap = int(r.choice([37, 300, 1029, 4096, 9000, 20001, 32768, 40000]))
+    S, H, G = int(r.integers(1, 9)), 2, int(r.integers(1, 5))
+    B = int(r.integers(1, max(2, t_cap)))
+    R = int(r.integers(0, 200))
+    Ts = r.integers(0, t_cap + 1, S).astype(np.int32)
+    Ts[0] = t_cap
+    Ps = np.minimum(r.integers(0, max(1, t_cap // 2), S), Ts).astype(np.int32)
+    pc = int(Ps.max())
+    log(f"[sweep {sweep}] t_cap={t_cap} S={S} B={B} R={R} G={G} T={Ts.tolist()} P={Ps.tolist()}")
+    sc = random_scores(700 + sweep, (1, S, H, t_cap), ties=0.2, specials=True)
+    hs = random_scores(800 + sweep, (1, S, H, G, t_cap), ties=0.3, specials=sweep % 2 == 0)
+    pos = np.sort(r.integers(0, 2 ** 31 - 1, (1, S, H, t_cap)), axis=-1).astype(np.int32)
+    seed, event = int(r.integers(0, 2 ** 63)), int(r.integers(0, 1000))
+    Tt, Pt = _i32(Ts), _i32(Ps)
+    got = {
+        "topk": kv.kv_select_topk(torch.from_numpy(sc).to(DEV), Tt, Pt, B, R, pc),
+        "random": kv.kv_select_random((1, S, H, t_cap), Tt, Pt, B, R, pc, seed, event),
+        "random-pos": kv.kv_select_random((1, S, H, t_cap), Tt, Pt, B, R, pc, seed, event, pos=_i32(pos)),
+        "recent": kv.kv_select_recent((1, S, H, t_cap), Tt, Pt, B, R, pc),
+        "union": kv.kv_select_union(torch.from_numpy(hs).to(DEV), torch.from_numpy(sc).to(DEV), Tt, Pt, B, R, pc),
+    }
+    got = {k: (v[0].cpu().numpy(), v[1].cpu().numpy()) for k, v in got.items()}
+    for s in range(S):
+        T, P = int(Ts[s]), int(Ps[s])
+        for h in range(H):
+            want = {
+                "topk": oracle.select_topk(sc[0, s, h, :T], T, P, B, R),
+                "random": oracle.select_random(T, P, B, R, None, seed, event, 0, h, s),
+                "random-pos": oracle.select_random(T, P, B, R, pos[0, s, h, :T], seed, event, 0, h, s),
+                "recent": oracle.select_recent(T, P, B, R),
+                "union": oracle.select_union(hs[0, s, h, :, :T], sc[0, s, h, :T], T, P, B, R),
+            }
+            for name, ref in want.items():
+                kept, nk = got[name]
+                assert int(nk[s]) == ref.size, (name, s, h)
+                assert np.array_equal(kept[0, s, h, :ref.size], ref), (name, s, h)
+                assert np.all(kept[0, s, h, ref.size:] == -1), (name, s, h)
+    log(f"[sweep {sweep}] all heads bit-exact")
