@@ -1089,3 +1089,87 @@ def test_selectors_random_sweep(sweep):
                 assert np.array_equal(kept[0, s, h, :ref.size], ref), (name, s, h)
                 assert np.all(kept[0, s, h, ref.size:] == -1), (name, s, h)
     log(f"[sweep {sweep}] all heads bit-exact")
+
+
+@pytest.mark.parametrize("sweep", range(16))
+def test_scores_random_sweep(sweep):
+    # random shapes within each call's limits: dtype, head_dim (every multiple of a 16-byte piece),
+    # lengths, theta, offsets, explicit positions, the norm term, pairing and group size; every head
+    # of tri_score, tri_score_rotated, tri_score_gqa (scores and z) and tri_score_gqa_rotated
+    # against the oracle
+    r = rng(4343, sweep)
+    dtype = "bf16" if sweep % 3 else "f32"
+    step = 8 if dtype == "bf16" else 4
+    d = int(r.integers(1, (256 if sweep % 2 else 128) // step + 1)) * step   # half the draws at most 128
+    S, H = int(r.integers(1, 4)), int(r.integers(1, 3))
+    t_cap = int(r.integers(1, 2500))
+    Ts = r.integers(0, t_cap + 1, S).astype(np.int32)
+    Ts[0] = t_cap
+    t_cur = (Ts + r.integers(0, 50, S)).astype(np.int32)
+    theta = float(r.choice([1e4, 5e5, 1e6]))
+    D = sorted(set(r.integers(0, 65537, int(r.integers(1, 18))).tolist()))
+    with_pos, norm = bool(r.integers(0, 2)), bool(r.integers(0, 2))
+    style = "half" if r.integers(0, 2) else "interleaved"
+    pc = d * (2 if dtype == "bf16" else 4) // 16
+    if pc < 2 or pc & (pc - 1):
+        style = "interleaved"      # half-split rows need a power-of-two number (>= 2) of pieces
+    G = int(r.integers(1, 9))
+    log(f"[score sweep {sweep}] {dtype} d={d} S={S} H={H} t_cap={t_cap} T={Ts.tolist()} |D|={len(D)} "
+        f"pos={with_pos} norm={norm} style={style} G={G}")
+    K = (r.standard_normal((1, 1, H, 1, d)) + 0.3 * r.standard_normal((1, S, H, t_cap, d))).astype(np.float32)
+    Kd = _to_dev_keys(K, dtype)
+    Kh = keys_f64(_host_keys(Kd, dtype), dtype)
+    pos = np.sort(r.integers(0, 2 ** 20, (1, S, H, t_cap)), axis=-1).astype(np.int32) if with_pos else None
+    pos_d = None if pos is None else _i32(pos)
+    qb = r.standard_normal((1, H, d)).astype(np.float32)
+    nu = r.standard_normal((1, H, G, d)).astype(np.float32)
+
+    def magnitudes(c, pairing):
+        re, im = oracle.band_slices(d, pairing)
+        return (np.hypot(c[..., re], c[..., im]) / r.uniform(0.6, 1.0, c.shape[:-1] + (d // 2,))).astype(np.float32)
+
+    qabs_i = magnitudes(qb, "interleaved") if norm else None
+    qabs_s = magnitudes(qb, style) if norm else None
+    tc, Tt = _i32(t_cur), _i32(Ts)
+    dev = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
+    got_pre = kv.tri_score(Kd, dev(qb), tc, Tt, theta, D, pos=pos_d, qabs=dev(qabs_i)).cpu().numpy()
+    pieces = d * (2 if dtype == "bf16" else 4) // 16
+    # half-split rows: a power-of-two number (>= 2) of 16-byte pieces, so a band's halves sit in
+    # lanes g and g ^ (lanes / 2)
+    half_ok = style == "interleaved" or (pieces >= 2 and pieces & (pieces - 1) == 0)
+    got_rot = kv.tri_score_rotated(Kd, dev(qb), tc, Tt, theta, D, rope_style=style,
+                                   qabs=dev(qabs_s)).cpu().numpy() if half_ok else None
+    gqa_ok = d <= (256 if dtype == "bf16" else 128)
+    qabs_g = magnitudes(nu, "interleaved") if norm else None
+    got_gqa = kv.tri_score_gqa(Kd, dev(nu), tc, Tt, theta, D, pos=pos_d, qabs=dev(qabs_g)) if gqa_ok else None
+    lpk = 1 << (pieces - 1).bit_length()
+    grot_ok = lpk <= 16 and (style == "interleaved" or (lpk == pieces and lpk >= 2))
+    qabs_gs = magnitudes(nu, style) if norm else None
+    got_grot = kv.tri_score_gqa_rotated(Kd, dev(nu), tc, Tt, theta, D, rope_style=style,
+                                        qabs=dev(qabs_gs)) if grot_ok else None
+    worst = 0.0
+    for s in range(S):
+        T, t = int(Ts[s]), int(t_cur[s])
+        for h in range(H):
+            kf, ps = Kh[0, s, h, :T], None if pos is None else pos[0, s, h, :T]
+            ref = oracle.score_full(kf, ps, qb[0, h], qabs_i[0, h], t, theta, D) if norm else \
+                oracle.score_literal(kf, ps, qb[0, h], t, theta, D)
+            worst = max(worst, assert_scores(got_pre[0, s, h, :T], ref, f"tri_score {s} {h}"))
+            if got_rot is not None:
+                ref = oracle.score_rotated(kf, qb[0, h], t, theta, D, style, None if qabs_s is None else qabs_s[0, h])
+                worst = max(worst, assert_scores(got_rot[0, s, h, :T], ref, f"rotated {s} {h}"))
+            if got_gqa is not None:
+                z, per = oracle.score_gqa(kf, ps, nu[0, h], t, theta, D, None if qabs_g is None else qabs_g[0, h])
+                zg, hg = got_gqa[0][0, s, h, :T].cpu().numpy(), got_gqa[1][0, s, h, :, :T].cpu().numpy()
+                for g in range(G):
+                    worst = max(worst, assert_scores(hg[g], per[g], f"gqa {s} {h} g{g}"))
+                assert_z(zg, z, f"gqa z {s} {h}")
+            if got_grot is not None:
+                z, per = oracle.score_gqa_rotated(kf, nu[0, h], t, theta, D, style,
+                                                  None if qabs_gs is None else qabs_gs[0, h])
+                zg, hg = got_grot[0][0, s, h, :T].cpu().numpy(), got_grot[1][0, s, h, :, :T].cpu().numpy()
+                for g in range(G):
+                    worst = max(worst, assert_scores(hg[g], per[g], f"gqa rotated {s} {h} g{g}"))
+                assert_z(zg, z, f"gqa rotated z {s} {h}")
+    log(f"[score sweep {sweep}] rotated={got_rot is not None} gqa={got_gqa is not None} "
+        f"gqa_rotated={got_grot is not None}: worst scaled error {worst:.2e}")
