@@ -1173,3 +1173,51 @@ def test_scores_random_sweep(sweep):
                 assert_z(zg, z, f"gqa rotated z {s} {h}")
     log(f"[score sweep {sweep}] rotated={got_rot is not None} gqa={got_gqa is not None} "
         f"gqa_rotated={got_grot is not None}: worst scaled error {worst:.2e}")
+
+
+@pytest.mark.parametrize("sweep", range(12))
+def test_compaction_random_sweep(sweep):
+    # random row widths (every multiple of a 16-byte piece up to 256 elements), dtypes, lengths,
+    # budgets and positions: the gather and in-place hole filling bit-exact against the oracle, on
+    # kept lists from random selection
+    r = rng(4444, sweep)
+    dtype = "bf16" if sweep % 2 else "f32"
+    step = 8 if dtype == "bf16" else 4
+    d = int(r.integers(1, 256 // step + 1)) * step
+    S, H = int(r.integers(1, 4)), int(r.integers(1, 3))
+    t_cap = int(r.integers(1, 3000))
+    Ts = r.integers(0, t_cap + 1, S).astype(np.int32)
+    Ts[0] = t_cap
+    Ps = np.minimum(r.integers(0, max(1, t_cap // 3), S), Ts).astype(np.int32)
+    B, R = int(r.integers(1, max(2, t_cap))), int(r.integers(0, 100))
+    with_pos = bool(r.integers(0, 2))
+    log(f"[compact sweep {sweep}] {dtype} d={d} S={S} H={H} t_cap={t_cap} T={Ts.tolist()} P={Ps.tolist()} "
+        f"B={B} R={R} pos={with_pos}")
+    Kf = r.standard_normal((1, S, H, t_cap, d)).astype(np.float32)
+    Vf = r.standard_normal((1, S, H, t_cap, d)).astype(np.float32)
+    Kd, Vd = _to_dev_keys(Kf, dtype), _to_dev_keys(Vf, dtype)
+    Kh, Vh = _host_keys(Kd, dtype), _host_keys(Vd, dtype)
+    pos = np.sort(r.integers(0, 2 ** 30, (1, S, H, t_cap)), axis=-1).astype(np.int32) if with_pos else None
+    pd = None if pos is None else _i32(pos)
+    kept, nk = kv.kv_select_random((1, S, H, t_cap), _i32(Ts), _i32(Ps), B, R, int(Ps.max()), 17 + sweep, 2)
+    oc = max(B, int(Ps.max()), 1)
+    Ko, Vo, Po = kv.kv_compact(Kd, Vd, kept, nk, _i32(Ts), oc, pos=pd)
+    Ko, Vo, Po = _host_keys(Ko, dtype), _host_keys(Vo, dtype), Po.cpu().numpy()
+    kv.kv_compact_inplace(Kd, Vd, kept, nk, _i32(Ts), pos=pd)
+    Ki, Vi = _host_keys(Kd, dtype), _host_keys(Vd, dtype)
+    Pi = None if pd is None else pd.cpu().numpy()
+    kh, nkh = kept.cpu().numpy(), nk.cpu().numpy()
+    for s in range(S):
+        n, T = int(nkh[s]), int(Ts[s])
+        for h in range(H):
+            ks = kh[0, s, h, :n]
+            p = None if pos is None else pos[0, s, h, :T]
+            rk, rv, rp = oracle.compact(Kh[0, s, h, :T], Vh[0, s, h, :T], p, ks)
+            assert np.array_equal(Ko[0, s, h, :n], rk) and np.array_equal(Vo[0, s, h, :n], rv), ("gather", s, h)
+            assert np.array_equal(Po[0, s, h, :n], rp), ("gather positions", s, h)
+            hk, hv, hp, _ = oracle.compact_holes(Kh[0, s, h, :T], Vh[0, s, h, :T], p, ks)
+            assert np.array_equal(Ki[0, s, h, :n], hk) and np.array_equal(Vi[0, s, h, :n], hv), ("in place", s, h)
+            assert np.array_equal(Ki[0, s, h, n:], Kh[0, s, h, n:]), ("in place tail", s, h)
+            if Pi is not None:
+                assert np.array_equal(Pi[0, s, h, :n], hp), ("in place positions", s, h)
+    log(f"[compact sweep {sweep}] bit-exact")
