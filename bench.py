@@ -668,6 +668,9 @@ def main():
                  "graph_replay_ms": graph_ms,
                  "graph_replay_entries_per_s": None if graph_ms is None else entries / (graph_ms * 1e-3),
                  "kernel_ms": k_ms,
+                 "kernel_share": {k: {"bytes": ab[b] / pass_bytes, "time": k_ms[k] / sum(k_ms.values())}
+                                  for k, b in (("tri_score", "score"), ("kv_select_topk", "select"),
+                                               ("kv_compact", "compact"))},
                  "kernel_gbs": {"tri_score": achieved,
                                 "kv_select_topk": ab["select"] / (k_ms["kv_select_topk"] * 1e-3) / 1e9,
                                 "kv_compact": ab["compact"] / (k_ms["kv_compact"] * 1e-3) / 1e9}},
