@@ -299,7 +299,14 @@ def cpu_baseline(w, K, qb, n_heads: int):
             oracle.compact(kf, kf, None, kept)
         dt = time.perf_counter() - t0
     n = len(host) * T
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": n / dt, "unit": "KV entries/s", "cores": 1, "kind": "oracle",
+            "host_cpu": model, "host_cpus_available": len(os.sched_getaffinity(0)),
             "sample": f"{len(host)} heads (layers 0..{(len(host) - 1) // H}, seq 0, all KV heads) x {T} slots "
                       f"= {n} entries; literal fp64 score + lexsort select + gather, {dt:.1f} s"}
 
