@@ -272,8 +272,9 @@ def other_workloads(args, dev):
     return res
 
 
-def cpu_baseline(w, K, qb, n_heads: int):
-    """The oracle (score -> select -> compact, fp64 NumPy, one thread) on a bounded sample."""
+def cpu_baseline(w, K, qb, n_heads: int, folded: bool = False):
+    """The oracle (score -> select -> compact, fp64 NumPy, one thread) on a bounded sample; the
+    score is the literal RoPE dot product, or with folded=True the oracle's folded statement."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -294,7 +295,8 @@ def cpu_baseline(w, K, qb, n_heads: int):
     with threadpool_limits(1):
         t0 = time.perf_counter()
         for (l, s, h), kf in host:
-            sc = oracle.score_literal(kf, None, qb[l, h], int(w.t_cur[s]), w.theta, w.deltas)
+            score = oracle.score_folded if folded else oracle.score_literal
+            sc = score(kf, None, qb[l, h], int(w.t_cur[s]), w.theta, w.deltas)
             kept = oracle.select_topk(sc, T, P, w.budget, w.recent)
             oracle.compact(kf, kf, None, kept)
         dt = time.perf_counter() - t0
@@ -308,7 +310,8 @@ def cpu_baseline(w, K, qb, n_heads: int):
     return {"value": n / dt, "unit": "KV entries/s", "cores": 1, "kind": "oracle",
             "host_cpu": model, "host_cpus_available": len(os.sched_getaffinity(0)),
             "sample": f"{len(host)} heads (layers 0..{(len(host) - 1) // H}, seq 0, all KV heads) x {T} slots "
-                      f"= {n} entries; literal fp64 score + lexsort select + gather, {dt:.1f} s"}
+                      f"= {n} entries; {'folded' if folded else 'literal'} fp64 score + lexsort select + gather, "
+                      f"{dt:.1f} s"}
 
 
 def main():
@@ -637,10 +640,11 @@ def main():
           f"random select {sel4_ms:.3f} ms, gather {gather_ms:.3f} ms, in place {inplace_ms:.3f} ms "
           f"({movers} rows moved)", file=sys.stderr, flush=True)
 
-    cpu = None
+    cpu = cpu_folded = None
     if args.cpu_heads > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, K, qb, args.cpu_heads)
+        cpu_folded = cpu_baseline(w, K, qb, args.cpu_heads, folded=True)
 
     others = None
     if not args.no_other_workloads:
@@ -696,6 +700,7 @@ def main():
         "periodic_event": periodic,
         "other_workloads": others,
         "cpu_baseline": cpu,
+        "cpu_baseline_folded": cpu_folded,
     }
     print(json.dumps(out))
 
