@@ -33,6 +33,8 @@
 //    coalesced 256-byte store.
 #include "score_params.hpp"
 
+#include <type_traits>
+
 #ifndef KV_SCORE_PIPELINE
 #define KV_SCORE_PIPELINE 1
 #endif
@@ -110,10 +112,10 @@ __device__ __forceinline__ float lane_dot(const uint4 &d, const float2 *v, const
 }
 
 // Norm-term weight of band b: E|q_b| - |q_bar_b| = (1 - R_b) E|q_b|, zero when E|q_b| = 0.
-__device__ __forceinline__ float norm_weight(const float *qabs, float2 q, int b) {
-  const float qa = qabs[b];
+__device__ __forceinline__ float norm_weight_of(float qa, float2 q) {
   return qa > 0.f ? qa - sqrtf(fmaf(q.x, q.x, q.y * q.y)) : 0.f;
 }
+__device__ __forceinline__ float norm_weight(const float *qabs, float2 q, int b) { return norm_weight_of(qabs[b], q); }
 
 // FULL: every lane of a key group holds bands (head_dim fills the LPK lanes exactly).
 template <bool BF16, int LPK, bool POS, bool FULL, bool NORM>
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const Score
   constexpr int NB = kScoreBatchesPerWave;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int g = lane % LPK;
   const int kk = lane / LPK;
   const int head = blockIdx.x / p.chunks_per_head;
@@ -266,68 +268,100 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const Score
   const int lane_off = kk * row_bytes + piece;
   const int step_bytes = KPS * row_bytes;
 
-  auto issue = [&](int nb, uint4(&d)[STEPS]) {
-    const int j0 = wave_first + nb * 64;
-    const int boff = j0 * row_bytes + lane_off;
-    if (j0 + 64 <= T) {
-#pragma unroll
-      for (int t = 0; t < STEPS; ++t) d[t] = ld16(rk, boff, t * step_bytes);
-    } else {
-      // ragged tail: slots at or past T read an in-range row; their sums feed unstored scores
-#pragma unroll
-      for (int t = 0; t < STEPS; ++t) {
-        const bool in = j0 + t * KPS + kk < T;
-        d[t] = ld16(rk, in ? boff + t * step_bytes : piece, 0);
-      }
-    }
-  };
-  uint4 da[STEPS], db[STEPS];
-  issue(0, da);
-
+  // The per-lane set-up inputs (query centre, fold coefficient, frequency, norm weight) are read
+  // before the key batches go out: the load counter completes in order, so waiting for an input
+  // read after the keys would also wait for the keys.
   const double tq = static_cast<double>(p.t_cur[s]);
-  float2 v[BPL], w[BPL];
-  float cn[BPL];
   const size_t lh = static_cast<size_t>(l) * p.H + h;
   const float2 *qrow = reinterpret_cast<const float2 *>(p.qbar + lh * p.d);
-  const double m0 = tq - static_cast<double>(wave_first + kk);
+  float2 qv[BPL], av[BPL];
+  double rv[BPL];
+  float qa[BPL];
 #pragma unroll
   for (int i = 0; i < BPL; ++i) {
     const int b = g * BPL + i;
+    qv[i] = av[i] = make_float2(0.f, 0.f);
+    rv[i] = 0.0;
+    qa[i] = 0.f;
     if (live) {
-      const double rev = p.rev[b];
-      w[i] = cis_rev(rev, -static_cast<double>(KPS));
-      v[i] = cmul(cmul(qrow[b], p.A[b]), cis_rev(rev, m0));
-      cn[i] = NORM ? norm_weight(p.qabs + lh * p.F, qrow[b], b) : 0.f;
-    } else {
-      w[i] = make_float2(1.f, 0.f);
-      v[i] = make_float2(0.f, 0.f);
-      cn[i] = 0.f;
+      qv[i] = qrow[b];
+      av[i] = p.A[b];
+      rv[i] = p.rev[b];
+      if (NORM) qa[i] = p.qabs[lh * p.F + b];
     }
   }
+  // The body, generated twice: for a wave whose batches all lie below T (every wave of a head but
+  // its last) the loads take no branch, so the compiler can count each wait to the batch it needs.
+  auto body = [&](auto all_below_T) {
+    constexpr bool ALL = decltype(all_below_T)::value;
+    auto issue = [&](int nb, uint4(&d)[STEPS]) {
+      const int j0 = wave_first + nb * 64;
+      const int boff = j0 * row_bytes + lane_off;
+      if (ALL || j0 + 64 <= T) {
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) d[t] = ld16(rk, boff, t * step_bytes);
+      } else {
+        // ragged tail: slots at or past T read an in-range row; their sums feed unstored scores
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+          const bool in = j0 + t * KPS + kk < T;
+          d[t] = ld16(rk, in ? boff + t * step_bytes : piece, 0);
+        }
+      }
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 da[STEPS], db[STEPS];
+    issue(0, da);
+    if (NB > 1) issue(1, db);
+    __builtin_amdgcn_sched_barrier(0);
 
-  auto consume = [&](int nb, const uint4(&d)[STEPS]) {
-    float acc[STEPS];
+    float2 v[BPL], w[BPL];
+    float cn[BPL];
+    const double m0 = tq - static_cast<double>(wave_first + kk);
 #pragma unroll
-    for (int t = 0; t < STEPS; ++t) {
-      const float a = lane_dot<BF16, NORM>(d[t], v, cn);
-      acc[t] = FULL ? a : (live ? a : 0.f);
-#pragma unroll
-      for (int i = 0; i < BPL; ++i) v[i] = cmul(v[i], w[i]);
+    for (int i = 0; i < BPL; ++i) {
+      if (live) {
+        const double rev = rv[i];
+        w[i] = cis_rev(rev, -static_cast<double>(KPS));
+        v[i] = cmul(cmul(qv[i], av[i]), cis_rev(rev, m0));
+        cn[i] = NORM ? norm_weight_of(qa[i], qv[i]) : 0.f;
+      } else {
+        w[i] = make_float2(1.f, 0.f);
+        v[i] = make_float2(0.f, 0.f);
+        cn[i] = 0.f;
+      }
     }
-    const float sc = reduce_scatter<STEPS>(acc, g);
-    const int jj = wave_first + nb * 64 + g * KPS + kk;
-    if (jj < T) st_score(p.scores + slot0 + jj, sc);
+
+    auto consume = [&](int nb, const uint4(&d)[STEPS]) {
+      float acc[STEPS];
+#pragma unroll
+      for (int t = 0; t < STEPS; ++t) {
+        const float a = lane_dot<BF16, NORM>(d[t], v, cn);
+        acc[t] = FULL ? a : (live ? a : 0.f);
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) v[i] = cmul(v[i], w[i]);
+      }
+      const float sc = reduce_scatter<STEPS>(acc, g);
+      const int jj = wave_first + nb * 64 + g * KPS + kk;
+      if (jj < T) st_score(p.scores + slot0 + jj, sc);
+    };
+
+    // The next batch is issued whether or not it holds live slots (a batch past T takes the ragged
+    // path and reads in-range rows whose sums are not stored): with a load that is always issued,
+    // each wait counts only the older batch, where a conditional issue made the compiler wait for
+    // every load in flight before the first batch's arithmetic.
+#pragma unroll
+    for (int nb = 0; nb < NB; nb += 2) {
+      if (nb >= nbat) break;
+      if (nb > 0 && nb + 1 < NB) issue(nb + 1, db);   // batch 1 went out with batch 0
+      consume(nb, da);
+      if (nb + 1 >= nbat) break;
+      if (nb + 2 < NB) issue(nb + 2, da);
+      consume(nb + 1, db);
+    }
   };
-
-#pragma unroll
-  for (int nb = 0; nb < NB; nb += 2) {
-    if (nb >= nbat) break;
-    if (nb + 1 < nbat) issue(nb + 1, db);
-    consume(nb, da);
-    if (nb + 1 >= nbat) break;
-    if (nb + 2 < nbat) issue(nb + 2, da);
-    consume(nb + 1, db);
-  }
+  if (wave_first + NB * 64 <= T) body(std::true_type{});
+  else body(std::false_type{});
 }
 
 template <bool BF16, bool POS, bool FULL, bool NORM>
