@@ -149,20 +149,53 @@ __global__ __launch_bounds__(kScoreThreads) void score_rotated_kernel(const RotS
   const double tq = static_cast<double>(p.t_cur[s]);
   float wgt[EPL];
   float cn[EPL];  // norm weight of the band owned by coordinate e (applied once per band)
+  if constexpr (PAGED) {
+    // Paged pools: the inputs of every coordinate are read first (an idle coordinate reads band 0)
+    // and only then combined, so the reads overlap instead of each waiting for the one before
+    // (shuffled 16-slot pool 3.25 -> 3.20 ms; dense heads, whose first rows arrive sooner, measured
+    // 1.6 % slower this way and keep the loop below).
+    float2 qfs[EPL], As[EPL];
+    double revs[EPL];
+    float qas[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int x = g * EPL + e;
-    wgt[e] = 0.f;
-    cn[e] = 0.f;
-    if (!live || x >= p.d) continue;
-    const int f = HALF ? (x < F ? x : x - F) : (x >> 1);
-    const bool is_re = HALF ? (x < F) : ((x & 1) == 0);
-    const float2 qf = HALF ? make_float2(q[f], q[f + F]) : make_float2(q[2 * f], q[2 * f + 1]);
-    const float2 W = cmul(cmul(qf, p.A[f]), cis_rev(p.rev[f], tq));
-    wgt[e] = is_re ? W.x : W.y;
-    if (NORM && is_re) {
-      const float qa = p.qabs[lh * F + f];
-      cn[e] = qa > 0.f ? qa - sqrtf(fmaf(qf.x, qf.x, qf.y * qf.y)) : 0.f;
+    for (int e = 0; e < EPL; ++e) {
+      const int x = g * EPL + e;
+      const bool valid = live && x < p.d;
+      const int f = !valid ? 0 : (HALF ? (x < F ? x : x - F) : (x >> 1));
+      qfs[e] = HALF ? make_float2(q[f], q[f + F]) : make_float2(q[2 * f], q[2 * f + 1]);
+      As[e] = p.A[f];
+      revs[e] = p.rev[f];
+      qas[e] = NORM ? p.qabs[lh * F + f] : 0.f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int x = g * EPL + e;
+      wgt[e] = 0.f;
+      cn[e] = 0.f;
+      if (!live || x >= p.d) continue;
+      const bool is_re = HALF ? (x < F) : ((x & 1) == 0);
+      const float2 qf = qfs[e];
+      const float2 W = cmul(cmul(qf, As[e]), cis_rev(revs[e], tq));
+      wgt[e] = is_re ? W.x : W.y;
+      if (NORM && is_re) cn[e] = qas[e] > 0.f ? qas[e] - sqrtf(fmaf(qf.x, qf.x, qf.y * qf.y)) : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int x = g * EPL + e;
+      wgt[e] = 0.f;
+      cn[e] = 0.f;
+      if (!live || x >= p.d) continue;
+      const int f = HALF ? (x < F ? x : x - F) : (x >> 1);
+      const bool is_re = HALF ? (x < F) : ((x & 1) == 0);
+      const float2 qf = HALF ? make_float2(q[f], q[f + F]) : make_float2(q[2 * f], q[2 * f + 1]);
+      const float2 W = cmul(cmul(qf, p.A[f]), cis_rev(p.rev[f], tq));
+      wgt[e] = is_re ? W.x : W.y;
+      if (NORM && is_re) {
+        const float qa = p.qabs[lh * F + f];
+        cn[e] = qa > 0.f ? qa - sqrtf(fmaf(qf.x, qf.x, qf.y * qf.y)) : 0.f;
+      }
     }
   }
 
