@@ -24,10 +24,12 @@ The binding holds no arithmetic of its own and has no CPU fallback: without
 the built library every call raises.
 """
 from ._lib import KvError, library_path, load as load_library
-from .binding import (gqa_workspace_bytes, kv_audit_kept, kv_compact, kv_compact_inplace, kv_select_random, kv_select_random_shared,
-                      kv_select_recent, kv_select_union, kv_select_topk, tri_score, tri_score_gqa,
+from .binding import (gqa_workspace_bytes, kv_audit_kept, kv_compact, kv_compact_inplace, kv_select_random,
+                      kv_select_random_shared, kv_select_recent, kv_select_union, kv_select_topk,
+                      score_workspace_bytes, select_workspace_bytes, tri_score, tri_score_gqa,
                       tri_score_gqa_rotated, tri_score_rotated)
 
-__all__ = ["tri_score", "tri_score_rotated", "tri_score_gqa", "tri_score_gqa_rotated", "gqa_workspace_bytes", "kv_select_topk", "kv_select_random", "kv_compact",
-           "kv_select_union", "kv_select_random_shared", "kv_select_recent", "kv_compact_inplace", "kv_audit_kept", "KvError", "library_path",
-           "load_library"]
+__all__ = ["tri_score", "tri_score_rotated", "tri_score_gqa", "tri_score_gqa_rotated", "gqa_workspace_bytes",
+           "score_workspace_bytes", "select_workspace_bytes", "kv_select_topk", "kv_select_random", "kv_compact",
+           "kv_select_union", "kv_select_random_shared", "kv_select_recent", "kv_compact_inplace", "kv_audit_kept",
+           "KvError", "library_path", "load_library"]

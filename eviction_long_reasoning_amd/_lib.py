@@ -11,7 +11,9 @@ import threading
 
 from .build import LIB_PATH
 
-KV_OK, KV_EINVAL, KV_EDTYPE, KV_ESHAPE, KV_EHIP = 0, -1, -2, -3, -5
+KV_OK, KV_EINVAL, KV_EDTYPE, KV_ESHAPE, KV_EWORKSPACE, KV_EHIP = 0, -1, -2, -3, -4, -5
+KV_DEV_SEQ_LEN, KV_DEV_PROMPT_LEN, KV_DEV_POS_ORDER = 0x1, 0x2, 0x4
+KV_WORKSPACE_HEADER = 256
 KV_F32, KV_BF16 = 0, 1
 KV_ROPE_INTERLEAVED, KV_ROPE_HALF = 0, 1
 
@@ -52,8 +54,11 @@ _I32 = ctypes.c_int32
 _SIGNATURES = {
     "kv_version": (_I32, []),
     "kv_status_string": (ctypes.c_char_p, [_I32]),
+    "kv_device_checks": (_I32, []),
     "tri_score": (_I32, [ctypes.POINTER(KvShape), _P, _P, _P, _P, _P, ctypes.c_double, ctypes.POINTER(_I32), _I32,
-                         _P, _P]),
+                         _P, _P, ctypes.c_size_t, _P]),
+    "kv_score_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(KvShape), _I32]),
+    "kv_select_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(KvShape), _I32]),
     "tri_score_rotated": (_I32, [ctypes.POINTER(KvShape), _P, ctypes.POINTER(KvPaged), _I32, _P, _P, _P,
                                  ctypes.c_double, ctypes.POINTER(_I32), _I32, _P, _P]),
     "tri_score_gqa": (_I32, [ctypes.POINTER(KvShape), _P, _P, _I32, _P, _P, _P, ctypes.c_double,
@@ -61,13 +66,14 @@ _SIGNATURES = {
     "kv_score_gqa_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(KvShape), _I32]),
     "tri_score_gqa_rotated": (_I32, [ctypes.POINTER(KvShape), _P, ctypes.POINTER(KvPaged), _I32, _I32, _P, _P, _P,
                                      ctypes.c_double, ctypes.POINTER(_I32), _I32, _P, _P, _P, ctypes.c_size_t, _P]),
-    "kv_select_topk": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, _P, _I32, _P, _P]),
+    "kv_select_topk": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, _P, _I32, _P, _P,
+                              ctypes.c_size_t, _P]),
     "kv_select_random": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, ctypes.c_uint64,
-                                ctypes.c_uint32, _P, _I32, _P, _P]),
+                                ctypes.c_uint32, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
     "kv_select_union": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _I32, _I32, _P, _P, _P, _I32, _P,
                                _P]),
     "kv_select_random_shared": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, ctypes.c_uint64,
-                                       ctypes.c_uint32, _P, _I32, _P, _P]),
+                                       ctypes.c_uint32, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
     "kv_audit_kept": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, _I32, _P, _P, _P]),
     "kv_select_recent": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, _I32, _P, _P]),
     "kv_compact_inplace": (_I32, [ctypes.POINTER(KvShape), _P, _P, _P, _P, _I32, _P, _P]),
@@ -79,8 +85,23 @@ _lib = None
 
 
 def library_path() -> str:
-    """The library to load: ``KVEVICT_LIB`` if set (an alternative build), else the in-tree one."""
+    """The library to load: ``KVEVICT_LIB`` if set (an alternative build, such as the one with
+    device checks, ``libkvevict_debug.so``), else the in-tree release build."""
     return os.environ.get("KVEVICT_LIB") or LIB_PATH
+
+
+def open_library(path: str):
+    """Load the library at ``path`` and declare the signatures of its entry points."""
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP kernels first "
+            "(python -m eviction_long_reasoning_amd.build or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
 
 
 def load():
@@ -90,17 +111,7 @@ def load():
         return _lib
     with _lock:
         if _lib is None:
-            path = library_path()
-            if not os.path.exists(path):
-                raise RuntimeError(
-                    f"{path} is missing: build the HIP kernels first "
-                    "(python -m eviction_long_reasoning_amd.build or __graft_entry__.build())")
-            lib = ctypes.CDLL(path)
-            for name, (res, args) in _SIGNATURES.items():
-                fn = getattr(lib, name)
-                fn.restype = res
-                fn.argtypes = args
-            _lib = lib
+            _lib = open_library(library_path())
     return _lib
 
 

@@ -11,6 +11,8 @@ Tensor layouts (head-major, see include/kvevict.h):
   scores      [L, S, H, t_cap]     float32
   kept        [L, S, H, b_cap]     int32
   seq_len, prompt_len, t_cur, n_kept  [S] int32
+  workspace   uint8 GPU tensor of at least the matching *_workspace_bytes query (allocated per
+              call when omitted; pass one to keep calls allocation-free)
 """
 from __future__ import annotations
 
@@ -56,9 +58,29 @@ def _shape(L, S, H, d, t_cap, dtype_code, seq_len_ptr) -> _lib.KvShape:
     return _lib.KvShape(int(L), int(S), int(H), int(d), int(t_cap), int(dtype_code), seq_len_ptr)
 
 
+def _workspace(ws: Optional[torch.Tensor], need: int, device):
+    """(tensor, pointer, bytes) of the caller's workspace, or of a fresh one of ``need`` bytes."""
+    if ws is None:
+        ws = torch.empty((max(int(need), _lib.KV_WORKSPACE_HEADER),), dtype=torch.uint8, device=device)
+    return ws, _dev_ptr(ws, "workspace", torch.uint8, None, device), ws.numel()
+
+
+def score_workspace_bytes(L: int, S: int, H: int, t_cap: int, d: int, dtype: torch.dtype, n_delta: int) -> int:
+    """Workspace bytes ``tri_score`` needs (0 for a shape or offset count it rejects)."""
+    shape = _shape(L, S, H, d, t_cap, _DT[dtype], None)
+    return int(_lib.load().kv_score_workspace_bytes(ctypes.byref(shape), int(n_delta)))
+
+
+def select_workspace_bytes(L: int, S: int, H: int, t_cap: int, b_cap: int) -> int:
+    """Workspace bytes ``kv_select_topk`` / ``kv_select_random(_shared)`` need (0 if rejected)."""
+    shape = _shape(L, S, H, 0, t_cap, 0, None)
+    return int(_lib.load().kv_select_workspace_bytes(ctypes.byref(shape), int(b_cap)))
+
+
 def tri_score(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len: torch.Tensor,
               rope_theta: float, deltas: Sequence[int], pos: Optional[torch.Tensor] = None,
-              out: Optional[torch.Tensor] = None, qabs: Optional[torch.Tensor] = None) -> torch.Tensor:
+              out: Optional[torch.Tensor] = None, qabs: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Offset-averaged RoPE query-centre score of every cached key (fp32 [L,S,H,t_cap]).
 
     With ``qabs`` ([L,H,d/2] fp32, mean query magnitude per band) the norm-based term is added.
@@ -79,7 +101,9 @@ def tri_score(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len:
     dl = [int(x) for x in deltas]
     arr = (ctypes.c_int32 * max(1, len(dl)))(*dl)
     shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
-    _invoke("tri_score", dev, ctypes.byref(shape), kp, pp, qp, ap, tp, float(rope_theta), arr, len(dl), op)
+    need = int(_lib.load().kv_score_workspace_bytes(ctypes.byref(shape), len(dl)))
+    workspace, wp, wb = _workspace(workspace, need, dev)
+    _invoke("tri_score", dev, ctypes.byref(shape), kp, pp, qp, ap, tp, float(rope_theta), arr, len(dl), op, wp, wb)
     return out
 
 
@@ -158,11 +182,8 @@ def tri_score_gqa(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_
     op = _dev_ptr(out, "out", torch.float32, (L, S, H, t_cap), dev)
     hp = _dev_ptr(head_out, "head_out", torch.float32, (L, S, H, G, t_cap), dev)
     shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
-    lib = _lib.load()
-    need = int(lib.kv_score_gqa_workspace_bytes(ctypes.byref(shape), int(G)))
-    if workspace is None:
-        workspace = torch.empty((max(need, 8),), dtype=torch.uint8, device=dev)
-    wp = _dev_ptr(workspace, "workspace", torch.uint8, None, dev)
+    need = int(_lib.load().kv_score_gqa_workspace_bytes(ctypes.byref(shape), int(G)))
+    workspace, wp, _ = _workspace(workspace, need, dev)
     dl = [int(x) for x in deltas]
     arr = (ctypes.c_int32 * max(1, len(dl)))(*dl)
     _invoke("tri_score_gqa", dev, ctypes.byref(shape), kp, pp, int(G), qp, ap, tp, float(rope_theta), arr,
@@ -214,9 +235,7 @@ def tri_score_gqa_rotated(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tens
     hp = _dev_ptr(head_out, "head_out", torch.float32, (L, S, H, G, t_cap), dev)
     shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
     need = int(_lib.load().kv_score_gqa_workspace_bytes(ctypes.byref(shape), int(G)))
-    if workspace is None:
-        workspace = torch.empty((max(need, 8),), dtype=torch.uint8, device=dev)
-    wp = _dev_ptr(workspace, "workspace", torch.uint8, None, dev)
+    workspace, wp, _ = _workspace(workspace, need, dev)
     dl = [int(x) for x in deltas]
     arr = (ctypes.c_int32 * max(1, len(dl)))(*dl)
     _invoke("tri_score_gqa_rotated", dev, ctypes.byref(shape), kp, None if paged is None else ctypes.byref(paged),
@@ -242,8 +261,8 @@ def _select_io(L, S, H, b_cap, device, kept, n_kept):
 
 def kv_select_topk(scores: torch.Tensor, seq_len: torch.Tensor, prompt_len: torch.Tensor, budget: int,
                    recent: int, prompt_cap: int, b_cap: Optional[int] = None,
-                   kept: Optional[torch.Tensor] = None, n_kept: Optional[torch.Tensor] = None
-                   ) -> Tuple[torch.Tensor, torch.Tensor]:
+                   kept: Optional[torch.Tensor] = None, n_kept: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per-head kept slots (ascending, -1 padded) under the top-n rule, and n_kept per sequence."""
     if scores.dim() != 4:
         raise ValueError("scores must be [L,S,H,t_cap]")
@@ -256,15 +275,17 @@ def kv_select_topk(scores: torch.Tensor, seq_len: torch.Tensor, prompt_len: torc
     kept, n_kept, kp, nkp = _select_io(L, S, H, b_cap, dev, kept, n_kept)
     shape = _shape(L, S, H, 0, t_cap, 0, sp)
     pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
-    _invoke("kv_select_topk", dev, ctypes.byref(shape), ctypes.byref(pol), sc, kp, b_cap, nkp)
+    need = int(_lib.load().kv_select_workspace_bytes(ctypes.byref(shape), b_cap))
+    workspace, wp, wb = _workspace(workspace, need, dev)
+    _invoke("kv_select_topk", dev, ctypes.byref(shape), ctypes.byref(pol), sc, kp, b_cap, nkp, wp, wb)
     return kept, n_kept
 
 
 def kv_select_random(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tensor, prompt_len: torch.Tensor,
                      budget: int, recent: int, prompt_cap: int, seed: int, event: int,
                      pos: Optional[torch.Tensor] = None, b_cap: Optional[int] = None,
-                     kept: Optional[torch.Tensor] = None, n_kept: Optional[torch.Tensor] = None
-                     ) -> Tuple[torch.Tensor, torch.Tensor]:
+                     kept: Optional[torch.Tensor] = None, n_kept: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per-head kept slots under Random Attention's rule (Philox draw per head and event)."""
     L, S, H, t_cap = (int(x) for x in cache_shape)
     dev = seq_len.device
@@ -275,8 +296,10 @@ def kv_select_random(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tens
     kept, n_kept, kp, nkp = _select_io(L, S, H, b_cap, dev, kept, n_kept)
     shape = _shape(L, S, H, 0, t_cap, 0, sp)
     pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
+    need = int(_lib.load().kv_select_workspace_bytes(ctypes.byref(shape), b_cap))
+    workspace, wp, wb = _workspace(workspace, need, dev)
     _invoke("kv_select_random", dev, ctypes.byref(shape), ctypes.byref(pol), pp, int(seed) & (2 ** 64 - 1),
-            int(event) & 0xFFFFFFFF, kp, b_cap, nkp)
+            int(event) & 0xFFFFFFFF, kp, b_cap, nkp, wp, wb)
     return kept, n_kept
 
 
@@ -309,8 +332,8 @@ def kv_select_union(head_scores: torch.Tensor, scores: torch.Tensor, seq_len: to
 def kv_select_random_shared(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tensor,
                             prompt_len: torch.Tensor, budget: int, recent: int, prompt_cap: int, seed: int,
                             event: int, pos: Optional[torch.Tensor] = None, b_cap: Optional[int] = None,
-                            kept: Optional[torch.Tensor] = None, n_kept: Optional[torch.Tensor] = None
-                            ) -> Tuple[torch.Tensor, torch.Tensor]:
+                            kept: Optional[torch.Tensor] = None, n_kept: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """The shared-draw control: every head keeps what layer 0 / KV head 0 would draw."""
     L, S, H, t_cap = (int(x) for x in cache_shape)
     dev = seq_len.device
@@ -321,8 +344,10 @@ def kv_select_random_shared(cache_shape: Tuple[int, int, int, int], seq_len: tor
     kept, n_kept, kp, nkp = _select_io(L, S, H, b_cap, dev, kept, n_kept)
     shape = _shape(L, S, H, 0, t_cap, 0, sp)
     pol = _lib.KvPolicy(int(budget), int(recent), int(prompt_cap), pl)
+    need = int(_lib.load().kv_select_workspace_bytes(ctypes.byref(shape), b_cap))
+    workspace, wp, wb = _workspace(workspace, need, dev)
     _invoke("kv_select_random_shared", dev, ctypes.byref(shape), ctypes.byref(pol), pp,
-            int(seed) & (2 ** 64 - 1), int(event) & 0xFFFFFFFF, kp, b_cap, nkp)
+            int(seed) & (2 ** 64 - 1), int(event) & 0xFFFFFFFF, kp, b_cap, nkp, wp, wb)
     return kept, n_kept
 
 

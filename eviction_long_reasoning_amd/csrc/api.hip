@@ -9,6 +9,12 @@
 
 #define KV_EXPORT extern "C" __attribute__((visibility("default")))
 
+// A build with -DKV_DEVICE_CHECKS=1 (libkvevict_debug.so) launches the precondition kernel of
+// checks.hip before each call's own kernels; the release build does not.
+#ifndef KV_DEVICE_CHECKS
+#define KV_DEVICE_CHECKS 0
+#endif
+
 namespace kvevict {
 namespace {
 
@@ -50,6 +56,29 @@ kv_status check_policy(const kv_policy *po, int b_cap) {
 
 kv_status hip_status(hipError_t e) { return e == hipSuccess ? KV_OK : KV_EHIP; }
 
+// Every workspace starts with the header (status word + reserved bytes); kernel scratch follows.
+kv_status check_workspace(const void *ws, size_t bytes, size_t need) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 7u) || bytes < need) return KV_EWORKSPACE;
+  return KV_OK;
+}
+
+// Debug build: verify the device-side preconditions (lengths, prompt lengths, position order) and
+// OR the KV_DEV_* bits of what fails into the workspace status word. Release build: nothing.
+kv_status device_checks(const kv_shape *sh, const kv_policy *po, const int32_t *pos, void *ws, hipStream_t st) {
+  if (!KV_DEVICE_CHECKS) return KV_OK;
+  CheckParams c{};
+  c.seq_len = sh->seq_len;
+  c.prompt_len = po ? po->prompt_len : nullptr;
+  c.prompt_cap = po ? po->prompt_cap : 0;
+  c.pos = pos;
+  c.L = sh->n_layers;
+  c.S = sh->n_seq;
+  c.H = sh->n_kv_heads;
+  c.t_cap = sh->t_cap;
+  c.status = static_cast<uint32_t *>(ws);
+  return hip_status(launch_device_checks(c, st));
+}
+
 // Band frequencies omega_f = theta^(-2f/d) (as revolutions per position, omega_f / 2pi) and the
 // fold coefficient A_f = (1/|D|) sum_delta exp(i omega_f delta), both in fp64 with the phase
 // reduced to [-1/2, 1/2] revolutions before sin/cos.
@@ -81,7 +110,9 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 using namespace kvevict;
 
-KV_EXPORT int32_t kv_version(void) { return (1 << 16) | 0; }
+KV_EXPORT int32_t kv_version(void) { return (2 << 16) | 0; }
+
+KV_EXPORT int32_t kv_device_checks(void) { return KV_DEVICE_CHECKS ? 1 : 0; }
 
 KV_EXPORT const char *kv_status_string(int32_t status) {
   switch (status) {
@@ -89,14 +120,21 @@ KV_EXPORT const char *kv_status_string(int32_t status) {
     case KV_EINVAL: return "invalid argument (null pointer, non-positive size, bad policy or aliasing)";
     case KV_EDTYPE: return "unknown element type";
     case KV_ESHAPE: return "shape or capacity outside what the kernels support";
+    case KV_EWORKSPACE: return "workspace missing, misaligned or smaller than its *_workspace_bytes query";
     case KV_EHIP: return "HIP kernel launch failed";
     default: return "unknown status";
   }
 }
 
+KV_EXPORT size_t kv_score_workspace_bytes(const kv_shape *shape, int32_t n_delta) {
+  if (check_shape(shape, true, false) != KV_OK || n_delta < 1 || n_delta > kMaxDeltas) return 0;
+  return kWorkspaceHeader;   // the score stream needs no scratch of its own
+}
+
 KV_EXPORT kv_status tri_score(const kv_shape *shape, const void *K, const int32_t *pos, const float *qbar,
                               const float *qabs, const int32_t *t_cur, double rope_theta, const int32_t *deltas,
-                              int32_t n_delta, float *scores, void *stream) {
+                              int32_t n_delta, float *scores, void *workspace, size_t workspace_bytes,
+                              void *stream) {
   kv_status st = check_shape(shape, true);
   if (st != KV_OK) return st;
   if (!K || !qbar || !t_cur || !deltas || !scores) return KV_EINVAL;
@@ -104,6 +142,7 @@ KV_EXPORT kv_status tri_score(const kv_shape *shape, const void *K, const int32_
   if (n_delta < 1 || n_delta > kMaxDeltas) return KV_EINVAL;
   if (!aligned16(K) || (reinterpret_cast<uintptr_t>(qbar) & 7u)) return KV_EINVAL;
   if (!words({pos, qabs, t_cur, scores, shape->seq_len})) return KV_EINVAL;
+  if ((st = check_workspace(workspace, workspace_bytes, kWorkspaceHeader)) != KV_OK) return st;
 
   ScoreParams p{};
   p.K = K;
@@ -131,7 +170,9 @@ KV_EXPORT kv_status tri_score(const kv_shape *shape, const void *K, const int32_
   if (lpk > 64) return KV_ESHAPE;
   const long long threads = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head * kScoreThreads;
   if (threads >= (1ll << 32)) return KV_ESHAPE;
-  return hip_status(launch_score(p, shape->dtype == KV_BF16, lpk, static_cast<hipStream_t>(stream)));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = device_checks(shape, nullptr, pos, workspace, hs)) != KV_OK) return st;
+  return hip_status(launch_score(p, shape->dtype == KV_BF16, lpk, hs));
 }
 
 KV_EXPORT kv_status tri_score_rotated(const kv_shape *shape, const void *K, const kv_paged *paged,
@@ -193,7 +234,7 @@ namespace {
 size_t gqa_workspace(const kv_shape *sh, int group) {
   const size_t heads = static_cast<size_t>(sh->n_layers) * sh->n_seq * sh->n_kv_heads;
   const size_t chunks = (static_cast<size_t>(sh->t_cap) + kGqaChunk - 1) / kGqaChunk;
-  return heads * chunks * static_cast<size_t>(group) * 2 * sizeof(double);
+  return kWorkspaceHeader + heads * chunks * static_cast<size_t>(group) * 2 * sizeof(double);
 }
 }  // namespace
 }  // namespace kvevict
@@ -209,14 +250,13 @@ KV_EXPORT kv_status tri_score_gqa(const kv_shape *shape, const void *K, const in
                                   void *workspace, size_t workspace_bytes, void *stream) {
   kv_status st = check_shape(shape, true);
   if (st != KV_OK) return st;
-  if (!K || !qbar || !t_cur || !deltas || !scores || !head_scores || !workspace) return KV_EINVAL;
+  if (!K || !qbar || !t_cur || !deltas || !scores || !head_scores) return KV_EINVAL;
   if (group < 1 || group > kGqaMaxGroup) return KV_EINVAL;
   if (!(rope_theta > 0.0) || !std::isfinite(rope_theta)) return KV_EINVAL;
   if (n_delta < 1 || n_delta > kMaxDeltas) return KV_EINVAL;
-  if (!aligned16(K) || (reinterpret_cast<uintptr_t>(qbar) & 7u) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
-    return KV_EINVAL;
+  if (!aligned16(K) || (reinterpret_cast<uintptr_t>(qbar) & 7u)) return KV_EINVAL;
   if (!words({pos, qabs, t_cur, head_scores, scores, shape->seq_len})) return KV_EINVAL;
-  if (workspace_bytes < gqa_workspace(shape, group)) return KV_ESHAPE;
+  if ((st = check_workspace(workspace, workspace_bytes, gqa_workspace(shape, group))) != KV_OK) return st;
   // one head's per-query-head scores are stored through a 32-bit buffer offset
   if (static_cast<long long>(group) * shape->t_cap * 4 >= (1ll << 31)) return KV_ESHAPE;
   const size_t heads = static_cast<size_t>(shape->n_layers) * shape->n_seq * shape->n_kv_heads;
@@ -234,7 +274,7 @@ KV_EXPORT kv_status tri_score_gqa(const kv_shape *shape, const void *K, const in
   p.t_cur = t_cur;
   p.seq_len = shape->seq_len;
   p.raw = head_scores;
-  p.partials = static_cast<double *>(workspace);
+  p.partials = reinterpret_cast<double *>(static_cast<char *>(workspace) + kWorkspaceHeader);
   p.scores = scores;
   p.L = shape->n_layers;
   p.S = shape->n_seq;
@@ -256,7 +296,9 @@ KV_EXPORT kv_status tri_score_gqa(const kv_shape *shape, const void *K, const in
   if (ppq > 8) return KV_ESHAPE;
   const long long threads = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head * kScoreThreads;
   if (threads >= (1ll << 32)) return KV_ESHAPE;
-  return hip_status(launch_score_gqa(p, shape->dtype == KV_BF16, ppq, static_cast<hipStream_t>(stream)));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = device_checks(shape, nullptr, pos, workspace, hs)) != KV_OK) return st;
+  return hip_status(launch_score_gqa(p, shape->dtype == KV_BF16, ppq, hs));
 }
 
 // max_slots: the largest t_cap the selector kernel behind the entry point takes.
@@ -267,16 +309,15 @@ KV_EXPORT kv_status tri_score_gqa_rotated(const kv_shape *shape, const void *K, 
                                           size_t workspace_bytes, void *stream) {
   kv_status st = check_shape(shape, true);
   if (st != KV_OK) return st;
-  if (!K || !qbar || !t_cur || !deltas || !scores || !head_scores || !workspace) return KV_EINVAL;
+  if (!K || !qbar || !t_cur || !deltas || !scores || !head_scores) return KV_EINVAL;
   if (group < 1 || group > kGqaRotatedMaxGroup) return KV_EINVAL;
   if (!(rope_theta > 0.0) || !std::isfinite(rope_theta)) return KV_EINVAL;
   if (n_delta < 1 || n_delta > kMaxDeltas) return KV_EINVAL;
   if (rope_style != KV_ROPE_INTERLEAVED && rope_style != KV_ROPE_HALF) return KV_EINVAL;
-  if (!aligned16(K) || (reinterpret_cast<uintptr_t>(qbar) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
-    return KV_EINVAL;
+  if (!aligned16(K) || (reinterpret_cast<uintptr_t>(qbar) & 3u)) return KV_EINVAL;
   if (!words({qabs, t_cur, head_scores, scores, shape->seq_len, paged ? paged->block_table : nullptr}))
     return KV_EINVAL;
-  if (workspace_bytes < gqa_workspace(shape, group)) return KV_ESHAPE;
+  if ((st = check_workspace(workspace, workspace_bytes, gqa_workspace(shape, group))) != KV_OK) return st;
   const size_t heads = static_cast<size_t>(shape->n_layers) * shape->n_seq * shape->n_kv_heads;
   const size_t score_bytes = heads * shape->t_cap * sizeof(float);
   if (overlaps(head_scores, score_bytes * group, scores, score_bytes) ||
@@ -291,7 +332,7 @@ KV_EXPORT kv_status tri_score_gqa_rotated(const kv_shape *shape, const void *K, 
   p.t_cur = t_cur;
   p.seq_len = shape->seq_len;
   p.raw = head_scores;
-  p.partials = static_cast<double *>(workspace);
+  p.partials = reinterpret_cast<double *>(static_cast<char *>(workspace) + kWorkspaceHeader);
   p.scores = scores;
   p.L = shape->n_layers;
   p.S = shape->n_seq;
@@ -327,8 +368,9 @@ KV_EXPORT kv_status tri_score_gqa_rotated(const kv_shape *shape, const void *K, 
   if (static_cast<long long>(group) * shape->t_cap * 4 >= (1ll << 31)) return KV_ESHAPE;
   const long long threads = static_cast<long long>(p.L) * p.S * p.H * p.chunks_per_head * kScoreThreads;
   if (threads >= (1ll << 32)) return KV_ESHAPE;
-  return hip_status(launch_score_gqa_rotated(p, shape->dtype == KV_BF16, layout, lpk,
-                                             static_cast<hipStream_t>(stream)));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = device_checks(shape, nullptr, nullptr, workspace, hs)) != KV_OK) return st;
+  return hip_status(launch_score_gqa_rotated(p, shape->dtype == KV_BF16, layout, lpk, hs));
 }
 
 static kv_status select_common(const kv_shape *shape, const kv_policy *policy, int32_t *kept, int32_t b_cap,
@@ -354,28 +396,56 @@ static kv_status select_common(const kv_shape *shape, const kv_policy *policy, i
   return KV_OK;
 }
 
+KV_EXPORT size_t kv_select_workspace_bytes(const kv_shape *shape, int32_t b_cap) {
+  if (check_shape(shape, false, false) != KV_OK || b_cap < 1 || shape->t_cap > kSelectMaxSlotsStream) return 0;
+  return kWorkspaceHeader + select_scratch_bytes(shape->n_layers, shape->n_seq, shape->n_kv_heads, shape->t_cap);
+}
+
+// The selectors' workspace: validated against the query, scratch after the header.
+static kv_status select_workspace(const kv_shape *shape, void *ws, size_t bytes, SelectParams &p) {
+  const size_t scratch = select_scratch_bytes(shape->n_layers, shape->n_seq, shape->n_kv_heads, shape->t_cap);
+  kv_status st = check_workspace(ws, bytes, kWorkspaceHeader + scratch);
+  if (st != KV_OK) return st;
+  p.scratch = scratch ? static_cast<char *>(ws) + kWorkspaceHeader : nullptr;
+  return KV_OK;
+}
+
 KV_EXPORT kv_status kv_select_topk(const kv_shape *shape, const kv_policy *policy, const float *scores,
-                                   int32_t *kept, int32_t b_cap, int32_t *n_kept, void *stream) {
+                                   int32_t *kept, int32_t b_cap, int32_t *n_kept, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
   SelectParams p{};
   kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p);
   if (st != KV_OK) return st;
   if (!scores || !words({scores})) return KV_EINVAL;
+  if ((st = select_workspace(shape, workspace, workspace_bytes, p)) != KV_OK) return st;
   p.scores = scores;
-  return hip_status(launch_select(p, SelectKind::kTopk, static_cast<hipStream_t>(stream)));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = device_checks(shape, policy, nullptr, workspace, hs)) != KV_OK) return st;
+  return hip_status(launch_select(p, SelectKind::kTopk, hs));
 }
 
-KV_EXPORT kv_status kv_select_random(const kv_shape *shape, const kv_policy *policy, const int32_t *pos,
-                                     uint64_t seed, uint32_t event, int32_t *kept, int32_t b_cap,
-                                     int32_t *n_kept, void *stream) {
+static kv_status select_random(const kv_shape *shape, const kv_policy *policy, const int32_t *pos, uint64_t seed,
+                               uint32_t event, int32_t *kept, int32_t b_cap, int32_t *n_kept, void *workspace,
+                               size_t workspace_bytes, void *stream, int shared_draw) {
   SelectParams p{};
   kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p);
   if (st != KV_OK) return st;
   if (!words({pos})) return KV_EINVAL;
+  if ((st = select_workspace(shape, workspace, workspace_bytes, p)) != KV_OK) return st;
   p.pos = pos;
   p.seed_lo = static_cast<uint32_t>(seed & 0xffffffffu);
   p.seed_hi = static_cast<uint32_t>(seed >> 32);
   p.event = event;
-  return hip_status(launch_select(p, SelectKind::kRandom, static_cast<hipStream_t>(stream)));
+  p.shared_draw = shared_draw;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = device_checks(shape, policy, pos, workspace, hs)) != KV_OK) return st;
+  return hip_status(launch_select(p, SelectKind::kRandom, hs));
+}
+
+KV_EXPORT kv_status kv_select_random(const kv_shape *shape, const kv_policy *policy, const int32_t *pos,
+                                     uint64_t seed, uint32_t event, int32_t *kept, int32_t b_cap,
+                                     int32_t *n_kept, void *workspace, size_t workspace_bytes, void *stream) {
+  return select_random(shape, policy, pos, seed, event, kept, b_cap, n_kept, workspace, workspace_bytes, stream, 0);
 }
 
 KV_EXPORT kv_status kv_select_union(const kv_shape *shape, const kv_policy *policy, int32_t group,
@@ -404,17 +474,8 @@ KV_EXPORT kv_status kv_audit_kept(const kv_shape *shape, const kv_policy *policy
 
 KV_EXPORT kv_status kv_select_random_shared(const kv_shape *shape, const kv_policy *policy, const int32_t *pos,
                                           uint64_t seed, uint32_t event, int32_t *kept, int32_t b_cap,
-                                          int32_t *n_kept, void *stream) {
-  SelectParams p{};
-  kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p);
-  if (st != KV_OK) return st;
-  if (!words({pos})) return KV_EINVAL;
-  p.pos = pos;
-  p.seed_lo = static_cast<uint32_t>(seed & 0xffffffffu);
-  p.seed_hi = static_cast<uint32_t>(seed >> 32);
-  p.event = event;
-  p.shared_draw = 1;
-  return hip_status(launch_select(p, SelectKind::kRandom, static_cast<hipStream_t>(stream)));
+                                          int32_t *n_kept, void *workspace, size_t workspace_bytes, void *stream) {
+  return select_random(shape, policy, pos, seed, event, kept, b_cap, n_kept, workspace, workspace_bytes, stream, 1);
 }
 
 KV_EXPORT kv_status kv_select_recent(const kv_shape *shape, const kv_policy *policy, int32_t *kept, int32_t b_cap,

@@ -6,6 +6,21 @@
 
 namespace kvevict {
 
+// Every caller workspace starts with this many bytes: the device status word, then reserved space.
+constexpr size_t kWorkspaceHeader = 256;
+
+// Device-side preconditions checked by a build with KV_DEVICE_CHECKS (the bits of kvevict.h's
+// KV_DEV_* are ORed into *status).
+struct CheckParams {
+  const int32_t *seq_len;     // [S]
+  const int32_t *prompt_len;  // [S] or nullptr (scoring calls)
+  int32_t prompt_cap;
+  const int32_t *pos;         // [L,S,H,t_cap] or nullptr
+  int32_t L, S, H, t_cap;
+  uint32_t *status;           // the workspace's first word
+};
+hipError_t launch_device_checks(const CheckParams &c, hipStream_t st);
+
 // Keys stored after RoPE, dense or paged.
 struct RotScoreParams {
   const void *K;               // dense [L,S,H,t_cap,d] or paged pool [L,n_blocks,block_size,H,d]
@@ -73,11 +88,16 @@ struct SelectParams {
   int32_t shared_draw;      // random: every (layer, head) draws as layer 0 / head 0
   const float *head_scores; // union: [L,S,H,G,t_cap] per-query-head scores (scores = combined)
   int32_t G, k_per_head;    // union: query heads per KV head; per-head top-k (<= 0: ceil(n_sel / G))
+  void *scratch;            // caller workspace past its header (select_scratch_bytes), or nullptr
 };
+
+// Scratch bytes the top-k / random selectors need past the workspace header for L*S*H heads of
+// t_cap slots.
+size_t select_scratch_bytes(int L, int S, int H, int t_cap);
 
 enum class SelectKind { kTopk, kRandom, kUnion };
 
-constexpr int kSelectMaxSlots = 65536;          // register-resident tiers
+constexpr int kSelectMaxSlots = 32768;          // register-resident tiers
 constexpr int kSelectMaxSlotsStream = 1 << 26;    // top-k and random past the tiers: keys re-read per step
 constexpr int kSelectMaxSlotsUnion = 1 << 18;     // union past the tiers: a bit per slot in LDS
 hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st);

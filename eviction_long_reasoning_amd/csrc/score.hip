@@ -309,10 +309,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const Score
         }
       }
     };
+    // Batch 1 goes out with batch 0, before the set-up arithmetic -- except with the norm term,
+    // whose set-up holds more registers: issued first there, its loads push the kernel past 256
+    // registers and to one wave per SIMD, so it goes out after the set-up.
+    constexpr bool EARLY_B1 = NB > 1 && !NORM;
     __builtin_amdgcn_sched_barrier(0);
     uint4 da[STEPS], db[STEPS];
     issue(0, da);
-    if (NB > 1) issue(1, db);
+    if (EARLY_B1) issue(1, db);
     __builtin_amdgcn_sched_barrier(0);
 
     float2 v[BPL], w[BPL];
@@ -346,6 +350,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const Score
       if (jj < T) st_score(p.scores + slot0 + jj, sc);
     };
 
+    if (NB > 1 && !EARLY_B1) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue(1, db);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // The next batch is issued whether or not it holds live slots (a batch past T takes the ragged
     // path and reads in-range rows whose sums are not stored): with a load that is always issued,
     // each wait counts only the older batch, where a conditional issue made the compiler wait for
@@ -353,14 +362,16 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const Score
 #pragma unroll
     for (int nb = 0; nb < NB; nb += 2) {
       if (nb >= nbat) break;
-      if (nb > 0 && nb + 1 < NB) issue(nb + 1, db);   // batch 1 went out with batch 0
+      if (nb > 0 && nb + 1 < NB) issue(nb + 1, db);   // batch 1 is already out
       consume(nb, da);
       if (nb + 1 >= nbat) break;
       if (nb + 2 < NB) issue(nb + 2, da);
       consume(nb + 1, db);
     }
   };
-  if (wave_first + NB * 64 <= T) body(std::true_type{});
+  // With the norm term the branch-free copy lets the scheduler hold more than 256 registers (one
+  // wave per SIMD, 35 % slower), so that form keeps the per-batch test.
+  if (!NORM && wave_first + NB * 64 <= T) body(std::true_type{});
   else body(std::false_type{});
 }
 

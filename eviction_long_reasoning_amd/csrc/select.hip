@@ -10,12 +10,12 @@
 // Appendix F: keep-sets sorted chronologically) and "TriAttention" (blog
 // walkthrough, eviction step: union-based selection over per-head top-k sets).
 //
-// One workgroup owns one (layer, seq, KV head). Its T slot keys live in
-// registers; thread t holds, for each round i, the four consecutive slots
-// 4*(i*NT + t) .. +3, so every round is one fully coalesced 16-byte-per-lane
-// load and the head's scores are read from HBM exactly once:
-//  1. Keys: fp32 scores mapped to order-preserving uint32 (NaN -> -inf,
-//     -0 -> +0) or, for the random selector, word 0 of Philox4x32-10.
+// One workgroup owns one (layer, seq, KV head). Its keys live in registers:
+// thread t holds slot i*NT + t in round i, so every round is one coalesced
+// 4-byte-per-lane load and the head's scores are read from HBM exactly once:
+//  1. Keys: fp32 scores with NaN ranked as -inf (float comparisons give the
+//     ranking, -0 equal to +0) or, for the random selector, word 0 of
+//     Philox4x32-10 compared as uint32.
 //  2. A 1024-bin LDS histogram (scores binned by value between the smallest
 //     and largest finite candidate, random keys by their top 10 bits) finds
 //     the bin holding the n_sel-th largest key; every key in a higher bin is
@@ -25,26 +25,14 @@
 //     thr must be taken (need). A crowded bin instead goes through 8-bit radix
 //     passes over a 256-bin histogram, from the highest bit where its keys
 //     differ (an OR/AND block reduction).
-//  4. One ordered scan in slot order counts, before each slot, the slots kept
-//     unconditionally (pinned, or above thr) and the slots equal to thr. A
-//     kept slot's output index is then (unconditional before) +
-//     min(equal before, need): ties go to the lower slot and the kept list is
-//     written in ascending order without a sort.
+//  4. Placement without a sort: the prompt and the recent window go to their
+//     fixed places; a selected evictable slot goes to P + (selected slots
+//     before it), counted from one ballot per (round, wave) and the lanes
+//     below it in its wave's ballot. Ties go to the lower slot, and the kept
+//     list comes out in ascending order.
 #include "kv_internal.hpp"
 
-#ifndef KV_SELECT_WIDE
-#define KV_SELECT_WIDE 0
-#endif
-// Top-k and random (union) caches longer than this run the kernel that re-reads its keys. Past
-// 32768 slots the 1024 x 64 register tier spills; the re-reading kernel was measured faster there
-// for top-k (40000 slots: 0.32 -> 0.22 ms; 65536: within 4 %) and random (0.48 -> 0.35, 0.66 ->
-// 0.57 ms), slower for the union (1.34 -> 1.54, 1.64 -> 2.72 ms), on 1152 heads.
-#ifndef KV_SELECT_STREAM_ABOVE
-#define KV_SELECT_STREAM_ABOVE 32768
-#endif
-#ifndef KV_UNION_STREAM_ABOVE
-#define KV_UNION_STREAM_ABOVE 65536
-#endif
+#include <type_traits>
 
 namespace kvevict {
 namespace {
@@ -101,6 +89,12 @@ __device__ __forceinline__ uint32_t wave_total(uint32_t incl) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
 }
 
+// Lanes below this one whose bit is set in a wave-wide mask.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
 constexpr uint32_t kKeyNegInf = 0x007FFFFFu;  // order_key(-inf)
 constexpr uint32_t kKeyPosInf = 0xFF800000u;  // order_key(+inf)
 constexpr int kValueBins = 1024;
@@ -110,27 +104,34 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Monotone (non-decreasing) map of a key to one of kValueBins bins spanning [fmin, fmax];
-// -inf and +inf go to the end bins. Rounded operations that cannot be contracted keep the
-// two evaluations of a key (histogram and membership) bit-identical.
-__device__ __forceinline__ uint32_t value_bin(uint32_t k, float fmin, float scale) {
+// Value binning of the threshold search: bins of equal width between the smallest and largest
+// finite candidate, bin(v) = floor(v * scale + off) clamped to [0, kValueBins - 1] with
+// off = -min * scale. One fused multiply-add, so the map never decreases as v grows: every bin's
+// values form an interval. The clamp happens in floating point before the conversion (a NaN, -inf
+// or negative value lands in bin 0, +inf in the last bin), so the conversion is always in range.
+__device__ __forceinline__ uint32_t bin_of_value(float v, float scale, float off) {
+  const float x = fminf(fmaxf(fmaf(v, scale, off), 0.f), static_cast<float>(kValueBins - 1));
+  return static_cast<uint32_t>(x);
+}
+// The same map over order keys (all 2^32 of them: the patterns past +-inf go to the end bins). For a
+// score x, bin_of_key(order_key(x)) == bin_of_value(x).
+__device__ __forceinline__ uint32_t bin_of_key(uint32_t k, float scale, float off) {
   if (k <= kKeyNegInf) return 0u;
   if (k >= kKeyPosInf) return kValueBins - 1u;
-  const float x = __fmul_rn(__fsub_rn(key_value(k), fmin), scale);
-  return min(static_cast<uint32_t>(x), static_cast<uint32_t>(kValueBins - 1));
+  return bin_of_value(key_value(k), scale, off);
 }
 
-// value_bin never decreases as the key grows (over all 2^32 keys), so the keys of one bin form an
-// interval. Run by one wave: the smallest key whose bin is at least `target`, or 2^32 when none
-// is, by a 64-way search over the key space (at most seven rounds). It evaluates the same
-// rounded expression as the histogram pass, so the interval test that replaces a second
-// evaluation per key agrees with it key for key.
-__device__ __forceinline__ uint64_t first_key_reaching(uint32_t target, float fmin, float scale, int lane) {
+// bin_of_key never decreases as the key grows, so the keys of one bin form an interval. Run by one
+// wave: the smallest key whose bin is at least `target`, or 2^32 when none is, by a 64-way search
+// over the key space (at most seven rounds). It evaluates the same rounded expression as the
+// histogram pass, so the interval test that replaces a second evaluation per key agrees with it key
+// for key.
+__device__ __forceinline__ uint64_t first_key_reaching(uint32_t target, float scale, float off, int lane) {
   uint64_t lo = 0, hi = uint64_t{1} << 32;   // keys below lo stay under target; hi reaches it (2^32: none)
   while (lo < hi) {
     const uint64_t step = (hi - lo + 63) >> 6;
     const uint64_t c = lo + static_cast<uint64_t>(lane) * step;
-    const bool reach = c >= hi || value_bin(static_cast<uint32_t>(c), fmin, scale) >= target;
+    const bool reach = c >= hi || bin_of_key(static_cast<uint32_t>(c), scale, off) >= target;
     const uint64_t m = __ballot(reach);
     if (m & 1ull) return lo;
     const int f = m ? __builtin_ctzll(m) : 64;               // first probe that reaches (64: none)
@@ -144,7 +145,7 @@ __device__ __forceinline__ uint64_t first_key_reaching(uint32_t target, float fm
 // Interval [lo, hi] of the keys of bin b, in LDS slots kb[0], kb[1]: scores (value bins) by waves 0
 // and 1 of the workgroup (the caller then synchronises), random keys (top 10 bits) directly.
 template <bool RANDOM>
-__device__ __forceinline__ void bin_interval(uint32_t b, float fmin, float scale, int wave, int lane,
+__device__ __forceinline__ void bin_interval(uint32_t b, float scale, float off, int wave, int lane,
                                              uint32_t *kb) {
   if (RANDOM) {
     if (wave == 0 && lane == 0) {
@@ -152,7 +153,7 @@ __device__ __forceinline__ void bin_interval(uint32_t b, float fmin, float scale
       kb[1] = (b << 22) | 0x3FFFFFu;
     }
   } else if (wave < 2) {
-    const uint64_t k = first_key_reaching(b + static_cast<uint32_t>(wave), fmin, scale, lane);
+    const uint64_t k = first_key_reaching(b + static_cast<uint32_t>(wave), scale, off, lane);
     if (lane == 0) kb[wave] = static_cast<uint32_t>(k - static_cast<uint64_t>(wave));  // bin b+1's first, minus one
   }
 }
@@ -206,6 +207,44 @@ __device__ __forceinline__ void block_min_max(uint32_t &mn, uint32_t &mx, uint32
   __syncthreads();  // lds may be reused right after
 }
 
+// Smallest and largest fp32 value over the workgroup; NaN inputs are ignored (fminf / fmaxf).
+template <int NT>
+__device__ __forceinline__ void block_fmin_fmax(float &mn, float &mx, float *lds /* 2*NT/64 */) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  }
+  if (lane == 0) {
+    lds[wave] = mn;
+    lds[NW + wave] = mx;
+  }
+  __syncthreads();
+  mn = INFINITY;
+  mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    mn = fminf(mn, lds[i]);
+    mx = fmaxf(mx, lds[NW + i]);
+  }
+  __syncthreads();  // lds may be reused right after
+}
+
+template <int NT>
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t *lds /* NT/64 */) {
+  constexpr int NW = NT / 64;
+  x = wave_total(wave_inclusive_sum(x));
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = x;
+  __syncthreads();
+  uint32_t t = 0u;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) t += lds[i];
+  __syncthreads();
+  return t;
+}
+
 template <int NT>
 __device__ __forceinline__ void block_or_and(uint32_t &o, uint32_t &a, uint32_t *lds /* 2*NT/64 */) {
   constexpr int NW = NT / 64;
@@ -228,17 +267,6 @@ __device__ __forceinline__ void block_or_and(uint32_t &o, uint32_t &a, uint32_t 
     a &= lds[NW + i];
   }
   __syncthreads();  // lds may be reused right after
-}
-
-// In-place exclusive scan of n values held in LDS, run by one wave (n may exceed 64).
-__device__ __forceinline__ void wave_exclusive_scan_lds(uint32_t *a, int n, int lane) {
-  uint32_t carry = 0u;
-  for (int c = 0; c < n; c += 64) {
-    const uint32_t v = (c + lane < n) ? a[c + lane] : 0u;
-    const uint32_t x = wave_inclusive_sum(v);
-    if (c + lane < n) a[c + lane] = carry + x - v;
-    carry += wave_total(x);
-  }
 }
 
 // Threshold among a short member list held in LDS (list[0..m), zero-padded to a multiple of 4;
@@ -272,231 +300,237 @@ __device__ __forceinline__ void rank_members(const uint32_t *list, uint32_t m, u
 template <int NT>
 constexpr uint32_t member_cap() { return 2 * NT < kValueBins - 4 ? 2 * NT : kValueBins - 4; }
 
-// The three rankings share one kernel body. KIND 0 (top-k): keys are the fp32 scores. KIND 1
-// (random): keys are Philox words. KIND 2 (union, "TriAttention" blog, eviction step): G + 1
-// passes over the same registers -- pass g < G ranks the evictable slots by query head g's own
-// score and adds its top-k to a per-thread union bit mask; the last pass ranks by the combined
-// score, inside the union when it holds at least n_sel slots, otherwise over the rest of the
-// evictable range with the whole union kept. Every pass is a threshold search (steps 2-3) and an
-// ordered scan (step 4); top-k and random run exactly one pass.
+// 4-byte buffer load: the per-round offset rides in a scalar register, and reads past the
+// resource's byte range return 0 without a memory access.
+__device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+constexpr uint32_t kNoKey = 0x7FC00000u;   // quiet NaN: a score slot that takes no part
+
+// The three rankings share one body. KIND 0 (top-k): keys are the fp32 scores. KIND 1 (random):
+// keys are Philox words. KIND 2 (union, "TriAttention" blog, eviction step): G + 1 passes -- pass
+// g < G ranks the evictable slots by query head g's own score and adds its top-k to a per-thread
+// union bit mask; the last pass ranks by the combined score, inside the union when it holds at
+// least n_sel slots, otherwise over the rest of the evictable range with the whole union kept.
+// Every pass is a threshold search and an ordered placement; top-k and random run one pass.
 //
-// VEC (score keys only): every score row is 16-byte aligned and t_cap is a multiple of 4, so
-// each round is one float4 load per lane (slots past T are loaded but never used).
-template <int NT, int KPT, int KIND, bool VEC>
-__global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
+// Layout: wave w owns the R*64 consecutive slots from w*R*64 on, and holds slot w*R*64 + i*64 + lane
+// in round i (one key per lane and round). A wave's round is 64 consecutive slots read as one
+// coalesced 256-byte load, and slot order is (wave, round, lane): a wave counts its kept slots in
+// a scalar register as it goes, and only the NW wave totals are exchanged for the placement. R is
+// a compile-time count the kernel picks per head (a quarter, half or all of the tier's KPT, the
+// smallest whose NT*R slots reach the last evictable one), so every phase is straight-line code
+// over registers: a uniform test per round, to skip rounds without evictable slots, cost more
+// than the work it skipped.
+//
+// Slots that take no part (the prompt, the recent window, slots past the range) need no test
+// either. Scores are held as fp32 with NaN replaced by -inf, so the float order is the ranking
+// (-0 and +0 compare equal), and a NaN bit pattern marks a slot that takes no part -- it fails
+// every comparison, fminf/fmaxf ignore it, and binning sends it to bin 0, which never moves the
+// bin found for the threshold (bins are counted from the top and the threshold's keys are real).
+// Random keys are uint32 words and a slot that takes no part holds 0: it is below or equal to
+// every word, lands in bin 0 and matters only when the threshold lies in bin 0 -- then (rarely,
+// and decided once per head) the member, tie and placement tests check the slot range as well.
+//
+// The prompt and recent window are placed arithmetically (kept[r] = r for r < P, the window after
+// the selected slots), so the ordered placement only ranks evictable slots: a selected slot's
+// output index is P + (selected slots before it).
+struct SelectSmem {
+  uint32_t *hist;     // kValueBins words; also the member list
+  float *fred;        // 2 * NW
+  uint32_t *red;      // 2 * NW
+  uint32_t *cnt_a;    // NW: per wave, evictable slots kept outright
+  uint32_t *cnt_e;    // NW: per wave, slots equal to the threshold
+  uint32_t *found;    // 3
+  uint32_t *n_members;
+};
+
+struct SelectHead {
+  int head, l, h, s;
+  int P, e_lo, e_hi, n_sel, n_cand;
+  int32_t *out;
+};
+
+// The smallest key whose bin is at least `target` (2^32 when none is), run by one wave. The bin
+// boundary sits near the value (target - off) / scale; one probe of the 64 keys around that
+// value's key settles it when the boundary lies among them (lane 0 below, some lane at or above:
+// the bin never decreases with the key, so the first lane that reaches is the boundary).
+// Otherwise, or for a boundary near an infinite or cancelling estimate, the 64-way search over the
+// whole key space.
+__device__ __forceinline__ uint64_t first_key_reaching_near(uint32_t target, float scale, float off, int lane) {
+  if (target == 0u) return 0u;
+  if (target >= static_cast<uint32_t>(kValueBins)) return uint64_t{1} << 32;
+  const float v = (static_cast<float>(target) - off) / scale;
+  if (v > -INFINITY && v < INFINITY) {
+    const uint32_t k0 = order_key(v);
+    if (k0 >= 32u && k0 <= 0xFFFFFFFFu - 32u) {
+      const uint32_t c = k0 - 32u + static_cast<uint32_t>(lane);
+      const uint64_t m = __ballot(bin_of_key(c, scale, off) >= target);
+      if (m != 0ull && !(m & 1ull)) return static_cast<uint64_t>(k0 - 32u) + static_cast<uint64_t>(__builtin_ctzll(m));
+    }
+  }
+  return first_key_reaching(target, scale, off, lane);
+}
+
+template <int NT, int R, int KIND>
+__device__ __forceinline__ void select_rounds(const SelectParams &p, const SelectSmem &sm, const SelectHead &hd) {
   constexpr int NW = NT / 64;
-  constexpr int R = KPT / 4;   // rounds of four consecutive slots per thread
   constexpr bool RANDOM = KIND == 1, UNION = KIND == 2;
-  __shared__ __align__(16) uint32_t hist[kValueBins];
-  __shared__ uint32_t red[2 * NW];
-  __shared__ uint32_t tot_a[R * NW];   // per (round, wave): slots kept unconditionally
-  __shared__ uint32_t tot_e[R * NW];   // per (round, wave): slots whose key equals thr
-  __shared__ uint32_t found[3];
-  __shared__ uint32_t n_members;
-  __shared__ uint32_t kb[2];   // key interval of the threshold's bin
-
+  static_assert(R <= 32, "one union bit per round");
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int head = blockIdx.x;
-  const int h = head % p.H;
-  const int s = (head / p.H) % p.S;
-  const int l = head / (p.H * p.S);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int e_lo = hd.e_lo, e_hi = hd.e_hi, n_sel = hd.n_sel, n_cand = hd.n_cand, P = hd.P;
+  uint32_t *hist = sm.hist;
+  uint32_t *found = sm.found;
+  const size_t slot0 = static_cast<size_t>(hd.head) * p.t_cap;
+  // Slot of round 0 for this lane, as a phase sees it: the thread index passes through an empty
+  // asm at the start of each phase, so slots and lane tests are derived where they are used. Left
+  // free, the compiler derives every round's slot and mask once and holds them across the kernel,
+  // more registers than the keys themselves.
+  auto slot_base = [&]() {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    return (t & ~63) * R + (t & 63);
+  };
+  // slot j0 + i*64 lies in [e_lo, e_hi): one unsigned comparison, no branch
+  auto evictable = [&](int j0, int i) {
+    return static_cast<uint32_t>(j0 + i * 64 - e_lo) < static_cast<uint32_t>(n_cand);
+  };
 
-  const int T = min(max(p.seq_len[s], 0), p.t_cap);
-  const int P = min(max(p.prompt_len[s], 0), min(p.prompt_cap, T));
-  const int B = p.budget;
-  int32_t *out = p.kept + static_cast<size_t>(head) * p.b_cap;
-  const bool writer = (l == 0 && h == 0 && tid == 0);
+  uint32_t key[R];
+  auto fkey = [&](int i) { return __uint_as_float(key[i]); };
+  // order key of round i's key (scores: order_key of the value; random: the word itself)
+  auto okey = [&](int i) { return RANDOM ? key[i] : order_key(fkey(i)); };
 
-  if (T <= B) {  // nothing to compress: keep 0..T-1
-    for (int r = tid; r < p.b_cap; r += NT) out[r] = r < T ? r : -1;
-    if (writer) p.n_kept[s] = T;
-    return;
-  }
-  const int Rw = min(p.recent, min(max(0, B - P), T - P));
-  const int e_lo = P, e_hi = T - Rw;
-  const int n_sel = max(0, B - P - Rw);
-  const int n_kept = max(B, P);
-  const int n_cand = e_hi - e_lo;
-
-  auto slot_of = [&](int i) { return 4 * ((i >> 2) * NT + tid) + (i & 3); };
-  uint64_t cand = 0ull;  // bit i: key[i] is an evictable candidate
+  if (RANDOM) {
+    // A draw costs about a hundred instructions: groups of rounds with no evictable slot in this
+    // wave are skipped (a wave-uniform test per group), the rest run straight-line so that the
+    // group's draws interleave.
+    constexpr int GR = R < 8 ? R : 8;
+    const uint32_t c1 = p.shared_draw ? 0u : (static_cast<uint32_t>(hd.l) << 16) | static_cast<uint32_t>(hd.h);
+    const __amdgpu_buffer_rsrc_t rp = rsrc_of(p.pos ? p.pos + slot0 : p.seq_len, p.pos ? e_hi * 4 : 0);
+    const int j0 = slot_base();
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int j = slot_of(i);
-    cand |= static_cast<uint64_t>(j >= e_lo && j < e_hi) << i;
+    for (int g = 0; g < R; g += GR) {
+      const int first = (wave * R + g) * 64, end = first + GR * 64;   // the group's slots in this wave
+#pragma unroll
+      for (int i = g; i < g + GR; ++i) key[i] = 0u;
+      if (end > e_lo && first < e_hi) {
+#pragma unroll
+        for (int i = g; i < g + GR; ++i) {
+          const int j = j0 + i * 64;
+          const uint32_t c0 = p.pos ? ld32(rp, j * 4, 0) : static_cast<uint32_t>(j);
+          const uint32_t w = philox_word0(c0, c1, static_cast<uint32_t>(hd.s), p.event, p.seed_lo, p.seed_hi);
+          key[i] = evictable(j0, i) ? w : 0u;
+        }
+      }
+    }
   }
-  const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
-  const int passes = UNION ? (n_sel > 0 ? p.G : 0) + 1 : 1;
-  const int k_head = UNION ? (p.k_per_head > 0 ? p.k_per_head : (n_sel + p.G - 1) / p.G) : 0;
-  uint64_t umask = 0ull;    // union: slots some query head ranks in its top-k
 
-  uint32_t key[KPT];
+  const int passes = UNION ? p.G + 1 : 1;
+  const int k_head = UNION ? (p.k_per_head > 0 ? p.k_per_head : (n_sel + p.G - 1) / p.G) : 0;
+  uint32_t umask = 0u;   // union: bit i set when round i's slot is in some query head's top-k
+
 #pragma unroll 1
   for (int pass = 0; pass < passes; ++pass) {
     const bool last = pass == passes - 1;
-    // ---- 1. keys: key[4*i + q] belongs to slot 4*(i*NT + tid) + q
     if (!RANDOM) {
-      const float *row = p.scores + slot0;
-      if (UNION && !last) row = p.head_scores + (static_cast<size_t>(head) * p.G + pass) * p.t_cap;
+      const float *row = UNION && !last ? p.head_scores + (static_cast<size_t>(hd.head) * p.G + pass) * p.t_cap
+                                        : p.scores + slot0;
+      // the offset rides in the per-lane operand and the instruction's offset, which the buffer's
+      // range check covers: slots at or past e_hi read 0 without a memory access
+      const __amdgpu_buffer_rsrc_t rs = rsrc_of(row, e_hi * 4);
+      const int j0 = slot_base();
+#pragma unroll
+      for (int i = 0; i < R; ++i) key[i] = ld32(rs, j0 * 4 + i * 256, 0);
+      const int j1 = slot_base();
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const int j4 = 4 * (i * NT + tid);
-        if (VEC) {
-          float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (j4 < p.t_cap) f = *reinterpret_cast<const float4 *>(row + j4);
-          key[4 * i] = order_key(f.x);
-          key[4 * i + 1] = order_key(f.y);
-          key[4 * i + 2] = order_key(f.z);
-          key[4 * i + 3] = order_key(f.w);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) key[4 * i + q] = (j4 + q < T) ? order_key(row[j4 + q]) : 0u;
-        }
-      }
-    } else {
-      const uint32_t c1 = p.shared_draw ? 0u : (static_cast<uint32_t>(l) << 16) | static_cast<uint32_t>(h);
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int j = slot_of(i);
-        uint32_t k = 0u;
-        if (j >= e_lo && j < e_hi) {
-          const uint32_t c0 = p.pos ? static_cast<uint32_t>(p.pos[slot0 + j]) : static_cast<uint32_t>(j);
-          k = philox_word0(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
-        }
-        key[i] = k;
+        const float x = fmaxf(__uint_as_float(key[i]), -INFINITY);   // NaN ranks as -inf
+        key[i] = evictable(j1, i) ? __float_as_uint(x) : kNoKey;
       }
     }
-    // Union, last pass: rank by the combined score with the union folded into the keys. A long
-    // union (>= n_sel slots) drops every other slot to key 0, below any score; a short one lifts
-    // its own slots to the top key, above any score, so the top-up comes from the rest.
-    int p_sel = n_sel;
+    int p_sel = n_sel, n_valid = n_cand;
+    bool short_union = false;
     if (UNION && !last) {
       p_sel = k_head;
     } else if (UNION) {
-      uint32_t nu = static_cast<uint32_t>(__popcll(umask));
-      nu = wave_total(wave_inclusive_sum(nu));
-      if (lane == 0) red[wave] = nu;
-      __syncthreads();
-      int n_union = 0;
+      const int n_union = static_cast<int>(block_sum<NT>(static_cast<uint32_t>(__builtin_popcount(umask)), sm.red));
+      // A long union (>= n_sel slots) is ranked alone; a short one is kept whole and the rest of the
+      // evictable range ranks for the places that remain.
+      short_union = n_union < n_sel;
+      const uint32_t drop = short_union ? umask : ~umask;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) n_union += static_cast<int>(red[w]);
-      __syncthreads();
-      const bool long_union = n_union >= n_sel;
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const bool in_u = (umask >> i) & 1ull;
-        if (long_union && !in_u) key[i] = 0u;
-        if (!long_union && in_u) key[i] = 0xFFFFFFFFu;
+      for (int i = 0; i < R; ++i)
+        if ((drop >> i) & 1u) key[i] = kNoKey;
+      if (short_union) {
+        p_sel = n_sel - n_union;
+        n_valid = n_cand - n_union;
+      } else {
+        n_valid = n_union;
       }
     }
 
-    // ---- 2./3. threshold: thr = p_sel-th largest candidate key; take `need` of the keys == thr
-    // mode: 0 = select none, 1 = select all candidates, 2 = threshold rule
-    int mode;
-    uint32_t thr = 0u, need = 0u;
-    bool all_ties = false;  // every key equal to thr is taken
-    if (p_sel <= 0 || n_cand <= 0) {
-      mode = 0;
-    } else if (p_sel >= n_cand) {
-      mode = 1;
-    } else {
-      mode = 2;
+    // ---- threshold: thr = the p_sel-th largest valid key; `need` of the keys equal to it are taken
+    // mode: 0 = take none, 1 = take every valid key, 2 = threshold rule
+    const int mode = p_sel <= 0 ? 0 : (p_sel >= n_valid ? 1 : 2);
+    uint32_t thr = 0u, need = 0u;   // thr as an order key (scores) or a word (random)
+    bool all_ties = true;           // every key equal to thr is taken
+    bool careful = false;           // random keys: the slot range decides membership, ties, placement
+    if (mode == 2) {
       uint32_t remaining = static_cast<uint32_t>(p_sel);
-      uint64_t mem = cand;  // keys the exact radix passes still have to order
-      bool ranked = false;  // threshold found by ranking a short member list
-      // Pass 1: 1024 bins. Scores are binned uniformly in value between the smallest and largest
-      // finite candidate (binning by value keeps a concentrated score distribution from piling
-      // into a few bins); uniform random keys by their top 10 bits. The binning is monotone, so
-      // the threshold lies in one bin and every key in a higher bin is strictly larger; the exact
-      // step then only sees that bin's keys.
-      bool binned = RANDOM;
-      float fmin = 0.f, scale = 0.f;
+      bool binned = RANDOM, ranked = false;
+      float scale = 0.f, off = 0.f;
       if (!RANDOM) {
-        uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+        float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-          if (((cand >> i) & 1ull) && key[i] > kKeyNegInf && key[i] < kKeyPosInf) {
-            kmn = min(kmn, key[i]);
-            kmx = max(kmx, key[i]);
-          }
+        for (int i = 0; i < R; ++i) {
+          mn = fminf(mn, fkey(i));
+          mx = fmaxf(mx, fkey(i));
         }
-        block_min_max<NT>(kmn, kmx, red);
-        fmin = key_value(kmn);
-        const float fmax = key_value(kmx);
-        scale = static_cast<float>(kValueBins) / (fmax - fmin);
-        binned = kmn < kmx && scale > 0.f && scale < 3.0e38f;
-      }
-      {
-        auto bin_of = [&](uint32_t k) { return RANDOM ? (k >> 22) : value_bin(k, fmin, scale); };
-        if (binned) {
-          for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
-          if (tid == 0) n_members = 0u;
-          __syncthreads();
+        block_fmin_fmax<NT>(mn, mx, sm.fred);
+        if (!(mn > -INFINITY && mx < INFINITY)) {   // an infinite key: the range of the finite ones
+          mn = INFINITY;
+          mx = -INFINITY;
 #pragma unroll
-          for (int i = 0; i < KPT; ++i)
-            if ((cand >> i) & 1ull) atomicAdd(&hist[bin_of(key[i])], 1u);
-          __syncthreads();
-          if (wave == 0) find_bin<kValueBins>(hist, remaining, lane, found);
-          __syncthreads();
-          const uint32_t b = found[0];
-          remaining -= found[1];
-          mem = 0ull;
-          // Membership in the threshold's bin. With 32 or more keys per thread, testing each key
-          // against the bin's key interval (found once by waves 0 and 1) beats evaluating its bin
-          // again; with fewer, the search and its barrier cost more than they save (2176-slot
-          // heads: 0.095 -> 0.111 ms). A random key's bin is a shift, cheaper than either.
-          if constexpr (!RANDOM && KPT >= 32) {
-            bin_interval<RANDOM>(b, fmin, scale, wave, lane, kb);
-            __syncthreads();
-            const uint32_t klo = kb[0], khi = kb[1];
-#pragma unroll
-            for (int i = 0; i < KPT; ++i)
-              if (((cand >> i) & 1ull) && key[i] >= klo && key[i] <= khi) mem |= 1ull << i;
-          } else {
-#pragma unroll
-            for (int i = 0; i < KPT; ++i)
-              if (((cand >> i) & 1ull) && bin_of(key[i]) == b) mem |= 1ull << i;
-          }
-          __syncthreads();  // `found` and `hist` are reused below
-          // The threshold's bin usually holds a few keys: list them in LDS (hist is free) and rank
-          // them directly instead of running the radix passes.
-#pragma unroll
-          for (int i = 0; i < KPT; ++i) {
-            if ((mem >> i) & 1ull) {
-              const uint32_t at = atomicAdd(&n_members, 1u);
-              if (at < member_cap<NT>()) hist[at] = key[i];
+          for (int i = 0; i < R; ++i) {
+            const float x = fkey(i);
+            if (x > -INFINITY && x < INFINITY) {
+              mn = fminf(mn, x);
+              mx = fmaxf(mx, x);
             }
           }
-          __syncthreads();
-          const uint32_t m = n_members;
-          if (m <= member_cap<NT>()) {
-            if (tid < 4) hist[m + tid] = 0u;   // pad to a multiple of 4 (m + 3 < kValueBins)
-            __syncthreads();
-            rank_members<NT>(hist, m, remaining, found);
-            __syncthreads();
-            thr = found[0];
-            need = found[1];
-            all_ties = found[2] == need;   // equal keys share the threshold's bin: all are listed
-            ranked = true;
-          }
-          __syncthreads();  // `found`, `hist` and n_members are reused below
+          block_fmin_fmax<NT>(mn, mx, sm.fred);
         }
+        scale = static_cast<float>(kValueBins) / (mx - mn);
+        off = -mn * scale;
+        binned = mn < mx && scale > 0.f && scale < 3.0e38f && fabsf(off) < 3.0e38f;
       }
-      // Exact radix passes over the member keys, from their highest differing bit.
-      if (!ranked) {
+      __syncthreads();   // the previous pass's readers of hist are done
+      // valid: the key takes part (scores: not the NaN mark; random: the slot range)
+      auto valid = [&](int i, int j0) {
+        if (RANDOM) return evictable(j0, i);
+        return fkey(i) == fkey(i);
+      };
+      // exact radix passes over the keys member(i, j0) still has to order
+      auto radix = [&](auto member) {
         uint32_t kor = 0u, kand = 0xFFFFFFFFu;
+        const int j0 = slot_base();
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-          if ((mem >> i) & 1ull) {
-            kor |= key[i];
-            kand &= key[i];
+        for (int i = 0; i < R; ++i)
+          if (member(i, j0)) {
+            kor |= okey(i);
+            kand &= okey(i);
           }
-        }
-        block_or_and<NT>(kor, kand, red);
+        block_or_and<NT>(kor, kand, sm.red);
         const uint32_t diff = kor ^ kand;
         if (diff == 0u) {
-          thr = kand;  // all member keys equal
+          thr = kand;   // all member keys equal
         } else {
           const int top = 31 - __clz(diff);
           uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
@@ -506,93 +540,217 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
             const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
             for (int i = tid; i < 256; i += NT) hist[i] = 0u;
             __syncthreads();
+            const int j1 = slot_base();
 #pragma unroll
-            for (int i = 0; i < KPT; ++i) {
-              if (((mem >> i) & 1ull) && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> lo) & dmask], 1u);
-            }
+            for (int i = 0; i < R; ++i)
+              if (member(i, j1) && (okey(i) & mask) == prefix) atomicAdd(&hist[(okey(i) >> lo) & dmask], 1u);
             __syncthreads();
             if (wave == 0) find_bin<256>(hist, remaining, lane, found);
             __syncthreads();
-            const uint32_t digit = found[0];
-            remaining -= found[1];
-            prefix |= digit << lo;
+            prefix |= found[0] << lo;
             mask |= dmask << lo;
+            remaining -= found[1];
             hi = lo - 1;
             __syncthreads();  // everyone has read `found` before the next pass may overwrite it
           }
           thr = prefix;
         }
         need = remaining;
+        all_ties = false;
+      };
+      if (binned) {
+        for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
+        if (tid == 0) *sm.n_members = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < R; ++i)   // NaN marks and random 0 marks land in bin 0
+          atomicAdd(&hist[RANDOM ? key[i] >> 22 : bin_of_value(fkey(i), scale, off)], 1u);
+        __syncthreads();
+        if (wave == 0) find_bin<kValueBins>(hist, remaining, lane, found);
+        __syncthreads();
+        const uint32_t b = found[0];
+        remaining -= found[1];
+        careful = RANDOM && b == 0u;
+        // Members of the threshold's bin: a key-interval test. Random keys' bins are their top 10
+        // bits; for scores every wave finds the bin's bounds itself (no barrier).
+        uint32_t klo, khi;
+        if (RANDOM) {
+          klo = b << 22;
+          khi = (b << 22) | 0x3FFFFFu;
+        } else {
+          klo = static_cast<uint32_t>(first_key_reaching_near(b, scale, off, lane));
+          khi = static_cast<uint32_t>(first_key_reaching_near(b + 1u, scale, off, lane) - 1u);
+        }
+        const float flo = key_value(max(klo, kKeyNegInf)), fhi = key_value(min(khi, kKeyPosInf));
+        auto member = [&](int i, int j0) {
+          if (RANDOM) return key[i] >= klo && key[i] <= khi && (!careful || valid(i, j0));
+          return fkey(i) >= flo && fkey(i) <= fhi;
+        };
+        // The bin usually holds a few dozen keys: list them in LDS (hist is free once every wave
+        // has read `found`) and rank them directly.
+        __syncthreads();
+        const int jm = slot_base();
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          if (member(i, jm)) {
+            const uint32_t at = atomicAdd(sm.n_members, 1u);
+            if (at < member_cap<NT>()) hist[at] = okey(i);
+          }
+        }
+        __syncthreads();
+        const uint32_t m = *sm.n_members;
+        if (m <= member_cap<NT>()) {
+          if (tid < 4) hist[m + tid] = 0u;   // pad to a multiple of 4 (m + 3 < kValueBins)
+          __syncthreads();
+          rank_members<NT>(hist, m, remaining, found);
+          __syncthreads();
+          thr = found[0];
+          need = found[1];
+          all_ties = found[2] == need;   // equal keys share the threshold's bin: all are listed
+          ranked = true;
+        }
+        if (!ranked) radix(member);   // a crowded bin: exact radix passes over its keys
+      } else {
+        // no usable value range (all finite candidates equal, or none finite): radix passes over
+        // every valid key
+        radix(valid);
       }
     }
 
-    // ---- 4. one ordered scan: unconditional (A) and equal-to-thr (E) slots before each slot.
-    // The last pass writes the kept list; a union head pass adds its top-k to the union.
-    uint64_t fa = 0ull, fe = 0ull;
+    // ---- placement. A: kept outright (above the threshold, or equal to it when every tie is
+    // taken, or a short union's own slot); E: equal to the threshold, kept while fewer than `need`
+    // earlier (lower-slot) ties are. A is one comparison against a bound: scores x >= a_f (mode 2:
+    // thr, or the next key up when ties are ranked; mode 1: -inf; mode 0: NaN), random keys
+    // key + a_add > a_thr in 64 bits.
+    const bool ties = mode == 2 && !all_ties;
+    const float thr_f = key_value(thr);
+    const float a_f = mode == 2 ? key_value(all_ties ? thr : thr + 1u) : (mode == 1 ? -INFINITY : __uint_as_float(kNoKey));
+    const uint64_t a_thr = mode == 2 ? thr : (mode == 1 ? 0ull : 0xFFFFFFFFull);
+    const uint64_t a_add = mode == 2 ? (all_ties ? 1ull : 0ull) : (mode == 1 ? 1ull : 0ull);
+    const uint32_t extra = UNION && last && short_union ? umask : 0u;
+    auto place = [&](auto careful_t) {
+      constexpr bool CAREFUL = decltype(careful_t)::value;
+      auto in_range = [&](int i, int j0) { return !CAREFUL || evictable(j0, i); };
+      auto is_a = [&](int i, int j0) {
+        bool a;
+        if (RANDOM) a = static_cast<uint64_t>(key[i]) + a_add > a_thr && in_range(i, j0);
+        else a = fkey(i) >= a_f;
+        if (UNION) a = a || ((extra >> i) & 1u);
+        return a;
+      };
+      auto is_e = [&](int i, int j0) { return RANDOM ? (key[i] == thr && in_range(i, j0)) : fkey(i) == thr_f; };
+      if (UNION && !last && !ties) {   // a query head's top-k needs no order
+        const int j0 = slot_base();
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const bool c = (cand >> i) & 1ull;
-      const bool pinned = last && !c && slot_of(i) < T;  // prompt or recent window
-      const bool a = pinned || (c && (mode == 1 || (mode == 2 && key[i] > thr)));
-      const bool e = c && mode == 2 && key[i] == thr;
-      fa |= static_cast<uint64_t>(a) << i;
-      fe |= static_cast<uint64_t>(e) << i;
-    }
-    if (UNION && !last) {
-      umask |= fa;
-      if (mode != 2) continue;   // uniform: no ties to rank
-      if (all_ties) {            // uniform: the ties need no order either
-        umask |= fe;
-        continue;
+        for (int i = 0; i < R; ++i)
+          if (is_a(i, j0)) umask |= 1u << i;
+        return;
       }
-      fa = 0ull;
-    }
-    // per round: the two counts packed as (A | E << 16); a wave's sums stay below 2^9 per half
-    uint32_t ex[R];
+      // this wave's totals, then the totals of the lower waves
+      uint32_t ta = 0u, te = 0u;
+      const int jc = slot_base();
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const uint32_t c = static_cast<uint32_t>(__popcll((fa >> (4 * i)) & 0xFull)) |
-                         (static_cast<uint32_t>(__popcll((fe >> (4 * i)) & 0xFull)) << 16);
-      const uint32_t x = wave_inclusive_sum(c);
-      if (lane == 63) {
-        tot_a[i * NW + wave] = x & 0xFFFFu;
-        tot_e[i * NW + wave] = x >> 16;
+      for (int i = 0; i < R; ++i) {
+        ta += static_cast<uint32_t>(__popcll(__ballot(is_a(i, jc))));
+        if (ties) te += static_cast<uint32_t>(__popcll(__ballot(is_e(i, jc))));
       }
-      ex[i] = x - c;
-    }
-    __syncthreads();
-    if (wave == 0) wave_exclusive_scan_lds(tot_a, R * NW, lane);
-    if (wave == (NW > 1 ? 1 : 0)) wave_exclusive_scan_lds(tot_e, R * NW, lane);
-    __syncthreads();
+      __syncthreads();   // the previous pass's readers of cnt_a / cnt_e are done
+      if (lane == 0) {
+        sm.cnt_a[wave] = ta;
+        sm.cnt_e[wave] = te;
+      }
+      __syncthreads();
+      const uint32_t va = lane < NW ? sm.cnt_a[lane] : 0u, ve = lane < NW ? sm.cnt_e[lane] : 0u;
+      uint32_t na = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_inclusive_sum(va) - va), wave));
+      uint32_t ne = ties ? static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_inclusive_sum(ve) - ve), wave)) : 0u;
+      const int jp = slot_base();
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      uint32_t na = tot_a[i * NW + wave] + (ex[i] & 0xFFFFu);
-      uint32_t ne = tot_e[i * NW + wave] + (ex[i] >> 16);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int bit = 4 * i + q;
-        const int j = slot_of(bit);
-        if ((fa >> bit) & 1ull) {
-          const uint32_t o = na + min(ne, need);
-          if (static_cast<int>(o) < p.b_cap) out[o] = j;
-          ++na;
-        } else if ((fe >> bit) & 1ull) {
-          if (ne < need) {
-            if (UNION && !last) {
-              umask |= 1ull << bit;
-            } else {
-              const uint32_t o = na + ne;
-              if (static_cast<int>(o) < p.b_cap) out[o] = j;
-            }
-          }
-          ++ne;
+      for (int i = 0; i < R; ++i) {
+        const bool a = is_a(i, jp);
+        const uint64_t ba = __ballot(a);
+        const uint32_t ra = na + lanes_below(ba);   // kept-outright slots before this one
+        na += static_cast<uint32_t>(__popcll(ba));
+        uint32_t re = 0u;
+        bool e = false;
+        if (ties) {
+          e = is_e(i, jp);
+          const uint64_t be = __ballot(e);
+          re = ne + lanes_below(be);                // tied slots before this one
+          ne += static_cast<uint32_t>(__popcll(be));
+        }
+        const bool take_e = e && re < need;
+        if (UNION && !last) {
+          if (a || take_e) umask |= 1u << i;
+        } else if (a || take_e) {
+          const uint32_t o = static_cast<uint32_t>(P) + ra + (a ? min(re, need) : re);
+          if (o < static_cast<uint32_t>(p.b_cap)) hd.out[o] = jp + i * 64;
         }
       }
-    }
-    if (UNION && !last) __syncthreads();  // tot_a / tot_e are rewritten by the next pass
+    };
+    if (RANDOM && careful) place(std::true_type{});
+    else place(std::false_type{});
   }
+}
+
+// One workgroup per (layer, seq, KV head): the partition, the fixed places of the prompt and the
+// recent window, then the ranking over R rounds, R the smallest of KPT/4, KPT/2 and KPT whose
+// NT*R slots reach the last evictable one.
+template <int NT, int KPT, int KIND>
+__global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
+  constexpr int NW = NT / 64;
+  __shared__ __align__(16) uint32_t hist[kValueBins];
+  __shared__ float fred[2 * NW];
+  __shared__ uint32_t red[2 * NW];
+  __shared__ uint32_t cnt_a[NW];
+  __shared__ uint32_t cnt_e[NW];
+  __shared__ uint32_t found[3];
+  __shared__ uint32_t n_members;
+  SelectSmem sm;   // filled field by field: an aggregate initialiser of LDS addresses is not
+                   // accepted by the unoptimised device build
+  sm.hist = hist;
+  sm.fred = fred;
+  sm.red = red;
+  sm.cnt_a = cnt_a;
+  sm.cnt_e = cnt_e;
+  sm.found = found;
+  sm.n_members = &n_members;
+
+  const int tid = threadIdx.x;
+  SelectHead hd;
+  hd.head = blockIdx.x;
+  hd.h = hd.head % p.H;
+  hd.s = (hd.head / p.H) % p.S;
+  hd.l = hd.head / (p.H * p.S);
+  // per-sequence values are uniform: keep them in scalar registers
+  const int T = __builtin_amdgcn_readfirstlane(min(max(p.seq_len[hd.s], 0), p.t_cap));
+  const int P = __builtin_amdgcn_readfirstlane(min(max(p.prompt_len[hd.s], 0), min(p.prompt_cap, T)));
+  const int B = p.budget;
+  int32_t *out = p.kept + static_cast<size_t>(hd.head) * p.b_cap;
+  const bool writer = (hd.l == 0 && hd.h == 0 && tid == 0);
+
+  if (T <= B) {  // nothing to compress: keep 0..T-1
+    for (int r = tid; r < p.b_cap; r += NT) out[r] = r < T ? r : -1;
+    if (writer) p.n_kept[hd.s] = T;
+    return;
+  }
+  const int Rw = min(p.recent, min(max(0, B - P), T - P));
+  hd.P = P;
+  hd.e_lo = P;
+  hd.e_hi = T - Rw;
+  hd.n_sel = max(0, B - P - Rw);
+  hd.n_cand = hd.e_hi - hd.e_lo;
+  hd.out = out;
+  const int n_kept = max(B, P);
+  for (int r = tid; r < P; r += NT) out[r] = r;
+  for (int r = tid; r < Rw; r += NT) out[P + hd.n_sel + r] = hd.e_hi + r;
   for (int r = n_kept + tid; r < p.b_cap; r += NT) out[r] = -1;
-  if (writer) p.n_kept[s] = n_kept;
+  if (writer) p.n_kept[hd.s] = n_kept;
+  if (hd.n_sel <= 0) return;   // n_sel > 0 implies n_cand > n_sel (T > B)
+
+  const int rounds = (hd.e_hi + NT - 1) / NT;
+  if (KPT >= 8 && rounds <= KPT / 4) select_rounds<NT, (KPT >= 8 ? KPT / 4 : KPT), KIND>(p, sm, hd);
+  else if (KPT >= 4 && rounds <= KPT / 2) select_rounds<NT, (KPT >= 4 ? KPT / 2 : KPT), KIND>(p, sm, hd);
+  else select_rounds<NT, KPT, KIND>(p, sm, hd);
 }
 
 // Caches past the register tiers (top-k and random past 32768 slots, the union past 65536;
@@ -702,8 +860,8 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
       // or every candidate when the scores have no usable value range
       bool binned = RANDOM, ranked = false;
       uint32_t bsel = 0u, klo = 0u, khi = 0xFFFFFFFFu;   // key interval of the threshold's bin
-      float fmin = 0.f, scale = 0.f;
-      auto bin_of = [&](uint32_t k) { return RANDOM ? (k >> 22) : value_bin(k, fmin, scale); };
+      float scale = 0.f, off = 0.f;
+      auto bin_of = [&](uint32_t k) { return RANDOM ? (k >> 22) : bin_of_key(k, scale, off); };
       if (!RANDOM) {
         uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
         for (int j = e_lo + tid; j < e_hi; j += NT) {
@@ -714,10 +872,10 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
           }
         }
         block_min_max<NT>(kmn, kmx, red);
-        fmin = key_value(kmn);
-        const float fmax = key_value(kmx);
+        const float fmin = key_value(kmn), fmax = key_value(kmx);
         scale = static_cast<float>(kValueBins) / (fmax - fmin);
-        binned = kmn < kmx && scale > 0.f && scale < 3.0e38f;
+        off = -fmin * scale;
+        binned = kmn < kmx && scale > 0.f && scale < 3.0e38f && fabsf(off) < 3.0e38f;
       }
       if (binned) {
         for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
@@ -729,7 +887,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
         __syncthreads();
         bsel = found[0];
         remaining -= found[1];
-        bin_interval<RANDOM>(bsel, fmin, scale, wave, lane, kb);
+        bin_interval<RANDOM>(bsel, scale, off, wave, lane, kb);
         __syncthreads();  // `found` and `hist` are reused below; kb is written
         klo = kb[0];
         khi = kb[1];
@@ -931,23 +1089,14 @@ __global__ __launch_bounds__(256) void audit_kernel(const SelectParams p, int32_
 }
 
 // Only the (tier, ranking) pairs launch_select dispatches are instantiated.
-template <int NT, int KPT, bool UNION>
+template <int NT, int KPT>
 hipError_t launch_cfg(const SelectParams &p, SelectKind kind, dim3 grid, hipStream_t st) {
-  bool vec = (p.t_cap % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.scores) & 15u) == 0);
-  if constexpr (UNION) {
-    vec = vec && ((reinterpret_cast<uintptr_t>(p.head_scores) & 15u) == 0);
-    if (vec)
-      hipLaunchKernelGGL((select_kernel<NT, KPT, 2, true>), grid, dim3(NT), 0, st, p);
-    else
-      hipLaunchKernelGGL((select_kernel<NT, KPT, 2, false>), grid, dim3(NT), 0, st, p);
-  } else {
-    if (kind == SelectKind::kRandom)
-      hipLaunchKernelGGL((select_kernel<NT, KPT, 1, false>), grid, dim3(NT), 0, st, p);
-    else if (vec)
-      hipLaunchKernelGGL((select_kernel<NT, KPT, 0, true>), grid, dim3(NT), 0, st, p);
-    else
-      hipLaunchKernelGGL((select_kernel<NT, KPT, 0, false>), grid, dim3(NT), 0, st, p);
-  }
+  if (kind == SelectKind::kUnion)
+    hipLaunchKernelGGL((select_kernel<NT, KPT, 2>), grid, dim3(NT), 0, st, p);
+  else if (kind == SelectKind::kRandom)
+    hipLaunchKernelGGL((select_kernel<NT, KPT, 1>), grid, dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((select_kernel<NT, KPT, 0>), grid, dim3(NT), 0, st, p);
   return hipGetLastError();
 }
 
@@ -968,48 +1117,32 @@ hipError_t launch_select_recent(const SelectParams &p, hipStream_t st) {
   return hipGetLastError();
 }
 
+size_t select_scratch_bytes(int, int, int, int) { return 0; }
+
 hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st) {
   const long long heads = static_cast<long long>(p.L) * p.S * p.H;
   if (heads <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(heads));
   const int t = p.t_cap;
+  // Register tiers: NT threads x KPT rounds of one key each cover t_cap slots.
+  if (t <= kSelectMaxSlots) {
+    if (t <= 256 * 8) return launch_cfg<256, 8>(p, kind, grid, st);
+    if (t <= 256 * 16) return launch_cfg<256, 16>(p, kind, grid, st);
+    if (t <= 512 * 16) return launch_cfg<512, 16>(p, kind, grid, st);
+    if (t <= 1024 * 16) return launch_cfg<1024, 16>(p, kind, grid, st);
+    return launch_cfg<1024, 32>(p, kind, grid, st);
+  }
+  // Past the tiers, the re-reading kernel (the union keeps its bits in dynamic LDS).
   if (kind == SelectKind::kUnion) {
-    // The union's extra passes hold more registers: past 8192 slots it runs 512-thread tiers
-    // (a 1024-thread workgroup is limited to 128 registers per lane); past 65536 slots, the
-    // re-reading kernel with the union bits in dynamic LDS.
-    if (t <= KV_UNION_STREAM_ABOVE) {
-      if (t <= 256 * 4) return launch_cfg<256, 4, true>(p, kind, grid, st);
-      if (t <= 256 * 16) return launch_cfg<256, 16, true>(p, kind, grid, st);
-      if (t <= 256 * 32) return launch_cfg<256, 32, true>(p, kind, grid, st);
-      if (t <= 512 * 32) return launch_cfg<512, 32, true>(p, kind, grid, st);
-      if (t <= 512 * 64) return launch_cfg<512, 64, true>(p, kind, grid, st);
-      if (t <= 1024 * 64) return launch_cfg<1024, 64, true>(p, kind, grid, st);
-    }
     if (t > kSelectMaxSlotsUnion) return hipErrorInvalidValue;
     const size_t union_bytes = static_cast<size_t>((t + 31) / 32) * 4;
     hipLaunchKernelGGL(select_stream_kernel<2>, grid, dim3(kStreamThreads), union_bytes, st, p);
-    return hipGetLastError();
+  } else if (kind == SelectKind::kRandom) {
+    hipLaunchKernelGGL(select_stream_kernel<1>, grid, dim3(kStreamThreads), 0, st, p);
+  } else {
+    hipLaunchKernelGGL(select_stream_kernel<0>, grid, dim3(kStreamThreads), 0, st, p);
   }
-  if (t > KV_SELECT_STREAM_ABOVE) {
-    if (kind == SelectKind::kRandom)
-      hipLaunchKernelGGL(select_stream_kernel<1>, grid, dim3(kStreamThreads), 0, st, p);
-    else
-      hipLaunchKernelGGL(select_stream_kernel<0>, grid, dim3(kStreamThreads), 0, st, p);
-    return hipGetLastError();
-  }
-  if (t <= 256 * 4) return launch_cfg<256, 4, false>(p, kind, grid, st);
-  if (t <= 256 * 16) return launch_cfg<256, 16, false>(p, kind, grid, st);
-  if (t <= 256 * 32) return launch_cfg<256, 32, false>(p, kind, grid, st);
-  if (t <= 512 * 32) return launch_cfg<512, 32, false>(p, kind, grid, st);
-#if KV_SELECT_WIDE
-  if (t <= 512 * 64) return launch_cfg<512, 64, false>(p, kind, grid, st);
-#else
-  if (t <= 1024 * 32) return launch_cfg<1024, 32, false>(p, kind, grid, st);
-#endif
-#if KV_SELECT_STREAM_ABOVE > 32768
-  if (t <= 1024 * 64) return launch_cfg<1024, 64, false>(p, kind, grid, st);
-#endif
-  return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace kvevict

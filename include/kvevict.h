@@ -29,7 +29,22 @@
  *    where marked "host". The library allocates nothing, keeps no global
  *    state, and never synchronises the stream; every call only enqueues
  *    kernels on `stream` (a hipStream_t; NULL = the null stream) and
- *    returns. Calls are re-entrant.
+ *    returns. Calls are re-entrant given distinct workspaces.
+ *  - Workspaces. tri_score, the selectors and tri_score_gqa take caller-owned
+ *    device scratch memory (`workspace`, `workspace_bytes`) sized by the
+ *    matching *_workspace_bytes query; a NULL, misaligned (8 bytes) or
+ *    smaller workspace is rejected with KV_EWORKSPACE. Its first 256 bytes are
+ *    a header: the first 4 are the device status word below, the rest is
+ *    reserved. Contents beyond the header on entry do not matter and on return
+ *    are unspecified. Calls that share a workspace must not overlap in time.
+ *  - Device status word (first uint32 of a workspace). Preconditions on device
+ *    data (valid lengths, prompt lengths, position order) cannot be checked on
+ *    the host without a synchronisation. A build with device checks
+ *    (kv_device_checks() == 1, libkvevict_debug.so) verifies them in an extra
+ *    kernel before each call's own kernels and ORs KV_DEV_* bits into the word;
+ *    the caller clears it. The release build never touches it. Either way the
+ *    kernels clamp device values into the validated ranges, so memory safety
+ *    never depends on them.
  *  - Cache layout is head-major: element (l, s, h, j, e) of a
  *    [n_layers, n_seq, n_kv_heads, t_cap, head_dim] tensor lives at
  *    ((((l*n_seq + s)*n_kv_heads + h)*t_cap + j)*head_dim + e). Per-slot
@@ -69,8 +84,17 @@ typedef enum kv_status {
   KV_EINVAL = -1,   /* NULL or misaligned pointer, non-positive size, bad policy value, aliasing outputs */
   KV_EDTYPE = -2,   /* unknown element type */
   KV_ESHAPE = -3,   /* head_dim / capacity outside what the kernels support */
+  KV_EWORKSPACE = -4, /* workspace NULL, not 8-byte aligned, or smaller than its query returns */
   KV_EHIP = -5      /* a kernel launch failed (hipGetLastError after the launch) */
 } kv_status;
+
+/* Bits of the device status word (debug build only; see "Device status word" above). */
+#define KV_DEV_SEQ_LEN 0x1u    /* some seq_len[s] outside [0, t_cap]: clamped into it            */
+#define KV_DEV_PROMPT_LEN 0x2u /* some prompt_len[s] outside [0, prompt_cap]: clamped (selectors) */
+#define KV_DEV_POS_ORDER 0x4u  /* some head's positions not strictly ascending over its valid
+                                  slots: slot order is then not time order, and ties break by
+                                  slot, not by position (expected after kv_compact_inplace)      */
+#define KV_WORKSPACE_HEADER 256 /* bytes of every workspace before any kernel scratch           */
 
 typedef enum kv_dtype {
   KV_F32 = 0,
@@ -124,6 +148,10 @@ int32_t kv_version(void);
 /* Static string for a kv_status value. */
 const char *kv_status_string(int32_t status);
 
+/* 1 when this library build checks device-side preconditions into the workspace status word
+ * (libkvevict_debug.so), 0 for the release build. */
+int32_t kv_device_checks(void);
+
 /*
  * tri_score -- importance of every cached key from the query centre.
  *
@@ -153,12 +181,19 @@ const char *kv_status_string(int32_t status);
  *  rope_theta  RoPE base (> 0).
  *  deltas   HOST [n_delta] int32 future offsets D, 1 <= n_delta <= 64.
  *  scores   device [L,S,H,t_cap] fp32 output; slots j >= T_s are not written.
+ *  workspace  device, at least kv_score_workspace_bytes(shape, n_delta) bytes (the header:
+ *           the score stream itself needs no scratch).
  * One head's rows must span less than 2 GiB (t_cap * head_dim * elem < 2^31 - 2^15).
+ * Device checks (debug build): KV_DEV_SEQ_LEN, and KV_DEV_POS_ORDER when pos is given.
  */
 kv_status tri_score(const kv_shape *shape, const void *K, const int32_t *pos,
                     const float *qbar, const float *qabs, const int32_t *t_cur, double rope_theta,
                     const int32_t *deltas, int32_t n_delta, float *scores,
-                    void *stream);
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes tri_score needs (0 for sizes it rejects: a shape outside its limits, or n_delta
+ * outside 1..64). shape->seq_len is not read and may be NULL. */
+size_t kv_score_workspace_bytes(const kv_shape *shape, int32_t n_delta);
 
 /* RoPE pairing of the stored coordinates: band f is (x[2f], x[2f+1]) or (x[f], x[f+d/2]). */
 typedef enum kv_rope_style {
@@ -223,10 +258,8 @@ kv_status tri_score_rotated(const kv_shape *shape, const void *K, const kv_paged
  *  qabs         device [L,H,G,d/2] fp32 or NULL.
  *  head_scores  device [L,S,H,G,t_cap] fp32 output (per-query-head scores).
  *  scores       device [L,S,H,t_cap] fp32 output.
- *  workspace    device, 8-byte aligned, at least
- *               kv_score_gqa_workspace_bytes(shape, group) bytes; its contents
- *               on entry do not matter and on return are unspecified.
- *               Calls that share a workspace must not overlap in time.
+ *  workspace    device, at least kv_score_gqa_workspace_bytes(shape, group)
+ *               bytes (the header, then the per-chunk partial sums).
  *  other arguments as for tri_score; slots j >= T_s are not written.
  */
 kv_status tri_score_gqa(const kv_shape *shape, const void *K, const int32_t *pos, int32_t group,
@@ -236,7 +269,8 @@ kv_status tri_score_gqa(const kv_shape *shape, const void *K, const int32_t *pos
                         size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace tri_score_gqa needs for this shape and group (0 for sizes or a group it
- * rejects). shape->seq_len is not read and may be NULL. tri_score_gqa_rotated needs the same. */
+ * rejects). shape->seq_len is not read and may be NULL. tri_score_gqa_rotated needs the same.
+ * Device checks (debug build): KV_DEV_SEQ_LEN, and KV_DEV_POS_ORDER when pos is given. */
 size_t kv_score_gqa_workspace_bytes(const kv_shape *shape, int32_t group);
 
 /*
@@ -273,14 +307,21 @@ kv_status tri_score_gqa_rotated(const kv_shape *shape, const void *K, const kv_p
  *  b_cap    must be >= max(budget, prompt_cap).
  *  n_kept   device [S] int32 output: |kept| of sequence s (same for every
  *           layer and head).
+ *  workspace  device, at least kv_select_workspace_bytes(shape, b_cap) bytes.
  * Requires t_cap <= 2^26. Up to 32768 slots a head's keys stay in registers;
  * longer caches (context lengths reach 128K tokens, [TA-sum] 3.4 "Handling
  * Multiple Future Positions", on the offset range) run a kernel that
  * re-reads the scores at every step.
+ * Device checks (debug build): KV_DEV_SEQ_LEN, KV_DEV_PROMPT_LEN.
  */
 kv_status kv_select_topk(const kv_shape *shape, const kv_policy *policy,
                          const float *scores, int32_t *kept, int32_t b_cap,
-                         int32_t *n_kept, void *stream);
+                         int32_t *n_kept, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* Workspace bytes kv_select_topk, kv_select_random and kv_select_random_shared need for this
+ * shape and b_cap (0 for sizes they reject). shape->seq_len is not read and may be NULL. */
+size_t kv_select_workspace_bytes(const kv_shape *shape, int32_t b_cap);
 
 /*
  * kv_select_random -- Random Attention's per-head uniform eviction.
@@ -294,13 +335,15 @@ kv_status kv_select_topk(const kv_shape *shape, const kv_policy *policy,
  *
  *  pos      device [L,S,H,t_cap] int32 positions for the counter, or NULL (p_j = j).
  *  seed     64-bit key; event: eviction counter (fresh draws per event).
- *  kept, b_cap, n_kept as for kv_select_topk (t_cap <= 2^26; past 32768
- *  slots the draws are recomputed at every step).
+ *  kept, b_cap, n_kept, workspace as for kv_select_topk (t_cap <= 2^26; past
+ *  32768 slots the draws are recomputed at every step).
+ * Device checks (debug build): KV_DEV_SEQ_LEN, KV_DEV_PROMPT_LEN, and
+ * KV_DEV_POS_ORDER when pos is given.
  */
 kv_status kv_select_random(const kv_shape *shape, const kv_policy *policy,
                            const int32_t *pos, uint64_t seed, uint32_t event,
                            int32_t *kept, int32_t b_cap, int32_t *n_kept,
-                           void *stream);
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * kv_audit_kept -- device-side audit of kept lists (for instance a caller's own selection, or a
@@ -348,12 +391,12 @@ kv_status kv_select_union(const kv_shape *shape, const kv_policy *policy, int32_
  * one random keep-set that every (layer, KV head) of a sequence uses. It is
  * kv_select_random with the counter's second word fixed to 0, i.e. every head
  * draws what layer 0 / KV head 0 draws. Heads whose position arrays agree keep
- * the same slots. Arguments as for kv_select_random.
+ * the same slots. Arguments (workspace included) as for kv_select_random.
  */
 kv_status kv_select_random_shared(const kv_shape *shape, const kv_policy *policy,
                                   const int32_t *pos, uint64_t seed, uint32_t event,
                                   int32_t *kept, int32_t b_cap, int32_t *n_kept,
-                                  void *stream);
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * kv_select_recent -- recency+prompt ([RA] section 4.1, the StreamingLLM-style

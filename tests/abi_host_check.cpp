@@ -28,21 +28,23 @@ int main() {
   kv_shape sh{1, 1, 1, 128, 4096, KV_BF16, seq};
   kv_policy pol{1024, 64, 128, seq};
 
-  if (kv_version() >> 16 != 1) ++failures;
+  if (kv_version() >> 16 != 2) ++failures;
+  if (kv_device_checks() != 0) ++failures;
+  void *wsp = reinterpret_cast<void *>(0x7000000);
   for (int s = -6; s <= 1; ++s)
     if (!kv_status_string(s) || !std::strlen(kv_status_string(s))) ++failures;
 
   // scoring: null shape, bad head_dim, bad dtype, misaligned keys, no offsets, bad theta
-  EXPECT(tri_score(nullptr, dummy, nullptr, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, (float *)dummy, nullptr), KV_EINVAL);
+  EXPECT(tri_score(nullptr, dummy, nullptr, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, (float *)dummy, wsp, 1 << 20, nullptr), KV_EINVAL);
   kv_shape odd = sh;
   odd.head_dim = 7;
-  EXPECT(tri_score(&odd, dummy, nullptr, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, (float *)dummy, nullptr), KV_ESHAPE);
+  EXPECT(tri_score(&odd, dummy, nullptr, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, (float *)dummy, wsp, 1 << 20, nullptr), KV_ESHAPE);
   kv_shape bad_dtype = sh;
   bad_dtype.dtype = 9;
-  EXPECT(tri_score(&bad_dtype, dummy, nullptr, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, (float *)dummy, nullptr), KV_EDTYPE);
-  EXPECT(tri_score(&sh, (void *)0x1008, nullptr, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, (float *)dummy, nullptr), KV_EINVAL);
-  EXPECT(tri_score(&sh, dummy, nullptr, (const float *)dummy, nullptr, seq, 1e4, deltas, 0, (float *)dummy, nullptr), KV_EINVAL);
-  EXPECT(tri_score(&sh, dummy, nullptr, (const float *)dummy, nullptr, seq, -1.0, deltas, 3, (float *)dummy, nullptr), KV_EINVAL);
+  EXPECT(tri_score(&bad_dtype, dummy, nullptr, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, (float *)dummy, wsp, 1 << 20, nullptr), KV_EDTYPE);
+  EXPECT(tri_score(&sh, (void *)0x1008, nullptr, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, (float *)dummy, wsp, 1 << 20, nullptr), KV_EINVAL);
+  EXPECT(tri_score(&sh, dummy, nullptr, (const float *)dummy, nullptr, seq, 1e4, deltas, 0, (float *)dummy, wsp, 1 << 20, nullptr), KV_EINVAL);
+  EXPECT(tri_score(&sh, dummy, nullptr, (const float *)dummy, nullptr, seq, -1.0, deltas, 3, (float *)dummy, wsp, 1 << 20, nullptr), KV_EINVAL);
 
   // rotated keys: unknown style and pool layout, a block table too short for t_cap
   EXPECT(tri_score_rotated(&sh, dummy, nullptr, 7, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, (float *)dummy, nullptr), KV_EINVAL);
@@ -55,12 +57,12 @@ int main() {
   kv_shape nolen = sh;
   nolen.seq_len = nullptr;
   const size_t need = kv_score_gqa_workspace_bytes(&nolen, 4);
-  if (need != 4 * 4 * 2 * sizeof(double)) ++failures;
+  if (need != KV_WORKSPACE_HEADER + 4 * 4 * 2 * sizeof(double)) ++failures;
   if (kv_score_gqa_workspace_bytes(&nolen, 17) != 0 || kv_score_gqa_workspace_bytes(nullptr, 4) != 0) ++failures;
   float *hs = reinterpret_cast<float *>(0x100000), *sc = reinterpret_cast<float *>(0x900000);
   void *ws = reinterpret_cast<void *>(0xA00000);
   EXPECT(tri_score_gqa(&sh, dummy, nullptr, 17, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, sc, ws, need, nullptr), KV_EINVAL);
-  EXPECT(tri_score_gqa(&sh, dummy, nullptr, 4, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, sc, ws, need - 8, nullptr), KV_ESHAPE);
+  EXPECT(tri_score_gqa(&sh, dummy, nullptr, 4, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, sc, ws, need - 8, nullptr), KV_EWORKSPACE);
   EXPECT(tri_score_gqa(&sh, dummy, nullptr, 4, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, hs, ws, need, nullptr), KV_EINVAL);
 
   // grouped-query scores of rotated keys: group beyond 8, head_dim beyond one piece per lane,
@@ -75,15 +77,29 @@ int main() {
   kv_paged pg3{seq, 256, 16, 8, 3};
   EXPECT(tri_score_gqa_rotated(&sh, dummy, &pg3, 0, 4, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, sc, ws, need, nullptr), KV_EINVAL);
 
+  // workspace queries and rejections: a missing, misaligned or short workspace
+  if (kv_score_workspace_bytes(&nolen, 3) != KV_WORKSPACE_HEADER || kv_score_workspace_bytes(&nolen, 0) != 0) ++failures;
+  const size_t need_sel = kv_select_workspace_bytes(&nolen, 1024);
+  if (need_sel < KV_WORKSPACE_HEADER || kv_select_workspace_bytes(&nolen, 0) != 0) ++failures;
+  EXPECT(tri_score(&sh, dummy, nullptr, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, (float *)dummy, nullptr, 1 << 20, nullptr), KV_EWORKSPACE);
+  EXPECT(tri_score(&sh, dummy, nullptr, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, (float *)dummy, (void *)0x7000004, 1 << 20, nullptr), KV_EWORKSPACE);
+  EXPECT(tri_score(&sh, dummy, nullptr, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, (float *)dummy, wsp, KV_WORKSPACE_HEADER - 1, nullptr), KV_EWORKSPACE);
+  {
+    int32_t *k = reinterpret_cast<int32_t *>(0x3000), *n = reinterpret_cast<int32_t *>(0x4000);
+    EXPECT(kv_select_topk(&sh, &pol, (const float *)dummy, k, 1024, n, wsp, need_sel - 1, nullptr), KV_EWORKSPACE);
+    EXPECT(kv_select_random(&sh, &pol, nullptr, 1, 0, k, 1024, n, nullptr, need_sel, nullptr), KV_EWORKSPACE);
+    EXPECT(kv_select_random_shared(&sh, &pol, nullptr, 1, 0, k, 1024, n, (void *)0x7000004, need_sel, nullptr), KV_EWORKSPACE);
+  }
+
   // selectors: b_cap below the budget, t_cap past every selector (2^26) or past the union's
   // limit (2^18), budget < 1, union without head scores
   int32_t *kept = reinterpret_cast<int32_t *>(0x3000), *nk = reinterpret_cast<int32_t *>(0x4000);
-  EXPECT(kv_select_topk(&sh, &pol, (const float *)dummy, kept, 1000, nk, nullptr), KV_ESHAPE);
+  EXPECT(kv_select_topk(&sh, &pol, (const float *)dummy, kept, 1000, nk, wsp, 1 << 20, nullptr), KV_ESHAPE);
   kv_shape big = sh;
   big.t_cap = (1 << 26) + 1;
-  EXPECT(kv_select_topk(&big, &pol, (const float *)dummy, kept, 1024, nk, nullptr), KV_ESHAPE);
-  EXPECT(kv_select_random(&big, &pol, nullptr, 1, 0, kept, 1024, nk, nullptr), KV_ESHAPE);
-  EXPECT(kv_select_random_shared(&big, &pol, nullptr, 1, 0, kept, 1024, nk, nullptr), KV_ESHAPE);
+  EXPECT(kv_select_topk(&big, &pol, (const float *)dummy, kept, 1024, nk, wsp, 1 << 20, nullptr), KV_ESHAPE);
+  EXPECT(kv_select_random(&big, &pol, nullptr, 1, 0, kept, 1024, nk, wsp, 1 << 20, nullptr), KV_ESHAPE);
+  EXPECT(kv_select_random_shared(&big, &pol, nullptr, 1, 0, kept, 1024, nk, wsp, 1 << 20, nullptr), KV_ESHAPE);
   big.t_cap = (1 << 18) + 1;
   EXPECT(kv_select_union(&big, &pol, 4, 0, (const float *)dummy, (const float *)dummy, kept, 1024, nk, nullptr), KV_ESHAPE);
   kv_policy zero = pol;

@@ -9,6 +9,8 @@ import re
 
 import pytest
 
+WS = ctypes.c_void_p(0x7000000)   # a workspace pointer: never dereferenced, validation fails first
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvevict.h")
 
@@ -30,8 +32,9 @@ def lib():
 
 def test_header_declares_the_four_calls():
     names = _declared_functions()
-    for n in ("tri_score", "tri_score_rotated", "tri_score_gqa", "kv_score_gqa_workspace_bytes", "kv_select_topk", "kv_select_random", "kv_compact", "kv_version",
-              "kv_status_string"):
+    for n in ("tri_score", "kv_score_workspace_bytes", "tri_score_rotated", "tri_score_gqa",
+              "kv_score_gqa_workspace_bytes", "kv_select_topk", "kv_select_workspace_bytes", "kv_select_random",
+              "kv_compact", "kv_version", "kv_status_string", "kv_device_checks"):
         assert n in names, names
 
 
@@ -41,7 +44,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kv_version() >> 16 == 1
+    assert lib.kv_version() >> 16 == 2
+    assert lib.kv_device_checks() == 0
     assert lib.kv_status_string(0).decode() == "ok"
     assert "invalid" in lib.kv_status_string(-1).decode()
     assert lib.kv_status_string(12345).decode() == "unknown status"
@@ -53,18 +57,17 @@ def test_host_validation_rejects_bad_arguments(lib):
     seq = ctypes.c_void_p(0x2000)
     arr = (ctypes.c_int32 * 1)(1)
     # null shape
-    assert lib.tri_score(None, dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, None) == L.KV_EINVAL
+    assert lib.tri_score(None, dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, WS, 1 << 20, None) == L.KV_EINVAL
     # odd head_dim / bad dtype / misaligned K
     sh = L.KvShape(1, 1, 1, 7, 16, L.KV_F32, seq)
-    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, None) == L.KV_ESHAPE
+    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, WS, 1 << 20, None) == L.KV_ESHAPE
     sh = L.KvShape(1, 1, 1, 8, 16, 9, seq)
-    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, None) == L.KV_EDTYPE
+    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, WS, 1 << 20, None) == L.KV_EDTYPE
     sh = L.KvShape(1, 1, 1, 8, 16, L.KV_BF16, seq)
-    assert lib.tri_score(ctypes.byref(sh), ctypes.c_void_p(0x1008), None, dummy, None, dummy, 1e4, arr, 1, dummy,
-                         None) == L.KV_EINVAL
+    assert lib.tri_score(ctypes.byref(sh), ctypes.c_void_p(0x1008), None, dummy, None, dummy, 1e4, arr, 1, dummy, WS, 1 << 20, None) == L.KV_EINVAL
     # no offsets, non-positive theta
-    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, 1e4, arr, 0, dummy, None) == L.KV_EINVAL
-    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, -1.0, arr, 1, dummy, None) == L.KV_EINVAL
+    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, 1e4, arr, 0, dummy, WS, 1 << 20, None) == L.KV_EINVAL
+    assert lib.tri_score(ctypes.byref(sh), dummy, None, dummy, None, dummy, -1.0, arr, 1, dummy, WS, 1 << 20, None) == L.KV_EINVAL
     # rotated keys: unknown style, half-split rows that do not split into whole lanes, bad paging
     assert lib.tri_score_rotated(ctypes.byref(sh), dummy, None, 7, dummy, None, dummy, 1e4, arr, 1, dummy,
                                  None) == L.KV_EINVAL
@@ -82,15 +85,16 @@ def test_host_validation_rejects_bad_arguments(lib):
                                  dummy, None) == L.KV_ESHAPE
     # one head's bf16 d = 128 rows beyond 32-bit byte offsets
     huge = L.KvShape(1, 1, 1, 128, ((1 << 31) - (64 << 9)) // 256, L.KV_BF16, seq)
-    assert lib.tri_score(ctypes.byref(huge), dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, None) == L.KV_ESHAPE
+    assert lib.tri_score(ctypes.byref(huge), dummy, None, dummy, None, dummy, 1e4, arr, 1, dummy, WS, 1 << 20, None) == L.KV_ESHAPE
     big = L.KvShape(1, 1, 1, 8, (1 << 18) + 1, L.KV_BF16, seq)   # past the union selector's LDS bits
     huge_sel = L.KvShape(1, 1, 1, 8, (1 << 26) + 1, L.KV_BF16, seq)  # past every selector
     # grouped-query scores: group outside 1..16, workspace too small, fp32 head_dim beyond 128
     shg = L.KvShape(2, 3, 4, 128, 1000, L.KV_BF16, None)
     need = lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg), 4)
-    assert need == 2 * 3 * 4 * 1 * 4 * 2 * 8       # (L*S*H) heads x 1 chunk of 1024 keys x G x (sum, sum of squares)
+    # the header, then (L*S*H) heads x 1 chunk of 1024 keys x G x (sum, sum of squares) in fp64
+    assert need == L.KV_WORKSPACE_HEADER + 2 * 3 * 4 * 1 * 4 * 2 * 8
     shg2 = L.KvShape(2, 3, 4, 128, 1025, L.KV_BF16, None)
-    assert lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg2), 4) == 2 * need
+    assert lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg2), 4) == 2 * need - L.KV_WORKSPACE_HEADER
     assert lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg), 17) == 0
     assert lib.kv_score_gqa_workspace_bytes(ctypes.byref(shg), 0) == 0
     assert lib.kv_score_gqa_workspace_bytes(None, 4) == 0
@@ -100,9 +104,9 @@ def test_host_validation_rejects_bad_arguments(lib):
         assert lib.tri_score_gqa(ctypes.byref(shg), dummy, None, grp, dummy, None, dummy, 1e4, arr, 1, hs, sc, ws,
                                  1 << 20, None) == L.KV_EINVAL
     assert lib.tri_score_gqa(ctypes.byref(shg), dummy, None, 4, dummy, None, dummy, 1e4, arr, 1, hs, sc, ws,
-                             need - 8, None) == L.KV_ESHAPE
+                             need - 8, None) == L.KV_EWORKSPACE
     assert lib.tri_score_gqa(ctypes.byref(shg), dummy, None, 4, dummy, None, dummy, 1e4, arr, 1, hs, sc,
-                             ctypes.c_void_p(0x100004), need, None) == L.KV_EINVAL      # misaligned workspace
+                             ctypes.c_void_p(0x100004), need, None) == L.KV_EWORKSPACE  # misaligned workspace
     assert lib.tri_score_gqa(ctypes.byref(shg), dummy, None, 4, dummy, None, dummy, 1e4, arr, 1, hs, hs, ws,
                              need, None) == L.KV_EINVAL      # scores alias the per-query-head scores
     shbig = L.KvShape(1, 1, 1, 16, 1 << 26, L.KV_BF16, seq)  # 16 query heads x 2^26 slots overflow 2^31 bytes
@@ -118,8 +122,7 @@ def test_host_validation_rejects_bad_arguments(lib):
     pol = L.KvPolicy(8, 2, 4, seq)
     assert lib.kv_select_recent(ctypes.byref(sh), ctypes.byref(pol), dummy, 7, dummy, None) == L.KV_ESHAPE
     assert lib.kv_select_recent(ctypes.byref(sh), None, dummy, 8, dummy, None) == L.KV_EINVAL
-    assert lib.kv_select_random_shared(ctypes.byref(huge_sel), ctypes.byref(pol), None, 1, 0, dummy, 8, dummy,
-                                       None) == L.KV_ESHAPE
+    assert lib.kv_select_random_shared(ctypes.byref(huge_sel), ctypes.byref(pol), None, 1, 0, dummy, 8, dummy, WS, 1 << 20, None) == L.KV_ESHAPE
     assert lib.kv_select_union(ctypes.byref(sh), ctypes.byref(pol), 4, 0, None, dummy, dummy, 8, dummy,
                                None) == L.KV_EINVAL
     assert lib.kv_select_union(ctypes.byref(sh), ctypes.byref(pol), 0, 0, dummy, dummy, dummy, 8, dummy,
@@ -137,20 +140,68 @@ def test_host_validation_rejects_bad_arguments(lib):
                                   None) == L.KV_EINVAL       # V not 16-byte aligned
     # selector: b_cap below budget or prompt cap, t_cap above the supported maximum, budget < 1
     pol = L.KvPolicy(8, 2, 4, seq)
-    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 7, dummy, None) == L.KV_ESHAPE
+    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 7, dummy, WS, 1 << 20, None) == L.KV_ESHAPE
     pol = L.KvPolicy(8, 2, 12, seq)
-    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 8, dummy, None) == L.KV_ESHAPE
+    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 8, dummy, WS, 1 << 20, None) == L.KV_ESHAPE
     pol = L.KvPolicy(8, 2, 4, seq)
-    assert lib.kv_select_random(ctypes.byref(huge_sel), ctypes.byref(pol), None, 1, 0, dummy, 8, dummy,
-                                None) == L.KV_ESHAPE
-    assert lib.kv_select_topk(ctypes.byref(huge_sel), ctypes.byref(pol), dummy, dummy, 8, dummy, None) == L.KV_ESHAPE
+    assert lib.kv_select_random(ctypes.byref(huge_sel), ctypes.byref(pol), None, 1, 0, dummy, 8, dummy, WS, 1 << 20, None) == L.KV_ESHAPE
+    assert lib.kv_select_topk(ctypes.byref(huge_sel), ctypes.byref(pol), dummy, dummy, 8, dummy, WS, 1 << 20, None) == L.KV_ESHAPE
     assert lib.kv_select_recent(ctypes.byref(huge_sel), ctypes.byref(pol), dummy, 8, dummy, None) == L.KV_ESHAPE
     pol = L.KvPolicy(0, 2, 4, seq)
-    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 8, dummy, None) == L.KV_EINVAL
+    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 8, dummy, WS, 1 << 20, None) == L.KV_EINVAL
     # compact: aliasing in/out is rejected
     a = ctypes.c_void_p(0x100000)
     assert lib.kv_compact(ctypes.byref(sh), a, ctypes.c_void_p(0x200000), None, dummy, 8, dummy, a,
                           ctypes.c_void_p(0x300000), None, 8, None) == L.KV_EINVAL
+
+
+def test_workspace_queries_and_rejections(lib):
+    # tri_score and the top-k / random selectors take a caller workspace sized by their queries;
+    # a missing, misaligned or short one is rejected before any launch
+    from eviction_long_reasoning_amd import _lib as L
+    ok = ctypes.c_void_p(0x1000)
+    arr = (ctypes.c_int32 * 17)(*[1 << i for i in range(17)])
+    sh = L.KvShape(36, 8, 8, 128, 32768, L.KV_BF16, None)
+    need_s = lib.kv_score_workspace_bytes(ctypes.byref(sh), 17)
+    assert need_s == L.KV_WORKSPACE_HEADER                    # the score stream needs no scratch of its own
+    assert lib.kv_score_workspace_bytes(ctypes.byref(sh), 0) == 0
+    assert lib.kv_score_workspace_bytes(ctypes.byref(sh), 65) == 0
+    assert lib.kv_score_workspace_bytes(None, 17) == 0
+    bad = L.KvShape(36, 8, 8, 7, 32768, L.KV_BF16, None)
+    assert lib.kv_score_workspace_bytes(ctypes.byref(bad), 17) == 0
+    need_k = lib.kv_select_workspace_bytes(ctypes.byref(sh), 3072)
+    assert need_k >= L.KV_WORKSPACE_HEADER and need_k % 8 == 0
+    assert lib.kv_select_workspace_bytes(ctypes.byref(sh), 0) == 0
+    huge = L.KvShape(1, 1, 1, 8, (1 << 26) + 1, L.KV_BF16, None)
+    assert lib.kv_select_workspace_bytes(ctypes.byref(huge), 8) == 0
+    sh.seq_len = ok
+    for ws, nbytes in ((None, 1 << 20), (ctypes.c_void_p(0x7000004), 1 << 20), (WS, need_s - 1)):
+        assert lib.tri_score(ctypes.byref(sh), ok, None, ok, None, ok, 1e6, arr, 17, ok, ws, nbytes,
+                             None) == L.KV_EWORKSPACE
+    pol = L.KvPolicy(3072, 128, 1024, ok)
+    for ws, nbytes in ((None, 1 << 30), (ctypes.c_void_p(0x7000004), 1 << 30), (WS, need_k - 1)):
+        assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), ok, ok, 3072, ok, ws, nbytes,
+                                  None) == L.KV_EWORKSPACE
+        assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, ok, 3072, ok, ws, nbytes,
+                                    None) == L.KV_EWORKSPACE
+        assert lib.kv_select_random_shared(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, ok, 3072, ok, ws,
+                                           nbytes, None) == L.KV_EWORKSPACE
+    assert "workspace" in lib.kv_status_string(L.KV_EWORKSPACE).decode()
+
+
+def test_device_check_build_loads_and_reports_itself():
+    # the build with device-side precondition checks exports the same entry points and says so
+    from eviction_long_reasoning_amd import _lib as L
+    from eviction_long_reasoning_amd.build import DEBUG_LIB_PATH, build, build_debug, LIB_PATH
+    if not os.path.exists(LIB_PATH):
+        build()
+    if not os.path.exists(DEBUG_LIB_PATH):
+        build_debug()
+    dbg = L.open_library(DEBUG_LIB_PATH)
+    assert dbg.kv_device_checks() == 1
+    assert dbg.kv_version() >> 16 == 2
+    for name in _declared_functions():
+        assert hasattr(dbg, name), name
 
 
 def test_gqa_rotated_validation(lib):
@@ -168,7 +219,7 @@ def test_gqa_rotated_validation(lib):
     assert call(sh, group=9) == L.KV_EINVAL                     # groups of at most 8
     assert call(sh, group=0) == L.KV_EINVAL
     assert call(sh, style=5) == L.KV_EINVAL
-    assert call(sh, workspace_bytes=need - 8) == L.KV_ESHAPE
+    assert call(sh, workspace_bytes=need - 8) == L.KV_EWORKSPACE
     assert call(sh, qbar=ctypes.c_void_p(0x1002)) == L.KV_EINVAL
     sh256 = L.KvShape(1, 1, 1, 256, 4096, L.KV_BF16, ok)       # 32 pieces: more than 16 lanes per key
     assert call(sh256, workspace_bytes=1 << 20) == L.KV_ESHAPE
@@ -185,9 +236,9 @@ def test_misaligned_word_arrays_are_rejected(lib):
     arr = (ctypes.c_int32 * 1)(1)
     sh = L.KvShape(1, 1, 1, 128, 4096, L.KV_BF16, ok)
     sh_odd = L.KvShape(1, 1, 1, 128, 4096, L.KV_BF16, odd)
-    assert lib.tri_score(ctypes.byref(sh), ok, None, ok, None, ok, 1e4, arr, 1, odd, None) == L.KV_EINVAL
-    assert lib.tri_score(ctypes.byref(sh_odd), ok, None, ok, None, ok, 1e4, arr, 1, ok, None) == L.KV_EINVAL
-    assert lib.tri_score(ctypes.byref(sh), ok, odd, ok, None, ok, 1e4, arr, 1, ok, None) == L.KV_EINVAL
+    assert lib.tri_score(ctypes.byref(sh), ok, None, ok, None, ok, 1e4, arr, 1, odd, WS, 1 << 20, None) == L.KV_EINVAL
+    assert lib.tri_score(ctypes.byref(sh_odd), ok, None, ok, None, ok, 1e4, arr, 1, ok, WS, 1 << 20, None) == L.KV_EINVAL
+    assert lib.tri_score(ctypes.byref(sh), ok, odd, ok, None, ok, 1e4, arr, 1, ok, WS, 1 << 20, None) == L.KV_EINVAL
     assert lib.tri_score_rotated(ctypes.byref(sh), ok, None, 0, ok, None, odd, 1e4, arr, 1, ok, None) == L.KV_EINVAL
     ws = ctypes.c_void_p(0x100000)
     need = lib.kv_score_gqa_workspace_bytes(ctypes.byref(sh), 4)
@@ -195,12 +246,11 @@ def test_misaligned_word_arrays_are_rejected(lib):
                              ctypes.c_void_p(0x300000), ws, need, None) == L.KV_EINVAL
     pol = L.KvPolicy(1024, 64, 128, ok)
     pol_odd = L.KvPolicy(1024, 64, 128, odd)
-    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), odd, ok, 1024, ok, None) == L.KV_EINVAL
-    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol_odd), ok, ok, 1024, ok, None) == L.KV_EINVAL
-    assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, odd, 1024, ok, None) == L.KV_EINVAL
-    assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), odd, 1, 0, ok, 1024, ok, None) == L.KV_EINVAL
-    assert lib.kv_select_random_shared(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, ok, 1024, odd,
-                                       None) == L.KV_EINVAL
+    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), odd, ok, 1024, ok, WS, 1 << 20, None) == L.KV_EINVAL
+    assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol_odd), ok, ok, 1024, ok, WS, 1 << 20, None) == L.KV_EINVAL
+    assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, odd, 1024, ok, WS, 1 << 20, None) == L.KV_EINVAL
+    assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), odd, 1, 0, ok, 1024, ok, WS, 1 << 20, None) == L.KV_EINVAL
+    assert lib.kv_select_random_shared(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, ok, 1024, odd, WS, 1 << 20, None) == L.KV_EINVAL
     assert lib.kv_select_union(ctypes.byref(sh), ctypes.byref(pol), 2, 0, odd, ok, ok, 1024, ok, None) == L.KV_EINVAL
     assert lib.kv_select_recent(ctypes.byref(sh_odd), ctypes.byref(pol), ok, 1024, ok, None) == L.KV_EINVAL
     assert lib.kv_audit_kept(ctypes.byref(sh), ctypes.byref(pol), ok, 1024, ok, odd, None) == L.KV_EINVAL
