@@ -8,6 +8,7 @@ package is a thin torch-tensor binding over it.
   tri_score_rotated the same for keys stored after RoPE, dense or paged
   tri_score_gqa     per-query-head scores of a GQA group, z-normalised, max over the group
   tri_score_gqa_rotated  the same for keys stored after RoPE, dense or paged
+  tri_score_gqa_noalloc  tri_score_gqa with the library's own scratch array (allocates nothing)
   kv_select_topk    keep prompt + recent window + top-scoring keys per head
   kv_select_random  keep prompt + recent window + per-head uniform random keys
   kv_compact        gather kept K/V rows and positions contiguously
@@ -27,9 +28,10 @@ from ._lib import KvError, library_path, load as load_library
 from .binding import (gqa_workspace_bytes, kv_audit_kept, kv_compact, kv_compact_inplace, kv_select_random,
                       kv_select_random_shared, kv_select_recent, kv_select_union, kv_select_topk,
                       score_workspace_bytes, select_workspace_bytes, tri_score, tri_score_gqa,
-                      tri_score_gqa_rotated, tri_score_rotated)
+                      tri_score_gqa_noalloc, tri_score_gqa_rotated, tri_score_rotated)
 
-__all__ = ["tri_score", "tri_score_rotated", "tri_score_gqa", "tri_score_gqa_rotated", "gqa_workspace_bytes",
+__all__ = ["tri_score", "tri_score_rotated", "tri_score_gqa", "tri_score_gqa_rotated", "tri_score_gqa_noalloc",
+           "gqa_workspace_bytes",
            "score_workspace_bytes", "select_workspace_bytes", "kv_select_topk", "kv_select_random", "kv_compact",
            "kv_select_union", "kv_select_random_shared", "kv_select_recent", "kv_compact_inplace", "kv_audit_kept",
            "KvError", "library_path", "load_library"]

@@ -64,6 +64,9 @@ _SIGNATURES = {
     "tri_score_gqa": (_I32, [ctypes.POINTER(KvShape), _P, _P, _I32, _P, _P, _P, ctypes.c_double,
                              ctypes.POINTER(_I32), _I32, _P, _P, _P, ctypes.c_size_t, _P]),
     "kv_score_gqa_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(KvShape), _I32]),
+    "tri_score_gqa_noalloc": (_I32, [ctypes.POINTER(KvShape), _P, _P, _I32, _P, _P, _P, ctypes.c_double,
+                                     ctypes.POINTER(_I32), _I32, _P, _P, _P]),
+    "kv_score_gqa_noalloc_max_bytes": (ctypes.c_size_t, []),
     "tri_score_gqa_rotated": (_I32, [ctypes.POINTER(KvShape), _P, ctypes.POINTER(KvPaged), _I32, _I32, _P, _P, _P,
                                      ctypes.c_double, ctypes.POINTER(_I32), _I32, _P, _P, _P, ctypes.c_size_t, _P]),
     "kv_select_topk": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, _P, _I32, _P, _P,

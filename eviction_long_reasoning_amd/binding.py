@@ -191,6 +191,32 @@ def tri_score_gqa(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_
     return out, head_out
 
 
+def tri_score_gqa_noalloc(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len: torch.Tensor,
+                          rope_theta: float, deltas: Sequence[int], out: torch.Tensor, head_out: torch.Tensor,
+                          pos: Optional[torch.Tensor] = None, qabs: Optional[torch.Tensor] = None) -> None:
+    """``tri_score_gqa`` without a workspace: the library's own device array holds the partial sums
+    and nothing is allocated (``out`` and ``head_out`` are required). Calls on one device must not
+    overlap in time."""
+    if K.dim() != 5 or K.dtype not in _DT or qbar.dim() != 4:
+        raise ValueError("K must be [L,S,H,t_cap,d] float32/bfloat16 and qbar [L,H,G,d]")
+    L, S, H, t_cap, d = K.shape
+    G = qbar.shape[2]
+    dev = K.device
+    kp = _dev_ptr(K, "K")
+    qp = _dev_ptr(qbar, "qbar", torch.float32, (L, H, G, d), dev)
+    tp = _dev_ptr(t_cur, "t_cur", torch.int32, (S,), dev)
+    sp = _dev_ptr(seq_len, "seq_len", torch.int32, (S,), dev)
+    pp = _dev_ptr(pos, "pos", torch.int32, (L, S, H, t_cap), dev)
+    ap = _dev_ptr(qabs, "qabs", torch.float32, (L, H, G, d // 2), dev)
+    op = _dev_ptr(out, "out", torch.float32, (L, S, H, t_cap), dev)
+    hp = _dev_ptr(head_out, "head_out", torch.float32, (L, S, H, G, t_cap), dev)
+    shape = _shape(L, S, H, d, t_cap, _DT[K.dtype], sp)
+    dl = [int(x) for x in deltas]
+    arr = (ctypes.c_int32 * max(1, len(dl)))(*dl)
+    _invoke("tri_score_gqa_noalloc", dev, ctypes.byref(shape), kp, pp, int(G), qp, ap, tp, float(rope_theta), arr,
+            len(dl), hp, op)
+
+
 def tri_score_gqa_rotated(K: torch.Tensor, qbar: torch.Tensor, t_cur: torch.Tensor, seq_len: torch.Tensor,
                           rope_theta: float, deltas: Sequence[int], rope_style: str = "interleaved",
                           block_table: Optional[torch.Tensor] = None, head_major: bool = False,

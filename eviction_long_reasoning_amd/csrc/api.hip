@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
+#include <mutex>
 
 #include "kvevict.h"
 #include "kv_internal.hpp"
@@ -299,6 +300,50 @@ KV_EXPORT kv_status tri_score_gqa(const kv_shape *shape, const void *K, const in
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   if ((st = device_checks(shape, nullptr, pos, workspace, hs)) != KV_OK) return st;
   return hip_status(launch_score_gqa(p, shape->dtype == KV_BF16, ppq, hs));
+}
+
+// ---- tri_score_gqa without a caller workspace (for callers that cannot allocate) ----
+//
+// The partial sums live in a file-scope device array instead. In host code `gqa_scratch` names a
+// host-side stand-in, not device memory: its device address is taken once per device with
+// hipGetSymbolAddress (with that device current) and only that address reaches the kernels.
+namespace kvevict {
+namespace {
+constexpr size_t kStaticScratchBytes = size_t{8} << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char gqa_scratch[kStaticScratchBytes];
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];   // device address of gqa_scratch on each device, once taken
+
+// The current device's copy of gqa_scratch, or nullptr when its address cannot be taken.
+void *device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(gqa_scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+}  // namespace kvevict
+
+KV_EXPORT size_t kv_score_gqa_noalloc_max_bytes(void) { return kStaticScratchBytes; }
+
+KV_EXPORT kv_status tri_score_gqa_noalloc(const kv_shape *shape, const void *K, const int32_t *pos, int32_t group,
+                                          const float *qbar, const float *qabs, const int32_t *t_cur,
+                                          double rope_theta, const int32_t *deltas, int32_t n_delta,
+                                          float *head_scores, float *scores, void *stream) {
+  kv_status st = check_shape(shape, true);
+  if (st != KV_OK) return st;
+  if (group < 1 || group > kGqaMaxGroup) return KV_EINVAL;
+  if (gqa_workspace(shape, group) > kStaticScratchBytes) return KV_EWORKSPACE;   // beyond the static array
+  void *ws = device_scratch();
+  if (!ws) return KV_EHIP;
+  return tri_score_gqa(shape, K, pos, group, qbar, qabs, t_cur, rope_theta, deltas, n_delta, head_scores, scores, ws,
+                       kStaticScratchBytes, stream);
 }
 
 // max_slots: the largest t_cap the selector kernel behind the entry point takes.

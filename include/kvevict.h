@@ -274,6 +274,26 @@ kv_status tri_score_gqa(const kv_shape *shape, const void *K, const int32_t *pos
 size_t kv_score_gqa_workspace_bytes(const kv_shape *shape, int32_t group);
 
 /*
+ * tri_score_gqa_noalloc -- tri_score_gqa for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no workspace
+ * argument. Its partial sums live in a device array of kv_score_gqa_noalloc_max_bytes() bytes
+ * (8 MiB, the header included) that the library keeps on every device it runs on until the
+ * process ends; the first call on a device takes that array's address (hipGetSymbolAddress) and
+ * no call allocates. A shape and group whose kv_score_gqa_workspace_bytes exceeds the array are
+ * rejected with KV_EWORKSPACE (KV_EHIP if the address cannot be taken). Every call on one device
+ * shares that device's array: calls that overlap in time on one device race and give unspecified
+ * scores -- serialise them (one stream, or events). The array keeps the last call's partial sums;
+ * nothing in it needs clearing. Other arguments and the results as for tri_score_gqa.
+ */
+kv_status tri_score_gqa_noalloc(const kv_shape *shape, const void *K, const int32_t *pos, int32_t group,
+                                const float *qbar, const float *qabs, const int32_t *t_cur,
+                                double rope_theta, const int32_t *deltas, int32_t n_delta,
+                                float *head_scores, float *scores, void *stream);
+
+/* Bytes of the device array behind tri_score_gqa_noalloc (the largest workspace it can stand in for). */
+size_t kv_score_gqa_noalloc_max_bytes(void);
+
+/*
  * tri_score_gqa_rotated -- the grouped-query rule (as tri_score_gqa) for keys
  * stored after RoPE, dense or through a paged block table, as a serving
  * engine keeps them ([TA-blog] implementation excerpt: the scorer works on

@@ -65,6 +65,14 @@ int main() {
   EXPECT(tri_score_gqa(&sh, dummy, nullptr, 4, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, sc, ws, need - 8, nullptr), KV_EWORKSPACE);
   EXPECT(tri_score_gqa(&sh, dummy, nullptr, 4, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, hs, ws, need, nullptr), KV_EINVAL);
 
+  // the allocation-free grouped-query form: a shape whose partial sums exceed its array, a bad group
+  if (kv_score_gqa_noalloc_max_bytes() < (size_t{1} << 20)) ++failures;
+  {
+    kv_shape big{36, 8, 8, 128, 32768, KV_BF16, seq};
+    EXPECT(tri_score_gqa_noalloc(&big, dummy, nullptr, 16, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, sc, nullptr), KV_EWORKSPACE);
+    EXPECT(tri_score_gqa_noalloc(&sh, dummy, nullptr, 17, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, sc, nullptr), KV_EINVAL);
+  }
+
   // grouped-query scores of rotated keys: group beyond 8, head_dim beyond one piece per lane,
   // half-split rows that do not fill whole lanes, unknown pool layout
   EXPECT(tri_score_gqa_rotated(&sh, dummy, nullptr, 0, 9, (const float *)dummy, nullptr, seq, 1e4, deltas, 3, hs, sc, ws, need, nullptr), KV_EINVAL);
