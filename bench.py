@@ -12,7 +12,8 @@ scored+selected+compacted per second. The roofline block is for the
 dominant kernel (tri_score): algorithmic bytes per launch (each key row read
 once + one fp32 score written per entry) over its mean launch time measured
 with HIP events on the launch stream. `cpu_baseline` times the fp64 NumPy
-oracle on a bounded sample of the same workload on the host.
+oracle on the same pass on the host, one worker process per available CPU;
+`cpu_protocol` times it on every workload.
 """
 from __future__ import annotations
 
@@ -36,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=36, help="layers of the full-pass workload (36 = full size)")
-    ap.add_argument("--cpu-heads", type=int, default=256, help="heads in the oracle's CPU sample (0 = skip)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-random", action="store_true", help="skip the random-eviction pass")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the 512-slot, one-layer and ragged-batch workloads")
@@ -272,46 +273,379 @@ def other_workloads(args, dev):
     return res
 
 
-def cpu_baseline(w, K, qb, n_heads: int, folded: bool = False):
-    """The oracle (score -> select -> compact, fp64 NumPy, one thread) on a bounded sample; the
-    score is the literal RoPE dot product, or with folded=True the oracle's folded statement."""
+# ------------------------------------------------------------------------------------------------
+# The CPU oracle, timed on the host's cores: one worker process per available CPU, each working
+# through (layer, seq, KV head) units -- score (the literal RoPE dot product or the folded form),
+# lexsort top-n select, gather of the kept K/V rows -- on the same bf16 bits the GPU reads, handed
+# over through shared memory. The pool is started before the GPU is touched.
+# ------------------------------------------------------------------------------------------------
+def _oracle_unit(task):
+    """One (layer, seq, KV head) unit of the oracle (runs in a worker process); returns T."""
     import numpy as np
+    from multiprocessing import shared_memory
     from threadpoolctl import threadpool_limits
 
     import oracle
     from workloads import bf16_to_f32
 
-    units = []
-    H = w.n_kv_heads
-    for idx in range(n_heads):
-        l, h = divmod(idx, H)
-        l %= w.n_layers
-        units.append((l, 0, h))
-    T, P = int(w.seq_len[0]), int(w.prompt_len[0])
-    host = []
-    for (l, s, h) in units:
-        bits = K[l, s, h, :T].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
-        host.append(((l, s, h), bf16_to_f32(bits).astype(np.float64)))
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        for (l, s, h), kf in host:
-            score = oracle.score_folded if folded else oracle.score_literal
-            sc = score(kf, None, qb[l, h], int(w.t_cur[s]), w.theta, w.deltas)
-            kept = oracle.select_topk(sc, T, P, w.budget, w.recent)
-            oracle.compact(kf, kf, None, kept)
-        dt = time.perf_counter() - t0
-    n = len(host) * T
-    model = None
+    shm_name, kv_shape, kv_dtype, pos_off, unit, T, P, B, R, qbar, t, theta, deltas, form = task
+    shm = shared_memory.SharedMemory(name=shm_name)
+    try:
+        n_units, t_cap, d = kv_shape
+        dt = np.uint16 if kv_dtype == "bf16" else np.float32
+        KV = np.ndarray((2, n_units, t_cap, d), dtype=dt, buffer=shm.buf)
+        pos = None
+        if pos_off >= 0:
+            pos = np.ndarray((n_units, t_cap), dtype=np.int32, buffer=shm.buf, offset=pos_off)[unit, :T]
+        with threadpool_limits(1):
+            k, v = KV[0, unit, :T], KV[1, unit, :T]
+            if kv_dtype == "bf16":
+                k, v = bf16_to_f32(k), bf16_to_f32(v)
+            k = k.astype(np.float64)
+            score = oracle.score_literal if form == "literal" else oracle.score_folded
+            sc = score(k, pos, qbar, t, theta, deltas)
+            kept = oracle.select_topk(sc, T, P, B, R)
+            oracle.compact(k, v, pos, kept)
+        del KV, k, v
+    finally:
+        shm.close()
+    return int(T)
+
+
+class OracleTimer:
+    """The worker pool and the per-workload timing of the oracle."""
+
+    def __init__(self):
+        import multiprocessing as mp
+        self.cores = len(os.sched_getaffinity(0))
+        self.pool = mp.get_context("spawn").Pool(self.cores)
+        self.pool.map(int, range(self.cores))   # workers up and importing before the GPU is used
+
+    def close(self):
+        self.pool.close()
+        self.pool.join()
+
+    def run(self, K, V, pos, units, form):
+        """Time the oracle over ``units`` = [(index into K/V, T, P, B, R, qbar, t, theta, deltas)];
+        K, V are host arrays [n, t_cap, d] (bf16 bits or fp32), pos None or int32 [n, t_cap].
+        Returns (seconds, entries)."""
+        import numpy as np
+        from multiprocessing import shared_memory
+        n, t_cap, d = K.shape
+        kv_bytes = 2 * K.nbytes
+        size = kv_bytes + (n * t_cap * 4 if pos is not None else 0)
+        shm = shared_memory.SharedMemory(create=True, size=size)
+        try:
+            buf = np.ndarray((2, n, t_cap, d), dtype=K.dtype, buffer=shm.buf)
+            buf[0], buf[1] = K, V
+            pos_off = -1
+            if pos is not None:
+                pos_off = kv_bytes
+                np.ndarray((n, t_cap), dtype=np.int32, buffer=shm.buf, offset=pos_off)[...] = pos
+            kd = "bf16" if K.dtype == np.uint16 else "f32"
+            tasks = [(shm.name, (n, t_cap, d), kd, pos_off, u[0], *u[1:], form) for u in units]
+            del buf
+            t0 = time.perf_counter()
+            done = self.pool.map(_oracle_unit, tasks, chunksize=1)
+            dt = time.perf_counter() - t0
+        finally:
+            shm.close()
+            shm.unlink()
+        return dt, int(sum(done))
+
+
+def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
     except OSError:
-        pass
-    return {"value": n / dt, "unit": "KV entries/s", "cores": 1, "kind": "oracle",
-            "host_cpu": model, "host_cpus_available": len(os.sched_getaffinity(0)),
-            "sample": f"{len(host)} heads (layers 0..{(len(host) - 1) // H}, seq 0, all KV heads) x {T} slots "
-                      f"= {n} entries; {'folded' if folded else 'literal'} fp64 score + lexsort select + gather, "
-                      f"{dt:.1f} s"}
+        return None
+
+
+def host_bits(t):
+    """A device tensor's bytes on the host as uint16 (bf16) or fp32 NumPy."""
+    import numpy as np
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def oracle_protocol(timer, dev, args, w3, K3, V3, qb3):
+    """The oracle on every workload: literal score on workloads 1, 2 and 5 and on one layer of
+    workload 3 (extrapolated to its 36 layers); folded score on all five -- workload 3 whole (a
+    layer at a time), workload 4 on one steady-state event (extrapolated to its 256 events)."""
+    import numpy as np
+    import torch
+
+    from workloads import centres, kv_numpy, kv_torch, workload
+    res = {}
+
+    def units_of(w, qb, layers, t=None):
+        out = []
+        for li, l in enumerate(layers):
+            for s in range(w.n_seq):
+                for h in range(w.n_kv_heads):
+                    tt = int(w.t_cur[s]) if t is None else int(t[s])
+                    out.append(((li * w.n_seq + s) * w.n_kv_heads + h, int(w.seq_len[s]), int(w.prompt_len[s]),
+                                w.budget, w.recent, qb[l, h].astype(np.float64), tt, w.theta, w.deltas))
+        return out
+
+    def record(name, w, forms, run_one, scale=1.0, note=""):
+        entry = {"workload": w.name}
+        for form in forms:
+            sec, n = run_one(form)
+            entry[form] = {"seconds": sec * scale, "entries": int(n * scale), "entries_per_s": n / sec,
+                           "measured_seconds": sec, "measured_entries": n}
+        if note:
+            entry["note"] = note
+        res[name] = entry
+        print(f"[bench] oracle {name}: " + ", ".join(f"{f} {entry[f]['entries_per_s']:.3g} entries/s"
+                                                     for f in forms), file=sys.stderr, flush=True)
+
+    # workload 1: the whole head from NumPy
+    w1 = workload(1)
+    K1, V1, _, qb1 = kv_numpy(w1)
+    record("tiny_fp32_512", w1, ("literal", "folded"),
+           lambda f: timer.run(K1.reshape(-1, w1.t_cap, w1.head_dim), V1.reshape(-1, w1.t_cap, w1.head_dim), None,
+                               units_of(w1, qb1, [0]), f))
+    # workload 2: one 8-head layer drawn on the device
+    w2 = workload(2)
+    mu2, qb2, _ = centres(w2)
+    K2, V2 = kv_torch(w2, dev, mu2)
+    k2, v2 = host_bits(K2).reshape(-1, w2.t_cap, w2.head_dim), host_bits(V2).reshape(-1, w2.t_cap, w2.head_dim)
+    del K2, V2
+    record("one_layer_32k", w2, ("literal", "folded"), lambda f: timer.run(k2, v2, None, units_of(w2, qb2, [0]), f))
+    del k2, v2
+    # workload 5: 128 ragged sequences
+    w5 = workload(5)
+    mu5, qb5, _ = centres(w5)
+    K5, V5 = kv_torch(w5, dev, mu5)
+    k5, v5 = host_bits(K5).reshape(-1, w5.t_cap, w5.head_dim), host_bits(V5).reshape(-1, w5.t_cap, w5.head_dim)
+    del K5, V5
+    torch.cuda.empty_cache()
+    record("ragged_128_seqs", w5, ("literal", "folded"), lambda f: timer.run(k5, v5, None, units_of(w5, qb5, [0]), f))
+    del k5, v5
+    # workload 3: folded over all layers, streamed a layer at a time; literal on layer 0 (x36)
+    L3 = K3.shape[0]
+
+    def w3_folded(form):
+        sec = n = 0
+        for l in range(L3):
+            k, v = host_bits(K3[l]).reshape(-1, w3.t_cap, w3.head_dim), host_bits(V3[l]).reshape(-1, w3.t_cap,
+                                                                                                 w3.head_dim)
+            dt, dn = timer.run(k, v, None, units_of(w3, qb3, [l]), form)
+            sec, n = sec + dt, n + dn
+        return sec, n
+    record("full_pass_32k", w3, ("folded",), w3_folded)
+    k, v = host_bits(K3[0]).reshape(-1, w3.t_cap, w3.head_dim), host_bits(V3[0]).reshape(-1, w3.t_cap, w3.head_dim)
+    record("full_pass_32k_literal_layer0", w3, ("literal",), lambda f: timer.run(k, v, None, units_of(w3, qb3, [0]), f),
+           scale=L3, note=f"layer 0 measured, seconds and entries scaled x{L3} to the whole pass")
+    del k, v
+    # workload 4: one steady-state event (every head at B + 128 entries, gappy positions)
+    w4 = workload(4)
+    w4f = workload(4, seq_len=np.full(w4.n_seq, w4.t_cap, np.int32))
+    mu4, qb4, _ = centres(w4f)
+    K4, V4 = kv_torch(w4f, dev, mu4)
+    k4, v4 = host_bits(K4).reshape(-1, w4f.t_cap, w4f.head_dim), host_bits(V4).reshape(-1, w4f.t_cap, w4f.head_dim)
+    del K4, V4
+    torch.cuda.empty_cache()
+    gap = np.random.default_rng(4).integers(1, 3, (k4.shape[0], w4f.t_cap)).astype(np.int64)
+    pos4 = np.cumsum(gap, axis=1).astype(np.int32)          # ascending, gappy (events evict slots)
+    t4 = np.full(w4f.n_seq, int(pos4.max()) + 1)
+    record("periodic_event", w4f, ("folded",),
+           lambda f: timer.run(k4, v4, pos4, units_of(w4f, qb4, range(w4f.n_layers), t4), f), scale=w4.n_events,
+           note=f"one steady-state event measured (every head at {w4f.t_cap} entries, gappy positions); seconds and "
+                f"entries scaled x{w4.n_events} to the simulated generation's events")
+    del k4, v4
+    return res
+
+
+def periodic_workload(args, dev, time_launches, mu4, qb4):
+    """The gpt-oss-20b-shaped periodic eviction: one steady-state event (every head at B + 128 = 2176
+    entries) kernel by kernel and as whole passes -- scored (tri_score with positions, top-B) or
+    random, each with the gather into a second buffer or in-place hole filling -- then a whole
+    simulated 32768-token generation: 256 events, 128 tokens appended to every sequence between
+    them (untimed), each event's pass timed alone on the device."""
+    import numpy as np
+    import torch
+
+    import eviction_long_reasoning_amd as kv
+    from workloads import centres, kv_torch, periodic_prompt_torch, periodic_tokens_torch, workload
+    i32 = lambda a: torch.as_tensor(np.asarray(a, np.int32), device=dev)
+    w4 = workload(4)
+    w4f = workload(4, seq_len=np.full(w4.n_seq, w4.t_cap, np.int32))
+    L, S, H, Tc, d = w4f.n_layers, w4f.n_seq, w4f.n_kv_heads, w4f.t_cap, w4f.head_dim
+    K4, V4 = kv_torch(w4f, dev, mu4)
+    pos4 = torch.arange(Tc, dtype=torch.int32, device=dev).expand(L, S, H, Tc).contiguous()
+    e = K4.element_size()
+    row = d * e
+    seq4, plen4 = i32(w4f.seq_len), i32(w4f.prompt_len)
+    qb4d, tcur4 = torch.from_numpy(qb4).to(dev), i32(np.full(S, Tc))   # the next position
+    b_cap, out4 = w4f.b_cap(), w4f.budget
+    heads = L * S * H
+    sc4 = torch.empty((L, S, H, Tc), dtype=torch.float32, device=dev)
+    kept4 = torch.empty((L, S, H, b_cap), dtype=torch.int32, device=dev)
+    nk4 = torch.empty((S,), dtype=torch.int32, device=dev)
+    ws_s = torch.empty((kv.score_workspace_bytes(L, S, H, Tc, d, K4.dtype, len(w4f.deltas)),), dtype=torch.uint8,
+                       device=dev)
+    ws_k = torch.empty((kv.select_workspace_bytes(L, S, H, Tc, b_cap),), dtype=torch.uint8, device=dev)
+    Ko4 = torch.empty((L, S, H, out4, d), dtype=K4.dtype, device=dev)
+    Vo4 = torch.empty_like(Ko4)
+    Po4 = torch.empty((L, S, H, out4), dtype=torch.int32, device=dev)
+
+    def score(K, pos, seq, tcur, out, ws):
+        kv.tri_score(K, qb4d, tcur, seq, w4f.theta, w4f.deltas, pos=pos, out=out, workspace=ws)
+
+    def draw(seq, plen, pos, ev, kept, nk, ws):
+        kv.kv_select_random(tuple(pos.shape), seq, plen, w4f.budget, w4f.recent, w4f.prompt_cap(), w4f.seed_random,
+                            ev, pos=pos, b_cap=b_cap, kept=kept, n_kept=nk, workspace=ws)
+
+    # kernel by kernel
+    score4_ms = time_launches(lambda: score(K4, pos4, seq4, tcur4, sc4, ws_s))
+    topk4_ms = time_launches(lambda: kv.kv_select_topk(sc4, seq4, plen4, w4f.budget, w4f.recent, w4f.prompt_cap(),
+                                                       b_cap=b_cap, kept=kept4, n_kept=nk4, workspace=ws_k))
+    sel4_ms = time_launches(lambda: draw(seq4, plen4, pos4, 1, kept4, nk4, ws_k))
+    gather_ms = time_launches(lambda: kv.kv_compact(K4, V4, kept4, nk4, seq4, out4, pos=pos4, K_out=Ko4, V_out=Vo4,
+                                                    pos_out=Po4))
+    n = w4f.entries
+    n_kept = int(nk4.sum()) * L * H
+    nkh = nk4.to(torch.int64)[None, :, None, None]
+    movers = int(((kept4.to(torch.int64) >= nkh) & (torch.arange(b_cap, device=dev) < nkh)).sum())
+    bytes_score = n * (row + 4 + 4)                       # key row and position read, score written
+    bytes_topk = n * 4 + heads * b_cap * 4                 # scores read, kept list written
+    bytes_draw = n * 4 + heads * b_cap * 4                 # positions read, kept list written
+    bytes_gather = n_kept * (4 * row + 4 + 4 + 4)          # K, V rows read and written; index, position
+    bytes_inplace = movers * (4 * row + 4 + 4)             # moved rows only
+
+    # whole passes over the steady-state event; the in-place passes start each rep from a copy of
+    # the event's cache (the copy is outside the timed region)
+    Ks, Vs, Ps = K4.clone(), V4.clone(), pos4.clone()
+
+    def restore():
+        K4.copy_(Ks)
+        V4.copy_(Vs)
+        pos4.copy_(Ps)
+
+    def scored(inplace):
+        score(K4, pos4, seq4, tcur4, sc4, ws_s)
+        kv.kv_select_topk(sc4, seq4, plen4, w4f.budget, w4f.recent, w4f.prompt_cap(), b_cap=b_cap, kept=kept4,
+                          n_kept=nk4, workspace=ws_k)
+        compact(inplace)
+
+    def rnd(inplace):
+        draw(seq4, plen4, pos4, 1, kept4, nk4, ws_k)
+        compact(inplace)
+
+    def compact(inplace):
+        if inplace:
+            kv.kv_compact_inplace(K4, V4, kept4, nk4, seq4, pos=pos4)
+        else:
+            kv.kv_compact(K4, V4, kept4, nk4, seq4, out4, pos=pos4, K_out=Ko4, V_out=Vo4, pos_out=Po4)
+
+    def pass_ms(fn):
+        for _ in range(args.warmup):
+            restore()
+            fn()
+        ms = []
+        for _ in range(max(10, args.steps)):
+            restore()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize(dev)
+            ms.append(ev[0].elapsed_time(ev[1]))
+        return percentiles(ms)
+
+    passes = {}
+    for name, fn, byts in (("scored_gather", lambda: scored(False), bytes_score + bytes_topk + bytes_gather),
+                           ("scored_in_place", lambda: scored(True), bytes_score + bytes_topk + bytes_inplace),
+                           ("random_gather", lambda: rnd(False), bytes_draw + bytes_gather),
+                           ("random_in_place", lambda: rnd(True), bytes_draw + bytes_inplace)):
+        st = pass_ms(fn)
+        passes[name] = {"ms": st, "algorithmic_bytes": byts, "gbs": byts / (st["median_ms"] * 1e-3) / 1e9,
+                        "entries_per_s": n / (st["median_ms"] * 1e-3)}
+    restore()
+    del Ks, Vs, Ps, K4, V4, pos4, sc4, Ko4, Vo4, Po4
+    torch.cuda.empty_cache()
+    print(f"[bench] periodic event, kernels: score (positions) {score4_ms:.3f} ms, top-k {topk4_ms:.3f} ms, random "
+          f"select {sel4_ms:.3f} ms, gather {gather_ms:.3f} ms; whole passes (median ms): "
+          + ", ".join(f"{k} {v['ms']['median_ms']:.3f}" for k, v in passes.items()), file=sys.stderr, flush=True)
+
+    # the simulated generation: every sequence starts at its prompt; events fire every 128 generated
+    # tokens; a sequence whose cache exceeds B is evicted back to B (its other slots copied as they are)
+    P = w4.prompt_len.astype(np.int64)
+    mu0, _, dr = centres(w4)
+    K0, V0 = periodic_prompt_torch(w4, mu0, dr, dev)
+    sc_g = torch.empty((L, S, H, Tc), dtype=torch.float32, device=dev)
+    gen = {}
+    for mode in ("scored", "random"):
+        for inplace in (False, True):
+            bufs = [(K0.clone(), V0.clone(), torch.arange(Tc, dtype=torch.int32, device=dev).expand(L, S, H, Tc).contiguous())]
+            if not inplace:
+                bufs.append((torch.empty_like(K0), torch.empty_like(V0), torch.empty((L, S, H, Tc), dtype=torch.int32,
+                                                                                     device=dev)))
+            cur, T = 0, P.copy()
+            marks, byts, ents = [], 0, 0
+            for ev in range(1, w4.n_events + 1):
+                Kc, Vc, Pc = bufs[cur]
+                Kn, Vn, pn = periodic_tokens_torch(w4, ev, (P + w4.new_per_event * (ev - 1)).astype(np.int32), mu0, dr,
+                                                   dev)
+                for t0 in np.unique(T):          # sequences at the same length append with one slice
+                    idx = torch.as_tensor(np.nonzero(T == t0)[0], device=dev)
+                    sl = slice(int(t0), int(t0) + w4.new_per_event)
+                    Kc[:, idx, :, sl] = Kn[:, idx]
+                    Vc[:, idx, :, sl] = Vn[:, idx]
+                    Pc[:, idx, :, sl] = pn[idx][None, :, None, :].expand(L, -1, H, -1)
+                T = T + w4.new_per_event
+                seq, tcur = i32(T), i32(P + w4.new_per_event * ev)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                if mode == "scored":
+                    score(Kc, Pc, seq, tcur, sc_g, ws_s)
+                    kv.kv_select_topk(sc_g, seq, i32(P), w4.budget, w4.recent, w4.prompt_cap(), b_cap=b_cap,
+                                      kept=kept4, n_kept=nk4, workspace=ws_k)
+                else:
+                    draw(seq, i32(P), Pc, ev, kept4, nk4, ws_k)
+                if inplace:
+                    kv.kv_compact_inplace(Kc, Vc, kept4, nk4, seq, pos=Pc)
+                else:
+                    Ko, Vo, Po = bufs[1 - cur]
+                    kv.kv_compact(Kc, Vc, kept4, nk4, seq, Tc, pos=Pc, K_out=Ko, V_out=Vo, pos_out=Po)
+                    cur = 1 - cur
+                e1.record()
+                marks.append((e0, e1))
+                nk_h = np.where(T > w4.budget, np.maximum(w4.budget, P), T)   # the partition's n_kept
+                n_ev = int(T.sum()) * L * H
+                kept_rows = int(nk_h.sum()) * L * H
+                ents += n_ev
+                if mode == "scored":
+                    byts += n_ev * (row + 4 + 4) + n_ev * 4 + heads * b_cap * 4
+                else:
+                    byts += n_ev * 4 + heads * b_cap * 4
+                byts += kept_rows * (4 * row + 12) if not inplace else 0
+                T = nk_h.astype(np.int64)
+            torch.cuda.synchronize(dev)
+            ms = [a.elapsed_time(b) for a, b in marks]
+            key = f"{mode}_{'in_place' if inplace else 'gather'}"
+            gen[key] = {"events": len(ms), "total_ms": float(np.sum(ms)), "event_ms": percentiles(ms),
+                        "entries": ents, "entries_per_s": ents / (np.sum(ms) * 1e-3)}
+            if not inplace:
+                gen[key]["algorithmic_bytes"] = byts
+                gen[key]["gbs"] = byts / (np.sum(ms) * 1e-3) / 1e9
+            print(f"[bench] simulated generation, {key}: {len(ms)} events, {np.sum(ms):.1f} ms in total "
+                  f"(median event {np.median(ms):.3f} ms)", file=sys.stderr, flush=True)
+            del bufs
+            torch.cuda.empty_cache()
+    return {"workload": w4f.name, "entries_per_event": n,
+            "kernels": {"tri_score_with_positions": {"ms": score4_ms, "algorithmic_bytes": bytes_score,
+                                                     "gbs": bytes_score / (score4_ms * 1e-3) / 1e9},
+                        "kv_select_topk_ms": topk4_ms, "kv_select_random_ms": sel4_ms,
+                        "kv_compact": {"ms": gather_ms, "algorithmic_bytes": bytes_gather,
+                                       "gbs": bytes_gather / (gather_ms * 1e-3) / 1e9},
+                        "in_place_rows_moved": movers, "in_place_algorithmic_bytes": bytes_inplace},
+            "event_passes": passes, "generation": gen}
 
 
 def main():
@@ -320,6 +654,9 @@ def main():
         print(json.dumps({"error": "the KV-eviction path runs on one GPU; --gpus must be 1 "
                                    "(the path shards per (layer, seq, KV head) with no exchange)"}))
         sys.exit(2)
+    # the oracle's worker processes start before anything touches the GPU
+    timer = None if (args.no_cpu or args.pmc_probe or args.pmc_probe_next) else OracleTimer()
+
     import numpy as np
     import torch
 
@@ -343,6 +680,9 @@ def main():
     Ko = torch.empty((L, S, H, out_cap, d), dtype=K.dtype, device=dev)
     Vo = torch.empty_like(Ko)
     Po = torch.empty((L, S, H, out_cap), dtype=torch.int32, device=dev)
+    ws_score = torch.empty((kv.score_workspace_bytes(L, S, H, Tc, d, K.dtype, len(w.deltas)),), dtype=torch.uint8,
+                           device=dev)
+    ws_sel = torch.empty((kv.select_workspace_bytes(L, S, H, Tc, b_cap),), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize(dev)
     print("[bench] inputs resident", file=sys.stderr, flush=True)
 
@@ -363,9 +703,10 @@ def main():
 
     def scored_pass(ev=None):
         if ev: ev[0].record()
-        kv.tri_score(K, qbd, tcur, seq, w.theta, w.deltas, out=scores)
+        kv.tri_score(K, qbd, tcur, seq, w.theta, w.deltas, out=scores, workspace=ws_score)
         if ev: ev[1].record()
-        kv.kv_select_topk(scores, seq, plen, w.budget, w.recent, w.prompt_cap(), b_cap=b_cap, kept=kept, n_kept=nk)
+        kv.kv_select_topk(scores, seq, plen, w.budget, w.recent, w.prompt_cap(), b_cap=b_cap, kept=kept, n_kept=nk,
+                          workspace=ws_sel)
         if ev: ev[2].record()
         kv.kv_compact(K, V, kept, nk, seq, out_cap, K_out=Ko, V_out=Vo, pos_out=Po)
         if ev: ev[3].record()
@@ -373,7 +714,7 @@ def main():
     def random_pass(event, ev=None):
         if ev: ev[0].record()
         kv.kv_select_random((L, S, H, Tc), seq, plen, w.budget, w.recent, w.prompt_cap(), 0x5EED000000000003,
-                            event, b_cap=b_cap, kept=kept, n_kept=nk)
+                            event, b_cap=b_cap, kept=kept, n_kept=nk, workspace=ws_sel)
         if ev: ev[1].record()
         kv.kv_compact(K, V, kept, nk, seq, out_cap, K_out=Ko, V_out=Vo, pos_out=Po)
         if ev: ev[2].record()
@@ -462,9 +803,54 @@ def main():
         rk = {"kv_select_random": float(np.mean([revs[i][0].elapsed_time(revs[i][1]) for i in range(args.steps)])),
               "kv_compact": float(np.mean([revs[i][1].elapsed_time(revs[i][2]) for i in range(args.steps)]))}
         rbytes = ab["random_select"] + ab["compact"]
-        rnd = {"ms_per_pass": rwall, "entries_per_s": entries / (rwall * 1e-3),
-               "gbs": rbytes / (rwall * 1e-3) / 1e9, "kernel_ms": rk, "algorithmic_bytes": rbytes}
-        print(f"[bench] random pass {rwall:.3f} ms, kernels {rk}", file=sys.stderr, flush=True)
+        # the same pass with the draw of layer chunk c + 1 (ALU-bound) running beside the
+        # compaction of chunk c (HBM-bound) on a second stream of the same priority; each chunk's
+        # call is told its first layer, so the draws, the kept lists and the rows are those of the
+        # single call above
+        side = torch.cuda.Stream()
+        n_chunks = 9
+        bounds = np.linspace(0, L, n_chunks + 1).astype(int)
+        nks = [torch.empty((S,), dtype=torch.int32, device=dev) for _ in range(n_chunks)]
+        cevs = [torch.cuda.Event() for _ in range(n_chunks)]
+
+        def random_pass_overlapped(event):
+            cur = torch.cuda.current_stream()
+            side.wait_stream(cur)
+            for c in range(n_chunks):
+                lo, hi = int(bounds[c]), int(bounds[c + 1])
+                kv.kv_select_random((hi - lo, S, H, Tc), seq, plen, w.budget, w.recent, w.prompt_cap(),
+                                    0x5EED000000000003, event, b_cap=b_cap, kept=kept[lo:hi], n_kept=nks[c],
+                                    workspace=ws_sel, layer_base=lo)
+                cevs[c].record(cur)
+                with torch.cuda.stream(side):
+                    side.wait_event(cevs[c])
+                    kv.kv_compact(K[lo:hi], V[lo:hi], kept[lo:hi], nks[c], seq, out_cap, K_out=Ko[lo:hi],
+                                  V_out=Vo[lo:hi], pos_out=Po[lo:hi])
+            cur.wait_stream(side)
+
+        random_pass(4242)
+        torch.cuda.synchronize(dev)
+        ref_kept, ref_rows = kept.clone(), Ko[:, :, :, :64].clone()
+        kept.fill_(-7)
+        random_pass_overlapped(4242)
+        torch.cuda.synchronize(dev)
+        same = bool(torch.equal(kept, ref_kept) and torch.equal(Ko[:, :, :, :64], ref_rows))
+        del ref_kept, ref_rows
+        for i in range(args.warmup):
+            random_pass_overlapped(i)
+        torch.cuda.synchronize(dev)
+        t2 = time.perf_counter()
+        for i in range(args.steps):
+            random_pass_overlapped(2000 + i)
+        torch.cuda.synchronize(dev)
+        owall = (time.perf_counter() - t2) * 1e3 / args.steps
+        best = min(rwall, owall)
+        rnd = {"ms_per_pass": best, "entries_per_s": entries / (best * 1e-3),
+               "gbs": rbytes / (best * 1e-3) / 1e9, "algorithmic_bytes": rbytes,
+               "serial": {"ms_per_pass": rwall, "kernel_ms": rk},
+               "overlapped": {"ms_per_pass": owall, "layer_chunks": n_chunks, "same_as_serial": same}}
+        print(f"[bench] random pass {rwall:.3f} ms serial (kernels {rk}), {owall:.3f} ms with the draw beside the "
+              f"compaction in {n_chunks} layer chunks (identical: {same})", file=sys.stderr, flush=True)
 
     # the full TriAttention score (trigonometric + norm-based term) over the same cache
     from workloads import query_magnitudes
@@ -593,58 +979,21 @@ def main():
     print(f"[bench] grouped-query scores: {[(g['group'], round(g['ms_per_launch'], 3)) for g in gqa]}, "
           f"union select {union_ms:.3f} ms, recency select {recent_ms:.3f} ms", file=sys.stderr, flush=True)
 
-    # one periodic eviction of the gpt-oss-20b-shaped workload at its steady state (every head
-    # holds B + 128 = 2176 entries): random selection, then the gather into a second buffer or
-    # in-place hole filling
-    w4f = workload(4, seq_len=np.full(w4.n_seq, w4.t_cap, np.int32))
-    K4, V4 = kv_torch(w4f, dev, mu4)
-    seq4, plen4 = i32(w4f.seq_len), i32(w4f.prompt_len)
-    kept4, nk4 = kv.kv_select_random(tuple(K4.shape[:4]), seq4, plen4, w4f.budget, w4f.recent, w4f.prompt_cap(),
-                                     w4f.seed_random, 1, pos=pos4)
-    sel4_ms = time_launches(lambda: kv.kv_select_random(tuple(K4.shape[:4]), seq4, plen4, w4f.budget, w4f.recent,
-                                                        w4f.prompt_cap(), w4f.seed_random, 1, pos=pos4,
-                                                        kept=kept4, n_kept=nk4))
-    # the scored eviction of the same event: scores with explicit positions, then top-B
-    sc4 = torch.empty(K4.shape[:4], dtype=torch.float32, device=dev)
-    qb4d, tcur4 = torch.from_numpy(qb4).to(dev), i32(np.full(w4f.n_seq, w4f.t_cap))   # next position
-    score4_ms = time_launches(lambda: kv.tri_score(K4, qb4d, tcur4, seq4, w4f.theta, w4f.deltas, pos=pos4, out=sc4))
-    topk4 = torch.empty_like(kept4)
-    topk4_ms = time_launches(lambda: kv.kv_select_topk(sc4, seq4, plen4, w4f.budget, w4f.recent, w4f.prompt_cap(),
-                                                       kept=topk4, n_kept=torch.empty_like(nk4)))
-    score4_bytes = w4f.entries * (K4.shape[4] * K4.element_size() + 4 + 4)
-    del sc4, topk4
-    out4 = w4f.budget
-    Ko4 = torch.empty((*K4.shape[:3], out4, K4.shape[4]), dtype=K4.dtype, device=dev)
-    Vo4 = torch.empty_like(Ko4)
-    Po4 = torch.empty(Ko4.shape[:4], dtype=torch.int32, device=dev)
-    gather_ms = time_launches(lambda: kv.kv_compact(K4, V4, kept4, nk4, seq4, out4, pos=pos4, K_out=Ko4, V_out=Vo4,
-                                                    pos_out=Po4))
-    del Ko4, Vo4, Po4
-    inplace_ms = time_launches(lambda: kv.kv_compact_inplace(K4, V4, kept4, nk4, seq4, pos=pos4))
-    nkh = nk4.to(torch.int64)[None, :, None, None]
-    movers = int(((kept4.to(torch.int64) >= nkh) & (torch.arange(kept4.shape[-1], device=dev) < nkh)).sum())
-    row4 = K4.shape[4] * K4.element_size()
-    n_kept4 = int(nk4.sum()) * w4f.n_layers * w4f.n_kv_heads
-    gather_bytes = n_kept4 * (4 * row4 + 4 + 4 + 4)
-    inplace_bytes = movers * (4 * row4 + 4 + 4)
-    del K4, V4, pos4
-    periodic = {"workload": w4f.name, "entries_per_event": w4f.entries, "random_select_ms": sel4_ms,
-                "tri_score_with_positions": {"ms": score4_ms, "algorithmic_bytes": score4_bytes,
-                                             "gbs": score4_bytes / (score4_ms * 1e-3) / 1e9},
-                "topk_select_ms": topk4_ms,
-                "gather": {"ms": gather_ms, "algorithmic_bytes": gather_bytes,
-                           "gbs": gather_bytes / (gather_ms * 1e-3) / 1e9},
-                "in_place": {"ms": inplace_ms, "rows_moved": movers, "algorithmic_bytes": inplace_bytes,
-                             "gbs": inplace_bytes / (inplace_ms * 1e-3) / 1e9}}
-    print(f"[bench] periodic event: score (positions) {score4_ms:.3f} ms, top-k {topk4_ms:.3f} ms, "
-          f"random select {sel4_ms:.3f} ms, gather {gather_ms:.3f} ms, in place {inplace_ms:.3f} ms "
-          f"({movers} rows moved)", file=sys.stderr, flush=True)
+    del pos4
+    periodic = periodic_workload(args, dev, time_launches, mu4, qb4)
 
-    cpu = cpu_folded = None
-    if args.cpu_heads > 0:
-        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, K, qb, args.cpu_heads)
-        cpu_folded = cpu_baseline(w, K, qb, args.cpu_heads, folded=True)
+
+    cpu = protocol = None
+    if timer is not None:
+        print(f"[bench] timing the CPU oracle on {timer.cores} worker processes", file=sys.stderr, flush=True)
+        protocol = oracle_protocol(timer, dev, args, w, K, V, qb)
+        timer.close()
+        fp = protocol["full_pass_32k"]["folded"]
+        cpu = {"value": fp["entries_per_s"], "unit": "KV entries/s", "cores": timer.cores, "kind": "oracle",
+               "host_cpu": cpu_model(), "gpu_over_cpu": entries / (ms_step * 1e-3) / fp["entries_per_s"],
+               "sample": f"the whole {w.name} pass ({fp['entries']} entries): folded fp64 score + lexsort top-n "
+                         f"select + gather per (layer, seq, KV head), {timer.cores} worker processes, "
+                         f"{fp['seconds']:.1f} s; every workload in cpu_protocol"}
 
     others = None
     if not args.no_other_workloads:
@@ -700,7 +1049,7 @@ def main():
         "periodic_event": periodic,
         "other_workloads": others,
         "cpu_baseline": cpu,
-        "cpu_baseline_folded": cpu_folded,
+        "cpu_protocol": protocol,
     }
     print(json.dumps(out))
 

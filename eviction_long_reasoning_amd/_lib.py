@@ -72,7 +72,7 @@ _SIGNATURES = {
     "kv_select_topk": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, _P, _I32, _P, _P,
                               ctypes.c_size_t, _P]),
     "kv_select_random": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, ctypes.c_uint64,
-                                ctypes.c_uint32, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
+                                ctypes.c_uint32, _I32, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
     "kv_select_union": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _I32, _I32, _P, _P, _P, _I32, _P,
                                _P]),
     "kv_select_random_shared": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, ctypes.c_uint64,

@@ -311,8 +311,12 @@ def kv_select_random(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tens
                      budget: int, recent: int, prompt_cap: int, seed: int, event: int,
                      pos: Optional[torch.Tensor] = None, b_cap: Optional[int] = None,
                      kept: Optional[torch.Tensor] = None, n_kept: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Per-head kept slots under Random Attention's rule (Philox draw per head and event)."""
+                     workspace: Optional[torch.Tensor] = None, layer_base: int = 0
+                     ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-head kept slots under Random Attention's rule (Philox draw per head and event).
+
+    ``layer_base`` is the model index of the first layer of ``cache_shape`` (layer l draws as layer
+    layer_base + l), so a pass split into layer chunks draws what one call over all layers draws."""
     L, S, H, t_cap = (int(x) for x in cache_shape)
     dev = seq_len.device
     b_cap = int(b_cap if b_cap is not None else max(budget, prompt_cap))
@@ -325,7 +329,7 @@ def kv_select_random(cache_shape: Tuple[int, int, int, int], seq_len: torch.Tens
     need = int(_lib.load().kv_select_workspace_bytes(ctypes.byref(shape), b_cap))
     workspace, wp, wb = _workspace(workspace, need, dev)
     _invoke("kv_select_random", dev, ctypes.byref(shape), ctypes.byref(pol), pp, int(seed) & (2 ** 64 - 1),
-            int(event) & 0xFFFFFFFF, kp, b_cap, nkp, wp, wb)
+            int(event) & 0xFFFFFFFF, int(layer_base), kp, b_cap, nkp, wp, wb)
     return kept, n_kept
 
 

@@ -470,12 +470,15 @@ KV_EXPORT kv_status kv_select_topk(const kv_shape *shape, const kv_policy *polic
 }
 
 static kv_status select_random(const kv_shape *shape, const kv_policy *policy, const int32_t *pos, uint64_t seed,
-                               uint32_t event, int32_t *kept, int32_t b_cap, int32_t *n_kept, void *workspace,
-                               size_t workspace_bytes, void *stream, int shared_draw) {
+                               uint32_t event, int32_t layer_base, int32_t *kept, int32_t b_cap, int32_t *n_kept,
+                               void *workspace, size_t workspace_bytes, void *stream, int shared_draw) {
   SelectParams p{};
   kv_status st = select_common(shape, policy, kept, b_cap, n_kept, p);
   if (st != KV_OK) return st;
   if (!words({pos})) return KV_EINVAL;
+  // the counter packs the layer into 16 bits
+  if (layer_base < 0 || static_cast<long long>(layer_base) + shape->n_layers > 65536) return KV_EINVAL;
+  p.layer_base = layer_base;
   if ((st = select_workspace(shape, workspace, workspace_bytes, p)) != KV_OK) return st;
   p.pos = pos;
   p.seed_lo = static_cast<uint32_t>(seed & 0xffffffffu);
@@ -488,9 +491,11 @@ static kv_status select_random(const kv_shape *shape, const kv_policy *policy, c
 }
 
 KV_EXPORT kv_status kv_select_random(const kv_shape *shape, const kv_policy *policy, const int32_t *pos,
-                                     uint64_t seed, uint32_t event, int32_t *kept, int32_t b_cap,
-                                     int32_t *n_kept, void *workspace, size_t workspace_bytes, void *stream) {
-  return select_random(shape, policy, pos, seed, event, kept, b_cap, n_kept, workspace, workspace_bytes, stream, 0);
+                                     uint64_t seed, uint32_t event, int32_t layer_base, int32_t *kept,
+                                     int32_t b_cap, int32_t *n_kept, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+  return select_random(shape, policy, pos, seed, event, layer_base, kept, b_cap, n_kept, workspace, workspace_bytes,
+                       stream, 0);
 }
 
 KV_EXPORT kv_status kv_select_union(const kv_shape *shape, const kv_policy *policy, int32_t group,
@@ -520,7 +525,7 @@ KV_EXPORT kv_status kv_audit_kept(const kv_shape *shape, const kv_policy *policy
 KV_EXPORT kv_status kv_select_random_shared(const kv_shape *shape, const kv_policy *policy, const int32_t *pos,
                                           uint64_t seed, uint32_t event, int32_t *kept, int32_t b_cap,
                                           int32_t *n_kept, void *workspace, size_t workspace_bytes, void *stream) {
-  return select_random(shape, policy, pos, seed, event, kept, b_cap, n_kept, workspace, workspace_bytes, stream, 1);
+  return select_random(shape, policy, pos, seed, event, 0, kept, b_cap, n_kept, workspace, workspace_bytes, stream, 1);
 }
 
 KV_EXPORT kv_status kv_select_recent(const kv_shape *shape, const kv_policy *policy, int32_t *kept, int32_t b_cap,

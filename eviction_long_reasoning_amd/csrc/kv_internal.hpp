@@ -86,6 +86,7 @@ struct SelectParams {
   int32_t budget, recent, prompt_cap;
   uint32_t seed_lo, seed_hi, event;
   int32_t shared_draw;      // random: every (layer, head) draws as layer 0 / head 0
+  int32_t layer_base;       // random: layer l of the call draws as layer layer_base + l
   const float *head_scores; // union: [L,S,H,G,t_cap] per-query-head scores (scores = combined)
   int32_t G, k_per_head;    // union: query heads per KV head; per-head top-k (<= 0: ceil(n_sel / G))
   void *scratch;            // caller workspace past its header (select_scratch_bytes), or nullptr

@@ -412,7 +412,8 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
     // wave are skipped (a wave-uniform test per group), the rest run straight-line so that the
     // group's draws interleave.
     constexpr int GR = R < 8 ? R : 8;
-    const uint32_t c1 = p.shared_draw ? 0u : (static_cast<uint32_t>(hd.l) << 16) | static_cast<uint32_t>(hd.h);
+    const uint32_t c1 =
+        p.shared_draw ? 0u : (static_cast<uint32_t>(hd.l + p.layer_base) << 16) | static_cast<uint32_t>(hd.h);
     const __amdgpu_buffer_rsrc_t rp = rsrc_of(p.pos ? p.pos + slot0 : p.seq_len, p.pos ? e_hi * 4 : 0);
     const int j0 = slot_base();
 #pragma unroll
@@ -800,7 +801,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
   const int n_kept = max(B, P);
   const int n_cand = e_hi - e_lo;
   const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
-  const uint32_t c1 = p.shared_draw ? 0u : (static_cast<uint32_t>(l) << 16) | static_cast<uint32_t>(h);
+  const uint32_t c1 = p.shared_draw ? 0u : (static_cast<uint32_t>(l + p.layer_base) << 16) | static_cast<uint32_t>(h);
   const int passes = UNION ? (n_sel > 0 ? p.G : 0) + 1 : 1;
   const int k_head = UNION ? (p.k_per_head > 0 ? p.k_per_head : (n_sel + p.G - 1) / p.G) : 0;
   const int words = (T + 31) >> 5;

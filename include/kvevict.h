@@ -355,13 +355,17 @@ size_t kv_select_workspace_bytes(const kv_shape *shape, int32_t b_cap);
  *
  *  pos      device [L,S,H,t_cap] int32 positions for the counter, or NULL (p_j = j).
  *  seed     64-bit key; event: eviction counter (fresh draws per event).
+ *  layer_base  model index of the call's first layer: layer l of the call draws as layer
+ *           layer_base + l (an engine that evicts layer by layer, or a pass split into layer
+ *           chunks, gets the same draws as one call over all layers); 0 <= layer_base and
+ *           layer_base + n_layers <= 65536.
  *  kept, b_cap, n_kept, workspace as for kv_select_topk (t_cap <= 2^26; past
  *  32768 slots the draws are recomputed at every step).
  * Device checks (debug build): KV_DEV_SEQ_LEN, KV_DEV_PROMPT_LEN, and
  * KV_DEV_POS_ORDER when pos is given.
  */
 kv_status kv_select_random(const kv_shape *shape, const kv_policy *policy,
-                           const int32_t *pos, uint64_t seed, uint32_t event,
+                           const int32_t *pos, uint64_t seed, uint32_t event, int32_t layer_base,
                            int32_t *kept, int32_t b_cap, int32_t *n_kept,
                            void *workspace, size_t workspace_bytes, void *stream);
 

@@ -95,7 +95,9 @@ int main() {
   {
     int32_t *k = reinterpret_cast<int32_t *>(0x3000), *n = reinterpret_cast<int32_t *>(0x4000);
     EXPECT(kv_select_topk(&sh, &pol, (const float *)dummy, k, 1024, n, wsp, need_sel - 1, nullptr), KV_EWORKSPACE);
-    EXPECT(kv_select_random(&sh, &pol, nullptr, 1, 0, k, 1024, n, nullptr, need_sel, nullptr), KV_EWORKSPACE);
+    EXPECT(kv_select_random(&sh, &pol, nullptr, 1, 0, 0, k, 1024, n, nullptr, need_sel, nullptr), KV_EWORKSPACE);
+    EXPECT(kv_select_random(&sh, &pol, nullptr, 1, 0, -1, k, 1024, n, wsp, need_sel, nullptr), KV_EINVAL);
+    EXPECT(kv_select_random(&sh, &pol, nullptr, 1, 0, 65536, k, 1024, n, wsp, need_sel, nullptr), KV_EINVAL);
     EXPECT(kv_select_random_shared(&sh, &pol, nullptr, 1, 0, k, 1024, n, (void *)0x7000004, need_sel, nullptr), KV_EWORKSPACE);
   }
 
@@ -106,7 +108,7 @@ int main() {
   kv_shape big = sh;
   big.t_cap = (1 << 26) + 1;
   EXPECT(kv_select_topk(&big, &pol, (const float *)dummy, kept, 1024, nk, wsp, 1 << 20, nullptr), KV_ESHAPE);
-  EXPECT(kv_select_random(&big, &pol, nullptr, 1, 0, kept, 1024, nk, wsp, 1 << 20, nullptr), KV_ESHAPE);
+  EXPECT(kv_select_random(&big, &pol, nullptr, 1, 0, 0, kept, 1024, nk, wsp, 1 << 20, nullptr), KV_ESHAPE);
   EXPECT(kv_select_random_shared(&big, &pol, nullptr, 1, 0, kept, 1024, nk, wsp, 1 << 20, nullptr), KV_ESHAPE);
   big.t_cap = (1 << 18) + 1;
   EXPECT(kv_select_union(&big, &pol, 4, 0, (const float *)dummy, (const float *)dummy, kept, 1024, nk, nullptr), KV_ESHAPE);

@@ -144,7 +144,7 @@ def test_host_validation_rejects_bad_arguments(lib):
     pol = L.KvPolicy(8, 2, 12, seq)
     assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), dummy, dummy, 8, dummy, WS, 1 << 20, None) == L.KV_ESHAPE
     pol = L.KvPolicy(8, 2, 4, seq)
-    assert lib.kv_select_random(ctypes.byref(huge_sel), ctypes.byref(pol), None, 1, 0, dummy, 8, dummy, WS, 1 << 20, None) == L.KV_ESHAPE
+    assert lib.kv_select_random(ctypes.byref(huge_sel), ctypes.byref(pol), None, 1, 0, 0, dummy, 8, dummy, WS, 1 << 20, None) == L.KV_ESHAPE
     assert lib.kv_select_topk(ctypes.byref(huge_sel), ctypes.byref(pol), dummy, dummy, 8, dummy, WS, 1 << 20, None) == L.KV_ESHAPE
     assert lib.kv_select_recent(ctypes.byref(huge_sel), ctypes.byref(pol), dummy, 8, dummy, None) == L.KV_ESHAPE
     pol = L.KvPolicy(0, 2, 4, seq)
@@ -182,11 +182,15 @@ def test_workspace_queries_and_rejections(lib):
     for ws, nbytes in ((None, 1 << 30), (ctypes.c_void_p(0x7000004), 1 << 30), (WS, need_k - 1)):
         assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), ok, ok, 3072, ok, ws, nbytes,
                                   None) == L.KV_EWORKSPACE
-        assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, ok, 3072, ok, ws, nbytes,
+        assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, 0, ok, 3072, ok, ws, nbytes,
                                     None) == L.KV_EWORKSPACE
         assert lib.kv_select_random_shared(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, ok, 3072, ok, ws,
                                            nbytes, None) == L.KV_EWORKSPACE
     assert "workspace" in lib.kv_status_string(L.KV_EWORKSPACE).decode()
+    # the draw's layer index is packed into 16 bits: layer_base + n_layers must stay within it
+    for base in (-1, 65536 - 36 + 1):
+        assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, base, ok, 3072, ok, WS,
+                                    need_k, None) == L.KV_EINVAL
 
 
 def test_device_check_build_loads_and_reports_itself():
@@ -248,8 +252,8 @@ def test_misaligned_word_arrays_are_rejected(lib):
     pol_odd = L.KvPolicy(1024, 64, 128, odd)
     assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol), odd, ok, 1024, ok, WS, 1 << 20, None) == L.KV_EINVAL
     assert lib.kv_select_topk(ctypes.byref(sh), ctypes.byref(pol_odd), ok, ok, 1024, ok, WS, 1 << 20, None) == L.KV_EINVAL
-    assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, odd, 1024, ok, WS, 1 << 20, None) == L.KV_EINVAL
-    assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), odd, 1, 0, ok, 1024, ok, WS, 1 << 20, None) == L.KV_EINVAL
+    assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, 0, odd, 1024, ok, WS, 1 << 20, None) == L.KV_EINVAL
+    assert lib.kv_select_random(ctypes.byref(sh), ctypes.byref(pol), odd, 1, 0, 0, ok, 1024, ok, WS, 1 << 20, None) == L.KV_EINVAL
     assert lib.kv_select_random_shared(ctypes.byref(sh), ctypes.byref(pol), None, 1, 0, ok, 1024, odd, WS, 1 << 20, None) == L.KV_EINVAL
     assert lib.kv_select_union(ctypes.byref(sh), ctypes.byref(pol), 2, 0, odd, ok, ok, 1024, ok, None) == L.KV_EINVAL
     assert lib.kv_select_recent(ctypes.byref(sh_odd), ctypes.byref(pol), ok, 1024, ok, None) == L.KV_EINVAL

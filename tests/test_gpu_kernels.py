@@ -566,6 +566,31 @@ def test_selectors_at_tier_edges_bit_exact(t_cap):
                 assert np.all(got[0, s, h, ref.size:] == -1), f"{name} {what} s{s} h{h} padding"
 
 
+def test_select_random_layer_chunks_draw_as_one_call():
+    # a pass split into layer chunks (each call told its first layer) keeps what one call keeps,
+    # and every chunk matches the oracle at the model's layer index
+    L, S, H, t_cap = 5, 2, 3, 3000
+    Ts, Ps = [3000, 2500], [200, 700]
+    B, R, pcap, seed, event = 1000, 64, 700, 0x5EED0000000000AB, 12
+    log("[random] layer chunks")
+    r = rng(571, t_cap)
+    pos = _i32(np.sort(r.integers(0, 2 ** 30, (L, S, H, t_cap)), axis=-1).astype(np.int32))
+    whole, nw = kv.kv_select_random((L, S, H, t_cap), _i32(Ts), _i32(Ps), B, R, pcap, seed, event, pos=pos)
+    parts = []
+    for lo, hi in ((0, 2), (2, 3), (3, 5)):
+        k, n = kv.kv_select_random((hi - lo, S, H, t_cap), _i32(Ts), _i32(Ps), B, R, pcap, seed, event,
+                                   pos=pos[lo:hi].contiguous(), layer_base=lo)
+        assert torch.equal(n, nw)
+        parts.append(k)
+    assert torch.equal(torch.cat(parts, 0), whole)
+    got = parts[2].cpu().numpy()
+    p = pos.cpu().numpy()
+    for s in range(S):
+        for h in range(H):
+            ref = oracle.select_random(Ts[s], Ps[s], B, R, p[4, s, h], seed, event, 4, h, s)
+            assert np.array_equal(got[1, s, h, :ref.size], ref)
+
+
 def test_select_random_fresh_per_event_and_head():
     Ts, Ps = [4000], [100]
     a, _ = kv.kv_select_random((1, 1, 2, 4000), _i32(Ts), _i32(Ps), 1000, 32, 100, 9, 1)

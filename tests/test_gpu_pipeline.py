@@ -17,7 +17,8 @@ import torch
 
 import eviction_long_reasoning_amd as kv
 import oracle
-from parity import assert_scores, assert_selection_near_threshold, assert_z, keys_f64, log
+from parity import (assert_scores, assert_selection_near_threshold, assert_union_near_thresholds, assert_z, keys_f64,
+                    log)
 from workloads import (centres, kv_numpy, kv_torch, periodic_prompt_torch, periodic_tokens_torch,
                        query_head_centres, query_head_magnitudes, query_magnitudes, workload)
 
@@ -227,7 +228,6 @@ def test_workload2_gqa_zscore_max():
         sch, hsh, kh, ukh = sc.cpu().numpy(), hs.cpu().numpy(), kept.cpu().numpy(), ukept.cpu().numpy()
         worst_s = worst_z = 0.0
         diffs = udiffs = 0
-        n_sel = oracle.partition(int(T[0]), int(P[0]), w.budget, w.recent).n_sel
         for h in range(w.n_kv_heads):
             zref, per = oracle.score_gqa(keys_f64(K[0, 0, h], w.dtype), None, nu[0, h], int(w.t_cur[0]), w.theta,
                                          w.deltas, qabs[0, h] if with_norm else None)
@@ -237,12 +237,12 @@ def test_workload2_gqa_zscore_max():
             rk = oracle.select_topk(zref, int(T[0]), int(P[0]), w.budget, w.recent)
             diffs += assert_selection_near_threshold(kh[0, 0, h, :int(nk[0])], rk, zref, int(T[0]), int(P[0]),
                                                      w.budget, w.recent, f"w2-gqa h{h}")
-            # the union rule compounds G + 1 rankings, so fp32-vs-fp64 rounding may swap a few
-            # near-threshold slots; the selector itself is bit-exact on identical inputs
+            # the union rule compounds G + 1 rankings: exact on the GPU's own scores, and against the
+            # oracle's scores every differing slot sits near one of the rule's thresholds
             uref = oracle.select_union(per, zref, int(T[0]), int(P[0]), w.budget, w.recent)
-            ud = len(set(uref.tolist()) ^ set(ukh[0, 0, h, :int(unk[0])].tolist()))
-            assert int(unk[0]) == uref.size and ud <= max(4, n_sel // 100), f"w2-union h{h}: {ud} slots differ"
-            udiffs += ud
+            assert int(unk[0]) == uref.size
+            udiffs += assert_union_near_thresholds(ukh[0, 0, h, :int(unk[0])], hsh[0, 0, h], sch[0, 0, h], per, zref,
+                                                   int(T[0]), int(P[0]), w.budget, w.recent, f"w2-union h{h}")
         log(f"[w2-gqa norm={with_norm}] 8 KV heads x 4 query heads: worst head-score error {worst_s:.2e}, "
             f"worst z error {worst_z:.2e}, kept differences {diffs}; union rule: {udiffs} slots differ")
 
