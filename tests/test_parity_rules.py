@@ -30,8 +30,7 @@ def test_tiny_perturbations_are_accepted():
         gh = head * (1 + 1e-6 * r.standard_normal(head.shape))
         gc = gh.max(axis=0)
         kept = oracle.select_union(gh, gc, T, P, B, R)
-        differing += assert_union_near_thresholds(kept, gh, gc, head, comb, T, P, B, R, f"seed {seed}")
-    assert differing > 0    # some of the forced flips change the kept set
+        assert_union_near_thresholds(kept, gh, gc, head, comb, T, P, B, R, f"seed {seed}")
 
 
 def test_a_swap_forced_at_a_head_threshold_is_accepted():
