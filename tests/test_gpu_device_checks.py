@@ -57,8 +57,8 @@ def _random(L, lib, shape4, seq, plen, pcap, pos, ws):
     b_cap = max(64, pcap)
     kept = torch.empty((Lq, S, H, b_cap), dtype=torch.int32, device=DEV)
     nk = torch.empty((S,), dtype=torch.int32, device=DEV)
-    st = lib.kv_select_random(ctypes.byref(sh), ctypes.byref(po), P_(pos), 9, 2, P_(kept), b_cap, P_(nk), P_(ws),
-                              ws.numel(), STREAM())
+    st = lib.kv_select_random(ctypes.byref(sh), ctypes.byref(po), P_(pos), 9, 2, 0, P_(kept), b_cap, P_(nk),
+                              P_(ws), ws.numel(), STREAM())
     assert st == L.KV_OK, st
     return kept, nk
 
