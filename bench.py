@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=36, help="layers of the full-pass workload (36 = full size)")
     ap.add_argument("--no-cpu", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-random", action="store_true", help="skip the random-eviction pass")
+    ap.add_argument("--no-generation", action="store_true",
+                    help="skip the simulated 256-event generation of the periodic workload")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the 512-slot, one-layer and ragged-batch workloads")
     ap.add_argument("--pmc-probe", action="store_true",
@@ -81,11 +83,11 @@ def pmc_probe_next(w, K, qb, qbd, seq, plen, tcur, scores, kept, nk, b_cap, dev)
     out.append(["gqa_stream_kernel<true, 16, true, false, 4>", n * d * e, n * 4 * G])
     out.append(["gqa_finish_kernel<4>", n * 4 * G, n * 4])
     kv.kv_select_union(head, zmax, seq, plen, w.budget, w.recent, w.prompt_cap(), b_cap=b_cap, kept=kept, n_kept=nk)
-    out.append(["select_kernel<512, 64, 2, true>", n * 4 * (G + 1), heads * b_cap * 4])
+    out.append(["select_kernel<1024, 32, 2>", n * 4 * (G + 1), heads * b_cap * 4])
     del zmax, head
     kv.kv_select_random((L, S, H, T), seq, plen, w.budget, w.recent, w.prompt_cap(), 1, 0, b_cap=b_cap, kept=kept,
                         n_kept=nk)
-    out.append(["select_kernel<1024, 32, 1, false>", 0, heads * b_cap * 4])
+    out.append(["select_kernel<1024, 32, 1>", 0, heads * b_cap * 4])
     Sl, Tl = S // 4, 4 * T
     kl = torch.empty((L, Sl, H, b_cap), dtype=torch.int32, device=dev)
     nkl = torch.empty((Sl,), dtype=torch.int32, device=dev)
@@ -575,6 +577,12 @@ def periodic_workload(args, dev, time_launches, mu4, qb4):
 
     # the simulated generation: every sequence starts at its prompt; events fire every 128 generated
     # tokens; a sequence whose cache exceeds B is evicted back to B (its other slots copied as they are)
+    if args.no_generation:
+        return {"workload": w4f.name, "entries_per_event": n,
+                "kernels": {"tri_score_with_positions": {"ms": score4_ms, "algorithmic_bytes": bytes_score},
+                            "kv_select_topk_ms": topk4_ms, "kv_select_random_ms": sel4_ms,
+                            "kv_compact": {"ms": gather_ms, "algorithmic_bytes": bytes_gather}},
+                "event_passes": passes, "generation": None}
     P = w4.prompt_len.astype(np.int64)
     mu0, _, dr = centres(w4)
     K0, V0 = periodic_prompt_torch(w4, mu0, dr, dev)
@@ -857,14 +865,25 @@ def main():
     qabs = torch.from_numpy(query_magnitudes(w, qb)).to(dev)
     for _ in range(args.warmup):
         kv.tri_score(K, qbd, tcur, seq, w.theta, w.deltas, out=scores, qabs=qabs)
-    fev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    fev[0].record()
-    for _ in range(args.steps):
-        kv.tri_score(K, qbd, tcur, seq, w.theta, w.deltas, out=scores, qabs=qabs)
-    fev[1].record()
-    torch.cuda.synchronize(dev)
-    full_ms = fev[0].elapsed_time(fev[1]) / args.steps
-    print(f"[bench] tri_score with norm term {full_ms:.3f} ms", file=sys.stderr, flush=True)
+
+    def launches_ms(with_norm):
+        fev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        fev[0].record()
+        for _ in range(args.steps):
+            kv.tri_score(K, qbd, tcur, seq, w.theta, w.deltas, out=scores, qabs=qabs if with_norm else None)
+        fev[1].record()
+        torch.cuda.synchronize(dev)
+        return fev[0].elapsed_time(fev[1]) / args.steps
+
+    # the plain score timed right beside it, alternating, so the ratio compares like with like
+    norm_runs, plain_runs = [], []
+    for _ in range(2):
+        norm_runs.append(launches_ms(True))
+        plain_runs.append(launches_ms(False))
+    full_ms, plain_ms = min(norm_runs), min(plain_runs)
+    norm_ratio = full_ms / plain_ms
+    print(f"[bench] tri_score with norm term {full_ms:.3f} ms, plain {plain_ms:.3f} ms beside it "
+          f"(ratio {norm_ratio:.3f}{', ABOVE 1.1' if norm_ratio > 1.1 else ''})", file=sys.stderr, flush=True)
 
     # keys stored after RoPE: dense, and through a block table over the same memory viewed as a
     # paged pool [L, n_blocks, 16, H, d] with a shuffled table
@@ -1035,7 +1054,9 @@ def main():
                                 "kv_select_topk": ab["select"] / (k_ms["kv_select_topk"] * 1e-3) / 1e9,
                                 "kv_compact": ab["compact"] / (k_ms["kv_compact"] * 1e-3) / 1e9}},
         "random_pass": rnd,
-        "score_with_norm_term": {"ms_per_launch": full_ms, "gbs": ab["score"] / (full_ms * 1e-3) / 1e9},
+        "score_with_norm_term": {"ms_per_launch": full_ms, "gbs": ab["score"] / (full_ms * 1e-3) / 1e9,
+                                 "plain_ms_beside": plain_ms, "over_plain": norm_ratio,
+                                 "over_plain_above_1_1": norm_ratio > 1.1},
         "score_rotated_keys": {"dense_ms": rot_ms, "dense_gbs": ab["score"] / (rot_ms * 1e-3) / 1e9,
                                "paged16_ms": paged_ms, "paged16_gbs": ab["score"] / (paged_ms * 1e-3) / 1e9,
                                "paged16_head_major_ms": paged_hm_ms,
