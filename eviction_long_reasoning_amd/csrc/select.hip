@@ -16,20 +16,28 @@
 //  1. Keys: fp32 scores with NaN ranked as -inf (float comparisons give the
 //     ranking, -0 equal to +0) or, for the random selector, word 0 of
 //     Philox4x32-10 compared as uint32.
-//  2. A 1024-bin LDS histogram (scores binned by value between the smallest
-//     and largest finite candidate, random keys by their top 10 bits) finds
-//     the bin holding the n_sel-th largest key; every key in a higher bin is
-//     larger.
-//  3. That bin's keys, usually a few dozen, are listed in LDS and ranked
-//     directly to give the n_sel-th largest key thr and how many keys equal to
-//     thr must be taken (need). A crowded bin instead goes through 8-bit radix
-//     passes over a 256-bin histogram, from the highest bit where its keys
-//     differ (an OR/AND block reduction).
-//  4. Placement without a sort: the prompt and the recent window go to their
-//     fixed places; a selected evictable slot goes to P + (selected slots
-//     before it), counted from one ballot per (round, wave) and the lanes
-//     below it in its wave's ballot. Ties go to the lower slot, and the kept
-//     list comes out in ascending order.
+//  2. Listed path (selections of at most half the candidates): a cut below the
+//     threshold -- from a sample of the scores (two rounds per thread, binned by
+//     value) or, for uniform random words, from the selection's share -- is
+//     checked by counting the keys at or above it (one ballot per round and
+//     wave). When at least n_sel and at most the list's capacity pass, those
+//     keys and their slots are copied to LDS in slot order, a 256-bin histogram
+//     over the list finds the threshold's bin, and its members are ranked
+//     directly: thr is the n_sel-th largest key, need the number of keys equal
+//     to it that are taken. Placement then runs over the list alone: one
+//     block-wide scan of per-thread (kept, tied) counts gives each kept entry
+//     its output index. A cut that fails the count falls back to step 3.
+//  3. Otherwise a 1024-bin LDS histogram over every key (scores binned by value
+//     between the smallest and largest finite candidate, random keys by their
+//     top 10 bits) finds the bin holding the n_sel-th largest key; its keys,
+//     usually a few dozen, are listed in LDS and ranked directly. A crowded bin
+//     instead goes through 8-bit radix passes over a 256-bin histogram, from
+//     the highest bit where its keys differ (an OR/AND block reduction).
+//     Placement without a sort: a selected evictable slot goes to P + (selected
+//     slots before it), counted from one ballot per (round, wave) and the lanes
+//     below it in its wave's ballot.
+//  4. The prompt and the recent window go to their fixed places. Ties go to the
+//     lower slot, and the kept list comes out in ascending order.
 #include "kv_internal.hpp"
 
 #include <type_traits>
@@ -300,6 +308,67 @@ __device__ __forceinline__ void rank_members(const uint32_t *list, uint32_t m, u
 template <int NT>
 constexpr uint32_t member_cap() { return 2 * NT < kValueBins - 4 ? 2 * NT : kValueBins - 4; }
 
+// The listed path. A sample of the keys (one per thread) puts a cut below the threshold with high
+// probability; the keys at or above it, typically 1.2-1.5 times the selection, are copied to LDS in
+// slot order, and the threshold search and the ordered placement run over that list instead of over
+// every key. The count of listed keys is checked before anything depends on the cut: a cut that
+// leaves fewer keys than the selection, or more than the list holds, falls back to the search over
+// all keys.
+constexpr int kSampleBins = 256;
+constexpr int kListBins = 256;
+constexpr int kListMax = 6144;
+// A quarter of the tier's slots: selections above half the candidates never list, and a small
+// list keeps the 256-thread tiers' LDS (and so their workgroups per CU) close to the histogram's.
+template <int NT, int KPT>
+constexpr int list_cap() { return NT * KPT / 4 < kListMax ? NT * KPT / 4 : kListMax; }
+
+// Equal-width bins between a cut and the largest key, for any bin count (the clamp happens in
+// floating point, so the conversion is always in range).
+__device__ __forceinline__ uint32_t bin_clamped(float v, float scale, float off, int nbins) {
+  const float x = fminf(fmaxf(fmaf(v, scale, off), 0.f), static_cast<float>(nbins - 1));
+  return static_cast<uint32_t>(x);
+}
+
+// Run by every wave on its own (no barrier): with lane L owning bins PER*L ... PER*L + PER - 1 of
+// an LDS histogram, the bin where the count from the top first reaches want_of(total) (0 when the
+// total stays below it) and the count in the bins above it, both wave-uniform.
+template <int NBINS, class Want>
+__device__ __forceinline__ void wave_find_bin(const uint32_t *hist, Want want_of, int lane, uint32_t &bin,
+                                              uint32_t &above, uint32_t &total) {
+  constexpr int PER = NBINS / 64;
+  uint32_t c[PER];
+  uint32_t local = 0u;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    c[q] = hist[PER * lane + q];
+    local += c[q];
+  }
+  const uint32_t incl = wave_inclusive_sum(local);
+  total = wave_total(incl);
+  const uint32_t want = want_of(total);
+  uint32_t cum = total - incl;
+  int mine = -1;
+  uint32_t mine_above = 0u;
+#pragma unroll
+  for (int q = PER - 1; q >= 0; --q) {
+    const uint32_t a = cum;
+    cum += c[q];
+    if (a < want && cum >= want) {
+      mine = PER * lane + q;
+      mine_above = a;
+    }
+  }
+  const uint64_t m = __ballot(mine >= 0);
+  if (m == 0ull) {
+    bin = 0u;
+    above = 0u;
+    return;
+  }
+  const int src = __builtin_ctzll(m);
+  bin = static_cast<uint32_t>(__builtin_amdgcn_readlane(mine, src));
+  above = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mine_above), src));
+}
+
 // 4-byte buffer load: the per-round offset rides in a scalar register, and reads past the
 // resource's byte range return 0 without a memory access.
 __device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
@@ -347,6 +416,14 @@ struct SelectSmem {
   uint32_t *cnt_e;    // NW: per wave, slots equal to the threshold
   uint32_t *found;    // 3
   uint32_t *n_members;
+  // the listed path
+  uint32_t *shist;    // kSampleBins: the sample's value histogram
+  uint32_t *mlist;    // kValueBins: the threshold bin's members, zero beyond the last
+  uint32_t *cnt_l;    // NW: per wave, listed keys, then packed placement counts
+  uint32_t *lkey;     // list_cap: key bits of the listed slots, in slot order (scores as fp32 bits,
+                      // random keys as the word)
+  uint32_t *lslot;    // list_cap: their slots (same index: one address, two immediate offsets)
+  int list_cap;
 };
 
 struct SelectHead {
@@ -483,12 +560,22 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
     uint32_t thr = 0u, need = 0u;   // thr as an order key (scores) or a word (random)
     bool all_ties = true;           // every key equal to thr is taken
     bool careful = false;           // random keys: the slot range decides membership, ties, placement
+    bool listed = false;            // the threshold came from the list, which is still in LDS
+    uint32_t n_list = 0u;
     if (mode == 2) {
       uint32_t remaining = static_cast<uint32_t>(p_sel);
       bool binned = RANDOM, ranked = false;
       float scale = 0.f, off = 0.f;
+      float mn = INFINITY, mx = -INFINITY;
+      // the listed path's LDS starts cleared (its readers in an earlier pass are behind a barrier;
+      // the barriers of the min/max reduction, or of the count below, order this before any use)
+      for (int i = tid; i < kValueBins; i += NT) {
+        hist[i] = 0u;
+        sm.mlist[i] = 0u;
+      }
+      for (int i = tid; i < kSampleBins; i += NT) sm.shist[i] = 0u;
+      if (tid == 0) *sm.n_members = 0u;
       if (!RANDOM) {
-        float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
           mn = fminf(mn, fkey(i));
@@ -512,6 +599,102 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
         off = -mn * scale;
         binned = mn < mx && scale > 0.f && scale < 3.0e38f && fabsf(off) < 3.0e38f;
       }
+
+      // ---- listed path: cut, count, list, then the threshold over the list
+      auto try_list = [&]() __attribute__((always_inline)) -> bool {
+        float cut_f = -INFINITY;   // scores: list x >= cut_f (NaN marks never pass)
+        uint32_t cut_k = 1u;       // random: list words >= cut_k (slots that take no part hold 0)
+        if (RANDOM) {
+          // the p_sel-th largest of n_valid uniform words sits near 2^32 (1 - p_sel / n_valid); the
+          // cut leaves about four standard deviations more
+          const float want = static_cast<float>(p_sel) + 4.f * sqrtf(static_cast<float>(p_sel)) + 16.f;
+          if (want < static_cast<float>(n_valid)) {
+            const double c = 4294967296.0 * (1.0 - static_cast<double>(want) / static_cast<double>(n_valid));
+            cut_k = c > 1.0 ? static_cast<uint32_t>(c) : 1u;
+          }
+        } else {
+          // two keys per thread (rounds R/4 and 3R/4: two blocks of 64 consecutive slots per wave,
+          // spread evenly over the head) into kSampleBins value bins; the cut is one bin below where
+          // the count from the top reaches the sample's expected share of p_sel plus three standard
+          // deviations. The rounds are fixed: a per-lane choice of round would index the key array.
+          const float sscale = static_cast<float>(kSampleBins) / (mx - mn), soff = -mn * sscale;
+          constexpr int kS0 = R >= 4 ? R / 4 : 0, kS1 = R >= 4 ? 3 * R / 4 : R - 1;
+          const float sx0 = fkey(kS0), sx1 = fkey(kS1);
+          if (sx0 == sx0) atomicAdd(&sm.shist[bin_clamped(sx0, sscale, soff, kSampleBins)], 1u);
+          if (kS1 != kS0 && sx1 == sx1) atomicAdd(&sm.shist[bin_clamped(sx1, sscale, soff, kSampleBins)], 1u);
+          __syncthreads();
+          uint32_t bc, above_s, n_s;
+          wave_find_bin<kSampleBins>(sm.shist, [&](uint32_t tot) {
+            const float lam = static_cast<float>(p_sel) * static_cast<float>(tot) / static_cast<float>(n_valid);
+            return static_cast<uint32_t>(lam + 3.f * sqrtf(lam) + 4.f);
+          }, lane, bc, above_s, n_s);
+          if (bc > 1u) cut_f = (static_cast<float>(bc - 1u) - soff) / sscale;
+        }
+        auto pass_cut = [&](int i) { return RANDOM ? key[i] >= cut_k : fkey(i) >= cut_f; };
+        uint32_t cnt = 0u;
+#pragma unroll
+        for (int i = 0; i < R; ++i) cnt += static_cast<uint32_t>(__popcll(__ballot(pass_cut(i))));
+        if (lane == 0) sm.cnt_l[wave] = cnt;
+        __syncthreads();
+        uint32_t total = 0u, base = 0u;
+        for (int w = 0; w < NW; ++w) {
+          const uint32_t c = sm.cnt_l[w];
+          if (w < wave) base += c;
+          total += c;
+        }
+        if (total < static_cast<uint32_t>(p_sel) || total > static_cast<uint32_t>(sm.list_cap)) return false;
+        // bins over the listed range: scores by value between the cut (or the smallest finite key)
+        // and the largest; random words by their offset above the cut
+        const float lo = cut_f > -INFINITY ? cut_f : mn;
+        const float scale2 = static_cast<float>(kListBins) / (mx - lo), off2 = -lo * scale2;
+        if (!RANDOM && !(mx > lo && scale2 > 0.f && scale2 < 3.0e38f && fabsf(off2) < 3.0e38f)) return false;
+        const uint32_t span = 0xFFFFFFFFu - cut_k;
+        const int bits = span ? 32 - __clz(span) : 0;
+        const int shift = bits > 8 ? bits - 8 : 0;
+        auto lbin = [&](uint32_t k) {
+          return RANDOM ? (k - cut_k) >> shift : bin_clamped(__uint_as_float(k), scale2, off2, kListBins);
+        };
+        {
+          const int j0 = slot_base();
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            const bool m = pass_cut(i);
+            const uint64_t b = __ballot(m);
+            if (m) {
+              const uint32_t at = base + lanes_below(b);
+              sm.lkey[at] = key[i];
+              sm.lslot[at] = static_cast<uint32_t>(j0 + i * 64);
+            }
+            base += static_cast<uint32_t>(__popcll(b));
+          }
+        }
+        __syncthreads();
+        for (uint32_t e = tid; e < total; e += NT) atomicAdd(&hist[lbin(sm.lkey[e])], 1u);
+        __syncthreads();
+        uint32_t b, above, tot;
+        wave_find_bin<kListBins>(hist, [&](uint32_t) { return static_cast<uint32_t>(p_sel); }, lane, b, above, tot);
+        const uint32_t rem = static_cast<uint32_t>(p_sel) - above;
+        for (uint32_t e = tid; e < total; e += NT) {
+          const uint32_t k = sm.lkey[e];
+          if (lbin(k) == b) {
+            const uint32_t at = atomicAdd(sm.n_members, 1u);
+            if (at < member_cap<NT>()) sm.mlist[at] = RANDOM ? k : order_key(__uint_as_float(k));
+          }
+        }
+        __syncthreads();
+        const uint32_t m = *sm.n_members;
+        if (m > member_cap<NT>()) return false;
+        rank_members<NT>(sm.mlist, m, rem, found);   // entries past m are still zero
+        __syncthreads();
+        thr = found[0];
+        need = found[1];
+        all_ties = found[2] == need;
+        n_list = total;
+        return true;
+      };
+      // above half the candidates the placement must visit every key anyway: no list
+      if (binned && 2 * p_sel <= n_valid) listed = try_list();
+      if (!listed) {
       __syncthreads();   // the previous pass's readers of hist are done
       // valid: the key takes part (scores: not the NaN mark; random: the slot range)
       auto valid = [&](int i, int j0) {
@@ -616,6 +799,48 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
         // every valid key
         radix(valid);
       }
+      }
+    }
+
+    // ---- placement from the list (top-k and random): thread t takes a contiguous run of list
+    // entries, so one block-wide scan of its (kept outright, tied) counts orders every output.
+    // Scores compare as fp32 against the threshold's value (-0 equals +0, as for order keys).
+    if (!UNION && listed) {
+      const uint32_t n = n_list;
+      const uint32_t per = (n + NT - 1) / NT;
+      const uint32_t e0 = min(n, static_cast<uint32_t>(tid) * per), e1 = min(n, e0 + per);
+      const float thr_v = key_value(thr);
+      auto is_a = [&](uint32_t k) {
+        if (RANDOM) return all_ties ? k >= thr : k > thr;
+        return all_ties ? __uint_as_float(k) >= thr_v : __uint_as_float(k) > thr_v;
+      };
+      auto is_t = [&](uint32_t k) { return RANDOM ? k == thr : __uint_as_float(k) == thr_v; };
+      uint32_t ca = 0u, ct = 0u;
+      for (uint32_t e = e0; e < e1; ++e) {
+        const uint32_t k = sm.lkey[e];
+        ca += is_a(k) ? 1u : 0u;
+        ct += (!all_ties && is_t(k)) ? 1u : 0u;
+      }
+      const uint32_t packed = ca | (ct << 16);   // both at most kListMax
+      const uint32_t incl = wave_inclusive_sum(packed);
+      if (lane == 63) sm.cnt_l[wave] = incl;
+      __syncthreads();
+      uint32_t below = incl - packed;
+      for (int w = 0; w < wave; ++w) below += sm.cnt_l[w];
+      uint32_t ra = below & 0xFFFFu, re = below >> 16;
+      for (uint32_t e = e0; e < e1; ++e) {
+        const uint32_t k = sm.lkey[e];
+        uint32_t o = 0xFFFFFFFFu;
+        if (is_a(k)) {
+          o = static_cast<uint32_t>(P) + ra + min(re, need);
+          ++ra;
+        } else if (!all_ties && is_t(k)) {
+          if (re < need) o = static_cast<uint32_t>(P) + ra + re;
+          ++re;
+        }
+        if (o < static_cast<uint32_t>(p.b_cap)) hd.out[o] = static_cast<int32_t>(sm.lslot[e]);
+      }
+      continue;
     }
 
     // ---- placement. A: kept outright (above the threshold, or equal to it when every tie is
@@ -706,6 +931,11 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   __shared__ uint32_t cnt_e[NW];
   __shared__ uint32_t found[3];
   __shared__ uint32_t n_members;
+  __shared__ uint32_t shist[kSampleBins];
+  __shared__ __align__(16) uint32_t mlist[kValueBins];
+  __shared__ uint32_t cnt_l[NW];
+  __shared__ uint32_t lkey[list_cap<NT, KPT>()];
+  __shared__ uint32_t lslot[list_cap<NT, KPT>()];
   SelectSmem sm;   // filled field by field: an aggregate initialiser of LDS addresses is not
                    // accepted by the unoptimised device build
   sm.hist = hist;
@@ -715,6 +945,12 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   sm.cnt_e = cnt_e;
   sm.found = found;
   sm.n_members = &n_members;
+  sm.shist = shist;
+  sm.mlist = mlist;
+  sm.cnt_l = cnt_l;
+  sm.lkey = lkey;
+  sm.lslot = lslot;
+  sm.list_cap = list_cap<NT, KPT>();
 
   const int tid = threadIdx.x;
   SelectHead hd;
@@ -754,8 +990,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   else select_rounds<NT, KPT, KIND>(p, sm, hd);
 }
 
-// Caches past the register tiers (top-k and random past 32768 slots, the union past 65536;
-// context lengths reach 128K tokens): the same rankings, threshold rule and ordered scan, with every step recomputing
+// Caches past the register tiers (past 32768 slots; context lengths reach 128K tokens): the same rankings, threshold rule and ordered scan, with every step recomputing
 // the keys from memory (a score load, or the Philox draw) instead of keeping them in registers.
 // Steps: min/max (scores) and the 1024-bin histogram, the threshold bin's keys ranked in LDS (or,
 // when crowded, OR/AND and 8-bit radix passes), then the ordered scan in chunks of 4 * NT slots

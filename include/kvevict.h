@@ -403,7 +403,7 @@ kv_status kv_audit_kept(const kv_shape *shape, const kv_policy *policy, const in
  *  scores       device [L,S,H,t_cap] fp32 combined score.
  *  group        1 <= group <= 64.
  *  kept, b_cap, n_kept as for kv_select_topk. Requires t_cap <= 2^18; past
- *  65536 slots the kernel re-reads the scores at every pass and holds the
+ *  32768 slots the kernel re-reads the scores at every pass and holds the
  *  union as a bit per slot in LDS (t_cap / 8 bytes).
  */
 kv_status kv_select_union(const kv_shape *shape, const kv_policy *policy, int32_t group,
