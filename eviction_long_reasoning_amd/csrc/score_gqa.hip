@@ -150,18 +150,32 @@ __global__ __launch_bounds__(kScoreThreads, PPQ <= 4 ? 2 : 1) void score_gqa_ker
   };
 
   // Tiles in flight: tile t + AHEAD loads while tile t is computed. The buffers shift down one
-  // slot per tile; fully unrolled (contiguous slots), the shifts are register renames. Explicit
-  // positions make the tile body too large to unroll, so that path keeps one tile ahead.
-  constexpr int AHEAD = (POS || PPQ > 4) ? 1 : 3;
+  // slot per tile; fully unrolled, the shifts are register renames. With explicit positions each
+  // tile's phases are derived during the tile before it, from a position loaded two tiles ahead
+  // (one ahead from four pieces per lane on, where the registers would cost a wave per SIMD).
+  // The VALU and the matrix cores do not run at the same time on this part (the SQ counter of
+  // cycles with both busy reads 0), so this gains only what the smaller live range saves.
+  constexpr int AHEAD = POS ? (PPQ <= 2 ? 2 : 1) : (PPQ > 4 ? 1 : 3);
   uint4 buf[AHEAD + 1][PPQ];
-  int32_t pbuf[AHEAD + 1];
+  int32_t pbuf[AHEAD + 1] = {};   // a tile past the wave's last one keeps position 0 (its phases go unused)
 #pragma unroll
   for (int a = 0; a < AHEAD; ++a)
     if (wave_first + a * kTile < T) load_tile(wave_first + a * kTile, buf[a], pbuf[a]);
 
-  // one tile: y on the VALU, the contraction on the matrix cores
-  auto tile_scores = [&](const uint4 (&cur)[PPQ], int32_t pcur) -> v4f {
-    if (POS) {
+  // Explicit positions, two tiles ahead: the first tile's phases here; each later tile's are
+  // derived during the tile before it (tile_scores' pnext), after that tile's products are issued.
+  // One tile ahead, each tile derives its own phases first (its position has had longest to arrive).
+  constexpr bool PIPE = POS && AHEAD == 2;
+  if (PIPE && wave_first < T) {
+    const double m = tq - static_cast<double>(pbuf[0]);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) z[n] = cis_rev(rev[n], m);
+  }
+
+  // one tile: y on the VALU, the contraction on the matrix cores; then the next tile's phases
+  // (explicit positions two tiles ahead: from pnext) or the fixed rotation to the next tile
+  auto tile_scores = [&](const uint4 (&cur)[PPQ], int32_t pcur, int32_t pnext) -> v4f {
+    if (POS && !PIPE) {
       const double m = tq - static_cast<double>(pcur);
 #pragma unroll
       for (int n = 0; n < NB; ++n) z[n] = cis_rev(rev[n], m);
@@ -185,7 +199,11 @@ __global__ __launch_bounds__(kScoreThreads, PPQ <= 4 ? 2 : 1) void score_gqa_ker
         }
       }
     }
-    if (!POS) {
+    if (PIPE) {
+      const double m = tq - static_cast<double>(pnext);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) z[n] = cis_rev(rev[n], m);
+    } else if (!POS) {
 #pragma unroll
       for (int n = 0; n < NB; ++n) z[n] = cmul(z[n], w[n]);
     }
@@ -219,7 +237,7 @@ __global__ __launch_bounds__(kScoreThreads, PPQ <= 4 ? 2 : 1) void score_gqa_ker
       uint4 cur[PPQ];
       int32_t pcur;
       next_tile(t, j0, cur, pcur);
-      const v4f acc = tile_scores(cur, pcur);
+      const v4f acc = tile_scores(cur, pcur, pbuf[0]);
       const v4u32 bits = {__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
                           __float_as_uint(acc[3])};
       __builtin_amdgcn_raw_buffer_store_b128(bits, rr, row_off + (j0 + 4 * q) * 4, 0, 2);
@@ -237,7 +255,7 @@ __global__ __launch_bounds__(kScoreThreads, PPQ <= 4 ? 2 : 1) void score_gqa_ker
       uint4 cur[PPQ];
       int32_t pcur;
       next_tile(t, j0, cur, pcur);
-      const v4f acc = tile_scores(cur, pcur);
+      const v4f acc = tile_scores(cur, pcur, pbuf[0]);
       const int jk = j0 + 4 * q;
       if (row < G) {
         float *dst = raw_head + static_cast<size_t>(row) * p.t_cap + jk;
