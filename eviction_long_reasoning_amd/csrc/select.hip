@@ -329,6 +329,13 @@ __device__ __forceinline__ uint32_t bin_clamped(float v, float scale, float off,
   return static_cast<uint32_t>(x);
 }
 
+// bin_clamped over order keys (the patterns below -inf go to bin 0, those from +inf up to the last).
+__device__ __forceinline__ uint32_t bin_of_key_n(uint32_t k, float scale, float off, int nbins) {
+  if (k <= kKeyNegInf) return 0u;
+  if (k >= kKeyPosInf) return static_cast<uint32_t>(nbins - 1);
+  return bin_clamped(key_value(k), scale, off, nbins);
+}
+
 // Run by every wave on its own (no barrier): with lane L owning bins PER*L ... PER*L + PER - 1 of
 // an LDS histogram, the bin where the count from the top first reaches want_of(total) (0 when the
 // total stays below it) and the count in the bins above it, both wave-uniform.
@@ -692,8 +699,9 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
         n_list = total;
         return true;
       };
-      // above half the candidates the placement must visit every key anyway: no list
-      if (binned && 2 * p_sel <= n_valid) listed = try_list();
+      // above half the candidates the placement must visit every key anyway, and a selection
+      // that leaves the list no room for the cut's margin cannot fit: no list
+      if (binned && 2 * p_sel <= n_valid && p_sel + p_sel / 8 + 64 <= sm.list_cap) listed = try_list();
       if (!listed) {
       __syncthreads();   // the previous pass's readers of hist are done
       // valid: the key takes part (scores: not the NaN mark; random: the slot range)
@@ -997,6 +1005,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
 // in slot order with the kept and tied counts carried from chunk to chunk. The union (KIND 2)
 // runs G + 1 such passes and keeps its union as a bit per slot in dynamic LDS (t_cap / 8 bytes).
 constexpr int kStreamThreads = 1024;
+constexpr int kStreamSamples = 4096;   // strided sample of the candidates for the listed path's cut
 static_assert(kSelectMaxSlotsUnion / 8 <= 32 * 1024, "union bits fit in 32 KB of LDS");
 
 template <int KIND>
@@ -1011,6 +1020,12 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
   __shared__ uint32_t n_members;
   __shared__ uint32_t kb[2];   // key interval of the threshold's bin
   extern __shared__ uint32_t ubits[];   // union: bit j set when slot j is in some head's top-k
+  // the listed path (top-k and random): keys and slots of the candidates at or above the cut
+  constexpr int LCAP = UNION ? 1 : kListMax;
+  __shared__ uint32_t lkey[LCAP];
+  __shared__ uint32_t lslot[LCAP];
+  __shared__ __align__(16) uint32_t mlist[UNION ? 4 : kValueBins];
+  __shared__ uint32_t shist[UNION ? 1 : kSampleBins];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -1085,6 +1100,8 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
     int mode;
     uint32_t thr = 0u, need = 0u;
     bool all_ties = false;  // every key equal to thr is taken
+    bool listed = false;    // the threshold came from the list, which is still in LDS
+    uint32_t n_list = 0u;
     if (p_sel <= 0 || n_cand <= 0) {
       mode = 0;
     } else if (p_sel >= n_cand) {
@@ -1096,8 +1113,14 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
       // or every candidate when the scores have no usable value range
       bool binned = RANDOM, ranked = false;
       uint32_t bsel = 0u, klo = 0u, khi = 0xFFFFFFFFu;   // key interval of the threshold's bin
-      float scale = 0.f, off = 0.f;
+      float scale = 0.f, off = 0.f, fmin = 0.f, fmax = 0.f;
       auto bin_of = [&](uint32_t k) { return RANDOM ? (k >> 22) : bin_of_key(k, scale, off); };
+      if (!UNION) {   // the listed path's LDS starts cleared (ordered before use by the barriers below)
+        for (int i = tid; i < kValueBins; i += NT) mlist[i] = 0u;
+        for (int i = tid; i < kSampleBins; i += NT) shist[i] = 0u;
+        for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
+        if (tid == 0) n_members = 0u;
+      }
       if (!RANDOM) {
         uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
         for (int j = e_lo + tid; j < e_hi; j += NT) {
@@ -1108,11 +1131,119 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
           }
         }
         block_min_max<NT>(kmn, kmx, red);
-        const float fmin = key_value(kmn), fmax = key_value(kmx);
+        fmin = key_value(kmn);
+        fmax = key_value(kmx);
         scale = static_cast<float>(kValueBins) / (fmax - fmin);
         off = -fmin * scale;
         binned = kmn < kmx && scale > 0.f && scale < 3.0e38f && fabsf(off) < 3.0e38f;
       }
+
+      // ---- listed path: a cut from a strided sample (scores) or the selection's share (random
+      // words); one sweep counts the candidates at or above it and lists them in LDS in slot order
+      // (chunks of 4 * NT slots, a block-wide scan each); the threshold is then found on the list
+      // as in the register kernel. A cut that leaves fewer than p_sel or more than the list holds,
+      // or a crowded threshold bin, falls back to the sweeps below.
+      auto stream_list = [&]() -> bool {
+        uint32_t cut = 1u;   // list keys >= cut (order keys, or words)
+        float lo_f = fmin;
+        if (RANDOM) {
+          const float want = static_cast<float>(p_sel) + 4.f * sqrtf(static_cast<float>(p_sel)) + 16.f;
+          if (want < static_cast<float>(n_cand)) {
+            const double c = 4294967296.0 * (1.0 - static_cast<double>(want) / static_cast<double>(n_cand));
+            cut = c > 1.0 ? static_cast<uint32_t>(c) : 1u;
+          }
+        } else {
+          const float sscale = static_cast<float>(kSampleBins) / (fmax - fmin), soff = -fmin * sscale;
+          const int ns = min(n_cand, kStreamSamples);
+          for (int i = tid; i < ns; i += NT) {
+            const int j = e_lo + static_cast<int>((static_cast<long long>(i) * n_cand) / ns);
+            atomicAdd(&shist[bin_of_key_n(key_of(j), sscale, soff, kSampleBins)], 1u);
+          }
+          __syncthreads();
+          uint32_t bc, above_s, n_s;
+          wave_find_bin<kSampleBins>(shist, [&](uint32_t tot) {
+            const float lam = static_cast<float>(p_sel) * static_cast<float>(tot) / static_cast<float>(n_cand);
+            return static_cast<uint32_t>(lam + 3.f * sqrtf(lam) + 4.f);
+          }, lane, bc, above_s, n_s);
+          cut = 0u;
+          if (bc > 1u) {
+            lo_f = (static_cast<float>(bc - 1u) - soff) / sscale;
+            cut = order_key(lo_f);
+          }
+        }
+        uint32_t carry = 0u;
+        for (int c = e_lo; c < e_hi; c += 4 * NT) {
+          const int j0 = c + 4 * tid;
+          uint32_t kk[4];
+          uint32_t f = 0u;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            kk[q] = 0u;
+            if (j0 + q < e_hi) {
+              kk[q] = key_of(j0 + q);
+              f |= static_cast<uint32_t>(kk[q] >= cut) << q;
+            }
+          }
+          const uint32_t cnt = static_cast<uint32_t>(__popc(f));
+          const uint32_t x = wave_inclusive_sum(cnt);
+          if (lane == 63) wsum[wave] = x;
+          __syncthreads();
+          uint32_t at = carry + x - cnt, tot = 0u;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            if (w < wave) at += wsum[w];
+            tot += wsum[w];
+          }
+          __syncthreads();   // wsum is rewritten by the next chunk
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if ((f >> q) & 1u) {
+              if (at < static_cast<uint32_t>(LCAP)) {
+                lkey[at] = kk[q];
+                lslot[at] = static_cast<uint32_t>(j0 + q);
+              }
+              ++at;
+            }
+          }
+          carry += tot;
+        }
+        __syncthreads();   // the last chunk's list entries are written before anyone reads the list
+        if (carry < static_cast<uint32_t>(p_sel) || carry > static_cast<uint32_t>(LCAP)) return false;
+        const float scale2 = static_cast<float>(kListBins) / (fmax - lo_f), off2 = -lo_f * scale2;
+        if (!RANDOM && !(fmax > lo_f && scale2 > 0.f && scale2 < 3.0e38f && fabsf(off2) < 3.0e38f)) return false;
+        const uint32_t span = 0xFFFFFFFFu - cut;
+        const int bits = span ? 32 - __clz(span) : 0;
+        const int shift = bits > 8 ? bits - 8 : 0;
+        auto lbin = [&](uint32_t k) {
+          return RANDOM ? (k - cut) >> shift : bin_of_key_n(k, scale2, off2, kListBins);
+        };
+        for (uint32_t e = tid; e < carry; e += NT) atomicAdd(&hist[lbin(lkey[e])], 1u);
+        __syncthreads();
+        uint32_t b, above, tot;
+        wave_find_bin<kListBins>(hist, [&](uint32_t) { return static_cast<uint32_t>(p_sel); }, lane, b, above, tot);
+        const uint32_t rem = static_cast<uint32_t>(p_sel) - above;
+        for (uint32_t e = tid; e < carry; e += NT) {
+          const uint32_t k = lkey[e];
+          if (lbin(k) == b) {
+            const uint32_t at = atomicAdd(&n_members, 1u);
+            if (at < member_cap<NT>()) mlist[at] = k;
+          }
+        }
+        __syncthreads();
+        const uint32_t m = n_members;
+        if (m > member_cap<NT>()) return false;
+        rank_members<NT>(mlist, m, rem, found);   // entries past m are still zero
+        __syncthreads();
+        thr = found[0];
+        need = found[1];
+        all_ties = found[2] == need;
+        n_list = carry;
+        return true;
+      };
+      if (!UNION && (RANDOM || binned) && 2 * p_sel <= n_cand && p_sel + p_sel / 8 + 64 <= LCAP)
+        listed = stream_list();
+      if (!listed) {
+      __syncthreads();   // the listed path's readers of hist are done
       if (binned) {
         for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
         if (tid == 0) n_members = 0u;
@@ -1189,6 +1320,44 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
         }
         need = remaining;
       }
+      }
+    }
+
+    // ---- placement from the list (top-k and random): the pins arithmetically, the selected slots
+    // by one block-wide scan over contiguous runs of list entries (as in the register kernel)
+    if (!UNION && listed) {
+      for (int r = tid; r < P; r += NT) out[r] = r;
+      for (int r = tid; r < Rw; r += NT) out[P + n_sel + r] = e_hi + r;
+      const uint32_t n = n_list;
+      const uint32_t per = (n + NT - 1) / NT;
+      const uint32_t e0 = min(n, static_cast<uint32_t>(tid) * per), e1 = min(n, e0 + per);
+      auto is_a = [&](uint32_t k) { return all_ties ? k >= thr : k > thr; };
+      uint32_t ca = 0u, ct = 0u;
+      for (uint32_t e = e0; e < e1; ++e) {
+        const uint32_t k = lkey[e];
+        ca += is_a(k) ? 1u : 0u;
+        ct += (!all_ties && k == thr) ? 1u : 0u;
+      }
+      const uint32_t packed = ca | (ct << 16);   // both at most kListMax
+      const uint32_t incl = wave_inclusive_sum(packed);
+      if (lane == 63) wsum[wave] = incl;
+      __syncthreads();
+      uint32_t below = incl - packed;
+      for (int w = 0; w < wave; ++w) below += wsum[w];
+      uint32_t ra = below & 0xFFFFu, re = below >> 16;
+      for (uint32_t e = e0; e < e1; ++e) {
+        const uint32_t k = lkey[e];
+        uint32_t o = 0xFFFFFFFFu;
+        if (is_a(k)) {
+          o = static_cast<uint32_t>(P) + ra + min(re, need);
+          ++ra;
+        } else if (!all_ties && k == thr) {
+          if (re < need) o = static_cast<uint32_t>(P) + ra + re;
+          ++re;
+        }
+        if (o < static_cast<uint32_t>(p.b_cap)) out[o] = static_cast<int32_t>(lslot[e]);
+      }
+      continue;
     }
 
     if (UNION && !last && (mode != 2 || all_ties)) {

@@ -50,7 +50,7 @@ def _row(pattern: str, r, t_cap: int, T: int, P: int, B: int, R: int) -> np.ndar
     elif pattern == "signed-zeros":   # +0 and -0 tie at the threshold: positives fall just short
         x = -np.abs(x) - np.float32(0.01)
         n_pos = int((share - 0.01) * t_cap)
-        idx = r.choice(t_cap, n_pos + t_cap // 60, replace=False)
+        idx = r.choice(t_cap, n_pos + min(t_cap // 60, 600), replace=False)
         x[idx[:n_pos]] = -x[idx[:n_pos]]
         zeros = idx[n_pos:]
         x[zeros] = np.where(r.random(zeros.size) < 0.5, np.float32(0.0), np.float32(-0.0))
@@ -62,6 +62,10 @@ def _row(pattern: str, r, t_cap: int, T: int, P: int, B: int, R: int) -> np.ndar
     elif pattern == "sample-high":    # the sampled rounds score far above the rest: the cut is too high
         rounds = _round_of(t_cap)
         x += np.where((rounds == 8) | (rounds == 24), np.float32(100.0), np.float32(0.0))
+    elif pattern == "stream-sample-high":   # past the register tiers the sample is 4096 evenly spaced
+        n_cand = part.e_hi - part.e_lo      # candidates: raise exactly those
+        ns = min(n_cand, 4096)
+        x[part.e_lo + (np.arange(ns, dtype=np.int64) * n_cand) // ns] += np.float32(100.0)
     return x
 
 
@@ -98,6 +102,16 @@ CASES = [
     ("tier-4096-over-cap", 4096, [4096], [64], 1700, 16, "normal"),
     ("tier-8192", 8192, [8192, 5000], [256, 3], 1500, 32, "signed-zeros"),
     ("tier-16384", 16384, [16384], [2048], 4000, 128, "trend"),
+    # past 32768 slots: the re-reading kernel's listed path (count and list in one sweep)
+    ("stream-40k", 40000, [40000, 33001], [1024, 0], 3072, 128, "normal"),
+    ("stream-131k-trend", 131072, [131072], [2048], 4096, 128, "trend"),
+    ("stream-70k-ties-straddle", 70000, [70000, 50000], [512, 0], 3072, 64, "ties-straddle"),
+    ("stream-70k-signed-zeros", 70000, [70000], [1000], 3072, 128, "signed-zeros"),
+    ("stream-70k-infinities", 70000, [70000], [256], 2048, 64, "infinities"),
+    ("stream-70k-tie-block", 70000, [70000], [1024], 3072, 128, "tie-block-over-cap"),
+    ("stream-70k-crowded-bin", 70000, [70000], [512], 2500, 100, "crowded-bin"),
+    ("stream-70k-sample-high", 70000, [70000], [1024], 3072, 128, "stream-sample-high"),
+    ("stream-70k-budget-past-list", 70000, [70000], [0], 8000, 64, "normal"),
 ]
 
 
@@ -127,6 +141,9 @@ RANDOM_CASES = [
     ("random-over-half", 8192, [8192], [0], 4065 + 64, 64),
     ("random-empty-sample", 32768, [32768], [30720], 32356, 1536),
     ("random-tier-2048", 2048, [2048, 700], [100, 0], 400, 16),
+    ("random-stream-70k", 70000, [70000, 40000], [1024, 0], 3072, 128),
+    ("random-stream-131k-small-share", 131072, [131072], [0], 64, 16),
+    ("random-stream-70k-budget-past-list", 70000, [70000], [0], 8000, 64),
 ]
 
 
