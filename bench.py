@@ -213,20 +213,21 @@ def other_workloads(args, dev):
                  Ko=torch.empty((L, S, H, w.out_cap, w.head_dim), dtype=K.dtype, device=dev),
                  Po=torch.empty((L, S, H, w.out_cap), dtype=torch.int32, device=dev))
         c["Vo"] = torch.empty_like(c["Ko"])
+        c["ws"] = torch.empty((kv.select_workspace_bytes(L, S, H, w.t_cap, w.b_cap()),), dtype=torch.uint8, device=dev)
         return c
 
     def scored(c):
         w = c["w"]
         kv.tri_score(c["K"], c["qb"], c["tcur"], c["seq"], w.theta, w.deltas, out=c["scores"])
         kv.kv_select_topk(c["scores"], c["seq"], c["plen"], w.budget, w.recent, w.prompt_cap(), b_cap=w.b_cap(),
-                          kept=c["kept"], n_kept=c["nk"])
+                          kept=c["kept"], n_kept=c["nk"], workspace=c["ws"])
         kv.kv_compact(c["K"], c["V"], c["kept"], c["nk"], c["seq"], w.out_cap, K_out=c["Ko"], V_out=c["Vo"],
                       pos_out=c["Po"])
 
     def random(c):
         w = c["w"]
         kv.kv_select_random(tuple(c["scores"].shape), c["seq"], c["plen"], w.budget, w.recent, w.prompt_cap(),
-                            w.seed_random, 0, b_cap=w.b_cap(), kept=c["kept"], n_kept=c["nk"])
+                            w.seed_random, 0, b_cap=w.b_cap(), kept=c["kept"], n_kept=c["nk"], workspace=c["ws"])
         kv.kv_compact(c["K"], c["V"], c["kept"], c["nk"], c["seq"], w.out_cap, K_out=c["Ko"], V_out=c["Vo"],
                       pos_out=c["Po"])
 

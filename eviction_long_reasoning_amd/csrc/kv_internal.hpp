@@ -90,7 +90,13 @@ struct SelectParams {
   const float *head_scores; // union: [L,S,H,G,t_cap] per-query-head scores (scores = combined)
   int32_t G, k_per_head;    // union: query heads per KV head; per-head top-k (<= 0: ceil(n_sel / G))
   void *scratch;            // caller workspace past its header (select_scratch_bytes), or nullptr
+  // split listing (few heads): chunk workgroups list each chunk's keys above the cut into scratch
+  int32_t split_chunks;     // chunks per head (0: no split)
+  int32_t split_list_cap;   // list capacity of the ranking workgroup's tier
+  uint32_t *split_count;    // [heads, split_chunks] listed keys per chunk
+  uint32_t *split_list;     // [heads, split_chunks, kSplitChunk, 2] (key bits, slot) per listed key
 };
+constexpr int kSplitChunk = 2048;   // slots per chunk workgroup (256 threads x 8)
 
 // Scratch bytes the top-k / random selectors need past the workspace header for L*S*H heads of
 // t_cap slots.

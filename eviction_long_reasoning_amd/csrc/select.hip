@@ -317,6 +317,7 @@ constexpr uint32_t member_cap() { return 2 * NT < kValueBins - 4 ? 2 * NT : kVal
 constexpr int kSampleBins = 256;
 constexpr int kListBins = 256;
 constexpr int kListMax = 6144;
+constexpr int kStreamSamples = 4096;   // evenly spaced candidates sampled for a cut when the keys are not in registers
 // A quarter of the tier's slots: selections above half the candidates never list, and a small
 // list keeps the 256-thread tiers' LDS (and so their workgroups per CU) close to the histogram's.
 template <int NT, int KPT>
@@ -438,6 +439,104 @@ struct SelectHead {
   int P, e_lo, e_hi, n_sel, n_cand;
   int32_t *out;
 };
+
+// The listed path's cut for Philox words: the p_sel-th largest of n_valid uniform words sits near
+// 2^32 (1 - p_sel / n_valid); the cut leaves about four standard deviations more. At least 1, so
+// a slot that takes no part (word 0) is never listed.
+__device__ __forceinline__ uint32_t random_cut(int p_sel, int n_valid) {
+  const float want = static_cast<float>(p_sel) + 4.f * sqrtf(static_cast<float>(p_sel)) + 16.f;
+  if (!(want < static_cast<float>(n_valid))) return 1u;
+  const double c = 4294967296.0 * (1.0 - static_cast<double>(want) / static_cast<double>(n_valid));
+  return c > 1.0 ? static_cast<uint32_t>(c) : 1u;
+}
+
+// Whether a head's selection takes the listed path: at most half the candidates (above that the
+// placement visits every key anyway), and room in a list of list_cap for the cut's margin.
+__device__ __forceinline__ bool listable(int p_sel, int n_valid, int list_cap) {
+  return p_sel > 0 && p_sel < n_valid && 2 * p_sel <= n_valid && p_sel + p_sel / 8 + 64 <= list_cap;
+}
+
+// The threshold over a list of `total` keys in sm.lkey (scores as fp32 bits between lo and hi,
+// random words at or above cut_k): a kListBins histogram (sm.hist, which must be zero), the bin
+// of the p_sel-th largest found by every wave, its members (sm.mlist, zero beyond any earlier
+// member list; *sm.n_members zero) ranked directly. False, with nothing decided, when the score
+// range is unusable or the bin is too crowded to rank; the caller then takes the full path.
+template <int NT, bool RANDOM>
+__device__ __forceinline__ bool list_threshold(const SelectSmem &sm, uint32_t total, uint32_t p_sel, float lo, float hi,
+                               uint32_t cut_k, uint32_t &thr, uint32_t &need, bool &all_ties) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const float scale2 = static_cast<float>(kListBins) / (hi - lo), off2 = -lo * scale2;
+  if (!RANDOM && !(hi > lo && scale2 > 0.f && scale2 < 3.0e38f && fabsf(off2) < 3.0e38f)) return false;
+  const uint32_t span = 0xFFFFFFFFu - cut_k;
+  const int bits = span ? 32 - __clz(span) : 0;
+  const int shift = bits > 8 ? bits - 8 : 0;
+  auto lbin = [&](uint32_t k) {
+    return RANDOM ? (k - cut_k) >> shift : bin_clamped(__uint_as_float(k), scale2, off2, kListBins);
+  };
+  for (uint32_t e = tid; e < total; e += NT) atomicAdd(&sm.hist[lbin(sm.lkey[e])], 1u);
+  __syncthreads();
+  uint32_t b, above, tot;
+  wave_find_bin<kListBins>(sm.hist, [&](uint32_t) { return p_sel; }, lane, b, above, tot);
+  const uint32_t rem = p_sel - above;
+  for (uint32_t e = tid; e < total; e += NT) {
+    const uint32_t k = sm.lkey[e];
+    if (lbin(k) == b) {
+      const uint32_t at = atomicAdd(sm.n_members, 1u);
+      if (at < member_cap<NT>()) sm.mlist[at] = RANDOM ? k : order_key(__uint_as_float(k));
+    }
+  }
+  __syncthreads();
+  const uint32_t m = *sm.n_members;
+  if (m > member_cap<NT>()) return false;
+  rank_members<NT>(sm.mlist, m, rem, sm.found);   // entries past m are still zero
+  __syncthreads();
+  thr = sm.found[0];
+  need = sm.found[1];
+  all_ties = sm.found[2] == need;
+  return true;
+}
+
+// Placement from a list in slot order: thread t takes a contiguous run of list entries, so one
+// block-wide scan of its (kept outright, tied) counts orders every output. Scores compare as fp32
+// against the threshold's value (-0 equals +0, as for order keys).
+template <int NT, bool RANDOM>
+__device__ __forceinline__ void list_place(const SelectSmem &sm, uint32_t n, uint32_t thr, uint32_t need, bool all_ties, int P,
+                           int32_t *out, int b_cap) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t per = (n + NT - 1) / NT;
+  const uint32_t e0 = min(n, static_cast<uint32_t>(tid) * per), e1 = min(n, e0 + per);
+  const float thr_v = key_value(thr);
+  auto is_a = [&](uint32_t k) {
+    if (RANDOM) return all_ties ? k >= thr : k > thr;
+    return all_ties ? __uint_as_float(k) >= thr_v : __uint_as_float(k) > thr_v;
+  };
+  auto is_t = [&](uint32_t k) { return RANDOM ? k == thr : __uint_as_float(k) == thr_v; };
+  uint32_t ca = 0u, ct = 0u;
+  for (uint32_t e = e0; e < e1; ++e) {
+    const uint32_t k = sm.lkey[e];
+    ca += is_a(k) ? 1u : 0u;
+    ct += (!all_ties && is_t(k)) ? 1u : 0u;
+  }
+  const uint32_t packed = ca | (ct << 16);   // both at most kListMax
+  const uint32_t incl = wave_inclusive_sum(packed);
+  if (lane == 63) sm.cnt_l[wave] = incl;
+  __syncthreads();
+  uint32_t below = incl - packed;
+  for (int w = 0; w < wave; ++w) below += sm.cnt_l[w];
+  uint32_t ra = below & 0xFFFFu, re = below >> 16;
+  for (uint32_t e = e0; e < e1; ++e) {
+    const uint32_t k = sm.lkey[e];
+    uint32_t o = 0xFFFFFFFFu;
+    if (is_a(k)) {
+      o = static_cast<uint32_t>(P) + ra + min(re, need);
+      ++ra;
+    } else if (!all_ties && is_t(k)) {
+      if (re < need) o = static_cast<uint32_t>(P) + ra + re;
+      ++re;
+    }
+    if (o < static_cast<uint32_t>(b_cap)) out[o] = static_cast<int32_t>(sm.lslot[e]);
+  }
+}
 
 // The smallest key whose bin is at least `target` (2^32 when none is), run by one wave. The bin
 // boundary sits near the value (target - off) / scale; one probe of the 64 keys around that
@@ -612,13 +711,7 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
         float cut_f = -INFINITY;   // scores: list x >= cut_f (NaN marks never pass)
         uint32_t cut_k = 1u;       // random: list words >= cut_k (slots that take no part hold 0)
         if (RANDOM) {
-          // the p_sel-th largest of n_valid uniform words sits near 2^32 (1 - p_sel / n_valid); the
-          // cut leaves about four standard deviations more
-          const float want = static_cast<float>(p_sel) + 4.f * sqrtf(static_cast<float>(p_sel)) + 16.f;
-          if (want < static_cast<float>(n_valid)) {
-            const double c = 4294967296.0 * (1.0 - static_cast<double>(want) / static_cast<double>(n_valid));
-            cut_k = c > 1.0 ? static_cast<uint32_t>(c) : 1u;
-          }
+          cut_k = random_cut(p_sel, n_valid);
         } else {
           // two keys per thread (rounds R/4 and 3R/4: two blocks of 64 consecutive slots per wave,
           // spread evenly over the head) into kSampleBins value bins; the cut is one bin below where
@@ -653,14 +746,7 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
         // bins over the listed range: scores by value between the cut (or the smallest finite key)
         // and the largest; random words by their offset above the cut
         const float lo = cut_f > -INFINITY ? cut_f : mn;
-        const float scale2 = static_cast<float>(kListBins) / (mx - lo), off2 = -lo * scale2;
-        if (!RANDOM && !(mx > lo && scale2 > 0.f && scale2 < 3.0e38f && fabsf(off2) < 3.0e38f)) return false;
-        const uint32_t span = 0xFFFFFFFFu - cut_k;
-        const int bits = span ? 32 - __clz(span) : 0;
-        const int shift = bits > 8 ? bits - 8 : 0;
-        auto lbin = [&](uint32_t k) {
-          return RANDOM ? (k - cut_k) >> shift : bin_clamped(__uint_as_float(k), scale2, off2, kListBins);
-        };
+        if (!RANDOM && !(mx > lo)) return false;
         {
           const int j0 = slot_base();
 #pragma unroll
@@ -676,32 +762,12 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
           }
         }
         __syncthreads();
-        for (uint32_t e = tid; e < total; e += NT) atomicAdd(&hist[lbin(sm.lkey[e])], 1u);
-        __syncthreads();
-        uint32_t b, above, tot;
-        wave_find_bin<kListBins>(hist, [&](uint32_t) { return static_cast<uint32_t>(p_sel); }, lane, b, above, tot);
-        const uint32_t rem = static_cast<uint32_t>(p_sel) - above;
-        for (uint32_t e = tid; e < total; e += NT) {
-          const uint32_t k = sm.lkey[e];
-          if (lbin(k) == b) {
-            const uint32_t at = atomicAdd(sm.n_members, 1u);
-            if (at < member_cap<NT>()) sm.mlist[at] = RANDOM ? k : order_key(__uint_as_float(k));
-          }
-        }
-        __syncthreads();
-        const uint32_t m = *sm.n_members;
-        if (m > member_cap<NT>()) return false;
-        rank_members<NT>(sm.mlist, m, rem, found);   // entries past m are still zero
-        __syncthreads();
-        thr = found[0];
-        need = found[1];
-        all_ties = found[2] == need;
+        if (!list_threshold<NT, RANDOM>(sm, total, static_cast<uint32_t>(p_sel), lo, mx, cut_k, thr, need, all_ties))
+          return false;
         n_list = total;
         return true;
       };
-      // above half the candidates the placement must visit every key anyway, and a selection
-      // that leaves the list no room for the cut's margin cannot fit: no list
-      if (binned && 2 * p_sel <= n_valid && p_sel + p_sel / 8 + 64 <= sm.list_cap) listed = try_list();
+      if (binned && listable(p_sel, n_valid, sm.list_cap)) listed = try_list();
       if (!listed) {
       __syncthreads();   // the previous pass's readers of hist are done
       // valid: the key takes part (scores: not the NaN mark; random: the slot range)
@@ -810,44 +876,9 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
       }
     }
 
-    // ---- placement from the list (top-k and random): thread t takes a contiguous run of list
-    // entries, so one block-wide scan of its (kept outright, tied) counts orders every output.
-    // Scores compare as fp32 against the threshold's value (-0 equals +0, as for order keys).
+    // ---- placement from the list (top-k and random)
     if (!UNION && listed) {
-      const uint32_t n = n_list;
-      const uint32_t per = (n + NT - 1) / NT;
-      const uint32_t e0 = min(n, static_cast<uint32_t>(tid) * per), e1 = min(n, e0 + per);
-      const float thr_v = key_value(thr);
-      auto is_a = [&](uint32_t k) {
-        if (RANDOM) return all_ties ? k >= thr : k > thr;
-        return all_ties ? __uint_as_float(k) >= thr_v : __uint_as_float(k) > thr_v;
-      };
-      auto is_t = [&](uint32_t k) { return RANDOM ? k == thr : __uint_as_float(k) == thr_v; };
-      uint32_t ca = 0u, ct = 0u;
-      for (uint32_t e = e0; e < e1; ++e) {
-        const uint32_t k = sm.lkey[e];
-        ca += is_a(k) ? 1u : 0u;
-        ct += (!all_ties && is_t(k)) ? 1u : 0u;
-      }
-      const uint32_t packed = ca | (ct << 16);   // both at most kListMax
-      const uint32_t incl = wave_inclusive_sum(packed);
-      if (lane == 63) sm.cnt_l[wave] = incl;
-      __syncthreads();
-      uint32_t below = incl - packed;
-      for (int w = 0; w < wave; ++w) below += sm.cnt_l[w];
-      uint32_t ra = below & 0xFFFFu, re = below >> 16;
-      for (uint32_t e = e0; e < e1; ++e) {
-        const uint32_t k = sm.lkey[e];
-        uint32_t o = 0xFFFFFFFFu;
-        if (is_a(k)) {
-          o = static_cast<uint32_t>(P) + ra + min(re, need);
-          ++ra;
-        } else if (!all_ties && is_t(k)) {
-          if (re < need) o = static_cast<uint32_t>(P) + ra + re;
-          ++re;
-        }
-        if (o < static_cast<uint32_t>(p.b_cap)) hd.out[o] = static_cast<int32_t>(sm.lslot[e]);
-      }
+      list_place<NT, RANDOM>(sm, n_list, thr, need, all_ties, P, hd.out, p.b_cap);
       continue;
     }
 
@@ -926,6 +957,144 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
   }
 }
 
+// Split draw, for random selection over batches with few heads and long caches: split_chunks
+// workgroups per head each draw kSplitChunk consecutive candidates' Philox words, so the draw (the
+// bulk of the work) runs on many CUs instead of one. Every chunk workgroup takes the same cut (the
+// selection's share, as in the register kernel), lists its candidates at or above it in slot order
+// into the workspace and writes their count. The head's ranking workgroup (select_kernel) then
+// gathers the lists in chunk order, which is slot order, and ranks and places over them; when they
+// do not fit, or the threshold's bin is too crowded, it takes its full path over every key instead.
+// Top-k selection was measured without a gain from the same split (its chunk and ranking kernels
+// took 5.3 + 8.4 us against 12-13 us for one workgroup per head on 8 heads of 32768 slots: the
+// ranking workgroup's chain of dependent loads and barriers costs what the split saves), so it keeps
+// one workgroup per head.
+constexpr int kSplitThreads = 256;
+constexpr int kSplitMaxChunks = kSelectMaxSlots / kSplitChunk;   // 16
+
+__global__ __launch_bounds__(kSplitThreads) void select_split_kernel(const SelectParams p) {
+  constexpr int NT = kSplitThreads, NW = NT / 64, R = kSplitChunk / NT;
+  __shared__ uint32_t cnt[NW];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int chunk = blockIdx.x % p.split_chunks;
+  const int head = blockIdx.x / p.split_chunks;
+  const int h = head % p.H, s = (head / p.H) % p.S, l = head / (p.H * p.S);
+  const int T = __builtin_amdgcn_readfirstlane(min(max(p.seq_len[s], 0), p.t_cap));
+  const int P = __builtin_amdgcn_readfirstlane(min(max(p.prompt_len[s], 0), min(p.prompt_cap, T)));
+  const int B = p.budget;
+  uint32_t *count = p.split_count + static_cast<size_t>(head) * p.split_chunks + chunk;
+  const int Rw = min(p.recent, min(max(0, B - P), T - P));
+  const int e_lo = P, e_hi = T - Rw;
+  const int n_sel = max(0, B - P - Rw), n_cand = e_hi - e_lo;
+  const int c_lo = e_lo + chunk * kSplitChunk;
+  // heads the ranking workgroup does not list, and chunks past the evictable range, list nothing
+  if (T <= B || !listable(n_sel, n_cand, p.split_list_cap) || c_lo >= e_hi) {
+    if (tid == 0) *count = 0u;
+    return;
+  }
+  const size_t slot0 = static_cast<size_t>(head) * p.t_cap;
+  const uint32_t cut_k = random_cut(n_sel, n_cand);
+  // positions through a buffer resource ending at e_hi (a slot past it reads 0 without a memory
+  // access), so no load waits behind a branch
+  const __amdgpu_buffer_rsrc_t rp = rsrc_of(p.pos ? p.pos + slot0 : p.seq_len, p.pos ? e_hi * 4 : 0);
+  const uint32_t c1 = p.shared_draw ? 0u : (static_cast<uint32_t>(l + p.layer_base) << 16) | static_cast<uint32_t>(h);
+  // the chunk's candidates: wave w holds slots c_lo + w*64*R + 64i + lane in round i
+  const int jb = c_lo + wave * 64 * R + lane;
+  uint32_t key[R];
+  bool pass[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int j = jb + i * 64;
+    const uint32_t c0 = p.pos ? ld32(rp, j * 4, 0) : static_cast<uint32_t>(j);
+    key[i] = philox_word0(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
+    pass[i] = j < e_hi && key[i] >= cut_k;
+  }
+  uint32_t c = 0u;
+#pragma unroll
+  for (int i = 0; i < R; ++i) c += static_cast<uint32_t>(__popcll(__ballot(pass[i])));
+  if (lane == 0) cnt[wave] = c;
+  __syncthreads();
+  uint32_t base = 0u, total = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) base += cnt[w];
+    total += cnt[w];
+  }
+  uint32_t *lst = p.split_list + (static_cast<size_t>(head) * p.split_chunks + chunk) * (2 * kSplitChunk);
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const uint64_t b = __ballot(pass[i]);
+    if (pass[i]) {
+      const uint32_t at = base + lanes_below(b);
+      lst[2 * at] = key[i];
+      lst[2 * at + 1] = static_cast<uint32_t>(jb + i * 64);
+    }
+    base += static_cast<uint32_t>(__popcll(b));
+  }
+  if (tid == 0) *count = total;
+}
+
+// The ranking workgroup's side of the split draw: gather the head's chunk lists into LDS (chunk
+// order is slot order), then the threshold and the placement over the list. False, with the shared
+// state to be reset by the caller's full path, when the lists do not fit or cannot be ranked.
+template <int NT>
+__device__ __forceinline__ bool split_rank(const SelectParams &p, const SelectSmem &sm, const SelectHead &hd) {
+  const int tid = threadIdx.x;
+  const int C = p.split_chunks;   // at most kSplitMaxChunks = NT / 64 (one count per wave slot)
+  for (int i = tid; i < kValueBins; i += NT) {
+    sm.hist[i] = 0u;
+    sm.mlist[i] = 0u;
+  }
+  if (tid == 0) *sm.n_members = 0u;
+  if (tid < C) sm.cnt_l[tid] = p.split_count[static_cast<size_t>(hd.head) * C + tid];
+  __syncthreads();
+  uint32_t total = 0u;
+  for (int c = 0; c < C; ++c) total += sm.cnt_l[c];
+  const uint32_t p_sel = static_cast<uint32_t>(hd.n_sel);
+  if (total < p_sel || total > static_cast<uint32_t>(sm.list_cap)) return false;
+  // list entry g lies in chunk c with pre[c] <= g < pre[c + 1]; every thread issues its loads
+  // before writing any of them to LDS
+  constexpr int GPT = (kListMax + NT - 1) / NT;   // list entries per thread at most
+  uint32_t pre[kSplitMaxChunks];
+  {
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int c = 0; c < kSplitMaxChunks; ++c) {
+      pre[c] = acc;
+      if (c < C) acc += sm.cnt_l[c];
+    }
+  }
+  uint2 got[GPT];
+#pragma unroll
+  for (int q = 0; q < GPT; ++q) {
+    const uint32_t g = static_cast<uint32_t>(tid + q * NT);
+    got[q] = make_uint2(0u, 0u);
+    if (g < total) {   // whole waves past the list skip their entry
+      int c = 0;
+#pragma unroll
+      for (int k = 1; k < kSplitMaxChunks; ++k)
+        if (k < C && pre[k] <= g) c = k;
+      const uint32_t e = g - pre[c];
+      got[q] = reinterpret_cast<const uint2 *>(p.split_list + (static_cast<size_t>(hd.head) * C + c) * (2 * kSplitChunk))[e];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < GPT; ++q) {
+    const uint32_t g = static_cast<uint32_t>(tid + q * NT);
+    if (g < total) {
+      sm.lkey[g] = got[q].x;
+      sm.lslot[g] = got[q].y;
+    }
+  }
+  __syncthreads();
+  uint32_t thr = 0u, need = 0u;
+  bool all_ties = true;
+  if (!list_threshold<NT, true>(sm, total, p_sel, 0.f, 0.f, random_cut(hd.n_sel, hd.n_cand), thr, need, all_ties))
+    return false;
+  list_place<NT, true>(sm, total, thr, need, all_ties, hd.P, hd.out, p.b_cap);
+  return true;
+}
+
 // One workgroup per (layer, seq, KV head): the partition, the fixed places of the prompt and the
 // recent window, then the ranking over R rounds, R the smallest of KPT/4, KPT/2 and KPT whose
 // NT*R slots reach the last evictable one.
@@ -992,6 +1161,13 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   if (writer) p.n_kept[hd.s] = n_kept;
   if (hd.n_sel <= 0) return;   // n_sel > 0 implies n_cand > n_sel (T > B)
 
+  // the split draw's ranking side (its chunk workgroups ran just before; only random selection on
+  // the 1024-thread tiers is launched with them, whose 16 waves hold the chunk counts)
+  if (NT == 1024 && KIND == 1 && p.split_chunks > 0 && listable(hd.n_sel, hd.n_cand, list_cap<NT, KPT>())) {
+    if (split_rank<NT>(p, sm, hd)) return;
+    __syncthreads();   // every thread has read the shared state before the full path resets it
+  }
+
   const int rounds = (hd.e_hi + NT - 1) / NT;
   if (KPT >= 8 && rounds <= KPT / 4) select_rounds<NT, (KPT >= 8 ? KPT / 4 : KPT), KIND>(p, sm, hd);
   else if (KPT >= 4 && rounds <= KPT / 2) select_rounds<NT, (KPT >= 4 ? KPT / 2 : KPT), KIND>(p, sm, hd);
@@ -1005,7 +1181,6 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
 // in slot order with the kept and tied counts carried from chunk to chunk. The union (KIND 2)
 // runs G + 1 such passes and keeps its union as a bit per slot in dynamic LDS (t_cap / 8 bytes).
 constexpr int kStreamThreads = 1024;
-constexpr int kStreamSamples = 4096;   // strided sample of the candidates for the listed path's cut
 static_assert(kSelectMaxSlotsUnion / 8 <= 32 * 1024, "union bits fit in 32 KB of LDS");
 
 template <int KIND>
@@ -1522,13 +1697,47 @@ hipError_t launch_select_recent(const SelectParams &p, hipStream_t st) {
   return hipGetLastError();
 }
 
-size_t select_scratch_bytes(int, int, int, int) { return 0; }
+// The split draw applies to random selection over batches of at most kSplitMaxHeads heads whose
+// caches fill the 1024-thread register tiers (one workgroup per head would leave most CUs idle);
+// its scratch is a count and a list of kSplitChunk entries per chunk. The selectors share one
+// workspace query, so top-k callers size for it too.
+constexpr long long kSplitMaxHeads = 64;
+static bool split_shape(long long heads, int t_cap) {
+  return heads <= kSplitMaxHeads && t_cap > 8192 && t_cap <= kSelectMaxSlots;
+}
+static size_t split_count_bytes(long long heads, int chunks) {
+  return (static_cast<size_t>(heads) * chunks * 4 + 255) & ~static_cast<size_t>(255);
+}
+
+size_t select_scratch_bytes(int L, int S, int H, int t_cap) {
+  const long long heads = static_cast<long long>(L) * S * H;
+  if (!split_shape(heads, t_cap)) return 0;
+  const int chunks = (t_cap + kSplitChunk - 1) / kSplitChunk;
+  return split_count_bytes(heads, chunks) + static_cast<size_t>(heads) * chunks * kSplitChunk * 8;
+}
 
 hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st) {
   const long long heads = static_cast<long long>(p.L) * p.S * p.H;
   if (heads <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(heads));
   const int t = p.t_cap;
+  // Random selection on few heads with long caches: the chunk workgroups draw and list first, then
+  // the tier's ranking workgroups.
+  // (n_sel never exceeds the budget: a budget whose selection cannot fit the list rules it out)
+  const int split_cap = t <= 1024 * 16 ? list_cap<1024, 16>() : list_cap<1024, 32>();
+  if (kind == SelectKind::kRandom && p.scratch && split_shape(heads, t) &&
+      static_cast<long long>(p.budget) + p.budget / 8 + 64 <= split_cap) {
+    SelectParams q = p;
+    q.split_chunks = (t + kSplitChunk - 1) / kSplitChunk;
+    q.split_list_cap = split_cap;
+    q.split_count = static_cast<uint32_t *>(p.scratch);
+    q.split_list = reinterpret_cast<uint32_t *>(static_cast<char *>(p.scratch) + split_count_bytes(heads, q.split_chunks));
+    const dim3 sgrid(static_cast<unsigned>(heads * q.split_chunks));
+    hipLaunchKernelGGL(select_split_kernel, sgrid, dim3(kSplitThreads), 0, st, q);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return t <= 1024 * 16 ? launch_cfg<1024, 16>(q, kind, grid, st) : launch_cfg<1024, 32>(q, kind, grid, st);
+  }
   // Register tiers: NT threads x KPT rounds of one key each cover t_cap slots.
   if (t <= kSelectMaxSlots) {
     if (t <= 256 * 8) return launch_cfg<256, 8>(p, kind, grid, st);

@@ -141,6 +141,10 @@ RANDOM_CASES = [
     ("random-over-half", 8192, [8192], [0], 4065 + 64, 64),
     ("random-empty-sample", 32768, [32768], [30720], 32356, 1536),
     ("random-tier-2048", 2048, [2048, 700], [100, 0], 400, 16),
+    # few heads with long caches: the draw split over chunk workgroups (both 1024-thread tiers,
+    # ragged lengths, a head that keeps everything)
+    ("random-split-16k", 16384, [16384, 9000], [512, 0], 2048, 64),
+    ("random-split-ragged-32k", 32768, [32768, 20000, 8000, 100], [1024, 0, 500, 10], 2048, 128),
     ("random-stream-70k", 70000, [70000, 40000], [1024, 0], 3072, 128),
     ("random-stream-131k-small-share", 131072, [131072], [0], 64, 16),
     ("random-stream-70k-budget-past-list", 70000, [70000], [0], 8000, 64),
@@ -197,3 +201,19 @@ def test_select_union_listed_branches_bit_exact(case):
             assert nk[s] == ref.size
             assert np.array_equal(kept[0, s, h, :ref.size], ref), f"{name} s{s} h{h}"
             assert np.all(kept[0, s, h, ref.size:] == -1)
+
+
+@pytest.mark.parametrize("L", [1, 40])
+def test_select_random_split_and_single_workgroup_bit_exact(L):
+    # 1 layer x 2 heads takes the split draw; 40 layers x 2 heads (80 heads) one workgroup per head
+    log(f"[listed random] L={L}")
+    S, H, t_cap, B, R = 1, 2, 32768, 3072, 128
+    Ts, Ps = [32768], [1024]
+    seed, event = 0x9E3779B97F4A7C15, 3
+    kept, nk = kv.kv_select_random((L, S, H, t_cap), _i32(Ts), _i32(Ps), B, R, 1024, seed, event, b_cap=B)
+    kept, nk = kept.cpu().numpy(), nk.cpu().numpy()
+    for l in range(0, L, 7):
+        for h in range(H):
+            ref = oracle.select_random(Ts[0], Ps[0], B, R, None, seed, event, l, h, 0)
+            assert nk[0] == ref.size
+            assert np.array_equal(kept[l, 0, h, :ref.size], ref), f"l{l} h{h}"
