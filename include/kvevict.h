@@ -340,7 +340,11 @@ kv_status kv_select_topk(const kv_shape *shape, const kv_policy *policy,
                          void *stream);
 
 /* Workspace bytes kv_select_topk, kv_select_random and kv_select_random_shared need for this
- * shape and b_cap (0 for sizes they reject). shape->seq_len is not read and may be NULL. */
+ * shape and b_cap (0 for sizes they reject). shape->seq_len is not read and may be NULL.
+ * It is the header alone, except for batches of at most 64 (layer, seq, KV head) heads with
+ * 8192 < t_cap <= 32768: there the random draw is spread over several workgroups per head, which
+ * hand their lists over in the workspace (8 bytes per slot and head, plus a count per 2048 slots).
+ * The contents need no initialisation and are not meaningful after the call. */
 size_t kv_select_workspace_bytes(const kv_shape *shape, int32_t b_cap);
 
 /*
