@@ -1328,11 +1328,15 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
             cut = c > 1.0 ? static_cast<uint32_t>(c) : 1u;
           }
         } else {
+          // the sample: 128 blocks of 32 consecutive candidates (one 128-byte line each) spread
+          // evenly over the evictable range. Single keys at a stride would fetch a line apiece;
+          // fewer, longer blocks miss top keys bunched between them (scores rising with the slot).
           const float sscale = static_cast<float>(kSampleBins) / (fmax - fmin), soff = -fmin * sscale;
-          const int ns = min(n_cand, kStreamSamples);
-          for (int i = tid; i < ns; i += NT) {
-            const int j = e_lo + static_cast<int>((static_cast<long long>(i) * n_cand) / ns);
-            atomicAdd(&shist[bin_of_key_n(key_of(j), sscale, soff, kSampleBins)], 1u);
+          constexpr int kBlock = 32, kBlocks = kStreamSamples / kBlock;
+          const int step = max(kBlock, n_cand / kBlocks);
+          for (int i = tid; i < kStreamSamples; i += NT) {
+            const int off = (i / kBlock) * step + (i % kBlock);
+            if (off < n_cand) atomicAdd(&shist[bin_of_key_n(key_of(e_lo + off), sscale, soff, kSampleBins)], 1u);
           }
           __syncthreads();
           uint32_t bc, above_s, n_s;
