@@ -817,7 +817,7 @@ def main():
         # call is told its first layer, so the draws, the kept lists and the rows are those of the
         # single call above
         side = torch.cuda.Stream()
-        n_chunks = 12   # 3 layers each: measured best of 3-36 chunks (finer ones are bound by the host's launches)
+        n_chunks = 9   # 4 layers each: measured best of 3-36 chunks (finer ones are bound by the host's launches)
         bounds = np.linspace(0, L, n_chunks + 1).astype(int)
         nks = [torch.empty((S,), dtype=torch.int32, device=dev) for _ in range(n_chunks)]
         cevs = [torch.cuda.Event() for _ in range(n_chunks)]

@@ -1174,12 +1174,16 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
   else select_rounds<NT, KPT, KIND>(p, sm, hd);
 }
 
-// Caches past the register tiers (past 32768 slots; context lengths reach 128K tokens): the same rankings, threshold rule and ordered scan, with every step recomputing
-// the keys from memory (a score load, or the Philox draw) instead of keeping them in registers.
-// Steps: min/max (scores) and the 1024-bin histogram, the threshold bin's keys ranked in LDS (or,
-// when crowded, OR/AND and 8-bit radix passes), then the ordered scan in chunks of 4 * NT slots
-// in slot order with the kept and tied counts carried from chunk to chunk. The union (KIND 2)
-// runs G + 1 such passes and keeps its union as a bit per slot in dynamic LDS (t_cap / 8 bytes).
+// The re-reading kernel: caches past the register tiers (past 32768 slots; context lengths reach
+// 128K tokens), and random selection from 16385 slots on (no keys held in registers, so its
+// workgroups share CUs with a concurrent kernel). The same rankings, threshold rule and ordered
+// scan as the register kernel, with every step recomputing the keys from memory (a score load, or
+// the Philox draw). Top-k and random first take the listed path (a cut, one sweep that lists the
+// keys at or above it in LDS, the threshold and placement over the list); the fallback steps are
+// min/max (scores) and the 1024-bin histogram, the threshold bin's keys ranked in LDS (or, when
+// crowded, OR/AND and 8-bit radix passes), then the ordered scan in chunks of 4 * NT slots in slot
+// order with the kept and tied counts carried from chunk to chunk. The union (KIND 2) runs G + 1
+// such passes and keeps its union as a bit per slot in dynamic LDS (t_cap / 8 bytes).
 constexpr int kStreamThreads = 1024;
 static_assert(kSelectMaxSlotsUnion / 8 <= 32 * 1024, "union bits fit in 32 KB of LDS");
 
@@ -1256,12 +1260,20 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
     const float *row = nullptr;   // the scores this pass ranks by (not read by the random draw)
     if (!RANDOM) row = UNION && !last ? p.head_scores + (static_cast<size_t>(head) * p.G + pass) * p.t_cap
                                       : p.scores + slot0;
-    auto key_of = [&](int j) -> uint32_t {  // j in [e_lo, e_hi)
+    // The row (scores) or the positions (random) are read through buffer resources over [0, e_hi):
+    // a read past e_hi returns 0 without a memory access, so the sweeps below issue their loads
+    // unconditionally (a load under a per-slot condition waits for everything in flight).
+    const __amdgpu_buffer_rsrc_t rrow = rsrc_of(RANDOM ? static_cast<const void *>(p.seq_len) : row,
+                                                RANDOM ? 0 : e_hi * 4);
+    const __amdgpu_buffer_rsrc_t rpos = rsrc_of(p.pos ? static_cast<const void *>(p.pos + slot0) : p.seq_len,
+                                                p.pos ? e_hi * 4 : 0);
+    // the key of slot j from the 4 bytes loaded for it (a score's bits, or a position)
+    auto key_from = [&](int j, uint32_t bits) -> uint32_t {
       if (RANDOM) {
-        const uint32_t c0 = p.pos ? static_cast<uint32_t>(p.pos[slot0 + j]) : static_cast<uint32_t>(j);
+        const uint32_t c0 = p.pos ? bits : static_cast<uint32_t>(j);
         return philox_word0(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
       }
-      const uint32_t k = order_key(row[j]);
+      const uint32_t k = order_key(__uint_as_float(bits));
       if (UNION && last) {
         const bool in_u = in_union(j);
         if (long_union && !in_u) return 0u;
@@ -1269,6 +1281,11 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
       }
       return k;
     };
+    auto load_of = [&](int j) -> uint32_t {
+      if (RANDOM) return p.pos ? ld32(rpos, j * 4, 0) : 0u;
+      return ld32(rrow, j * 4, 0);
+    };
+    auto key_of = [&](int j) -> uint32_t { return key_from(j, load_of(j)); };  // j in [e_lo, e_hi)
     const int p_sel = UNION && !last ? k_head : n_sel;
 
     // mode: 0 = select none, 1 = select all candidates, 2 = threshold rule
@@ -1298,11 +1315,18 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
       }
       if (!RANDOM) {
         uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
-        for (int j = e_lo + tid; j < e_hi; j += NT) {
-          const uint32_t k = key_of(j);
-          if (k > kKeyNegInf && k < kKeyPosInf) {
-            kmn = min(kmn, k);
-            kmx = max(kmx, k);
+        constexpr int U = 8;   // loads in flight per thread
+        for (int j = e_lo + tid; j < e_hi; j += U * NT) {
+          uint32_t b[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) b[u] = load_of(j + u * NT);
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const uint32_t k = key_from(j + u * NT, b[u]);
+            if (j + u * NT < e_hi && k > kKeyNegInf && k < kKeyPosInf) {
+              kmn = min(kmn, k);
+              kmx = max(kmx, k);
+            }
           }
         }
         block_min_max<NT>(kmn, kmx, red);
@@ -1332,11 +1356,21 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
           // evenly over the evictable range. Single keys at a stride would fetch a line apiece;
           // fewer, longer blocks miss top keys bunched between them (scores rising with the slot).
           const float sscale = static_cast<float>(kSampleBins) / (fmax - fmin), soff = -fmin * sscale;
-          constexpr int kBlock = 32, kBlocks = kStreamSamples / kBlock;
+          constexpr int kBlock = 32, kBlocks = kStreamSamples / kBlock, SPT = kStreamSamples / NT;
+          static_assert(kStreamSamples % NT == 0, "whole sample rounds per thread");
           const int step = max(kBlock, n_cand / kBlocks);
-          for (int i = tid; i < kStreamSamples; i += NT) {
+          uint32_t sb[SPT];
+#pragma unroll
+          for (int u = 0; u < SPT; ++u) {
+            const int i = tid + u * NT;
+            sb[u] = load_of(e_lo + (i / kBlock) * step + (i % kBlock));
+          }
+#pragma unroll
+          for (int u = 0; u < SPT; ++u) {
+            const int i = tid + u * NT;
             const int off = (i / kBlock) * step + (i % kBlock);
-            if (off < n_cand) atomicAdd(&shist[bin_of_key_n(key_of(e_lo + off), sscale, soff, kSampleBins)], 1u);
+            if (off < n_cand)
+              atomicAdd(&shist[bin_of_key_n(key_from(e_lo + off, sb[u]), sscale, soff, kSampleBins)], 1u);
           }
           __syncthreads();
           uint32_t bc, above_s, n_s;
@@ -1350,16 +1384,28 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
             cut = order_key(lo_f);
           }
         }
+        // KC consecutive candidates per thread and chunk, the next chunk's loads issued before
+        // this chunk's keys are formed and listed (the last chunk's next reads past e_hi: no access)
+        constexpr int KC = RANDOM ? 8 : 4;
+        uint32_t nxt[KC];
+#pragma unroll
+        for (int q = 0; q < KC; ++q) nxt[q] = load_of(e_lo + KC * tid + q);
         uint32_t carry = 0u;
-        for (int c = e_lo; c < e_hi; c += 4 * NT) {
-          const int j0 = c + 4 * tid;
-          uint32_t kk[4];
+        for (int c = e_lo; c < e_hi; c += KC * NT) {
+          const int j0 = c + KC * tid;
+          uint32_t cur[KC];
+#pragma unroll
+          for (int q = 0; q < KC; ++q) {
+            cur[q] = nxt[q];
+            nxt[q] = load_of(j0 + KC * NT + q);
+          }
+          uint32_t kk[KC];
           uint32_t f = 0u;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+          for (int q = 0; q < KC; ++q) {
             kk[q] = 0u;
             if (j0 + q < e_hi) {
-              kk[q] = key_of(j0 + q);
+              kk[q] = key_from(j0 + q, cur[q]);
               f |= static_cast<uint32_t>(kk[q] >= cut) << q;
             }
           }
@@ -1375,7 +1421,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
           }
           __syncthreads();   // wsum is rewritten by the next chunk
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+          for (int q = 0; q < KC; ++q) {
             if ((f >> q) & 1u) {
               if (at < static_cast<uint32_t>(LCAP)) {
                 lkey[at] = kk[q];
@@ -1705,7 +1751,10 @@ hipError_t launch_select_recent(const SelectParams &p, hipStream_t st) {
 // caches fill the 1024-thread register tiers (one workgroup per head would leave most CUs idle);
 // its scratch is a count and a list of kSplitChunk entries per chunk. The selectors share one
 // workspace query, so top-k callers size for it too.
-constexpr long long kSplitMaxHeads = 64;
+#ifndef KV_SPLIT_MAX_HEADS
+#define KV_SPLIT_MAX_HEADS 64
+#endif
+constexpr long long kSplitMaxHeads = KV_SPLIT_MAX_HEADS;
 static bool split_shape(long long heads, int t_cap) {
   return heads <= kSplitMaxHeads && t_cap > 8192 && t_cap <= kSelectMaxSlots;
 }
@@ -1741,6 +1790,15 @@ hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st)
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return t <= 1024 * 16 ? launch_cfg<1024, 16>(q, kind, grid, st) : launch_cfg<1024, 32>(q, kind, grid, st);
+  }
+  // Random selection over 16,385-32,768 slots: the re-reading kernel, which draws each key once
+  // on its listed path and holds no keys in registers (57 VGPRs against the 1024 x 32 tier's 119).
+  // Alone the two take the same time to within 2 %; beside another kernel (the compaction of a
+  // previous layer chunk) its workgroups find room on CUs that the tier's, which need a whole CU's
+  // registers, do not.
+  if (kind == SelectKind::kRandom && t > 1024 * 16 && t <= kSelectMaxSlots) {
+    hipLaunchKernelGGL(select_stream_kernel<1>, grid, dim3(kStreamThreads), 0, st, p);
+    return hipGetLastError();
   }
   // Register tiers: NT threads x KPT rounds of one key each cover t_cap slots.
   if (t <= kSelectMaxSlots) {
