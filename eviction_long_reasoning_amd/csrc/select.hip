@@ -1285,7 +1285,19 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
       if (RANDOM) return p.pos ? ld32(rpos, j * 4, 0) : 0u;
       return ld32(rrow, j * 4, 0);
     };
-    auto key_of = [&](int j) -> uint32_t { return key_from(j, load_of(j)); };  // j in [e_lo, e_hi)
+    // visit(j, key) for every candidate slot, U loads in flight per thread (fewer for the draw,
+    // whose keys cost far more arithmetic than their position loads)
+    auto sweep = [&](auto &&visit) __attribute__((always_inline)) {
+      constexpr int U = RANDOM ? 2 : 8;
+      for (int j = e_lo + tid; j < e_hi; j += U * NT) {
+        uint32_t b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) b[u] = load_of(j + u * NT);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (j + u * NT < e_hi) visit(j + u * NT, key_from(j + u * NT, b[u]));
+      }
+    };
     const int p_sel = UNION && !last ? k_head : n_sel;
 
     // mode: 0 = select none, 1 = select all candidates, 2 = threshold rule
@@ -1315,20 +1327,12 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
       }
       if (!RANDOM) {
         uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
-        constexpr int U = 8;   // loads in flight per thread
-        for (int j = e_lo + tid; j < e_hi; j += U * NT) {
-          uint32_t b[U];
-#pragma unroll
-          for (int u = 0; u < U; ++u) b[u] = load_of(j + u * NT);
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const uint32_t k = key_from(j + u * NT, b[u]);
-            if (j + u * NT < e_hi && k > kKeyNegInf && k < kKeyPosInf) {
-              kmn = min(kmn, k);
-              kmx = max(kmx, k);
-            }
+        sweep([&](int, uint32_t k) {
+          if (k > kKeyNegInf && k < kKeyPosInf) {
+            kmn = min(kmn, k);
+            kmx = max(kmx, k);
           }
-        }
+        });
         block_min_max<NT>(kmn, kmx, red);
         fmin = key_value(kmn);
         fmax = key_value(kmx);
@@ -1473,7 +1477,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
         for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
         if (tid == 0) n_members = 0u;
         __syncthreads();
-        for (int j = e_lo + tid; j < e_hi; j += NT) atomicAdd(&hist[bin_of(key_of(j))], 1u);
+        sweep([&](int, uint32_t k) { atomicAdd(&hist[bin_of(k)], 1u); });
         __syncthreads();
         if (wave == 0) find_bin<kValueBins>(hist, remaining, lane, found);
         __syncthreads();
@@ -1484,13 +1488,12 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
         klo = kb[0];
         khi = kb[1];
         // a short member list is ranked directly (as in the register kernel)
-        for (int j = e_lo + tid; j < e_hi; j += NT) {
-          const uint32_t k = key_of(j);
+        sweep([&](int, uint32_t k) {
           if (k >= klo && k <= khi) {
             const uint32_t at = atomicAdd(&n_members, 1u);
             if (at < member_cap<NT>()) hist[at] = k;
           }
-        }
+        });
         __syncthreads();
         const uint32_t m = n_members;
         if (m <= member_cap<NT>()) {
@@ -1508,13 +1511,12 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
       auto member = [&](uint32_t k) { return !binned || (k >= klo && k <= khi); };
       if (!ranked) {
         uint32_t kor = 0u, kand = 0xFFFFFFFFu;
-        for (int j = e_lo + tid; j < e_hi; j += NT) {
-          const uint32_t k = key_of(j);
+        sweep([&](int, uint32_t k) {
           if (member(k)) {
             kor |= k;
             kand &= k;
           }
-        }
+        });
         block_or_and<NT>(kor, kand, red);
         const uint32_t diff = kor ^ kand;
         if (diff == 0u) {
@@ -1528,10 +1530,9 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
             const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
             for (int i = tid; i < 256; i += NT) hist[i] = 0u;
             __syncthreads();
-            for (int j = e_lo + tid; j < e_hi; j += NT) {
-              const uint32_t k = key_of(j);
+            sweep([&](int, uint32_t k) {
               if ((k & mask) == prefix && member(k)) atomicAdd(&hist[(k >> lo) & dmask], 1u);
-            }
+            });
             __syncthreads();
             if (wave == 0) find_bin<256>(hist, remaining, lane, found);
             __syncthreads();
@@ -1587,9 +1588,12 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
 
     if (UNION && !last && (mode != 2 || all_ties)) {
       // a head's top-k needs no order: mark every candidate above (or at) the threshold
-      for (int j = e_lo + tid; j < e_hi; j += NT) {
-        const uint32_t k = mode == 2 ? key_of(j) : 0u;
-        if (mode == 1 || (mode == 2 && k >= thr)) atomicOr(&ubits[j >> 5], 1u << (j & 31));
+      if (mode == 2) {
+        sweep([&](int j, uint32_t k) {
+          if (k >= thr) atomicOr(&ubits[j >> 5], 1u << (j & 31));
+        });
+      } else if (mode == 1) {
+        for (int j = e_lo + tid; j < e_hi; j += NT) atomicOr(&ubits[j >> 5], 1u << (j & 31));
       }
       __syncthreads();
       continue;
@@ -1597,9 +1601,22 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
 
     // ordered scan: thread t takes slots c + 4t .. c + 4t + 3 of each chunk. The last pass writes
     // the kept list; a union head pass adds its top-k (ties to the lower slots) to the union.
+    // The union's passes (which always scan) issue the keys' loads for chunk c + 1 before chunk c
+    // is ranked (reads at or past e_hi return 0 without an access; bits loaded for slots below
+    // e_lo are not used); top-k and random scan only on their fallback and keep the registers.
+    constexpr bool AHEAD = UNION;
     uint32_t carry_a = 0u, carry_e = 0u;  // unconditional / tied slots in earlier chunks
+    uint32_t nb4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) nb4[q] = AHEAD && mode == 2 ? load_of(4 * tid + q) : 0u;
     for (int c = 0; c < T; c += 4 * NT) {
       const int j0 = c + 4 * tid;
+      uint32_t cb4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        cb4[q] = nb4[q];
+        nb4[q] = AHEAD && mode == 2 ? load_of(j0 + 4 * NT + q) : 0u;
+      }
       uint32_t fa = 0u, fe = 0u;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -1608,7 +1625,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const Sel
         const bool cnd = j >= e_lo && j < e_hi;
         bool a = last ? (!cnd || mode == 1) : (cnd && mode == 1), e = false;  // pins: last pass
         if (cnd && mode == 2) {
-          const uint32_t k = key_of(j);
+          const uint32_t k = key_from(j, AHEAD ? cb4[q] : load_of(j));
           a = k > thr;
           e = k == thr;
         }
