@@ -87,13 +87,13 @@ def pmc_probe_next(w, K, qb, qbd, seq, plen, tcur, scores, kept, nk, b_cap, dev)
     del zmax, head
     kv.kv_select_random((L, S, H, T), seq, plen, w.budget, w.recent, w.prompt_cap(), 1, 0, b_cap=b_cap, kept=kept,
                         n_kept=nk)
-    out.append(["select_kernel<1024, 32, 1>", 0, heads * b_cap * 4])
+    out.append(["select_stream_kernel<1, 512>", 0, heads * b_cap * 4])
     Sl, Tl = S // 4, 4 * T
     kl = torch.empty((L, Sl, H, b_cap), dtype=torch.int32, device=dev)
     nkl = torch.empty((Sl,), dtype=torch.int32, device=dev)
     kv.kv_select_topk(scores.view(L, Sl, H, Tl), i32_dev(np.full(Sl, Tl), dev), i32_dev(np.full(Sl, w.prompt_len[0]), dev),
                       w.budget, w.recent, w.prompt_cap(), b_cap=b_cap, kept=kl, n_kept=nkl)
-    out.append(["select_stream_kernel<0>", n * 4, L * Sl * H * b_cap * 4])
+    out.append(["select_stream_kernel<0, 1024>", n * 4, L * Sl * H * b_cap * 4])
     zmax, head = kv.tri_score_gqa_rotated(K.view(L, S * bps, bs, H, d), nu, tcur, seq, w.theta, w.deltas,
                                           block_table=table)
     out.append(["gqa_rotated_kernel<true, 16, false, 1, false, 4>", n * d * e + L * H * S * bps * 4, n * 4 * G])

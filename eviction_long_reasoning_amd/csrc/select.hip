@@ -1185,11 +1185,11 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
 // order with the kept and tied counts carried from chunk to chunk. The union (KIND 2) runs G + 1
 // such passes and keeps its union as a bit per slot in dynamic LDS (t_cap / 8 bytes).
 constexpr int kStreamThreads = 1024;
+constexpr int kLeanRandomThreads = 512;   // random selection within the register tiers' sizes
 static_assert(kSelectMaxSlotsUnion / 8 <= 32 * 1024, "union bits fit in 32 KB of LDS");
 
-template <int KIND>
-__global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(const SelectParams p) {
-  constexpr int NT = kStreamThreads;
+template <int KIND, int NT = kStreamThreads>
+__global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p) {
   constexpr int NW = NT / 64;
   constexpr bool RANDOM = KIND == 1, UNION = KIND == 2;
   __shared__ __align__(16) uint32_t hist[kValueBins];
@@ -1808,13 +1808,14 @@ hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st)
     if (e != hipSuccess) return e;
     return t <= 1024 * 16 ? launch_cfg<1024, 16>(q, kind, grid, st) : launch_cfg<1024, 32>(q, kind, grid, st);
   }
-  // Random selection over 16,385-32,768 slots: the re-reading kernel, which draws each key once
-  // on its listed path and holds no keys in registers (57 VGPRs against the 1024 x 32 tier's 119).
-  // Alone the two take the same time to within 2 %; beside another kernel (the compaction of a
-  // previous layer chunk) its workgroups find room on CUs that the tier's, which need a whole CU's
-  // registers, do not.
+  // Random selection over 16,385-32,768 slots: the re-reading kernel at 512 threads, which draws
+  // each key once on its listed path and holds no keys in registers (50 VGPRs against the
+  // 1024 x 32 tier's 119). Two of its workgroups share a CU, and beside another kernel (the
+  // compaction of a previous layer chunk) they find room on CUs that the tier's, which need a
+  // whole CU's registers, do not. On 2,304 heads it draws in 0.157 ms against 0.186 ms; on 256
+  // heads or fewer (one workgroup per CU) it takes about 15 % longer than 1,024 threads would.
   if (kind == SelectKind::kRandom && t > 1024 * 16 && t <= kSelectMaxSlots) {
-    hipLaunchKernelGGL(select_stream_kernel<1>, grid, dim3(kStreamThreads), 0, st, p);
+    hipLaunchKernelGGL((select_stream_kernel<1, kLeanRandomThreads>), grid, dim3(kLeanRandomThreads), 0, st, p);
     return hipGetLastError();
   }
   // Register tiers: NT threads x KPT rounds of one key each cover t_cap slots.
