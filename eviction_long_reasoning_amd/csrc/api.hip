@@ -614,7 +614,7 @@ KV_EXPORT kv_status kv_compact(const kv_shape *shape, const void *K_in, const vo
   const int rows_wg = compact_rows_per_wg(G);
   const int max_rows = b_cap < out_cap ? b_cap : out_cap;
   p.wgs_per_head = (max_rows + rows_wg - 1) / rows_wg;
-  const long long threads = static_cast<long long>(heads) * p.wgs_per_head * 256;
+  const long long threads = static_cast<long long>(heads) * p.wgs_per_head * compact_wgs_per_slice() * 256;
   if (threads >= (1ll << 32)) return KV_ESHAPE;
   return hip_status(launch_compact(p, static_cast<hipStream_t>(stream)));
 }

@@ -6,12 +6,13 @@
 // order. Row r of a head's output is row kept[r] of its input, for K, V and
 // the positions.
 //
-// Mapping: a row of d elements is row16 16-byte pieces; G = row16 rounded up
-// to a power of two lanes copy one row (global_load/store_dwordx4), 64/G rows
-// per wave instruction, and each thread keeps kUnroll rows of K and V in
-// flight before storing. A workgroup owns a contiguous range of output rows of
-// one head, so stores are fully contiguous and loads are whole rows (kept
-// indices ascend, so neighbouring kept rows often share DRAM pages).
+// Mapping: a row of d elements is row16 16-byte pieces; G = row16 rounded up to a power of two
+// lanes copy one row (16-byte loads and stores), 256/G rows per pass. Workgroups come in pairs
+// over the same output rows of one head, the even one moving K (and the positions), the odd one
+// V, two passes each; every thread keeps one row piece in flight and loads the next pass's kept
+// index before the current pass's row, so the index is not on the row's path. Stores are fully
+// contiguous and loads are whole rows (kept indices ascend, so neighbouring kept rows often share
+// DRAM pages).
 //
 // Hole filling is the in-place alternative: only kept rows at or beyond the
 // new length move, each into an evicted slot below it, so a periodic eviction
@@ -24,10 +25,7 @@ namespace kvevict {
 namespace {
 
 constexpr int kCompactThreads = 256;
-#ifndef KV_COMPACT_UNROLL
-#define KV_COMPACT_UNROLL 2
-#endif
-constexpr int kUnroll = KV_COMPACT_UNROLL;
+constexpr int kPasses = 2;   // passes of 256 / G rows per workgroup
 
 // Every row is moved exactly once, so loads and stores use the non-temporal cache policy.
 typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
@@ -43,12 +41,13 @@ __device__ __forceinline__ void st_stream(uint4 *p, const uint4 &x) {
 template <int G>
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(const CompactParams p) {
   constexpr int ROWS_PER_PASS = kCompactThreads / G;
-  constexpr int ROWS_PER_WG = ROWS_PER_PASS * kUnroll;
-  const int head = blockIdx.x / p.wgs_per_head;
-  const int part = blockIdx.x - head * p.wgs_per_head;
+  const int wg = static_cast<int>(blockIdx.x >> 1);
+  const int which = static_cast<int>(blockIdx.x & 1);   // 0: K and the positions, 1: V
+  const int head = wg / p.wgs_per_head;
+  const int part = wg - head * p.wgs_per_head;
   const int s = (head / p.H) % p.S;
   const int nk = min(min(max(p.n_kept[s], 0), p.b_cap), p.out_cap);
-  const int r0 = part * ROWS_PER_WG;
+  const int r0 = part * ROWS_PER_PASS * kPasses;
   if (r0 >= nk) return;
 
   const int c = threadIdx.x % G;
@@ -57,30 +56,25 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(const CompactP
   const size_t in_row0 = static_cast<size_t>(head) * p.t_cap;
   const size_t out_row0 = static_cast<size_t>(head) * p.out_cap;
   const int32_t *kept = p.kept + static_cast<size_t>(head) * p.b_cap;
+  const uint4 *src = which ? p.V_in : p.K_in;
+  uint4 *dst = which ? p.V_out : p.K_out;
+  auto source_row = [&](int r) {   // kept[r], or -1 past n_kept or out of range
+    const int j = r < nk ? kept[r] : -1;
+    return (j >= 0 && j < p.t_cap) ? j : -1;
+  };
 
-  int src[kUnroll];
-  uint4 kv[kUnroll], vv[kUnroll];
+  int j_next = source_row(r0 + rr);
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int r = r0 + u * ROWS_PER_PASS + rr;
-    int j = r < nk ? kept[r] : -1;
-    j = (j >= 0 && j < p.t_cap) ? j : -1;
-    src[u] = j;
+  for (int b = 0; b < kPasses; ++b) {
+    const int r = r0 + b * ROWS_PER_PASS + rr;
+    const int j = j_next;
+    if (b + 1 < kPasses) j_next = source_row(r + ROWS_PER_PASS);
     const bool ld = j >= 0 && lane_live;
     const size_t off = (in_row0 + static_cast<size_t>(ld ? j : 0)) * p.row16 + (ld ? c : 0);
-    kv[u] = ld ? ld_stream(p.K_in + off) : make_uint4(0u, 0u, 0u, 0u);
-    vv[u] = ld ? ld_stream(p.V_in + off) : make_uint4(0u, 0u, 0u, 0u);
-  }
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int r = r0 + u * ROWS_PER_PASS + rr;
-    const int j = src[u];
-    if (j >= 0 && lane_live) {
-      const size_t off = (out_row0 + static_cast<size_t>(r)) * p.row16 + c;
-      st_stream(p.K_out + off, kv[u]);
-      st_stream(p.V_out + off, vv[u]);
-    }
-    if (j >= 0 && c == 0 && p.pos_out) p.pos_out[out_row0 + r] = p.pos_in ? p.pos_in[in_row0 + j] : j;
+    const uint4 v = ld ? ld_stream(src + off) : make_uint4(0u, 0u, 0u, 0u);
+    if (ld) st_stream(dst + (out_row0 + static_cast<size_t>(r)) * p.row16 + c, v);
+    if (j >= 0 && c == 0 && which == 0 && p.pos_out)
+      p.pos_out[out_row0 + r] = p.pos_in ? p.pos_in[in_row0 + j] : j;
   }
 }
 
@@ -143,13 +137,14 @@ __global__ __launch_bounds__(kCompactThreads) void holes_kernel(const HoleParams
 
 }  // namespace
 
-int compact_rows_per_wg(int group) { return (kCompactThreads / group) * kUnroll; }
+int compact_rows_per_wg(int group) { return (kCompactThreads / group) * kPasses; }
+int compact_wgs_per_slice() { return 2; }
 
 hipError_t launch_compact(const CompactParams &p, hipStream_t st) {
   int G = 1;
   while (G < p.row16) G <<= 1;
   if (G > 64) return hipErrorInvalidValue;
-  const long long blocks = static_cast<long long>(p.L) * p.S * p.H * p.wgs_per_head;
+  const long long blocks = static_cast<long long>(p.L) * p.S * p.H * p.wgs_per_head * compact_wgs_per_slice();
   if (blocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(blocks)), blk(kCompactThreads);
   switch (G) {

@@ -125,6 +125,7 @@ struct CompactParams {
 };
 
 int compact_rows_per_wg(int group);  // output rows per compact workgroup for a lane-group size
+int compact_wgs_per_slice();         // workgroups per (head, row range): 2 when K and V move apart
 hipError_t launch_compact(const CompactParams &p, hipStream_t st);
 
 // In-place hole filling: kept rows at or beyond n_kept move into evicted slots below it.
