@@ -707,15 +707,16 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
       }
 
       // ---- listed path: cut, count, list, then the threshold over the list
-      auto try_list = [&]() __attribute__((always_inline)) -> bool {
+      // the `want` largest keys (the selection, or the count to evict when the keys are flipped)
+      auto try_list = [&](int want) __attribute__((always_inline)) -> bool {
         float cut_f = -INFINITY;   // scores: list x >= cut_f (NaN marks never pass)
         uint32_t cut_k = 1u;       // random: list words >= cut_k (slots that take no part hold 0)
         if (RANDOM) {
-          cut_k = random_cut(p_sel, n_valid);
+          cut_k = random_cut(want, n_valid);
         } else {
           // two keys per thread (rounds R/4 and 3R/4: two blocks of 64 consecutive slots per wave,
           // spread evenly over the head) into kSampleBins value bins; the cut is one bin below where
-          // the count from the top reaches the sample's expected share of p_sel plus three standard
+          // the count from the top reaches the sample's expected share of `want` plus three standard
           // deviations. The rounds are fixed: a per-lane choice of round would index the key array.
           const float sscale = static_cast<float>(kSampleBins) / (mx - mn), soff = -mn * sscale;
           constexpr int kS0 = R >= 4 ? R / 4 : 0, kS1 = R >= 4 ? 3 * R / 4 : R - 1;
@@ -725,7 +726,7 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
           __syncthreads();
           uint32_t bc, above_s, n_s;
           wave_find_bin<kSampleBins>(sm.shist, [&](uint32_t tot) {
-            const float lam = static_cast<float>(p_sel) * static_cast<float>(tot) / static_cast<float>(n_valid);
+            const float lam = static_cast<float>(want) * static_cast<float>(tot) / static_cast<float>(n_valid);
             return static_cast<uint32_t>(lam + 3.f * sqrtf(lam) + 4.f);
           }, lane, bc, above_s, n_s);
           if (bc > 1u) cut_f = (static_cast<float>(bc - 1u) - soff) / sscale;
@@ -742,7 +743,7 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
           if (w < wave) base += c;
           total += c;
         }
-        if (total < static_cast<uint32_t>(p_sel) || total > static_cast<uint32_t>(sm.list_cap)) return false;
+        if (total < static_cast<uint32_t>(want) || total > static_cast<uint32_t>(sm.list_cap)) return false;
         // bins over the listed range: scores by value between the cut (or the smallest finite key)
         // and the largest; random words by their offset above the cut
         const float lo = cut_f > -INFINITY ? cut_f : mn;
@@ -762,13 +763,49 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
           }
         }
         __syncthreads();
-        if (!list_threshold<NT, RANDOM>(sm, total, static_cast<uint32_t>(p_sel), lo, mx, cut_k, thr, need, all_ties))
+        if (!list_threshold<NT, RANDOM>(sm, total, static_cast<uint32_t>(want), lo, mx, cut_k, thr, need, all_ties))
           return false;
         n_list = total;
         return true;
       };
-      if (binned && listable(p_sel, n_valid, sm.list_cap)) listed = try_list();
-      if (!listed) {
+      // More than half selected: the same listing from the other end. The keys are flipped (scores
+      // negated, random words complemented) so the q = n_valid - p_sel lowest come first; the list
+      // gives the q-th lowest key, the number of keys equal to it (all of them are listed) and how
+      // many of those the q lowest take. The kept set is then every key above it and, of the keys
+      // equal to it, the lowest-slot (ties - taken), placed by the ordered scan below.
+      bool flipped = false;
+      const int q_evict = n_valid - p_sel;
+      auto flip_keys = [&]() {
+        const int jf = slot_base();
+#pragma unroll
+        for (int i = 0; i < R; ++i) key[i] = RANDOM ? (evictable(jf, i) ? ~key[i] : 0u) : key[i] ^ 0x80000000u;
+      };
+      const bool list_top = binned && listable(p_sel, n_valid, sm.list_cap);
+      const bool list_low = !UNION && !list_top && binned && listable(q_evict, n_valid, sm.list_cap);
+      const float mn0 = mn, mx0 = mx;
+      if (list_low) {
+        flip_keys();
+        mn = -mx0;
+        mx = -mn0;
+      }
+      if (list_top || list_low) {   // one call site: the listing is inlined once
+        const bool ok = try_list(list_low ? q_evict : p_sel);
+        listed = list_top && ok;
+        flipped = list_low && ok;
+      }
+      if (list_low) {
+        mn = mn0;
+        mx = mx0;
+        flip_keys();
+      }
+      if (flipped) {
+        const uint32_t ties_at = sm.found[2];   // keys equal to the q-th lowest (rank_members' count)
+        thr = RANDOM ? ~thr : order_key(-key_value(thr));
+        need = ties_at - need;                  // the ties kept: those the q lowest leave
+        all_ties = need == ties_at;
+        careful = RANDOM && thr == 0u;          // word 0 is also the mark of a slot that takes no part
+      }
+      if (!listed && !flipped) {
       __syncthreads();   // the previous pass's readers of hist are done
       // valid: the key takes part (scores: not the NaN mark; random: the slot range)
       auto valid = [&](int i, int j0) {

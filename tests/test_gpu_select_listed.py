@@ -3,8 +3,10 @@
 Selections of at most half the candidates first list the keys at or above a cut taken from a
 sample (two fixed rounds per thread, R/4 and 3R/4 of its R rounds) and rank and place over that
 list; a cut that leaves too few keys or more than the list holds, or a threshold bin too crowded
-to rank directly, falls back to the histogram over every key. Each case below is built so that a
-given branch runs (the comment says which); every one must give the oracle's keep-set exactly.
+to rank directly, falls back to the histogram over every key. Selections of more than half (in the
+register tiers) list the keys to evict the same way, with the keys flipped, and place by the
+ordered scan. Each case below is built so that a given branch runs (the comment says which); every
+one must give the oracle's keep-set exactly.
 """
 import numpy as np
 import pytest
@@ -39,13 +41,18 @@ def _row(pattern: str, r, t_cap: int, T: int, P: int, B: int, R: int) -> np.ndar
         x += np.arange(t_cap, dtype=np.float32) * np.float32(4.0 / t_cap)
     elif pattern == "tie-block-over-cap":   # 9000 equal keys above the rest: the count exceeds the list
         x[r.choice(t_cap, 9000, replace=False)] = np.float32(5.0)
+    elif pattern == "crowded-low":    # the same from below: 1500 equal keys hold an over-half threshold
+        x *= np.float32(0.3)
+        idx = r.choice(t_cap, 2500, replace=False)
+        x[idx[:1500]] = np.float32(-2.0)
+        x[idx[1500:]] = np.float32(-2.5) - np.float32(7.0) * r.random(1000, dtype=np.float32)
     elif pattern == "crowded-bin":    # 1500 equal keys hold the threshold: its list bin is too crowded
         x *= np.float32(0.3)
         idx = r.choice(t_cap, 2500, replace=False)
         x[idx[:1500]] = np.float32(2.0)
         x[idx[1500:]] = np.float32(2.5) + np.float32(7.0) * r.random(1000, dtype=np.float32)
     elif pattern == "ties-straddle":  # a block of equal keys just below the selection's share
-        v = np.float32(np.quantile(x[P:T], 1.0 - share + 0.004))
+        v = np.float32(np.quantile(x[P:T], min(1.0, 1.0 - share + 0.004)))
         x[r.choice(t_cap, max(8, t_cap // 100), replace=False)] = v
     elif pattern == "signed-zeros":   # +0 and -0 tie at the threshold: positives fall just short
         x = -np.abs(x) - np.float32(0.01)
@@ -102,6 +109,21 @@ CASES = [
     ("tier-4096-over-cap", 4096, [4096], [64], 1700, 16, "normal"),
     ("tier-8192", 8192, [8192, 5000], [256, 3], 1500, 32, "signed-zeros"),
     ("tier-16384", 16384, [16384], [2048], 4000, 128, "trend"),
+    # more than half selected: the keys to evict listed with the keys flipped (register tiers)
+    ("flip-32k", 32768, [32768, 30001], [1024, 17], 30000, 128, "normal"),
+    ("flip-ties-straddle", 32768, [32768, 20000], [1024, 0], 29000, 128, "ties-straddle"),
+    ("flip-signed-zeros", 32768, [32768], [1000], 30000, 128, "signed-zeros"),
+    ("flip-infinities", 32768, [32768], [256], 31000, 64, "infinities"),
+    # the 400th lowest key is -inf (300 -inf and 300 NaN, which ranks as -inf): the ties at -inf
+    # keep their 200 lowest slots
+    ("flip-at-neg-inf", 32768, [32768], [256], 32368, 64, "infinities"),
+    ("flip-crowded-low", 32768, [32768], [512], 30500, 100, "crowded-low"),
+    ("flip-trend", 32768, [32768], [1024], 29000, 128, "trend"),
+    ("flip-sample-high", 32768, [32768], [1024], 29000, 128, "sample-high"),
+    ("flip-tier-2048", 2048, [2048, 1999], [100, 0], 1800, 16, "ties-straddle"),
+    ("flip-tier-4096", 4096, [4096, 2176], [64, 300], 3900, 16, "normal"),
+    ("flip-tier-8192", 8192, [8192, 5000], [256, 3], 7000, 32, "signed-zeros"),
+    ("flip-tier-16384", 16384, [16384], [2048], 15000, 128, "trend"),
     # past 32768 slots: the re-reading kernel's listed path (count and list in one sweep)
     ("stream-40k", 40000, [40000, 33001], [1024, 0], 3072, 128, "normal"),
     ("stream-131k-trend", 131072, [131072], [2048], 4096, 128, "trend"),
@@ -141,6 +163,11 @@ RANDOM_CASES = [
     ("random-over-half", 8192, [8192], [0], 4065 + 64, 64),
     ("random-empty-sample", 32768, [32768], [30720], 32356, 1536),
     ("random-tier-2048", 2048, [2048, 700], [100, 0], 400, 16),
+    # more than half selected: the words to evict listed complemented (tiers up to 16384 slots)
+    ("random-flip-2048", 2048, [2048, 700], [100, 0], 1800, 16),
+    ("random-flip-4096", 4096, [4096, 2176], [64, 300], 3900, 16),
+    ("random-flip-8192", 8192, [8192], [0], 7000, 64),
+    ("random-flip-16k", 16384, [16384, 9000], [512, 0], 15000, 64),
     # few heads with long caches: the draw split over chunk workgroups (both 1024-thread tiers,
     # ragged lengths, a head that keeps everything)
     ("random-split-16k", 16384, [16384, 9000], [512, 0], 2048, 64),
