@@ -1851,7 +1851,10 @@ hipError_t launch_select(const SelectParams &p, SelectKind kind, hipStream_t st)
   // compaction of a previous layer chunk) they find room on CUs that the tier's, which need a
   // whole CU's registers, do not. On 2,304 heads it draws in 0.157 ms against 0.186 ms; on 256
   // heads or fewer (one workgroup per CU) it takes about 15 % longer than 1,024 threads would.
-  if (kind == SelectKind::kRandom && t > 1024 * 16 && t <= kSelectMaxSlots) {
+  // A budget over half the cache (periodic eviction of a small buffer) stays in the register tier:
+  // there a selection of more than half the candidates lists the keys to evict, where the
+  // re-reading kernel would redraw every key in each of its fallback sweeps.
+  if (kind == SelectKind::kRandom && t > 1024 * 16 && t <= kSelectMaxSlots && 2ll * p.budget <= t) {
     hipLaunchKernelGGL((select_stream_kernel<1, kLeanRandomThreads>), grid, dim3(kLeanRandomThreads), 0, st, p);
     return hipGetLastError();
   }

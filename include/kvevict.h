@@ -364,10 +364,11 @@ size_t kv_select_workspace_bytes(const kv_shape *shape, int32_t b_cap);
  *           chunks, gets the same draws as one call over all layers); 0 <= layer_base and
  *           layer_base + n_layers <= 65536.
  *  kept, b_cap, n_kept, workspace as for kv_select_topk (t_cap <= 2^26). From
- *  16385 slots on the draws are not held in registers but drawn once per sweep
- *  (recomputed at every step when a sweep is repeated), so the call's workgroups
- *  can share CUs with a concurrent kernel such as the compaction of another layer
- *  chunk; with the split draw above, the chunk workgroups draw instead.
+ *  16385 slots on, with a budget of at most half of t_cap, the draws are not held
+ *  in registers but drawn once per sweep (recomputed at every step when a sweep is
+ *  repeated), so the call's workgroups can share CUs with a concurrent kernel such
+ *  as the compaction of another layer chunk; with the split draw above, the chunk
+ *  workgroups draw instead.
  * Device checks (debug build): KV_DEV_SEQ_LEN, KV_DEV_PROMPT_LEN, and
  * KV_DEV_POS_ORDER when pos is given.
  */

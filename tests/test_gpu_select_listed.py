@@ -168,6 +168,8 @@ RANDOM_CASES = [
     ("random-flip-4096", 4096, [4096, 2176], [64, 300], 3900, 16),
     ("random-flip-8192", 8192, [8192], [0], 7000, 64),
     ("random-flip-16k", 16384, [16384, 9000], [512, 0], 15000, 64),
+    # a budget over half the cache keeps random selection in the 1024 x 32 register tier
+    ("random-flip-32k", 32768, [32768, 30001], [1024, 17], 30000, 128),
     # few heads with long caches: the draw split over chunk workgroups (both 1024-thread tiers,
     # ragged lengths, a head that keeps everything)
     ("random-split-16k", 16384, [16384, 9000], [512, 0], 2048, 64),
