@@ -1216,7 +1216,8 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
 // workgroups share CUs with a concurrent kernel). The same rankings, threshold rule and ordered
 // scan as the register kernel, with every step recomputing the keys from memory (a score load, or
 // the Philox draw). Top-k and random first take the listed path (a cut, one sweep that lists the
-// keys at or above it in LDS, the threshold and placement over the list); the fallback steps are
+// keys at or above it in LDS, the threshold and placement over the list; random selections of more
+// than half list the words to evict, complemented, and place by the ordered scan); the fallback steps are
 // min/max (scores) and the 1024-bin histogram, the threshold bin's keys ranked in LDS (or, when
 // crowded, OR/AND and 8-bit radix passes), then the ordered scan in chunks of 4 * NT slots in slot
 // order with the kept and tied counts carried from chunk to chunk. The union (KIND 2) runs G + 1
@@ -1383,11 +1384,13 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
       // (chunks of 4 * NT slots, a block-wide scan each); the threshold is then found on the list
       // as in the register kernel. A cut that leaves fewer than p_sel or more than the list holds,
       // or a crowded threshold bin, falls back to the sweeps below.
-      auto stream_list = [&]() -> bool {
+      // the want_n largest keys, or with fl (random words only) the want_n lowest, listed complemented
+      auto flipped_key = [&](uint32_t k) { return ~k; };
+      auto stream_list = [&](int want_n, bool fl) -> bool {
         uint32_t cut = 1u;   // list keys >= cut (order keys, or words)
         float lo_f = fmin;
         if (RANDOM) {
-          const float want = static_cast<float>(p_sel) + 4.f * sqrtf(static_cast<float>(p_sel)) + 16.f;
+          const float want = static_cast<float>(want_n) + 4.f * sqrtf(static_cast<float>(want_n)) + 16.f;
           if (want < static_cast<float>(n_cand)) {
             const double c = 4294967296.0 * (1.0 - static_cast<double>(want) / static_cast<double>(n_cand));
             cut = c > 1.0 ? static_cast<uint32_t>(c) : 1u;
@@ -1416,7 +1419,7 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
           __syncthreads();
           uint32_t bc, above_s, n_s;
           wave_find_bin<kSampleBins>(shist, [&](uint32_t tot) {
-            const float lam = static_cast<float>(p_sel) * static_cast<float>(tot) / static_cast<float>(n_cand);
+            const float lam = static_cast<float>(want_n) * static_cast<float>(tot) / static_cast<float>(n_cand);
             return static_cast<uint32_t>(lam + 3.f * sqrtf(lam) + 4.f);
           }, lane, bc, above_s, n_s);
           cut = 0u;
@@ -1447,6 +1450,7 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
             kk[q] = 0u;
             if (j0 + q < e_hi) {
               kk[q] = key_from(j0 + q, cur[q]);
+              if (RANDOM && fl) kk[q] = flipped_key(kk[q]);
               f |= static_cast<uint32_t>(kk[q] >= cut) << q;
             }
           }
@@ -1474,7 +1478,7 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
           carry += tot;
         }
         __syncthreads();   // the last chunk's list entries are written before anyone reads the list
-        if (carry < static_cast<uint32_t>(p_sel) || carry > static_cast<uint32_t>(LCAP)) return false;
+        if (carry < static_cast<uint32_t>(want_n) || carry > static_cast<uint32_t>(LCAP)) return false;
         const float scale2 = static_cast<float>(kListBins) / (fmax - lo_f), off2 = -lo_f * scale2;
         if (!RANDOM && !(fmax > lo_f && scale2 > 0.f && scale2 < 3.0e38f && fabsf(off2) < 3.0e38f)) return false;
         const uint32_t span = 0xFFFFFFFFu - cut;
@@ -1486,8 +1490,8 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
         for (uint32_t e = tid; e < carry; e += NT) atomicAdd(&hist[lbin(lkey[e])], 1u);
         __syncthreads();
         uint32_t b, above, tot;
-        wave_find_bin<kListBins>(hist, [&](uint32_t) { return static_cast<uint32_t>(p_sel); }, lane, b, above, tot);
-        const uint32_t rem = static_cast<uint32_t>(p_sel) - above;
+        wave_find_bin<kListBins>(hist, [&](uint32_t) { return static_cast<uint32_t>(want_n); }, lane, b, above, tot);
+        const uint32_t rem = static_cast<uint32_t>(want_n) - above;
         for (uint32_t e = tid; e < carry; e += NT) {
           const uint32_t k = lkey[e];
           if (lbin(k) == b) {
@@ -1506,9 +1510,27 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
         n_list = carry;
         return true;
       };
-      if (!UNION && (RANDOM || binned) && 2 * p_sel <= n_cand && p_sel + p_sel / 8 + 64 <= LCAP)
-        listed = stream_list();
-      if (!listed) {
+      // Random, more than half selected: the q = n_cand - p_sel words to evict listed complemented
+      // (as in the register kernel), then the ordered scan below places the kept set; one draw
+      // fewer per key than the fallback's sweeps. For scores the same listing and scan measured
+      // slower than the fallback (0.53-0.56 against 0.46-0.47 ms on 576 heads of 131,072 slots
+      // with 4,000 to evict), so scores keep it.
+      bool flipped = false;
+      const int q_evict = n_cand - p_sel;
+      const bool list_top = !UNION && (RANDOM || binned) && 2 * p_sel <= n_cand && p_sel + p_sel / 8 + 64 <= LCAP;
+      const bool list_low = RANDOM && !list_top && 2 * q_evict <= n_cand && q_evict + q_evict / 8 + 64 <= LCAP;
+      if (list_top || list_low) {   // one call site: the listing is inlined once
+        const bool ok = stream_list(list_low ? q_evict : p_sel, list_low);
+        listed = list_top && ok;
+        flipped = list_low && ok;
+        if (flipped) {
+          const uint32_t ties_at = found[2];   // words equal to the q-th lowest
+          thr = ~thr;
+          need = ties_at - need;               // the ties kept: those the q lowest leave
+          all_ties = need == ties_at;
+        }
+      }
+      if (!listed && !flipped) {
       __syncthreads();   // the listed path's readers of hist are done
       if (binned) {
         for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;

@@ -4,8 +4,8 @@ Selections of at most half the candidates first list the keys at or above a cut 
 sample (two fixed rounds per thread, R/4 and 3R/4 of its R rounds) and rank and place over that
 list; a cut that leaves too few keys or more than the list holds, or a threshold bin too crowded
 to rank directly, falls back to the histogram over every key. Selections of more than half (in the
-register tiers) list the keys to evict the same way, with the keys flipped, and place by the
-ordered scan. Each case below is built so that a given branch runs (the comment says which); every
+register tiers and the re-reading kernel) list the keys to evict the same way, with the keys
+flipped, and place by the ordered scan. Each case below is built so that a given branch runs (the comment says which); every
 one must give the oracle's keep-set exactly.
 """
 import numpy as np
@@ -134,6 +134,11 @@ CASES = [
     ("stream-70k-crowded-bin", 70000, [70000], [512], 2500, 100, "crowded-bin"),
     ("stream-70k-sample-high", 70000, [70000], [1024], 3072, 128, "stream-sample-high"),
     ("stream-70k-budget-past-list", 70000, [70000], [0], 8000, 64, "normal"),
+    # the re-reading kernel's listing from the other end (more than half selected)
+    ("stream-flip-70k", 70000, [70000, 50000], [1024, 0], 66000, 128, "ties-straddle"),
+    ("stream-flip-70k-signed-zeros", 70000, [70000], [1000], 66000, 128, "signed-zeros"),
+    ("stream-flip-70k-infinities", 70000, [70000], [256], 68000, 64, "infinities"),
+    ("stream-flip-131k-trend", 131072, [131072], [2048], 127000, 128, "trend"),
 ]
 
 
@@ -177,6 +182,10 @@ RANDOM_CASES = [
     ("random-stream-70k", 70000, [70000, 40000], [1024, 0], 3072, 128),
     ("random-stream-131k-small-share", 131072, [131072], [0], 64, 16),
     ("random-stream-70k-budget-past-list", 70000, [70000], [0], 8000, 64),
+    # the re-reading kernel's listing from the other end: past the tiers, and a short head of a
+    # 32768-slot cache whose budget is half the cache (the 512-thread kernel)
+    ("random-stream-flip-70k", 70000, [70000, 40000], [1024, 0], 66000, 128),
+    ("random-stream-flip-32k-short", 32768, [20000, 32768], [0, 0], 16384, 64),
 ]
 
 
