@@ -1221,7 +1221,8 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectParams p) {
 // min/max (scores) and the 1024-bin histogram, the threshold bin's keys ranked in LDS (or, when
 // crowded, OR/AND and 8-bit radix passes), then the ordered scan in chunks of 4 * NT slots in slot
 // order with the kept and tied counts carried from chunk to chunk. The union (KIND 2) runs G + 1
-// such passes and keeps its union as a bit per slot in dynamic LDS (t_cap / 8 bytes).
+// such passes and keeps its union as a bit per slot in dynamic LDS (t_cap / 8 bytes); a listed
+// head pass marks its selected slots from the list.
 constexpr int kStreamThreads = 1024;
 constexpr int kLeanRandomThreads = 512;   // random selection within the register tiers' sizes
 static_assert(kSelectMaxSlotsUnion / 8 <= 32 * 1024, "union bits fit in 32 KB of LDS");
@@ -1237,12 +1238,12 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
   __shared__ uint32_t n_members;
   __shared__ uint32_t kb[2];   // key interval of the threshold's bin
   extern __shared__ uint32_t ubits[];   // union: bit j set when slot j is in some head's top-k
-  // the listed path (top-k and random): keys and slots of the candidates at or above the cut
-  constexpr int LCAP = UNION ? 1 : kListMax;
+  // the listed path: keys and slots of the candidates at or above the cut
+  constexpr int LCAP = kListMax;
   __shared__ uint32_t lkey[LCAP];
   __shared__ uint32_t lslot[LCAP];
-  __shared__ __align__(16) uint32_t mlist[UNION ? 4 : kValueBins];
-  __shared__ uint32_t shist[UNION ? 1 : kSampleBins];
+  __shared__ __align__(16) uint32_t mlist[kValueBins];
+  __shared__ uint32_t shist[kSampleBins];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -1357,7 +1358,7 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
       uint32_t bsel = 0u, klo = 0u, khi = 0xFFFFFFFFu;   // key interval of the threshold's bin
       float scale = 0.f, off = 0.f, fmin = 0.f, fmax = 0.f;
       auto bin_of = [&](uint32_t k) { return RANDOM ? (k >> 22) : bin_of_key(k, scale, off); };
-      if (!UNION) {   // the listed path's LDS starts cleared (ordered before use by the barriers below)
+      {   // the listed path's LDS starts cleared (ordered before use by the barriers below)
         for (int i = tid; i < kValueBins; i += NT) mlist[i] = 0u;
         for (int i = tid; i < kSampleBins; i += NT) shist[i] = 0u;
         for (int i = tid; i < kValueBins; i += NT) hist[i] = 0u;
@@ -1517,7 +1518,7 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
       // with 4,000 to evict), so scores keep it.
       bool flipped = false;
       const int q_evict = n_cand - p_sel;
-      const bool list_top = !UNION && (RANDOM || binned) && 2 * p_sel <= n_cand && p_sel + p_sel / 8 + 64 <= LCAP;
+      const bool list_top = (RANDOM || binned) && 2 * p_sel <= n_cand && p_sel + p_sel / 8 + 64 <= LCAP;
       const bool list_low = RANDOM && !list_top && 2 * q_evict <= n_cand && q_evict + q_evict / 8 + 64 <= LCAP;
       if (list_top || list_low) {   // one call site: the listing is inlined once
         const bool ok = stream_list(list_low ? q_evict : p_sel, list_low);
@@ -1608,11 +1609,15 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
       }
     }
 
-    // ---- placement from the list (top-k and random): the pins arithmetically, the selected slots
-    // by one block-wide scan over contiguous runs of list entries (as in the register kernel)
-    if (!UNION && listed) {
-      for (int r = tid; r < P; r += NT) out[r] = r;
-      for (int r = tid; r < Rw; r += NT) out[P + n_sel + r] = e_hi + r;
+    // ---- placement from the list: the pins arithmetically, the selected slots by one block-wide
+    // scan over contiguous runs of list entries (as in the register kernel); a union head pass
+    // marks its selected slots in the union's bits instead
+    if (listed) {
+      const bool mark = UNION && !last;
+      if (!mark) {
+        for (int r = tid; r < P; r += NT) out[r] = r;
+        for (int r = tid; r < Rw; r += NT) out[P + n_sel + r] = e_hi + r;
+      }
       const uint32_t n = n_list;
       const uint32_t per = (n + NT - 1) / NT;
       const uint32_t e0 = min(n, static_cast<uint32_t>(tid) * per), e1 = min(n, e0 + per);
@@ -1640,8 +1645,13 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
           if (re < need) o = static_cast<uint32_t>(P) + ra + re;
           ++re;
         }
-        if (o < static_cast<uint32_t>(p.b_cap)) out[o] = static_cast<int32_t>(lslot[e]);
+        if (mark) {
+          if (o != 0xFFFFFFFFu) atomicOr(&ubits[lslot[e] >> 5], 1u << (lslot[e] & 31u));
+        } else if (o < static_cast<uint32_t>(p.b_cap)) {
+          out[o] = static_cast<int32_t>(lslot[e]);
+        }
       }
+      if (mark) __syncthreads();   // the union's bits are complete before the next pass reads them
       continue;
     }
 
