@@ -27,6 +27,10 @@
 //     to it that are taken. Placement then runs over the list alone: one
 //     block-wide scan of per-thread (kept, tied) counts gives each kept entry
 //     its output index. A cut that fails the count falls back to step 3.
+//     Selections of more than half list the keys to evict the same way, with
+//     the keys flipped (scores negated, random words complemented): the list
+//     gives the threshold and how many of its ties are kept (the lowest slots),
+//     and step 3's ballot placement writes the kept set.
 //  3. Otherwise a 1024-bin LDS histogram over every key (scores binned by value
 //     between the smallest and largest finite candidate, random keys by their
 //     top 10 bits) finds the bin holding the n_sel-th largest key; its keys,
@@ -317,9 +321,10 @@ constexpr uint32_t member_cap() { return 2 * NT < kValueBins - 4 ? 2 * NT : kVal
 constexpr int kSampleBins = 256;
 constexpr int kListBins = 256;
 constexpr int kListMax = 6144;
-constexpr int kStreamSamples = 4096;   // evenly spaced candidates sampled for a cut when the keys are not in registers
-// A quarter of the tier's slots: selections above half the candidates never list, and a small
-// list keeps the 256-thread tiers' LDS (and so their workgroups per CU) close to the histogram's.
+constexpr int kStreamSamples = 4096;   // candidates sampled for a cut when the keys are not in registers
+// A quarter of the tier's slots: a listing (of the selection, or of the keys to evict) never
+// takes more than half the candidates, and a small list keeps the 256-thread tiers' LDS (and so
+// their workgroups per CU) close to the histogram's.
 template <int NT, int KPT>
 constexpr int list_cap() { return NT * KPT / 4 < kListMax ? NT * KPT / 4 : kListMax; }
 
@@ -450,8 +455,9 @@ __device__ __forceinline__ uint32_t random_cut(int p_sel, int n_valid) {
   return c > 1.0 ? static_cast<uint32_t>(c) : 1u;
 }
 
-// Whether a head's selection takes the listed path: at most half the candidates (above that the
-// placement visits every key anyway), and room in a list of list_cap for the cut's margin.
+// Whether p_sel of n_valid keys can be listed: at most half the candidates (more than half are
+// listed from the other end, as the keys to evict), and room in a list of list_cap for the cut's
+// margin.
 __device__ __forceinline__ bool listable(int p_sel, int n_valid, int list_cap) {
   return p_sel > 0 && p_sel < n_valid && 2 * p_sel <= n_valid && p_sel + p_sel / 8 + 64 <= list_cap;
 }
