@@ -792,11 +792,35 @@ def main():
     torch.cuda.synchronize(dev)
     contig_gbs = ab["compact"] / (cev[0].elapsed_time(cev[1]) / args.steps * 1e-3) / 1e9
     del kept_c
+    # the score stream's own access pattern with no arithmetic (kv_stream_ceiling over all of K):
+    # reads only, and reads plus one 4-byte store per 256 bytes read, as tri_score stores its scores
+    k_bytes = K.numel() * K.element_size()
+    pat = {}
+    if k_bytes % (128 << 10) == 0:
+        sink = torch.empty((k_bytes // 256,), dtype=torch.int32, device=dev)
+        for tag, stores in (("read", False), ("read_write", True)):
+            kv.stream_ceiling(K, sink, stores)
+            cev[0].record()
+            for _ in range(args.steps):
+                kv.stream_ceiling(K, sink, stores)
+            cev[1].record()
+            torch.cuda.synchronize(dev)
+            ms = cev[0].elapsed_time(cev[1]) / args.steps
+            moved = k_bytes + (k_bytes // 64 if stores else 0)   # plus 4 bytes per 256 read with stores
+            pat[tag] = (ms, moved / (ms * 1e-3) / 1e9)
+        del sink
     ceilings = {"device_copy_gbs": copy_gbs, "compact_contiguous_gbs": contig_gbs,
                 "kv_compact_frac_of_contiguous": ab["compact"] / (k_ms["kv_compact"] * 1e-3) / 1e9 / contig_gbs,
                 "pass_gbs_over_device_copy": pass_bytes / (ms_step * 1e-3) / 1e9 / copy_gbs}
+    if pat:
+        score_gbs = ab["score"] / (k_ms["tri_score"] * 1e-3) / 1e9
+        ceilings.update({"score_pattern_read_gbs": pat["read"][1],
+                         "score_pattern_read_write_gbs": pat["read_write"][1],
+                         "tri_score_frac_of_pattern": score_gbs / pat["read_write"][1]})
     print(f"[bench] copy ceilings: device copy {copy_gbs:.0f} GB/s, kv_compact on contiguous slots "
-          f"{contig_gbs:.0f} GB/s", file=sys.stderr, flush=True)
+          f"{contig_gbs:.0f} GB/s" + (f"; score pattern over K: reads {pat['read'][1]:.0f} GB/s, with stores "
+          f"{pat['read_write'][1]:.0f} GB/s ({pat['read_write'][0]:.3f} ms)" if pat else ""),
+          file=sys.stderr, flush=True)
 
     rnd = None
     if not args.no_random:

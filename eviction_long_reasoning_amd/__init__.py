@@ -21,17 +21,22 @@ and the policy variants:
   kv_compact_inplace       fill evicted slots with the kept rows beyond the new length
   kv_audit_kept            per-head count of kept-list entries that break the partition rules
 
+and a measurement aid:
+
+  stream_ceiling           tri_score's loads (and stores) without its arithmetic
+
 The binding holds no arithmetic of its own and has no CPU fallback: without
 the built library every call raises.
 """
 from ._lib import KvError, library_path, load as load_library
 from .binding import (gqa_workspace_bytes, kv_audit_kept, kv_compact, kv_compact_inplace, kv_select_random,
                       kv_select_random_shared, kv_select_recent, kv_select_union, kv_select_topk,
-                      score_workspace_bytes, select_workspace_bytes, tri_score, tri_score_gqa,
+                      score_workspace_bytes, select_workspace_bytes, stream_ceiling, tri_score, tri_score_gqa,
                       tri_score_gqa_noalloc, tri_score_gqa_rotated, tri_score_rotated)
 
 __all__ = ["tri_score", "tri_score_rotated", "tri_score_gqa", "tri_score_gqa_rotated", "tri_score_gqa_noalloc",
            "gqa_workspace_bytes",
            "score_workspace_bytes", "select_workspace_bytes", "kv_select_topk", "kv_select_random", "kv_compact",
            "kv_select_union", "kv_select_random_shared", "kv_select_recent", "kv_compact_inplace", "kv_audit_kept",
+           "stream_ceiling",
            "KvError", "library_path", "load_library"]

@@ -78,6 +78,7 @@ _SIGNATURES = {
     "kv_select_random_shared": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, ctypes.c_uint64,
                                        ctypes.c_uint32, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
     "kv_audit_kept": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, _I32, _P, _P, _P]),
+    "kv_stream_ceiling": (_I32, [_P, ctypes.c_size_t, _P, _I32, _P]),
     "kv_select_recent": (_I32, [ctypes.POINTER(KvShape), ctypes.POINTER(KvPolicy), _P, _I32, _P, _P]),
     "kv_compact_inplace": (_I32, [ctypes.POINTER(KvShape), _P, _P, _P, _P, _I32, _P, _P]),
     "kv_compact": (_I32, [ctypes.POINTER(KvShape), _P, _P, _P, _P, _I32, _P, _P, _P, _P, _I32, _P]),

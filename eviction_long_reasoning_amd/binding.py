@@ -419,6 +419,20 @@ def kv_audit_kept(kept: torch.Tensor, n_kept: torch.Tensor, seq_len: torch.Tenso
     return bad
 
 
+def stream_ceiling(buf: torch.Tensor, out: torch.Tensor, with_stores: bool) -> None:
+    """Measurement aid: read ``buf`` (a contiguous GPU tensor of a whole number of 128 KB) with
+    tri_score's access pattern and no arithmetic, writing one 4-byte value per 256 bytes read into
+    ``out`` (with_stores) or one per 32 KB (without). See kv_stream_ceiling in include/kvevict.h."""
+    dev = buf.device
+    bp = _dev_ptr(buf, "buf", None, None, dev)
+    nbytes = buf.numel() * buf.element_size()
+    need = nbytes // 256 if with_stores else nbytes // 32768
+    op = _dev_ptr(out, "out", None, None, dev)
+    if out.numel() * out.element_size() < 4 * need:
+        raise ValueError(f"out must hold {need} 4-byte words")
+    _invoke("kv_stream_ceiling", dev, bp, ctypes.c_size_t(nbytes), op, int(bool(with_stores)))
+
+
 def kv_compact_inplace(K: torch.Tensor, V: torch.Tensor, kept: torch.Tensor, n_kept: torch.Tensor,
                        seq_len: torch.Tensor, pos: Optional[torch.Tensor] = None) -> None:
     """In-place hole filling: afterwards slots 0..n_kept-1 of each head hold the kept rows."""

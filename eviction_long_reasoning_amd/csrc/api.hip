@@ -522,6 +522,14 @@ KV_EXPORT kv_status kv_audit_kept(const kv_shape *shape, const kv_policy *policy
   return hip_status(launch_audit(p, bad, static_cast<hipStream_t>(stream)));
 }
 
+KV_EXPORT kv_status kv_stream_ceiling(const void *buf, size_t bytes, uint32_t *out, int32_t with_stores, void *stream) {
+  if (!buf || !out || !aligned16(buf) || !words({out})) return KV_EINVAL;
+  if (bytes == 0 || bytes % kStreamCeilingChunk != 0) return KV_EINVAL;
+  if (bytes / kStreamCeilingChunk >= (1ull << 31)) return KV_ESHAPE;
+  return hip_status(launch_stream_ceiling(buf, bytes, out, with_stores != 0,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 KV_EXPORT kv_status kv_select_random_shared(const kv_shape *shape, const kv_policy *policy, const int32_t *pos,
                                           uint64_t seed, uint32_t event, int32_t *kept, int32_t b_cap,
                                           int32_t *n_kept, void *workspace, size_t workspace_bytes, void *stream) {

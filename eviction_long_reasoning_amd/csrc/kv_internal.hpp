@@ -141,4 +141,8 @@ struct HoleParams {
 
 hipError_t launch_compact_holes(const HoleParams &p, hipStream_t st);
 
+// The score stream's access pattern alone (measurement aid): bytes a multiple of 128 KB.
+constexpr size_t kStreamCeilingChunk = 131072;
+hipError_t launch_stream_ceiling(const void *buf, size_t bytes, uint32_t *out, bool stores, hipStream_t st);
+
 }  // namespace kvevict

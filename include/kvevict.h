@@ -23,6 +23,10 @@
  *
  *   kv_audit_kept            count, per head, the entries of a kept list that break the rules
  *
+ * and a measurement aid:
+ *
+ *   kv_stream_ceiling        tri_score's loads (and stores) without its arithmetic
+ *
  * Conventions shared by every call
  * --------------------------------
  *  - All array arguments are DEVICE pointers owned by the caller, except
@@ -391,6 +395,26 @@ kv_status kv_select_random(const kv_shape *shape, const kv_policy *policy,
  */
 kv_status kv_audit_kept(const kv_shape *shape, const kv_policy *policy, const int32_t *kept,
                         int32_t b_cap, const int32_t *n_kept, int32_t *bad, void *stream);
+
+/*
+ * kv_stream_ceiling -- a measurement aid, not part of the method: the memory system's ceiling for
+ * tri_score's access pattern (bf16 keys of head_dim 128). It reads `bytes` of `buf` once as
+ * tri_score does -- workgroups of 256 threads over 128 KB each, every wave two batches of sixteen
+ * 16-byte pieces per lane, the second issued before the first is combined, non-temporal loads --
+ * and combines each lane's pieces by XOR instead of scoring them. Timed beside tri_score over the
+ * same bytes it separates the cost of the access pattern from that of the arithmetic.
+ *
+ *  buf     device, 16-byte aligned; bytes a positive multiple of 131072 (below 2^48).
+ *  out     device uint32 words:
+ *          with_stores != 0 (tri_score's score stream, non-temporal): bytes / 256 words; word
+ *            (w * 128 + b * 64 + lane) is the XOR of the 64 32-bit words of lane `lane`'s 16 pieces
+ *            of batch b (0, 1) of wave w, waves numbered in address order (32 KB each), a lane's
+ *            pieces being the 16 bytes at lane * 16 + t * 1024 (t < 16) of its batch's 16 KB;
+ *          with_stores == 0: bytes / 32768 words, word w the XOR over wave w's lanes and batches.
+ * Errors: KV_EINVAL for NULL or misaligned pointers or a size that is not a whole number of 128 KB;
+ * KV_ESHAPE from 2^48 bytes on.
+ */
+kv_status kv_stream_ceiling(const void *buf, size_t bytes, uint32_t *out, int32_t with_stores, void *stream);
 
 /*
  * kv_select_union -- union-based selection ([TA-blog] eviction step) over the

@@ -123,6 +123,16 @@ int main() {
   EXPECT(kv_compact(&sh, a, (void *)0x2000000, nullptr, kept, 1024, nk, a, (void *)0x3000000, nullptr, 1024, nullptr), KV_EINVAL);
   EXPECT(kv_compact_inplace(&sh, a, (void *)0x1000010, nullptr, kept, 1024, nk, nullptr), KV_EINVAL);
 
+  // measurement aid: NULL or misaligned pointers, a size that is not a whole number of 128 KB
+  uint32_t *o = reinterpret_cast<uint32_t *>(0x5000);
+  EXPECT(kv_stream_ceiling(nullptr, 131072, o, 1, nullptr), KV_EINVAL);
+  EXPECT(kv_stream_ceiling(a, 131072, nullptr, 0, nullptr), KV_EINVAL);
+  EXPECT(kv_stream_ceiling((void *)0x1000008, 131072, o, 1, nullptr), KV_EINVAL);
+  EXPECT(kv_stream_ceiling(a, 131072, (uint32_t *)0x5002, 1, nullptr), KV_EINVAL);
+  EXPECT(kv_stream_ceiling(a, 0, o, 1, nullptr), KV_EINVAL);
+  EXPECT(kv_stream_ceiling(a, 131072 + 4096, o, 1, nullptr), KV_EINVAL);
+  EXPECT(kv_stream_ceiling(a, static_cast<size_t>(1) << 48, o, 1, nullptr), KV_ESHAPE);
+
   if (failures) std::fprintf(stderr, "%d failures\n", failures);
   else std::printf("host checks ok\n");
   return failures ? 1 : 0;

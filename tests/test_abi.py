@@ -155,6 +155,18 @@ def test_host_validation_rejects_bad_arguments(lib):
                           ctypes.c_void_p(0x300000), None, 8, None) == L.KV_EINVAL
 
 
+def test_stream_ceiling_validation(lib):
+    from eviction_long_reasoning_amd import _lib as L
+    a, o = ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x5000)   # never dereferenced
+    assert lib.kv_stream_ceiling(None, 131072, o, 1, None) == L.KV_EINVAL
+    assert lib.kv_stream_ceiling(a, 131072, None, 0, None) == L.KV_EINVAL
+    assert lib.kv_stream_ceiling(ctypes.c_void_p(0x1000008), 131072, o, 1, None) == L.KV_EINVAL   # misaligned
+    assert lib.kv_stream_ceiling(a, 131072, ctypes.c_void_p(0x5002), 1, None) == L.KV_EINVAL
+    assert lib.kv_stream_ceiling(a, 0, o, 1, None) == L.KV_EINVAL
+    assert lib.kv_stream_ceiling(a, 131072 + 4096, o, 1, None) == L.KV_EINVAL                  # not whole 128 KB
+    assert lib.kv_stream_ceiling(a, 1 << 48, o, 1, None) == L.KV_ESHAPE
+
+
 def test_workspace_queries_and_rejections(lib):
     # tri_score and the top-k / random selectors take a caller workspace sized by their queries;
     # a missing, misaligned or short one is rejected before any launch

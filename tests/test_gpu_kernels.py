@@ -1246,3 +1246,26 @@ def test_compaction_random_sweep(sweep):
             if Pi is not None:
                 assert np.array_equal(Pi[0, s, h, :n], hp), ("in place positions", s, h)
     log(f"[compact sweep {sweep}] bit-exact")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("with_stores", [True, False])
+def test_stream_ceiling_reads_every_byte_once(with_stores):
+    """The measurement aid's output is a fixed XOR of what it read: wave w covers bytes
+    [32 KB w, 32 KB (w+1)), lane l of batch b takes the 16-byte pieces at 16 KB b + 1 KB t + 16 l
+    (t = 0..15). With stores each (wave, batch, lane) value lands in word 128 w + 64 b + l; without,
+    word w holds the XOR over all of them. A missed or doubled piece changes the result."""
+    n_bytes = 3 * 131072
+    words = rng(41).integers(0, 2**32, size=n_bytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).to(DEV)
+    per = words.reshape(n_bytes // 32768, 2, 16, 64, 4)
+    lane_x = np.bitwise_xor.reduce(np.bitwise_xor.reduce(per, axis=4), axis=2)   # [waves, 2, 64]
+    if with_stores:
+        want = lane_x.reshape(-1)
+    else:
+        want = np.bitwise_xor.reduce(lane_x.reshape(lane_x.shape[0], -1), axis=1)
+    out = torch.full((want.size + 8,), -7, dtype=torch.int32, device=DEV)
+    kv.stream_ceiling(buf, out, with_stores)
+    got = out.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got[:want.size], want)
+    assert (got[want.size:] == np.uint32(2**32 - 7)).all()   # nothing past the output
