@@ -111,7 +111,7 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 using namespace kvevict;
 
-KV_EXPORT int32_t kv_version(void) { return (2 << 16) | 0; }
+KV_EXPORT int32_t kv_version(void) { return (2 << 16) | 1; }
 
 KV_EXPORT int32_t kv_device_checks(void) { return KV_DEVICE_CHECKS ? 1 : 0; }
 

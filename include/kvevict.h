@@ -146,7 +146,7 @@ typedef struct kv_policy {
  * Kept sets are written in ascending (chronological) order, [RA] Appendix F.
  */
 
-/* Library version, (major << 16) | minor. */
+/* Library version, (major << 16) | minor: 2.1 (2.1 added kv_stream_ceiling). */
 int32_t kv_version(void);
 
 /* Static string for a kv_status value. */
