@@ -52,9 +52,9 @@ namespace {
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
 // Easy as 1, 2, 3", SC'11): 10 rounds of two 32x32->64 products on counter
 // words 0 and 2 with the published multipliers, the key advanced between
-// rounds by the published Weyl constants. Returns output word 0.
-__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
-                                                 uint32_t k0, uint32_t k1) {
+// rounds by the published Weyl constants. Returns the block's four words.
+__device__ __forceinline__ uint4 philox_block(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                              uint32_t k0, uint32_t k1) {
   constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
   constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
 #pragma unroll
@@ -72,7 +72,16 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
     k0 += kWeylA;
     k1 += kWeylB;
   }
-  return c0;
+  return make_uint4(c0, c1, c2, c3);
+}
+
+// The draw of position p: word p mod 4 of the block with counter word 0 = p div 4, so one block
+// serves four consecutive positions.
+__device__ __forceinline__ uint32_t philox_draw(uint32_t p, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                uint32_t k1) {
+  const uint4 b = philox_block(p >> 2, c1, c2, c3, k0, k1);
+  const uint32_t w = p & 3u;
+  return w == 0u ? b.x : w == 1u ? b.y : w == 2u ? b.z : b.w;
 }
 
 // Order-preserving uint32 image of an fp32 score: NaN ranks as -inf, -0 equals +0.
@@ -611,12 +620,50 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
 #pragma unroll
       for (int i = g; i < g + GR; ++i) key[i] = 0u;
       if (end > e_lo && first < e_hi) {
+        uint32_t c0s[GR];   // the positions of this lane's slots in the group
 #pragma unroll
-        for (int i = g; i < g + GR; ++i) {
-          const int j = j0 + i * 64;
-          const uint32_t c0 = p.pos ? ld32(rp, j * 4, 0) : static_cast<uint32_t>(j);
-          const uint32_t w = philox_word0(c0, c1, static_cast<uint32_t>(hd.s), p.event, p.seed_lo, p.seed_hi);
-          key[i] = evictable(j0, i) ? w : 0u;
+        for (int k = 0; k < GR; ++k) {
+          const int j = j0 + (g + k) * 64;
+          c0s[k] = p.pos ? ld32(rp, j * 4, 0) : static_cast<uint32_t>(j);
+        }
+        // When the group's positions run consecutively from a multiple of 4 (always, without
+        // explicit positions), its 64 * GR slots take 16 * GR whole Philox blocks: each lane draws
+        // GR / 4 of them and takes its words from the lanes that drew them (round g + k, lane m:
+        // word m mod 4 of block 16 k + m / 4). Otherwise every slot draws its own block.
+        bool shared = false;
+        if constexpr (GR % 4 == 0) {
+          const uint32_t p0 = p.pos ? static_cast<uint32_t>(__shfl(static_cast<int>(c0s[0]), 0, 64))
+                                    : static_cast<uint32_t>(first);
+          bool run = (p0 & 3u) == 0u;
+#pragma unroll
+          for (int k = 0; k < GR; ++k) run = run && c0s[k] == p0 + static_cast<uint32_t>(k * 64 + lane);
+          shared = __builtin_amdgcn_ballot_w64(!run) == 0;
+          if (shared) {
+            uint4 blk[GR / 4];
+#pragma unroll
+            for (int b = 0; b < GR / 4; ++b)
+              blk[b] = philox_block((p0 >> 2) + static_cast<uint32_t>(64 * b + lane), c1, static_cast<uint32_t>(hd.s),
+                                    p.event, p.seed_lo, p.seed_hi);
+            const int sel = lane & 3;
+#pragma unroll
+            for (int k = 0; k < GR; ++k) {
+              const int src = 16 * (k & 3) + (lane >> 2);
+              const uint4 &bk = blk[k / 4];
+              const uint32_t x = static_cast<uint32_t>(__shfl(static_cast<int>(bk.x), src, 64));
+              const uint32_t y = static_cast<uint32_t>(__shfl(static_cast<int>(bk.y), src, 64));
+              const uint32_t z = static_cast<uint32_t>(__shfl(static_cast<int>(bk.z), src, 64));
+              const uint32_t w = static_cast<uint32_t>(__shfl(static_cast<int>(bk.w), src, 64));
+              const uint32_t wd = sel == 0 ? x : sel == 1 ? y : sel == 2 ? z : w;
+              key[g + k] = evictable(j0, g + k) ? wd : 0u;
+            }
+          }
+        }
+        if (!shared) {
+#pragma unroll
+          for (int k = 0; k < GR; ++k) {
+            const uint32_t w = philox_draw(c0s[k], c1, static_cast<uint32_t>(hd.s), p.event, p.seed_lo, p.seed_hi);
+            key[g + k] = evictable(j0, g + k) ? w : 0u;
+          }
         }
       }
     }
@@ -1049,7 +1096,7 @@ __global__ __launch_bounds__(kSplitThreads) void select_split_kernel(const Selec
   for (int i = 0; i < R; ++i) {
     const int j = jb + i * 64;
     const uint32_t c0 = p.pos ? ld32(rp, j * 4, 0) : static_cast<uint32_t>(j);
-    key[i] = philox_word0(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
+    key[i] = philox_draw(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
     pass[i] = j < e_hi && key[i] >= cut_k;
   }
   uint32_t c = 0u;
@@ -1316,7 +1363,7 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
     auto key_from = [&](int j, uint32_t bits) -> uint32_t {
       if (RANDOM) {
         const uint32_t c0 = p.pos ? bits : static_cast<uint32_t>(j);
-        return philox_word0(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
+        return philox_draw(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
       }
       const uint32_t k = order_key(__uint_as_float(bits));
       if (UNION && last) {
@@ -1436,13 +1483,17 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
           }
         }
         // KC consecutive candidates per thread and chunk, the next chunk's loads issued before
-        // this chunk's keys are formed and listed (the last chunk's next reads past e_hi: no access)
+        // this chunk's keys are formed and listed (the last chunk's next reads past e_hi: no access).
+        // Random draws at the slots' own positions start their chunks at a multiple of 4 slots, so
+        // a thread's 8 slots are exactly two Philox blocks (slots below e_lo take no part).
         constexpr int KC = RANDOM ? 8 : 4;
+        const bool blocks = RANDOM && !p.pos;
+        const int c_first = blocks ? (e_lo & ~3) : e_lo;
         uint32_t nxt[KC];
 #pragma unroll
-        for (int q = 0; q < KC; ++q) nxt[q] = load_of(e_lo + KC * tid + q);
+        for (int q = 0; q < KC; ++q) nxt[q] = load_of(c_first + KC * tid + q);
         uint32_t carry = 0u;
-        for (int c = e_lo; c < e_hi; c += KC * NT) {
+        for (int c = c_first; c < e_hi; c += KC * NT) {
           const int j0 = c + KC * tid;
           uint32_t cur[KC];
 #pragma unroll
@@ -1452,13 +1503,34 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const SelectParams p)
           }
           uint32_t kk[KC];
           uint32_t f = 0u;
+          if (RANDOM && blocks) {
+            uint32_t w8[8];
 #pragma unroll
-          for (int q = 0; q < KC; ++q) {
-            kk[q] = 0u;
-            if (j0 + q < e_hi) {
-              kk[q] = key_from(j0 + q, cur[q]);
-              if (RANDOM && fl) kk[q] = flipped_key(kk[q]);
-              f |= static_cast<uint32_t>(kk[q] >= cut) << q;
+            for (int b = 0; b < 2; ++b) {
+              const uint4 blk = philox_block(static_cast<uint32_t>(j0 >> 2) + b, c1, static_cast<uint32_t>(s), p.event,
+                                             p.seed_lo, p.seed_hi);
+              w8[4 * b] = blk.x;
+              w8[4 * b + 1] = blk.y;
+              w8[4 * b + 2] = blk.z;
+              w8[4 * b + 3] = blk.w;
+            }
+#pragma unroll
+            for (int q = 0; q < KC; ++q) {
+              kk[q] = 0u;
+              if (j0 + q >= e_lo && j0 + q < e_hi) {
+                kk[q] = fl ? flipped_key(w8[q]) : w8[q];
+                f |= static_cast<uint32_t>(kk[q] >= cut) << q;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < KC; ++q) {
+              kk[q] = 0u;
+              if (j0 + q < e_hi) {
+                kk[q] = key_from(j0 + q, cur[q]);
+                if (RANDOM && fl) kk[q] = flipped_key(kk[q]);
+                f |= static_cast<uint32_t>(kk[q] >= cut) << q;
+              }
             }
           }
           const uint32_t cnt = static_cast<uint32_t>(__popc(f));

@@ -354,9 +354,10 @@ size_t kv_select_workspace_bytes(const kv_shape *shape, int32_t b_cap);
 /*
  * kv_select_random -- Random Attention's per-head uniform eviction.
  *
- * Every evictable slot j gets u_j = word 0 of Philox4x32-10 (Salmon et al.,
- * SC'11) with counter (p_j, (l << 16) | h, s, event) and key
- * (seed & 0xffffffff, seed >> 32) -- an i.i.d. uniform drawn independently
+ * Every evictable slot j gets u_j = word (p_j & 3) of Philox4x32-10 (Salmon
+ * et al., SC'11) with counter (p_j >> 2, (l << 16) | h, s, event) and key
+ * (seed & 0xffffffff, seed >> 32) -- one block gives the draws of four
+ * consecutive positions -- an i.i.d. uniform drawn independently
  * per KV head at every eviction; prompt and recent window are pinned; the
  * n_sel largest u_j are kept (ties to the lower slot). [RA] section 3,
  * Eq. 3 and Algorithm 1. No scores or keys are read.

@@ -33,10 +33,10 @@ the design notes):
     holds the latest R' slots, so |kept| = B whenever P <= B.
   * Ranking is (score descending, slot ascending); NaN ranks as -inf and
     -0.0 equals +0.0.
-  * The random score of a candidate slot j is word 0 of Philox4x32-10 with
-    counter (p_j, (layer << 16) | head, seq, event) and key (seed mod 2^32,
-    seed >> 32), read as the uniform u = word0 / 2^32; ties go to the lower
-    slot.
+  * The random score of a candidate slot j is word (p_j mod 4) of
+    Philox4x32-10 with counter (p_j div 4, (layer << 16) | head, seq, event)
+    and key (seed mod 2^32, seed >> 32), read as the uniform u = word / 2^32;
+    ties go to the lower slot.
   * Recency+prompt keeps the prompt and the n_kept - P latest slots (the
     evictable range's n_sel latest slots joined to the recent window).
   * The shared draw is the draw of layer 0, KV head 0, used by every
@@ -115,7 +115,9 @@ def select_topk(scores, T: int, P: int, B: int, R: int) -> np.ndarray:
 
 
 def random_uniforms(pos, layer: int, head: int, seq: int, event: int, seed: int) -> np.ndarray:
-    """u_j = word0(Philox4x32-10(ctr=(p_j, layer<<16|head, seq, event), key=seed)) / 2^32."""
+    """u_j = word (p_j mod 4) of Philox4x32-10(ctr=(p_j div 4, layer<<16|head, seq, event),
+    key=seed) / 2^32: each block of the counter-based generator gives the four uniforms of four
+    consecutive positions, a distinct word for every distinct position."""
     p = np.asarray(pos, dtype=np.int64).astype(np.uint64) & np.uint64(0xFFFFFFFF)
     n = p.size
     c1 = np.full(n, ((int(layer) << 16) | int(head)) & 0xFFFFFFFF, np.uint64)
@@ -123,8 +125,9 @@ def random_uniforms(pos, layer: int, head: int, seq: int, event: int, seed: int)
     c3 = np.full(n, int(event) & 0xFFFFFFFF, np.uint64)
     k0 = np.full(n, int(seed) & 0xFFFFFFFF, np.uint64)
     k1 = np.full(n, (int(seed) >> 32) & 0xFFFFFFFF, np.uint64)
-    w0 = philox4x32_10_np(p, c1, c2, c3, k0, k1)[0]
-    return w0.astype(np.float64) / 4294967296.0
+    words = np.stack(philox4x32_10_np(p >> np.uint64(2), c1, c2, c3, k0, k1))   # (4, n)
+    u = words[(p & np.uint64(3)).astype(np.int64), np.arange(n)]
+    return u.astype(np.float64) / 4294967296.0
 
 
 def select_random(T: int, P: int, B: int, R: int, pos: Optional[np.ndarray],

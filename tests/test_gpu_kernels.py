@@ -530,6 +530,40 @@ def test_select_random_bit_exact(case, with_pos):
                 assert np.all(kept[l, s, h, ref.size:] == -1)
 
 
+# Positions that run consecutively from a multiple of 4 let a group of 512 slots share 128 Philox
+# blocks (each lane draws some and passes words to the lanes that need them); any other layout
+# draws per slot. Layouts: runs from offsets 0..3 (only 0 and 4 share), a run broken once inside a
+# group, runs restarting every 300 slots, and the slots themselves; every tier from the 256-thread
+# one to the re-reading kernel, budgets below and above half the cache.
+@pytest.mark.parametrize("t_cap,budget", [(2048, 500), (2176, 1900), (8192, 3000), (16384, 9000),
+                                          (32768, 20000), (32768, 3072), (70000, 20000)])
+def test_select_random_block_sharing_layouts(t_cap, budget):
+    L, S, H = 1, 7, 2
+    Ts = [t_cap, t_cap - 5, t_cap, t_cap, t_cap - 77, t_cap, t_cap]
+    Ps = [64, 37, 1, 130, 0, 1000, 3]
+    R = 128
+    pcap = max(Ps)
+    base = np.arange(t_cap, dtype=np.int64)
+    layouts = [base + 40, base + 41, base + 42, base + 7, base + 4 * 1000,
+               np.where(base < 700, base, base + 9), (base // 300) * 1000 + base % 300]
+    pos = np.zeros((L, S, H, t_cap), np.int32)
+    for s in range(S):
+        pos[0, s, :] = layouts[s]
+    seed, event = 0x0123456789ABCDEF, 5
+    log(f"[random blocks] t_cap {t_cap} budget {budget}")
+    for with_pos in (True, False):
+        kept, nk = kv.kv_select_random((L, S, H, t_cap), _i32(Ts), _i32(Ps), budget, R, pcap, seed, event,
+                                       pos=_i32(pos) if with_pos else None)
+        kept, nk = kept.cpu().numpy(), nk.cpu().numpy()
+        for s in range(S):
+            for h in range(H):
+                ref = oracle.select_random(Ts[s], Ps[s], budget, R, pos[0, s, h] if with_pos else None,
+                                           seed, event, 0, h, s)
+                assert nk[s] == ref.size
+                assert np.array_equal(kept[0, s, h, :ref.size], ref), f"t_cap {t_cap} s{s} h{h} pos={with_pos}"
+                assert np.all(kept[0, s, h, ref.size:] == -1)
+
+
 # every tier boundary of the selectors (register tiers, the union's tiers, the re-reading kernel)
 TIER_EDGES = [1, 3, 1024, 1025, 4096, 4097, 8192, 8193, 16384, 16385, 32768, 32769, 65536, 65537]
 

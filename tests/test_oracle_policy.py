@@ -116,14 +116,17 @@ def test_random_kept_structure():
 
 
 def test_random_uniforms_layout():
-    # slot position p draws word 0 of the Philox block with counter (p, layer<<16|head, seq, event)
-    # and key (seed mod 2^32, seed >> 32): checked against the scalar generator (itself pinned to an
-    # independent implementation), so a wrong counter word, word or key order fails here
+    # position p draws word p mod 4 of the Philox block with counter (p div 4, layer<<16|head, seq,
+    # event) and key (seed mod 2^32, seed >> 32): checked against the scalar generator (itself
+    # pinned to an independent implementation), so a wrong counter word, word or key order fails
     layer, head, seq, event, seed = 5, 3, 7, 11, 0x0123456789ABCDEF
     key = (seed & 0xFFFFFFFF, seed >> 32)
-    pos = np.array([0, 1, 2, 3, 4097, 2 ** 31 + 6])
-    want = [philox4x32_10((p, (layer << 16) | head, seq, event), key)[0] / 2 ** 32 for p in pos.tolist()]
+    pos = np.array([0, 1, 2, 3, 4, 7, 4097, 4098, 2 ** 31 + 6, 2 ** 32 - 1])
+    want = [philox4x32_10((p >> 2, (layer << 16) | head, seq, event), key)[p & 3] / 2 ** 32 for p in pos.tolist()]
     assert np.array_equal(random_uniforms(pos, layer, head, seq, event, seed), np.array(want))
+    # the four positions of a block take its four words, so no two positions share a uniform
+    quad = random_uniforms(np.arange(8, 12), layer, head, seq, event, seed) * 2 ** 32
+    assert quad.tolist() == [float(w) for w in philox4x32_10((2, (layer << 16) | head, seq, event), key)]
     # each argument reaches the draw
     base = random_uniforms(pos, layer, head, seq, event, seed)
     for args in ((layer + 1, head, seq, event, seed), (layer, head + 1, seq, event, seed),
