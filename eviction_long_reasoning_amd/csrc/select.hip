@@ -14,8 +14,9 @@
 // thread t holds slot i*NT + t in round i, so every round is one coalesced
 // 4-byte-per-lane load and the head's scores are read from HBM exactly once:
 //  1. Keys: fp32 scores with NaN ranked as -inf (float comparisons give the
-//     ranking, -0 equal to +0) or, for the random selector, word 0 of
-//     Philox4x32-10 compared as uint32.
+//     ranking, -0 equal to +0) or, for the random selector, word p mod 4 of
+//     the Philox4x32-10 block at counter p div 4 (p the slot's position),
+//     compared as uint32.
 //  2. Listed path (selections of at most half the candidates): a cut below the
 //     threshold -- from a sample of the scores (two rounds per thread, binned by
 //     value) or, for uniform random words, from the selection's share -- is
