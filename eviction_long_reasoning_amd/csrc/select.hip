@@ -85,6 +85,47 @@ __device__ __forceinline__ uint32_t philox_draw(uint32_t p, uint32_t c1, uint32_
   return w == 0u ? b.x : w == 1u ? b.y : w == 2u ? b.z : b.w;
 }
 
+// The draws of a wave's GR rounds of 64 consecutive slots (round k, lane m: slot first + 64 k + m),
+// pos[k] this lane's position in round k. When the positions run consecutively from a multiple of
+// 4 over the whole group (always when they are the slots themselves and `first` is one), its 16 GR
+// Philox blocks are drawn once each, GR / 4 per lane, and every lane takes its words from the lanes
+// that drew them (round k, lane m: word m mod 4 of block 16 k + m / 4, drawn by lane
+// 16 (k mod 4) + m / 4); otherwise every slot draws its own block. Call from wave-uniform control
+// flow with every lane active.
+template <int GR>
+__device__ __forceinline__ void philox_group(uint32_t (&w)[GR], const uint32_t (&pos)[GR], int lane, uint32_t c1,
+                                             uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1) {
+  bool shared = false;
+  if constexpr (GR % 4 == 0) {
+    const uint32_t p0 = static_cast<uint32_t>(__shfl(static_cast<int>(pos[0]), 0, 64));
+    bool run = (p0 & 3u) == 0u;
+#pragma unroll
+    for (int k = 0; k < GR; ++k) run = run && pos[k] == p0 + static_cast<uint32_t>(k * 64 + lane);
+    shared = __builtin_amdgcn_ballot_w64(!run) == 0;
+    if (shared) {
+      uint4 blk[GR / 4];
+#pragma unroll
+      for (int b = 0; b < GR / 4; ++b)
+        blk[b] = philox_block((p0 >> 2) + static_cast<uint32_t>(64 * b + lane), c1, c2, c3, k0, k1);
+      const int sel = lane & 3;
+#pragma unroll
+      for (int k = 0; k < GR; ++k) {
+        const int src = 16 * (k & 3) + (lane >> 2);
+        const uint4 &bk = blk[k / 4];
+        const uint32_t x = static_cast<uint32_t>(__shfl(static_cast<int>(bk.x), src, 64));
+        const uint32_t y = static_cast<uint32_t>(__shfl(static_cast<int>(bk.y), src, 64));
+        const uint32_t z = static_cast<uint32_t>(__shfl(static_cast<int>(bk.z), src, 64));
+        const uint32_t v = static_cast<uint32_t>(__shfl(static_cast<int>(bk.w), src, 64));
+        w[k] = sel == 0 ? x : sel == 1 ? y : sel == 2 ? z : v;
+      }
+    }
+  }
+  if (!shared) {
+#pragma unroll
+    for (int k = 0; k < GR; ++k) w[k] = philox_draw(pos[k], c1, c2, c3, k0, k1);
+  }
+}
+
 // Order-preserving uint32 image of an fp32 score: NaN ranks as -inf, -0 equals +0.
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t b = __float_as_uint(f);
@@ -627,45 +668,10 @@ __device__ __forceinline__ void select_rounds(const SelectParams &p, const Selec
           const int j = j0 + (g + k) * 64;
           c0s[k] = p.pos ? ld32(rp, j * 4, 0) : static_cast<uint32_t>(j);
         }
-        // When the group's positions run consecutively from a multiple of 4 (always, without
-        // explicit positions), its 64 * GR slots take 16 * GR whole Philox blocks: each lane draws
-        // GR / 4 of them and takes its words from the lanes that drew them (round g + k, lane m:
-        // word m mod 4 of block 16 k + m / 4). Otherwise every slot draws its own block.
-        bool shared = false;
-        if constexpr (GR % 4 == 0) {
-          const uint32_t p0 = p.pos ? static_cast<uint32_t>(__shfl(static_cast<int>(c0s[0]), 0, 64))
-                                    : static_cast<uint32_t>(first);
-          bool run = (p0 & 3u) == 0u;
+        uint32_t w[GR];
+        philox_group<GR>(w, c0s, lane, c1, static_cast<uint32_t>(hd.s), p.event, p.seed_lo, p.seed_hi);
 #pragma unroll
-          for (int k = 0; k < GR; ++k) run = run && c0s[k] == p0 + static_cast<uint32_t>(k * 64 + lane);
-          shared = __builtin_amdgcn_ballot_w64(!run) == 0;
-          if (shared) {
-            uint4 blk[GR / 4];
-#pragma unroll
-            for (int b = 0; b < GR / 4; ++b)
-              blk[b] = philox_block((p0 >> 2) + static_cast<uint32_t>(64 * b + lane), c1, static_cast<uint32_t>(hd.s),
-                                    p.event, p.seed_lo, p.seed_hi);
-            const int sel = lane & 3;
-#pragma unroll
-            for (int k = 0; k < GR; ++k) {
-              const int src = 16 * (k & 3) + (lane >> 2);
-              const uint4 &bk = blk[k / 4];
-              const uint32_t x = static_cast<uint32_t>(__shfl(static_cast<int>(bk.x), src, 64));
-              const uint32_t y = static_cast<uint32_t>(__shfl(static_cast<int>(bk.y), src, 64));
-              const uint32_t z = static_cast<uint32_t>(__shfl(static_cast<int>(bk.z), src, 64));
-              const uint32_t w = static_cast<uint32_t>(__shfl(static_cast<int>(bk.w), src, 64));
-              const uint32_t wd = sel == 0 ? x : sel == 1 ? y : sel == 2 ? z : w;
-              key[g + k] = evictable(j0, g + k) ? wd : 0u;
-            }
-          }
-        }
-        if (!shared) {
-#pragma unroll
-          for (int k = 0; k < GR; ++k) {
-            const uint32_t w = philox_draw(c0s[k], c1, static_cast<uint32_t>(hd.s), p.event, p.seed_lo, p.seed_hi);
-            key[g + k] = evictable(j0, g + k) ? w : 0u;
-          }
-        }
+        for (int k = 0; k < GR; ++k) key[g + k] = evictable(j0, g + k) ? w[k] : 0u;
       }
     }
   }
@@ -1093,12 +1099,21 @@ __global__ __launch_bounds__(kSplitThreads) void select_split_kernel(const Selec
   const int jb = c_lo + wave * 64 * R + lane;
   uint32_t key[R];
   bool pass[R];
+  constexpr int GR = R % 4 == 0 ? 4 : 1;   // rounds per group of draws
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int j = jb + i * 64;
-    const uint32_t c0 = p.pos ? ld32(rp, j * 4, 0) : static_cast<uint32_t>(j);
-    key[i] = philox_draw(c0, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
-    pass[i] = j < e_hi && key[i] >= cut_k;
+  for (int g = 0; g < R; g += GR) {
+    uint32_t c0s[GR], w[GR];
+#pragma unroll
+    for (int k = 0; k < GR; ++k) {
+      const int j = jb + (g + k) * 64;
+      c0s[k] = p.pos ? ld32(rp, j * 4, 0) : static_cast<uint32_t>(j);
+    }
+    philox_group<GR>(w, c0s, lane, c1, static_cast<uint32_t>(s), p.event, p.seed_lo, p.seed_hi);
+#pragma unroll
+    for (int k = 0; k < GR; ++k) {
+      key[g + k] = w[k];
+      pass[g + k] = jb + (g + k) * 64 < e_hi && w[k] >= cut_k;
+    }
   }
   uint32_t c = 0u;
 #pragma unroll
